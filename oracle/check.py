@@ -1,0 +1,166 @@
+"""Comparison of a bf16 result against the oracle -- TEST INFRASTRUCTURE ONLY.
+
+Tolerance (the parity bar for floating point):
+
+* strict: every output within 2 bf16 ULP of the oracle's output, where the ULP
+  distance of two bf16 values is the difference of their sign-magnitude
+  ordered 16-bit codes (+0 and -0 are the same point; NaN matches only NaN);
+* mean relative error <= 0.3% over outputs whose oracle value is non-zero;
+* bit-exact fraction >= 99.9% (a single-rounding kernel also meets the first
+  two bars, so this one is what pins the four bf16 roundings in the device
+  path).
+
+An fp32 accumulation cannot hold 2 ULP where a dot product nearly cancels.
+An output that fails the strict check therefore passes only if it lies in
+its *admissible interval*: the oracle's epilogue applied over every gate and
+up pre-activation an fp32 sum of depth ``d`` can reach,
+``G +- gamma_d * sum|h*w|`` with ``gamma_d = d*2^-24 / (1 - d*2^-24)``
+(the order-independent error bound of a floating-point inner product), widened
+by 2 ULP.  Such outputs are counted and reported with their condition number
+``kappa = sum|h*w| / |sum h*w|``; one with kappa < 1e4 is never excused.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from . import DualGemvResult, round_bf16, silu_bf16
+
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns widen quietly
+        return b.view(np.float32).astype(np.float64)
+
+
+def is_nan_bits(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+
+
+def ordered(bits: np.ndarray) -> np.ndarray:
+    """Sign-magnitude bf16 codes mapped to integers that count ULPs (+0 == -0)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def from_ordered(o: np.ndarray) -> np.ndarray:
+    o = np.asarray(o, dtype=np.int64)
+    return np.where(o < 0, 0x8000 | (-o), o).astype(np.uint16)
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """ULP distance between bf16 bit arrays; NaN vs NaN is 0, NaN vs number is 2^16."""
+    na, nb = is_nan_bits(a), is_nan_bits(b)
+    d = np.abs(ordered(a) - ordered(b))
+    d = np.where(na & nb, 0, d)
+    return np.where(na ^ nb, 1 << 16, d)
+
+
+def gamma(depth: int) -> float:
+    du = depth * U32
+    return du / (1.0 - du)
+
+
+def _admissible_range(pre: float, abs_sum: float, depth: int, k_len: int):
+    """Smallest and largest bf16 (ordered codes) that rounding any reachable sum can give."""
+    tau = gamma(depth) * abs_sum + k_len * 2.0 ** -53 * abs_sum  # device bound + oracle's own fp64 error
+    lo, hi = round_bf16(np.array([pre - tau, pre + tau]))
+    return int(ordered(lo)), int(ordered(hi))
+
+
+def admissible_out_range(G: float, U: float, Ga: float, Ua: float, depth: int, k_len: int):
+    """Ordered-code interval of outputs reachable from any admissible (g, u)."""
+    g_lo, g_hi = _admissible_range(G, Ga, depth, k_len)
+    u_lo, u_hi = _admissible_range(U, Ua, depth, k_len)
+    g_set = from_ordered(np.arange(g_lo, g_hi + 1))
+    s = bf16_to_f64(silu_bf16(g_set))
+    s_min, s_max = float(np.min(s)), float(np.max(s))
+    u_min, u_max = float(bf16_to_f64(from_ordered(np.array([u_lo])))[0]), \
+        float(bf16_to_f64(from_ordered(np.array([u_hi])))[0])
+    corners = np.array([s_min * u_min, s_min * u_max, s_max * u_min, s_max * u_max])
+    # fp32 product then bf16 rounding, both monotone: the corner extremes bound the set
+    p32 = corners.astype(np.float32).astype(np.float64)
+    codes = ordered(round_bf16(p32))
+    return int(codes.min()), int(codes.max())
+
+
+@dataclass
+class Report:
+    n: int = 0
+    max_ulp: int = 0
+    over_2ulp: int = 0
+    interval_pass: int = 0
+    interval_max_kappa: float = 0.0
+    failures: int = 0
+    bit_exact_frac: float = 1.0
+    mean_rel: float = 0.0
+    failure_idx: List[int] = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return self.failures == 0 and self.bit_exact_frac >= 0.999 and self.mean_rel <= 3e-3
+
+    def summary(self) -> str:
+        return (f"n={self.n} max_ulp={self.max_ulp} over2={self.over_2ulp} "
+                f"interval_pass={self.interval_pass} (max kappa {self.interval_max_kappa:.3g}) "
+                f"failures={self.failures} bit_exact={self.bit_exact_frac:.6f} "
+                f"mean_rel={self.mean_rel:.3e}")
+
+
+def compare(got: np.ndarray, ref: DualGemvResult, depth: int, k_len: int,
+            max_listed: int = 20) -> Report:
+    """Check device output bits ``got`` against the oracle's result ``ref``.
+
+    ``depth`` is the longest chain of fp32 additions the device sum can take for
+    one output (per-lane terms plus reduction levels); ``k_len`` is K.
+    """
+    got = np.asarray(got, dtype=np.uint16).ravel()
+    want = np.asarray(ref.out, dtype=np.uint16).ravel()
+    if got.shape != want.shape:
+        raise ValueError(f"size mismatch {got.shape} vs {want.shape}")
+    rep = Report(n=int(got.size))
+    if got.size == 0:
+        return rep
+    d = ulp_distance(got, want)
+    rep.max_ulp = int(d.max())
+    rep.bit_exact_frac = float(np.mean((got == want) | (is_nan_bits(got) & is_nan_bits(want))))
+    w = bf16_to_f64(want)
+    g = bf16_to_f64(got)
+    nz = (w != 0) & np.isfinite(w) & np.isfinite(g)
+    rep.mean_rel = float(np.mean(np.abs(g[nz] - w[nz]) / np.abs(w[nz]))) if nz.any() else 0.0
+    bad = np.nonzero(d > 2)[0]
+    rep.over_2ulp = int(bad.size)
+    G, U = np.asarray(ref.gate_pre).ravel(), np.asarray(ref.up_pre).ravel()
+    Ga, Ua = np.asarray(ref.gate_abs).ravel(), np.asarray(ref.up_abs).ravel()
+    for i in bad:
+        kappa = max(Ga[i] / abs(G[i]) if G[i] != 0 else np.inf,
+                    Ua[i] / abs(U[i]) if U[i] != 0 else np.inf)
+        o = int(ordered(got[i:i + 1])[0])
+        ok = False
+        if kappa >= 1e4 and not is_nan_bits(got[i:i + 1])[0]:
+            lo, hi = admissible_out_range(float(G[i]), float(U[i]), float(Ga[i]), float(Ua[i]),
+                                          depth, k_len)
+            ok = lo - 2 <= o <= hi + 2
+        if ok:
+            rep.interval_pass += 1
+            rep.interval_max_kappa = max(rep.interval_max_kappa, float(kappa))
+        else:
+            rep.failures += 1
+            if len(rep.failure_idx) < max_listed:
+                rep.failure_idx.append(int(i))
+    return rep
+
+
+def compare_strict_bits(got: np.ndarray, want: np.ndarray) -> Optional[np.ndarray]:
+    """Indices where two bf16 bit arrays differ (NaN matches NaN); None when identical."""
+    got = np.asarray(got, dtype=np.uint16).ravel()
+    want = np.asarray(want, dtype=np.uint16).ravel()
+    diff = (got != want) & ~(is_nan_bits(got) & is_nan_bits(want))
+    idx = np.nonzero(diff)[0]
+    return idx if idx.size else None
