@@ -1,0 +1,189 @@
+"""Python face of the C ABI in include/glu_gemv.h (argument marshalling only).
+
+Every step of the projection runs in the HIP kernels of ``libglu_gemv.so``;
+this module checks tensors, passes their device pointers and torch's current
+HIP stream, and turns a non-OK status into an exception.  If the library is
+missing or cannot be loaded, calls raise: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads torch's HIP runtime first, so the library binds to the same one
+
+from . import build as _build
+
+LIBRARY_PATH = _build.LIBRARY
+
+# enum values of include/glu_gemv.h
+GLU_OK = 0
+GLU_ERR_UNSUPPORTED = 6
+KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC = range(5)
+KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
+                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic"}
+
+EXPORTED_SYMBOLS = (
+    "glu_dual_gemv",
+    "glu_status_string",
+    "glu_last_hip_error",
+    "glu_version",
+    "glu_dual_gemv_plan",
+    "glu_dual_gemv_tuned",
+    "glu_dual_gemv_plan_tuned",
+)
+
+
+class GluError(RuntimeError):
+    """A non-OK glu_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("m_per_launch", ctypes.c_int), ("launches", ctypes.c_int),
+                ("grid", ctypes.c_int), ("block", ctypes.c_int), ("accum_depth", ctypes.c_int)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
+        return d
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("rows_per_wave", ctypes.c_int), ("waves_per_block", ctypes.c_int),
+                ("grid", ctypes.c_int), ("mfma_segments", ctypes.c_int)]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIBRARY_PATH):
+        raise RuntimeError(f"HIP library {LIBRARY_PATH} is not built; run __graft_entry__.build() "
+                           "(or python -m glu_mlp_gemv_amd.build)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    u16p, i64, vp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
+    lib.glu_dual_gemv.argtypes = [u16p, u16p, u16p, u16p, i64, i64, i64, vp]
+    lib.glu_dual_gemv.restype = ctypes.c_int
+    lib.glu_dual_gemv_tuned.argtypes = [u16p, u16p, u16p, u16p, i64, i64, i64, vp, ctypes.POINTER(Tuning)]
+    lib.glu_dual_gemv_tuned.restype = ctypes.c_int
+    lib.glu_status_string.argtypes = [ctypes.c_int]
+    lib.glu_status_string.restype = ctypes.c_char_p
+    lib.glu_last_hip_error.argtypes = []
+    lib.glu_last_hip_error.restype = ctypes.c_int
+    lib.glu_version.argtypes = []
+    lib.glu_version.restype = ctypes.c_int
+    lib.glu_dual_gemv_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Plan)]
+    lib.glu_dual_gemv_plan.restype = ctypes.c_int
+    lib.glu_dual_gemv_plan_tuned.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning),
+                                             ctypes.POINTER(Plan)]
+    lib.glu_dual_gemv_plan_tuned.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().glu_status_string(int(status)).decode()
+
+
+def _raise_for(status: int):
+    if status != GLU_OK:
+        msg = status_string(status)
+        hip = library().glu_last_hip_error()
+        if hip:
+            msg += f" (hipError {hip})"
+        raise GluError(status, msg)
+
+
+def make_tuning(**kw) -> Tuning:
+    t = Tuning()
+    for k, v in kw.items():
+        if not hasattr(t, k):
+            raise TypeError(f"unknown tuning field {k}")
+        setattr(t, k, int(v))
+    return t
+
+
+def plan(M: int, N: int, K: int, aligned16: bool = True, tuning: Optional[Tuning] = None) -> dict:
+    """The launch the library would make for a shape (host only, no GPU needed)."""
+    p = Plan()
+    lib = library()
+    if tuning is None:
+        st = lib.glu_dual_gemv_plan(M, N, K, int(aligned16), ctypes.byref(p))
+    else:
+        st = lib.glu_dual_gemv_plan_tuned(M, N, K, int(aligned16), ctypes.byref(tuning), ctypes.byref(p))
+    _raise_for(st)
+    return p.as_dict()
+
+
+def _check(name: str, t: torch.Tensor, ndims):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dim() not in ndims:
+        raise ValueError(f"{name} must have {' or '.join(map(str, ndims))} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def dual_gemv(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor,
+              out: Optional[torch.Tensor] = None, tuning: Optional[Tuning] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """out = bf16(bf16(silu(bf16(hidden @ gate_w.T))) * bf16(hidden @ up_w.T)).
+
+    hidden [M, K] (or [K], then the result is [N]), gate_w and up_w [N, K], all
+    bf16, contiguous, on one GPU.  ``out`` [M, N] (or [N]) is written in place if
+    given.  Runs asynchronously on ``stream`` (default: torch's current stream).
+    """
+    _check("hidden", hidden, (1, 2))
+    _check("gate_w", gate_w, (2,))
+    _check("up_w", up_w, (2,))
+    vec = hidden.dim() == 1
+    M = 1 if vec else hidden.shape[0]
+    K = hidden.shape[-1]
+    N = gate_w.shape[0]
+    if tuple(gate_w.shape) != (N, K) or tuple(up_w.shape) != (N, K):
+        raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, gate_w {tuple(gate_w.shape)}, "
+                         f"up_w {tuple(up_w.shape)}")
+    dev = hidden.device
+    if gate_w.device != dev or up_w.device != dev:
+        raise ValueError("hidden, gate_w and up_w must be on the same device")
+    want = (N,) if vec else (M, N)
+    if out is None:
+        out = torch.empty(want, dtype=torch.bfloat16, device=dev)
+    else:
+        _check("out", out, (len(want),))
+        if tuple(out.shape) != want or out.device != dev:
+            raise ValueError(f"out must be {want} on {dev}, got {tuple(out.shape)} on {out.device}")
+    lib = library()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        if tuning is None:
+            st = lib.glu_dual_gemv(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(), out.data_ptr(),
+                                   M, N, K, s.cuda_stream)
+        else:
+            st = lib.glu_dual_gemv_tuned(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(), out.data_ptr(),
+                                         M, N, K, s.cuda_stream, ctypes.byref(tuning))
+    _raise_for(st)
+    return out
+
+
+def dual_gemv_raw(hidden_ptr: int, gate_ptr: int, up_ptr: int, out_ptr: int, M: int, N: int, K: int,
+                  stream_handle: int = 0, tuning: Optional[Tuning] = None) -> int:
+    """The C call on raw device addresses; returns the glu_status (used by boundary tests)."""
+    lib = library()
+    if tuning is None:
+        return lib.glu_dual_gemv(hidden_ptr, gate_ptr, up_ptr, out_ptr, M, N, K, stream_handle)
+    return lib.glu_dual_gemv_tuned(hidden_ptr, gate_ptr, up_ptr, out_ptr, M, N, K, stream_handle,
+                                   ctypes.byref(tuning))

@@ -1,0 +1,305 @@
+// C ABI of the dual-weight GLU projection: argument validation, the choice of
+// kernel by M (DeepSpeed PR #8602, comment "Plan B: Dual-Weight GEMV": the
+// DualWeightGluGEMV forward sends a 1-D hidden to the custom kernel and a
+// batch elsewhere; the later dispatcher routes by batch size), and launch.
+// Validation happens before any HIP call; nothing is allocated or cached.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/glu_gemv.h"
+#include "../../include/glu_gemv_tuning.h"
+#include "glu_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = 0x7fffffff;    // N and K index rows and columns in 32 bits
+constexpr int64_t kMaxFastK = 0x7fffffff;  // the MFMA kernel takes any K % 8 == 0
+constexpr int64_t kMaxValuK = 8192;        // VALU: at most 16 chunks per lane per row
+constexpr int64_t kValuMaxDefaultK = 4096;  // longer rows stream faster through the MFMA kernel
+constexpr int kCUs = 256;                  // MI355X compute units
+constexpr int kValuDefaultWaves = 4;       // waves per workgroup
+constexpr int kValuWavesPerCU = 3;         // persistent waves per CU the grid aims for
+constexpr int kMfmaDefaultWaves = 4;
+constexpr int kMfmaWavesPerCU = 4;
+constexpr int kMfmaSlice = 32;
+
+bool mul_overflows(int64_t a, int64_t b, int64_t limit)
+{
+    return a != 0 && b > limit / a;
+}
+
+struct Launch {
+    int kernel = GLU_KERNEL_NONE;
+    int m_per_launch = 0;
+    int launches = 0;
+    glu::ValuConfig valu{};
+    glu::MfmaConfig mfma{};
+    int generic_grid = 0;
+    int accum_depth = 0;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Persistent grid: about `target` waves in total, each owning the same number of
+// work units to within one.
+int64_t balanced_waves(int64_t units, int64_t target)
+{
+    const int64_t per = ceil_div(units, target < 1 ? 1 : target);
+    return ceil_div(units, per);
+}
+
+glu_status plan_valu(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
+{
+    if (M > glu::kValuMaxM || K > kMaxValuK) return GLU_ERR_UNSUPPORTED;
+    glu::ValuConfig c{};
+    const int64_t nchunks = K / 8;
+    const int64_t cpl = ceil_div(nchunks, glu::kWave);
+    c.NB = cpl <= 8 ? 1 : 2;
+    c.U = (int)ceil_div(cpl, c.NB);
+    c.ragged = (int64_t)c.NB * c.U * glu::kWave != nchunks;
+    c.R = (t && t->rows_per_wave) ? t->rows_per_wave : 1;
+    const int waves = (t && t->waves_per_block) ? t->waves_per_block : kValuDefaultWaves;
+    if (waves < 1 || waves * glu::kWave > glu::kValuMaxThreads) return GLU_ERR_UNSUPPORTED;
+    c.block = waves * glu::kWave;
+    // rows of hidden per launch: all of them, unless staging in LDS needs slices
+    int64_t m_pl = M;
+    if (glu::valu_hidden_in_lds((int)M, c.U, c.NB)) {
+        const int64_t m_fit = glu::kLdsBudget / (2 * K);
+        m_pl = M < m_fit ? M : m_fit;
+    }
+    const int64_t groups = ceil_div(N, c.R);
+    int64_t grid;
+    if (t && t->grid > 0) {
+        grid = t->grid;
+    } else {
+        grid = ceil_div(balanced_waves(groups, (int64_t)kCUs * kValuWavesPerCU), waves);
+    }
+    c.grid = (int)(grid < 1 ? 1 : grid);
+    c.M = (int)m_pl;
+    if (!glu::valu_supported(c)) return GLU_ERR_UNSUPPORTED;
+    glu::ValuConfig last = c;  // the last slice may be narrower: it must be instantiated too
+    last.M = (int)(M - (ceil_div(M, m_pl) - 1) * m_pl);
+    if (!glu::valu_supported(last)) return GLU_ERR_UNSUPPORTED;
+    L->kernel = GLU_KERNEL_VALU;
+    L->valu = c;
+    L->m_per_launch = (int)m_pl;
+    L->launches = (int)ceil_div(M, m_pl);
+    L->accum_depth = 8 * c.U * c.NB + glu::kWaveSumDepth;
+    return GLU_OK;
+}
+
+// Segments per stage: the largest of 5, 4, 2 that divides the segment count (no
+// ragged tail) and keeps the stage's registers in budget as hidden tiles grow.
+int default_segments(int64_t nsegs, int mt4, bool hidden_lds)
+{
+    const int cap = !hidden_lds ? 2 : (mt4 <= 2 ? 5 : (mt4 <= 4 ? 4 : 2));
+    for (int u : {5, 4, 2}) {
+        if (u <= cap && nsegs % u == 0) return u;
+    }
+    return cap < 4 ? cap : 4;
+}
+
+glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
+{
+    glu::MfmaConfig c{};
+    const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
+    c.MT4 = (int)((m_pl + 3) / 4);
+    const int64_t nchunks = K / 8;
+    const int64_t nsegs = ceil_div(nchunks, 16);
+    c.hidden_lds = m_pl * K * 2 <= glu::kLdsBudget;
+    c.U = (t && t->mfma_segments) ? t->mfma_segments : default_segments(nsegs, c.MT4, c.hidden_lds);
+    if (c.U < 1) return GLU_ERR_UNSUPPORTED;
+    c.nsg = (int)ceil_div(nsegs, c.U);
+    c.ragged = (int64_t)c.nsg * c.U * 16 != nchunks;
+    const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
+    if (waves < 1 || waves * glu::kWave > glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
+    c.block = waves * glu::kWave;
+    const int64_t groups = ceil_div(N, 4);
+    int64_t grid;
+    if (t && t->grid > 0) {
+        grid = t->grid;
+    } else {
+        grid = ceil_div(balanced_waves(groups, (int64_t)kCUs * kMfmaWavesPerCU), waves);
+    }
+    c.grid = (int)(grid < 1 ? 1 : grid);
+    if (!glu::mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
+    L->kernel = GLU_KERNEL_MFMA;
+    L->mfma = c;
+    L->m_per_launch = (int)m_pl;
+    L->launches = (int)ceil_div(M, m_pl);
+    // per output lane: one MFMA per segment, each adding a 32-product block
+    // (a summation tree of depth 5) to the accumulator, then two quad additions;
+    // the matrix core's internal rounding is not specified, so every step is
+    // counted at twice the fp32 unit roundoff (a truncating adder)
+    L->accum_depth = (int)(2 * (nsegs + 5 + 2));
+    return GLU_OK;
+}
+
+glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const glu_tuning* t, Launch* L)
+{
+    if (M < 0 || N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return GLU_ERR_BAD_SHAPE;
+    const int64_t lim = INT64_MAX / 2;  // element counts must also fit as byte counts
+    if (mul_overflows(M, K, lim) || mul_overflows(N, K, lim) || mul_overflows(M, N, lim)) {
+        return GLU_ERR_BAD_SHAPE;
+    }
+    *L = Launch{};
+    if (M == 0 || N == 0) return GLU_OK;
+    if (K == 0) {
+        L->kernel = GLU_KERNEL_ZERO;
+        L->m_per_launch = (int)(M > kMaxDim ? kMaxDim : M);
+        L->launches = 1;
+        return GLU_OK;
+    }
+    const int forced = t ? t->kernel : 0;
+    const bool fast = aligned16 && (K % 8 == 0) && K <= kMaxFastK;
+    if (forced != 0 && forced != GLU_KERNEL_GENERIC && !fast) return GLU_ERR_UNSUPPORTED;
+    if (forced == GLU_KERNEL_VALU) return plan_valu(M, N, K, t, L);
+    if (forced == GLU_KERNEL_MFMA) return plan_mfma(M, N, K, t, L);
+    if (forced == 0 && fast) {
+        if (M == 1 && K <= kValuMaxDefaultK) return plan_valu(M, N, K, t, L);
+        return plan_mfma(M, N, K, t, L);
+    }
+    if (forced != 0 && forced != GLU_KERNEL_GENERIC) return GLU_ERR_UNSUPPORTED;
+    L->kernel = GLU_KERNEL_GENERIC;
+    L->m_per_launch = (int)(M < 8 ? M : 8);
+    L->launches = (int)ceil_div(M, L->m_per_launch);
+    L->generic_grid = (int)ceil_div(N, 4);
+    L->accum_depth = (int)ceil_div(K, glu::kWave) + glu::kWaveSumDepth;
+    return GLU_OK;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
+{
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+glu_status fail_launch(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return GLU_ERR_LAUNCH;
+}
+
+glu_status run(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out,
+               int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* t)
+{
+    if (M < 0 || N < 0 || K < 0) return GLU_ERR_BAD_SHAPE;
+    Launch L;
+    // shape errors first, independent of the pointers
+    glu_status st = plan_launch(M, N, K, true, nullptr, &L);
+    if (st != GLU_OK) return st;
+    if (M == 0 || N == 0) return GLU_OK;
+    if (!out || (K > 0 && (!hidden || !gate_w || !up_w))) return GLU_ERR_NULL_POINTER;
+    const uintptr_t odd = ((uintptr_t)out | (uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w) & 1u;
+    if (odd) return GLU_ERR_MISALIGNED;
+    const int64_t out_bytes = M * N * 2;
+    if (K > 0 && (overlaps(out, out_bytes, hidden, M * K * 2) || overlaps(out, out_bytes, gate_w, N * K * 2) ||
+                  overlaps(out, out_bytes, up_w, N * K * 2))) {
+        return GLU_ERR_ALIASING;
+    }
+    const bool aligned16 = (((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w) & 15u) == 0;
+    st = plan_launch(M, N, K, aligned16, t, &L);
+    if (st != GLU_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    switch (L.kernel) {
+    case GLU_KERNEL_ZERO:
+        e = glu::zero_launch(out, M, N, s);
+        break;
+    case GLU_KERNEL_GENERIC:
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
+            const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
+            e = glu::generic_launch(mc, hidden + m0 * K, gate_w, up_w, out + m0 * N, N, K, N, s);
+        }
+        break;
+    case GLU_KERNEL_VALU:
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
+            glu::ValuConfig c = L.valu;
+            c.M = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
+            e = glu::valu_launch(c, hidden + m0 * K, gate_w, up_w, out + m0 * N, N, K, N, s);
+        }
+        break;
+    case GLU_KERNEL_MFMA:
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
+            const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
+            e = glu::mfma_launch(L.mfma, mc, hidden + m0 * K, gate_w, up_w, out + m0 * N, N, K, N, s);
+        }
+        break;
+    default:
+        return GLU_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? GLU_OK : fail_launch(e);
+}
+
+void fill_plan(const Launch& L, glu_plan* p)
+{
+    p->kernel = L.kernel;
+    p->m_per_launch = L.m_per_launch;
+    p->launches = L.launches;
+    p->accum_depth = L.accum_depth;
+    switch (L.kernel) {
+    case GLU_KERNEL_VALU: p->grid = L.valu.grid; p->block = L.valu.block; break;
+    case GLU_KERNEL_MFMA: p->grid = L.mfma.grid; p->block = L.mfma.block; break;
+    case GLU_KERNEL_GENERIC: p->grid = L.generic_grid; p->block = 4 * glu::kWave; break;
+    case GLU_KERNEL_ZERO: p->grid = 0; p->block = 256; break;
+    default: p->grid = 0; p->block = 0; break;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+glu_status glu_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream)
+{
+    return run(hidden, gate_w, up_w, out, M, N, K, stream, nullptr);
+}
+
+glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                               uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream,
+                               const glu_tuning* tuning)
+{
+    return run(hidden, gate_w, up_w, out, M, N, K, stream, tuning);
+}
+
+glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan)
+{
+    return glu_dual_gemv_plan_tuned(M, N, K, aligned16, nullptr, plan);
+}
+
+glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned16,
+                                    const glu_tuning* tuning, glu_plan* plan)
+{
+    if (!plan) return GLU_ERR_NULL_POINTER;
+    Launch L;
+    const glu_status st = plan_launch(M, N, K, aligned16 != 0, tuning, &L);
+    if (st != GLU_OK) return st;
+    fill_plan(L, plan);
+    return GLU_OK;
+}
+
+const char* glu_status_string(int status)
+{
+    switch (status) {
+    case GLU_OK: return "GLU_OK";
+    case GLU_ERR_NULL_POINTER: return "GLU_ERR_NULL_POINTER: a non-empty array is NULL";
+    case GLU_ERR_BAD_SHAPE: return "GLU_ERR_BAD_SHAPE: negative or oversized M, N or K";
+    case GLU_ERR_MISALIGNED: return "GLU_ERR_MISALIGNED: a pointer is not 2-byte aligned";
+    case GLU_ERR_ALIASING: return "GLU_ERR_ALIASING: out overlaps an input";
+    case GLU_ERR_LAUNCH: return "GLU_ERR_LAUNCH: the HIP kernel launch failed";
+    case GLU_ERR_UNSUPPORTED: return "GLU_ERR_UNSUPPORTED: the requested launch shape is not available";
+    default: return "unknown glu_status";
+    }
+}
+
+int glu_last_hip_error(void) { return g_last_hip_error; }
+
+int glu_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI (glu_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace glu {
+
+constexpr int kWave = 64;
+constexpr int kWaveSumDepth = 6;  // fp32 addition levels of the wave64 butterfly
+constexpr int kValuMaxM = 8;
+constexpr int kValuMaxThreads = 512;
+constexpr int kLdsBudget = 64 * 1024;  // dynamic LDS per workgroup, bytes
+constexpr int kMfmaMaxThreads = 256;  // 4 waves: the compiler may use AGPRs for the accumulators
+
+struct ValuConfig {
+    int M;        // rows of hidden in this launch (1..8)
+    int R;        // output rows per wave per group
+    int U;        // 16-byte chunks per lane per stage
+    int NB;       // stages per row group (1 or 2): NB * U * 64 >= K / 8
+    bool ragged;  // NB * U * 64 > K / 8: clamp and zero the excess chunks
+    int grid;     // workgroups (persistent)
+    int block;    // threads per workgroup (multiple of 64)
+};
+
+struct MfmaConfig {
+    int MT4;          // hidden-row tiles of 4 (M <= 4 * MT4 <= 32)
+    int U;            // 128-element K segments per pipeline stage
+    int nsg;          // stages per group of 4 weight rows: nsg * U * 16 >= K / 8
+    bool ragged;      // nsg * U * 16 > K / 8: clamp and zero the excess chunks
+    bool hidden_lds;  // hidden staged in LDS (M * K * 2 <= 64 KiB), else read from L2
+    int grid;         // workgroups (persistent)
+    int block;        // threads per workgroup (multiple of 64)
+};
+
+// per-M instantiation tables (glu_valu_m<M>.hip)
+using ValuFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int64_t);
+ValuFn valu_pick_1(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_2(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_3(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_4(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_5(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_6(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_7(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_8(int R, int U, int NB, bool ragged);
+
+// whether hidden is staged in LDS (else held in registers) for a VALU configuration
+constexpr bool valu_hidden_in_lds(int M, int U, int NB) { return M * U * NB > 16; }
+
+bool valu_supported(const ValuConfig& c);
+hipError_t valu_launch(const ValuConfig& c, const uint16_t* hidden, const uint16_t* gate_w,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       hipStream_t stream);
+
+bool mfma_supported(const MfmaConfig& c);
+hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       hipStream_t stream);
+
+// Any alignment (2-byte), any K >= 1; M <= 8 per launch.
+hipError_t generic_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                          uint16_t* out, int64_t N, int64_t K, int64_t ldo, hipStream_t stream);
+
+// out[m, j] = +0 for m < M, j < N (K == 0).
+hipError_t zero_launch(uint16_t* out, int64_t M, int64_t N, hipStream_t stream);
+
+}  // namespace glu

@@ -1,0 +1,259 @@
+// MFMA kernel for the dual-weight GLU projection at batch 2 <= M <= 32.
+//
+// The pages route small batches to a tensor-core fused GLU kernel and larger
+// ones to a library GEMM (DeepSpeed PR #9057, commit notes on the Ampere GLU
+// routing and the WMMA fused kernel kept for small M).  On gfx950 the product
+// stays bound by streaming the weights from HBM, and how the weights are read
+// decides the speed: a wave has to stream whole weight rows, neighbouring
+// waves neighbouring rows, in full 128-byte lines.  The usual MFMA operand
+// layout (16 weight rows x 64 bytes per load) breaks both rules, so this
+// kernel feeds v_mfma_f32_16x16x32_bf16 a block-diagonal problem instead:
+//
+//   A[i][k] = W[4g + rho][s*128 + 32*beta + k]      i = 4*rho + beta, k < 32
+//   B[k][n] = h[4t + mu][s*128 + 32*beta' + k]      n = 4*mu + beta'
+//   D[i][n] = sum over k of A[i][k] * B[k][n]
+//
+// For a 128-element segment s of 4 weight rows and 4 hidden rows, the
+// diagonal blocks beta == beta' of D are the four 32-element partial dots of
+// every (weight row, hidden row) pair; the other 3/4 of D is discarded.  Lane
+// l supplies A row l%16 and B column l%16 as the 8 bf16 at k = 8*(l/16), so
+// one 16-byte load per lane reads 4 weight rows x 256 contiguous bytes, and
+// accumulating D over all segments of K sums every block.  D lane l holds
+// D[4*(l/16) + e][l%16]: the useful entry is e = l%4, and the four lanes of a
+// quad hold the four blocks of one pair (weight row 4g + l/16, hidden row
+// 4t + (l%16)/4), so two DPP additions finish the dot products.
+//
+// A wave owns groups of 4 weight rows (persistent: groups w, w+W, ...) and
+// streams a group in stages of U segments; the loads of stage s+1 are issued
+// before the MFMAs of stage s.  hidden [M,K] is staged in LDS when it fits in
+// 64 KiB, else read from L2 with each stage's weights.  MFMA work is 1/4 useful, which still
+// leaves the matrix cores far from busy at M <= 32.
+#include <type_traits>
+
+#include "glu_device.h"
+#include "glu_launch.h"
+
+namespace glu {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// MT4: hidden-row tiles of 4 (M <= 4*MT4); U: 128-element segments per stage;
+// nsg: stages per group (nsg * U * 16 >= K/8, equality unless RAGGED).
+// Dynamic LDS: M * K * 2 bytes when HLDS.
+template <int MT4, int U, bool HLDS, bool RAGGED>
+__global__ void __launch_bounds__(kMfmaMaxThreads)
+mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+            const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
+            int M, int N, int K, int64_t ldo, int nsg)
+{
+    extern __shared__ u32x4_t h_lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int wave_id = blockIdx.x * wpb + threadIdx.x / kWave;
+    const int nwaves = gridDim.x * wpb;
+    const int nchunks = K >> 3;
+    const int i16 = lane & 15;
+    const int rho_a = i16 >> 2;              // weight row of this lane's A data
+    const int cseg = (i16 & 3) * 4 + (lane >> 4);  // 16-byte chunk within a 256-byte segment
+    const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
+
+    if constexpr (HLDS) {
+        for (int i = threadIdx.x; i < M * nchunks; i += blockDim.x) {
+            h_lds[i] = h4[i];
+        }
+        __syncthreads();
+    }
+
+    const int ngroups = (N + 3) / 4;
+    if (wave_id >= ngroups) return;  // no barrier follows
+    const int my_groups = (ngroups - 1 - wave_id) / nwaves + 1;
+    const int nstages = my_groups * nsg;
+
+    // hidden rows of this lane's B data, one per tile (rows past M repeat row M-1, never stored)
+    int hrow[MT4];
+#pragma unroll
+    for (int t = 0; t < MT4; ++t) hrow[t] = min(4 * t + rho_a, M - 1);
+
+    constexpr int BT = HLDS ? 1 : MT4;  // hidden operands carried with a stage (L2 path only)
+    constexpr int BU = HLDS ? 1 : U;
+
+    auto load = [&](int s, u32x4_t (&A)[2][U], u32x4_t (&Bq)[BT][BU]) {
+        const int gi = s / nsg;
+        const int sb = s - gi * nsg;
+        const int g = wave_id + gi * nwaves;
+        const int row = min(4 * g + rho_a, N - 1);  // rows past N re-read row N-1, never stored
+        const u32x4_t* gp = reinterpret_cast<const u32x4_t*>(gate_w + (int64_t)row * K);
+        const u32x4_t* up = reinterpret_cast<const u32x4_t*>(up_w + (int64_t)row * K);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int c = (sb * U + u) * 16 + cseg;
+            if (RAGGED) c = min(c, nchunks - 1);
+            A[0][u] = __builtin_nontemporal_load(gp + c);
+            A[1][u] = __builtin_nontemporal_load(up + c);
+        }
+        if constexpr (!HLDS) {
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    int c = (sb * U + u) * 16 + cseg;
+                    if (RAGGED) c = min(c, nchunks - 1);
+                    Bq[t][u] = h4[(int64_t)hrow[t] * nchunks + c];
+                }
+            }
+        }
+    };
+
+    f32x4_t acc[MT4][2];
+
+    auto finish_group = [&](int g) {
+        // useful entry e = lane % 4, then the quad sum over the four blocks
+        const int e = lane & 3;
+        float res[2][(MT4 + 3) / 4];
+#pragma unroll
+        for (int t = 0; t < MT4; ++t) {
+#pragma unroll
+            for (int gu = 0; gu < 2; ++gu) {
+                const f32x4_t d = acc[t][gu];
+                float v = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
+                v = dpp_add<0xB1>(v);  // lane ^ 1
+                v = dpp_add<0x4E>(v);  // lane ^ 2
+                if (e == (t & 3)) res[gu][t >> 2] = v;
+            }
+        }
+        // lane l keeps tiles t with t % 4 == l % 4: hidden row 4t + (l%16)/4, weight row 4g + l/16
+        const int row = 4 * g + (lane >> 4);
+#pragma unroll
+        for (int k = 0; k < (MT4 + 3) / 4; ++k) {
+            const int t = 4 * k + e;
+            const int m = 4 * t + ((lane & 15) >> 2);
+            if (t < MT4 && m < M && row < N) {
+                out[(int64_t)m * ldo + row] = glu_epilogue(res[0][k], res[1][k]);
+            }
+        }
+    };
+
+    auto compute = [&](int s, const u32x4_t (&A)[2][U], const u32x4_t (&Bq)[BT][BU]) {
+        const int gi = s / nsg;
+        const int sb = s - gi * nsg;
+        if (sb == 0) {
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+                acc[t][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                acc[t][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = (sb * U + u) * 16 + cseg;
+            const bool ok = !RAGGED || c < nchunks;
+            const int cc = RAGGED ? min(c, nchunks - 1) : c;
+            const u32x4_t ag = RAGGED ? (ok ? A[0][u] : z) : A[0][u];
+            const u32x4_t au = RAGGED ? (ok ? A[1][u] : z) : A[1][u];
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+                u32x4_t b;
+                if constexpr (HLDS) {
+                    b = h_lds[hrow[t] * nchunks + cc];
+                } else {
+                    b = Bq[t][u];
+                }
+                if constexpr (RAGGED) b = ok ? b : z;
+                acc[t][0] = mfma16(ag, b, acc[t][0]);
+                acc[t][1] = mfma16(au, b, acc[t][1]);
+            }
+        }
+        if (sb == nsg - 1) finish_group(wave_id + gi * nwaves);
+    };
+
+    u32x4_t a0[2][U], a1[2][U], b0[BT][BU], b1[BT][BU];
+    load(0, a0, b0);
+    int s = 0;
+    while (true) {
+        if (s + 1 >= nstages) {
+            compute(s, a0, b0);
+            break;
+        }
+        load(s + 1, a1, b1);
+        compute(s, a0, b0);
+        ++s;
+        if (s + 1 >= nstages) {
+            compute(s, a1, b1);
+            break;
+        }
+        load(s + 1, a0, b0);
+        compute(s, a1, b1);
+        ++s;
+    }
+}
+
+namespace {
+
+using MfmaFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, int64_t, int);
+
+template <int MT4, bool HL, bool RG>
+MfmaFn pick_u(int U)
+{
+    switch (U) {
+    case 2: return mfma_kernel<MT4, 2, HL, RG>;
+    case 4: return mfma_kernel<MT4, 4, HL, RG>;
+    case 5: return mfma_kernel<MT4, 5, HL, RG>;
+    case 8: return mfma_kernel<MT4, 8, HL, RG>;
+    default: return nullptr;
+    }
+}
+
+template <int MT4>
+MfmaFn pick_flags(const MfmaConfig& c)
+{
+    if (c.hidden_lds) return c.ragged ? pick_u<MT4, true, true>(c.U) : pick_u<MT4, true, false>(c.U);
+    return c.ragged ? pick_u<MT4, false, true>(c.U) : pick_u<MT4, false, false>(c.U);
+}
+
+MfmaFn pick(const MfmaConfig& c)
+{
+    switch (c.MT4) {
+    case 1: return pick_flags<1>(c);
+    case 2: return pick_flags<2>(c);
+    case 3: return pick_flags<3>(c);
+    case 4: return pick_flags<4>(c);
+    case 5: return pick_flags<5>(c);
+    case 6: return pick_flags<6>(c);
+    case 7: return pick_flags<7>(c);
+    case 8: return pick_flags<8>(c);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+bool mfma_supported(const MfmaConfig& c)
+{
+    if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
+    return pick(c) != nullptr;
+}
+
+hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       hipStream_t stream)
+{
+    MfmaConfig cm = c;
+    cm.MT4 = (M + 3) / 4;
+    MfmaFn fn = pick(cm);
+    if (!fn || M < 1 || M > 4 * cm.MT4) return hipErrorInvalidValue;
+    const size_t lds = cm.hidden_lds ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
+    hipLaunchKernelGGL(fn, dim3(cm.grid), dim3(cm.block), lds, stream,
+                       hidden, gate_w, up_w, out, M, (int)N, (int)K, ldo, cm.nsg);
+    return hipGetLastError();
+}
+
+}  // namespace glu

@@ -1,0 +1,12 @@
+// Instantiations of the VALU GEMV (glu_valu.h) for M = 7 hidden rows.
+#include "glu_valu.h"
+
+namespace glu {
+
+ValuFn valu_pick_7(int R, int U, int NB, bool ragged)
+{
+    if (R == 1) return valu_pick_m<7, 1>(U, NB, ragged);
+    return nullptr;
+}
+
+}  // namespace glu

@@ -1,0 +1,111 @@
+/*
+ * glu_gemv.h -- C ABI of the dual-weight GLU projection for MI355X (gfx950).
+ *
+ * The operation (DeepSpeed PR #8602, "HybridEngineRollout graph capture +
+ * segment-KI for Qwen3.5 hybrid", comment "Plan B: Dual-Weight GEMV": the
+ * DualWeightGluGEMV forward and its kernel, which read gate.weight and
+ * up.weight directly instead of a concatenated copy; rounding per DeepSpeed
+ * PR #9057, "preserve HF precision boundaries in segKI kernels", section
+ * "Changes"):
+ *
+ *   G[m,j]   = sum_k hidden[m,k] * gate_w[j,k]        (fp32 accumulation)
+ *   U[m,j]   = sum_k hidden[m,k] * up_w[j,k]          (fp32 accumulation)
+ *   g = bf16(G), u = bf16(U)                          (round to nearest even)
+ *   s = bf16( g / (1 + exp(-g)) )                     (fp32 silu, IEEE steps)
+ *   out[m,j] = bf16( s * u )                          (fp32 product)
+ *
+ * Every array is dense and row-major; bf16 values travel as their raw 16-bit
+ * patterns (uint16_t), so this header needs no HIP or bf16 type:
+ *   hidden [M, K]   activations, one row per token
+ *   gate_w [N, K]   gate projection weight, nn.Linear layout [out, in]
+ *   up_w   [N, K]   up projection weight, same layout
+ *   out    [M, N]   result
+ *
+ * Ownership: the caller allocates all four buffers in device memory of the
+ * current HIP device and keeps them alive until the work on `stream` is
+ * done.  The library allocates nothing, copies nothing, concatenates
+ * nothing and caches nothing keyed on pointers: every call reads the weights
+ * as they are at execution time, so in-place weight updates are seen by the
+ * next call.
+ *
+ * Execution: asynchronous on `stream` (a hipStream_t; NULL is the null
+ * stream).  No host synchronisation, no allocation, a launch configuration
+ * fixed by (M, N, K) and the pointers' alignment: the call may be captured
+ * into a HIP graph.  Deterministic: identical inputs give bitwise-identical
+ * output on every call (no atomics, fixed reduction order).  Stateless and
+ * reentrant; concurrent calls on different streams are independent.
+ *
+ * Errors are returned, never thrown; arguments are validated before any HIP
+ * call, so an invalid call launches nothing.
+ */
+#ifndef GLU_GEMV_H
+#define GLU_GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum glu_status {
+    GLU_OK = 0,
+    GLU_ERR_NULL_POINTER = 1, /* a non-empty array was given as NULL */
+    GLU_ERR_BAD_SHAPE = 2,    /* M, N or K negative, or an element/byte count overflows int64 */
+    GLU_ERR_MISALIGNED = 3,   /* a pointer is not 2-byte aligned */
+    GLU_ERR_ALIASING = 4,     /* out overlaps hidden, gate_w or up_w */
+    GLU_ERR_LAUNCH = 5,       /* the HIP launch failed; see glu_last_hip_error() */
+    GLU_ERR_UNSUPPORTED = 6   /* a tuning override the library cannot serve (glu_gemv_tuning.h) */
+} glu_status;
+
+/*
+ * out = bf16(bf16(silu(bf16(hidden @ gate_w^T))) * bf16(hidden @ up_w^T)).
+ *
+ * M >= 0, N >= 0, K >= 0.  M == 0 or N == 0: nothing to do, GLU_OK, pointers
+ * unchecked.  K == 0: every output is +0 (the empty sums give silu(0) * 0).
+ * Fast path: hidden, gate_w and up_w 16-byte aligned and K a multiple of 8;
+ * any other 2-byte-aligned input takes a slower path with the same result
+ * contract.  M == 1 with K <= 4096 runs a VALU GEMV; other shapes run a
+ * block-diagonal MFMA kernel; M > 32 is processed in slices of 32 rows of
+ * hidden (one launch per slice, each streaming the weights again).
+ */
+glu_status glu_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* glu_status_string(int status);
+
+/* hipError_t of the most recent GLU_ERR_LAUNCH on the calling thread (0 if none). */
+int glu_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int glu_version(void);
+
+/*
+ * Which kernel glu_dual_gemv would launch for a shape, decided on the host
+ * alone (no HIP call; usable without a GPU).  `aligned16` states whether
+ * hidden, gate_w and up_w are all 16-byte aligned.
+ */
+typedef struct glu_plan {
+    int kernel;        /* GLU_KERNEL_* */
+    int m_per_launch;  /* rows of hidden one launch covers */
+    int launches;      /* launches one call makes */
+    int grid;          /* workgroups per launch */
+    int block;         /* threads per workgroup */
+    int accum_depth;   /* longest chain of fp32 additions behind one output */
+} glu_plan;
+
+enum {
+    GLU_KERNEL_NONE = 0,    /* M == 0 or N == 0 */
+    GLU_KERNEL_ZERO = 1,    /* K == 0: fill out with +0 */
+    GLU_KERNEL_VALU = 2,    /* M == 1, K <= 4096, fast path (any M <= 8 on request) */
+    GLU_KERNEL_MFMA = 3,    /* other fast-path shapes (slices of 32 rows of hidden) */
+    GLU_KERNEL_GENERIC = 4  /* unaligned or K % 8 != 0 */
+};
+
+glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLU_GEMV_H */

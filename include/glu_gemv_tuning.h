@@ -1,0 +1,42 @@
+/*
+ * glu_gemv_tuning.h -- launch-shape overrides of glu_dual_gemv, for
+ * benchmark sweeps and tests that pin a particular kernel.
+ *
+ * Same operation, arguments, ownership, execution and error contract as
+ * glu_dual_gemv (include/glu_gemv.h); `tuning` only changes how the work is
+ * laid out on the GPU, never the result contract.  A zero field keeps the
+ * default.  A combination the library was not built with, or a kernel that
+ * cannot serve the shape (GLU_KERNEL_VALU above M = 8, any fast kernel on
+ * unaligned input or K % 8 != 0), returns GLU_ERR_UNSUPPORTED and launches
+ * nothing.  tuning == NULL is glu_dual_gemv.
+ */
+#ifndef GLU_GEMV_TUNING_H
+#define GLU_GEMV_TUNING_H
+
+#include "glu_gemv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct glu_tuning {
+    int kernel;           /* 0 = automatic, else GLU_KERNEL_VALU / _MFMA / _GENERIC */
+    int rows_per_wave;    /* VALU: output rows per wave per group (1; 2 at M = 1) */
+    int waves_per_block;  /* VALU, MFMA: waves per workgroup (1..8) */
+    int grid;             /* VALU, MFMA: workgroups of the persistent grid */
+    int mfma_segments;    /* MFMA: 128-element K segments per pipeline stage (2, 4, 5, 8) */
+} glu_tuning;
+
+glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                               uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream,
+                               const glu_tuning* tuning);
+
+/* glu_dual_gemv_plan with overrides (host only, no HIP call). */
+glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned16,
+                                    const glu_tuning* tuning, glu_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLU_GEMV_TUNING_H */

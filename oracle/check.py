@@ -8,16 +8,22 @@ Tolerance (the parity bar for floating point):
 * mean relative error <= 0.3% over outputs whose oracle value is non-zero;
 * bit-exact fraction >= 99.9% (a single-rounding kernel also meets the first
   two bars, so this one is what pins the four bf16 roundings in the device
-  path).
+  path); on small outputs, where one near-tie already moves the fraction by
+  more than 0.1%, up to SMALL_SAMPLE_SLACK non-exact outputs also pass.
 
-An fp32 accumulation cannot hold 2 ULP where a dot product nearly cancels.
-An output that fails the strict check therefore passes only if it lies in
-its *admissible interval*: the oracle's epilogue applied over every gate and
-up pre-activation an fp32 sum of depth ``d`` can reach,
-``G +- gamma_d * sum|h*w|`` with ``gamma_d = d*2^-24 / (1 - d*2^-24)``
-(the order-independent error bound of a floating-point inner product), widened
-by 2 ULP.  Such outputs are counted and reported with their condition number
-``kappa = sum|h*w| / |sum h*w|``; one with kappa < 1e4 is never excused.
+No fp32 accumulation can hold 2 ULP on every output.  Where a dot product
+nearly cancels, its relative error is unbounded; and where G lies within the
+fp32 error of a bf16 rounding boundary, any summation order may round g (or u)
+to either neighbour, and silu(g)*u turns that one-ULP step into up to ~3 ULP
+of the output.  Both are outputs with several correct results.  An output
+that fails the strict check therefore passes only if it lies in its
+*admissible interval*: the oracle's epilogue applied over every gate and up
+pre-activation that an fp32 sum of depth ``d`` can reach,
+``G +- gamma_d * sum|h*w|`` with ``gamma_d = d*2^-24 / (1 - d*2^-24)`` (the
+order-independent error bound of a floating-point inner product), widened by
+2 ULP.  ``d`` counts rounding steps in units of 2^-24; a kernel whose adder
+may truncate states twice its chain length.  Such outputs are counted and
+reported with their condition number ``kappa = sum|h*w| / |sum h*w|``.
 """
 from __future__ import annotations
 
@@ -29,6 +35,7 @@ import numpy as np
 from . import DualGemvResult, round_bf16, silu_bf16
 
 U32 = 2.0 ** -24  # unit roundoff of fp32
+SMALL_SAMPLE_SLACK = 3  # non-bit-exact outputs always allowed (each still within the ULP bar)
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -97,20 +104,30 @@ class Report:
     over_2ulp: int = 0
     interval_pass: int = 0
     interval_max_kappa: float = 0.0
+    interval_min_kappa: float = float("inf")
     failures: int = 0
     bit_exact_frac: float = 1.0
     mean_rel: float = 0.0
     failure_idx: List[int] = field(default_factory=list)
+    failure_info: List[dict] = field(default_factory=list)
+
+    @property
+    def bit_exact_ok(self) -> bool:
+        inexact = round((1.0 - self.bit_exact_frac) * self.n)
+        return self.bit_exact_frac >= 0.999 or inexact <= SMALL_SAMPLE_SLACK
 
     @property
     def ok(self) -> bool:
-        return self.failures == 0 and self.bit_exact_frac >= 0.999 and self.mean_rel <= 3e-3
+        return self.failures == 0 and self.bit_exact_ok and self.mean_rel <= 3e-3
 
     def summary(self) -> str:
-        return (f"n={self.n} max_ulp={self.max_ulp} over2={self.over_2ulp} "
-                f"interval_pass={self.interval_pass} (max kappa {self.interval_max_kappa:.3g}) "
-                f"failures={self.failures} bit_exact={self.bit_exact_frac:.6f} "
-                f"mean_rel={self.mean_rel:.3e}")
+        s = (f"n={self.n} max_ulp={self.max_ulp} over2={self.over_2ulp} "
+             f"interval_pass={self.interval_pass} (kappa {self.interval_min_kappa:.3g}..{self.interval_max_kappa:.3g}) "
+             f"failures={self.failures} bit_exact={self.bit_exact_frac:.6f} "
+             f"mean_rel={self.mean_rel:.3e}")
+        if self.failure_info:
+            s += f" first failures: {self.failure_info[:3]}"
+        return s
 
 
 def compare(got: np.ndarray, ref: DualGemvResult, depth: int, k_len: int,
@@ -143,17 +160,25 @@ def compare(got: np.ndarray, ref: DualGemvResult, depth: int, k_len: int,
                     Ua[i] / abs(U[i]) if U[i] != 0 else np.inf)
         o = int(ordered(got[i:i + 1])[0])
         ok = False
-        if kappa >= 1e4 and not is_nan_bits(got[i:i + 1])[0]:
+        lo = hi = None
+        if not is_nan_bits(got[i:i + 1])[0]:
             lo, hi = admissible_out_range(float(G[i]), float(U[i]), float(Ga[i]), float(Ua[i]),
                                           depth, k_len)
             ok = lo - 2 <= o <= hi + 2
         if ok:
             rep.interval_pass += 1
             rep.interval_max_kappa = max(rep.interval_max_kappa, float(kappa))
+            rep.interval_min_kappa = min(rep.interval_min_kappa, float(kappa))
         else:
             rep.failures += 1
             if len(rep.failure_idx) < max_listed:
                 rep.failure_idx.append(int(i))
+                info = {"index": int(i), "got": f"{int(got[i]):#06x}", "want": f"{int(want[i]):#06x}",
+                        "ulp": int(d[i]), "kappa": float(kappa), "G": float(G[i]), "U": float(U[i]),
+                        "sum_abs_g": float(Ga[i]), "sum_abs_u": float(Ua[i])}
+                if lo is not None:
+                    info["interval"] = [lo, hi, o]
+                rep.failure_info.append(info)
     return rep
 
 

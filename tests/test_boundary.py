@@ -1,0 +1,158 @@
+"""The C ABI on the host: the library loads, exports what include/*.h declares,
+plans launches, and rejects bad arguments before any HIP call (CPU only)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from glu_mlp_gemv_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# status codes of include/glu_gemv.h
+OK, NULLP, SHAPE, ALIGN, ALIAS, LAUNCH, UNSUP = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIBRARY_PATH):
+        pytest.fail("libglu_gemv.so is not built (run __graft_entry__.build())")
+    return api.library()
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(glu_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "glu_dual_gemv" in names and len(names) >= 7
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(api.EXPORTED_SYMBOLS) == set(names)
+
+
+def test_version_and_strings(lib):
+    assert lib.glu_version() >= 100
+    for s in range(7):
+        assert api.status_string(s).startswith("GLU_")
+    assert api.status_string(99) == "unknown glu_status"
+    assert lib.glu_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("M,N,K,aligned,kernel,launches", [
+    (0, 10, 10, True, api.KERNEL_NONE, 0),
+    (3, 0, 10, True, api.KERNEL_NONE, 0),
+    (3, 10, 0, True, api.KERNEL_ZERO, 1),
+    (1, 9216, 2560, True, api.KERNEL_VALU, 1),
+    (8, 12288, 4096, True, api.KERNEL_MFMA, 1),
+    (2, 12288, 8192, True, api.KERNEL_MFMA, 1),
+    (1, 12288, 4096, True, api.KERNEL_VALU, 1),
+    (1, 12288, 8192, True, api.KERNEL_MFMA, 1),
+    (1, 12288, 8200, True, api.KERNEL_MFMA, 1),      # past the VALU path's 16 chunks per lane
+    (9, 100, 512, True, api.KERNEL_MFMA, 1),
+    (32, 17408, 5120, True, api.KERNEL_MFMA, 1),
+    (70, 17408, 5120, True, api.KERNEL_MFMA, 3),     # slices of 32 rows
+    (1, 100, 2560, False, api.KERNEL_GENERIC, 1),    # unaligned
+    (1, 100, 1003, True, api.KERNEL_GENERIC, 1),     # K % 8 != 0
+    (20, 100, 1003, True, api.KERNEL_GENERIC, 3),
+    (1, 100, 65536, True, api.KERNEL_MFMA, 1),       # K past the VALU path's 16 chunks per lane
+    (4, 100, 9000, True, api.KERNEL_MFMA, 1),
+])
+def test_plan(lib, M, N, K, aligned, kernel, launches):
+    p = api.plan(M, N, K, aligned)
+    assert p["kernel"] == kernel, p
+    assert p["launches"] == launches, p
+    if kernel in (api.KERNEL_VALU, api.KERNEL_MFMA, api.KERNEL_GENERIC):
+        assert p["grid"] > 0 and p["block"] % 64 == 0 and p["accum_depth"] >= 1
+
+
+def test_plan_accum_depth_valu(lib):
+    p = api.plan(1, 9216, 2560, True)
+    # 2560 / 8 = 320 chunks over 64 lanes = 5 chunks of 8 terms, plus 6 butterfly levels
+    assert p["accum_depth"] == 5 * 8 + 6
+
+
+@pytest.mark.parametrize("M,N,K", [(-1, 1, 1), (1, -1, 1), (1, 1, -1), (1, 1 << 31, 8), (1, 8, 1 << 31),
+                                   (1 << 40, 1, 1 << 40), (1 << 62, 1 << 2, 1)])
+def test_plan_rejects_bad_shapes(lib, M, N, K):
+    p = api.Plan()
+    assert lib.glu_dual_gemv_plan(M, N, K, 1, ctypes.byref(p)) == SHAPE
+
+
+def test_plan_valu_hidden_slices(lib):
+    # hidden staged in LDS: slices of 64 KiB / (2 K) rows
+    t = api.make_tuning(kernel=api.KERNEL_VALU)
+    p = api.plan(8, 12288, 8192, True, t)
+    assert p["kernel"] == api.KERNEL_VALU and p["launches"] == 2 and p["m_per_launch"] == 4
+
+
+def test_plan_tuning_overrides(lib):
+    t = api.make_tuning(kernel=api.KERNEL_MFMA)
+    assert api.plan(4, 1000, 1024, True, t)["kernel"] == api.KERNEL_MFMA
+    t = api.make_tuning(kernel=api.KERNEL_GENERIC)
+    assert api.plan(4, 1000, 1024, True, t)["kernel"] == api.KERNEL_GENERIC
+    p = api.Plan()
+    t = api.make_tuning(kernel=api.KERNEL_VALU)
+    assert lib.glu_dual_gemv_plan_tuned(9, 1000, 1024, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP
+    t = api.make_tuning(kernel=api.KERNEL_VALU)
+    assert lib.glu_dual_gemv_plan_tuned(1, 1000, 1024, 0, ctypes.byref(t), ctypes.byref(p)) == UNSUP
+    t = api.make_tuning(rows_per_wave=3)
+    assert lib.glu_dual_gemv_plan_tuned(1, 1000, 1024, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP
+    t = api.make_tuning(rows_per_wave=2, waves_per_block=2, grid=100)
+    q = api.plan(1, 1000, 1024, True, t)
+    assert q["grid"] == 100 and q["block"] == 128
+    assert lib.glu_dual_gemv_plan(1, 1, 1, 1, None) == NULLP
+
+
+# Fake device addresses: every call below fails validation, so nothing reaches HIP.
+A = 0x7f0000000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, A, A + 4096, A + 8192, 1, 8, 8), NULLP),                 # hidden NULL
+    ((A, 0, A + 4096, A + 8192, 1, 8, 8), NULLP),
+    ((A, A + 4096, 0, A + 8192, 1, 8, 8), NULLP),
+    ((A, A + 4096, A + 8192, 0, 1, 8, 8), NULLP),                 # out NULL
+    ((0, 0, 0, 0, 0, 5, 5), OK),                                  # M == 0: nothing to do
+    ((0, 0, 0, 0, 5, 0, 5), OK),                                  # N == 0
+    ((A + 1, A + 4096, A + 8192, A + 16384, 1, 8, 8), ALIGN),     # odd addresses
+    ((A, A + 4097, A + 8192, A + 16384, 1, 8, 8), ALIGN),
+    ((A, A + 4096, A + 8193, A + 16384, 1, 8, 8), ALIGN),
+    ((A, A + 4096, A + 8192, A + 16385, 1, 8, 8), ALIGN),
+    ((A, A + 4096, A + 8192, A + 4096 + 64, 1, 8, 8), ALIAS),     # out inside gate_w
+    ((A, A + 4096, A + 8192, A + 8, 1, 8, 8), ALIAS),             # out overlaps hidden's 16 bytes
+    ((A, A + 4096, A + 8192, A + 8192 + 126, 1, 8, 8), ALIAS),    # out's first element is up_w's last
+    ((A, A + 4096, A + 8192, A + 1, 1, 8, 8), ALIGN),             # misalignment reported before aliasing
+    ((A, A + 4096, A + 8192, A + 16384, -1, 8, 8), SHAPE),
+    ((A, A + 4096, A + 8192, A + 16384, 1, -8, 8), SHAPE),
+    ((A, A + 4096, A + 8192, A + 16384, 1, 8, -8), SHAPE),
+    ((A, A + 4096, A + 8192, A + 16384, 1 << 62, 8, 8), SHAPE),
+])
+def test_validation_before_any_hip_call(lib, args, status):
+    assert api.dual_gemv_raw(*args) == status
+    assert lib.glu_last_hip_error() == 0
+
+
+def test_adjacent_buffers_do_not_alias(lib):
+    # out placed exactly after up_w's last byte is valid, but launching needs a GPU:
+    # check the aliasing predicate through a shape that then fails on something else
+    # (a NULL hidden with K > 0 is reported first, so no launch happens)
+    assert api.dual_gemv_raw(0, A + 4096, A + 8192, A + 8192 + 128, 1, 8, 8) == NULLP
+
+
+def test_python_face_rejects_cpu_tensors():
+    import torch
+    h = torch.zeros(1, 8, dtype=torch.bfloat16)
+    w = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        api.dual_gemv(h, w, w)
+    with pytest.raises(TypeError):
+        api.dual_gemv(h.float(), w, w)

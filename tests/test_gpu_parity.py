@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path through the C ABI against the oracle (needs an MI355X).
+
+Bar (written out in oracle/check.py): every output within 2 bf16 ULP of the
+oracle or inside its admissible interval (near-cancelled dots only, kappa >=
+1e4, counted), mean relative error <= 0.3%, bit-exact fraction >= 99.9%.
+Integer-exact properties (determinism, row consistency, exhaustive epilogue,
+canaries) are checked bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check
+from glu_mlp_gemv_amd import api, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_from_bits(b: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_run(h, wg, wu, tuning=None):
+    out = api.dual_gemv(h, wg, wu, tuning=tuning)
+    torch.cuda.synchronize()
+    return out
+
+
+def parity(h_cpu, wg_cpu, wu_cpu, tuning=None, label=""):
+    M, K = h_cpu.shape
+    N = wg_cpu.shape[0]
+    plan = api.plan(M, N, K, True, tuning)
+    say(f"[parity] {label} M={M} N={N} K={K} plan={plan}")
+    h, wg, wu = h_cpu.to(DEV), wg_cpu.to(DEV), wu_cpu.to(DEV)
+    got = bits(gpu_run(h, wg, wu, tuning))
+    ref = oracle.dual_gemv(bits(h_cpu), bits(wg_cpu), bits(wu_cpu), with_pre=True)
+    rep = check.compare(got, ref, depth=plan["accum_depth"], k_len=K)
+    say(f"[parity] {label}: {rep.summary()}")
+    return rep, got, ref
+
+
+# ---- the workloads at full size ---------------------------------------------
+
+CASES = []
+for name, w in inputs.WORKLOADS.items():
+    if w.layers > 1:
+        continue
+    for M in w.Ms:
+        for seed in w.seeds:
+            CASES.append((name, M, seed))
+
+
+@pytest.mark.parametrize("name,M,seed", CASES, ids=[f"{n}-M{m}-s{s}" for n, m, s in CASES])
+def test_workload_parity(name, M, seed):
+    h, wg, wu = inputs.case(name, M=M, seed=seed)
+    rep, _, _ = parity(h, wg, wu, label=f"{name} seed {seed}")
+    assert rep.ok, rep.summary()
+
+
+def test_decode_stack_parity():
+    """32 layers of K=2560 N=9216 in layer order; every layer's output against the oracle."""
+    w = inputs.WORKLOADS["stack32_k2560_n9216"]
+    hs = inputs.stack_hidden(0, w.layers, w.K)
+    layers = inputs.stack_weights(0, w.layers, w.N, w.K, device=DEV)
+    hs_dev = hs.to(DEV)
+    outs = [api.dual_gemv(hs_dev[l:l + 1], *layers[l]) for l in range(w.layers)]
+    torch.cuda.synchronize()
+    depth = api.plan(1, w.N, w.K)["accum_depth"]
+    worst = None
+    for l in range(w.layers):
+        wg, wu = (bits(t) for t in layers[l])
+        ref = oracle.dual_gemv(bits(hs[l:l + 1]), wg, wu, with_pre=True)
+        rep = check.compare(bits(outs[l]), ref, depth=depth, k_len=w.K)
+        assert rep.ok, f"layer {l}: {rep.summary()}"
+        if worst is None or rep.bit_exact_frac < worst.bit_exact_frac:
+            worst = rep
+    say(f"[stack] worst layer: {worst.summary()}")
+
+
+# ---- ragged and small shapes, every kernel ------------------------------------
+
+SMALL = [(1, 1, 8), (1, 3, 8), (1, 65, 64), (1, 3000, 1024), (2, 777, 520), (3, 1000, 4104),
+         (5, 129, 2560), (8, 3000, 1024), (8, 640, 8192), (1, 100, 8192), (1, 300, 5128), (2, 257, 6144),
+         (4, 1000, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_valu(M, N, K):
+    h, wg, wu = inputs.hidden(M, K, 3), *inputs.weights(N, K, 3)
+    t = api.make_tuning(kernel=api.KERNEL_VALU)
+    rep, _, _ = parity(h, wg, wu, tuning=t, label="valu")
+    assert rep.ok, rep.summary()
+
+
+MFMA_SHAPES = [(9, 100, 512), (16, 17, 64), (16, 1000, 1032), (17, 333, 2560), (32, 3000, 1024),
+               (31, 64, 5120), (33, 200, 520), (70, 1000, 1024), (4, 999, 1024), (1, 2000, 2560),
+               (2, 100, 40000), (8, 700, 8)]
+MFMA_TUNINGS = [dict(), dict(mfma_segments=2), dict(mfma_segments=8, waves_per_block=2),
+                dict(grid=3, waves_per_block=1)]
+
+
+@pytest.mark.parametrize("tn", range(len(MFMA_TUNINGS)))
+@pytest.mark.parametrize("M,N,K", MFMA_SHAPES)
+def test_small_mfma(M, N, K, tn):
+    h, wg, wu = inputs.hidden(M, K, 4), *inputs.weights(N, K, 4)
+    t = api.make_tuning(kernel=api.KERNEL_MFMA, **MFMA_TUNINGS[tn])
+    rep, _, _ = parity(h, wg, wu, tuning=t, label=f"mfma {MFMA_TUNINGS[tn]}")
+    assert rep.ok, rep.summary()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1003), (3, 257, 77), (9, 100, 1), (20, 50, 130)])
+def test_generic_k_not_multiple_of_8(M, N, K):
+    h, wg, wu = inputs.hidden(M, K, 5), *inputs.weights(N, K, 5)
+    rep, _, _ = parity(h, wg, wu, label="generic")
+    assert rep.ok, rep.summary()
+
+
+def test_generic_unaligned_pointers():
+    M, N, K = 2, 500, 1024
+    h, wg, wu = inputs.hidden(M, K, 6), *inputs.weights(N, K, 6)
+    # views that start one element (2 bytes) into a larger buffer
+    hb = torch.empty(M * K + 1, dtype=torch.bfloat16, device=DEV)[1:].view(M, K)
+    gb = torch.empty(N * K + 1, dtype=torch.bfloat16, device=DEV)[1:].view(N, K)
+    ub = torch.empty(N * K + 1, dtype=torch.bfloat16, device=DEV)[1:].view(N, K)
+    hb.copy_(h); gb.copy_(wg); ub.copy_(wu)
+    assert hb.data_ptr() % 16 != 0
+    say("[unaligned] generic path")
+    got = bits(gpu_run(hb, gb, ub))
+    ref = oracle.dual_gemv(bits(h), bits(wg), bits(wu), with_pre=True)
+    rep = check.compare(got, ref, depth=api.plan(M, N, K, False)["accum_depth"], k_len=K)
+    assert rep.ok, rep.summary()
+
+
+@pytest.mark.parametrize("kernel", [0, api.KERNEL_GENERIC])
+def test_zero_and_empty_sizes(kernel):
+    t = api.make_tuning(kernel=kernel) if kernel else None
+    out = torch.full((3, 5), 7.0, dtype=torch.bfloat16, device=DEV)
+    e = torch.empty(3, 0, dtype=torch.bfloat16, device=DEV)
+    w = torch.empty(5, 0, dtype=torch.bfloat16, device=DEV)
+    say("[zero] K=0")
+    api.dual_gemv(e, w, w, out=out, tuning=t)
+    torch.cuda.synchronize()
+    assert np.all(bits(out) == 0), "K == 0 must give +0"
+    o2 = torch.full((0, 5), 7.0, dtype=torch.bfloat16, device=DEV)
+    api.dual_gemv(torch.empty(0, 8, dtype=torch.bfloat16, device=DEV),
+                  torch.zeros(5, 8, dtype=torch.bfloat16, device=DEV),
+                  torch.zeros(5, 8, dtype=torch.bfloat16, device=DEV), out=o2, tuning=t)
+    torch.cuda.synchronize()
+
+
+# ---- exhaustive epilogue through the public API ------------------------------
+
+def _epilogue_case(u_bits: np.ndarray, tuning):
+    """N = 65536 rows: gate row j holds g_j = pattern j at k = 0, so G = g_j exactly."""
+    K = 32
+    N = 1 << 16
+    g_bits = np.arange(N, dtype=np.uint32).astype(np.uint16)
+    wg = np.zeros((N, K), dtype=np.uint16)
+    wu = np.zeros((N, K), dtype=np.uint16)
+    wg[:, 0] = g_bits
+    wu[:, 0] = u_bits
+    h = np.zeros((1, K), dtype=np.uint16)
+    h[0, 0] = 0x3F80  # 1.0
+    ref = oracle.dual_gemv(h, wg, wu)
+    got = bits(gpu_run(bf16_from_bits(h).to(DEV), bf16_from_bits(wg).to(DEV), bf16_from_bits(wu).to(DEV),
+                       tuning))
+    return got.ravel(), ref.ravel(), g_bits
+
+
+EPILOGUE_PATHS = {"valu": dict(kernel=api.KERNEL_VALU), "generic": dict(kernel=api.KERNEL_GENERIC),
+                  "mfma": dict(kernel=api.KERNEL_MFMA)}
+
+
+@pytest.mark.parametrize("path", list(EPILOGUE_PATHS))
+@pytest.mark.parametrize("up", ["one", "random"])
+def test_exhaustive_epilogue(path, up):
+    N = 1 << 16
+    if up == "one":
+        u = np.full(N, 0x3F80, dtype=np.uint16)
+    else:
+        u = np.random.default_rng(21).integers(0, 1 << 16, N).astype(np.uint16)
+    say(f"[epilogue] path={path} up={up}")
+    got, ref, g = _epilogue_case(u, api.make_tuning(**EPILOGUE_PATHS[path]))
+    bad = check.compare_strict_bits(got, ref)
+    if bad is not None:
+        sample = [(hex(g[i]), hex(u[i]), hex(got[i]), hex(ref[i])) for i in bad[:12]]
+        pytest.fail(f"{bad.size} of {N} differ (g, u, gpu, oracle): {sample}")
+
+
+# ---- boundary semantics -------------------------------------------------------
+
+def test_determinism_and_freshness():
+    h, wg, wu = inputs.case("decode_k2560_n9216", seed=1)
+    hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
+    a = bits(gpu_run(hd, gd, ud))
+    for _ in range(3):
+        assert np.array_equal(a, bits(gpu_run(hd, gd, ud))), "repeated calls must be bitwise equal"
+    # in-place weight update: the next call must read the new weights
+    gd.mul_(-1.0)
+    fresh = bits(gpu_run(hd, gd, ud))
+    ref = oracle.dual_gemv(bits(h), bits(gd.cpu()), bits(wu), with_pre=True)
+    rep = check.compare(fresh, ref, depth=api.plan(1, 9216, 2560)["accum_depth"], k_len=2560)
+    assert rep.ok, rep.summary()
+    assert not np.array_equal(a, fresh)
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 8])
+def test_batched_rows_equal_single_row_valu(M):
+    """VALU path: row m of a batched call is bitwise the M=1 call on hidden row m."""
+    h, wg, wu = inputs.case("batch_k4096_n12288", M=8, seed=1)
+    h = h[:M].contiguous()
+    hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
+    t = api.make_tuning(kernel=api.KERNEL_VALU)
+    batched = bits(gpu_run(hd, gd, ud, t))
+    for m in range(M):
+        single = bits(gpu_run(hd[m:m + 1].contiguous(), gd, ud, t))
+        assert np.array_equal(single[0], batched[m]), f"row {m}"
+
+
+@pytest.mark.parametrize("M", [2, 8, 16, 32])
+def test_batched_rows_mfma_vs_single(M):
+    """MFMA path: rows agree with the M=1 GEMV bit for bit except near rounding ties."""
+    h, wg, wu = inputs.case("mfma_k5120_n17408", M=32, seed=1)
+    h = h[:M].contiguous()
+    hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
+    batched = bits(gpu_run(hd, gd, ud))
+    worst = 0
+    for m in sorted({0, M // 2, M - 1}):
+        single = bits(gpu_run(hd[m:m + 1].contiguous(), gd, ud))[0]
+        d = check.ulp_distance(single, batched[m])
+        worst = max(worst, int(np.sort(d)[-5]))  # near-cancelled outputs may differ more
+        assert np.mean(d == 0) > 0.998
+    say(f"[mfma-vs-valu] 5th worst ULP {worst}")
+
+
+def test_saturated_gate_scaling_is_exact():
+    """With every gate saturated (G >= 17), out(2h) == 4 * out(h) bitwise."""
+    M, N, K = 2, 1000, 1024
+    h = torch.full((M, K), 0.5, dtype=torch.bfloat16)
+    wg = (torch.rand(N, K, generator=torch.Generator().manual_seed(3)) * 0.1 + 0.05).to(torch.bfloat16)
+    _, wu = inputs.weights(N, K, 9)
+    hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
+    for tuning in (None, api.make_tuning(kernel=api.KERNEL_MFMA)):
+        o1 = gpu_run(hd, gd, ud, tuning).float()
+        o2 = gpu_run((hd.float() * 2).to(torch.bfloat16), gd, ud, tuning).float()
+        assert torch.equal(o2, o1 * 4)
+
+
+def test_nan_and_zero_gate():
+    M, N, K = 1, 300, 512
+    h, wg, wu = inputs.hidden(M, K, 7), *inputs.weights(N, K, 7)
+    h[0, 10] = float("nan")
+    got = bits(gpu_run(h.to(DEV), wg.to(DEV), wu.to(DEV)))
+    assert check.is_nan_bits(got).all()
+    z = bits(gpu_run(inputs.hidden(M, K, 7).to(DEV), torch.zeros(N, K, dtype=torch.bfloat16, device=DEV),
+                     wu.to(DEV)))
+    assert np.all((z & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [(1, 1, 8, 0), (1, 65, 520, 0), (3, 3000, 1024, 0),
+                                          (8, 130, 2560, 0), (20, 33, 512, 0), (1, 65, 520, api.KERNEL_MFMA),
+                                          (2, 65, 1003, 0)])
+def test_output_canaries(M, N, K, kernel):
+    """Nothing is written outside out[M, N] (sentinels on both sides)."""
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), -3.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[pad:pad + M * N].view(M, N)
+    h, wg, wu = inputs.hidden(M, K, 8), *inputs.weights(N, K, 8)
+    t = api.make_tuning(kernel=kernel) if kernel else None
+    say(f"[canary] M={M} N={N} K={K}")
+    api.dual_gemv(h.to(DEV), wg.to(DEV), wu.to(DEV), out=out, tuning=t)
+    torch.cuda.synchronize()
+    b = buf.float().cpu()
+    assert torch.all(b[:pad] == -3.0) and torch.all(b[pad + M * N:] == -3.0)
+    ref = oracle.dual_gemv(bits(h), bits(wg), bits(wu), with_pre=True)
+    rep = check.compare(bits(out), ref, depth=api.plan(M, N, K, True, t)["accum_depth"], k_len=K)
+    assert rep.ok, rep.summary()
+
+
+def test_graph_capture_replays():
+    """A captured call replays correctly several times with eager work between replays."""
+    h, wg, wu = inputs.case("tail_k1024_n3000", seed=0)
+    hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
+    out = torch.empty(1, 3000, dtype=torch.bfloat16, device=DEV)
+    eager = bits(gpu_run(hd, gd, ud))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.dual_gemv(hd, gd, ud, out=out)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.dual_gemv(hd, gd, ud, out=out)
+    for i in range(4):
+        out.fill_(1.0)
+        _ = (hd.float() * 3).sum()  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), f"replay {i}"
