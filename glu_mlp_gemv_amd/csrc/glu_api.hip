@@ -93,9 +93,9 @@ glu_status plan_valu(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
 
 // Segments per stage: the largest of 5, 4, 2 that divides the segment count (no
 // ragged tail) and keeps the stage's registers in budget as hidden tiles grow.
-int default_segments(int64_t nsegs, int mt4, bool hidden_lds)
+int default_segments(int64_t nsegs, int mt4, int hidden)
 {
-    const int cap = !hidden_lds ? 2 : (mt4 <= 2 ? 5 : (mt4 <= 4 ? 4 : 2));
+    const int cap = hidden == glu::kHiddenL2 ? 2 : (hidden == glu::kHiddenSlices ? 4 : (mt4 <= 2 ? 5 : (mt4 <= 4 ? 4 : 2)));
     for (int u : {5, 4, 2}) {
         if (u <= cap && nsegs % u == 0) return u;
     }
@@ -109,22 +109,35 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     c.MT4 = (int)((m_pl + 3) / 4);
     const int64_t nchunks = K / 8;
     const int64_t nsegs = ceil_div(nchunks, 16);
-    c.hidden_lds = m_pl * K * 2 <= glu::kLdsBudget;
-    c.U = (t && t->mfma_segments) ? t->mfma_segments : default_segments(nsegs, c.MT4, c.hidden_lds);
+    const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
+    const int seg_req = t ? t->mfma_segments : 0;
+    if (t && t->mfma_hidden) {
+        c.hidden = t->mfma_hidden - 1;
+    } else if (glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsBudget) {
+        c.hidden = glu::kHiddenLds;
+    } else if (waves * glu::kWave == glu::kMfmaMaxThreads && (seg_req == 0 || seg_req == 2 || seg_req == 4)) {
+        c.hidden = glu::kHiddenSlices;
+    } else {
+        c.hidden = glu::kHiddenL2;
+    }
+    c.U = (t && t->mfma_segments) ? t->mfma_segments : default_segments(nsegs, c.MT4, c.hidden);
     if (c.U < 1) return GLU_ERR_UNSUPPORTED;
     c.nsg = (int)ceil_div(nsegs, c.U);
     c.ragged = (int64_t)c.nsg * c.U * 16 != nchunks;
-    const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
     if (waves < 1 || waves * glu::kWave > glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
     c.block = waves * glu::kWave;
     const int64_t groups = ceil_div(N, 4);
     int64_t grid;
     if (t && t->grid > 0) {
         grid = t->grid;
+    } else if (c.hidden == glu::kHiddenSlices) {
+        // workgroups take blocks of `waves` adjacent groups
+        grid = balanced_waves(ceil_div(groups, waves), (int64_t)kCUs * kMfmaWavesPerCU / waves);
     } else {
         grid = ceil_div(balanced_waves(groups, (int64_t)kCUs * kMfmaWavesPerCU), waves);
     }
     c.grid = (int)(grid < 1 ? 1 : grid);
+    if (c.hidden == glu::kHiddenSlices && c.block != glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
     if (!glu::mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
     L->kernel = GLU_KERNEL_MFMA;
     L->mfma = c;

@@ -23,12 +23,17 @@ struct ValuConfig {
     int block;    // threads per workgroup (multiple of 64)
 };
 
+// Where the MFMA kernel keeps hidden [M,K]:
+constexpr int kHiddenLds = 0;     // all of it in LDS (M rows of K/8 + 1 chunks <= 64 KiB)
+constexpr int kHiddenL2 = 1;      // read from L2 with each stage's weights
+constexpr int kHiddenSlices = 2;  // per-stage K-slices in an LDS ring, waves in lockstep
+
 struct MfmaConfig {
     int MT4;          // hidden-row tiles of 4 (M <= 4 * MT4 <= 32)
     int U;            // 128-element K segments per pipeline stage
     int nsg;          // stages per group of 4 weight rows: nsg * U * 16 >= K / 8
     bool ragged;      // nsg * U * 16 > K / 8: clamp and zero the excess chunks
-    bool hidden_lds;  // hidden staged in LDS (M * K * 2 <= 64 KiB), else read from L2
+    int hidden;       // kHiddenLds, kHiddenL2 or kHiddenSlices
     int grid;         // workgroups (persistent)
     int block;        // threads per workgroup (multiple of 64)
 };
@@ -53,6 +58,8 @@ hipError_t valu_launch(const ValuConfig& c, const uint16_t* hidden, const uint16
                        hipStream_t stream);
 
 bool mfma_supported(const MfmaConfig& c);
+size_t mfma_slice_lds_bytes(int mt4, int u);
+size_t mfma_hidden_lds_bytes(int m, int64_t k);
 hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
                        hipStream_t stream);

@@ -47,7 +47,7 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f3
 
 // MT4: hidden-row tiles of 4 (M <= 4*MT4); U: 128-element segments per stage;
 // nsg: stages per group (nsg * U * 16 >= K/8, equality unless RAGGED).
-// Dynamic LDS: M * K * 2 bytes when HLDS.
+// Dynamic LDS: M * (K/8 + 1) * 16 bytes when HLDS.
 template <int MT4, int U, bool HLDS, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
@@ -65,9 +65,13 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     const int cseg = (i16 & 3) * 4 + (lane >> 4);  // 16-byte chunk within a 256-byte segment
     const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
 
+    // hidden rows in LDS are padded by one chunk so the 4 rows a read touches
+    // fall in different banks
+    const int hpitch = nchunks + 1;
     if constexpr (HLDS) {
         for (int i = threadIdx.x; i < M * nchunks; i += blockDim.x) {
-            h_lds[i] = h4[i];
+            const int m = i / nchunks;
+            h_lds[i + m] = h4[i];
         }
         __syncthreads();
     }
@@ -163,7 +167,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             for (int t = 0; t < MT4; ++t) {
                 u32x4_t b;
                 if constexpr (HLDS) {
-                    b = h_lds[hrow[t] * nchunks + cc];
+                    b = h_lds[hrow[t] * hpitch + cc];
                 } else {
                     b = Bq[t][u];
                 }
@@ -196,6 +200,159 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     }
 }
 
+// The same block-diagonal product when hidden does not fit in LDS: the W = 4
+// waves of a workgroup take the 4 adjacent row groups of a block and advance
+// through K in lockstep, one stage at a time, and the workgroup stages only
+// the K-slice of hidden that the stage needs (all M rows, U segments) in a
+// double-buffered LDS ring.  The hidden loads of stage s+1 are issued before
+// its weight loads, so waiting for them never waits for the weights; one
+// barrier per stage separates the slice writes from the reads.
+// Dynamic LDS: 2 * 4*MT4 * U*16 * 16 bytes.  blockDim.x == 256.
+template <int MT4, int U, bool RAGGED>
+__global__ void __launch_bounds__(kMfmaMaxThreads)
+mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+                  const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
+                  int M, int N, int K, int64_t ldo, int nsg)
+{
+    constexpr int W = kMfmaMaxThreads / kWave;             // waves in lockstep
+    constexpr int MP = 4 * MT4;                            // hidden rows in a slice (padded)
+    constexpr int SC = U * 16;                             // 16-byte chunks of one row in a slice
+    constexpr int HPT = (MP * SC + kMfmaMaxThreads - 1) / kMfmaMaxThreads;  // slice loads per thread
+    extern __shared__ u32x4_t hs[];                        // [2][MP][SC], chunk c of row r at c ^ (r & 3)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nchunks = K >> 3;
+    const int i16 = lane & 15;
+    const int rho_a = i16 >> 2;
+    const int cseg = (i16 & 3) * 4 + (lane >> 4);
+    const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
+
+    const int ngroups = (N + 3) / 4;
+    const int nblocks = (ngroups + W - 1) / W;
+    if ((int)blockIdx.x >= nblocks) return;  // whole workgroup
+    const int my_blocks = (nblocks - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+    const int nstages = my_blocks * nsg;  // the same for every wave of the workgroup
+
+    auto group_of = [&](int s) { return ((int)blockIdx.x + (s / nsg) * (int)gridDim.x) * W + wave; };
+
+    auto load_h = [&](int s, u32x4_t (&hr)[HPT]) {
+        const int sb = s % nsg;
+#pragma unroll
+        for (int i = 0; i < HPT; ++i) {
+            const int e = min(i * kMfmaMaxThreads + (int)threadIdx.x, MP * SC - 1);
+            const int m = min(e / SC, M - 1);  // padded rows repeat row M-1, never stored
+            int c = sb * SC + (e % SC);
+            if (RAGGED) c = min(c, nchunks - 1);
+            hr[i] = h4[(int64_t)m * nchunks + c];
+        }
+    };
+    auto store_h = [&](int s, const u32x4_t (&hr)[HPT]) {
+        u32x4_t* dst = hs + (s & 1) * MP * SC;
+#pragma unroll
+        for (int i = 0; i < HPT; ++i) {
+            const int e = i * kMfmaMaxThreads + (int)threadIdx.x;
+            // XOR swizzle: the 4 rows one read touches land in different banks
+            if (e < MP * SC) dst[e ^ ((e / SC) & 3)] = hr[i];
+        }
+    };
+    auto load_w = [&](int s, u32x4_t (&A)[2][U]) {
+        const int sb = s % nsg;
+        const int row = min(4 * group_of(s) + rho_a, N - 1);  // rows past N re-read row N-1, never stored
+        const u32x4_t* gp = reinterpret_cast<const u32x4_t*>(gate_w + (int64_t)row * K);
+        const u32x4_t* up = reinterpret_cast<const u32x4_t*>(up_w + (int64_t)row * K);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int c = (sb * U + u) * 16 + cseg;
+            if (RAGGED) c = min(c, nchunks - 1);
+            A[0][u] = __builtin_nontemporal_load(gp + c);
+            A[1][u] = __builtin_nontemporal_load(up + c);
+        }
+    };
+
+    f32x4_t acc[MT4][2];
+
+    auto finish_group = [&](int g) {
+        const int e = lane & 3;
+        float res[2][(MT4 + 3) / 4];
+#pragma unroll
+        for (int t = 0; t < MT4; ++t) {
+#pragma unroll
+            for (int gu = 0; gu < 2; ++gu) {
+                const f32x4_t d = acc[t][gu];
+                float v = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
+                v = dpp_add<0xB1>(v);
+                v = dpp_add<0x4E>(v);
+                if (e == (t & 3)) res[gu][t >> 2] = v;
+            }
+        }
+        const int row = 4 * g + (lane >> 4);
+#pragma unroll
+        for (int k = 0; k < (MT4 + 3) / 4; ++k) {
+            const int t = 4 * k + e;
+            const int m = 4 * t + ((lane & 15) >> 2);
+            if (t < MT4 && m < M && row < N) {
+                out[(int64_t)m * ldo + row] = glu_epilogue(res[0][k], res[1][k]);
+            }
+        }
+    };
+
+    auto compute = [&](int s, const u32x4_t (&A)[2][U]) {
+        const int sb = s % nsg;
+        if (sb == 0) {
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+                acc[t][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                acc[t][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        const u32x4_t* src = hs + (s & 1) * MP * SC;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = !RAGGED || (sb * U + u) * 16 + cseg < nchunks;
+            const u32x4_t ag = RAGGED ? (ok ? A[0][u] : z) : A[0][u];
+            const u32x4_t au = RAGGED ? (ok ? A[1][u] : z) : A[1][u];
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+                u32x4_t b = src[(4 * t + rho_a) * SC + ((u * 16 + cseg) ^ rho_a)];
+                if constexpr (RAGGED) b = ok ? b : z;
+                acc[t][0] = mfma16(ag, b, acc[t][0]);
+                acc[t][1] = mfma16(au, b, acc[t][1]);
+            }
+        }
+        if (sb == nsg - 1) finish_group(group_of(s));
+    };
+
+    // one full step: prefetch stage s+1 (hidden slice, then weights), compute s,
+    // publish the slice of s+1, and wait for the whole workgroup
+    u32x4_t hr[HPT];
+    auto step = [&](int s, const u32x4_t (&cur)[2][U], u32x4_t (&nxt)[2][U]) {
+        load_h(s + 1, hr);
+        load_w(s + 1, nxt);
+        compute(s, cur);
+        store_h(s + 1, hr);
+        __syncthreads();
+    };
+
+    u32x4_t a0[2][U], a1[2][U];
+    load_h(0, hr);
+    load_w(0, a0);
+    store_h(0, hr);
+    __syncthreads();
+    int s = 0;
+    while (s + 2 < nstages) {
+        step(s, a0, a1);
+        step(s + 1, a1, a0);
+        s += 2;
+    }
+    if (s + 1 < nstages) {
+        step(s, a0, a1);
+        compute(s + 1, a1);
+    } else {
+        compute(s, a0);
+    }
+}
+
 namespace {
 
 using MfmaFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, int64_t, int);
@@ -212,11 +369,27 @@ MfmaFn pick_u(int U)
     }
 }
 
+template <int MT4, bool RG>
+MfmaFn pick_slice_u(int U)
+{
+    switch (U) {
+    case 2: return mfma_slice_kernel<MT4, 2, RG>;
+    case 4: return mfma_slice_kernel<MT4, 4, RG>;
+    default: return nullptr;
+    }
+}
+
 template <int MT4>
 MfmaFn pick_flags(const MfmaConfig& c)
 {
-    if (c.hidden_lds) return c.ragged ? pick_u<MT4, true, true>(c.U) : pick_u<MT4, true, false>(c.U);
-    return c.ragged ? pick_u<MT4, false, true>(c.U) : pick_u<MT4, false, false>(c.U);
+    switch (c.hidden) {
+    case kHiddenLds: return c.ragged ? pick_u<MT4, true, true>(c.U) : pick_u<MT4, true, false>(c.U);
+    case kHiddenL2: return c.ragged ? pick_u<MT4, false, true>(c.U) : pick_u<MT4, false, false>(c.U);
+    case kHiddenSlices:
+        if (c.block != kMfmaMaxThreads) return nullptr;
+        return c.ragged ? pick_slice_u<MT4, true>(c.U) : pick_slice_u<MT4, false>(c.U);
+    default: return nullptr;
+    }
 }
 
 MfmaFn pick(const MfmaConfig& c)
@@ -236,9 +409,14 @@ MfmaFn pick(const MfmaConfig& c)
 
 }  // namespace
 
+size_t mfma_slice_lds_bytes(int mt4, int u) { return (size_t)2 * 4 * mt4 * u * 16 * 16; }
+
+size_t mfma_hidden_lds_bytes(int m, int64_t k) { return (size_t)m * (size_t)(k / 8 + 1) * 16; }
+
 bool mfma_supported(const MfmaConfig& c)
 {
     if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
+    if (c.hidden == kHiddenSlices && mfma_slice_lds_bytes(c.MT4, c.U) > (size_t)kLdsBudget) return false;
     return pick(c) != nullptr;
 }
 
@@ -250,7 +428,9 @@ hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const
     cm.MT4 = (M + 3) / 4;
     MfmaFn fn = pick(cm);
     if (!fn || M < 1 || M > 4 * cm.MT4) return hipErrorInvalidValue;
-    const size_t lds = cm.hidden_lds ? (size_t)M * (size_t)K * sizeof(uint16_t) : 0;
+    size_t lds = 0;
+    if (cm.hidden == kHiddenLds) lds = mfma_hidden_lds_bytes(M, K);
+    if (cm.hidden == kHiddenSlices) lds = mfma_slice_lds_bytes(cm.MT4, cm.U);
     hipLaunchKernelGGL(fn, dim3(cm.grid), dim3(cm.block), lds, stream,
                        hidden, gate_w, up_w, out, M, (int)N, (int)K, ldo, cm.nsg);
     return hipGetLastError();

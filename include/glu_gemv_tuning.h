@@ -25,6 +25,9 @@ typedef struct glu_tuning {
     int waves_per_block;  /* VALU, MFMA: waves per workgroup (1..8) */
     int grid;             /* VALU, MFMA: workgroups of the persistent grid */
     int mfma_segments;    /* MFMA: 128-element K segments per pipeline stage (2, 4, 5, 8) */
+    int mfma_hidden;      /* MFMA: where hidden lives: 1 = all in LDS (M*K*2 <= 64 KiB),
+                             2 = read from L2 per stage, 3 = per-stage K-slices in LDS
+                             with the workgroup's 4 waves in lockstep (segments 2 or 4) */
 } glu_tuning;
 
 glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,

@@ -107,7 +107,8 @@ MFMA_SHAPES = [(9, 100, 512), (16, 17, 64), (16, 1000, 1032), (17, 333, 2560), (
                (31, 64, 5120), (33, 200, 520), (70, 1000, 1024), (4, 999, 1024), (1, 2000, 2560),
                (2, 100, 40000), (8, 700, 8)]
 MFMA_TUNINGS = [dict(), dict(mfma_segments=2), dict(mfma_segments=8, waves_per_block=2),
-                dict(grid=3, waves_per_block=1)]
+                dict(grid=3, waves_per_block=1), dict(mfma_hidden=2), dict(mfma_hidden=3),
+                dict(mfma_hidden=3, mfma_segments=2, grid=2)]
 
 
 @pytest.mark.parametrize("tn", range(len(MFMA_TUNINGS)))
