@@ -3,16 +3,25 @@
 One step is one pass of a 32-layer decode stack: 32 distinct weight sets of
 M=1, K=2560, N=9216 (a 4B-class decoder MLP gate/up, 3.02 GB in total, far
 beyond the 256 MB Infinity Cache), called back to back in layer order with a
-per-layer hidden vector.  Inputs are seeded synthetic data already resident in
-HBM when timing starts.  The metric is achieved HBM bandwidth: algorithmic
-bytes (both weight matrices once, hidden and output) over time.
+per-layer hidden vector, captured once as a HIP graph and replayed per step
+(a decode step is one graph replay).  Inputs are seeded synthetic data
+already resident in HBM when timing starts.  The metric is achieved HBM
+bandwidth: algorithmic bytes (both weight matrices once, hidden and output)
+over time.
 
-Prints ONE JSON line.  Extra modes (written to --extra-json, not stdout):
---workloads times the batched workloads and M=1 at their (K, N).
+Prints ONE JSON line.  Other modes:
+  --workloads FILE     also time the batched workloads (JSON written to FILE)
+  --calibrate-copy     run a 256 MiB device copy first (reference kernel for
+                       rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE scaling)
+  --summarize KIND DIR turn rocprofv3 output in DIR into the text summaries
+                       kept under profiles/ (KIND: trace | counters); host
+                       only, no GPU
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -22,8 +31,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+CALIBRATION_BYTES = 256 * 1024 * 1024
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+METRIC = "achieved HBM GB/s (and % of peak) for dual GEMV+SiLU·mul, M=1, K=2560, N=9216"
+STACK = dict(M=1, K=2560, N=9216, layers=32)
 
 
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
@@ -32,6 +45,7 @@ def algorithmic_bytes(M: int, N: int, K: int) -> int:
 
 
 def source_hash() -> str:
+    """Hash of the HIP sources: counter figures are valid only for the kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "glu_mlp_gemv_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
@@ -40,29 +54,39 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key: str):
-    """HBM bytes per launch from committed counter runs, if taken on the current kernels."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(p):
+def load_traffic(kernel_name: str):
+    """HBM bytes per launch of a kernel from the committed counter summary, if current."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        d = json.load(open(p))
+        d = json.load(open(TRAFFIC_JSON))
     except ValueError:
         return None
     if d.get("source_hash") != source_hash():
         return None
-    ent = d.get("kernels", {}).get(kernel_key)
+    ent = d.get("kernels", {}).get(kernel_name)
     return None if ent is None else ent.get("bytes_per_launch")
 
 
-def make_stack(torch, inputs, layers, N, K, seed, dev):
-    ws = [inputs.weights(N, K, inputs.stack_layer_seed(seed, l), device=dev) for l in range(layers)]
-    hs = inputs.stack_hidden(seed, layers, K).to(dev)
-    outs = torch.empty(layers, N, dtype=torch.bfloat16, device=dev)
-    return ws, hs, outs
+# ---------------------------------------------------------------- timing ----
+
+def capture(torch, fn):
+    """A HIP graph of one call of fn, captured on a side stream after a warm-up call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def time_region(torch, fn, steps, warmup, stream):
+    """Milliseconds for `steps` calls of fn, events on the launch stream, synchronised both sides."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -73,7 +97,7 @@ def time_region(torch, fn, steps, warmup, stream):
         fn()
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end)  # ms
+    return start.elapsed_time(end)
 
 
 def cpu_baseline(torch, ws, hs, layers_sample: int, min_seconds: float):
@@ -102,21 +126,6 @@ def cpu_baseline(torch, ws, hs, layers_sample: int, min_seconds: float):
                       f"M=1 K={K} N={N} stack, {el:.1f} s wall, {threads} OpenMP threads"}
 
 
-def capture(torch, fn):
-    """A HIP graph of one call of fn (captured on a side stream after a warm-up call)."""
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        fn()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        fn()
-    torch.cuda.synchronize()
-    return g
-
-
 def bench_workloads(torch, api, inputs, dev, reps=30):
     """Batched workloads and M=1 at the same (K, N), each over a rotation pool of >= 1.4 GB,
     one graph replay per pass over the pool."""
@@ -141,8 +150,9 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
             flops = 4 * M * w.N * w.K
             res.append({"workload": name, "M": M, "K": w.K, "N": w.N, "us_per_call": round(us, 3),
                         "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                        "TFLOPs": round(flops / us / 1e6, 2), "kernel": api.plan(M, w.N, w.K)["kernel_name"],
-                        "pool_sets": sets})
+                        "TFLOPs": round(flops / us / 1e6, 2),
+                        "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5),
+                        "kernel": api.plan(M, w.N, w.K)["kernel_name"], "pool_sets": sets})
             print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
             del g
         del pool
@@ -150,36 +160,25 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=5.0)
-    ap.add_argument("--workloads", action="store_true", help="also time the batched workloads")
-    ap.add_argument("--extra-json", default=None, help="file for the --workloads results")
-    ap.add_argument("--tuning", default=None, help="JSON dict of glu_tuning fields (sweeps)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the projection shards along N with no communication: one GPU runs the same kernel on its rows). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def run(args):
     import torch
     from glu_mlp_gemv_amd import api, inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = inputs.WORKLOADS["stack32_k2560_n9216"]
-    M, N, K, L = 1, w.N, w.K, w.layers
+    if args.calibrate_copy:
+        a = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    M, N, K, L = STACK["M"], STACK["N"], STACK["K"], STACK["layers"]
     tuning = api.make_tuning(**json.loads(args.tuning)) if args.tuning else None
     plan = api.plan(M, N, K, True, tuning)
 
-    ws, hs, outs = make_stack(torch, inputs, L, N, K, args.seed, dev)
+    ws = [inputs.weights(N, K, inputs.stack_layer_seed(args.seed, l), device=dev) for l in range(L)]
+    hs = inputs.stack_hidden(args.seed, L, K).to(dev)
+    outs = torch.empty(L, N, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -187,31 +186,31 @@ def main():
         for l in range(L):
             api.dual_gemv(hs[l], ws[l][0], ws[l][1], out=outs[l], tuning=tuning)
 
-    # eager: raw C calls on precomputed device addresses (host cost per launch is minimal)
-    lib = api.library()
-    ptrs = [(hs[l].data_ptr(), ws[l][0].data_ptr(), ws[l][1].data_ptr(), outs[l].data_ptr())
-            for l in range(L)]
-    sh = stream.cuda_stream
-
-    def step_eager():
-        for p in ptrs:
-            lib.glu_dual_gemv(p[0], p[1], p[2], p[3], M, N, K, sh)
-
-    ms_eager = time_region(torch, step_eager, args.steps, args.warmup, stream)
-    # the decode step as deployed: one graph replay of the 32 launches
     graph = capture(torch, step)
     ms = time_region(torch, graph.replay, args.steps, args.warmup, stream)
     ms_per_step = ms / args.steps
     bytes_call = algorithmic_bytes(M, N, K)
-    bytes_step = bytes_call * L
-    gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
-    launch_us = ms * 1e3 / (args.steps * L * plan["launches"])
+    gbs = bytes_call * L / (ms_per_step * 1e-3) / 1e9
+    launches = args.steps * L * plan["launches"]
+    launch_us = ms * 1e3 / launches
     achieved = bytes_call / plan["launches"] / (launch_us * 1e-6) / 1e9
 
-    kernel_key = f"{plan['kernel_name']}_M{M}_K{K}_N{N}"
-    traffic = load_traffic(kernel_key)
+    # the same step launched eagerly, one C call per layer on precomputed addresses
+    ms_eager = None
+    if tuning is None:
+        lib = api.library()
+        ptrs = [(hs[l].data_ptr(), ws[l][0].data_ptr(), ws[l][1].data_ptr(), outs[l].data_ptr())
+                for l in range(L)]
+        sh = stream.cuda_stream
+
+        def step_eager():
+            for p in ptrs:
+                lib.glu_dual_gemv(p[0], p[1], p[2], p[3], M, N, K, sh)
+        ms_eager = time_region(torch, step_eager, args.steps, args.warmup, stream)
+
+    kernel = plan["kernel_symbol"]
     line = {
-        "metric": "achieved HBM GB/s (and % of peak) for dual GEMV+SiLU·mul, M=1, K=2560, N=9216",
+        "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -223,27 +222,112 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "glu_dual_gemv M=1 K=2560 N=9216, 32-layer decode stack (3.02 GB of "
-                               "bf16 gate/up weights), layers called back to back",
+        "config": {"workload": "glu_dual_gemv M=1 K=2560 N=9216, 32-layer decode stack (3.02 GB of bf16 "
+                               "gate/up weights), one HIP graph replay of the 32 launches per step",
                    "M": M, "K": K, "N": N, "layers": L, "bytes_per_call": bytes_call,
                    "us_per_call": round(launch_us * plan["launches"], 3),
-                   "timing": "one HIP graph replay per step (32 launches); events on the launch stream",
-                   "eager_ms_per_step": round(ms_eager / args.steps, 5),
-                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": plan,
-                   "accumulate": "fp32", "tuning": json.loads(args.tuning) if args.tuning else None},
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "eager_ms_per_step": None if ms_eager is None else round(ms_eager / args.steps, 5),
+                   "kernel": kernel, "plan": plan, "accumulate": "fp32",
+                   "tuning": json.loads(args.tuning) if args.tuning else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(kernel)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, ws, hs, layers_sample=4, min_seconds=args.cpu_seconds)
     if args.workloads:
         extra = {"workloads": bench_workloads(torch, api, inputs, dev), "stack": line}
-        path = args.extra_json or os.path.join(ROOT, "gpurun_out", "bench_workloads.json")
-        os.makedirs(os.path.dirname(path), exist_ok=True)
-        with open(path, "w") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(args.workloads)), exist_ok=True)
+        with open(args.workloads, "w") as f:
             json.dump(extra, f, indent=1)
     print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------- profile summaries ----
+
+def _rows(pattern):
+    out = []
+    for p in sorted(glob.glob(pattern, recursive=True)):
+        with open(p) as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
+def summarize_trace(d: str):
+    """Kernel-trace statistics (rocprofv3 --kernel-trace --stats -f csv) as a markdown table."""
+    stats = _rows(os.path.join(d, "**", "*kernel_stats.csv"))
+    if not stats:
+        raise SystemExit(f"no *kernel_stats.csv under {d}")
+    lines = ["| kernel | calls | total ns | average ns | min ns | max ns | % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {r['TotalDurationNs']} | "
+                     f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines)
+
+
+def summarize_counters(d: str, command: str):
+    """FETCH_SIZE / WRITE_SIZE per dispatch, scaled by the calibration copy of known size.
+
+    ``d`` is one directory or several separated by commas (one counter per run)."""
+    rows = []
+    for one in d.split(","):
+        rows.extend(_rows(os.path.join(one, "**", "*counter_collection.csv")))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    per = {}
+    for r in rows:
+        per.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    cal_kib = CALIBRATION_BYTES / 1024
+    scale = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        cal = [v for (k, c), vs in per.items() if c == cname and "copyBuffer" in k for v in vs
+               if v > 0.25 * cal_kib]
+        if cal:
+            scale[cname] = cal_kib / max(cal)
+    kernels = {}
+    for (k, c), vs in per.items():
+        if "glu::" not in k:
+            continue
+        short = k.split("(")[0].replace("void ", "").strip()
+        ent = kernels.setdefault(short, {})
+        ent[c + "_kib_per_dispatch"] = round(sum(vs) / len(vs), 2)
+        ent["dispatches"] = len(vs)
+    for ent in kernels.values():
+        have = [c for c in ("FETCH_SIZE", "WRITE_SIZE") if c + "_kib_per_dispatch" in ent and c in scale]
+        ent["bytes_per_launch"] = (round(sum(ent[c + "_kib_per_dispatch"] * scale[c] * 1024 for c in have))
+                                   if len(have) == 2 else None)
+    return {"source_hash": source_hash(), "calibration": {"copy_bytes": CALIBRATION_BYTES, "scale": scale},
+            "command": command, "kernels": kernels}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--workloads", default=None, metavar="FILE", help="also time the batched workloads")
+    ap.add_argument("--tuning", default=None, help="JSON dict of glu_tuning fields")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"))
+    ap.add_argument("--command", default="", help="the profiled command, recorded in counter summaries")
+    args = ap.parse_args()
+    if args.summarize:
+        kind, d = args.summarize
+        if kind == "trace":
+            print(summarize_trace(d))
+        else:
+            print(json.dumps(summarize_counters(d, args.command), indent=1))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the projection shards "
+              "along N with no communication: one GPU runs the same kernel on its rows). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    run(args)
 
 
 if __name__ == "__main__":

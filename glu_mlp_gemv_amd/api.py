@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "glu_dual_gemv_plan",
     "glu_dual_gemv_tuned",
     "glu_dual_gemv_plan_tuned",
+    "glu_dual_gemv_describe",
 )
 
 
@@ -86,6 +87,9 @@ def library() -> ctypes.CDLL:
     lib.glu_dual_gemv_plan_tuned.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning),
                                              ctypes.POINTER(Plan)]
     lib.glu_dual_gemv_plan_tuned.restype = ctypes.c_int
+    lib.glu_dual_gemv_describe.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning), ctypes.c_char_p,
+                                           ctypes.c_int]
+    lib.glu_dual_gemv_describe.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -121,7 +125,13 @@ def plan(M: int, N: int, K: int, aligned16: bool = True, tuning: Optional[Tuning
     else:
         st = lib.glu_dual_gemv_plan_tuned(M, N, K, int(aligned16), ctypes.byref(tuning), ctypes.byref(p))
     _raise_for(st)
-    return p.as_dict()
+    d = p.as_dict()
+    buf = ctypes.create_string_buffer(256)
+    st = lib.glu_dual_gemv_describe(M, N, K, int(aligned16), ctypes.byref(tuning) if tuning is not None else None,
+                                    buf, 256)
+    _raise_for(st)
+    d["kernel_symbol"] = buf.value.decode()
+    return d
 
 
 def _check(name: str, t: torch.Tensor, ndims):

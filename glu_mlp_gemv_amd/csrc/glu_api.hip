@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
 
 #include "../../include/glu_gemv.h"
 #include "../../include/glu_gemv_tuning.h"
@@ -294,6 +295,39 @@ glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned
     const glu_status st = plan_launch(M, N, K, aligned16 != 0, tuning, &L);
     if (st != GLU_OK) return st;
     fill_plan(L, plan);
+    return GLU_OK;
+}
+
+glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16,
+                                  const glu_tuning* tuning, char* buf, int len)
+{
+    if (!buf || len < 1) return GLU_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Launch L;
+    const glu_status st = plan_launch(M, N, K, aligned16 != 0, tuning, &L);
+    if (st != GLU_OK) return st;
+    const char* tf[2] = {"false", "true"};
+    switch (L.kernel) {
+    case GLU_KERNEL_VALU: {
+        const glu::ValuConfig& c = L.valu;
+        snprintf(buf, (size_t)len, "glu::valu_kernel<%d, %d, %d, %d, %s, %s>", c.M, c.R, c.U, c.NB,
+                 tf[glu::valu_hidden_in_lds(c.M, c.U, c.NB)], tf[c.ragged]);
+        break;
+    }
+    case GLU_KERNEL_MFMA: {
+        const glu::MfmaConfig& c = L.mfma;
+        if (c.hidden == glu::kHiddenSlices) {
+            snprintf(buf, (size_t)len, "glu::mfma_slice_kernel<%d, %d, %s>", c.MT4, c.U, tf[c.ragged]);
+        } else {
+            snprintf(buf, (size_t)len, "glu::mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,
+                     tf[c.hidden == glu::kHiddenLds], tf[c.ragged]);
+        }
+        break;
+    }
+    case GLU_KERNEL_GENERIC: snprintf(buf, (size_t)len, "glu::generic_kernel<%d>", L.m_per_launch); break;
+    case GLU_KERNEL_ZERO: snprintf(buf, (size_t)len, "glu::zero_kernel"); break;
+    default: snprintf(buf, (size_t)len, "none"); break;
+    }
     return GLU_OK;
 }
 

@@ -24,7 +24,7 @@ struct ValuConfig {
 };
 
 // Where the MFMA kernel keeps hidden [M,K]:
-constexpr int kHiddenLds = 0;     // all of it in LDS (M rows of K/8 + 1 chunks <= 64 KiB)
+constexpr int kHiddenLds = 0;     // all of it in LDS (mfma_hidden_lds_bytes <= 64 KiB)
 constexpr int kHiddenL2 = 1;      // read from L2 with each stage's weights
 constexpr int kHiddenSlices = 2;  // per-stage K-slices in an LDS ring, waves in lockstep
 

@@ -47,7 +47,7 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f3
 
 // MT4: hidden-row tiles of 4 (M <= 4*MT4); U: 128-element segments per stage;
 // nsg: stages per group (nsg * U * 16 >= K/8, equality unless RAGGED).
-// Dynamic LDS: M * (K/8 + 1) * 16 bytes when HLDS.
+// Dynamic LDS when HLDS: M * K * 2 bytes, or M * (K/8 + 1) * 16 when K/8 is not a multiple of 4.
 template <int MT4, int U, bool HLDS, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
@@ -65,13 +65,16 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     const int cseg = (i16 & 3) * 4 + (lane >> 4);  // 16-byte chunk within a 256-byte segment
     const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
 
-    // hidden rows in LDS are padded by one chunk so the 4 rows a read touches
-    // fall in different banks
-    const int hpitch = nchunks + 1;
+    // the 4 hidden rows one read touches must fall in different LDS banks: chunk
+    // c of row m sits at c ^ (m & 3) when K/8 is a multiple of 4, else rows are
+    // padded by one chunk
+    const bool hswz = (nchunks & 3) == 0;
+    const int hpitch = hswz ? nchunks : nchunks + 1;
     if constexpr (HLDS) {
         for (int i = threadIdx.x; i < M * nchunks; i += blockDim.x) {
             const int m = i / nchunks;
-            h_lds[i + m] = h4[i];
+            const int c = i - m * nchunks;
+            h_lds[m * hpitch + (hswz ? c ^ (m & 3) : c)] = h4[i];
         }
         __syncthreads();
     }
@@ -167,7 +170,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             for (int t = 0; t < MT4; ++t) {
                 u32x4_t b;
                 if constexpr (HLDS) {
-                    b = h_lds[hrow[t] * hpitch + cc];
+                    b = h_lds[hrow[t] * hpitch + (hswz ? cc ^ (hrow[t] & 3) : cc)];
                 } else {
                     b = Bq[t][u];
                 }
@@ -411,7 +414,11 @@ MfmaFn pick(const MfmaConfig& c)
 
 size_t mfma_slice_lds_bytes(int mt4, int u) { return (size_t)2 * 4 * mt4 * u * 16 * 16; }
 
-size_t mfma_hidden_lds_bytes(int m, int64_t k) { return (size_t)m * (size_t)(k / 8 + 1) * 16; }
+size_t mfma_hidden_lds_bytes(int m, int64_t k)
+{
+    const int64_t nchunks = k / 8;
+    return (size_t)m * (size_t)(nchunks % 4 == 0 ? nchunks : nchunks + 1) * 16;
+}
 
 bool mfma_supported(const MfmaConfig& c)
 {

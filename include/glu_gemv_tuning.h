@@ -38,6 +38,16 @@ glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, c
 glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned16,
                                     const glu_tuning* tuning, glu_plan* plan);
 
+/*
+ * Name of the kernel instance the first launch of a call would run, as a
+ * profiler prints it (e.g. "glu::valu_kernel<1, 1, 5, 1, false, false>"),
+ * NUL-terminated into buf[len].  Host only, no HIP call.  Returns the plan's
+ * status; GLU_ERR_NULL_POINTER if buf is NULL or len < 1 (truncates silently
+ * when len is short).
+ */
+glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16,
+                                  const glu_tuning* tuning, char* buf, int len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert "glu_dual_gemv" in names and len(names) >= 7
+    assert "glu_dual_gemv" in names and len(names) >= 8
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, f"declared but not exported: {missing}"
     assert set(api.EXPORTED_SYMBOLS) == set(names)
@@ -72,6 +72,14 @@ def test_plan(lib, M, N, K, aligned, kernel, launches):
     assert p["launches"] == launches, p
     if kernel in (api.KERNEL_VALU, api.KERNEL_MFMA, api.KERNEL_GENERIC):
         assert p["grid"] > 0 and p["block"] % 64 == 0 and p["accum_depth"] >= 1
+
+
+def test_describe_names_the_instantiated_kernel(lib):
+    assert api.plan(1, 9216, 2560)["kernel_symbol"] == "glu::valu_kernel<1, 1, 5, 1, false, false>"
+    assert api.plan(8, 12288, 4096)["kernel_symbol"] == "glu::mfma_kernel<2, 4, true, false>"
+    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<8, 4, false>"
+    assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
+    assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
 
 
 def test_plan_accum_depth_valu(lib):
