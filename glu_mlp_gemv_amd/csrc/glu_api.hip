@@ -17,7 +17,9 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxDim = 0x7fffffff;    // N and K index rows and columns in 32 bits
-constexpr int64_t kMaxFastK = 0x7fffffff;  // the MFMA kernel takes any K % 8 == 0
+// the VALU and MFMA kernels address a group's weight rows and the hidden
+// rows of one launch with 32-bit byte offsets: 32 rows * K * 2 bytes < 2^32
+constexpr int64_t kMaxFastK = (int64_t)1 << 25;
 constexpr int64_t kMaxValuK = 8192;        // VALU: at most 16 chunks per lane per row
 constexpr int64_t kValuMaxDefaultK = 4096;  // longer rows stream faster through the MFMA kernel
 constexpr int kCUs = 256;                  // MI355X compute units

@@ -57,7 +57,8 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     extern __shared__ u32x4_t h_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int wave_id = blockIdx.x * wpb + threadIdx.x / kWave;
+    // wave-uniform, stated so that the stage loop compiles to scalar control flow
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + threadIdx.x / kWave);
     const int nwaves = gridDim.x * wpb;
     const int nchunks = K >> 3;
     const int i16 = lane & 15;
@@ -96,15 +97,19 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
         const int gi = s / nsg;
         const int sb = s - gi * nsg;
         const int g = wave_id + gi * nwaves;
-        const int row = min(4 * g + rho_a, N - 1);  // rows past N re-read row N-1, never stored
-        const u32x4_t* gp = reinterpret_cast<const u32x4_t*>(gate_w + (int64_t)row * K);
-        const u32x4_t* up = reinterpret_cast<const u32x4_t*>(up_w + (int64_t)row * K);
+        // a wave-uniform base for the group plus a 32-bit lane offset, so the
+        // addresses never share registers with loads still in flight
+        const int64_t row0 = 4 * (int64_t)g;
+        const uint32_t rr = (uint32_t)(min(4 * g + rho_a, N - 1) - 4 * g);  // rows past N re-read row N-1, never stored
+        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * K);
+        const char* up = reinterpret_cast<const char*>(up_w + row0 * K);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int c = (sb * U + u) * 16 + cseg;
             if (RAGGED) c = min(c, nchunks - 1);
-            A[0][u] = __builtin_nontemporal_load(gp + c);
-            A[1][u] = __builtin_nontemporal_load(up + c);
+            const uint32_t off = (rr * (uint32_t)nchunks + (uint32_t)c) * 16u;  // bytes, below 8*K
+            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + off));
+            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + off));
         }
         if constexpr (!HLDS) {
 #pragma unroll
@@ -113,7 +118,8 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
                 for (int u = 0; u < U; ++u) {
                     int c = (sb * U + u) * 16 + cseg;
                     if (RAGGED) c = min(c, nchunks - 1);
-                    Bq[t][u] = h4[(int64_t)hrow[t] * nchunks + c];
+                    const uint32_t off = ((uint32_t)hrow[t] * (uint32_t)nchunks + (uint32_t)c) * 16u;
+                    Bq[t][u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(hidden) + off);
                 }
             }
         }
@@ -191,6 +197,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             break;
         }
         load(s + 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage\'s math
         compute(s, a0, b0);
         ++s;
         if (s + 1 >= nstages) {
@@ -198,6 +205,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             break;
         }
         load(s + 1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage\'s math
         compute(s, a1, b1);
         ++s;
     }
@@ -223,7 +231,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     constexpr int HPT = (MP * SC + kMfmaMaxThreads - 1) / kMfmaMaxThreads;  // slice loads per thread
     extern __shared__ u32x4_t hs[];                        // [2][MP][SC], chunk c of row r at c ^ (r & 3)
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int nchunks = K >> 3;
     const int i16 = lane & 15;
     const int rho_a = i16 >> 2;
@@ -260,15 +268,20 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     };
     auto load_w = [&](int s, u32x4_t (&A)[2][U]) {
         const int sb = s % nsg;
-        const int row = min(4 * group_of(s) + rho_a, N - 1);  // rows past N re-read row N-1, never stored
-        const u32x4_t* gp = reinterpret_cast<const u32x4_t*>(gate_w + (int64_t)row * K);
-        const u32x4_t* up = reinterpret_cast<const u32x4_t*>(up_w + (int64_t)row * K);
+        // the last workgroup's waves can sit past the last group when the group
+        // count is not a multiple of W: they re-read the last group, never stored
+        const int g = min(group_of(s), ngroups - 1);
+        const int64_t row0 = 4 * (int64_t)g;  // wave-uniform base, 32-bit lane offsets
+        const uint32_t rr = (uint32_t)(min(4 * g + rho_a, N - 1) - 4 * g);  // 0..3: rows past N re-read row N-1
+        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * K);
+        const char* up = reinterpret_cast<const char*>(up_w + row0 * K);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int c = (sb * U + u) * 16 + cseg;
             if (RAGGED) c = min(c, nchunks - 1);
-            A[0][u] = __builtin_nontemporal_load(gp + c);
-            A[1][u] = __builtin_nontemporal_load(up + c);
+            const uint32_t off = (rr * (uint32_t)nchunks + (uint32_t)c) * 16u;  // bytes, below 8*K
+            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + off));
+            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + off));
         }
     };
 
@@ -332,6 +345,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     auto step = [&](int s, const u32x4_t (&cur)[2][U], u32x4_t (&nxt)[2][U]) {
         load_h(s + 1, hr);
         load_w(s + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage\'s math
         compute(s, cur);
         store_h(s + 1, hr);
         __syncthreads();

@@ -65,7 +65,8 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     constexpr int SLOTS = kWave / MR;  // row groups whose results one epilogue pass holds
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int wave_id = blockIdx.x * wpb + threadIdx.x / kWave;
+    // wave-uniform, stated so that the stage loop compiles to scalar control flow
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + threadIdx.x / kWave);
     const int nwaves = gridDim.x * wpb;
     const int nchunks = K >> 3;
     const u32x4* h4 = reinterpret_cast<const u32x4*>(hidden);
@@ -118,22 +119,22 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
 
     float ag[M][R], au[M][R];
     float resG = 0.0f, resU = 0.0f;
-    int slot = 0;
-    int window_g0 = 0;  // index (in this wave's sequence) of the first group held in slots
 
-    auto flush = [&]() {
-        if (lane < slot * MR) {
+    // Results of group gi sit in lanes (gi % SLOTS)*MR + m*R + r; the epilogue
+    // runs when a window of SLOTS groups is full or the last group is done.
+    // Both follow from the group index alone (no loop-carried counter).
+    auto flush = [&](int gi_last) {
+        const int win0 = gi_last - gi_last % SLOTS;
+        if (lane < (gi_last - win0 + 1) * MR) {
             const int gl = lane / MR;
             const int rem = lane - gl * MR;
             const int m = rem / R;
             const int r = rem - m * R;
-            const int row = (wave_id + (window_g0 + gl) * nwaves) * R + r;
+            const int row = (wave_id + (win0 + gl) * nwaves) * R + r;
             if (row < N) {
                 out[(int64_t)m * ldo + row] = glu_epilogue(resG, resU);
             }
         }
-        window_g0 += slot;
-        slot = 0;
     };
 
     // the chunks of batch B (a compile-time index, so hidden registers are never indexed at run time)
@@ -187,6 +188,7 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             }
         }
         if (b == NB - 1) {
+            const int slot = gi % SLOTS;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
 #pragma unroll
@@ -199,8 +201,7 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
                     }
                 }
             }
-            ++slot;
-            if (slot == SLOTS) flush();
+            if (slot == SLOTS - 1 || gi == my_groups - 1) flush(gi);
         }
     };
 
@@ -213,6 +214,7 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             break;
         }
         load(s + 1, bG, bU);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage\'s math
         compute(s, aG, aU);
         ++s;
         if (s + 1 >= nstages) {
@@ -220,10 +222,10 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             break;
         }
         load(s + 1, aG, aU);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage\'s math
         compute(s, bG, bU);
         ++s;
     }
-    if (slot > 0) flush();
 }
 
 template <int M, int R, int U, int NB, bool RAGGED>

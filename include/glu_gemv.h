@@ -62,9 +62,9 @@ typedef enum glu_status {
  *
  * M >= 0, N >= 0, K >= 0.  M == 0 or N == 0: nothing to do, GLU_OK, pointers
  * unchecked.  K == 0: every output is +0 (the empty sums give silu(0) * 0).
- * Fast path: hidden, gate_w and up_w 16-byte aligned and K a multiple of 8;
- * any other 2-byte-aligned input takes a slower path with the same result
- * contract.  M == 1 with K <= 4096 runs a VALU GEMV; other shapes run a
+ * Fast path: hidden, gate_w and up_w 16-byte aligned, K a multiple of 8 and
+ * K <= 2^25; any other 2-byte-aligned input takes a slower path with the same
+ * result contract.  M == 1 with K <= 4096 runs a VALU GEMV; other shapes run a
  * block-diagonal MFMA kernel; M > 32 is processed in slices of 32 rows of
  * hidden (one launch per slice, each streaming the weights again).
  */
@@ -99,7 +99,7 @@ enum {
     GLU_KERNEL_ZERO = 1,    /* K == 0: fill out with +0 */
     GLU_KERNEL_VALU = 2,    /* M == 1, K <= 4096, fast path (any M <= 8 on request) */
     GLU_KERNEL_MFMA = 3,    /* other fast-path shapes (slices of 32 rows of hidden) */
-    GLU_KERNEL_GENERIC = 4  /* unaligned or K % 8 != 0 */
+    GLU_KERNEL_GENERIC = 4  /* unaligned, K % 8 != 0 or K > 2^25 */
 };
 
 glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan);

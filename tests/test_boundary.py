@@ -65,6 +65,8 @@ def test_version_and_strings(lib):
     (20, 100, 1003, True, api.KERNEL_GENERIC, 3),
     (1, 100, 65536, True, api.KERNEL_MFMA, 1),       # K past the VALU path's 16 chunks per lane
     (4, 100, 9000, True, api.KERNEL_MFMA, 1),
+    (32, 4, 1 << 25, True, api.KERNEL_MFMA, 1),       # 32-bit byte offsets cover 32 rows of K
+    (32, 4, (1 << 25) + 8, True, api.KERNEL_GENERIC, 4),
 ])
 def test_plan(lib, M, N, K, aligned, kernel, launches):
     p = api.plan(M, N, K, aligned)
