@@ -319,7 +319,8 @@ glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16
     case GLU_KERNEL_MFMA: {
         const glu::MfmaConfig& c = L.mfma;
         if (c.hidden == glu::kHiddenSlices) {
-            snprintf(buf, (size_t)len, "glu::mfma_slice_kernel<%d, %d, %s>", c.MT4, c.U, tf[c.ragged]);
+            snprintf(buf, (size_t)len, "glu::mfma_slice_kernel<%d, %d, %d, %s>", c.MT4, c.U,
+                     glu::mfma_slice_depth(c.U), tf[c.ragged]);
         } else {
             snprintf(buf, (size_t)len, "glu::mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,
                      tf[c.hidden == glu::kHiddenLds], tf[c.ragged]);

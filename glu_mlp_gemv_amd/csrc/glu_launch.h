@@ -59,6 +59,8 @@ hipError_t valu_launch(const ValuConfig& c, const uint16_t* hidden, const uint16
 
 bool mfma_supported(const MfmaConfig& c);
 size_t mfma_slice_lds_bytes(int mt4, int u);
+// weight stages the lockstep kernel keeps in flight for U segments per stage
+int mfma_slice_depth(int u);
 size_t mfma_hidden_lds_bytes(int m, int64_t k);
 hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,

@@ -213,13 +213,28 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
 
 // The same block-diagonal product when hidden does not fit in LDS: the W = 4
 // waves of a workgroup take the 4 adjacent row groups of a block and advance
-// through K in lockstep, one stage at a time, and the workgroup stages only
-// the K-slice of hidden that the stage needs (all M rows, U segments) in a
-// double-buffered LDS ring.  The hidden loads of stage s+1 are issued before
-// its weight loads, so waiting for them never waits for the weights; one
-// barrier per stage separates the slice writes from the reads.
+// through K in lockstep, one stage of U segments at a time, and the workgroup
+// keeps only the K-slice of hidden that a stage needs (all M rows) in a
+// double-buffered LDS ring.  What keeps HBM busy is the depth of the weight
+// pipeline: the weights of stage s+DW are issued at stage s (DW*U segments,
+// 2*DW*U KiB per wave, in flight), and the hidden slice of stage s+2 is
+// loaded at stage s and written to LDS at the end of stage s+1, so neither
+// the L2 latency of hidden nor the HBM latency of the weights sits between
+// two stages.  One barrier per stage separates the slice writes from reads.
 // Dynamic LDS: 2 * 4*MT4 * U*16 * 16 bytes.  blockDim.x == 256.
-template <int MT4, int U, bool RAGGED>
+// calls f(integral_constant<Q>, s0 + Q) for Q = Q0 .. L-1 while s0 + Q < n
+template <int Q, int L, class F>
+__device__ __forceinline__ void run_stages(F& f, int s0, int n)
+{
+    if constexpr (Q < L) {
+        if (s0 + Q < n) {
+            f(std::integral_constant<int, Q>{}, s0 + Q);
+            run_stages<Q + 1, L>(f, s0, n);
+        }
+    }
+}
+
+template <int MT4, int U, int DW, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
                   const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
@@ -229,6 +244,8 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     constexpr int MP = 4 * MT4;                            // hidden rows in a slice (padded)
     constexpr int SC = U * 16;                             // 16-byte chunks of one row in a slice
     constexpr int HPT = (MP * SC + kMfmaMaxThreads - 1) / kMfmaMaxThreads;  // slice loads per thread
+    constexpr int NB = DW + 1;                             // weight stages held in registers
+    constexpr int L = NB % 2 == 0 ? NB : 2 * NB;           // unrolled stages: buffer and parity static
     extern __shared__ u32x4_t hs[];                        // [2][MP][SC], chunk c of row r at c ^ (r & 3)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -244,9 +261,9 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     const int my_blocks = (nblocks - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
     const int nstages = my_blocks * nsg;  // the same for every wave of the workgroup
 
-    auto group_of = [&](int s) { return ((int)blockIdx.x + (s / nsg) * (int)gridDim.x) * W + wave; };
+    auto group_of = [&](int s) __attribute__((always_inline)) { return ((int)blockIdx.x + (s / nsg) * (int)gridDim.x) * W + wave; };
 
-    auto load_h = [&](int s, u32x4_t (&hr)[HPT]) {
+    auto load_h = [&](int s, u32x4_t (&hr)[HPT]) __attribute__((always_inline)) {
         const int sb = s % nsg;
 #pragma unroll
         for (int i = 0; i < HPT; ++i) {
@@ -254,19 +271,19 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
             const int m = min(e / SC, M - 1);  // padded rows repeat row M-1, never stored
             int c = sb * SC + (e % SC);
             if (RAGGED) c = min(c, nchunks - 1);
-            hr[i] = h4[(int64_t)m * nchunks + c];
+            hr[i] = h4[(uint32_t)m * (uint32_t)nchunks + (uint32_t)c];
         }
     };
-    auto store_h = [&](int s, const u32x4_t (&hr)[HPT]) {
+    auto store_h = [&](int s, const u32x4_t (&hr)[HPT]) __attribute__((always_inline)) {
         u32x4_t* dst = hs + (s & 1) * MP * SC;
 #pragma unroll
         for (int i = 0; i < HPT; ++i) {
             const int e = i * kMfmaMaxThreads + (int)threadIdx.x;
             // XOR swizzle: the 4 rows one read touches land in different banks
-            if (e < MP * SC) dst[e ^ ((e / SC) & 3)] = hr[i];
+            if ((MP * SC) % kMfmaMaxThreads == 0 || e < MP * SC) dst[e ^ ((e / SC) & 3)] = hr[i];
         }
     };
-    auto load_w = [&](int s, u32x4_t (&A)[2][U]) {
+    auto load_w = [&](int s, u32x4_t (&A)[2][U]) __attribute__((always_inline)) {
         const int sb = s % nsg;
         // the last workgroup's waves can sit past the last group when the group
         // count is not a multiple of W: they re-read the last group, never stored
@@ -287,7 +304,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
 
     f32x4_t acc[MT4][2];
 
-    auto finish_group = [&](int g) {
+    auto finish_group = [&](int g) __attribute__((always_inline)) {
         const int e = lane & 3;
         float res[2][(MT4 + 3) / 4];
 #pragma unroll
@@ -312,7 +329,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
         }
     };
 
-    auto compute = [&](int s, const u32x4_t (&A)[2][U]) {
+    auto compute = [&](int s, const u32x4_t (&A)[2][U]) __attribute__((always_inline)) {
         const int sb = s % nsg;
         if (sb == 0) {
 #pragma unroll
@@ -323,51 +340,63 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
         }
         const u32x4_t* src = hs + (s & 1) * MP * SC;
         const u32x4_t z = {0u, 0u, 0u, 0u};
+        // all MT4 hidden operands of a segment are read before its MFMAs, so
+        // the LDS latency is paid once per segment rather than once per tile
+        u32x4_t b[2][MT4];
+        auto read_b = [&](int u, u32x4_t (&bt)[MT4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) bt[t] = src[(4 * t + rho_a) * SC + ((u * 16 + cseg) ^ rho_a)];
+        };
+        read_b(0, b[0]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (u + 1 < U) read_b(u + 1, b[(u + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);  // the next segment's reads stay ahead of these MFMAs
             const bool ok = !RAGGED || (sb * U + u) * 16 + cseg < nchunks;
             const u32x4_t ag = RAGGED ? (ok ? A[0][u] : z) : A[0][u];
             const u32x4_t au = RAGGED ? (ok ? A[1][u] : z) : A[1][u];
 #pragma unroll
             for (int t = 0; t < MT4; ++t) {
-                u32x4_t b = src[(4 * t + rho_a) * SC + ((u * 16 + cseg) ^ rho_a)];
-                if constexpr (RAGGED) b = ok ? b : z;
-                acc[t][0] = mfma16(ag, b, acc[t][0]);
-                acc[t][1] = mfma16(au, b, acc[t][1]);
+                u32x4_t bt = b[u & 1][t];
+                if constexpr (RAGGED) bt = ok ? bt : z;
+                acc[t][0] = mfma16(ag, bt, acc[t][0]);
+                acc[t][1] = mfma16(au, bt, acc[t][1]);
             }
         }
         if (sb == nsg - 1) finish_group(group_of(s));
     };
 
-    // one full step: prefetch stage s+1 (hidden slice, then weights), compute s,
-    // publish the slice of s+1, and wait for the whole workgroup
-    u32x4_t hr[HPT];
-    auto step = [&](int s, const u32x4_t (&cur)[2][U], u32x4_t (&nxt)[2][U]) {
-        load_h(s + 1, hr);
-        load_w(s + 1, nxt);
-        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage\'s math
-        compute(s, cur);
-        store_h(s + 1, hr);
+    u32x4_t A[NB][2][U];  // weights of stage s live in A[s % NB]
+    u32x4_t hr[2][HPT];   // hidden slice of stage s lives in hr[s % 2] from stage s-2 to s-1
+
+    // stage s at unrolled position Q = s % L: prefetch, compute, publish, wait.
+    // In the steady state (TAIL false) every prefetch is live and nothing
+    // branches around a load, so the waits can leave all prefetches in flight;
+    // the last stages (TAIL true) skip what lies past the end.
+    auto stage = [&](auto Qc, auto tailc, int s) __attribute__((always_inline)) {
+        constexpr int Q = decltype(Qc)::value;
+        constexpr bool TAIL = decltype(tailc)::value;
+        if (!TAIL || s + 2 < nstages) load_h(s + 2, hr[Q % 2]);     // hr[s % 2] was published at s-1
+        if (!TAIL || s + DW < nstages) load_w(s + DW, A[(Q + DW) % NB]);  // consumed at s-1
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage's math
+        compute(s, A[Q % NB]);
+        if (!TAIL || s + 1 < nstages) store_h(s + 1, hr[(Q + 1) % 2]);
         __syncthreads();
     };
+    auto steady = [&](auto Qc, int s) __attribute__((always_inline)) { stage(Qc, std::false_type{}, s); };
+    auto tail = [&](auto Qc, int s) __attribute__((always_inline)) { stage(Qc, std::true_type{}, s); };
 
-    u32x4_t a0[2][U], a1[2][U];
-    load_h(0, hr);
-    load_w(0, a0);
-    store_h(0, hr);
+    load_h(0, hr[0]);
+    if (1 < nstages) load_h(1, hr[1]);
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+        if (j < nstages) load_w(j, A[j]);
+    }
+    store_h(0, hr[0]);
     __syncthreads();
-    int s = 0;
-    while (s + 2 < nstages) {
-        step(s, a0, a1);
-        step(s + 1, a1, a0);
-        s += 2;
-    }
-    if (s + 1 < nstages) {
-        step(s, a0, a1);
-        compute(s + 1, a1);
-    } else {
-        compute(s, a0);
-    }
+    int s0 = 0;
+    for (; s0 + L + DW <= nstages; s0 += L) run_stages<0, L>(steady, s0, nstages);
+    for (; s0 < nstages; s0 += L) run_stages<0, L>(tail, s0, nstages);
 }
 
 namespace {
@@ -389,9 +418,10 @@ MfmaFn pick_u(int U)
 template <int MT4, bool RG>
 MfmaFn pick_slice_u(int U)
 {
+    // weights of slice_depth(U) stages in flight: 8 segments, 16 KiB per wave
     switch (U) {
-    case 2: return mfma_slice_kernel<MT4, 2, RG>;
-    case 4: return mfma_slice_kernel<MT4, 4, RG>;
+    case 2: return mfma_slice_kernel<MT4, 2, 4, RG>;
+    case 4: return mfma_slice_kernel<MT4, 4, 2, RG>;
     default: return nullptr;
     }
 }
@@ -427,6 +457,8 @@ MfmaFn pick(const MfmaConfig& c)
 }  // namespace
 
 size_t mfma_slice_lds_bytes(int mt4, int u) { return (size_t)2 * 4 * mt4 * u * 16 * 16; }
+
+int mfma_slice_depth(int u) { return u > 0 ? 8 / u : 0; }
 
 size_t mfma_hidden_lds_bytes(int m, int64_t k)
 {

@@ -79,7 +79,7 @@ def test_plan(lib, M, N, K, aligned, kernel, launches):
 def test_describe_names_the_instantiated_kernel(lib):
     assert api.plan(1, 9216, 2560)["kernel_symbol"] == "glu::valu_kernel<1, 1, 5, 1, false, false>"
     assert api.plan(8, 12288, 4096)["kernel_symbol"] == "glu::mfma_kernel<2, 4, true, false>"
-    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<8, 4, false>"
+    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<8, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
     assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
 
