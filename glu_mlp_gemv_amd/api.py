@@ -56,7 +56,8 @@ class Plan(ctypes.Structure):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("rows_per_wave", ctypes.c_int), ("waves_per_block", ctypes.c_int),
-                ("grid", ctypes.c_int), ("mfma_segments", ctypes.c_int), ("mfma_hidden", ctypes.c_int)]
+                ("grid", ctypes.c_int), ("mfma_segments", ctypes.c_int), ("mfma_hidden", ctypes.c_int),
+                ("mfma_depth", ctypes.c_int)]
 
 
 _LIB: Optional[ctypes.CDLL] = None

@@ -116,6 +116,8 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     const int seg_req = t ? t->mfma_segments : 0;
     if (t && t->mfma_hidden) {
         c.hidden = t->mfma_hidden - 1;
+    } else if (t && t->rows_per_wave == 8) {
+        c.hidden = glu::kHiddenSlices;  // the only place 8 rows per wave are built for
     } else if (glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsBudget) {
         c.hidden = glu::kHiddenLds;
     } else if (waves * glu::kWave == glu::kMfmaMaxThreads && (seg_req == 0 || seg_req == 2 || seg_req == 4)) {
@@ -123,13 +125,34 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     } else {
         c.hidden = glu::kHiddenL2;
     }
-    c.U = (t && t->mfma_segments) ? t->mfma_segments : default_segments(nsegs, c.MT4, c.hidden);
+    // 8 weight rows per wave halve the MFMAs, operand reads and hidden-slice
+    // traffic per weight byte, which pays once the slices carry more than 8
+    // rows of hidden; below that 4 rows stream the weights faster
+    const bool seg8 = seg_req == 0 || seg_req == 4 || seg_req == 8;  // stage sizes built for 8 rows
+    const int rows_dflt = (c.hidden == glu::kHiddenSlices && m_pl > 8 && seg8) ? 8 : 4;
+    c.rows = (t && t->rows_per_wave) ? t->rows_per_wave : rows_dflt;
+    if (c.rows != 4 && !(c.rows == 8 && c.hidden == glu::kHiddenSlices)) return GLU_ERR_UNSUPPORTED;
+    // segments of 128 K-elements at 4 rows per wave, of 64 at 8
+    const int64_t seg_chunks = c.rows == 8 ? 8 : 16;
+    const int64_t nseg = ceil_div(nchunks, seg_chunks);
+    if (c.rows == 8) {
+        c.U = (t && t->mfma_segments) ? t->mfma_segments : 8;
+    } else {
+        c.U = (t && t->mfma_segments) ? t->mfma_segments : default_segments(nsegs, c.MT4, c.hidden);
+    }
     if (c.U < 1) return GLU_ERR_UNSUPPORTED;
-    c.nsg = (int)ceil_div(nsegs, c.U);
-    c.ragged = (int64_t)c.nsg * c.U * 16 != nchunks;
+    if (c.hidden == glu::kHiddenSlices) {
+        int dflt = c.rows == 8 ? glu::mfma8_slice_depth(c.U) : glu::mfma_slice_depth(c.U);
+        if (c.rows == 8 && c.U == 8 && m_pl <= 16) dflt = 2;  // fewer MFMAs per stage: room for a deeper pipeline
+        c.depth = (t && t->mfma_depth) ? t->mfma_depth : dflt;
+    } else if (t && t->mfma_depth) {
+        return GLU_ERR_UNSUPPORTED;  // only the lockstep kernels take a depth
+    }
+    c.nsg = (int)ceil_div(nseg, c.U);
+    c.ragged = (int64_t)c.nsg * c.U * seg_chunks != nchunks;
     if (waves < 1 || waves * glu::kWave > glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
     c.block = waves * glu::kWave;
-    const int64_t groups = ceil_div(N, 4);
+    const int64_t groups = ceil_div(N, c.rows);
     int64_t grid;
     if (t && t->grid > 0) {
         grid = t->grid;
@@ -147,10 +170,11 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     L->m_per_launch = (int)m_pl;
     L->launches = (int)ceil_div(M, m_pl);
     // per output lane: one MFMA per segment, each adding a 32-product block
-    // (a summation tree of depth 5) to the accumulator, then two quad additions;
-    // the matrix core's internal rounding is not specified, so every step is
-    // counted at twice the fp32 unit roundoff (a truncating adder)
-    L->accum_depth = (int)(2 * (nsegs + 5 + 2));
+    // (a summation tree of depth 5) to the accumulator, then the block sums
+    // (two quad additions at 4 rows, one pair addition at 8); the matrix
+    // core's internal rounding is not specified, so every step is counted at
+    // twice the fp32 unit roundoff (a truncating adder)
+    L->accum_depth = (int)(2 * (nseg + 5 + 2));
     return GLU_OK;
 }
 
@@ -318,9 +342,12 @@ glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16
     }
     case GLU_KERNEL_MFMA: {
         const glu::MfmaConfig& c = L.mfma;
-        if (c.hidden == glu::kHiddenSlices) {
+        if (c.hidden == glu::kHiddenSlices && c.rows == 8) {
+            snprintf(buf, (size_t)len, "glu::mfma8_slice_kernel<%d, %d, %d, %s>", (4 * c.MT4 + 7) / 8, c.U,
+                     c.depth, tf[c.ragged]);
+        } else if (c.hidden == glu::kHiddenSlices) {
             snprintf(buf, (size_t)len, "glu::mfma_slice_kernel<%d, %d, %d, %s>", c.MT4, c.U,
-                     glu::mfma_slice_depth(c.U), tf[c.ragged]);
+                     c.depth, tf[c.ragged]);
         } else {
             snprintf(buf, (size_t)len, "glu::mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,
                      tf[c.hidden == glu::kHiddenLds], tf[c.ragged]);

@@ -29,11 +29,13 @@ constexpr int kHiddenL2 = 1;      // read from L2 with each stage's weights
 constexpr int kHiddenSlices = 2;  // per-stage K-slices in an LDS ring, waves in lockstep
 
 struct MfmaConfig {
+    int rows;         // weight rows per wave: 4, or 8 (kHiddenSlices only)
     int MT4;          // hidden-row tiles of 4 (M <= 4 * MT4 <= 32)
-    int U;            // 128-element K segments per pipeline stage
-    int nsg;          // stages per group of 4 weight rows: nsg * U * 16 >= K / 8
-    bool ragged;      // nsg * U * 16 > K / 8: clamp and zero the excess chunks
+    int U;            // K segments per pipeline stage: 128 elements at 4 rows, 64 at 8
+    int nsg;          // stages per row group: nsg * U * seg >= K, seg = 128 or 64
+    bool ragged;      // the stages run past K: clamp and zero the excess chunks
     int hidden;       // kHiddenLds, kHiddenL2 or kHiddenSlices
+    int depth;        // kHiddenSlices: pipeline stages of weights in flight
     int grid;         // workgroups (persistent)
     int block;        // threads per workgroup (multiple of 64)
 };
@@ -59,9 +61,16 @@ hipError_t valu_launch(const ValuConfig& c, const uint16_t* hidden, const uint16
 
 bool mfma_supported(const MfmaConfig& c);
 size_t mfma_slice_lds_bytes(int mt4, int u);
-// weight stages the lockstep kernel keeps in flight for U segments per stage
+// default weight stages the lockstep kernel keeps in flight for U segments per stage
 int mfma_slice_depth(int u);
 size_t mfma_hidden_lds_bytes(int m, int64_t k);
+// the 8-row lockstep kernel (glu_mfma8.hip): mt8 hidden tiles of 8 rows
+size_t mfma8_slice_lds_bytes(int mt8, int u);
+int mfma8_slice_depth(int u);
+bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block);
+hipError_t mfma8_launch(int M, int U, int depth, int nsg, bool ragged, int grid, const uint16_t* hidden,
+                        const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K,
+                        int64_t ldo, hipStream_t stream);
 hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
                        hipStream_t stream);

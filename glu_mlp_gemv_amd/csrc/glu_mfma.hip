@@ -28,22 +28,10 @@
 // before the MFMAs of stage s.  hidden [M,K] is staged in LDS when it fits in
 // 64 KiB, else read from L2 with each stage's weights.  MFMA work is 1/4 useful, which still
 // leaves the matrix cores far from busy at M <= 32.
-#include <type_traits>
-
 #include "glu_device.h"
-#include "glu_launch.h"
+#include "glu_mfma_common.h"
 
 namespace glu {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 // MT4: hidden-row tiles of 4 (M <= 4*MT4); U: 128-element segments per stage;
 // nsg: stages per group (nsg * U * 16 >= K/8, equality unless RAGGED).
@@ -66,16 +54,16 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     const int cseg = (i16 & 3) * 4 + (lane >> 4);  // 16-byte chunk within a 256-byte segment
     const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
 
-    // the 4 hidden rows one read touches must fall in different LDS banks: chunk
-    // c of row m sits at c ^ (m & 3) when K/8 is a multiple of 4, else rows are
-    // padded by one chunk
+    // the hidden rows one read touches must fall in different LDS banks: chunk
+    // c of row m sits at c ^ lds_swz4(m) when K/8 is a multiple of 4, else rows
+    // are padded by one chunk
     const bool hswz = (nchunks & 3) == 0;
     const int hpitch = hswz ? nchunks : nchunks + 1;
     if constexpr (HLDS) {
         for (int i = threadIdx.x; i < M * nchunks; i += blockDim.x) {
             const int m = i / nchunks;
             const int c = i - m * nchunks;
-            h_lds[m * hpitch + (hswz ? c ^ (m & 3) : c)] = h4[i];
+            h_lds[m * hpitch + (hswz ? c ^ lds_swz4(m) : c)] = h4[i];
         }
         __syncthreads();
     }
@@ -176,7 +164,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
             for (int t = 0; t < MT4; ++t) {
                 u32x4_t b;
                 if constexpr (HLDS) {
-                    b = h_lds[hrow[t] * hpitch + (hswz ? cc ^ (hrow[t] & 3) : cc)];
+                    b = h_lds[hrow[t] * hpitch + (hswz ? cc ^ lds_swz4(hrow[t]) : cc)];
                 } else {
                     b = Bq[t][u];
                 }
@@ -222,18 +210,6 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
 // the L2 latency of hidden nor the HBM latency of the weights sits between
 // two stages.  One barrier per stage separates the slice writes from reads.
 // Dynamic LDS: 2 * 4*MT4 * U*16 * 16 bytes.  blockDim.x == 256.
-// calls f(integral_constant<Q>, s0 + Q) for Q = Q0 .. L-1 while s0 + Q < n
-template <int Q, int L, class F>
-__device__ __forceinline__ void run_stages(F& f, int s0, int n)
-{
-    if constexpr (Q < L) {
-        if (s0 + Q < n) {
-            f(std::integral_constant<int, Q>{}, s0 + Q);
-            run_stages<Q + 1, L>(f, s0, n);
-        }
-    }
-}
-
 template <int MT4, int U, int DW, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
@@ -246,7 +222,8 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     constexpr int HPT = (MP * SC + kMfmaMaxThreads - 1) / kMfmaMaxThreads;  // slice loads per thread
     constexpr int NB = DW + 1;                             // weight stages held in registers
     constexpr int L = NB % 2 == 0 ? NB : 2 * NB;           // unrolled stages: buffer and parity static
-    extern __shared__ u32x4_t hs[];                        // [2][MP][SC], chunk c of row r at c ^ (r & 3)
+    constexpr int AHEAD = DW > 2 ? DW : 2;                 // farthest prefetch, in stages
+    extern __shared__ u32x4_t hs[];                        // [2][MP][SC], chunk c of row r at c ^ lds_swz4(r)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int nchunks = K >> 3;
@@ -279,8 +256,8 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
 #pragma unroll
         for (int i = 0; i < HPT; ++i) {
             const int e = i * kMfmaMaxThreads + (int)threadIdx.x;
-            // XOR swizzle: the 4 rows one read touches land in different banks
-            if ((MP * SC) % kMfmaMaxThreads == 0 || e < MP * SC) dst[e ^ ((e / SC) & 3)] = hr[i];
+            // XOR swizzle: the rows one read touches land in different banks
+            if ((MP * SC) % kMfmaMaxThreads == 0 || e < MP * SC) dst[e ^ lds_swz4(e / SC)] = hr[i];
         }
     };
     auto load_w = [&](int s, u32x4_t (&A)[2][U]) __attribute__((always_inline)) {
@@ -345,7 +322,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
         u32x4_t b[2][MT4];
         auto read_b = [&](int u, u32x4_t (&bt)[MT4]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int t = 0; t < MT4; ++t) bt[t] = src[(4 * t + rho_a) * SC + ((u * 16 + cseg) ^ rho_a)];
+            for (int t = 0; t < MT4; ++t) bt[t] = src[(4 * t + rho_a) * SC + ((u * 16 + cseg) ^ lds_swz4(rho_a))];
         };
         read_b(0, b[0]);
 #pragma unroll
@@ -395,7 +372,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     store_h(0, hr[0]);
     __syncthreads();
     int s0 = 0;
-    for (; s0 + L + DW <= nstages; s0 += L) run_stages<0, L>(steady, s0, nstages);
+    for (; s0 + L + AHEAD <= nstages; s0 += L) run_stages<0, L>(steady, s0, nstages);
     for (; s0 < nstages; s0 += L) run_stages<0, L>(tail, s0, nstages);
 }
 
@@ -416,14 +393,12 @@ MfmaFn pick_u(int U)
 }
 
 template <int MT4, bool RG>
-MfmaFn pick_slice_u(int U)
+MfmaFn pick_slice_u(int U, int depth)
 {
-    // weights of slice_depth(U) stages in flight: 8 segments, 16 KiB per wave
-    switch (U) {
-    case 2: return mfma_slice_kernel<MT4, 2, 4, RG>;
-    case 4: return mfma_slice_kernel<MT4, 4, 2, RG>;
-    default: return nullptr;
-    }
+    // 8 segments (16 KiB per wave) of weights in flight
+    if (U == 2 && depth == 4) return mfma_slice_kernel<MT4, 2, 4, RG>;
+    if (U == 4 && depth == 2) return mfma_slice_kernel<MT4, 4, 2, RG>;
+    return nullptr;
 }
 
 template <int MT4>
@@ -434,7 +409,7 @@ MfmaFn pick_flags(const MfmaConfig& c)
     case kHiddenL2: return c.ragged ? pick_u<MT4, false, true>(c.U) : pick_u<MT4, false, false>(c.U);
     case kHiddenSlices:
         if (c.block != kMfmaMaxThreads) return nullptr;
-        return c.ragged ? pick_slice_u<MT4, true>(c.U) : pick_slice_u<MT4, false>(c.U);
+        return c.ragged ? pick_slice_u<MT4, true>(c.U, c.depth) : pick_slice_u<MT4, false>(c.U, c.depth);
     default: return nullptr;
     }
 }
@@ -468,6 +443,10 @@ size_t mfma_hidden_lds_bytes(int m, int64_t k)
 
 bool mfma_supported(const MfmaConfig& c)
 {
+    if (c.rows == 8) {
+        return c.hidden == kHiddenSlices && mfma8_supported((4 * c.MT4 + 7) / 8, c.U, c.depth, c.ragged, c.block);
+    }
+    if (c.rows != 4) return false;
     if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
     if (c.hidden == kHiddenSlices && mfma_slice_lds_bytes(c.MT4, c.U) > (size_t)kLdsBudget) return false;
     return pick(c) != nullptr;
@@ -477,6 +456,10 @@ hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const
                        const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
                        hipStream_t stream)
 {
+    if (c.rows == 8) {
+        if (c.hidden != kHiddenSlices) return hipErrorInvalidValue;
+        return mfma8_launch(M, c.U, c.depth, c.nsg, c.ragged, c.grid, hidden, gate_w, up_w, out, N, K, ldo, stream);
+    }
     MfmaConfig cm = c;
     cm.MT4 = (M + 3) / 4;
     MfmaFn fn = pick(cm);

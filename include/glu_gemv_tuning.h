@@ -21,13 +21,19 @@ extern "C" {
 
 typedef struct glu_tuning {
     int kernel;           /* 0 = automatic, else GLU_KERNEL_VALU / _MFMA / _GENERIC */
-    int rows_per_wave;    /* VALU: output rows per wave per group (1; 2 at M = 1) */
+    int rows_per_wave;    /* VALU: output rows per wave per group (1; 2 at M = 1).
+                             MFMA: weight rows per wave, 4, or 8 with mfma_hidden = 3 */
     int waves_per_block;  /* VALU, MFMA: waves per workgroup (1..8) */
     int grid;             /* VALU, MFMA: workgroups of the persistent grid */
-    int mfma_segments;    /* MFMA: 128-element K segments per pipeline stage (2, 4, 5, 8) */
+    int mfma_segments;    /* MFMA: K segments per pipeline stage; a segment is 128
+                             elements at 4 rows per wave (2, 4, 5, 8), 64 at 8 (4, 8) */
     int mfma_hidden;      /* MFMA: where hidden lives: 1 = all in LDS (M*K*2 <= 64 KiB),
                              2 = read from L2 per stage, 3 = per-stage K-slices in LDS
-                             with the workgroup's 4 waves in lockstep (segments 2 or 4) */
+                             with the workgroup's 4 waves in lockstep (segments 2 or 4
+                             at 4 rows per wave) */
+    int mfma_depth;       /* MFMA with mfma_hidden = 3: pipeline stages of weights kept
+                             in flight (4 rows: 4 at 2 segments, 2 at 4; 8 rows: 2 or 4
+                             at 4 segments, 1 or 2 at 8) */
 } glu_tuning;
 
 glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,

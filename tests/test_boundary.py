@@ -79,7 +79,8 @@ def test_plan(lib, M, N, K, aligned, kernel, launches):
 def test_describe_names_the_instantiated_kernel(lib):
     assert api.plan(1, 9216, 2560)["kernel_symbol"] == "glu::valu_kernel<1, 1, 5, 1, false, false>"
     assert api.plan(8, 12288, 4096)["kernel_symbol"] == "glu::mfma_kernel<2, 4, true, false>"
-    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<8, 4, 2, false>"
+    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma8_slice_kernel<4, 8, 1, false>"
+    assert api.plan(8, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<2, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
     assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
 
@@ -166,3 +167,16 @@ def test_python_face_rejects_cpu_tensors():
         api.dual_gemv(h, w, w)
     with pytest.raises(TypeError):
         api.dual_gemv(h.float(), w, w)
+
+
+def test_every_tuned_gpu_case_plans(lib):
+    """Each launch-shape override the GPU parity tests use must plan on the host (no GPU needed)."""
+    from cases import EPILOGUE_PATHS, MFMA_SHAPES, MFMA_TUNINGS, SMALL
+    for M, N, K in MFMA_SHAPES:
+        for kw in MFMA_TUNINGS:
+            p = api.plan(M, N, K, True, api.make_tuning(kernel=api.KERNEL_MFMA, **kw))
+            assert p["kernel"] == api.KERNEL_MFMA, (M, N, K, kw)
+    for M, N, K in SMALL:
+        assert api.plan(M, N, K, True, api.make_tuning(kernel=api.KERNEL_VALU))["kernel"] == api.KERNEL_VALU
+    for kw in EPILOGUE_PATHS.values():
+        api.plan(1, 1 << 16, 8, True, api.make_tuning(**kw))

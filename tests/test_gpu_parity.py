@@ -13,6 +13,7 @@ import torch
 import oracle
 from oracle import check
 from glu_mlp_gemv_amd import api, inputs
+from cases import EPILOGUE_PATHS, MFMA_SHAPES, MFMA_TUNINGS, SMALL
 
 pytestmark = pytest.mark.gpu
 
@@ -90,9 +91,6 @@ def test_decode_stack_parity():
 
 # ---- ragged and small shapes, every kernel ------------------------------------
 
-SMALL = [(1, 1, 8), (1, 3, 8), (1, 65, 64), (1, 3000, 1024), (2, 777, 520), (3, 1000, 4104),
-         (5, 129, 2560), (8, 3000, 1024), (8, 640, 8192), (1, 100, 8192), (1, 300, 5128), (2, 257, 6144),
-         (4, 1000, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
@@ -103,12 +101,6 @@ def test_small_valu(M, N, K):
     assert rep.ok, rep.summary()
 
 
-MFMA_SHAPES = [(9, 100, 512), (16, 17, 64), (16, 1000, 1032), (17, 333, 2560), (32, 3000, 1024),
-               (31, 64, 5120), (33, 200, 520), (70, 1000, 1024), (4, 999, 1024), (1, 2000, 2560),
-               (2, 100, 40000), (8, 700, 8)]
-MFMA_TUNINGS = [dict(), dict(mfma_segments=2), dict(mfma_segments=8, waves_per_block=2),
-                dict(grid=3, waves_per_block=1), dict(mfma_hidden=2), dict(mfma_hidden=3),
-                dict(mfma_hidden=3, mfma_segments=2, grid=2)]
 
 
 @pytest.mark.parametrize("tn", range(len(MFMA_TUNINGS)))
@@ -179,8 +171,6 @@ def _epilogue_case(u_bits: np.ndarray, tuning):
     return got.ravel(), ref.ravel(), g_bits
 
 
-EPILOGUE_PATHS = {"valu": dict(kernel=api.KERNEL_VALU), "generic": dict(kernel=api.KERNEL_GENERIC),
-                  "mfma": dict(kernel=api.KERNEL_MFMA)}
 
 
 @pytest.mark.parametrize("path", list(EPILOGUE_PATHS))
