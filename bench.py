@@ -157,6 +157,35 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
             del g
         del pool
         torch.cuda.empty_cache()
+    # row-strided operands: gate and up as the two column halves of one fused
+    # [N, 2K] block (each keeps the fused row stride 2K), at the decode shape
+    N, K = STACK["N"], STACK["K"]
+    sets = max(4, -(-1_400_000_000 // (2 * N * K * 2)))
+    fused = [torch.cat(inputs.weights(N, K, 300 + i, device=dev), dim=1) for i in range(sets)]
+    for layout in ("packed", "fused"):
+        # the same weights, as two packed copies or as the two halves of the fused block
+        ops = ([(f[:, :K].contiguous(), f[:, K:].contiguous()) for f in fused] if layout == "packed"
+               else [(f[:, :K], f[:, K:]) for f in fused])
+        for M in (1, 4):
+            h = inputs.hidden(M, K, 0).to(dev)
+            out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+            def one_pass():
+                for wg, wu in ops:
+                    api.dual_gemv(h, wg, wu, out=out)
+            g = capture(torch, one_pass)
+            ms = time_region(torch, g.replay, reps, 2, stream)
+            us = ms * 1e3 / (reps * sets)
+            b = algorithmic_bytes(M, N, K)
+            res.append({"workload": f"rows_{layout}_k2560_n9216", "M": M, "K": K, "N": N,
+                        "us_per_call": round(us, 3), "GBs": round(b / us / 1e3, 1),
+                        "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4), "row_stride": ops[0][0].stride(0),
+                        "kernel": api.plan(M, N, K)["kernel_name"], "pool_sets": sets})
+            print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+            del g
+        del ops
+    del fused
+    torch.cuda.empty_cache()
     return res
 
 

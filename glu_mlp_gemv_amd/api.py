@@ -20,12 +20,15 @@ LIBRARY_PATH = _build.LIBRARY
 # enum values of include/glu_gemv.h
 GLU_OK = 0
 GLU_ERR_UNSUPPORTED = 6
+GLU_ERR_BAD_STRIDE = 7
 KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC = range(5)
 KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
                 KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic"}
 
 EXPORTED_SYMBOLS = (
     "glu_dual_gemv",
+    "glu_dual_gemv_strided",
+    "glu_dual_gemv_strided_tuned",
     "glu_status_string",
     "glu_last_hip_error",
     "glu_version",
@@ -77,6 +80,11 @@ def library() -> ctypes.CDLL:
     lib.glu_dual_gemv.restype = ctypes.c_int
     lib.glu_dual_gemv_tuned.argtypes = [u16p, u16p, u16p, u16p, i64, i64, i64, vp, ctypes.POINTER(Tuning)]
     lib.glu_dual_gemv_tuned.restype = ctypes.c_int
+    lib.glu_dual_gemv_strided.argtypes = [u16p, i64, u16p, i64, u16p, i64, u16p, i64, i64, i64, i64, vp]
+    lib.glu_dual_gemv_strided.restype = ctypes.c_int
+    lib.glu_dual_gemv_strided_tuned.argtypes = [u16p, i64, u16p, i64, u16p, i64, u16p, i64, i64, i64, i64, vp,
+                                                ctypes.POINTER(Tuning)]
+    lib.glu_dual_gemv_strided_tuned.restype = ctypes.c_int
     lib.glu_status_string.argtypes = [ctypes.c_int]
     lib.glu_status_string.restype = ctypes.c_char_p
     lib.glu_last_hip_error.argtypes = []
@@ -144,8 +152,22 @@ def _check(name: str, t: torch.Tensor, ndims):
         raise ValueError(f"{name} must be on a GPU, got {t.device}")
     if t.dim() not in ndims:
         raise ValueError(f"{name} must have {' or '.join(map(str, ndims))} dims, got {t.dim()}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+
+
+def _row_stride(name: str, t: torch.Tensor) -> int:
+    """Element stride between rows of a 2-D view whose rows are contiguous; refuses any other layout."""
+    if t.dim() == 1:
+        if t.shape[0] > 1 and t.stride(0) != 1:
+            raise ValueError(f"{name}: elements must be contiguous, got stride {t.stride(0)}")
+        return t.shape[0]
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: the elements of a row must be contiguous, got strides {tuple(t.stride())}")
+    if rows <= 1:
+        return cols  # a single row: its stride is never used
+    if t.stride(0) < cols:
+        raise ValueError(f"{name}: rows overlap (row stride {t.stride(0)} < row length {cols})")
+    return t.stride(0)
 
 
 def dual_gemv(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor,
@@ -154,8 +176,12 @@ def dual_gemv(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor,
     """out = bf16(bf16(silu(bf16(hidden @ gate_w.T))) * bf16(hidden @ up_w.T)).
 
     hidden [M, K] (or [K], then the result is [N]), gate_w and up_w [N, K], all
-    bf16, contiguous, on one GPU.  ``out`` [M, N] (or [N]) is written in place if
-    given.  Runs asynchronously on ``stream`` (default: torch's current stream).
+    bf16 on one GPU.  Each may be a row-strided view (rows contiguous, any row
+    stride at least the row length, e.g. a slice of a wider fused block): the
+    stride the tensor reports is what the kernel uses, and any other layout is
+    refused.  ``out`` [M, N] (or [N]), written in place if given, may be
+    row-strided too.  Runs asynchronously on ``stream`` (default: torch's
+    current stream).
     """
     _check("hidden", hidden, (1, 2))
     _check("gate_w", gate_w, (2,))
@@ -177,15 +203,20 @@ def dual_gemv(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor,
         _check("out", out, (len(want),))
         if tuple(out.shape) != want or out.device != dev:
             raise ValueError(f"out must be {want} on {dev}, got {tuple(out.shape)} on {out.device}")
+    ldh = _row_stride("hidden", hidden)
+    ldg = _row_stride("gate_w", gate_w)
+    ldu = _row_stride("up_w", up_w)
+    ldo = _row_stride("out", out)
     lib = library()
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         if tuning is None:
-            st = lib.glu_dual_gemv(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(), out.data_ptr(),
-                                   M, N, K, s.cuda_stream)
+            st = lib.glu_dual_gemv_strided(hidden.data_ptr(), ldh, gate_w.data_ptr(), ldg, up_w.data_ptr(), ldu,
+                                           out.data_ptr(), ldo, M, N, K, s.cuda_stream)
         else:
-            st = lib.glu_dual_gemv_tuned(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(), out.data_ptr(),
-                                         M, N, K, s.cuda_stream, ctypes.byref(tuning))
+            st = lib.glu_dual_gemv_strided_tuned(hidden.data_ptr(), ldh, gate_w.data_ptr(), ldg, up_w.data_ptr(),
+                                                 ldu, out.data_ptr(), ldo, M, N, K, s.cuda_stream,
+                                                 ctypes.byref(tuning))
     _raise_for(st)
     return out
 
@@ -198,3 +229,15 @@ def dual_gemv_raw(hidden_ptr: int, gate_ptr: int, up_ptr: int, out_ptr: int, M: 
         return lib.glu_dual_gemv(hidden_ptr, gate_ptr, up_ptr, out_ptr, M, N, K, stream_handle)
     return lib.glu_dual_gemv_tuned(hidden_ptr, gate_ptr, up_ptr, out_ptr, M, N, K, stream_handle,
                                    ctypes.byref(tuning))
+
+
+def dual_gemv_strided_raw(hidden_ptr: int, ldh: int, gate_ptr: int, ldg: int, up_ptr: int, ldu: int, out_ptr: int,
+                          ldo: int, M: int, N: int, K: int, stream_handle: int = 0,
+                          tuning: Optional[Tuning] = None) -> int:
+    """The strided C call on raw device addresses; returns the glu_status (used by boundary tests)."""
+    lib = library()
+    if tuning is None:
+        return lib.glu_dual_gemv_strided(hidden_ptr, ldh, gate_ptr, ldg, up_ptr, ldu, out_ptr, ldo, M, N, K,
+                                         stream_handle)
+    return lib.glu_dual_gemv_strided_tuned(hidden_ptr, ldh, gate_ptr, ldg, up_ptr, ldu, out_ptr, ldo, M, N, K,
+                                           stream_handle, ctypes.byref(tuning))

@@ -224,8 +224,19 @@ glu_status fail_launch(hipError_t e)
     return GLU_ERR_LAUNCH;
 }
 
-glu_status run(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out,
-               int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* t)
+// Elements spanned by `rows` rows of `len` elements at stride `ld`, or -1 if
+// that does not fit in int64 as a byte count.
+int64_t extent(int64_t rows, int64_t ld, int64_t len)
+{
+    const int64_t lim = INT64_MAX / 2;
+    if (rows <= 0 || len <= 0) return 0;
+    if (mul_overflows(rows - 1, ld, lim) || (rows - 1) * ld > lim - len) return -1;
+    return (rows - 1) * ld + len;
+}
+
+glu_status run(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int64_t ldg, const uint16_t* up_w,
+               int64_t ldu, uint16_t* out, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream,
+               const glu_tuning* t)
 {
     if (M < 0 || N < 0 || K < 0) return GLU_ERR_BAD_SHAPE;
     Launch L;
@@ -233,41 +244,51 @@ glu_status run(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* u
     glu_status st = plan_launch(M, N, K, true, nullptr, &L);
     if (st != GLU_OK) return st;
     if (M == 0 || N == 0) return GLU_OK;
+    // strides: every row must fit in front of the next; inputs only matter when K > 0
+    if (ldo < N || (K > 0 && (ldh < K || ldg < K || ldu < K))) return GLU_ERR_BAD_STRIDE;
+    const int64_t out_len = extent(M, ldo, N);
+    const int64_t h_len = K > 0 ? extent(M, ldh, K) : 0;
+    const int64_t g_len = K > 0 ? extent(N, ldg, K) : 0;
+    const int64_t u_len = K > 0 ? extent(N, ldu, K) : 0;
+    if (out_len < 0 || h_len < 0 || g_len < 0 || u_len < 0) return GLU_ERR_BAD_STRIDE;
     if (!out || (K > 0 && (!hidden || !gate_w || !up_w))) return GLU_ERR_NULL_POINTER;
     const uintptr_t odd = ((uintptr_t)out | (uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w) & 1u;
     if (odd) return GLU_ERR_MISALIGNED;
-    const int64_t out_bytes = M * N * 2;
-    if (K > 0 && (overlaps(out, out_bytes, hidden, M * K * 2) || overlaps(out, out_bytes, gate_w, N * K * 2) ||
-                  overlaps(out, out_bytes, up_w, N * K * 2))) {
+    if (K > 0 && (overlaps(out, out_len * 2, hidden, h_len * 2) || overlaps(out, out_len * 2, gate_w, g_len * 2) ||
+                  overlaps(out, out_len * 2, up_w, u_len * 2))) {
         return GLU_ERR_ALIASING;
     }
-    const bool aligned16 = (((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w) & 15u) == 0;
+    // the fast kernels read 16-byte chunks of every row: pointers and row
+    // strides must keep rows 16-byte aligned, and strides fit their 32-bit offsets
+    const bool aligned16 = (((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w) & 15u) == 0 &&
+                           ((ldh | ldg | ldu) & 7) == 0 && ldh <= kMaxFastK && ldg <= kMaxFastK && ldu <= kMaxFastK;
     st = plan_launch(M, N, K, aligned16, t, &L);
     if (st != GLU_OK) return st;
 
+    const glu::RowStrides ld{ldh, ldg, ldu, ldo};
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     switch (L.kernel) {
     case GLU_KERNEL_ZERO:
-        e = glu::zero_launch(out, M, N, s);
+        e = glu::zero_launch(out, M, N, ldo, s);
         break;
     case GLU_KERNEL_GENERIC:
         for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
             const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
-            e = glu::generic_launch(mc, hidden + m0 * K, gate_w, up_w, out + m0 * N, N, K, N, s);
+            e = glu::generic_launch(mc, hidden + m0 * ldh, gate_w, up_w, out + m0 * ldo, N, K, ld, s);
         }
         break;
     case GLU_KERNEL_VALU:
         for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
             glu::ValuConfig c = L.valu;
             c.M = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
-            e = glu::valu_launch(c, hidden + m0 * K, gate_w, up_w, out + m0 * N, N, K, N, s);
+            e = glu::valu_launch(c, hidden + m0 * ldh, gate_w, up_w, out + m0 * ldo, N, K, ld, s);
         }
         break;
     case GLU_KERNEL_MFMA:
         for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
             const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
-            e = glu::mfma_launch(L.mfma, mc, hidden + m0 * K, gate_w, up_w, out + m0 * N, N, K, N, s);
+            e = glu::mfma_launch(L.mfma, mc, hidden + m0 * ldh, gate_w, up_w, out + m0 * ldo, N, K, ld, s);
         }
         break;
     default:
@@ -298,14 +319,28 @@ extern "C" {
 glu_status glu_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream)
 {
-    return run(hidden, gate_w, up_w, out, M, N, K, stream, nullptr);
+    return run(hidden, K, gate_w, K, up_w, K, out, N, M, N, K, stream, nullptr);
+}
+
+glu_status glu_dual_gemv_strided(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int64_t ldg,
+                                 const uint16_t* up_w, int64_t ldu, uint16_t* out, int64_t ldo,
+                                 int64_t M, int64_t N, int64_t K, void* stream)
+{
+    return run(hidden, ldh, gate_w, ldg, up_w, ldu, out, ldo, M, N, K, stream, nullptr);
 }
 
 glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                                uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream,
                                const glu_tuning* tuning)
 {
-    return run(hidden, gate_w, up_w, out, M, N, K, stream, tuning);
+    return run(hidden, K, gate_w, K, up_w, K, out, N, M, N, K, stream, tuning);
+}
+
+glu_status glu_dual_gemv_strided_tuned(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int64_t ldg,
+                                       const uint16_t* up_w, int64_t ldu, uint16_t* out, int64_t ldo,
+                                       int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* tuning)
+{
+    return run(hidden, ldh, gate_w, ldg, up_w, ldu, out, ldo, M, N, K, stream, tuning);
 }
 
 glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan)
@@ -371,12 +406,13 @@ const char* glu_status_string(int status)
     case GLU_ERR_ALIASING: return "GLU_ERR_ALIASING: out overlaps an input";
     case GLU_ERR_LAUNCH: return "GLU_ERR_LAUNCH: the HIP kernel launch failed";
     case GLU_ERR_UNSUPPORTED: return "GLU_ERR_UNSUPPORTED: the requested launch shape is not available";
+    case GLU_ERR_BAD_STRIDE: return "GLU_ERR_BAD_STRIDE: a row stride is shorter than its row, or the rows overflow";
     default: return "unknown glu_status";
     }
 }
 
 int glu_last_hip_error(void) { return g_last_hip_error; }
 
-int glu_version(void) { return 100; }
+int glu_version(void) { return 200; }
 
 }  // extern "C"

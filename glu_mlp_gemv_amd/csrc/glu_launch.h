@@ -40,8 +40,16 @@ struct MfmaConfig {
     int block;        // threads per workgroup (multiple of 64)
 };
 
+// Row strides in elements: row m of hidden at hidden + m*h, row j of gate_w
+// at gate_w + j*g, of up_w at up_w + j*u, row m of out at out + m*o.  The
+// fast kernels take h, g and u as multiples of 8 no larger than 2^25 (their
+// lane offsets are 32-bit byte counts over up to 32 rows).
+struct RowStrides {
+    int64_t h, g, u, o;
+};
+
 // per-M instantiation tables (glu_valu_m<M>.hip)
-using ValuFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int64_t);
+using ValuFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, RowStrides);
 ValuFn valu_pick_1(int R, int U, int NB, bool ragged);
 ValuFn valu_pick_2(int R, int U, int NB, bool ragged);
 ValuFn valu_pick_3(int R, int U, int NB, bool ragged);
@@ -56,7 +64,7 @@ constexpr bool valu_hidden_in_lds(int M, int U, int NB) { return M * U * NB > 16
 
 bool valu_supported(const ValuConfig& c);
 hipError_t valu_launch(const ValuConfig& c, const uint16_t* hidden, const uint16_t* gate_w,
-                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, RowStrides ld,
                        hipStream_t stream);
 
 bool mfma_supported(const MfmaConfig& c);
@@ -70,16 +78,16 @@ int mfma8_slice_depth(int u);
 bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block);
 hipError_t mfma8_launch(int M, int U, int depth, int nsg, bool ragged, int grid, const uint16_t* hidden,
                         const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K,
-                        int64_t ldo, hipStream_t stream);
+                        RowStrides ld, hipStream_t stream);
 hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
-                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, RowStrides ld,
                        hipStream_t stream);
 
-// Any alignment (2-byte), any K >= 1; M <= 8 per launch.
+// Any alignment (2-byte), any K >= 1, any strides; M <= 8 per launch.
 hipError_t generic_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
-                          uint16_t* out, int64_t N, int64_t K, int64_t ldo, hipStream_t stream);
+                          uint16_t* out, int64_t N, int64_t K, RowStrides ld, hipStream_t stream);
 
-// out[m, j] = +0 for m < M, j < N (K == 0).
-hipError_t zero_launch(uint16_t* out, int64_t M, int64_t N, hipStream_t stream);
+// out[m*ldo + j] = +0 for m < M, j < N (K == 0).
+hipError_t zero_launch(uint16_t* out, int64_t M, int64_t N, int64_t ldo, hipStream_t stream);
 
 }  // namespace glu

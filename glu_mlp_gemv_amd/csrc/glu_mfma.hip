@@ -40,8 +40,10 @@ template <int MT4, int U, bool HLDS, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
             const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
-            int M, int N, int K, int64_t ldo, int nsg)
+            int M, int N, int K, RowStrides ld, int nsg)
 {
+    const int64_t ldo = ld.o;
+    const uint32_t ldh8 = (uint32_t)(ld.h >> 3), ldg8 = (uint32_t)(ld.g >> 3), ldu8 = (uint32_t)(ld.u >> 3);
     extern __shared__ u32x4_t h_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
@@ -63,7 +65,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
         for (int i = threadIdx.x; i < M * nchunks; i += blockDim.x) {
             const int m = i / nchunks;
             const int c = i - m * nchunks;
-            h_lds[m * hpitch + (hswz ? c ^ lds_swz4(m) : c)] = h4[i];
+            h_lds[m * hpitch + (hswz ? c ^ lds_swz4(m) : c)] = h4[m * ldh8 + c];
         }
         __syncthreads();
     }
@@ -89,15 +91,16 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
         // addresses never share registers with loads still in flight
         const int64_t row0 = 4 * (int64_t)g;
         const uint32_t rr = (uint32_t)(min(4 * g + rho_a, N - 1) - 4 * g);  // rows past N re-read row N-1, never stored
-        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * K);
-        const char* up = reinterpret_cast<const char*>(up_w + row0 * K);
+        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * ld.g);
+        const char* up = reinterpret_cast<const char*>(up_w + row0 * ld.u);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int c = (sb * U + u) * 16 + cseg;
             if (RAGGED) c = min(c, nchunks - 1);
-            const uint32_t off = (rr * (uint32_t)nchunks + (uint32_t)c) * 16u;  // bytes, below 8*K
-            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + off));
-            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + off));
+            // bytes, below 4 rows at the stride
+            const uint32_t offg = (rr * ldg8 + (uint32_t)c) * 16u, offu = (rr * ldu8 + (uint32_t)c) * 16u;
+            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + offg));
+            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + offu));
         }
         if constexpr (!HLDS) {
 #pragma unroll
@@ -106,7 +109,7 @@ mfma_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
                 for (int u = 0; u < U; ++u) {
                     int c = (sb * U + u) * 16 + cseg;
                     if (RAGGED) c = min(c, nchunks - 1);
-                    const uint32_t off = ((uint32_t)hrow[t] * (uint32_t)nchunks + (uint32_t)c) * 16u;
+                    const uint32_t off = ((uint32_t)hrow[t] * ldh8 + (uint32_t)c) * 16u;
                     Bq[t][u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(hidden) + off);
                 }
             }
@@ -214,8 +217,10 @@ template <int MT4, int U, int DW, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
                   const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
-                  int M, int N, int K, int64_t ldo, int nsg)
+                  int M, int N, int K, RowStrides ld, int nsg)
 {
+    const int64_t ldo = ld.o;
+    const uint32_t ldh8 = (uint32_t)(ld.h >> 3), ldg8 = (uint32_t)(ld.g >> 3), ldu8 = (uint32_t)(ld.u >> 3);
     constexpr int W = kMfmaMaxThreads / kWave;             // waves in lockstep
     constexpr int MP = 4 * MT4;                            // hidden rows in a slice (padded)
     constexpr int SC = U * 16;                             // 16-byte chunks of one row in a slice
@@ -248,7 +253,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
             const int m = min(e / SC, M - 1);  // padded rows repeat row M-1, never stored
             int c = sb * SC + (e % SC);
             if (RAGGED) c = min(c, nchunks - 1);
-            hr[i] = h4[(uint32_t)m * (uint32_t)nchunks + (uint32_t)c];
+            hr[i] = h4[(uint32_t)m * ldh8 + (uint32_t)c];
         }
     };
     auto store_h = [&](int s, const u32x4_t (&hr)[HPT]) __attribute__((always_inline)) {
@@ -267,15 +272,16 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
         const int g = min(group_of(s), ngroups - 1);
         const int64_t row0 = 4 * (int64_t)g;  // wave-uniform base, 32-bit lane offsets
         const uint32_t rr = (uint32_t)(min(4 * g + rho_a, N - 1) - 4 * g);  // 0..3: rows past N re-read row N-1
-        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * K);
-        const char* up = reinterpret_cast<const char*>(up_w + row0 * K);
+        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * ld.g);
+        const char* up = reinterpret_cast<const char*>(up_w + row0 * ld.u);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int c = (sb * U + u) * 16 + cseg;
             if (RAGGED) c = min(c, nchunks - 1);
-            const uint32_t off = (rr * (uint32_t)nchunks + (uint32_t)c) * 16u;  // bytes, below 8*K
-            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + off));
-            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + off));
+            // bytes, below 4 rows at the stride
+            const uint32_t offg = (rr * ldg8 + (uint32_t)c) * 16u, offu = (rr * ldu8 + (uint32_t)c) * 16u;
+            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + offg));
+            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + offu));
         }
     };
 
@@ -378,7 +384,7 @@ mfma_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
 
 namespace {
 
-using MfmaFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, int64_t, int);
+using MfmaFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, RowStrides, int);
 
 template <int MT4, bool HL, bool RG>
 MfmaFn pick_u(int U)
@@ -453,12 +459,12 @@ bool mfma_supported(const MfmaConfig& c)
 }
 
 hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
-                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, RowStrides ld,
                        hipStream_t stream)
 {
     if (c.rows == 8) {
         if (c.hidden != kHiddenSlices) return hipErrorInvalidValue;
-        return mfma8_launch(M, c.U, c.depth, c.nsg, c.ragged, c.grid, hidden, gate_w, up_w, out, N, K, ldo, stream);
+        return mfma8_launch(M, c.U, c.depth, c.nsg, c.ragged, c.grid, hidden, gate_w, up_w, out, N, K, ld, stream);
     }
     MfmaConfig cm = c;
     cm.MT4 = (M + 3) / 4;
@@ -468,7 +474,7 @@ hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const
     if (cm.hidden == kHiddenLds) lds = mfma_hidden_lds_bytes(M, K);
     if (cm.hidden == kHiddenSlices) lds = mfma_slice_lds_bytes(cm.MT4, cm.U);
     hipLaunchKernelGGL(fn, dim3(cm.grid), dim3(cm.block), lds, stream,
-                       hidden, gate_w, up_w, out, M, (int)N, (int)K, ldo, cm.nsg);
+                       hidden, gate_w, up_w, out, M, (int)N, (int)K, ld, cm.nsg);
     return hipGetLastError();
 }
 

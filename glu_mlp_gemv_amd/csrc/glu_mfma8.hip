@@ -37,8 +37,10 @@ template <int MT8, int U, int DW, bool RAGGED>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 mfma8_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
                    const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
-                   int M, int N, int K, int64_t ldo, int nsg)
+                   int M, int N, int K, RowStrides ld, int nsg)
 {
+    const int64_t ldo = ld.o;
+    const uint32_t ldh8 = (uint32_t)(ld.h >> 3), ldg8 = (uint32_t)(ld.g >> 3), ldu8 = (uint32_t)(ld.u >> 3);
     constexpr int W = kMfmaMaxThreads / kWave;             // waves in lockstep
     constexpr int MP = 8 * MT8;                            // hidden rows in a slice (padded)
     constexpr int SC = U * 8;                              // 16-byte chunks of one row in a slice
@@ -74,7 +76,7 @@ mfma8_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restri
             const int m = min(e / SC, M - 1);  // padded rows repeat row M-1, never stored
             int c = sb * SC + (e % SC);
             if (RAGGED) c = min(c, nchunks - 1);
-            hr[i] = h4[(uint32_t)m * (uint32_t)nchunks + (uint32_t)c];
+            hr[i] = h4[(uint32_t)m * ldh8 + (uint32_t)c];
         }
     };
     auto store_h = [&](int s, const u32x4_t (&hr)[HPT]) __attribute__((always_inline)) {
@@ -93,15 +95,16 @@ mfma8_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restri
         const int g = min(group_of(s), ngroups - 1);
         const int64_t row0 = 8 * (int64_t)g;  // wave-uniform base, 32-bit lane offsets
         const uint32_t rr = (uint32_t)(min(8 * g + rho, N - 1) - 8 * g);  // 0..7: rows past N re-read row N-1
-        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * K);
-        const char* up = reinterpret_cast<const char*>(up_w + row0 * K);
+        const char* gp = reinterpret_cast<const char*>(gate_w + row0 * ld.g);
+        const char* up = reinterpret_cast<const char*>(up_w + row0 * ld.u);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int c = (sb * U + u) * 8 + cw;
             if (RAGGED) c = min(c, nchunks - 1);
-            const uint32_t off = (rr * (uint32_t)nchunks + (uint32_t)c) * 16u;  // bytes, below 16*K
-            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + off));
-            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + off));
+            // bytes, below 8 rows at the stride
+            const uint32_t offg = (rr * ldg8 + (uint32_t)c) * 16u, offu = (rr * ldu8 + (uint32_t)c) * 16u;
+            A[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + offg));
+            A[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + offu));
         }
     };
 
@@ -201,7 +204,7 @@ mfma8_slice_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restri
 
 namespace {
 
-using Mfma8Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, int64_t, int);
+using Mfma8Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, RowStrides, int);
 
 template <int MT8, bool RG>
 Mfma8Fn pick8_u(int U, int depth)
@@ -240,13 +243,13 @@ bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block)
 
 hipError_t mfma8_launch(int M, int U, int depth, int nsg, bool ragged, int grid, const uint16_t* hidden,
                         const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K,
-                        int64_t ldo, hipStream_t stream)
+                        RowStrides ld, hipStream_t stream)
 {
     const int mt8 = (M + 7) / 8;
     Mfma8Fn fn = pick8(mt8, U, depth, ragged);
     if (!fn || M < 1 || M > 8 * mt8) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(kMfmaMaxThreads), mfma8_slice_lds_bytes(mt8, U), stream,
-                       hidden, gate_w, up_w, out, M, (int)N, (int)K, ldo, nsg);
+                       hidden, gate_w, up_w, out, M, (int)N, (int)K, ld, nsg);
     return hipGetLastError();
 }
 

@@ -52,15 +52,17 @@ __device__ __forceinline__ float dot_chunk(const u32x4& h, const u32x4& w, float
     return acc;
 }
 
-// hidden [M,K], gate_w/up_w [N,K] (16-byte aligned, K % 8 == 0), out [M,ldo].
+// hidden [M,K], gate_w/up_w [N,K] (16-byte aligned, K % 8 == 0), out [M,N], rows at the strides of ld.
 // NB <= 2; NB * U * 64 >= K/8, with equality unless RAGGED.  Dynamic LDS: M * K * 2 bytes when HLDS, else none.
 template <int M, int R, int U, int NB, bool HLDS, bool RAGGED>
 __global__ void __launch_bounds__(kValuMaxThreads)
 valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
             const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
-            int N, int K, int64_t ldo)
+            int N, int K, RowStrides ld)
 {
     static_assert(NB == 1 || NB == 2, "a row group streams in one or two batches");
+    const int64_t ldo = ld.o;
+    const int ldh8 = (int)(ld.h >> 3);  // hidden row stride in 16-byte chunks
     constexpr int MR = M * R;
     constexpr int SLOTS = kWave / MR;  // row groups whose results one epilogue pass holds
     const int lane = threadIdx.x & (kWave - 1);
@@ -75,7 +77,8 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     u32x4 hreg[HLDS ? 1 : M][HLDS ? 1 : NB][HLDS ? 1 : U];
     if constexpr (HLDS) {
         for (int i = threadIdx.x; i < M * nchunks; i += blockDim.x) {
-            h_lds[i] = h4[i];
+            const int m = i / nchunks;
+            h_lds[i] = h4[m * ldh8 + (i - m * nchunks)];
         }
         __syncthreads();
     } else {
@@ -87,7 +90,7 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
                 for (int i = 0; i < U; ++i) {
                     const int c = (b * U + i) * kWave + lane;
                     const int cc = RAGGED ? min(c, nchunks - 1) : c;
-                    hreg[m][b][i] = h4[(int64_t)m * nchunks + cc];
+                    hreg[m][b][i] = h4[m * ldh8 + cc];
                 }
             }
         }
@@ -105,8 +108,8 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = min(g * R + r, N - 1);  // rows past N re-read row N-1, never stored
-            const u32x4* gp = reinterpret_cast<const u32x4*>(gate_w + (int64_t)row * K);
-            const u32x4* up = reinterpret_cast<const u32x4*>(up_w + (int64_t)row * K);
+            const u32x4* gp = reinterpret_cast<const u32x4*>(gate_w + (int64_t)row * ld.g);
+            const u32x4* up = reinterpret_cast<const u32x4*>(up_w + (int64_t)row * ld.u);
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 const int c = (b * U + i) * kWave + lane;

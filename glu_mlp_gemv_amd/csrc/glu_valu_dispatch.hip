@@ -29,14 +29,14 @@ bool valu_supported(const ValuConfig& c)
 }
 
 hipError_t valu_launch(const ValuConfig& c, const uint16_t* hidden, const uint16_t* gate_w,
-                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, int64_t ldo,
+                       const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, RowStrides ld,
                        hipStream_t stream)
 {
     ValuFn fn = pick(c);
     if (!fn) return hipErrorInvalidValue;
     const size_t lds = valu_hidden_in_lds(c.M, c.U, c.NB) ? (size_t)c.M * (size_t)K * sizeof(uint16_t) : 0;
     hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.block), lds, stream,
-                       hidden, gate_w, up_w, out, (int)N, (int)K, ldo);
+                       hidden, gate_w, up_w, out, (int)N, (int)K, ld);
     return hipGetLastError();
 }
 

@@ -54,7 +54,9 @@ typedef enum glu_status {
     GLU_ERR_MISALIGNED = 3,   /* a pointer is not 2-byte aligned */
     GLU_ERR_ALIASING = 4,     /* out overlaps hidden, gate_w or up_w */
     GLU_ERR_LAUNCH = 5,       /* the HIP launch failed; see glu_last_hip_error() */
-    GLU_ERR_UNSUPPORTED = 6   /* a tuning override the library cannot serve (glu_gemv_tuning.h) */
+    GLU_ERR_UNSUPPORTED = 6,  /* a tuning override the library cannot serve (glu_gemv_tuning.h) */
+    GLU_ERR_BAD_STRIDE = 7    /* glu_dual_gemv_strided: a row stride below its row length, or
+                                 rows whose extent overflows int64 */
 } glu_status;
 
 /*
@@ -70,6 +72,35 @@ typedef enum glu_status {
  */
 glu_status glu_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * glu_dual_gemv on row-strided operands: row m of hidden starts at
+ * hidden + m*ldh, row j of gate_w at gate_w + j*ldg, row j of up_w at
+ * up_w + j*ldu, row m of out at out + m*ldo (strides in elements; the K, resp.
+ * N, elements of a row are contiguous).  This is what a view sliced out of a
+ * wider row block looks like, e.g. the gate and up halves of a fused
+ * projection's output or a column slice of a larger matrix.  The fix for
+ * exactly such a view, read as if it were packed, is in DeepSpeed PR #9057
+ * "fix(module-inject): preserve HF precision boundaries in segKI kernels"
+ * (commit notes: q sliced from the fused q|k|v block keeps the fused row
+ * stride; pass the real stride and fail closed on one that disagrees); see
+ * also PR #8602's commit notes on the strided gdn_gates input.
+ *
+ * Strides must be at least the row length: ldh, ldg, ldu >= K (when K > 0)
+ * and ldo >= N, else GLU_ERR_BAD_STRIDE and nothing is launched; nothing
+ * ever reads or writes between rows.  Rows may not overlap (a stride below
+ * the row length is refused, never read as broadcast).  The fast kernels
+ * run when the pointers are 16-byte aligned, K and ldh, ldg, ldu are
+ * multiples of 8 and the strides are at most 2^25; any other layout takes
+ * the 2-byte generic kernel with the same result.  The result is bitwise
+ * the result of glu_dual_gemv on the same rows stored packed.  Ownership,
+ * execution and the other errors are those of glu_dual_gemv (aliasing is
+ * checked on the strided extents).  glu_dual_gemv(h, g, u, o, M, N, K, s) is
+ * glu_dual_gemv_strided(h, K, g, K, u, K, o, N, M, N, K, s).
+ */
+glu_status glu_dual_gemv_strided(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int64_t ldg,
+                                 const uint16_t* up_w, int64_t ldu, uint16_t* out, int64_t ldo,
+                                 int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* glu_status_string(int status);

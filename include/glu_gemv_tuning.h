@@ -40,6 +40,11 @@ glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, c
                                uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream,
                                const glu_tuning* tuning);
 
+/* glu_dual_gemv_strided (glu_gemv.h) with the same overrides. */
+glu_status glu_dual_gemv_strided_tuned(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int64_t ldg,
+                                       const uint16_t* up_w, int64_t ldu, uint16_t* out, int64_t ldo,
+                                       int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* tuning);
+
 /* glu_dual_gemv_plan with overrides (host only, no HIP call). */
 glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned16,
                                     const glu_tuning* tuning, glu_plan* plan);

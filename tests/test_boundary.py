@@ -12,7 +12,7 @@ from glu_mlp_gemv_amd import api
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # status codes of include/glu_gemv.h
-OK, NULLP, SHAPE, ALIGN, ALIAS, LAUNCH, UNSUP = range(7)
+OK, NULLP, SHAPE, ALIGN, ALIAS, LAUNCH, UNSUP, STRIDE = range(8)
 
 
 @pytest.fixture(scope="module")
@@ -180,3 +180,46 @@ def test_every_tuned_gpu_case_plans(lib):
         assert api.plan(M, N, K, True, api.make_tuning(kernel=api.KERNEL_VALU))["kernel"] == api.KERNEL_VALU
     for kw in EPILOGUE_PATHS.values():
         api.plan(1, 1 << 16, 8, True, api.make_tuning(**kw))
+
+
+# (hidden, ldh, gate_w, ldg, up_w, ldu, out, ldo, M, N, K): every case fails before a launch
+@pytest.mark.parametrize("args,status", [
+    ((A, 8, A + 4096, 8, A + 8192, 8, A + 16384, 7, 2, 8, 8), STRIDE),       # out rows overlap
+    ((A, 7, A + 4096, 8, A + 8192, 8, A + 16384, 8, 2, 8, 8), STRIDE),       # hidden rows overlap
+    ((A, 8, A + 4096, 7, A + 8192, 8, A + 16384, 8, 2, 8, 8), STRIDE),
+    ((A, 8, A + 4096, 8, A + 8192, 0, A + 16384, 8, 2, 8, 8), STRIDE),
+    ((A, -8, A + 4096, 8, A + 8192, 8, A + 16384, 8, 2, 8, 8), STRIDE),      # negative stride
+    ((A, 8, A + 4096, 8, A + 8192, 8, A + 16384, 1 << 62, 2, 8, 8), STRIDE),  # out rows overflow
+    ((A, 1 << 62, A + 4096, 8, A + 8192, 8, A + 16384, 8, 2, 8, 8), STRIDE),
+    ((0, 0, 0, 0, 0, 0, A + 16384, 3, 2, 8, 0), STRIDE),                      # K == 0 still writes out
+    ((0, 0, 0, 0, 0, 0, 0, 0, 0, 8, 8), OK),                                  # M == 0: strides unchecked
+    ((0, 8, A + 4096, 64, A + 8192, 8, A + 16384, 8, 2, 8, 8), NULLP),        # valid strides, NULL hidden
+    ((A, 8, A + 4096, 64, A + 8192, 8, A + 4096 + 200, 8, 1, 8, 8), ALIAS),    # out in the span of gate_w's rows
+    ((A + 2, 8, A + 4096, 64, A + 8192, 8, A + 16385, 8, 1, 8, 8), ALIGN),
+])
+def test_strided_validation_before_any_hip_call(lib, args, status):
+    assert api.dual_gemv_strided_raw(*args) == status
+    assert lib.glu_last_hip_error() == 0
+
+
+def test_strided_aliasing_span_edge(lib):
+    # gate_w rows at stride 64 elements, N = 8, K = 8: the span is (7*64 + 8)*2 = 912 bytes, so an
+    # out starting at byte 910 overlaps it and one starting at 912 does not (then the NULL up_w is
+    # reported instead, before any launch)
+    assert api.dual_gemv_strided_raw(A, 8, A + 4096, 64, A + 8192, 8, A + 4096 + 910, 8, 1, 8, 8) == ALIAS
+    assert api.dual_gemv_strided_raw(A, 8, A + 4096, 64, 0, 8, A + 4096 + 912, 8, 1, 8, 8) == NULLP
+
+
+def test_python_face_row_strides():
+    import torch
+    big = torch.zeros(6, 40, dtype=torch.bfloat16)
+    assert api._row_stride("x", big) == 40
+    assert api._row_stride("x", big[:, :24]) == 40          # a column slice keeps the wide row stride
+    assert api._row_stride("x", big[1:2, :24]) == 24        # one row: its stride is never used
+    assert api._row_stride("x", big[0]) == 40
+    with pytest.raises(ValueError):
+        api._row_stride("x", big.t())                        # rows not contiguous
+    with pytest.raises(ValueError):
+        api._row_stride("x", big.as_strided((4, 24), (16, 1)))  # rows overlap
+    with pytest.raises(ValueError):
+        api._row_stride("x", big[0, ::2])                    # 1-D with a gap
