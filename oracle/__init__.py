@@ -1,4 +1,4 @@
-"""Oracle for the dual-weight GLU projection -- TEST INFRASTRUCTURE ONLY.
+"""Oracle for the dual-weight GLU projection and the grouped GEMV -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library
@@ -43,6 +43,8 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.glu_oracle_silu_bf16.restype = ctypes.c_int
     lib.glu_oracle_round_bf16.argtypes = [_f64p, _u16p, _i64]
     lib.glu_oracle_round_bf16.restype = ctypes.c_int
+    lib.glu_oracle_linear.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, _i64, _f64p, _f64p, ctypes.c_int]
+    lib.glu_oracle_linear.restype = ctypes.c_int
     lib.glu_oracle_max_threads.argtypes = []
     lib.glu_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -125,6 +127,35 @@ def dual_gemv(hidden: np.ndarray, gate_w: np.ndarray, up_w: np.ndarray,
         raise RuntimeError(f"glu_oracle_dual_gemv failed ({rc})")
     if with_pre:
         return DualGemvResult(out, *pre)
+    return out
+
+
+class LinearResult(NamedTuple):
+    out: np.ndarray   # uint16 [M,N] bf16 bits
+    pre: np.ndarray   # fp64 [M,N]  h . W[j]
+    abs: np.ndarray   # fp64 [M,N]  sum |h * W[j]|
+
+
+def linear(hidden: np.ndarray, w: np.ndarray, threads: int = 0, with_pre: bool = False):
+    """One projection of a grouped GEMV: bf16(hidden @ w^T) for bf16 bit arrays hidden [M,K], w [N,K].
+
+    With ``with_pre`` the fp64 dot products and absolute sums come back too (a
+    :class:`LinearResult`); otherwise only the uint16 ``out`` array.
+    """
+    h = _u16(hidden)
+    ww = _u16(w)
+    if h.ndim != 2 or ww.ndim != 2 or ww.shape[1] != h.shape[1]:
+        raise ValueError(f"shape mismatch: hidden {h.shape}, w {ww.shape}")
+    M, K = h.shape
+    N = ww.shape[0]
+    out = np.zeros((M, N), dtype=np.uint16)
+    pre = [np.zeros((M, N), dtype=np.float64) for _ in range(2)] if with_pre else [None, None]
+    rc = _load().glu_oracle_linear(_ptr(h, _u16p), _ptr(ww, _u16p), _ptr(out, _u16p), M, N, K,
+                                   *(_ptr(p, _f64p) for p in pre), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"glu_oracle_linear failed ({rc})")
+    if with_pre:
+        return LinearResult(out, *pre)
     return out
 
 

@@ -24,6 +24,11 @@ order-independent error bound of a floating-point inner product), widened by
 2 ULP.  ``d`` counts rounding steps in units of 2^-24; a kernel whose adder
 may truncate states twice its chain length.  Such outputs are counted and
 reported with their condition number ``kappa = sum|h*w| / |sum h*w|``.
+
+``compare_linear`` applies the same bars to a plain projection (one bf16
+rounding of the dot, no epilogue): there the admissible interval is the
+rounding of every reachable sum, ``[RNE(G - tau), RNE(G + tau)]``, exactly
+(rounding is monotone), with no widening.
 """
 from __future__ import annotations
 
@@ -32,7 +37,7 @@ from typing import List, Optional
 
 import numpy as np
 
-from . import DualGemvResult, round_bf16, silu_bf16
+from . import DualGemvResult, LinearResult, round_bf16, silu_bf16
 
 U32 = 2.0 ** -24  # unit roundoff of fp32
 SMALL_SAMPLE_SLACK = 3  # non-bit-exact outputs always allowed (each still within the ULP bar)
@@ -176,6 +181,49 @@ def compare(got: np.ndarray, ref: DualGemvResult, depth: int, k_len: int,
                 info = {"index": int(i), "got": f"{int(got[i]):#06x}", "want": f"{int(want[i]):#06x}",
                         "ulp": int(d[i]), "kappa": float(kappa), "G": float(G[i]), "U": float(U[i]),
                         "sum_abs_g": float(Ga[i]), "sum_abs_u": float(Ua[i])}
+                if lo is not None:
+                    info["interval"] = [lo, hi, o]
+                rep.failure_info.append(info)
+    return rep
+
+
+def compare_linear(got: np.ndarray, ref: LinearResult, depth: int, k_len: int, max_listed: int = 20) -> Report:
+    """Check device output bits of one plain projection against the oracle's ``linear`` result."""
+    got = np.asarray(got, dtype=np.uint16).ravel()
+    want = np.asarray(ref.out, dtype=np.uint16).ravel()
+    if got.shape != want.shape:
+        raise ValueError(f"size mismatch {got.shape} vs {want.shape}")
+    rep = Report(n=int(got.size))
+    if got.size == 0:
+        return rep
+    d = ulp_distance(got, want)
+    rep.max_ulp = int(d.max())
+    rep.bit_exact_frac = float(np.mean((got == want) | (is_nan_bits(got) & is_nan_bits(want))))
+    w = bf16_to_f64(want)
+    g = bf16_to_f64(got)
+    nz = (w != 0) & np.isfinite(w) & np.isfinite(g)
+    rep.mean_rel = float(np.mean(np.abs(g[nz] - w[nz]) / np.abs(w[nz]))) if nz.any() else 0.0
+    bad = np.nonzero(d > 2)[0]
+    rep.over_2ulp = int(bad.size)
+    P, A = np.asarray(ref.pre).ravel(), np.asarray(ref.abs).ravel()
+    for i in bad:
+        kappa = A[i] / abs(P[i]) if P[i] != 0 else np.inf
+        o = int(ordered(got[i:i + 1])[0])
+        ok = False
+        lo = hi = None
+        if not is_nan_bits(got[i:i + 1])[0]:
+            lo, hi = _admissible_range(float(P[i]), float(A[i]), depth, k_len)
+            ok = lo <= o <= hi
+        if ok:
+            rep.interval_pass += 1
+            rep.interval_max_kappa = max(rep.interval_max_kappa, float(kappa))
+            rep.interval_min_kappa = min(rep.interval_min_kappa, float(kappa))
+        else:
+            rep.failures += 1
+            if len(rep.failure_idx) < max_listed:
+                rep.failure_idx.append(int(i))
+                info = {"index": int(i), "got": f"{int(got[i]):#06x}", "want": f"{int(want[i]):#06x}",
+                        "ulp": int(d[i]), "kappa": float(kappa), "pre": float(P[i]), "sum_abs": float(A[i])}
                 if lo is not None:
                     info["interval"] = [lo, hi, o]
                 rep.failure_info.append(info)

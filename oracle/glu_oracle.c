@@ -30,6 +30,13 @@
  *   5. out = RNE_bf16( fl32(s*u) ): two bf16 tensors multiply in fp32 and
  *      round once to bf16.  s*u is exact in fp32 unless it underflows.
  *
+ * A second function, glu_oracle_linear, evaluates one projection of a
+ * grouped GEMV: the pages' single/triple/quad GEMV kernels behind PR #8602's
+ * grouped_linear(x, weights, glu_epilogue) dispatcher (commit notes), taken
+ * without the GLU epilogue, i.e. n nn.Linear projections of one hidden.  A
+ * bf16 nn.Linear output is one bf16 tensor, so
+ *   out[m,j] = RNE_bf16( sum_k h[m,k]*W[j,k] ),  the sum in fp64 as in 1.
+ *
  * Readings where the pages are silent: the silu formula is x/(1+exp(-x))
  * (the PR #8602 listing never defines its SILU); rounding is to nearest,
  * ties to even, throughout (that listing's _rn conversion); no denormal
@@ -188,6 +195,43 @@ int glu_oracle_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const u
         if (up_pre) up_pre[idx] = U;
         if (gate_abs) gate_abs[idx] = Ga;
         if (up_abs) up_abs[idx] = Ua;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * One projection: out[m,j] = RNE_bf16(sum_k hidden[m,k] * w[j,k]) with the
+ * sum in fp64 in increasing k.  Arrays are dense row-major bf16 bit patterns:
+ * hidden [M,K], w [N,K], out [M,N].  The optional fp64 outputs (each [M,N],
+ * may be NULL) receive the sum and sum_k |hidden*w| for the interval check.
+ */
+int glu_oracle_linear(const uint16_t* hidden, const uint16_t* w, uint16_t* out, int64_t M, int64_t N,
+                      int64_t K, double* pre, double* abs_sum, int threads)
+{
+    if (M < 0 || N < 0 || K < 0) {
+        return ORACLE_ERR_ARG;
+    }
+    if (M == 0 || N == 0) {
+        return ORACLE_OK;
+    }
+    if (!out || (K > 0 && (!hidden || !w))) {
+        return ORACLE_ERR_ARG;
+    }
+    set_threads(threads);
+    const int64_t total = M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t pos = 0; pos < total; ++pos) {
+        const uint16_t* hvec = hidden + (pos / N) * K;
+        const uint16_t* wrow = w + (pos % N) * K;
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) {
+            const double prod = bf16_bits_to_double(hvec[kk]) * bf16_bits_to_double(wrow[kk]);
+            acc += prod;
+            acc_abs += fabs(prod);
+        }
+        out[pos] = rne_bf16_from_double(acc);
+        if (pre) pre[pos] = acc;
+        if (abs_sum) abs_sum[pos] = acc_abs;
     }
     return ORACLE_OK;
 }

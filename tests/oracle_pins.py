@@ -266,6 +266,52 @@ def pin_sampled_matches_full():
     assert np.array_equal(smp.up_abs, full.up_abs[rows, cols])
 
 
+# ---- one projection of the grouped GEMV ------------------------------------
+
+def pin_linear_brute_force_tiny():
+    """Tiny shapes: every projection output equals the exact rational dot rounded to bf16."""
+    rng = np.random.default_rng(31)
+    for M, K, N in [(1, 1, 3), (1, 5, 4), (2, 8, 5), (3, 17, 3), (1, 64, 2)]:
+        h = _random_bf16(rng, (M, K))
+        w = _random_bf16(rng, (N, K))
+        res = oracle.linear(h, w, with_pre=True)
+        for m in range(M):
+            for j in range(N):
+                hv = [exact.bf16_bits_to_value(b) for b in h[m].tolist()]
+                dot = sum((a * exact.bf16_bits_to_value(b) for a, b in zip(hv, w[j].tolist())), Fraction(0))
+                r = exact.round_to_format(dot, exact.BF16)
+                want = exact.value_to_bf16_bits(r, negative_zero=(r == 0 and dot < 0))
+                assert exact.bits_equal(want, int(res.out[m, j])), (M, K, N, m, j, hex(want), hex(int(res.out[m, j])))
+                bound = K * 2.0 ** -53 * float(res.abs[m, j]) * 1.01
+                assert abs(float(dot) - res.pre[m, j]) <= bound, (M, K, N, m, j)
+
+
+def pin_linear_torch():
+    """The projection's dots equal torch's fp64 matmul, and torch's own bf16 linear on the CPU
+    (fp32 accumulation, one rounding) lands within the parity bar of the oracle."""
+    h, wg, _ = inputs.case("tail_k1024_n3000", M=3, seed=8)
+    res = oracle.linear(bits_of(h), bits_of(wg), with_pre=True)
+    P = (h.double() @ wg.double().T).numpy()
+    assert np.all(np.abs(P - res.pre) <= 1024 * 2.0 ** -52 * res.abs), "projection differs from h @ W^T"
+    A = (h.double().abs() @ wg.double().abs().T).numpy()
+    np.testing.assert_allclose(res.abs, A, rtol=1e-14)
+    lin = torch.nn.functional.linear(h, wg)
+    rep = check.compare_linear(bits_of(lin), res, depth=1024, k_len=1024)
+    assert rep.failures == 0 and rep.bit_exact_frac >= 0.999 and rep.mean_rel <= 3e-3, rep.summary()
+
+
+def pin_linear_scaling():
+    """Scaling h by a power of two scales every dot exactly and the rounded output by the same power."""
+    h, wg, _ = inputs.case("tail_k1024_n3000", M=1, seed=9)
+    base = oracle.linear(bits_of(h), bits_of(wg), with_pre=True)
+    for a in (-2, 3):
+        hs = (h.float() * 2.0 ** a).to(torch.bfloat16)
+        sc = oracle.linear(bits_of(hs), bits_of(wg), with_pre=True)
+        assert np.array_equal(sc.pre, base.pre * 2.0 ** a)
+        want = bits_of((tensor_of(base.out).float() * 2.0 ** a).to(torch.bfloat16))
+        assert check.compare_strict_bits(sc.out, want) is None
+
+
 ALL_PINS = [
     pin_round_matches_torch_cast,
     pin_round_matches_exact_for_fp64,
@@ -282,4 +328,7 @@ ALL_PINS = [
     pin_linearity,
     pin_row_independence,
     pin_sampled_matches_full,
+    pin_linear_brute_force_tiny,
+    pin_linear_torch,
+    pin_linear_scaling,
 ]

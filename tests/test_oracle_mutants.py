@@ -40,6 +40,11 @@ MUTANTS = [
     ("overflow_threshold_off_by_one", "ldexp(1.0 - ldexp(1.0, -9), 128)", "ldexp(1.0 - ldexp(1.0, -9), 127)", 0),
     ("gate_not_rounded", "const uint16_t g = rne_bf16_from_double(G);",
      "const uint16_t g = float_bits_hi((float)G);", 0),
+    ("linear_last_term_dropped", "for (int64_t kk = 0; kk < K; ++kk)", "for (int64_t kk = 0; kk + 1 < K; ++kk)", 0),
+    ("linear_weight_row_shifted", "const uint16_t* wrow = w + (pos % N) * K;",
+     "const uint16_t* wrow = w + ((pos + 1) % N) * K;", 0),
+    ("linear_truncated", "out[pos] = rne_bf16_from_double(acc);", "out[pos] = float_bits_hi((float)acc);", 0),
+    ("linear_hidden_row_ignored", "const uint16_t* hvec = hidden + (pos / N) * K;", "const uint16_t* hvec = hidden;", 0),
 ]
 
 # cheap pins first; the exhaustive sweeps only run if nothing cheaper caught the mutant
