@@ -186,6 +186,31 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
         del ops
     del fused
     torch.cuda.empty_cache()
+    # grouped GEMV: n projections of one hidden, weights read in place
+    for name, Ns in (("grouped_qkv_like_k2560", (4096, 1024, 1024)), ("grouped_gdn_like_k2560", (8192, 4096, 32, 32))):
+        rows = sum(Ns)
+        per = rows * K * 2
+        sets = max(4, -(-1_400_000_000 // per))
+        pool = [[inputs.weights(n_i, K, 400 + 10 * i + t, device=dev)[0] for t, n_i in enumerate(Ns)]
+                for i in range(sets)]
+        for M in (1, 4):
+            h = inputs.hidden(M, K, 0).to(dev)
+            outs = [torch.empty(M, n_i, dtype=torch.bfloat16, device=dev) for n_i in Ns]
+
+            def one_pass():
+                for ws in pool:
+                    api.grouped_gemv(h, ws, outs=outs)
+            g = capture(torch, one_pass)
+            ms = time_region(torch, g.replay, reps, 2, stream)
+            us = ms * 1e3 / (reps * sets)
+            b = per + M * K * 2 + M * rows * 2
+            res.append({"workload": name, "M": M, "K": K, "N": list(Ns), "us_per_call": round(us, 3),
+                        "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "kernel": api.grouped_plan(M, K, rows)["kernel_name"], "pool_sets": sets})
+            print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+            del g
+        del pool
+        torch.cuda.empty_cache()
     return res
 
 

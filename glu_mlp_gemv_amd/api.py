@@ -27,6 +27,10 @@ KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
 
 EXPORTED_SYMBOLS = (
     "glu_dual_gemv",
+    "glu_grouped_gemv",
+    "glu_grouped_gemv_tuned",
+    "glu_grouped_gemv_plan",
+    "glu_grouped_gemv_plan_tuned",
     "glu_dual_gemv_strided",
     "glu_dual_gemv_strided_tuned",
     "glu_status_string",
@@ -63,6 +67,13 @@ class Tuning(ctypes.Structure):
                 ("mfma_depth", ctypes.c_int)]
 
 
+class Projection(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("out", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("ldw", ctypes.c_int64), ("ldo", ctypes.c_int64)]
+
+
+GROUP_MAX = 8
+
 _LIB: Optional[ctypes.CDLL] = None
 
 
@@ -85,6 +96,16 @@ def library() -> ctypes.CDLL:
     lib.glu_dual_gemv_strided_tuned.argtypes = [u16p, i64, u16p, i64, u16p, i64, u16p, i64, i64, i64, i64, vp,
                                                 ctypes.POINTER(Tuning)]
     lib.glu_dual_gemv_strided_tuned.restype = ctypes.c_int
+    projp = ctypes.POINTER(Projection)
+    lib.glu_grouped_gemv.argtypes = [u16p, i64, projp, ctypes.c_int, i64, i64, vp]
+    lib.glu_grouped_gemv.restype = ctypes.c_int
+    lib.glu_grouped_gemv_tuned.argtypes = [u16p, i64, projp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(Tuning)]
+    lib.glu_grouped_gemv_tuned.restype = ctypes.c_int
+    lib.glu_grouped_gemv_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Plan)]
+    lib.glu_grouped_gemv_plan.restype = ctypes.c_int
+    lib.glu_grouped_gemv_plan_tuned.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning),
+                                                ctypes.POINTER(Plan)]
+    lib.glu_grouped_gemv_plan_tuned.restype = ctypes.c_int
     lib.glu_status_string.argtypes = [ctypes.c_int]
     lib.glu_status_string.restype = ctypes.c_char_p
     lib.glu_last_hip_error.argtypes = []
@@ -241,3 +262,78 @@ def dual_gemv_strided_raw(hidden_ptr: int, ldh: int, gate_ptr: int, ldg: int, up
                                          stream_handle)
     return lib.glu_dual_gemv_strided_tuned(hidden_ptr, ldh, gate_ptr, ldg, up_ptr, ldu, out_ptr, ldo, M, N, K,
                                            stream_handle, ctypes.byref(tuning))
+
+
+def grouped_plan(M: int, K: int, rows: int, fast: bool = True, tuning: Optional[Tuning] = None) -> dict:
+    """The launch glu_grouped_gemv would make (host only): rows = sum of N over the projections."""
+    p = Plan()
+    lib = library()
+    if tuning is None:
+        st = lib.glu_grouped_gemv_plan(M, K, rows, int(fast), ctypes.byref(p))
+    else:
+        st = lib.glu_grouped_gemv_plan_tuned(M, K, rows, int(fast), ctypes.byref(tuning), ctypes.byref(p))
+    _raise_for(st)
+    return p.as_dict()
+
+
+def grouped_gemv(hidden: torch.Tensor, weights, outs=None, tuning: Optional[Tuning] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+    """[bf16(hidden @ W.T) for W in weights], each W [N_i, K] read in place (no concatenation).
+
+    hidden [M, K] (or [K]: each result is then [N_i]); 1 to 8 weights, all bf16
+    on one GPU; row-strided views are read at the stride they report (rows must
+    be contiguous).  ``outs`` (same count, [M, N_i] each) are written in place
+    if given.  Runs asynchronously on ``stream`` (default: torch's current one).
+    """
+    weights = list(weights)
+    if not 1 <= len(weights) <= GROUP_MAX:
+        raise ValueError(f"1 to {GROUP_MAX} weights, got {len(weights)}")
+    _check("hidden", hidden, (1, 2))
+    vec = hidden.dim() == 1
+    M = 1 if vec else hidden.shape[0]
+    K = hidden.shape[-1]
+    dev = hidden.device
+    for i, w in enumerate(weights):
+        _check(f"weights[{i}]", w, (2,))
+        if w.shape[1] != K or w.device != dev:
+            raise ValueError(f"weights[{i}] must be [N, {K}] on {dev}, got {tuple(w.shape)} on {w.device}")
+    if outs is None:
+        outs = [torch.empty((w.shape[0],) if vec else (M, w.shape[0]), dtype=torch.bfloat16, device=dev)
+                for w in weights]
+    else:
+        outs = list(outs)
+        if len(outs) != len(weights):
+            raise ValueError("one output per weight")
+        for i, (o, w) in enumerate(zip(outs, weights)):
+            want = (w.shape[0],) if vec else (M, w.shape[0])
+            _check(f"outs[{i}]", o, (len(want),))
+            if tuple(o.shape) != want or o.device != dev:
+                raise ValueError(f"outs[{i}] must be {want} on {dev}, got {tuple(o.shape)} on {o.device}")
+    projs = (Projection * len(weights))()
+    for i, (w, o) in enumerate(zip(weights, outs)):
+        projs[i] = Projection(w.data_ptr(), o.data_ptr(), w.shape[0], _row_stride(f"weights[{i}]", w),
+                              _row_stride(f"outs[{i}]", o))
+    ldh = _row_stride("hidden", hidden)
+    lib = library()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        if tuning is None:
+            st = lib.glu_grouped_gemv(hidden.data_ptr(), ldh, projs, len(weights), M, K, s.cuda_stream)
+        else:
+            st = lib.glu_grouped_gemv_tuned(hidden.data_ptr(), ldh, projs, len(weights), M, K, s.cuda_stream,
+                                            ctypes.byref(tuning))
+    _raise_for(st)
+    return outs
+
+
+def grouped_gemv_raw(hidden_ptr: int, ldh: int, projections, M: int, K: int, stream_handle: int = 0,
+                     n: Optional[int] = None) -> int:
+    """The grouped C call on raw addresses: projections is a list of (weight, out, N, ldw, ldo) tuples
+    (or None for a NULL array); returns the glu_status (used by boundary tests)."""
+    lib = library()
+    if projections is None:
+        return lib.glu_grouped_gemv(hidden_ptr, ldh, None, n or 0, M, K, stream_handle)
+    arr = (Projection * max(1, len(projections)))()
+    for i, p in enumerate(projections):
+        arr[i] = Projection(*p)
+    return lib.glu_grouped_gemv(hidden_ptr, ldh, arr, len(projections) if n is None else n, M, K, stream_handle)

@@ -10,6 +10,7 @@
 
 #include "../../include/glu_gemv.h"
 #include "../../include/glu_gemv_tuning.h"
+#include "glu_grouped.h"
 #include "glu_launch.h"
 
 namespace {
@@ -297,6 +298,166 @@ glu_status run(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int6
     return e == hipSuccess ? GLU_OK : fail_launch(e);
 }
 
+// ---- grouped GEMV ------------------------------------------------------------
+
+// VALU grouped kernel: at most 16 chunks per lane per row (K <= 8192), M <= 8 per launch
+glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, const glu_tuning* t, Launch* L)
+{
+    if (M < 0 || K < 0 || rows < 0 || M > kMaxDim || K > kMaxDim || rows > kMaxDim) return GLU_ERR_BAD_SHAPE;
+    const int64_t lim = INT64_MAX / 2;
+    if (mul_overflows(M, K, lim) || mul_overflows(rows, K, lim) || mul_overflows(M, rows, lim)) {
+        return GLU_ERR_BAD_SHAPE;
+    }
+    *L = Launch{};
+    if (t && (t->mfma_segments || t->mfma_hidden || t->mfma_depth)) return GLU_ERR_UNSUPPORTED;
+    if (M == 0 || rows == 0) return GLU_OK;
+    if (K == 0) {
+        L->kernel = GLU_KERNEL_ZERO;
+        L->m_per_launch = (int)(M > kMaxDim ? kMaxDim : M);
+        L->launches = 1;
+        return GLU_OK;
+    }
+    const int forced = t ? t->kernel : 0;
+    if (forced != 0 && forced != GLU_KERNEL_VALU && forced != GLU_KERNEL_GENERIC) return GLU_ERR_UNSUPPORTED;
+    const bool valu = fast && K <= kMaxValuK;
+    if (forced == GLU_KERNEL_VALU && !valu) return GLU_ERR_UNSUPPORTED;
+    if (valu && forced != GLU_KERNEL_GENERIC) {
+        glu::ValuConfig c{};
+        const int64_t nchunks = K / 8;
+        const int64_t cpl = ceil_div(nchunks, glu::kWave);
+        c.NB = cpl <= 8 ? 1 : 2;
+        c.U = (int)ceil_div(cpl, c.NB);
+        c.ragged = (int64_t)c.NB * c.U * glu::kWave != nchunks;
+        int64_t m_pl = M < glu::kValuMaxM ? M : glu::kValuMaxM;
+        if (glu::valu_hidden_in_lds((int)m_pl, c.U, c.NB)) {
+            const int64_t m_fit = glu::kLdsBudget / (2 * K);
+            m_pl = m_pl < m_fit ? m_pl : m_fit;
+        }
+        c.M = (int)m_pl;
+        c.R = (t && t->rows_per_wave) ? t->rows_per_wave : (m_pl <= 4 ? 2 : 1);
+        const int waves = (t && t->waves_per_block) ? t->waves_per_block : kValuDefaultWaves;
+        if (waves < 1 || waves * glu::kWave > glu::kValuMaxThreads) return GLU_ERR_UNSUPPORTED;
+        c.block = waves * glu::kWave;
+        const int64_t groups = ceil_div(rows, c.R);
+        const int64_t grid = (t && t->grid > 0) ? t->grid
+                                                : ceil_div(balanced_waves(groups, (int64_t)kCUs * kValuWavesPerCU), waves);
+        c.grid = (int)(grid < 1 ? 1 : grid);
+        if (!glu::grouped_supported(c)) return GLU_ERR_UNSUPPORTED;
+        glu::ValuConfig last = c;  // the last slice may be narrower: it must be instantiated too
+        last.M = (int)(M - (ceil_div(M, m_pl) - 1) * m_pl);
+        if (!glu::grouped_supported(last)) return GLU_ERR_UNSUPPORTED;
+        L->kernel = GLU_KERNEL_VALU;
+        L->valu = c;
+        L->m_per_launch = (int)m_pl;
+        L->launches = (int)ceil_div(M, m_pl);
+        L->accum_depth = 8 * c.U * c.NB + glu::kWaveSumDepth;
+        return GLU_OK;
+    }
+    if (t && (t->rows_per_wave || t->waves_per_block || t->grid)) return GLU_ERR_UNSUPPORTED;
+    L->kernel = GLU_KERNEL_GENERIC;
+    L->m_per_launch = (int)(M < 8 ? M : 8);
+    L->launches = (int)ceil_div(M, L->m_per_launch);
+    L->generic_grid = (int)ceil_div(rows, glu::kGroupedGenericWaves);
+    L->accum_depth = (int)ceil_div(K, glu::kWave) + glu::kWaveSumDepth;
+    return GLU_OK;
+}
+
+glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n, int64_t M,
+                       int64_t K, void* stream, const glu_tuning* t)
+{
+    if (n < 1 || n > glu::kGroupMax) return GLU_ERR_BAD_SHAPE;
+    if (!proj) return GLU_ERR_NULL_POINTER;
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GLU_ERR_BAD_SHAPE;
+    int64_t rows = 0;
+    for (int i = 0; i < n; ++i) {
+        if (proj[i].N < 0 || proj[i].N > kMaxDim) return GLU_ERR_BAD_SHAPE;
+        rows += proj[i].N;
+    }
+    Launch L;
+    glu_status st = plan_grouped(M, K, rows, true, nullptr, &L);  // shape errors first
+    if (st != GLU_OK) return st;
+    if (M == 0 || rows == 0) return GLU_OK;
+    // strides and extents
+    if (K > 0 && ldh < K) return GLU_ERR_BAD_STRIDE;
+    int64_t h_len = K > 0 ? extent(M, ldh, K) : 0;
+    if (h_len < 0) return GLU_ERR_BAD_STRIDE;
+    int64_t w_len[glu::kGroupMax] = {}, o_len[glu::kGroupMax] = {};
+    for (int i = 0; i < n; ++i) {
+        const glu_projection& p = proj[i];
+        if (p.N == 0) continue;
+        if (p.ldo < p.N || (K > 0 && p.ldw < K)) return GLU_ERR_BAD_STRIDE;
+        o_len[i] = extent(M, p.ldo, p.N);
+        w_len[i] = K > 0 ? extent(p.N, p.ldw, K) : 0;
+        if (o_len[i] < 0 || w_len[i] < 0) return GLU_ERR_BAD_STRIDE;
+    }
+    // pointers
+    if (K > 0 && !hidden) return GLU_ERR_NULL_POINTER;
+    uintptr_t odd = (uintptr_t)hidden, a16 = (uintptr_t)hidden;
+    for (int i = 0; i < n; ++i) {
+        const glu_projection& p = proj[i];
+        if (p.N == 0) continue;
+        if (!p.out || (K > 0 && !p.weight)) return GLU_ERR_NULL_POINTER;
+        odd |= (uintptr_t)p.out | (uintptr_t)p.weight;
+        a16 |= (uintptr_t)p.weight;
+    }
+    if (odd & 1u) return GLU_ERR_MISALIGNED;
+    for (int i = 0; i < n; ++i) {
+        const glu_projection& p = proj[i];
+        if (p.N == 0) continue;
+        if (K > 0 && overlaps(p.out, o_len[i] * 2, hidden, h_len * 2)) return GLU_ERR_ALIASING;
+        for (int j = 0; j < n; ++j) {
+            if (proj[j].N == 0) continue;
+            if (K > 0 && overlaps(p.out, o_len[i] * 2, proj[j].weight, w_len[j] * 2)) return GLU_ERR_ALIASING;
+            if (j != i && overlaps(p.out, o_len[i] * 2, proj[j].out, o_len[j] * 2)) return GLU_ERR_ALIASING;
+        }
+    }
+    bool fast = (a16 & 15u) == 0 && K % 8 == 0 && (ldh & 7) == 0 && ldh <= kMaxFastK;
+    glu::GroupDesc d{};
+    for (int i = 0; i < n; ++i) {
+        const glu_projection& p = proj[i];
+        if (p.N == 0) continue;
+        fast = fast && (p.ldw & 7) == 0 && p.ldw <= kMaxFastK;
+        d.w[d.n] = p.weight;
+        d.out[d.n] = p.out;
+        d.ldw[d.n] = p.ldw;
+        d.ldo[d.n] = p.ldo;
+        d.row0[d.n] = d.rows;
+        d.rows += (int)p.N;
+        ++d.n;
+    }
+    d.row0[d.n] = d.rows;
+    st = plan_grouped(M, K, rows, fast, t, &L);
+    if (st != GLU_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    switch (L.kernel) {
+    case GLU_KERNEL_ZERO:
+        for (int i = 0; i < d.n && e == hipSuccess; ++i) {
+            e = glu::zero_launch(d.out[i], M, d.row0[i + 1] - d.row0[i], d.ldo[i], s);
+        }
+        break;
+    case GLU_KERNEL_VALU:
+    case GLU_KERNEL_GENERIC:
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
+            const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
+            glu::GroupDesc dm = d;
+            for (int i = 0; i < d.n; ++i) dm.out[i] = d.out[i] + m0 * d.ldo[i];
+            if (L.kernel == GLU_KERNEL_VALU) {
+                glu::ValuConfig c = L.valu;
+                c.M = mc;
+                e = glu::grouped_launch(c, hidden + m0 * ldh, ldh, K, dm, s);
+            } else {
+                e = glu::grouped_generic_launch(mc, hidden + m0 * ldh, ldh, K, dm, s);
+            }
+        }
+        break;
+    default:
+        return GLU_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? GLU_OK : fail_launch(e);
+}
+
 void fill_plan(const Launch& L, glu_plan* p)
 {
     p->kernel = L.kernel;
@@ -341,6 +502,35 @@ glu_status glu_dual_gemv_strided_tuned(const uint16_t* hidden, int64_t ldh, cons
                                        int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* tuning)
 {
     return run(hidden, ldh, gate_w, ldg, up_w, ldu, out, ldo, M, N, K, stream, tuning);
+}
+
+glu_status glu_grouped_gemv(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n,
+                            int64_t M, int64_t K, void* stream)
+{
+    return run_grouped(hidden, ldh, proj, n, M, K, stream, nullptr);
+}
+
+glu_status glu_grouped_gemv_tuned(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n,
+                                  int64_t M, int64_t K, void* stream, const glu_tuning* tuning)
+{
+    return run_grouped(hidden, ldh, proj, n, M, K, stream, tuning);
+}
+
+glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, glu_plan* plan)
+{
+    return glu_grouped_gemv_plan_tuned(M, K, rows, fast, nullptr, plan);
+}
+
+glu_status glu_grouped_gemv_plan_tuned(int64_t M, int64_t K, int64_t rows, int fast, const glu_tuning* tuning,
+                                       glu_plan* plan)
+{
+    if (!plan) return GLU_ERR_NULL_POINTER;
+    Launch L;
+    const glu_status st = plan_grouped(M, K, rows, fast != 0, tuning, &L);
+    if (st != GLU_OK) return st;
+    fill_plan(L, plan);
+    if (L.kernel == GLU_KERNEL_GENERIC) plan->block = glu::kGroupedGenericWaves * glu::kWave;
+    return GLU_OK;
 }
 
 glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan)

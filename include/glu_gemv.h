@@ -135,6 +135,52 @@ enum {
 
 glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan);
 
+/*
+ * Grouped GEMV: n projections of one hidden, out_i = bf16(hidden @ W_i^T)
+ * for i < n, each W_i read in place.  This is the pages' single/triple/quad
+ * GEMV (the QKV and GatedDeltaNet input projections) behind the
+ * grouped_linear dispatcher of DeepSpeed PR #8602 (commit notes), without
+ * the GLU epilogue: every output is the fp32 dot product rounded once to
+ * bf16 (round to nearest, ties to even), as a bf16 nn.Linear output.
+ */
+#define GLU_GROUP_MAX 8
+
+typedef struct glu_projection {
+    const uint16_t* weight;  /* [N, K] bf16 bits, row j at weight + j*ldw */
+    uint16_t* out;           /* [M, N] bf16 bits, row m at out + m*ldo */
+    int64_t N;               /* output features (>= 0; 0 skips the projection) */
+    int64_t ldw;             /* weight row stride in elements, >= K */
+    int64_t ldo;             /* output row stride in elements, >= N */
+} glu_projection;
+
+/*
+ * hidden [M, K] at row stride ldh (>= K), 1 <= n <= GLU_GROUP_MAX entries in
+ * proj (host memory, read during the call only; the arrays they point to are
+ * device memory owned by the caller).  Validation before any HIP call, in
+ * this order: n or a size out of range -> GLU_ERR_BAD_SHAPE; a stride below
+ * its row length or an overflowing extent -> GLU_ERR_BAD_STRIDE; M == 0 or
+ * every N == 0 -> GLU_OK, nothing launched; a NULL array that would be read
+ * or written -> GLU_ERR_NULL_POINTER; a pointer not 2-byte aligned ->
+ * GLU_ERR_MISALIGNED; an output overlapping hidden, a weight or another
+ * output -> GLU_ERR_ALIASING.  K == 0 writes +0 everywhere.
+ *
+ * Kernels: with hidden and every weight 16-byte aligned, K, ldh and every ldw
+ * multiples of 8, strides at most 2^25 and K <= 8192, a VALU GEMV that
+ * streams the n weights as one row space, M <= 8 rows of hidden per launch
+ * (larger M in slices of 8, each streaming the weights again); any other
+ * layout takes a generic kernel with 2-byte loads and the same result
+ * contract.  Asynchronous on stream, deterministic, allocates nothing.
+ */
+glu_status glu_grouped_gemv(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n,
+                            int64_t M, int64_t K, void* stream);
+
+/*
+ * The launch glu_grouped_gemv would make for M rows of hidden, K, and `rows`
+ * = sum of N over the projections (host only, no HIP call); `fast` states
+ * whether the layout meets the fast kernel's conditions above.
+ */
+glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, glu_plan* plan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,16 @@ glu_status glu_dual_gemv_strided_tuned(const uint16_t* hidden, int64_t ldh, cons
                                        const uint16_t* up_w, int64_t ldu, uint16_t* out, int64_t ldo,
                                        int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* tuning);
 
+/* glu_grouped_gemv (glu_gemv.h) with overrides: kernel GLU_KERNEL_VALU or
+ * GLU_KERNEL_GENERIC, rows_per_wave 1 or 2 (2 only up to M = 4),
+ * waves_per_block, grid; the MFMA fields must be 0. */
+glu_status glu_grouped_gemv_tuned(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n,
+                                  int64_t M, int64_t K, void* stream, const glu_tuning* tuning);
+
+/* glu_grouped_gemv_plan with overrides (host only, no HIP call). */
+glu_status glu_grouped_gemv_plan_tuned(int64_t M, int64_t K, int64_t rows, int fast, const glu_tuning* tuning,
+                                       glu_plan* plan);
+
 /* glu_dual_gemv_plan with overrides (host only, no HIP call). */
 glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned16,
                                     const glu_tuning* tuning, glu_plan* plan);

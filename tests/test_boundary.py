@@ -223,3 +223,55 @@ def test_python_face_row_strides():
         api._row_stride("x", big.as_strided((4, 24), (16, 1)))  # rows overlap
     with pytest.raises(ValueError):
         api._row_stride("x", big[0, ::2])                    # 1-D with a gap
+
+
+# ---- grouped GEMV -------------------------------------------------------------
+
+def _proj(w, o, N, ldw, ldo):
+    return (w, o, N, ldw, ldo)
+
+
+@pytest.mark.parametrize("hidden,ldh,projs,M,K,status", [
+    (A, 8, [], 1, 8, SHAPE),                                                   # n == 0
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4)] * 9, 1, 8, SHAPE),             # n > 8
+    (A, 8, [_proj(A + 4096, A + 16384, -1, 8, 4)], 1, 8, SHAPE),                # negative N
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4)], -1, 8, SHAPE),
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4)], 1, -8, SHAPE),
+    (A, 8, [_proj(A + 4096, A + 16384, 1 << 31, 8, 1 << 31)], 1, 8, SHAPE),     # rows past 32 bits
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 7, 4)], 1, 8, STRIDE),                # weight rows overlap
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 3)], 1, 8, STRIDE),                # out rows overlap
+    (A, 7, [_proj(A + 4096, A + 16384, 4, 8, 4)], 2, 8, STRIDE),                # hidden rows overlap
+    (A, 8, [_proj(A + 4096, A + 16384, 0, 0, 0)], 1, 8, OK),                    # no output rows
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4)], 0, 8, OK),                    # M == 0
+    (0, 8, [_proj(A + 4096, A + 16384, 4, 8, 4)], 1, 8, NULLP),
+    (A, 8, [_proj(0, A + 16384, 4, 8, 4)], 1, 8, NULLP),
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4), _proj(A + 8192, 0, 4, 8, 4)], 1, 8, NULLP),
+    (A, 8, [_proj(A + 4097, A + 16384, 4, 8, 4)], 1, 8, ALIGN),
+    (A, 8, [_proj(A + 4096, A + 4096 + 32, 4, 8, 4)], 1, 8, ALIAS),             # out inside its weight
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4), _proj(A + 8192, A + 16384 + 4, 4, 8, 4)], 1, 8, ALIAS),  # outs overlap
+    (A, 8, [_proj(A + 4096, A + 16384, 4, 8, 4), _proj(A + 8192, A + 8192 + 8, 4, 8, 4)], 1, 8, ALIAS),
+    (A, 8, [_proj(A + 4096, A + 4, 4, 8, 4)], 1, 8, ALIAS),                     # out overlaps hidden
+])
+def test_grouped_validation_before_any_hip_call(lib, hidden, ldh, projs, M, K, status):
+    n = len(projs)
+    assert api.grouped_gemv_raw(hidden, ldh, projs if projs else [_proj(0, 0, 0, 0, 0)], M, K, n=n) == status
+    assert lib.glu_last_hip_error() == 0
+
+
+def test_grouped_null_projection_array(lib):
+    assert api.grouped_gemv_raw(A, 8, None, 1, 8, n=1) == NULLP
+
+
+def test_grouped_plans():
+    p = api.grouped_plan(1, 2560, 4096 + 1024 + 1024)
+    assert p["kernel"] == api.KERNEL_VALU and p["launches"] == 1
+    assert api.grouped_plan(9, 2560, 100)["launches"] == 2          # slices of 8 rows of hidden
+    assert api.grouped_plan(1, 2560, 100, fast=False)["kernel"] == api.KERNEL_GENERIC
+    assert api.grouped_plan(1, 16384, 100)["kernel"] == api.KERNEL_GENERIC  # past 16 chunks per lane
+    assert api.grouped_plan(4, 0, 100)["kernel"] == api.KERNEL_ZERO
+    assert api.grouped_plan(0, 64, 100)["kernel"] == api.KERNEL_NONE
+    with pytest.raises(api.GluError):
+        api.grouped_plan(1, 64, 100, tuning=api.make_tuning(mfma_segments=4))
+    with pytest.raises(api.GluError):
+        api.grouped_plan(1, 64, 100, fast=False, tuning=api.make_tuning(kernel=api.KERNEL_VALU))
+    assert api.grouped_plan(2, 64, 100, tuning=api.make_tuning(kernel=api.KERNEL_GENERIC))["kernel"] == api.KERNEL_GENERIC
