@@ -193,7 +193,7 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
         sets = max(4, -(-1_400_000_000 // per))
         pool = [[inputs.weights(n_i, K, 400 + 10 * i + t, device=dev)[0] for t, n_i in enumerate(Ns)]
                 for i in range(sets)]
-        for M in (1, 4):
+        for M in (1, 4, 16, 32):
             h = inputs.hidden(M, K, 0).to(dev)
             outs = [torch.empty(M, n_i, dtype=torch.bfloat16, device=dev) for n_i in Ns]
 

@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "glu_grouped_gemv_tuned",
     "glu_grouped_gemv_plan",
     "glu_grouped_gemv_plan_tuned",
+    "glu_grouped_gemv_describe",
     "glu_dual_gemv_strided",
     "glu_dual_gemv_strided_tuned",
     "glu_status_string",
@@ -120,6 +121,9 @@ def library() -> ctypes.CDLL:
     lib.glu_dual_gemv_describe.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning), ctypes.c_char_p,
                                            ctypes.c_int]
     lib.glu_dual_gemv_describe.restype = ctypes.c_int
+    lib.glu_grouped_gemv_describe.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning), ctypes.c_char_p,
+                                              ctypes.c_int]
+    lib.glu_grouped_gemv_describe.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -264,16 +268,25 @@ def dual_gemv_strided_raw(hidden_ptr: int, ldh: int, gate_ptr: int, ldg: int, up
                                            stream_handle, ctypes.byref(tuning))
 
 
-def grouped_plan(M: int, K: int, rows: int, fast: bool = True, tuning: Optional[Tuning] = None) -> dict:
-    """The launch glu_grouped_gemv would make (host only): rows = sum of N over the projections."""
+def grouped_plan(M: int, K: int, rows: int, fast: bool = True, tuning: Optional[Tuning] = None,
+                 mult4: bool = True) -> dict:
+    """The launch glu_grouped_gemv would make (host only): rows = sum of N over the projections,
+    ``fast`` whether the layout is a fast one, ``mult4`` whether every N is a multiple of 4."""
     p = Plan()
     lib = library()
+    flags = int(fast) | (2 if mult4 else 0)
     if tuning is None:
-        st = lib.glu_grouped_gemv_plan(M, K, rows, int(fast), ctypes.byref(p))
+        st = lib.glu_grouped_gemv_plan(M, K, rows, flags, ctypes.byref(p))
     else:
-        st = lib.glu_grouped_gemv_plan_tuned(M, K, rows, int(fast), ctypes.byref(tuning), ctypes.byref(p))
+        st = lib.glu_grouped_gemv_plan_tuned(M, K, rows, flags, ctypes.byref(tuning), ctypes.byref(p))
     _raise_for(st)
-    return p.as_dict()
+    d = p.as_dict()
+    buf = ctypes.create_string_buffer(256)
+    st = lib.glu_grouped_gemv_describe(M, K, rows, flags, ctypes.byref(tuning) if tuning is not None else None,
+                                       buf, 256)
+    _raise_for(st)
+    d["kernel_symbol"] = buf.value.decode()
+    return d
 
 
 def grouped_gemv(hidden: torch.Tensor, weights, outs=None, tuning: Optional[Tuning] = None,

@@ -300,8 +300,12 @@ glu_status run(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int6
 
 // ---- grouped GEMV ------------------------------------------------------------
 
-// VALU grouped kernel: at most 16 chunks per lane per row (K <= 8192), M <= 8 per launch
-glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, const glu_tuning* t, Launch* L)
+// Grouped GEMV launch.  `fast`: the layout meets the fast kernels' conditions;
+// `mult4`: every projection's row count is a multiple of 4.  M >= 2 (or a
+// forced MFMA) with both takes the block-diagonal MFMA kernel, M <= 32 per
+// launch; else the VALU kernel (at most 16 chunks per lane per row, K <= 8192,
+// M <= 8 per launch); else the generic kernel.
+glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult4, const glu_tuning* t, Launch* L)
 {
     if (M < 0 || K < 0 || rows < 0 || M > kMaxDim || K > kMaxDim || rows > kMaxDim) return GLU_ERR_BAD_SHAPE;
     const int64_t lim = INT64_MAX / 2;
@@ -309,7 +313,6 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, const glu
         return GLU_ERR_BAD_SHAPE;
     }
     *L = Launch{};
-    if (t && (t->mfma_segments || t->mfma_hidden || t->mfma_depth)) return GLU_ERR_UNSUPPORTED;
     if (M == 0 || rows == 0) return GLU_OK;
     if (K == 0) {
         L->kernel = GLU_KERNEL_ZERO;
@@ -318,6 +321,52 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, const glu
         return GLU_OK;
     }
     const int forced = t ? t->kernel : 0;
+    const bool mfma_fields = t && (t->mfma_segments || t->mfma_hidden || t->mfma_depth);
+    const bool mfma = fast && mult4 && (forced == GLU_KERNEL_MFMA || (forced == 0 && (M >= 2 || mfma_fields)));
+    if (forced == GLU_KERNEL_MFMA && !mfma) return GLU_ERR_UNSUPPORTED;
+    if (mfma_fields && !mfma) return GLU_ERR_UNSUPPORTED;
+    if (mfma) {
+        if (t && (t->mfma_depth || t->rows_per_wave)) return GLU_ERR_UNSUPPORTED;
+        glu::MfmaConfig c{};
+        const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
+        c.rows = 4;
+        c.MT4 = (int)((m_pl + 3) / 4);
+        const int64_t nchunks = K / 8;
+        const int64_t nsegs = ceil_div(nchunks, 16);
+        if (t && t->mfma_hidden) {
+            c.hidden = t->mfma_hidden - 1;
+        } else {
+            c.hidden = glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsMax ? glu::kHiddenLds
+                                                                                       : glu::kHiddenL2;
+        }
+        if (c.hidden == glu::kHiddenLds && glu::mfma_hidden_lds_bytes((int)m_pl, K) > (size_t)glu::kLdsMax) {
+            return GLU_ERR_UNSUPPORTED;
+        }
+        // one weight stream leaves registers for 5 segments in flight per stage at every MT4 when hidden
+        // sits in LDS (with MT4 x 2 hidden registers per segment, 2 when it comes from L2)
+        const int dflt_u = c.hidden == glu::kHiddenL2 ? 2 : (nsegs % 5 == 0 ? 5 : 4);
+        c.U = (t && t->mfma_segments) ? t->mfma_segments : dflt_u;
+        if (c.U < 1) return GLU_ERR_UNSUPPORTED;
+        c.nsg = (int)ceil_div(nsegs, c.U);
+        c.ragged = (int64_t)c.nsg * c.U * 16 != nchunks;
+        const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
+        if (waves < 1 || waves * glu::kWave > glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
+        c.block = waves * glu::kWave;
+        // 8 waves per CU where two workgroups' hidden fits one CU's LDS, else 4
+        const bool two_fit = c.hidden != glu::kHiddenLds ||
+                             2 * glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsMax;
+        const int64_t per_cu = two_fit ? 2 * kMfmaWavesPerCU : kMfmaWavesPerCU;
+        const int64_t grid = (t && t->grid > 0) ? t->grid
+                                                : ceil_div(balanced_waves(rows / 4, (int64_t)kCUs * per_cu), waves);
+        c.grid = (int)(grid < 1 ? 1 : grid);
+        if (!glu::grouped_mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
+        L->kernel = GLU_KERNEL_MFMA;
+        L->mfma = c;
+        L->m_per_launch = (int)m_pl;
+        L->launches = (int)ceil_div(M, m_pl);
+        L->accum_depth = (int)(2 * (nsegs + 5 + 2));
+        return GLU_OK;
+    }
     if (forced != 0 && forced != GLU_KERNEL_VALU && forced != GLU_KERNEL_GENERIC) return GLU_ERR_UNSUPPORTED;
     const bool valu = fast && K <= kMaxValuK;
     if (forced == GLU_KERNEL_VALU && !valu) return GLU_ERR_UNSUPPORTED;
@@ -374,7 +423,7 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         rows += proj[i].N;
     }
     Launch L;
-    glu_status st = plan_grouped(M, K, rows, true, nullptr, &L);  // shape errors first
+    glu_status st = plan_grouped(M, K, rows, true, true, nullptr, &L);  // shape errors first
     if (st != GLU_OK) return st;
     if (M == 0 || rows == 0) return GLU_OK;
     // strides and extents
@@ -412,11 +461,13 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         }
     }
     bool fast = (a16 & 15u) == 0 && K % 8 == 0 && (ldh & 7) == 0 && ldh <= kMaxFastK;
+    bool mult4 = true;
     glu::GroupDesc d{};
     for (int i = 0; i < n; ++i) {
         const glu_projection& p = proj[i];
         if (p.N == 0) continue;
         fast = fast && (p.ldw & 7) == 0 && p.ldw <= kMaxFastK;
+        mult4 = mult4 && p.N % 4 == 0;
         d.w[d.n] = p.weight;
         d.out[d.n] = p.out;
         d.ldw[d.n] = p.ldw;
@@ -426,7 +477,7 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         ++d.n;
     }
     d.row0[d.n] = d.rows;
-    st = plan_grouped(M, K, rows, fast, t, &L);
+    st = plan_grouped(M, K, rows, fast, mult4, t, &L);
     if (st != GLU_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
@@ -439,11 +490,14 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         break;
     case GLU_KERNEL_VALU:
     case GLU_KERNEL_GENERIC:
+    case GLU_KERNEL_MFMA:
         for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
             const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
             glu::GroupDesc dm = d;
             for (int i = 0; i < d.n; ++i) dm.out[i] = d.out[i] + m0 * d.ldo[i];
-            if (L.kernel == GLU_KERNEL_VALU) {
+            if (L.kernel == GLU_KERNEL_MFMA) {
+                e = glu::grouped_mfma_launch(L.mfma, mc, hidden + m0 * ldh, ldh, K, dm, s);
+            } else if (L.kernel == GLU_KERNEL_VALU) {
                 glu::ValuConfig c = L.valu;
                 c.M = mc;
                 e = glu::grouped_launch(c, hidden + m0 * ldh, ldh, K, dm, s);
@@ -526,7 +580,7 @@ glu_status glu_grouped_gemv_plan_tuned(int64_t M, int64_t K, int64_t rows, int f
 {
     if (!plan) return GLU_ERR_NULL_POINTER;
     Launch L;
-    const glu_status st = plan_grouped(M, K, rows, fast != 0, tuning, &L);
+    const glu_status st = plan_grouped(M, K, rows, (fast & 1) != 0, (fast & 2) != 0, tuning, &L);
     if (st != GLU_OK) return st;
     fill_plan(L, plan);
     if (L.kernel == GLU_KERNEL_GENERIC) plan->block = glu::kGroupedGenericWaves * glu::kWave;
@@ -549,25 +603,25 @@ glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned
     return GLU_OK;
 }
 
-glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16,
-                                  const glu_tuning* tuning, char* buf, int len)
+namespace {
+
+// profiler name of the kernel instance a launch plan runs first
+void describe_launch(const Launch& L, bool grouped, char* buf, int len)
 {
-    if (!buf || len < 1) return GLU_ERR_NULL_POINTER;
-    buf[0] = '\0';
-    Launch L;
-    const glu_status st = plan_launch(M, N, K, aligned16 != 0, tuning, &L);
-    if (st != GLU_OK) return st;
     const char* tf[2] = {"false", "true"};
     switch (L.kernel) {
     case GLU_KERNEL_VALU: {
         const glu::ValuConfig& c = L.valu;
-        snprintf(buf, (size_t)len, "glu::valu_kernel<%d, %d, %d, %d, %s, %s>", c.M, c.R, c.U, c.NB,
-                 tf[glu::valu_hidden_in_lds(c.M, c.U, c.NB)], tf[c.ragged]);
+        snprintf(buf, (size_t)len, "glu::%s<%d, %d, %d, %d, %s, %s>", grouped ? "grouped_kernel" : "valu_kernel",
+                 c.M, c.R, c.U, c.NB, tf[glu::valu_hidden_in_lds(c.M, c.U, c.NB)], tf[c.ragged]);
         break;
     }
     case GLU_KERNEL_MFMA: {
         const glu::MfmaConfig& c = L.mfma;
-        if (c.hidden == glu::kHiddenSlices && c.rows == 8) {
+        if (grouped) {
+            snprintf(buf, (size_t)len, "glu::grouped_mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,
+                     tf[c.hidden == glu::kHiddenLds], tf[c.ragged]);
+        } else if (c.hidden == glu::kHiddenSlices && c.rows == 8) {
             snprintf(buf, (size_t)len, "glu::mfma8_slice_kernel<%d, %d, %d, %s>", (4 * c.MT4 + 7) / 8, c.U,
                      c.depth, tf[c.ragged]);
         } else if (c.hidden == glu::kHiddenSlices) {
@@ -579,10 +633,38 @@ glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16
         }
         break;
     }
-    case GLU_KERNEL_GENERIC: snprintf(buf, (size_t)len, "glu::generic_kernel<%d>", L.m_per_launch); break;
+    case GLU_KERNEL_GENERIC:
+        snprintf(buf, (size_t)len, "glu::%s<%d>", grouped ? "grouped_generic_kernel" : "generic_kernel",
+                 L.m_per_launch);
+        break;
     case GLU_KERNEL_ZERO: snprintf(buf, (size_t)len, "glu::zero_kernel"); break;
     default: snprintf(buf, (size_t)len, "none"); break;
     }
+}
+
+}  // namespace
+
+glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16,
+                                  const glu_tuning* tuning, char* buf, int len)
+{
+    if (!buf || len < 1) return GLU_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Launch L;
+    const glu_status st = plan_launch(M, N, K, aligned16 != 0, tuning, &L);
+    if (st != GLU_OK) return st;
+    describe_launch(L, false, buf, len);
+    return GLU_OK;
+}
+
+glu_status glu_grouped_gemv_describe(int64_t M, int64_t K, int64_t rows, int fast, const glu_tuning* tuning,
+                                     char* buf, int len)
+{
+    if (!buf || len < 1) return GLU_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Launch L;
+    const glu_status st = plan_grouped(M, K, rows, (fast & 1) != 0, (fast & 2) != 0, tuning, &L);
+    if (st != GLU_OK) return st;
+    describe_launch(L, true, buf, len);
     return GLU_OK;
 }
 

@@ -46,21 +46,6 @@ __device__ __forceinline__ RowRef row_ref(const GroupDesc& d, int row)
     return r;
 }
 
-__device__ __forceinline__ void store_row(const GroupDesc& d, int m, int row, uint16_t v)
-{
-    uint16_t* o = d.out[0];
-    int64_t ldo = d.ldo[0];
-    int local = row;
-#pragma unroll
-    for (int t = 1; t < kGroupMax; ++t) {
-        const bool in = t < d.n && row >= d.row0[t];
-        o = in ? d.out[t] : o;
-        ldo = in ? d.ldo[t] : ldo;
-        local = in ? row - d.row0[t] : local;
-    }
-    o[(int64_t)m * ldo + local] = v;
-}
-
 }  // namespace
 
 // hidden [M,K] at row stride ldh (16-byte aligned rows, K % 8 == 0), the
@@ -137,7 +122,7 @@ grouped_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int K, GroupDes
             const int m = rem / R;
             const int r = rem - m * R;
             const int row = (wave_id + (win0 + gl) * nwaves) * R + r;
-            if (row < rows) store_row(d, m, row, f32_to_bf16_rne(res));
+            if (row < rows) group_store(d, m, row, f32_to_bf16_rne(res));
         }
     };
 
@@ -246,7 +231,7 @@ grouped_generic_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int64_t
         const float sum = wave_sum(acc[m]);
         if (lane == m) res = sum;
     }
-    if (lane < M) store_row(d, lane, row, f32_to_bf16_rne(res));
+    if (lane < M) group_store(d, lane, row, f32_to_bf16_rne(res));
 }
 
 namespace {

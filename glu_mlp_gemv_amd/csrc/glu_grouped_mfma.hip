@@ -1,0 +1,274 @@
+// Grouped GEMV at batch M >= 2: the block-diagonal MFMA layout of the dual
+// kernel (glu_mfma.hip) with one weight stream.
+//
+// The virtual row space of the n projections (glu_grouped.hip) is cut into
+// groups of 4 rows; every projection's row count is a multiple of 4, so a
+// group never straddles two projections and is addressed as a wave-uniform
+// base plus 32-bit lane offsets.  v_mfma_f32_16x16x32_bf16 takes A = the
+// group's 4 weight rows x 4 K-blocks of 32 (one 16-byte load per lane reads
+// 4 rows x 256 contiguous bytes) and B = 4 hidden rows x the same blocks; the
+// diagonal blocks of D are the partial dots, summed over segments in the
+// accumulator and over blocks by two DPP steps.  Persistent waves stream
+// their groups in stages of U segments with a two-buffer register pipeline.
+// hidden lives whole in LDS (XOR-swizzled, conflict-free operand reads) or,
+// when it does not fit, is read from L2 with each stage.  The epilogue rounds
+// each sum once to bf16 and writes it to its projection's output row.
+#include "glu_device.h"
+#include "glu_grouped.h"
+#include "glu_mfma_common.h"
+
+namespace glu {
+
+namespace {
+
+// base of virtual row `row` (a multiple of 4) and the stride of its projection
+struct GroupRef {
+    const uint16_t* w;
+    int64_t ldw;
+};
+
+__device__ __forceinline__ GroupRef group_ref(const GroupDesc& d, int row)
+{
+    const uint16_t* w = d.w[0];
+    int64_t ldw = d.ldw[0];
+    int local = row;
+#pragma unroll
+    for (int t = 1; t < kGroupMax; ++t) {
+        const bool in = t < d.n && row >= d.row0[t];
+        w = in ? d.w[t] : w;
+        ldw = in ? d.ldw[t] : ldw;
+        local = in ? row - d.row0[t] : local;
+    }
+    return GroupRef{w + (int64_t)local * ldw, ldw};
+}
+
+}  // namespace
+
+// MT4: hidden-row tiles of 4 (M <= 4*MT4); U: 128-element segments per stage;
+// nsg: stages per group (nsg*U*16 >= K/8, equality unless RAGGED); d.rows % 4 == 0.
+// Dynamic LDS when HLDS: M * K * 2 bytes, or M * (K/8 + 1) * 16 when K/8 is not a multiple of 4
+// (up to the 160 KiB of one workgroup: M = 32 at K = 2560).
+template <int MT4, int U, bool HLDS, bool RAGGED>
+__global__ void __launch_bounds__(kMfmaMaxThreads)
+grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int K, GroupDesc d, int nsg)
+{
+    extern __shared__ u32x4_t h_lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + threadIdx.x / kWave);
+    const int nwaves = gridDim.x * wpb;
+    const int nchunks = K >> 3;
+    const uint32_t ldh8 = (uint32_t)(ldh >> 3);
+    const int i16 = lane & 15;
+    const int rho_a = i16 >> 2;                     // weight row of this lane's A data
+    const int cseg = (i16 & 3) * 4 + (lane >> 4);   // 16-byte chunk within a 256-byte segment
+    const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
+
+    const bool hswz = (nchunks & 3) == 0;
+    const int hpitch = hswz ? nchunks : nchunks + 1;
+    if constexpr (HLDS) {
+        // kStageLoads loads in flight per lane (indices past the end re-read the last chunk), then their stores
+        constexpr int kStageLoads = 8;
+        const int total = M * nchunks;
+        for (int i0 = threadIdx.x; i0 < total; i0 += kStageLoads * (int)blockDim.x) {
+            u32x4_t v[kStageLoads];
+#pragma unroll
+            for (int q = 0; q < kStageLoads; ++q) {
+                const int i = min(i0 + q * (int)blockDim.x, total - 1);
+                const int m = i / nchunks;
+                v[q] = h4[(uint32_t)m * ldh8 + (uint32_t)(i - m * nchunks)];
+            }
+#pragma unroll
+            for (int q = 0; q < kStageLoads; ++q) {
+                const int i = i0 + q * (int)blockDim.x;
+                if (i < total) {
+                    const int m = i / nchunks;
+                    const int c = i - m * nchunks;
+                    h_lds[m * hpitch + (hswz ? c ^ lds_swz4(m) : c)] = v[q];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    const int ngroups = d.rows / 4;
+    if (wave_id >= ngroups) return;  // no barrier follows
+    const int my_groups = (ngroups - 1 - wave_id) / nwaves + 1;
+    const int nstages = my_groups * nsg;
+
+    int hrow[MT4];  // hidden rows of this lane's B data (rows past M repeat row M-1, never stored)
+#pragma unroll
+    for (int t = 0; t < MT4; ++t) hrow[t] = min(4 * t + rho_a, M - 1);
+
+    constexpr int BT = HLDS ? 1 : MT4;
+    constexpr int BU = HLDS ? 1 : U;
+
+    auto load = [&](int s, u32x4_t (&A)[U], u32x4_t (&Bq)[BT][BU]) {
+        const int gi = s / nsg;
+        const int sb = s - gi * nsg;
+        const GroupRef ref = group_ref(d, 4 * (wave_id + gi * nwaves));
+        const char* wp = reinterpret_cast<const char*>(ref.w);
+        const uint32_t ldw8 = (uint32_t)(ref.ldw >> 3);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int c = (sb * U + u) * 16 + cseg;
+            if (RAGGED) c = min(c, nchunks - 1);
+            const uint32_t off = ((uint32_t)rho_a * ldw8 + (uint32_t)c) * 16u;  // bytes, below 4 rows at the stride
+            A[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + off));
+        }
+        if constexpr (!HLDS) {
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    int c = (sb * U + u) * 16 + cseg;
+                    if (RAGGED) c = min(c, nchunks - 1);
+                    const uint32_t off = ((uint32_t)hrow[t] * ldh8 + (uint32_t)c) * 16u;
+                    Bq[t][u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(hidden) + off);
+                }
+            }
+        }
+    };
+
+    f32x4_t acc[MT4];
+
+    auto finish_group = [&](int g) {
+        // useful entry e = lane % 4, then the quad sum over the four blocks
+        const int e = lane & 3;
+        float res[(MT4 + 3) / 4];
+#pragma unroll
+        for (int t = 0; t < MT4; ++t) {
+            const f32x4_t dd = acc[t];
+            float v = e == 0 ? dd[0] : e == 1 ? dd[1] : e == 2 ? dd[2] : dd[3];
+            v = dpp_add<0xB1>(v);  // lane ^ 1
+            v = dpp_add<0x4E>(v);  // lane ^ 2
+            if (e == (t & 3)) res[t >> 2] = v;
+        }
+        // lane l keeps tiles t with t % 4 == l % 4: hidden row 4t + (l%16)/4, virtual row 4g + l/16
+        const int row = 4 * g + (lane >> 4);
+#pragma unroll
+        for (int k = 0; k < (MT4 + 3) / 4; ++k) {
+            const int t = 4 * k + e;
+            const int m = 4 * t + ((lane & 15) >> 2);
+            if (t < MT4 && m < M) group_store(d, m, row, f32_to_bf16_rne(res[k]));
+        }
+    };
+
+    auto compute = [&](int s, const u32x4_t (&A)[U], const u32x4_t (&Bq)[BT][BU]) {
+        const int gi = s / nsg;
+        const int sb = s - gi * nsg;
+        if (sb == 0) {
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = (sb * U + u) * 16 + cseg;
+            const bool ok = !RAGGED || c < nchunks;
+            const int cc = RAGGED ? min(c, nchunks - 1) : c;
+            const u32x4_t a = RAGGED ? (ok ? A[u] : z) : A[u];
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+                u32x4_t b;
+                if constexpr (HLDS) {
+                    b = h_lds[hrow[t] * hpitch + (hswz ? cc ^ lds_swz4(hrow[t]) : cc)];
+                } else {
+                    b = Bq[t][u];
+                }
+                if constexpr (RAGGED) b = ok ? b : z;
+                acc[t] = mfma16(a, b, acc[t]);
+            }
+        }
+        if (sb == nsg - 1) finish_group(wave_id + gi * nwaves);
+    };
+
+    u32x4_t a0[U], a1[U], b0[BT][BU], b1[BT][BU];
+    load(0, a0, b0);
+    int s = 0;
+    while (true) {
+        if (s + 1 >= nstages) {
+            compute(s, a0, b0);
+            break;
+        }
+        load(s + 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before any of this stage's math
+        compute(s, a0, b0);
+        ++s;
+        if (s + 1 >= nstages) {
+            compute(s, a1, b1);
+            break;
+        }
+        load(s + 1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s, a1, b1);
+        ++s;
+    }
+}
+
+namespace {
+
+using GroupedMfmaFn = void (*)(const uint16_t*, int64_t, int, int, GroupDesc, int);
+
+template <int MT4, bool HL, bool RG>
+GroupedMfmaFn pick_u(int U)
+{
+    switch (U) {
+    case 2: return grouped_mfma_kernel<MT4, 2, HL, RG>;
+    case 4: if constexpr (HL) return grouped_mfma_kernel<MT4, 4, HL, RG>; else return nullptr;
+    case 5: if constexpr (HL) return grouped_mfma_kernel<MT4, 5, HL, RG>; else return nullptr;
+    default: return nullptr;
+    }
+}
+
+template <int MT4>
+GroupedMfmaFn pick_flags(int U, bool hlds, bool ragged)
+{
+    if (hlds) return ragged ? pick_u<MT4, true, true>(U) : pick_u<MT4, true, false>(U);
+    return ragged ? pick_u<MT4, false, true>(U) : pick_u<MT4, false, false>(U);
+}
+
+GroupedMfmaFn pick(int mt4, int U, bool hlds, bool ragged)
+{
+    switch (mt4) {
+    case 1: return pick_flags<1>(U, hlds, ragged);
+    case 2: return pick_flags<2>(U, hlds, ragged);
+    case 3: return pick_flags<3>(U, hlds, ragged);
+    case 4: return pick_flags<4>(U, hlds, ragged);
+    case 5: return pick_flags<5>(U, hlds, ragged);
+    case 6: return pick_flags<6>(U, hlds, ragged);
+    case 7: return pick_flags<7>(U, hlds, ragged);
+    case 8: return pick_flags<8>(U, hlds, ragged);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+bool grouped_mfma_supported(const MfmaConfig& c)
+{
+    if (c.rows != 4 || (c.hidden != kHiddenLds && c.hidden != kHiddenL2)) return false;
+    if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
+    return pick(c.MT4, c.U, c.hidden == kHiddenLds, c.ragged) != nullptr;
+}
+
+hipError_t grouped_mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, int64_t ldh, int64_t K,
+                               const GroupDesc& d, hipStream_t stream)
+{
+    const int mt4 = (M + 3) / 4;
+    const bool hlds = c.hidden == kHiddenLds;
+    GroupedMfmaFn fn = pick(mt4, c.U, hlds, c.ragged);
+    if (!fn || M < 1 || d.rows % 4 != 0) return hipErrorInvalidValue;
+    const size_t lds = hlds ? mfma_hidden_lds_bytes(M, K) : 0;
+    if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
+    if (lds > (size_t)kLdsBudget) {
+        // past 64 KiB of dynamic LDS the launch states its size to the runtime first
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.block), lds, stream, hidden, ldh, M, (int)K, d, c.nsg);
+    return hipGetLastError();
+}
+
+}  // namespace glu

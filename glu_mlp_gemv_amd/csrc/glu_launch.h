@@ -11,6 +11,7 @@ constexpr int kWaveSumDepth = 6;  // fp32 addition levels of the wave64 butterfl
 constexpr int kValuMaxM = 8;
 constexpr int kValuMaxThreads = 512;
 constexpr int kLdsBudget = 64 * 1024;  // dynamic LDS per workgroup, bytes
+constexpr int kLdsMax = 160 * 1024;    // LDS of one workgroup on gfx950, bytes
 constexpr int kMfmaMaxThreads = 256;  // 4 waves: the compiler may use AGPRs for the accumulators
 
 struct ValuConfig {

@@ -164,10 +164,12 @@ typedef struct glu_projection {
  * GLU_ERR_MISALIGNED; an output overlapping hidden, a weight or another
  * output -> GLU_ERR_ALIASING.  K == 0 writes +0 everywhere.
  *
- * Kernels: with hidden and every weight 16-byte aligned, K, ldh and every ldw
- * multiples of 8, strides at most 2^25 and K <= 8192, a VALU GEMV that
- * streams the n weights as one row space, M <= 8 rows of hidden per launch
- * (larger M in slices of 8, each streaming the weights again); any other
+ * Kernels ("fast layout": hidden and every weight 16-byte aligned, K, ldh and
+ * every ldw multiples of 8, strides at most 2^25): for M >= 2 with a fast
+ * layout and every N a multiple of 4, a block-diagonal MFMA GEMV, M <= 32
+ * rows of hidden per launch; else, with a fast layout and K <= 8192, a VALU
+ * GEMV, M <= 8 rows per launch (both stream the n weights as one row space;
+ * larger M runs in slices, each streaming the weights again); any other
  * layout takes a generic kernel with 2-byte loads and the same result
  * contract.  Asynchronous on stream, deterministic, allocates nothing.
  */
@@ -176,8 +178,9 @@ glu_status glu_grouped_gemv(const uint16_t* hidden, int64_t ldh, const glu_proje
 
 /*
  * The launch glu_grouped_gemv would make for M rows of hidden, K, and `rows`
- * = sum of N over the projections (host only, no HIP call); `fast` states
- * whether the layout meets the fast kernel's conditions above.
+ * = sum of N over the projections (host only, no HIP call).  `fast` is a
+ * bit set: 1 = the layout is a fast layout (above), 2 = every N is a
+ * multiple of 4.
  */
 glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, glu_plan* plan);
 

@@ -45,9 +45,10 @@ glu_status glu_dual_gemv_strided_tuned(const uint16_t* hidden, int64_t ldh, cons
                                        const uint16_t* up_w, int64_t ldu, uint16_t* out, int64_t ldo,
                                        int64_t M, int64_t N, int64_t K, void* stream, const glu_tuning* tuning);
 
-/* glu_grouped_gemv (glu_gemv.h) with overrides: kernel GLU_KERNEL_VALU or
- * GLU_KERNEL_GENERIC, rows_per_wave 1 or 2 (2 only up to M = 4),
- * waves_per_block, grid; the MFMA fields must be 0. */
+/* glu_grouped_gemv (glu_gemv.h) with overrides: kernel GLU_KERNEL_VALU,
+ * GLU_KERNEL_MFMA or GLU_KERNEL_GENERIC; for VALU rows_per_wave 1 or 2 (2
+ * only up to M = 4); for MFMA mfma_segments (2, 4, 5; 2 with hidden read
+ * from L2) and mfma_hidden 1 or 2; waves_per_block and grid for both. */
 glu_status glu_grouped_gemv_tuned(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n,
                                   int64_t M, int64_t K, void* stream, const glu_tuning* tuning);
 
@@ -68,6 +69,11 @@ glu_status glu_dual_gemv_plan_tuned(int64_t M, int64_t N, int64_t K, int aligned
  */
 glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16,
                                   const glu_tuning* tuning, char* buf, int len);
+
+/* The same for glu_grouped_gemv: arguments as glu_grouped_gemv_plan_tuned
+ * (glu_gemv.h), e.g. "glu::grouped_mfma_kernel<1, 5, true, false>". */
+glu_status glu_grouped_gemv_describe(int64_t M, int64_t K, int64_t rows, int fast, const glu_tuning* tuning,
+                                     char* buf, int len);
 
 #ifdef __cplusplus
 }

@@ -265,13 +265,36 @@ def test_grouped_null_projection_array(lib):
 def test_grouped_plans():
     p = api.grouped_plan(1, 2560, 4096 + 1024 + 1024)
     assert p["kernel"] == api.KERNEL_VALU and p["launches"] == 1
-    assert api.grouped_plan(9, 2560, 100)["launches"] == 2          # slices of 8 rows of hidden
+    assert p["kernel_symbol"] == "glu::grouped_kernel<1, 2, 5, 1, false, false>"
+    # M >= 2 with every N a multiple of 4: the MFMA kernel, slices of 32 rows of hidden
+    p = api.grouped_plan(9, 2560, 100)
+    assert p["kernel"] == api.KERNEL_MFMA and p["launches"] == 1
+    assert p["kernel_symbol"] == "glu::grouped_mfma_kernel<3, 5, true, false>"
+    assert api.grouped_plan(33, 2560, 100)["launches"] == 2
+    # hidden in LDS up to one workgroup's 160 KiB (32 rows at K = 2560), else read through L2
+    assert api.grouped_plan(16, 2560, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<4, 5, true, false>"
+    assert api.grouped_plan(32, 2560, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 5, true, false>"
+    assert api.grouped_plan(32, 2568, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 2, false, true>"
+    # otherwise the VALU kernel in slices of 8
+    p = api.grouped_plan(9, 2560, 100, mult4=False)
+    assert p["kernel"] == api.KERNEL_VALU and p["launches"] == 2
+    assert api.grouped_plan(2, 2560, 100, fast=False)["kernel"] == api.KERNEL_GENERIC
     assert api.grouped_plan(1, 2560, 100, fast=False)["kernel"] == api.KERNEL_GENERIC
     assert api.grouped_plan(1, 16384, 100)["kernel"] == api.KERNEL_GENERIC  # past 16 chunks per lane
     assert api.grouped_plan(4, 0, 100)["kernel"] == api.KERNEL_ZERO
     assert api.grouped_plan(0, 64, 100)["kernel"] == api.KERNEL_NONE
-    with pytest.raises(api.GluError):
-        api.grouped_plan(1, 64, 100, tuning=api.make_tuning(mfma_segments=4))
+    # MFMA fields ask for the MFMA kernel, which needs a fast layout and every N a multiple of 4
+    t = api.make_tuning(mfma_segments=4)
+    assert api.grouped_plan(1, 64, 100, tuning=t)["kernel"] == api.KERNEL_MFMA
+    for bad in (dict(mult4=False), dict(fast=False)):
+        with pytest.raises(api.GluError):
+            api.grouped_plan(1, 64, 100, tuning=t, **bad)
+        with pytest.raises(api.GluError):
+            api.grouped_plan(4, 64, 100, tuning=api.make_tuning(kernel=api.KERNEL_MFMA), **bad)
+    for bad in (dict(mfma_depth=2), dict(mfma_segments=3), dict(mfma_hidden=3), dict(rows_per_wave=8),
+                dict(kernel=api.KERNEL_MFMA, mfma_segments=4, mfma_hidden=2)):
+        with pytest.raises(api.GluError):
+            api.grouped_plan(4, 2560, 100, tuning=api.make_tuning(**bad))
     with pytest.raises(api.GluError):
         api.grouped_plan(1, 64, 100, fast=False, tuning=api.make_tuning(kernel=api.KERNEL_VALU))
     assert api.grouped_plan(2, 64, 100, tuning=api.make_tuning(kernel=api.KERNEL_GENERIC))["kernel"] == api.KERNEL_GENERIC

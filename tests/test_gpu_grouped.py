@@ -35,30 +35,54 @@ def weight_set(Ns, K, seed):
 
 
 def check_all(h, ws, outs, tuning=None, fast=True, label=""):
+    """Every output within the per-output bar and each projection's mean error within its bar; the
+    bit-exact fraction over all outputs of the call."""
     M, K = h.shape
     rows = sum(w.shape[0] for w in ws)
-    plan = api.grouped_plan(M, K, rows, fast, tuning)
+    mult4 = all(w.shape[0] % 4 == 0 for w in ws)
+    plan = api.grouped_plan(M, K, rows, fast, tuning, mult4)
     print(f"[grouped] {label} M={M} K={K} Ns={[w.shape[0] for w in ws]} plan={plan}", flush=True)
+    reps = []
     for i, (w, o) in enumerate(zip(ws, outs)):
         ref = oracle.linear(bits(h), bits(w), with_pre=True)
         rep = check.compare_linear(bits(o), ref, depth=plan["accum_depth"], k_len=K)
         print(f"[grouped]   projection {i}: {rep.summary()}", flush=True)
-        assert rep.ok, (i, rep.summary())
+        assert rep.failures == 0 and rep.mean_rel <= 3e-3, (i, rep.summary())
+        reps.append(rep)
+    n, inexact = sum(r.n for r in reps), sum(r.inexact for r in reps)
+    print(f"[grouped]   call: {n - inexact} of {n} outputs bit-exact", flush=True)
+    assert check.pooled_bit_exact_ok(reps), (inexact, n)
 
 
+MFMA = api.KERNEL_MFMA
 CASES = [
-    ((4096, 1024, 1024), 2560, 1, {}),        # QKV-like triple at decode
-    ((4096, 1024, 1024), 2560, 4, {}),
+    ((4096, 1024, 1024), 2560, 1, {}),        # QKV-like triple at decode (VALU)
+    ((4096, 1024, 1024), 2560, 4, {}),        # MFMA, hidden in LDS
+    ((4096, 1024, 1024), 2560, 16, {}),       # MFMA, 80 KiB of hidden in LDS
+    ((4096, 1024, 1024), 2560, 32, {}),       # MFMA, 160 KiB of hidden in LDS
+    ((1024, 512), 4096, 32, {}),              # MFMA, hidden via L2
     ((2048, 1024, 32, 32), 2560, 1, {}),      # GDN-input-like quad
+    ((2048, 1024, 32, 32), 2560, 2, {}),
     ((2048, 1024, 32, 32), 2560, 8, {}),
-    ((1, 3, 300), 1024, 3, {}),               # ragged projection sizes
-    ((7, 0, 64, 1, 129, 2, 33, 5), 512, 2, {}),  # eight projections, one empty
+    ((1, 3, 300), 1024, 3, {}),               # ragged projection sizes: VALU
+    ((7, 0, 64, 1, 129, 2, 33, 5), 512, 2, {}),  # eight projections, one empty: VALU
+    ((8, 0, 64, 4, 128, 12, 32, 4), 512, 6, {}),  # eight projections, one empty: MFMA
     ((1000, 24), 8192, 1, {}),                # two stages per row (K/8 > 512)
-    ((640, 640), 4104, 5, {}),                # ragged K
-    ((300, 200), 1024, 9, {}),                # slices of 8 rows of hidden
-    ((64, 65), 2048, 40, {}),
+    ((1000, 24), 8192, 3, {}),                # MFMA, K/8 = 1024 chunks in LDS
+    ((640, 640), 4104, 5, {}),                # ragged K, padded LDS rows
+    ((12, 4), 2056, 16, {}),                  # ragged K, hidden in LDS
+    ((12, 4), 4104, 32, {}),                  # ragged K, hidden via L2
+    ((300, 200), 1024, 9, {}),                # MFMA, three hidden tiles
+    ((1024, 256), 1024, 33, {}),              # slices of 32 rows of hidden, then 1
+    ((64, 65), 2048, 40, {}),                 # N % 4 != 0: VALU in slices of 8
     ((500, 77), 1024, 2, dict(kernel=api.KERNEL_GENERIC)),
     ((500, 77), 1024, 4, dict(kernel=api.KERNEL_VALU, rows_per_wave=1, waves_per_block=2, grid=5)),
+    ((4096, 1024), 2560, 1, dict(kernel=MFMA)),
+    ((500, 76), 1024, 4, dict(kernel=MFMA, mfma_hidden=2)),
+    ((1024, 512), 4096, 8, dict(mfma_segments=4)),
+    ((1024, 512), 4096, 7, dict(kernel=MFMA, mfma_segments=2, grid=3, waves_per_block=2)),
+    ((256, 8), 2048, 12, dict(kernel=MFMA, grid=1000)),
+    ((4096, 1024, 1024), 2560, 4, dict(kernel=api.KERNEL_VALU)),
 ]
 
 
@@ -86,11 +110,19 @@ def test_grouped_generic_layouts():
         check_all(h, ws, [o.cpu() for o in outs], fast=False, label=f"generic K={K} pad={pad}")
 
 
-def test_grouped_strided_views_and_canaries():
-    """Weights as column slices of a wider block (NaN in the gaps), outputs into wider rows."""
-    M, K = 4, 2560
+STRIDED = [((700, 130, 64), 4), ((700, 132, 64), 4), ((700, 132, 64), 16)]
+
+
+@pytest.mark.parametrize("Ns,M", STRIDED)
+def test_grouped_strided_views_and_canaries(Ns, M):
+    """Weights as column slices of a wider block (NaN in the gaps), hidden rows padded with NaN,
+    outputs into wider rows."""
+    K = 2560
     h = inputs.hidden(M, K, 33)
-    ws = weight_set((700, 130, 64), K, 33)
+    ws = weight_set(Ns, K, 33)
+    hbuf = torch.full((M, K + 8), NAN, dtype=torch.int16).view(torch.bfloat16)
+    hbuf[:, :K] = h
+    hv = hbuf.to(DEV)[:, :K]
     views, bufs_out, outs = [], [], []
     for w in ws:
         buf = torch.full((w.shape[0], K + 24), NAN, dtype=torch.int16).view(torch.bfloat16)
@@ -99,7 +131,7 @@ def test_grouped_strided_views_and_canaries():
         ob = torch.full((M, w.shape[0] + 5), CANARY, dtype=torch.int16, device=DEV).view(torch.bfloat16)
         bufs_out.append(ob)
         outs.append(ob[:, :w.shape[0]])
-    api.grouped_gemv(h.to(DEV), views, outs=outs)
+    api.grouped_gemv(hv, views, outs=outs)
     torch.cuda.synchronize()
     check_all(h, ws, [o.cpu() for o in outs], label="strided")
     for ob, w in zip(bufs_out, ws):
@@ -110,18 +142,24 @@ def test_grouped_strided_views_and_canaries():
         assert np.array_equal(bits(a), bits(b)), "strided and packed runs differ"
 
 
-def test_grouped_rows_independent_of_batch_and_group():
-    """A row's result depends on nothing but its own hidden row and weight row: batched rows equal
-    single-row calls bitwise, and a projection's output does not change with its companions."""
+@pytest.mark.parametrize("kernel", [api.KERNEL_VALU, api.KERNEL_MFMA])
+def test_grouped_rows_independent_of_batch_and_group(kernel):
+    """Within one kernel a row's result depends on nothing but its own hidden row and weight row:
+    batched rows equal single-row calls bitwise, and a projection's output does not change with its
+    companions.  (The VALU and MFMA kernels sum in different orders, so a batch and a single row
+    are compared on the same kernel.)"""
     K = 2560
+    t = api.make_tuning(kernel=kernel)
     h = inputs.hidden(6, K, 34).to(DEV)
     ws = [w.to(DEV) for w in weight_set((1500, 300, 32), K, 34)]
-    batched = api.grouped_gemv(h, ws)
-    alone = api.grouped_gemv(h, ws[1:2])
+    plan6, plan1 = api.grouped_plan(6, K, 1832, tuning=t), api.grouped_plan(1, K, 1832, tuning=t)
+    print(f"[grouped] rows: {plan6['kernel_symbol']} vs {plan1['kernel_symbol']}", flush=True)
+    batched = api.grouped_gemv(h, ws, tuning=t)
+    alone = api.grouped_gemv(h, ws[1:2], tuning=t)
     torch.cuda.synchronize()
     assert np.array_equal(bits(batched[1]), bits(alone[0]))
     for m in range(6):
-        single = api.grouped_gemv(h[m], ws)
+        single = api.grouped_gemv(h[m], ws, tuning=t)
         torch.cuda.synchronize()
         for b, s in zip(batched, single):
             assert np.array_equal(bits(b[m]), bits(s)), m
