@@ -157,6 +157,37 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
             del g
         del pool
         torch.cuda.empty_cache()
+    # large batches (prefill-like): the tiled GEMM, and the 32-row chunked MFMA path it replaces
+    for (K, N), Ms in (((5120, 17408), (64, 128, 256, 512, 1024)), ((2560, 9216), (64, 256, 1024))):
+        per = 2 * N * K * 2
+        sets = max(4, -(-1_400_000_000 // per))
+        pool = [inputs.weights(N, K, 500 + i, device=dev) for i in range(sets)]
+        for M in Ms:
+            h = inputs.hidden(M, K, 0).to(dev)
+            out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            variants = [("gemm", None)]
+            if M in (64, 256):
+                variants.append(("mfma_chunks", api.make_tuning(kernel=api.KERNEL_MFMA)))
+            for kname, t in variants:
+                def one_pass():
+                    for wg, wu in pool:
+                        api.dual_gemv(h, wg, wu, out=out, tuning=t)
+                g = capture(torch, one_pass)
+                r = max(3, reps // max(1, M // 64))
+                ms = time_region(torch, g.replay, r, 1, stream)
+                us = ms * 1e3 / (r * sets)
+                b = algorithmic_bytes(M, N, K)
+                flops = 4 * M * N * K
+                res.append({"workload": f"prefill_k{K}_n{N}", "M": M, "K": K, "N": N, "us_per_call": round(us, 3),
+                            "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                            "TFLOPs": round(flops / us / 1e6, 2),
+                            "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "kernel": api.plan(M, N, K, True, t)["kernel_symbol"], "variant": kname,
+                            "pool_sets": sets})
+                print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+                del g
+        del pool
+        torch.cuda.empty_cache()
     # row-strided operands: gate and up as the two column halves of one fused
     # [N, 2K] block (each keeps the fused row stride 2K), at the decode shape
     N, K = STACK["N"], STACK["K"]

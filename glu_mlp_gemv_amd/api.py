@@ -21,9 +21,9 @@ LIBRARY_PATH = _build.LIBRARY
 GLU_OK = 0
 GLU_ERR_UNSUPPORTED = 6
 GLU_ERR_BAD_STRIDE = 7
-KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC = range(5)
+KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC, KERNEL_GEMM = range(6)
 KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
-                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic"}
+                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic", KERNEL_GEMM: "gemm"}
 
 EXPORTED_SYMBOLS = (
     "glu_dual_gemv",
@@ -65,7 +65,7 @@ class Plan(ctypes.Structure):
 class Tuning(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("rows_per_wave", ctypes.c_int), ("waves_per_block", ctypes.c_int),
                 ("grid", ctypes.c_int), ("mfma_segments", ctypes.c_int), ("mfma_hidden", ctypes.c_int),
-                ("mfma_depth", ctypes.c_int)]
+                ("mfma_depth", ctypes.c_int), ("gemm_tile_n", ctypes.c_int), ("gemm_tile_m", ctypes.c_int)]
 
 
 class Projection(ctypes.Structure):

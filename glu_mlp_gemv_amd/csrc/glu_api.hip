@@ -28,6 +28,8 @@ constexpr int kValuDefaultWaves = 4;       // waves per workgroup
 constexpr int kValuWavesPerCU = 3;         // persistent waves per CU the grid aims for
 constexpr int kMfmaDefaultWaves = 4;
 constexpr int kMfmaWavesPerCU = 4;
+constexpr int64_t kGemmSlice = 65536;        // rows of hidden per GEMM launch
+constexpr int64_t kGemmMaxN = 1 << 30;       // GEMM tile row indices stay in 32 bits
 constexpr int kMfmaSlice = 32;
 
 bool mul_overflows(int64_t a, int64_t b, int64_t limit)
@@ -41,6 +43,8 @@ struct Launch {
     int launches = 0;
     glu::ValuConfig valu{};
     glu::MfmaConfig mfma{};
+    glu::GemmConfig gemm{};
+    int gemm_grid = 0;
     int generic_grid = 0;
     int accum_depth = 0;
 };
@@ -179,6 +183,39 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     return GLU_OK;
 }
 
+// Tiled GEMM: bm = 64 hidden rows per tile up to M = 64, else 128; bn = 128
+// weight rows per tile where that still gives every CU a tile, else 64.
+glu_status plan_gemm(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
+{
+    if (N > kGemmMaxN) return GLU_ERR_UNSUPPORTED;
+    if (t && (t->rows_per_wave || t->waves_per_block || t->grid || t->mfma_segments || t->mfma_hidden ||
+              t->mfma_depth)) {
+        return GLU_ERR_UNSUPPORTED;
+    }
+    glu::GemmConfig c{};
+    c.bm = (t && t->gemm_tile_m) ? t->gemm_tile_m : (M <= 64 ? 64 : 128);
+    c.ktail = K % 64 != 0;
+    int64_t m_pl = M < kGemmSlice ? M : kGemmSlice;
+    if (t && t->gemm_tile_n) {
+        c.bn = t->gemm_tile_n;
+    } else {
+        c.bn = 128;
+        if (glu::gemm_grid(c, m_pl, N) < kCUs) c.bn = 64;
+    }
+    if (!glu::gemm_supported(c)) return GLU_ERR_UNSUPPORTED;
+    // the grid of one launch stays below 2^30 workgroups
+    const int64_t nbn = ceil_div(N, c.bn);
+    const int64_t max_m = (((int64_t)1 << 30) / nbn) * c.bm;
+    if (m_pl > max_m) m_pl = max_m;
+    L->kernel = GLU_KERNEL_GEMM;
+    L->gemm = c;
+    L->m_per_launch = (int)m_pl;
+    L->launches = (int)ceil_div(M, m_pl);
+    L->gemm_grid = (int)glu::gemm_grid(c, m_pl, N);
+    L->accum_depth = (int)(2 * (ceil_div(K, 32) + 6));
+    return GLU_OK;
+}
+
 glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const glu_tuning* t, Launch* L)
 {
     if (M < 0 || N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return GLU_ERR_BAD_SHAPE;
@@ -197,12 +234,17 @@ glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const gl
     const int forced = t ? t->kernel : 0;
     const bool fast = aligned16 && (K % 8 == 0) && K <= kMaxFastK;
     if (forced != 0 && forced != GLU_KERNEL_GENERIC && !fast) return GLU_ERR_UNSUPPORTED;
+    const bool gemm_fields = t && (t->gemm_tile_n || t->gemm_tile_m);
+    if (gemm_fields && forced != 0 && forced != GLU_KERNEL_GEMM) return GLU_ERR_UNSUPPORTED;
     if (forced == GLU_KERNEL_VALU) return plan_valu(M, N, K, t, L);
     if (forced == GLU_KERNEL_MFMA) return plan_mfma(M, N, K, t, L);
+    if (forced == GLU_KERNEL_GEMM) return plan_gemm(M, N, K, t, L);
     if (forced == 0 && fast) {
+        if (gemm_fields || (M > kMfmaSlice && N <= kGemmMaxN)) return plan_gemm(M, N, K, t, L);
         if (M == 1 && K <= kValuMaxDefaultK) return plan_valu(M, N, K, t, L);
         return plan_mfma(M, N, K, t, L);
     }
+    if (gemm_fields) return GLU_ERR_UNSUPPORTED;
     if (forced != 0 && forced != GLU_KERNEL_GENERIC) return GLU_ERR_UNSUPPORTED;
     L->kernel = GLU_KERNEL_GENERIC;
     L->m_per_launch = (int)(M < 8 ? M : 8);
@@ -292,6 +334,12 @@ glu_status run(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int6
             e = glu::mfma_launch(L.mfma, mc, hidden + m0 * ldh, gate_w, up_w, out + m0 * ldo, N, K, ld, s);
         }
         break;
+    case GLU_KERNEL_GEMM:
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += L.m_per_launch) {
+            const int mc = (int)(M - m0 < L.m_per_launch ? M - m0 : L.m_per_launch);
+            e = glu::gemm_launch(L.gemm, mc, hidden + m0 * ldh, gate_w, up_w, out + m0 * ldo, (int)N, (int)K, ld, s);
+        }
+        break;
     default:
         return GLU_ERR_UNSUPPORTED;
     }
@@ -321,6 +369,7 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
         return GLU_OK;
     }
     const int forced = t ? t->kernel : 0;
+    if (t && (t->gemm_tile_n || t->gemm_tile_m)) return GLU_ERR_UNSUPPORTED;
     const bool mfma_fields = t && (t->mfma_segments || t->mfma_hidden || t->mfma_depth);
     const bool mfma = fast && mult4 && (forced == GLU_KERNEL_MFMA || (forced == 0 && (M >= 2 || mfma_fields)));
     if (forced == GLU_KERNEL_MFMA && !mfma) return GLU_ERR_UNSUPPORTED;
@@ -522,6 +571,7 @@ void fill_plan(const Launch& L, glu_plan* p)
     case GLU_KERNEL_VALU: p->grid = L.valu.grid; p->block = L.valu.block; break;
     case GLU_KERNEL_MFMA: p->grid = L.mfma.grid; p->block = L.mfma.block; break;
     case GLU_KERNEL_GENERIC: p->grid = L.generic_grid; p->block = 4 * glu::kWave; break;
+    case GLU_KERNEL_GEMM: p->grid = L.gemm_grid; p->block = 4 * glu::kWave; break;
     case GLU_KERNEL_ZERO: p->grid = 0; p->block = 256; break;
     default: p->grid = 0; p->block = 0; break;
     }
@@ -636,6 +686,9 @@ void describe_launch(const Launch& L, bool grouped, char* buf, int len)
     case GLU_KERNEL_GENERIC:
         snprintf(buf, (size_t)len, "glu::%s<%d>", grouped ? "grouped_generic_kernel" : "generic_kernel",
                  L.m_per_launch);
+        break;
+    case GLU_KERNEL_GEMM:
+        snprintf(buf, (size_t)len, "glu::gemm_kernel<%d, %d, %s>", L.gemm.bn, L.gemm.bm, tf[L.gemm.ktail]);
         break;
     case GLU_KERNEL_ZERO: snprintf(buf, (size_t)len, "glu::zero_kernel"); break;
     default: snprintf(buf, (size_t)len, "none"); break;

@@ -91,4 +91,18 @@ hipError_t generic_launch(int M, const uint16_t* hidden, const uint16_t* gate_w,
 // out[m*ldo + j] = +0 for m < M, j < N (K == 0).
 hipError_t zero_launch(uint16_t* out, int64_t M, int64_t N, int64_t ldo, hipStream_t stream);
 
+// Tiled dual GEMM for large M (glu_gemm.hip): bn x bm output tiles (bn weight
+// rows, bm hidden rows; each 64 or 128), K in stages of 64 elements.
+struct GemmConfig {
+    int bn;
+    int bm;
+    bool ktail;  // K % 64 != 0
+};
+size_t gemm_lds_bytes(int bn, int bm);
+bool gemm_supported(const GemmConfig& c);
+int64_t gemm_grid(const GemmConfig& c, int64_t M, int64_t N);
+// K % 8 == 0, 16-byte aligned rows (fast layout); out rows may have any stride
+hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                       const uint16_t* up_w, uint16_t* out, int N, int K, const RowStrides& ld, hipStream_t stream);
+
 }  // namespace glu

@@ -129,8 +129,9 @@ enum {
     GLU_KERNEL_NONE = 0,    /* M == 0 or N == 0 */
     GLU_KERNEL_ZERO = 1,    /* K == 0: fill out with +0 */
     GLU_KERNEL_VALU = 2,    /* M == 1, K <= 4096, fast path (any M <= 8 on request) */
-    GLU_KERNEL_MFMA = 3,    /* other fast-path shapes (slices of 32 rows of hidden) */
-    GLU_KERNEL_GENERIC = 4  /* unaligned, K % 8 != 0 or K > 2^25 */
+    GLU_KERNEL_MFMA = 3,    /* other fast-path shapes up to M = 32 */
+    GLU_KERNEL_GENERIC = 4, /* unaligned, K % 8 != 0 or K > 2^25 */
+    GLU_KERNEL_GEMM = 5     /* M > 32, fast path: tiled MFMA GEMM, slices of 65536 rows of hidden */
 };
 
 glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan);

@@ -20,7 +20,7 @@ extern "C" {
 #endif
 
 typedef struct glu_tuning {
-    int kernel;           /* 0 = automatic, else GLU_KERNEL_VALU / _MFMA / _GENERIC */
+    int kernel;           /* 0 = automatic, else GLU_KERNEL_VALU / _MFMA / _GENERIC / _GEMM */
     int rows_per_wave;    /* VALU: output rows per wave per group (1; 2 at M = 1).
                              MFMA: weight rows per wave, 4, or 8 with mfma_hidden = 3 */
     int waves_per_block;  /* VALU, MFMA: waves per workgroup (1..8) */
@@ -34,6 +34,8 @@ typedef struct glu_tuning {
     int mfma_depth;       /* MFMA with mfma_hidden = 3: pipeline stages of weights kept
                              in flight (4 rows: 4 at 2 segments, 2 at 4; 8 rows: 2 or 4
                              at 4 segments, 1 or 2 at 8) */
+    int gemm_tile_n;      /* GEMM: weight rows per output tile (64 or 128) */
+    int gemm_tile_m;      /* GEMM: hidden rows per output tile (64 or 128) */
 } glu_tuning;
 
 glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,

@@ -59,7 +59,9 @@ def test_version_and_strings(lib):
     (1, 12288, 8200, True, api.KERNEL_MFMA, 1),      # past the VALU path's 16 chunks per lane
     (9, 100, 512, True, api.KERNEL_MFMA, 1),
     (32, 17408, 5120, True, api.KERNEL_MFMA, 1),
-    (70, 17408, 5120, True, api.KERNEL_MFMA, 3),     # slices of 32 rows
+    (70, 17408, 5120, True, api.KERNEL_GEMM, 1),     # tiled GEMM above 32 rows
+    (33, 100, 512, True, api.KERNEL_GEMM, 1),
+    (100000, 300, 64, True, api.KERNEL_GEMM, 2),     # slices of 65536 rows
     (1, 100, 2560, False, api.KERNEL_GENERIC, 1),    # unaligned
     (1, 100, 1003, True, api.KERNEL_GENERIC, 1),     # K % 8 != 0
     (20, 100, 1003, True, api.KERNEL_GENERIC, 3),
@@ -72,7 +74,7 @@ def test_plan(lib, M, N, K, aligned, kernel, launches):
     p = api.plan(M, N, K, aligned)
     assert p["kernel"] == kernel, p
     assert p["launches"] == launches, p
-    if kernel in (api.KERNEL_VALU, api.KERNEL_MFMA, api.KERNEL_GENERIC):
+    if kernel in (api.KERNEL_VALU, api.KERNEL_MFMA, api.KERNEL_GENERIC, api.KERNEL_GEMM):
         assert p["grid"] > 0 and p["block"] % 64 == 0 and p["accum_depth"] >= 1
 
 
@@ -82,6 +84,9 @@ def test_describe_names_the_instantiated_kernel(lib):
     assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma8_slice_kernel<4, 8, 1, false>"
     assert api.plan(8, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<2, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
+    assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false>"
+    assert api.plan(1024, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<128, 128, false>"
+    assert api.plan(200, 129, 1032)["kernel_symbol"] == "glu::gemm_kernel<64, 128, true>"
     assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
 
 
@@ -298,3 +303,25 @@ def test_grouped_plans():
     with pytest.raises(api.GluError):
         api.grouped_plan(1, 64, 100, fast=False, tuning=api.make_tuning(kernel=api.KERNEL_VALU))
     assert api.grouped_plan(2, 64, 100, tuning=api.make_tuning(kernel=api.KERNEL_GENERIC))["kernel"] == api.KERNEL_GENERIC
+
+
+def test_gemm_plans_and_overrides(lib):
+    t = api.make_tuning(kernel=api.KERNEL_GEMM, gemm_tile_n=128, gemm_tile_m=64)
+    p = api.plan(1, 5, 8, True, t)
+    assert p["kernel"] == api.KERNEL_GEMM and p["kernel_symbol"] == "glu::gemm_kernel<128, 64, true>"
+    # the tile fields alone ask for the GEMM kernel; they go with no other kernel
+    assert api.plan(8, 1000, 1024, True, api.make_tuning(gemm_tile_n=64))["kernel"] == api.KERNEL_GEMM
+    p = api.Plan()
+    for bad in (dict(kernel=api.KERNEL_MFMA, gemm_tile_n=64), dict(kernel=api.KERNEL_GEMM, gemm_tile_n=96),
+                dict(kernel=api.KERNEL_GEMM, gemm_tile_m=32), dict(kernel=api.KERNEL_GEMM, mfma_segments=4),
+                dict(kernel=api.KERNEL_GEMM, grid=10), dict(kernel=api.KERNEL_GEMM, waves_per_block=2)):
+        t = api.make_tuning(**bad)
+        assert lib.glu_dual_gemv_plan_tuned(64, 1000, 1024, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP, bad
+    t = api.make_tuning(kernel=api.KERNEL_GEMM)
+    assert lib.glu_dual_gemv_plan_tuned(64, 1000, 1024, 0, ctypes.byref(t), ctypes.byref(p)) == UNSUP  # unaligned
+    assert lib.glu_dual_gemv_plan_tuned(64, 1000, 1020, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP  # K % 8
+    # the grouped GEMV has no GEMM kernel
+    with pytest.raises(api.GluError):
+        api.grouped_plan(64, 1024, 100, tuning=api.make_tuning(gemm_tile_n=64))
+    with pytest.raises(api.GluError):
+        api.grouped_plan(64, 1024, 100, tuning=api.make_tuning(kernel=api.KERNEL_GEMM))
