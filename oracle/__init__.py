@@ -7,7 +7,9 @@ in ``glu_mlp_gemv_amd``; neither imports the other.
 The arithmetic lives in ``glu_oracle.c`` (fp64 dot products, bf16 rounding of
 gate and up, fp32 silu rounded to bf16, bf16 product; its header states the
 definition and the passages it follows).  This module is a ctypes face over it
-that takes and returns numpy ``uint16`` arrays holding bf16 bit patterns.
+that takes and returns numpy ``uint16`` arrays holding bf16 bit patterns.  The
+backward (gradients of hidden and of both weights) is ``oracle.backward``, in
+numpy over this module's forward sums.
 """
 from __future__ import annotations
 

@@ -237,6 +237,50 @@ def compare_linear(got: np.ndarray, ref: LinearResult, depth: int, k_len: int, m
     return rep
 
 
+def compare_grad_sum(got: np.ndarray, want: np.ndarray, A: np.ndarray, Aabs: np.ndarray, B: np.ndarray,
+                     Babs: np.ndarray, depth: int, k_len: int, max_listed: int = 20) -> Report:
+    """Check the bf16 sum of two single-rounded contractions, RNE(fl32(RNE(A) + RNE(B))) (the
+    gradient of hidden in the backward), against the oracle's bits ``want``.  The same bars as
+    ``compare``; an output over 2 ULP passes only inside the sum of the two admissible intervals
+    (rounding and fp32 addition are monotone, so the interval's ends bound every reachable value)."""
+    got = np.asarray(got, dtype=np.uint16).ravel()
+    want = np.asarray(want, dtype=np.uint16).ravel()
+    if got.shape != want.shape:
+        raise ValueError(f"size mismatch {got.shape} vs {want.shape}")
+    rep = Report(n=int(got.size))
+    if got.size == 0:
+        return rep
+    d = ulp_distance(got, want)
+    rep.max_ulp = int(d.max())
+    rep.bit_exact_frac = float(np.mean((got == want) | (is_nan_bits(got) & is_nan_bits(want))))
+    w = bf16_to_f64(want)
+    g = bf16_to_f64(got)
+    nz = (w != 0) & np.isfinite(w) & np.isfinite(g)
+    rep.mean_rel = float(np.mean(np.abs(g[nz] - w[nz]) / np.abs(w[nz]))) if nz.any() else 0.0
+    bad = np.nonzero(d > 2)[0]
+    rep.over_2ulp = int(bad.size)
+    A, Aa, B, Ba = (np.asarray(x, dtype=np.float64).ravel() for x in (A, Aabs, B, Babs))
+    for i in bad:
+        ok = False
+        if not is_nan_bits(got[i:i + 1])[0]:
+            a_lo, a_hi = _admissible_range(float(A[i]), float(Aa[i]), depth, k_len)
+            b_lo, b_hi = _admissible_range(float(B[i]), float(Ba[i]), depth, k_len)
+            ends = bf16_to_f64(from_ordered(np.array([a_lo, a_hi, b_lo, b_hi])))
+            sums = np.array([ends[0] + ends[2], ends[1] + ends[3]]).astype(np.float32).astype(np.float64)
+            lo, hi = (int(x) for x in ordered(round_bf16(sums)))
+            o = int(ordered(got[i:i + 1])[0])
+            ok = lo <= o <= hi
+        if ok:
+            rep.interval_pass += 1
+        else:
+            rep.failures += 1
+            if len(rep.failure_idx) < max_listed:
+                rep.failure_idx.append(int(i))
+                rep.failure_info.append({"index": int(i), "got": f"{int(got[i]):#06x}",
+                                         "want": f"{int(want[i]):#06x}", "ulp": int(d[i])})
+    return rep
+
+
 def compare_strict_bits(got: np.ndarray, want: np.ndarray) -> Optional[np.ndarray]:
     """Indices where two bf16 bit arrays differ (NaN matches NaN); None when identical."""
     got = np.asarray(got, dtype=np.uint16).ravel()
