@@ -85,8 +85,8 @@ def test_describe_names_the_instantiated_kernel(lib):
     assert api.plan(8, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<2, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
     assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false>"
-    assert api.plan(1024, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<128, 128, false>"
-    assert api.plan(200, 129, 1032)["kernel_symbol"] == "glu::gemm_kernel<64, 128, true>"
+    assert api.plan(1024, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 128, false>"
+    assert api.plan(200, 129, 1032)["kernel_symbol"] == "glu::gemm_kernel<64, 64, true>"
     assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
 
 
