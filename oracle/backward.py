@@ -93,35 +93,42 @@ def silu_grad32(ds: np.ndarray, g: np.ndarray) -> np.ndarray:
     return (ds * sig) * (one + g * (one - sig))
 
 
-def dual_gemv_backward(hidden: np.ndarray, gate_w: np.ndarray, up_w: np.ndarray, dout: np.ndarray,
-                       threads: int = 0) -> BackwardResult:
-    """Gradients of the GLU projection for bf16 bit arrays hidden [M,K], gate_w/up_w [N,K], dout [M,N]."""
-    h = _u16(hidden)
-    wg = _u16(gate_w)
-    wu = _u16(up_w)
-    go = _u16(dout)
-    M, K = h.shape
-    N = wg.shape[0]
-    if wg.shape != (N, K) or wu.shape != (N, K) or go.shape != (M, N):
-        raise ValueError(f"shape mismatch: hidden {h.shape}, gate_w {wg.shape}, up_w {wu.shape}, dout {go.shape}")
+class ContractResult(NamedTuple):
+    dh: np.ndarray        # uint16 [M,K]
+    dwg: np.ndarray       # uint16 [N,K]
+    dwu: np.ndarray       # uint16 [N,K]
+    dhg_pre: np.ndarray
+    dhu_pre: np.ndarray
+    dhg_abs: np.ndarray
+    dhu_abs: np.ndarray
+    dwg_pre: np.ndarray
+    dwu_pre: np.ndarray
+    dwg_abs: np.ndarray
+    dwu_abs: np.ndarray
+
+
+def act_grads(g_bits: np.ndarray, u_bits: np.ndarray, dout: np.ndarray):
+    """Steps 2 and 3, elementwise: (ds, du, dg) bf16 bits from the forward's bf16 g and u and dout."""
     with np.errstate(all="ignore"):
-        # 1. the forward's bf16 values
-        fwd = dual_gemv(h, wg, wu, threads=threads, with_pre=True)
-        g = bits_to_f32(_rne(fwd.gate_pre))
-        u = bits_to_f32(_rne(fwd.up_pre))
+        g = bits_to_f32(_u16(g_bits))
+        u = bits_to_f32(_u16(u_bits))
         s = bits_to_f32(_rne(_silu32(g)))
-        # 2. backward of s * u
-        go32 = bits_to_f32(go)
+        go32 = bits_to_f32(_u16(dout))
         ds_bits = _rne(go32 * u)
         du_bits = _rne(go32 * s)
-        # 3. backward of silu
         dg_bits = _rne(silu_grad32(bits_to_f32(ds_bits), g))
-        # 4. backward of the products with hidden
+    return ds_bits, du_bits, dg_bits
+
+
+def contract(hidden: np.ndarray, gate_w: np.ndarray, up_w: np.ndarray, dg_bits: np.ndarray,
+             du_bits: np.ndarray) -> ContractResult:
+    """Step 4: the three gradients from the bf16 gradients dg, du [M,N] of the pre-activations."""
+    with np.errstate(all="ignore"):
         dg64 = bits_to_f32(dg_bits).astype(np.float64)
         du64 = bits_to_f32(du_bits).astype(np.float64)
-        h64 = bits_to_f32(h).astype(np.float64)
-        wg64 = bits_to_f32(wg).astype(np.float64)
-        wu64 = bits_to_f32(wu).astype(np.float64)
+        h64 = bits_to_f32(_u16(hidden)).astype(np.float64)
+        wg64 = bits_to_f32(_u16(gate_w)).astype(np.float64)
+        wu64 = bits_to_f32(_u16(up_w)).astype(np.float64)
         dhg_pre = dg64 @ wg64
         dhu_pre = du64 @ wu64
         dhg_abs = np.abs(dg64) @ np.abs(wg64)
@@ -133,6 +140,28 @@ def dual_gemv_backward(hidden: np.ndarray, gate_w: np.ndarray, up_w: np.ndarray,
         dh_g = bits_to_f32(_rne(dhg_pre))
         dh_u = bits_to_f32(_rne(dhu_pre))
         dh_bits = _rne(dh_g + dh_u)
-    return BackwardResult(dh_bits, _rne(dwg_pre), _rne(dwu_pre), dg_bits, du_bits, ds_bits,
-                          dhg_pre, dhu_pre, dhg_abs, dhu_abs, dwg_pre, dwu_pre, dwg_abs, dwu_abs,
-                          fwd.gate_pre, fwd.up_pre)
+    return ContractResult(dh_bits, _rne(dwg_pre), _rne(dwu_pre), dhg_pre, dhu_pre, dhg_abs, dhu_abs,
+                          dwg_pre, dwu_pre, dwg_abs, dwu_abs)
+
+
+def dual_gemv_backward(hidden: np.ndarray, gate_w: np.ndarray, up_w: np.ndarray, dout: np.ndarray,
+                       threads: int = 0) -> BackwardResult:
+    """Gradients of the GLU projection for bf16 bit arrays hidden [M,K], gate_w/up_w [N,K], dout [M,N]."""
+    h = _u16(hidden)
+    wg = _u16(gate_w)
+    wu = _u16(up_w)
+    go = _u16(dout)
+    M, K = h.shape
+    N = wg.shape[0]
+    if wg.shape != (N, K) or wu.shape != (N, K) or go.shape != (M, N):
+        raise ValueError(f"shape mismatch: hidden {h.shape}, gate_w {wg.shape}, up_w {wu.shape}, dout {go.shape}")
+    # 1. the forward's bf16 values
+    fwd = dual_gemv(h, wg, wu, threads=threads, with_pre=True)
+    g_bits = _rne(fwd.gate_pre)
+    u_bits = _rne(fwd.up_pre)
+    # 2.-3. backward of s * u and of silu
+    ds_bits, du_bits, dg_bits = act_grads(g_bits, u_bits, go)
+    # 4. backward of the products with hidden
+    c = contract(h, wg, wu, dg_bits, du_bits)
+    return BackwardResult(c.dh, c.dwg, c.dwu, dg_bits, du_bits, ds_bits, c.dhg_pre, c.dhu_pre, c.dhg_abs,
+                          c.dhu_abs, c.dwg_pre, c.dwu_pre, c.dwg_abs, c.dwu_abs, fwd.gate_pre, fwd.up_pre)

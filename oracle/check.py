@@ -89,6 +89,12 @@ def _admissible_range(pre: float, abs_sum: float, depth: int, k_len: int):
     return int(ordered(lo)), int(ordered(hi))
 
 
+def admissible_bf16_set(pre: float, abs_sum: float, depth: int, k_len: int) -> np.ndarray:
+    """Every bf16 (bits) that rounding a reachable fp32 sum of depth ``depth`` can give."""
+    lo, hi = _admissible_range(pre, abs_sum, depth, k_len)
+    return from_ordered(np.arange(lo, hi + 1))
+
+
 def admissible_out_range(G: float, U: float, Ga: float, Ua: float, depth: int, k_len: int):
     """Ordered-code interval of outputs reachable from any admissible (g, u)."""
     g_lo, g_hi = _admissible_range(G, Ga, depth, k_len)

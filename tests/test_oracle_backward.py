@@ -24,11 +24,12 @@ MUTANTS = [
     ("ds_times_s", "ds_bits = _rne(go32 * u)", "ds_bits = _rne(go32 * s)"),
     ("du_times_u", "du_bits = _rne(go32 * s)", "du_bits = _rne(go32 * u)"),
     ("dh_up_branch_dropped", "dh_bits = _rne(dh_g + dh_u)", "dh_bits = _rne(dh_g)"),
+    ("contract_swaps_gradients", "c = contract(h, wg, wu, dg_bits, du_bits)", "c = contract(h, wg, wu, du_bits, dg_bits)"),
     ("dh_up_uses_gate_weights", "dhu_pre = du64 @ wu64", "dhu_pre = du64 @ wg64"),
     ("dwg_uses_du", "dwg_pre = dg64.T @ h64", "dwg_pre = du64.T @ h64"),
     ("dh_contributions_not_rounded", "dh_g = bits_to_f32(_rne(dhg_pre))", "dh_g = dhg_pre.astype(np.float32)"),
-    ("dg_not_rounded", "dg64 = bits_to_f32(dg_bits).astype(np.float64)",
-     "dg64 = silu_grad32(bits_to_f32(ds_bits), g).astype(np.float64)"),
+    ("dg_truncated", "dg_bits = _rne(silu_grad32(bits_to_f32(ds_bits), g))",
+     "dg_bits = (silu_grad32(bits_to_f32(ds_bits), g).view(np.uint32) >> 16).astype(np.uint16)"),
     ("silu_unrounded_in_du", "s = bits_to_f32(_rne(_silu32(g)))", "s = _silu32(g)"),
 ]
 
