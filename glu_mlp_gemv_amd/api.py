@@ -21,9 +21,10 @@ LIBRARY_PATH = _build.LIBRARY
 GLU_OK = 0
 GLU_ERR_UNSUPPORTED = 6
 GLU_ERR_BAD_STRIDE = 7
-KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC, KERNEL_GEMM = range(6)
+GLU_ERR_WORKSPACE = 8
+KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC, KERNEL_GEMM, KERNEL_BACKWARD = range(7)
 KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
-                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic", KERNEL_GEMM: "gemm"}
+                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic", KERNEL_GEMM: "gemm", KERNEL_BACKWARD: "backward"}
 
 EXPORTED_SYMBOLS = (
     "glu_dual_gemv",
@@ -41,6 +42,9 @@ EXPORTED_SYMBOLS = (
     "glu_dual_gemv_tuned",
     "glu_dual_gemv_plan_tuned",
     "glu_dual_gemv_describe",
+    "glu_dual_gemv_backward",
+    "glu_dual_gemv_backward_workspace",
+    "glu_dual_gemv_backward_plan",
 )
 
 
@@ -124,6 +128,12 @@ def library() -> ctypes.CDLL:
     lib.glu_grouped_gemv_describe.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tuning), ctypes.c_char_p,
                                               ctypes.c_int]
     lib.glu_grouped_gemv_describe.restype = ctypes.c_int
+    lib.glu_dual_gemv_backward.argtypes = [u16p, u16p, u16p, u16p, u16p, u16p, u16p, i64, i64, i64, vp, i64, vp]
+    lib.glu_dual_gemv_backward.restype = ctypes.c_int
+    lib.glu_dual_gemv_backward_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.glu_dual_gemv_backward_workspace.restype = ctypes.c_int
+    lib.glu_dual_gemv_backward_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    lib.glu_dual_gemv_backward_plan.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -244,6 +254,86 @@ def dual_gemv(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor,
                                                  ctypes.byref(tuning))
     _raise_for(st)
     return out
+
+
+def backward_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes glu_dual_gemv_backward needs (host only)."""
+    b = ctypes.c_int64(0)
+    _raise_for(library().glu_dual_gemv_backward_workspace(M, N, K, ctypes.byref(b)))
+    return int(b.value)
+
+
+def backward_plan(M: int, N: int, K: int) -> dict:
+    """The backward's launch for a shape (host only)."""
+    p = Plan()
+    _raise_for(library().glu_dual_gemv_backward_plan(M, N, K, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def dual_gemv_backward(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor, dout: torch.Tensor,
+                       dhidden: Optional[torch.Tensor] = None, dgate_w: Optional[torch.Tensor] = None,
+                       dup_w: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None):
+    """Gradients (dhidden, dgate_w, dup_w) of dual_gemv for the upstream gradient ``dout``.
+
+    hidden [M, K] (or [K], then dout is [N] and dhidden [K]), gate_w and up_w
+    [N, K], dout [M, N]; all bf16, contiguous, on one GPU; M <= 8.  Outputs are
+    allocated unless given (contiguous, overwritten).  ``workspace``: a uint8
+    device tensor of at least backward_workspace_bytes(M, N, K) bytes, else one
+    is allocated; on return it begins with dg and du, the bf16 gradients of the
+    gate and up pre-activations ([2, M, N]).
+    """
+    _check("hidden", hidden, (1, 2))
+    _check("gate_w", gate_w, (2,))
+    _check("up_w", up_w, (2,))
+    _check("dout", dout, (1, 2))
+    vec = hidden.dim() == 1
+    M = 1 if vec else hidden.shape[0]
+    K = hidden.shape[-1]
+    N = gate_w.shape[0]
+    dev = hidden.device
+    if tuple(gate_w.shape) != (N, K) or tuple(up_w.shape) != (N, K):
+        raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, gate_w {tuple(gate_w.shape)}, "
+                         f"up_w {tuple(up_w.shape)}")
+    if tuple(dout.shape) != ((N,) if vec else (M, N)):
+        raise ValueError(f"dout must be {(N,) if vec else (M, N)}, got {tuple(dout.shape)}")
+    for name, t in (("gate_w", gate_w), ("up_w", up_w), ("hidden", hidden), ("dout", dout)):
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def out_tensor(name, t, shape):
+        if t is None:
+            return torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        _check(name, t, (len(shape),))
+        if tuple(t.shape) != tuple(shape) or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {tuple(shape)} tensor on {dev}")
+        return t
+    dhidden = out_tensor("dhidden", dhidden, tuple(hidden.shape))
+    dgate_w = out_tensor("dgate_w", dgate_w, (N, K))
+    dup_w = out_tensor("dup_w", dup_w, (N, K))
+    need = backward_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    lib = library()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = lib.glu_dual_gemv_backward(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(), dout.data_ptr(),
+                                        dhidden.data_ptr(), dgate_w.data_ptr(), dup_w.data_ptr(), M, N, K,
+                                        workspace.data_ptr(), workspace.numel(), s.cuda_stream)
+    _raise_for(st)
+    return dhidden, dgate_w, dup_w
+
+
+def dual_gemv_backward_raw(hidden_ptr: int, gate_ptr: int, up_ptr: int, dout_ptr: int, dh_ptr: int, dwg_ptr: int,
+                           dwu_ptr: int, M: int, N: int, K: int, ws_ptr: int, ws_bytes: int,
+                           stream_handle: int = 0) -> int:
+    """The C call on raw device addresses; returns the glu_status (used by boundary tests)."""
+    return library().glu_dual_gemv_backward(hidden_ptr, gate_ptr, up_ptr, dout_ptr, dh_ptr, dwg_ptr, dwu_ptr,
+                                            M, N, K, ws_ptr, ws_bytes, stream_handle)
 
 
 def dual_gemv_raw(hidden_ptr: int, gate_ptr: int, up_ptr: int, out_ptr: int, M: int, N: int, K: int,

@@ -10,6 +10,7 @@
 
 #include "../../include/glu_gemv.h"
 #include "../../include/glu_gemv_tuning.h"
+#include "glu_backward.h"
 #include "glu_grouped.h"
 #include "glu_launch.h"
 
@@ -55,6 +56,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // work units to within one.
 int64_t balanced_waves(int64_t units, int64_t target)
 {
+    if (units < 1) return 0;
     const int64_t per = ceil_div(units, target < 1 ? 1 : target);
     return ceil_div(units, per);
 }
@@ -373,6 +375,7 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
     if (mfma_fields && !mfma) return GLU_ERR_UNSUPPORTED;
     if (mfma) {
         if (t && (t->mfma_depth || t->rows_per_wave)) return GLU_ERR_UNSUPPORTED;
+        if (rows % 4 != 0) return GLU_ERR_UNSUPPORTED;  // whole 4-row groups only
         glu::MfmaConfig c{};
         const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
         c.rows = 4;
@@ -469,7 +472,7 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         rows += proj[i].N;
     }
     Launch L;
-    glu_status st = plan_grouped(M, K, rows, true, true, nullptr, &L);  // shape errors first
+    glu_status st = plan_grouped(M, K, rows, false, false, nullptr, &L);  // shape errors first
     if (st != GLU_OK) return st;
     if (M == 0 || rows == 0) return GLU_OK;
     // strides and extents
@@ -555,6 +558,71 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
     default:
         return GLU_ERR_UNSUPPORTED;
     }
+    return e == hipSuccess ? GLU_OK : fail_launch(e);
+}
+
+// ---- backward ------------------------------------------------------------------
+
+glu_status plan_backward(int64_t M, int64_t N, int64_t K, glu::BwdPlan* bp)
+{
+    Launch L;
+    const glu_status st = plan_launch(M, N, K, true, nullptr, &L);  // shape errors
+    if (st != GLU_OK) return st;
+    if (M > glu::kBwdMaxM) return GLU_ERR_UNSUPPORTED;
+    *bp = glu::bwd_plan(M, N, K);
+    return GLU_OK;
+}
+
+glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* dout,
+                        uint16_t* dh, uint16_t* dwg, uint16_t* dwu, int64_t M, int64_t N, int64_t K, void* ws,
+                        int64_t ws_bytes, void* stream)
+{
+    glu::BwdPlan bp;
+    glu_status st = plan_backward(M, N, K, &bp);
+    if (st != GLU_OK) return st;
+    const int64_t hk = M * K, nk = N * K, mn = M * N;
+    if ((hk > 0 && (!hidden || !dh)) || (nk > 0 && (!gate_w || !up_w || !dwg || !dwu)) || (mn > 0 && !dout)) {
+        return GLU_ERR_NULL_POINTER;
+    }
+    const uintptr_t odd = ((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w | (uintptr_t)dout |
+                           (uintptr_t)dh | (uintptr_t)dwg | (uintptr_t)dwu) & 1u;
+    if (odd) return GLU_ERR_MISALIGNED;
+    // outputs (and the workspace) overlap no input and no other output
+    const bool run_all = M > 0 && N > 0 && K > 0;
+    const void* ins[4] = {hidden, gate_w, up_w, dout};
+    const int64_t in_bytes[4] = {hk * 2, nk * 2, nk * 2, mn * 2};
+    const void* outs[4] = {dh, dwg, dwu, run_all ? ws : nullptr};
+    const int64_t out_bytes[4] = {hk * 2, nk * 2, nk * 2, run_all ? bp.workspace_bytes : 0};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 4; ++b) {
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return GLU_ERR_ALIASING;
+            if (b > a && overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return GLU_ERR_ALIASING;
+        }
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (!run_all) {
+        // an empty sum is zero: dh when N == 0, the weight gradients when M == 0
+        if (N == 0 && hk > 0) e = glu::zero_launch(dh, M, K, K, s);
+        if (M == 0 && nk > 0 && e == hipSuccess) e = glu::zero_launch(dwg, N, K, K, s);
+        if (M == 0 && nk > 0 && e == hipSuccess) e = glu::zero_launch(dwu, N, K, K, s);
+        return e == hipSuccess ? GLU_OK : fail_launch(e);
+    }
+    const bool fast = ((((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w | (uintptr_t)dwg | (uintptr_t)dwu) &
+                        15u) == 0) && K % 8 == 0 && K <= kMaxFastK;
+    if (!fast) return GLU_ERR_UNSUPPORTED;
+    if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < bp.workspace_bytes) return GLU_ERR_WORKSPACE;
+    uint16_t* gu = static_cast<uint16_t*>(ws);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + bp.gu_bytes);
+    // g = bf16(h Wg^T), u = bf16(h Wu^T): the grouped GEMV into the workspace
+    glu_projection proj[2] = {{gate_w, gu, N, K, N}, {up_w, gu + mn, N, K, N}};
+    st = run_grouped(hidden, K, proj, 2, M, K, stream, nullptr);
+    if (st != GLU_OK) return st;
+    e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
+    if (e == hipSuccess) {
+        e = glu::contract_launch(bp, (int)M, hidden, gate_w, up_w, gu, dwg, dwu, partial, (int)N, (int)K, s);
+    }
+    if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
     return e == hipSuccess ? GLU_OK : fail_launch(e);
 }
 
@@ -718,6 +786,42 @@ glu_status glu_grouped_gemv_describe(int64_t M, int64_t K, int64_t rows, int fas
     return GLU_OK;
 }
 
+glu_status glu_dual_gemv_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes)
+{
+    if (!bytes) return GLU_ERR_NULL_POINTER;
+    *bytes = 0;
+    glu::BwdPlan bp;
+    const glu_status st = plan_backward(M, N, K, &bp);
+    if (st != GLU_OK) return st;
+    *bytes = (M > 0 && N > 0 && K > 0) ? bp.workspace_bytes : 0;
+    return GLU_OK;
+}
+
+glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan* plan)
+{
+    if (!plan) return GLU_ERR_NULL_POINTER;
+    glu::BwdPlan bp;
+    const glu_status st = plan_backward(M, N, K, &bp);
+    if (st != GLU_OK) return st;
+    const bool run_all = M > 0 && N > 0 && K > 0;
+    plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
+    plan->m_per_launch = (int)M;
+    plan->launches = run_all ? 4 : 0;
+    plan->grid = run_all ? bp.nranges * bp.nslabs : 0;
+    plan->block = 256;
+    plan->accum_depth = bp.accum_depth;
+    return GLU_OK;
+}
+
+glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                                  const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
+                                  int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                  void* stream)
+{
+    return run_backward(hidden, gate_w, up_w, dout, dhidden, dgate_w, dup_w, M, N, K, workspace, workspace_bytes,
+                        stream);
+}
+
 const char* glu_status_string(int status)
 {
     switch (status) {
@@ -729,12 +833,13 @@ const char* glu_status_string(int status)
     case GLU_ERR_LAUNCH: return "GLU_ERR_LAUNCH: the HIP kernel launch failed";
     case GLU_ERR_UNSUPPORTED: return "GLU_ERR_UNSUPPORTED: the requested launch shape is not available";
     case GLU_ERR_BAD_STRIDE: return "GLU_ERR_BAD_STRIDE: a row stride is shorter than its row, or the rows overflow";
+    case GLU_ERR_WORKSPACE: return "GLU_ERR_WORKSPACE: the workspace is NULL, misaligned or too small";
     default: return "unknown glu_status";
     }
 }
 
 int glu_last_hip_error(void) { return g_last_hip_error; }
 
-int glu_version(void) { return 200; }
+int glu_version(void) { return 300; }
 
 }  // extern "C"

@@ -1,0 +1,30 @@
+// Internal interface of the backward kernels (glu_backward.hip).
+#pragma once
+
+#include "glu_launch.h"
+
+namespace glu {
+
+constexpr int kBwdMaxM = 8;
+constexpr int kBwdTargetBlocks = 512;  // contraction workgroups aimed for (2 per CU)
+
+struct BwdPlan {
+    int nslabs;              // 512-column slabs of K
+    int nranges;             // row ranges of N
+    int rows_per_range;
+    int64_t gu_bytes;        // workspace head: [2][M][N] bf16 (g, u, then dg, du), 256-byte padded
+    int64_t partial_bytes;   // then [nranges][2][M][K] fp32 partial sums of dh
+    int64_t workspace_bytes;
+    int accum_depth;         // longest fp32 addition chain behind one dh contribution
+};
+
+BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K);
+hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int M, int N, hipStream_t stream);
+// K % 8 == 0, hidden / gate_w / up_w / dwg / dwu 16-byte aligned, packed rows
+hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                           const uint16_t* up_w, const uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial,
+                           int N, int K, hipStream_t stream);
+hipError_t dh_reduce_launch(const BwdPlan& p, const float* partial, uint16_t* dh, int64_t ldh_out, int M, int K,
+                            hipStream_t stream);
+
+}  // namespace glu

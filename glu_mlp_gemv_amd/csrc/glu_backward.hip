@@ -1,0 +1,290 @@
+// Backward of the dual-weight GLU projection for M <= 8 rows of hidden.
+//
+// The segKI "Plan B" autograd Function keeps hidden, gate_w and up_w and
+// returns gradients for all three, equal to those of the composite
+// silu(h Wg^T) * (h Wu^T) (DeepSpeed PR #9057 discussion, "Plan B Design" and
+// "Verification Results").  Over bf16 tensors every gradient tensor is
+// rounded once to bf16, as autograd of the bf16 composite does:
+//   ds = bf16(dout u), du = bf16(dout s), dg = bf16(silu'(g) ds) in fp32,
+//   dh = bf16(fp32(bf16(dg Wg) + bf16(du Wu))), dWg = bf16(dg^T h), dWu = bf16(du^T h).
+//
+// Launches (after the grouped GEMV has written g = bf16(h Wg^T) and
+// u = bf16(h Wu^T) into the workspace):
+//  * act_grad_kernel: dg and du from g, u and dout, elementwise, in place;
+//  * contract_kernel: workgroups own (row range, 512-column slab) tiles.  Each
+//    wave streams its rows' 1 KiB slab pieces of Wg and Wu once, accumulates
+//    dh's two contributions for the slab in fp32 registers, and writes the
+//    same rows' slab of dWg and dWu (sum over the M rows of hidden, in order).
+//    The 4 waves' dh sums are added in LDS in a fixed order and written as the
+//    workgroup's fp32 partial;
+//  * dh_reduce_kernel: sums the row ranges' partials in order, rounds each
+//    contribution and their fp32 sum to bf16.
+// No atomics: results are bitwise reproducible.
+#include "glu_backward.h"
+#include "glu_device.h"
+
+namespace glu {
+
+namespace {
+
+constexpr int kSlab = 512;          // columns per contraction tile (8 per lane)
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * kWave;
+
+typedef unsigned u32x4_b __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float f32r(double x) { return (float)x; }
+
+// fp32 steps evaluated in fp64 and rounded once to fp32: for +, -, *, / of
+// fp32 operands this equals the IEEE fp32 result (53 >= 2 * 24 + 2 bits)
+__device__ __forceinline__ void act_grad(float g, float u, float go, uint16_t* dg_out, uint16_t* du_out)
+{
+    const float e = (float)exp(-(double)g);
+    const float d = f32r(1.0 + (double)e);
+    const float s = bf16_to_f32(f32_to_bf16_rne(f32r((double)g / (double)d)));  // silu(g) as a bf16 tensor
+    const float ds = bf16_to_f32(f32_to_bf16_rne(f32r((double)go * (double)u)));
+    *du_out = f32_to_bf16_rne(f32r((double)go * (double)s));
+    const float sig = f32r(1.0 / (double)d);
+    const float t1 = f32r((double)ds * (double)sig);
+    const float t2 = f32r(1.0 - (double)sig);
+    const float t3 = f32r((double)g * (double)t2);
+    const float t4 = f32r(1.0 + (double)t3);
+    *dg_out = f32_to_bf16_rne(f32r((double)t1 * (double)t4));
+}
+
+}  // namespace
+
+// gu: [2][M][N] bf16, g then u on entry, dg then du on return; dout [M][ldd]
+__global__ void __launch_bounds__(256)
+act_grad_kernel(uint16_t* __restrict__ gu, const uint16_t* __restrict__ dout, int64_t ldd, int M, int N)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t MN = (int64_t)M * N;
+    if (i >= MN) return;
+    const int64_t m = i / N;
+    const int64_t j = i - m * N;
+    const float g = bf16_to_f32(gu[i]);
+    const float u = bf16_to_f32(gu[MN + i]);
+    const float go = bf16_to_f32(dout[m * ldd + j]);
+    uint16_t dg, du;
+    act_grad(g, u, go, &dg, &du);
+    gu[i] = dg;
+    gu[MN + i] = du;
+}
+
+// M: rows of hidden (1..8).  Workgroup b: slab b % nslabs, rows
+// [r * rows_per_range, min(N, (r + 1) * rows_per_range)) with r = b / nslabs.
+// partial: [nranges][2][M][K] fp32.
+template <int M>
+__global__ void __launch_bounds__(kBwdThreads)
+contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+                const uint16_t* __restrict__ up_w, const uint16_t* __restrict__ dgu, uint16_t* __restrict__ dwg,
+                uint16_t* __restrict__ dwu, float* __restrict__ partial, int N, int K, int nslabs,
+                int rows_per_range)
+{
+    __shared__ float red[2 * M * kSlab];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slab = blockIdx.x % nslabs;
+    const int range = blockIdx.x / nslabs;
+    const int c0 = slab * kSlab + lane * 8;
+    const bool col_ok = c0 < K;  // K % 8 == 0: a lane's 8 columns are all inside or all outside
+    const int j_begin = range * rows_per_range;
+    const int j_end = min(j_begin + rows_per_range, N);
+    const int64_t MN = (int64_t)M * N;
+
+    float hv[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        u32x4_b w = {0u, 0u, 0u, 0u};
+        if (col_ok) w = *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hv[m][2 * q] = bf16lo(w[q]);
+            hv[m][2 * q + 1] = bf16hi(w[q]);
+        }
+    }
+    float ag[M][8], au[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ag[m][e] = 0.0f;
+            au[m][e] = 0.0f;
+        }
+    }
+
+    for (int j = j_begin + wave; j < j_end; j += kBwdWaves) {
+        float dg[M], du[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            dg[m] = bf16_to_f32(dgu[(int64_t)m * N + j]);
+            du[m] = bf16_to_f32(dgu[MN + (int64_t)m * N + j]);
+        }
+        if (!col_ok) continue;
+        const u32x4_b wgv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(gate_w + (int64_t)j * K + c0));
+        const u32x4_b wuv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(up_w + (int64_t)j * K + c0));
+        float wgf[8], wuf[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wgf[2 * q] = bf16lo(wgv[q]);
+            wgf[2 * q + 1] = bf16hi(wgv[q]);
+            wuf[2 * q] = bf16lo(wuv[q]);
+            wuf[2 * q + 1] = bf16hi(wuv[q]);
+        }
+        // dh contributions (a product of two bf16 values is exact in fp32, so fma adds it unrounded)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ag[m][e] = __builtin_fmaf(dg[m], wgf[e], ag[m][e]);
+                au[m][e] = __builtin_fmaf(du[m], wuf[e], au[m][e]);
+            }
+        }
+        // this row's slab of dWg and dWu: sums over the rows of hidden in order
+        uint16_t og[8], ou[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float sg = 0.0f, su = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                sg = __builtin_fmaf(dg[m], hv[m][e], sg);
+                su = __builtin_fmaf(du[m], hv[m][e], su);
+            }
+            og[e] = f32_to_bf16_rne(sg);
+            ou[e] = f32_to_bf16_rne(su);
+        }
+        u32x4_b pg, pu;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            pg[q] = (uint32_t)og[2 * q] | ((uint32_t)og[2 * q + 1] << 16);
+            pu[q] = (uint32_t)ou[2 * q] | ((uint32_t)ou[2 * q + 1] << 16);
+        }
+        __builtin_nontemporal_store(pg, reinterpret_cast<u32x4_b*>(dwg + (int64_t)j * K + c0));
+        __builtin_nontemporal_store(pu, reinterpret_cast<u32x4_b*>(dwu + (int64_t)j * K + c0));
+    }
+
+    // the waves' dh sums, added in the order 3, 2, 1, 0
+    const int base = lane * 8;
+    for (int w = kBwdWaves - 1; w >= 0; --w) {
+        if (wave == w) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ig = m * kSlab + base + e;
+                    const int iu = (M + m) * kSlab + base + e;
+                    const float vg = (w == kBwdWaves - 1) ? ag[m][e] : red[ig] + ag[m][e];
+                    const float vu = (w == kBwdWaves - 1) ? au[m][e] : red[iu] + au[m][e];
+                    if (w > 0) {
+                        red[ig] = vg;
+                        red[iu] = vu;
+                    } else if (col_ok) {
+                        float* pg = partial + (((int64_t)range * 2 + 0) * M + m) * K + c0;
+                        float* pu = partial + (((int64_t)range * 2 + 1) * M + m) * K + c0;
+                        pg[e] = vg;
+                        pu[e] = vu;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// dh[m][c] = bf16(fp32(bf16(sum_r Pg[r][m][c]) + bf16(sum_r Pu[r][m][c]))), r in order
+__global__ void __launch_bounds__(256)
+dh_reduce_kernel(const float* __restrict__ partial, uint16_t* __restrict__ dh, int64_t ldh_out, int M, int K,
+                 int nranges)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t MK = (int64_t)M * K;
+    if (i >= MK) return;
+    const int64_t m = i / K;
+    const int64_t c = i - m * K;
+    float sg = 0.0f, su = 0.0f;
+    for (int r = 0; r < nranges; ++r) {
+        sg += partial[((int64_t)r * 2 + 0) * MK + i];
+        su += partial[((int64_t)r * 2 + 1) * MK + i];
+    }
+    const float a = bf16_to_f32(f32_to_bf16_rne(sg));
+    const float b = bf16_to_f32(f32_to_bf16_rne(su));
+    dh[m * ldh_out + c] = f32_to_bf16_rne(a + b);
+}
+
+namespace {
+
+using ContractFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
+                            uint16_t*, float*, int, int, int, int);
+
+ContractFn pick_contract(int M)
+{
+    switch (M) {
+    case 1: return contract_kernel<1>;
+    case 2: return contract_kernel<2>;
+    case 3: return contract_kernel<3>;
+    case 4: return contract_kernel<4>;
+    case 5: return contract_kernel<5>;
+    case 6: return contract_kernel<6>;
+    case 7: return contract_kernel<7>;
+    case 8: return contract_kernel<8>;
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
+{
+    BwdPlan p{};
+    p.nslabs = (int)((K + kSlab - 1) / kSlab);
+    if (p.nslabs < 1) p.nslabs = 1;
+    int64_t ranges = (kBwdTargetBlocks + p.nslabs - 1) / p.nslabs;
+    if (ranges > N) ranges = N;
+    if (ranges < 1) ranges = 1;
+    p.rows_per_range = (int)((N + ranges - 1) / ranges);
+    if (p.rows_per_range < 1) p.rows_per_range = 1;
+    p.nranges = (int)((N + p.rows_per_range - 1) / p.rows_per_range);
+    if (p.nranges < 1) p.nranges = 1;
+    p.gu_bytes = ((int64_t)2 * M * N * 2 + 255) / 256 * 256;
+    p.partial_bytes = (int64_t)p.nranges * 2 * M * K * 4;
+    p.workspace_bytes = p.gu_bytes + p.partial_bytes;
+    // dh: within a wave its rows in order, then 4 waves, then the ranges
+    p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves + p.nranges;
+    return p;
+}
+
+hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int M, int N, hipStream_t stream)
+{
+    const int64_t n = (int64_t)M * N;
+    if (n <= 0) return hipSuccess;
+    const int64_t grid = (n + 255) / 256;
+    hipLaunchKernelGGL(act_grad_kernel, dim3((unsigned)grid), dim3(256), 0, stream, gu, dout, ldd, M, N);
+    return hipGetLastError();
+}
+
+hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                           const uint16_t* up_w, const uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial,
+                           int N, int K, hipStream_t stream)
+{
+    ContractFn fn = pick_contract(M);
+    if (!fn || N < 1 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)p.nranges * p.nslabs;
+    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kBwdThreads), 0, stream, hidden, gate_w, up_w, dgu, dwg, dwu,
+                       partial, N, K, p.nslabs, p.rows_per_range);
+    return hipGetLastError();
+}
+
+hipError_t dh_reduce_launch(const BwdPlan& p, const float* partial, uint16_t* dh, int64_t ldh_out, int M, int K,
+                            hipStream_t stream)
+{
+    const int64_t n = (int64_t)M * K;
+    if (n <= 0) return hipSuccess;
+    const int64_t grid = (n + 255) / 256;
+    hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partial, dh, ldh_out, M, K,
+                       p.nranges);
+    return hipGetLastError();
+}
+
+}  // namespace glu

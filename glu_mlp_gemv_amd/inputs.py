@@ -24,6 +24,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 HIDDEN_SEED_OFFSET = 1 << 40
+GRAD_SEED_OFFSET = 2 << 40  # upstream gradients draw from their own stream
 WEIGHT_STD = 0.02
 OUTLIER_STD = 0.2
 OUTLIER_FRAC = 0.01
@@ -43,6 +44,12 @@ def hidden(M: int, K: int, seed: int, device="cpu", row0_scale: float = 1.0,
     if row0_scale != 1.0 and M > 0:
         h[0] *= row0_scale
     return h.to(torch.bfloat16)
+
+
+def grad_out(M: int, N: int, seed: int, device="cpu", std: float = 1.0) -> torch.Tensor:
+    """Upstream gradient rows [M, N] ~ N(0, std^2) for the backward (their own seed stream)."""
+    g = _gen(device, seed + GRAD_SEED_OFFSET)
+    return (torch.randn((M, N), generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
 
 
 def _one_weight(N: int, K: int, g: torch.Generator, device, std: float,

@@ -55,8 +55,10 @@ typedef enum glu_status {
     GLU_ERR_ALIASING = 4,     /* out overlaps hidden, gate_w or up_w */
     GLU_ERR_LAUNCH = 5,       /* the HIP launch failed; see glu_last_hip_error() */
     GLU_ERR_UNSUPPORTED = 6,  /* a tuning override the library cannot serve (glu_gemv_tuning.h) */
-    GLU_ERR_BAD_STRIDE = 7    /* glu_dual_gemv_strided: a row stride below its row length, or
+    GLU_ERR_BAD_STRIDE = 7,   /* glu_dual_gemv_strided: a row stride below its row length, or
                                  rows whose extent overflows int64 */
+    GLU_ERR_WORKSPACE = 8     /* glu_dual_gemv_backward: workspace NULL, not 256-byte aligned
+                                 or smaller than glu_dual_gemv_backward_workspace asks */
 } glu_status;
 
 /*
@@ -131,7 +133,8 @@ enum {
     GLU_KERNEL_VALU = 2,    /* M == 1, K <= 4096, fast path (any M <= 8 on request) */
     GLU_KERNEL_MFMA = 3,    /* other fast-path shapes up to M = 32 */
     GLU_KERNEL_GENERIC = 4, /* unaligned, K % 8 != 0 or K > 2^25 */
-    GLU_KERNEL_GEMM = 5     /* M > 32, fast path: tiled MFMA GEMM, slices of 65536 rows of hidden */
+    GLU_KERNEL_GEMM = 5,    /* M > 32, fast path: tiled MFMA GEMM, slices of 65536 rows of hidden */
+    GLU_KERNEL_BACKWARD = 6 /* glu_dual_gemv_backward_plan: the four backward launches */
 };
 
 glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, glu_plan* plan);
@@ -184,6 +187,53 @@ glu_status glu_grouped_gemv(const uint16_t* hidden, int64_t ldh, const glu_proje
  * multiple of 4.
  */
 glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, glu_plan* plan);
+
+/*
+ * Backward of glu_dual_gemv: the gradients of hidden, gate_w and up_w for an
+ * upstream gradient dout of out.  The segKI "Plan B" autograd Function keeps
+ * hidden, gate_w and up_w and returns gradients equal to those of the
+ * composite silu(h Wg^T) * (h Wu^T) (DeepSpeed PR #9057 discussion, sections
+ * "Plan B Design" and "Verification Results"); over bf16 tensors each
+ * gradient tensor is rounded once to bf16, round to nearest even, as
+ * autograd of the bf16 composite rounds it.  With g, u, s the forward's bf16
+ * gate, up and silu(g) (glu_dual_gemv):
+ *   ds = bf16(dout * u)          du = bf16(dout * s)
+ *   dg = bf16(ds * sig * (1 + g * (1 - sig))), sig = 1 / (1 + exp(-g)),
+ *        evaluated in fp32 as (ds * sig) * (1 + g * (1 - sig))
+ *   dhidden = bf16(fp32(bf16(dg @ gate_w) + bf16(du @ up_w)))      [M,K]
+ *   dgate_w = bf16(dg^T @ hidden),  dup_w = bf16(du^T @ hidden)     [N,K]
+ * The contractions accumulate in fp32; dgate_w and dup_w sum the M rows of
+ * hidden in order, dhidden sums over the N weight rows in a fixed order.
+ *
+ * Arrays: bf16 bit patterns, dense row-major, on the current HIP device,
+ * caller-owned: hidden [M,K], gate_w and up_w [N,K], dout [M,N]; outputs
+ * dhidden [M,K], dgate_w and dup_w [N,K] (overwritten, not accumulated into).
+ * workspace: device memory of at least glu_dual_gemv_backward_workspace()
+ * bytes, 256-byte aligned, not overlapping any argument.  On return it
+ * begins with dg and du, the bf16 gradients of the gate and up
+ * pre-activations ([2][M][N], dense); the rest is scratch.  Limits: M <= 8 (else GLU_ERR_UNSUPPORTED); hidden, gate_w, up_w,
+ * dgate_w, dup_w 16-byte aligned and K % 8 == 0 (else GLU_ERR_UNSUPPORTED).
+ * Empty sums give +0: N == 0 zero-fills dhidden, M == 0 zero-fills both
+ * weight gradients; K == 0 has nothing to write.  Validation (NULL arrays,
+ * shapes, 2-byte alignment, overlap of an output or the workspace with an
+ * input or another output, workspace) happens before any HIP call.  Four
+ * launches on stream (the grouped GEMV for g and u, then the gradient
+ * kernels), asynchronous, deterministic, allocating nothing.
+ */
+glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                                  const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
+                                  int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
+/* Workspace bytes glu_dual_gemv_backward needs for (M, N, K), into *bytes
+ * (0 when an extent is zero).  Host only.  GLU_ERR_BAD_SHAPE or
+ * GLU_ERR_UNSUPPORTED (M > 8) as the call would return. */
+glu_status glu_dual_gemv_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+
+/* The backward's launch for (M, N, K), host only: kernel GLU_KERNEL_BACKWARD,
+ * grid of the contraction kernel, accum_depth = longest fp32 addition chain
+ * behind one of dhidden's two contributions. */
+glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan* plan);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,7 @@ from glu_mlp_gemv_amd import api
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # status codes of include/glu_gemv.h
-OK, NULLP, SHAPE, ALIGN, ALIAS, LAUNCH, UNSUP, STRIDE = range(8)
+OK, NULLP, SHAPE, ALIGN, ALIAS, LAUNCH, UNSUP, STRIDE, WORKSPACE = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strings(lib):
     assert lib.glu_version() >= 100
-    for s in range(7):
+    for s in range(9):
         assert api.status_string(s).startswith("GLU_")
     assert api.status_string(99) == "unknown glu_status"
     assert lib.glu_last_hip_error() == 0
@@ -267,6 +267,18 @@ def test_grouped_null_projection_array(lib):
     assert api.grouped_gemv_raw(A, 8, None, 1, 8, n=1) == NULLP
 
 
+@pytest.mark.parametrize("M,rows", [(2, 1), (2, 2), (5, 3), (33, 2), (2, 0)])
+def test_grouped_plan_tiny_row_counts(M, rows):
+    """Fewer rows than one 4-row group: every flag combination plans (or refuses) without a host fault."""
+    for fast in (False, True):
+        for mult4 in (False, True):
+            try:
+                p = api.grouped_plan(M, 520, rows, fast, None, mult4)
+            except api.GluError:
+                continue
+            assert p["kernel"] in (api.KERNEL_NONE, api.KERNEL_VALU, api.KERNEL_GENERIC, api.KERNEL_MFMA)
+
+
 def test_grouped_plans():
     p = api.grouped_plan(1, 2560, 4096 + 1024 + 1024)
     assert p["kernel"] == api.KERNEL_VALU and p["launches"] == 1
@@ -325,3 +337,71 @@ def test_gemm_plans_and_overrides(lib):
         api.grouped_plan(64, 1024, 100, tuning=api.make_tuning(gemm_tile_n=64))
     with pytest.raises(api.GluError):
         api.grouped_plan(64, 1024, 100, tuning=api.make_tuning(kernel=api.KERNEL_GEMM))
+
+
+# ---- backward -----------------------------------------------------------------
+
+def test_backward_plan_and_workspace(lib):
+    p = api.backward_plan(1, 9216, 2560)
+    assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 4 and p["grid"] % 5 == 0
+    assert api.backward_workspace_bytes(1, 9216, 2560) > 2 * 9216 * 2
+    assert api.backward_workspace_bytes(0, 9216, 2560) == 0
+    assert api.backward_plan(0, 5, 8)["kernel"] == api.KERNEL_ZERO   # weight gradients of an empty batch
+    assert api.backward_plan(3, 0, 8)["kernel"] == api.KERNEL_ZERO   # hidden's gradient of no outputs
+    assert api.backward_plan(3, 5, 0)["kernel"] == api.KERNEL_NONE
+    with pytest.raises(api.GluError):
+        api.backward_plan(9, 10, 64)          # M > 8
+    with pytest.raises(api.GluError):
+        api.backward_workspace_bytes(-1, 10, 64)
+    b = ctypes.c_int64(0)
+    assert lib.glu_dual_gemv_backward_workspace(1, 1, 8, None) == NULLP
+    assert lib.glu_dual_gemv_backward_plan(1, 1, 8, None) == NULLP
+
+
+def _bwd_ptrs(M, N, K):
+    """Disjoint fake device addresses for (hidden, gate_w, up_w, dout, dh, dwg, dwu, ws) of one shape."""
+    sizes = [M * K * 2, N * K * 2, N * K * 2, M * N * 2, M * K * 2, N * K * 2, N * K * 2,
+             max(api.backward_workspace_bytes(M, N, K), 1)]
+    ptrs, at = [], A
+    for sz in sizes:
+        ptrs.append(at)
+        at += (sz + 4095) // 4096 * 4096 + 4096
+    return ptrs, sizes[-1]
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, None),
+    ({0: 0}, NULLP), ({1: 0}, NULLP), ({3: 0}, NULLP), ({4: 0}, NULLP), ({6: 0}, NULLP),
+    ({0: 1}, ALIGN), ({3: 1}, ALIGN), ({5: 1}, ALIGN),               # odd addresses (offsets added)
+    ({1: 8}, UNSUP), ({5: 8}, UNSUP),                              # 8 but not 16-byte aligned
+    ({7: 0}, WORKSPACE), ({7: 64}, WORKSPACE), ("small", WORKSPACE),
+    ("dh_on_hidden", ALIAS), ("dwg_on_up", ALIAS), ("dwu_on_dwg", ALIAS), ("ws_on_dout", ALIAS),
+])
+def test_backward_validation_before_any_hip_call(lib, change, status):
+    M, N, K = 2, 64, 128
+    p, ws_bytes = _bwd_ptrs(M, N, K)
+    if change == "small":
+        ws_bytes -= 4
+    elif change == "dh_on_hidden":
+        p[4] = p[0] + 2
+    elif change == "dwg_on_up":
+        p[5] = p[2] + 16
+    elif change == "dwu_on_dwg":
+        p[6] = p[5] + 16
+    elif change == "ws_on_dout":
+        p[7] = p[3] - 256
+    elif isinstance(change, dict):
+        for i, v in change.items():
+            p[i] = 0 if v == 0 and i != 7 else (0 if v == 0 else p[i] + v)
+    if status is None:
+        return  # the valid call would launch: covered on the GPU
+    assert api.dual_gemv_backward_raw(*p[:7], M, N, K, p[7], ws_bytes) == status
+    assert lib.glu_last_hip_error() == 0
+
+
+def test_backward_shape_limits(lib):
+    p, ws = _bwd_ptrs(2, 64, 128)
+    assert api.dual_gemv_backward_raw(*p[:7], 9, 64, 128, p[7], ws) == UNSUP      # M > 8
+    assert api.dual_gemv_backward_raw(*p[:7], 2, 64, 100, p[7], ws) == UNSUP      # K % 8 != 0
+    assert api.dual_gemv_backward_raw(*p[:7], -1, 64, 128, p[7], ws) == SHAPE
+    assert api.dual_gemv_backward_raw(*p[:7], 2, 1 << 40, 1 << 40, p[7], ws) == SHAPE

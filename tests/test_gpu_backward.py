@@ -1,0 +1,181 @@
+"""GPU parity of the backward (glu_dual_gemv_backward) against the oracle's backward, through
+the C ABI (needs an MI355X).
+
+Bars (oracle/check.py): dgate_w and dup_w are single roundings of sums over
+the M rows of hidden (compare_linear, depth M); dhidden is the bf16 sum of two
+single-rounded contractions over the N weight rows (compare_grad_sum, depth
+from the backward's plan).  Every output within 2 ULP or its admissible
+interval, mean relative error <= 0.3 %, >= 99.9 % bit-exact over the call.
+Inputs: hidden N(0,1), weights N(0, 0.02^2), upstream gradient N(0,1).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import LinearResult, check
+from oracle.backward import act_grads, contract
+from oracle.backward import dual_gemv_backward as oracle_backward
+from glu_mlp_gemv_amd import api, autograd, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+CANARY = 0x1234
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_backward(h, wg, wu, go, outs=()):
+    """The GPU backward on host tensors; returns (dh, dwg, dwu) and the workspace's (dg, du) as bits."""
+    M, K = h.shape
+    N = wg.shape[0]
+    ws = torch.empty(max(api.backward_workspace_bytes(M, N, K), 1), dtype=torch.uint8, device=DEV)
+    got = api.dual_gemv_backward(h.to(DEV), wg.to(DEV), wu.to(DEV), go.to(DEV), *outs, workspace=ws)
+    torch.cuda.synchronize()
+    head = bits(ws[:4 * M * N].view(torch.bfloat16)).reshape(2, M, N)
+    return got, head[0], head[1]
+
+
+def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
+    """dg, du: equal to the oracle's, or to what the oracle's elementwise step gives from another
+    admissible (g, u) (an fp32 forward sum next to a bf16 rounding boundary may round either way).
+    The contractions: against the oracle's contraction of the device's own dg and du."""
+    M, K = h.shape
+    N = wg.shape[0]
+    hb, gb, ub, ob = bits(h), bits(wg), bits(wu), bits(go)
+    ref = oracle_backward(hb, gb, ub, ob)
+    diff = np.argwhere((dg_gpu != ref.dg) | (du_gpu != ref.du))
+    if diff.size:
+        fwd = oracle.dual_gemv(hb, gb, ub, with_pre=True)
+        depth = api.grouped_plan(M, K, 2 * N, True, None, N % 4 == 0)["accum_depth"]
+        for m, j in diff:
+            g_set = check.admissible_bf16_set(fwd.gate_pre[m, j], fwd.gate_abs[m, j], depth, K)
+            u_set = check.admissible_bf16_set(fwd.up_pre[m, j], fwd.up_abs[m, j], depth, K)
+            gg, uu = np.meshgrid(g_set, u_set)
+            _, du_c, dg_c = act_grads(gg.ravel(), uu.ravel(), np.full(gg.size, ob[m, j], dtype=np.uint16))
+            ok = np.any((dg_c == dg_gpu[m, j]) & (du_c == du_gpu[m, j]))
+            assert ok, (label, "dg/du from no admissible (g, u)", int(m), int(j), hex(int(dg_gpu[m, j])),
+                        hex(int(ref.dg[m, j])), hex(int(du_gpu[m, j])), hex(int(ref.du[m, j])))
+    say(f"[backward] {label} M={M} N={N} K={K}: {len(diff)} of {M * N} (dg, du) pairs from a neighbouring "
+        f"admissible (g, u)")
+    c = contract(hb, gb, ub, dg_gpu, du_gpu)
+    dh, dwg, dwu = (bits(t) for t in got)
+    plan = api.backward_plan(M, N, K)
+    reps = {
+        "dwg": check.compare_linear(dwg, LinearResult(c.dwg, c.dwg_pre, c.dwg_abs), depth=M, k_len=M),
+        "dwu": check.compare_linear(dwu, LinearResult(c.dwu, c.dwu_pre, c.dwu_abs), depth=M, k_len=M),
+        "dh": check.compare_grad_sum(dh, c.dh, c.dhg_pre, c.dhg_abs, c.dhu_pre, c.dhu_abs,
+                                     depth=plan["accum_depth"], k_len=N),
+    }
+    for name, rep in reps.items():
+        say(f"[backward] {label} M={M} N={N} K={K} {name}: {rep.summary()}")
+        assert rep.failures == 0 and rep.mean_rel <= 3e-3, (name, rep.summary())
+    assert check.pooled_bit_exact_ok(list(reps.values())), {k: r.summary() for k, r in reps.items()}
+    return reps
+
+
+CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2048), (5, 1, 520),
+         (8, 513, 4096), (8, 12288, 4096), (6, 3000, 1024), (7, 64, 40000)]
+
+
+@pytest.mark.parametrize("M,N,K", CASES)
+def test_backward_parity(M, N, K):
+    h, (wg, wu), go = inputs.hidden(M, K, 71), inputs.weights(N, K, 71), inputs.grad_out(M, N, 71)
+    got, dg, du = run_backward(h, wg, wu, go)
+    check_backward(h, wg, wu, go, got, dg, du, label="packed")
+
+
+def test_backward_outliers_and_scaled_row():
+    """The batched workload's weights (1 % outliers) and a row of hidden scaled by 8."""
+    h, wg, wu = inputs.case("mfma_k5120_n17408", M=16, seed=1)
+    h, wg, wu = h[:8].clone(), wg[:4096].clone(), wu[:4096].clone()
+    h[0] = (h[0].float() * 8).bfloat16()
+    go = inputs.grad_out(8, wg.shape[0], 72)
+    got, dg, du = run_backward(h, wg, wu, go)
+    check_backward(h, wg, wu, go, got, dg, du, label="outliers")
+
+
+def test_backward_determinism_and_given_outputs():
+    M, N, K = 4, 2000, 1024
+    h, (wg, wu), go = inputs.hidden(M, K, 73), inputs.weights(N, K, 73), inputs.grad_out(M, N, 73)
+    hd, gd, ud, od = h.to(DEV), wg.to(DEV), wu.to(DEV), go.to(DEV)
+    a = [bits(t) for t in api.dual_gemv_backward(hd, gd, ud, od)]
+    ws = torch.empty(api.backward_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    outs = (torch.full((M, K), 7.0, dtype=torch.bfloat16, device=DEV),
+            torch.full((N, K), 7.0, dtype=torch.bfloat16, device=DEV),
+            torch.full((N, K), 7.0, dtype=torch.bfloat16, device=DEV))
+    for _ in range(3):
+        api.dual_gemv_backward(hd, gd, ud, od, *outs, workspace=ws)
+        torch.cuda.synchronize()
+        assert all(np.array_equal(x, bits(y)) for x, y in zip(a, outs)), "repeated calls must be bitwise equal"
+
+
+def test_backward_canaries_around_outputs():
+    """Outputs as views into larger buffers holding a canary before and after: nothing outside is written."""
+    M, N, K = 3, 333, 1032
+    h, (wg, wu), go = inputs.hidden(M, K, 74), inputs.weights(N, K, 74), inputs.grad_out(M, N, 74)
+    pad = 64  # elements; keeps 16-byte alignment of the views
+    bufs = [torch.full((n + 2 * pad,), CANARY, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+            for n in (M * K, N * K, N * K)]
+    views = [b[pad:pad + n].view(shape) for b, n, shape in zip(bufs, (M * K, N * K, N * K), ((M, K), (N, K), (N, K)))]
+    _, dg, du = run_backward(h, wg, wu, go, outs=views)
+    for b in bufs:
+        bb = bits(b)
+        assert (bb[:pad] == CANARY).all() and (bb[-pad:] == CANARY).all(), "a write landed outside an output"
+    check_backward(h, wg, wu, go, views, dg, du, label="canaries")
+
+
+def test_backward_empty_sums_are_zero():
+    K = 64
+    # N == 0: hidden's gradient is an empty sum
+    dh = torch.full((2, K), 5.0, dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros(0, K, dtype=torch.bfloat16, device=DEV)
+    api.dual_gemv_backward(torch.ones(2, K, dtype=torch.bfloat16, device=DEV), w, w,
+                           torch.zeros(2, 0, dtype=torch.bfloat16, device=DEV), dhidden=dh,
+                           dgate_w=torch.zeros(0, K, dtype=torch.bfloat16, device=DEV),
+                           dup_w=torch.zeros(0, K, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert (bits(dh) == 0).all()
+    # M == 0: the weights' gradients are empty sums
+    dwg = torch.full((5, K), 5.0, dtype=torch.bfloat16, device=DEV)
+    dwu = torch.full((5, K), 5.0, dtype=torch.bfloat16, device=DEV)
+    api.dual_gemv_backward(torch.zeros(0, K, dtype=torch.bfloat16, device=DEV),
+                           torch.ones(5, K, dtype=torch.bfloat16, device=DEV),
+                           torch.ones(5, K, dtype=torch.bfloat16, device=DEV),
+                           torch.zeros(0, 5, dtype=torch.bfloat16, device=DEV),
+                           dhidden=torch.zeros(0, K, dtype=torch.bfloat16, device=DEV), dgate_w=dwg, dup_w=dwu)
+    torch.cuda.synchronize()
+    assert (bits(dwg) == 0).all() and (bits(dwu) == 0).all()
+
+
+def test_backward_gate_zero_closed_form():
+    """Wg = 0: g = 0, so du = 0 (dWu = 0), dWg = bf16(sum_m (ds/2) h), dh = bf16(dg @ 0 + 0) = 0."""
+    M, N, K = 4, 256, 512
+    h, (_, wu), go = inputs.hidden(M, K, 75), inputs.weights(N, K, 75), inputs.grad_out(M, N, 75)
+    wg = torch.zeros(N, K, dtype=torch.bfloat16)
+    (dh, dwg, dwu), dg, du = run_backward(h, wg, wu, go)
+    assert (bits(dwu) & 0x7FFF == 0).all() and (bits(dh) & 0x7FFF == 0).all()
+    check_backward(h, wg, wu, go, (dh, dwg, dwu), dg, du, label="gate zero")
+
+
+def test_autograd_function_matches_both_entry_points():
+    """The autograd Function's forward is glu_dual_gemv and its gradients glu_dual_gemv_backward."""
+    M, N, K = 2, 700, 1024
+    h, (wg, wu), go = inputs.hidden(M, K, 76), inputs.weights(N, K, 76), inputs.grad_out(M, N, 76)
+    hd, gd, ud = (t.to(DEV).requires_grad_() for t in (h, wg, wu))
+    out = autograd.dual_weight_glu(hd, gd, ud)
+    out.backward(go.to(DEV))
+    torch.cuda.synchronize()
+    fwd = api.dual_gemv(h.to(DEV), wg.to(DEV), wu.to(DEV))
+    ref = api.dual_gemv_backward(h.to(DEV), wg.to(DEV), wu.to(DEV), go.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(fwd))
+    for a, b in zip((hd.grad, gd.grad, ud.grad), ref):
+        assert np.array_equal(bits(a), bits(b))

@@ -83,6 +83,9 @@ CASES = [
     ((1024, 512), 4096, 7, dict(kernel=MFMA, mfma_segments=2, grid=3, waves_per_block=2)),
     ((256, 8), 2048, 12, dict(kernel=MFMA, grid=1000)),
     ((4096, 1024, 1024), 2560, 4, dict(kernel=api.KERNEL_VALU)),
+    ((1, 1), 520, 2, {}),                     # fewer rows than one 4-row group, M >= 2
+    ((2,), 520, 5, {}),
+    ((3,), 64, 33, {}),
 ]
 
 
