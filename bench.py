@@ -188,6 +188,33 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
                 del g
         del pool
         torch.cuda.empty_cache()
+    # backward: gradients of hidden and both weights (reads Wg, Wu once more, writes dWg, dWu)
+    for (K, N), Ms in (((2560, 9216), (1, 4)), ((4096, 12288), (1, 8))):
+        per = 4 * N * K * 2  # weights and their gradients per set
+        sets = max(4, -(-1_400_000_000 // per))
+        pool = [(*inputs.weights(N, K, 600 + i, device=dev),
+                 torch.empty(N, K, dtype=torch.bfloat16, device=dev),
+                 torch.empty(N, K, dtype=torch.bfloat16, device=dev)) for i in range(sets)]
+        for M in Ms:
+            h = inputs.hidden(M, K, 0).to(dev)
+            go = inputs.grad_out(M, N, 0).to(dev)
+            dh = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(api.backward_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+
+            def one_pass():
+                for wg, wu, dwg, dwu in pool:
+                    api.dual_gemv_backward(h, wg, wu, go, dh, dwg, dwu, workspace=ws)
+            g = capture(torch, one_pass)
+            ms = time_region(torch, g.replay, reps, 2, stream)
+            us = ms * 1e3 / (reps * sets)
+            b = 8 * N * K + 4 * M * K + 2 * M * N
+            res.append({"workload": f"backward_k{K}_n{N}", "M": M, "K": K, "N": N, "us_per_call": round(us, 3),
+                        "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "kernel": "backward", "pool_sets": sets})
+            print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+            del g
+        del pool
+        torch.cuda.empty_cache()
     # row-strided operands: gate and up as the two column halves of one fused
     # [N, 2K] block (each keeps the fused row stride 2K), at the decode shape
     N, K = STACK["N"], STACK["K"]

@@ -17,7 +17,8 @@
 //    same rows' slab of dWg and dWu (sum over the M rows of hidden, in order).
 //    The 4 waves' dh sums are added in LDS in a fixed order and written as the
 //    workgroup's fp32 partial;
-//  * dh_reduce_kernel: sums the row ranges' partials in order, rounds each
+//  * dh_reduce_kernel: sums the row ranges' partials in a fixed order (16 lane
+//    groups over interleaved ranges, then the groups in order), rounds each
 //    contribution and their fp32 sum to bf16.
 // No atomics: results are bitwise reproducible.
 #include "glu_backward.h"
@@ -30,6 +31,9 @@ namespace {
 constexpr int kSlab = 512;          // columns per contraction tile (8 per lane)
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * kWave;
+constexpr int kRowsPerIter = 4;     // weight rows whose loads a wave issues together
+constexpr int kReduceCols = 16;     // 4-element groups of dh per reduction workgroup
+constexpr int kReduceParts = 16;    // lane groups splitting the row ranges of one element
 
 typedef unsigned u32x4_b __attribute__((ext_vector_type(4)));
 
@@ -114,54 +118,71 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
         }
     }
 
-    for (int j = j_begin + wave; j < j_end; j += kBwdWaves) {
-        float dg[M], du[M];
+    // rows j0 + 4i (i < kRowsPerIter) per iteration: their loads are issued together
+    for (int j0 = j_begin + wave; j0 < j_end; j0 += kBwdWaves * kRowsPerIter) {
+        u32x4_b wgv[kRowsPerIter], wuv[kRowsPerIter];
+        float dg[kRowsPerIter][M], du[kRowsPerIter][M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            dg[m] = bf16_to_f32(dgu[(int64_t)m * N + j]);
-            du[m] = bf16_to_f32(dgu[MN + (int64_t)m * N + j]);
-        }
-        if (!col_ok) continue;
-        const u32x4_b wgv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(gate_w + (int64_t)j * K + c0));
-        const u32x4_b wuv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(up_w + (int64_t)j * K + c0));
-        float wgf[8], wuf[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            wgf[2 * q] = bf16lo(wgv[q]);
-            wgf[2 * q + 1] = bf16hi(wgv[q]);
-            wuf[2 * q] = bf16lo(wuv[q]);
-            wuf[2 * q + 1] = bf16hi(wuv[q]);
-        }
-        // dh contributions (a product of two bf16 values is exact in fp32, so fma adds it unrounded)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                ag[m][e] = __builtin_fmaf(dg[m], wgf[e], ag[m][e]);
-                au[m][e] = __builtin_fmaf(du[m], wuf[e], au[m][e]);
-            }
-        }
-        // this row's slab of dWg and dWu: sums over the rows of hidden in order
-        uint16_t og[8], ou[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float sg = 0.0f, su = 0.0f;
+        for (int i = 0; i < kRowsPerIter; ++i) {
+            const int j = min(j0 + kBwdWaves * i, j_end - 1);  // past the range: re-read a valid row, unused
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                sg = __builtin_fmaf(dg[m], hv[m][e], sg);
-                su = __builtin_fmaf(du[m], hv[m][e], su);
+                dg[i][m] = bf16_to_f32(dgu[(int64_t)m * N + j]);
+                du[i][m] = bf16_to_f32(dgu[MN + (int64_t)m * N + j]);
             }
-            og[e] = f32_to_bf16_rne(sg);
-            ou[e] = f32_to_bf16_rne(su);
+            if (col_ok) {
+                wgv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(gate_w + (int64_t)j * K + c0));
+                wuv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(up_w + (int64_t)j * K + c0));
+            } else {
+                wgv[i] = u32x4_b{0u, 0u, 0u, 0u};
+                wuv[i] = u32x4_b{0u, 0u, 0u, 0u};
+            }
         }
-        u32x4_b pg, pu;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            pg[q] = (uint32_t)og[2 * q] | ((uint32_t)og[2 * q + 1] << 16);
-            pu[q] = (uint32_t)ou[2 * q] | ((uint32_t)ou[2 * q + 1] << 16);
+        for (int i = 0; i < kRowsPerIter; ++i) {
+            const int j = j0 + kBwdWaves * i;
+            if (j >= j_end) break;  // wave-uniform
+            float wgf[8], wuf[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wgf[2 * q] = bf16lo(wgv[i][q]);
+                wgf[2 * q + 1] = bf16hi(wgv[i][q]);
+                wuf[2 * q] = bf16lo(wuv[i][q]);
+                wuf[2 * q + 1] = bf16hi(wuv[i][q]);
+            }
+            // dh contributions (a product of two bf16 values is exact in fp32, so fma adds it unrounded)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ag[m][e] = __builtin_fmaf(dg[i][m], wgf[e], ag[m][e]);
+                    au[m][e] = __builtin_fmaf(du[i][m], wuf[e], au[m][e]);
+                }
+            }
+            if (!col_ok) continue;
+            // this row's slab of dWg and dWu: sums over the rows of hidden in order
+            u32x4_b pg, pu;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint16_t og[2], ou[2];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int e = 2 * q + h2;
+                    float sg = 0.0f, su = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        sg = __builtin_fmaf(dg[i][m], hv[m][e], sg);
+                        su = __builtin_fmaf(du[i][m], hv[m][e], su);
+                    }
+                    og[h2] = f32_to_bf16_rne(sg);
+                    ou[h2] = f32_to_bf16_rne(su);
+                }
+                pg[q] = (uint32_t)og[0] | ((uint32_t)og[1] << 16);
+                pu[q] = (uint32_t)ou[0] | ((uint32_t)ou[1] << 16);
+            }
+            __builtin_nontemporal_store(pg, reinterpret_cast<u32x4_b*>(dwg + (int64_t)j * K + c0));
+            __builtin_nontemporal_store(pu, reinterpret_cast<u32x4_b*>(dwu + (int64_t)j * K + c0));
         }
-        __builtin_nontemporal_store(pg, reinterpret_cast<u32x4_b*>(dwg + (int64_t)j * K + c0));
-        __builtin_nontemporal_store(pu, reinterpret_cast<u32x4_b*>(dwu + (int64_t)j * K + c0));
     }
 
     // the waves' dh sums, added in the order 3, 2, 1, 0
@@ -192,24 +213,49 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
     }
 }
 
-// dh[m][c] = bf16(fp32(bf16(sum_r Pg[r][m][c]) + bf16(sum_r Pu[r][m][c]))), r in order
-__global__ void __launch_bounds__(256)
+// dh[m][c] = bf16(fp32(bf16(sum Pg) + bf16(sum Pu))) over the row ranges' partials.  A lane
+// owns 4 consecutive elements (16-byte loads); lane group p sums ranges p, p + 16, p + 32, ... in
+// order, then group 0 adds the 16 group sums in order 0..15.  M * K % 4 == 0 (K % 8 == 0).
+__global__ void __launch_bounds__(kReduceCols * kReduceParts)
 dh_reduce_kernel(const float* __restrict__ partial, uint16_t* __restrict__ dh, int64_t ldh_out, int M, int K,
                  int nranges)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    typedef float f32x4_b __attribute__((ext_vector_type(4)));
+    __shared__ f32x4_b part[2][kReduceParts][kReduceCols];
+    const int col = threadIdx.x % kReduceCols;
+    const int grp = threadIdx.x / kReduceCols;
     const int64_t MK = (int64_t)M * K;
-    if (i >= MK) return;
-    const int64_t m = i / K;
-    const int64_t c = i - m * K;
-    float sg = 0.0f, su = 0.0f;
-    for (int r = 0; r < nranges; ++r) {
-        sg += partial[((int64_t)r * 2 + 0) * MK + i];
-        su += partial[((int64_t)r * 2 + 1) * MK + i];
+    const int64_t i4 = (int64_t)blockIdx.x * kReduceCols + col;  // index of 4 elements
+    const bool ok = i4 * 4 < MK;
+    f32x4_b sg = {0.0f, 0.0f, 0.0f, 0.0f}, su = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ok) {
+        const f32x4_b* p4 = reinterpret_cast<const f32x4_b*>(partial);
+        const int64_t MK4 = MK / 4;
+#pragma unroll 4
+        for (int r = grp; r < nranges; r += kReduceParts) {
+            sg += p4[((int64_t)r * 2 + 0) * MK4 + i4];
+            su += p4[((int64_t)r * 2 + 1) * MK4 + i4];
+        }
     }
-    const float a = bf16_to_f32(f32_to_bf16_rne(sg));
-    const float b = bf16_to_f32(f32_to_bf16_rne(su));
-    dh[m * ldh_out + c] = f32_to_bf16_rne(a + b);
+    part[0][grp][col] = sg;
+    part[1][grp][col] = su;
+    __syncthreads();
+    if (grp != 0 || !ok) return;
+    f32x4_b tg = part[0][0][col], tu = part[1][0][col];
+#pragma unroll
+    for (int p = 1; p < kReduceParts; ++p) {
+        tg += part[0][p][col];
+        tu += part[1][p][col];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i4 * 4 + e;
+        const int64_t m = i / K;
+        const int64_t c = i - m * K;
+        const float a = bf16_to_f32(f32_to_bf16_rne(tg[e]));
+        const float b = bf16_to_f32(f32_to_bf16_rne(tu[e]));
+        dh[m * ldh_out + c] = f32_to_bf16_rne(a + b);
+    }
 }
 
 namespace {
@@ -249,8 +295,9 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     p.gu_bytes = ((int64_t)2 * M * N * 2 + 255) / 256 * 256;
     p.partial_bytes = (int64_t)p.nranges * 2 * M * K * 4;
     p.workspace_bytes = p.gu_bytes + p.partial_bytes;
-    // dh: within a wave its rows in order, then 4 waves, then the ranges
-    p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves + p.nranges;
+    // dh: within a wave its rows in order, then 4 waves, then every 16th range, then the 16 group sums
+    p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves +
+                    (p.nranges + kReduceParts - 1) / kReduceParts + kReduceParts;
     return p;
 }
 
@@ -281,9 +328,9 @@ hipError_t dh_reduce_launch(const BwdPlan& p, const float* partial, uint16_t* dh
 {
     const int64_t n = (int64_t)M * K;
     if (n <= 0) return hipSuccess;
-    const int64_t grid = (n + 255) / 256;
-    hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partial, dh, ldh_out, M, K,
-                       p.nranges);
+    const int64_t grid = (n / 4 + kReduceCols - 1) / kReduceCols;
+    hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)grid), dim3(kReduceCols * kReduceParts), 0, stream, partial,
+                       dh, ldh_out, M, K, p.nranges);
     return hipGetLastError();
 }
 
