@@ -10,12 +10,13 @@ bandwidth: algorithmic bytes (both weight matrices once, hidden and output)
 over time.
 
 Prints ONE JSON line.  Other modes:
-  --workloads FILE     also time the batched workloads (JSON written to FILE)
+  --workloads FILE     also time the batched workloads (JSON written to FILE);
+                       --filter S keeps the sections whose name contains S
   --calibrate-copy     run a 256 MiB device copy first (reference kernel for
                        rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE scaling)
   --summarize KIND DIR turn rocprofv3 output in DIR into the text summaries
-                       kept under profiles/ (KIND: trace | counters); host
-                       only, no GPU
+                       kept under profiles/ (KIND: trace | trace-grid |
+                       counters); host only, no GPU
 """
 from __future__ import annotations
 
@@ -126,12 +127,16 @@ def cpu_baseline(torch, ws, hs, layers_sample: int, min_seconds: float):
                       f"M=1 K={K} N={N} stack, {el:.1f} s wall, {threads} OpenMP threads"}
 
 
-def bench_workloads(torch, api, inputs, dev, reps=30):
+def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
     """Batched workloads and M=1 at the same (K, N), each over a rotation pool of >= 1.4 GB,
-    one graph replay per pass over the pool."""
+    one graph replay per pass over the pool.  ``only``: run the sections whose name contains it
+    (batched, prefill, backward, rows, grouped)."""
     res = []
     stream = torch.cuda.current_stream()
-    for name in ("batch_k4096_n12288", "mfma_k5120_n17408"):
+
+    def want(section):
+        return only is None or only in section
+    for name in (("batch_k4096_n12288", "mfma_k5120_n17408") if want("batched") else ()):
         w = inputs.WORKLOADS[name]
         per = 2 * w.N * w.K * 2
         sets = max(4, -(-1_400_000_000 // per))
@@ -158,7 +163,8 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
         del pool
         torch.cuda.empty_cache()
     # large batches (prefill-like): the tiled GEMM, and the 32-row chunked MFMA path it replaces
-    for (K, N), Ms in (((5120, 17408), (64, 128, 256, 512, 1024)), ((2560, 9216), (64, 256, 1024))):
+    for (K, N), Ms in ((((5120, 17408), (64, 128, 256, 512, 1024)), ((2560, 9216), (64, 256, 1024)))
+                       if want("prefill") else ()):
         per = 2 * N * K * 2
         sets = max(4, -(-1_400_000_000 // per))
         pool = [inputs.weights(N, K, 500 + i, device=dev) for i in range(sets)]
@@ -189,7 +195,7 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
         del pool
         torch.cuda.empty_cache()
     # backward: gradients of hidden and both weights (reads Wg, Wu once more, writes dWg, dWu)
-    for (K, N), Ms in (((2560, 9216), (1, 4)), ((4096, 12288), (1, 8))):
+    for (K, N), Ms in ((((2560, 9216), (1, 4)), ((4096, 12288), (1, 8))) if want("backward") else ()):
         per = 4 * N * K * 2  # weights and their gradients per set
         sets = max(4, -(-1_400_000_000 // per))
         pool = [(*inputs.weights(N, K, 600 + i, device=dev),
@@ -216,36 +222,39 @@ def bench_workloads(torch, api, inputs, dev, reps=30):
         del pool
         torch.cuda.empty_cache()
     # row-strided operands: gate and up as the two column halves of one fused
-    # [N, 2K] block (each keeps the fused row stride 2K), at the decode shape
-    N, K = STACK["N"], STACK["K"]
-    sets = max(4, -(-1_400_000_000 // (2 * N * K * 2)))
-    fused = [torch.cat(inputs.weights(N, K, 300 + i, device=dev), dim=1) for i in range(sets)]
-    for layout in ("packed", "fused"):
-        # the same weights, as two packed copies or as the two halves of the fused block
-        ops = ([(f[:, :K].contiguous(), f[:, K:].contiguous()) for f in fused] if layout == "packed"
-               else [(f[:, :K], f[:, K:]) for f in fused])
-        for M in (1, 4):
-            h = inputs.hidden(M, K, 0).to(dev)
-            out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    if want("rows"):
+        # [N, 2K] block (each keeps the fused row stride 2K), at the decode shape
+        N, K = STACK["N"], STACK["K"]
+        sets = max(4, -(-1_400_000_000 // (2 * N * K * 2)))
+        fused = [torch.cat(inputs.weights(N, K, 300 + i, device=dev), dim=1) for i in range(sets)]
+        for layout in ("packed", "fused"):
+            # the same weights, as two packed copies or as the two halves of the fused block
+            ops = ([(f[:, :K].contiguous(), f[:, K:].contiguous()) for f in fused] if layout == "packed"
+                   else [(f[:, :K], f[:, K:]) for f in fused])
+            for M in (1, 4):
+                h = inputs.hidden(M, K, 0).to(dev)
+                out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
 
-            def one_pass():
-                for wg, wu in ops:
-                    api.dual_gemv(h, wg, wu, out=out)
-            g = capture(torch, one_pass)
-            ms = time_region(torch, g.replay, reps, 2, stream)
-            us = ms * 1e3 / (reps * sets)
-            b = algorithmic_bytes(M, N, K)
-            res.append({"workload": f"rows_{layout}_k2560_n9216", "M": M, "K": K, "N": N,
-                        "us_per_call": round(us, 3), "GBs": round(b / us / 1e3, 1),
-                        "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4), "row_stride": ops[0][0].stride(0),
-                        "kernel": api.plan(M, N, K)["kernel_name"], "pool_sets": sets})
-            print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
-            del g
-        del ops
-    del fused
-    torch.cuda.empty_cache()
+                def one_pass():
+                    for wg, wu in ops:
+                        api.dual_gemv(h, wg, wu, out=out)
+                g = capture(torch, one_pass)
+                ms = time_region(torch, g.replay, reps, 2, stream)
+                us = ms * 1e3 / (reps * sets)
+                b = algorithmic_bytes(M, N, K)
+                res.append({"workload": f"rows_{layout}_k2560_n9216", "M": M, "K": K, "N": N,
+                            "us_per_call": round(us, 3), "GBs": round(b / us / 1e3, 1),
+                            "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4), "row_stride": ops[0][0].stride(0),
+                            "kernel": api.plan(M, N, K)["kernel_name"], "pool_sets": sets})
+                print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+                del g
+            del ops
+        del fused
+        torch.cuda.empty_cache()
     # grouped GEMV: n projections of one hidden, weights read in place
-    for name, Ns in (("grouped_qkv_like_k2560", (4096, 1024, 1024)), ("grouped_gdn_like_k2560", (8192, 4096, 32, 32))):
+    for name, Ns in ((("grouped_qkv_like_k2560", (4096, 1024, 1024)), ("grouped_gdn_like_k2560", (8192, 4096, 32, 32)))
+                     if want("grouped") else ()):
+        K = STACK["K"]
         rows = sum(Ns)
         per = rows * K * 2
         sets = max(4, -(-1_400_000_000 // per))
@@ -348,7 +357,7 @@ def run(args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, ws, hs, layers_sample=4, min_seconds=args.cpu_seconds)
     if args.workloads:
-        extra = {"workloads": bench_workloads(torch, api, inputs, dev), "stack": line}
+        extra = {"workloads": bench_workloads(torch, api, inputs, dev, only=args.filter), "stack": line}
         os.makedirs(os.path.dirname(os.path.abspath(args.workloads)), exist_ok=True)
         with open(args.workloads, "w") as f:
             json.dump(extra, f, indent=1)
@@ -375,6 +384,27 @@ def summarize_trace(d: str):
     for r in stats:
         lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {r['TotalDurationNs']} | "
                      f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines)
+
+
+def summarize_trace_grid(d: str):
+    """Per-dispatch kernel trace grouped by (kernel, grid size): a kernel run at several shapes gets
+    one row per shape (the grid tells them apart), average and median duration."""
+    rows = _rows(os.path.join(d, "**", "*kernel_trace.csv"))
+    if not rows:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if not name.startswith(("glu::", "void glu::")):
+            continue
+        key = (name.split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]), int(r["LDS_Block_Size"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["| kernel | grid (threads) | LDS bytes | dispatches | average ns | median ns | min ns |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, lds), ts in sorted(groups.items()):
+        ts.sort()
+        lines.append(f"| `{name}` | {grid} | {lds} | {len(ts)} | {sum(ts) / len(ts):.0f} | {ts[len(ts) // 2]} | {ts[0]} |")
     return "\n".join(lines)
 
 
@@ -422,6 +452,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--workloads", default=None, metavar="FILE", help="also time the batched workloads")
+    ap.add_argument("--filter", default=None, help="with --workloads: only the sections whose name contains this "
+                                                   "(batched, prefill, backward, rows, grouped)")
     ap.add_argument("--tuning", default=None, help="JSON dict of glu_tuning fields")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"))
@@ -431,6 +463,8 @@ def main():
         kind, d = args.summarize
         if kind == "trace":
             print(summarize_trace(d))
+        elif kind == "trace-grid":
+            print(summarize_trace_grid(d))
         else:
             print(json.dumps(summarize_counters(d, args.command), indent=1))
         return
