@@ -45,11 +45,19 @@ def algorithmic_bytes(M: int, N: int, K: int) -> int:
     return 2 * N * K * 2 + M * K * 2 + M * N * 2
 
 
+# the sources the headline kernel (the VALU GEMV) is compiled from: its template, its per-M
+# instantiations and dispatch, and the headers they include
+HEADLINE_SOURCES = ("glu_valu", "glu_device.h", "glu_launch.h")
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources: counter figures are valid only for the kernels they were taken on."""
+    """Hash of the headline kernel's HIP sources: counter figures are valid only for the kernel
+    they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "glu_mlp_gemv_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.startswith(HEADLINE_SOURCES):
+            continue
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
