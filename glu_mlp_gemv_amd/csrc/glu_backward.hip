@@ -97,16 +97,12 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
     const int j_end = min(j_begin + rows_per_range, N);
     const int64_t MN = (int64_t)M * N;
 
-    float hv[M][8];
+    // this lane's 8 columns of every row of hidden, as packed bf16 pairs (widened where used)
+    u32x4_b hw[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        u32x4_b w = {0u, 0u, 0u, 0u};
-        if (col_ok) w = *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + c0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            hv[m][2 * q] = bf16lo(w[q]);
-            hv[m][2 * q + 1] = bf16hi(w[q]);
-        }
+        hw[m] = u32x4_b{0u, 0u, 0u, 0u};
+        if (col_ok) hw[m] = *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + c0);
     }
     float ag[M][8], au[M][8];
 #pragma unroll
@@ -118,12 +114,14 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
         }
     }
 
-    // rows j0 + 4i (i < kRowsPerIter) per iteration: their loads are issued together
-    for (int j0 = j_begin + wave; j0 < j_end; j0 += kBwdWaves * kRowsPerIter) {
-        u32x4_b wgv[kRowsPerIter], wuv[kRowsPerIter];
-        float dg[kRowsPerIter][M], du[kRowsPerIter][M];
+    // rows j0 + 4i (i < RPI) per iteration: their loads are issued together (fewer rows above
+    // M = 4, where the dh accumulators take most of the registers)
+    constexpr int RPI = M <= 4 ? kRowsPerIter : (M <= 6 ? kRowsPerIter / 2 : 1);
+    for (int j0 = j_begin + wave; j0 < j_end; j0 += kBwdWaves * RPI) {
+        u32x4_b wgv[RPI], wuv[RPI];
+        float dg[RPI][M], du[RPI][M];
 #pragma unroll
-        for (int i = 0; i < kRowsPerIter; ++i) {
+        for (int i = 0; i < RPI; ++i) {
             const int j = min(j0 + kBwdWaves * i, j_end - 1);  // past the range: re-read a valid row, unused
 #pragma unroll
             for (int m = 0; m < M; ++m) {
@@ -139,7 +137,7 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
             }
         }
 #pragma unroll
-        for (int i = 0; i < kRowsPerIter; ++i) {
+        for (int i = 0; i < RPI; ++i) {
             const int j = j0 + kBwdWaves * i;
             if (j >= j_end) break;  // wave-uniform
             float wgf[8], wuf[8];
@@ -167,12 +165,12 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
                 uint16_t og[2], ou[2];
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    const int e = 2 * q + h2;
                     float sg = 0.0f, su = 0.0f;
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        sg = __builtin_fmaf(dg[i][m], hv[m][e], sg);
-                        su = __builtin_fmaf(du[i][m], hv[m][e], su);
+                        const float hme = h2 ? bf16hi(hw[m][q]) : bf16lo(hw[m][q]);
+                        sg = __builtin_fmaf(dg[i][m], hme, sg);
+                        su = __builtin_fmaf(du[i][m], hme, su);
                     }
                     og[h2] = f32_to_bf16_rne(sg);
                     ou[h2] = f32_to_bf16_rne(su);
