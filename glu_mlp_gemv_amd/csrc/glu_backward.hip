@@ -8,8 +8,11 @@
 //   ds = bf16(dout u), du = bf16(dout s), dg = bf16(silu'(g) ds) in fp32,
 //   dh = bf16(fp32(bf16(dg Wg) + bf16(du Wu))), dWg = bf16(dg^T h), dWu = bf16(du^T h).
 //
-// Launches (after the grouped GEMV has written g = bf16(h Wg^T) and
-// u = bf16(h Wu^T) into the workspace):
+// M = 1 with K <= 2560: one pass (fused1_kernel, below) reads each row of Wg
+// and Wu once, forms G and U, dg and du, writes the row of dWg and dWu and
+// accumulates dh, then dh_reduce_kernel adds the workgroups' partials.
+// Otherwise four launches (after the grouped GEMV has written
+// g = bf16(h Wg^T) and u = bf16(h Wu^T) into the workspace):
 //  * act_grad_kernel: dg and du from g, u and dout, elementwise, in place;
 //  * contract_kernel: workgroups own (row range, 512-column slab) tiles.  Each
 //    wave streams its rows' 1 KiB slab pieces of Wg and Wu once, accumulates
@@ -211,6 +214,145 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
     }
 }
 
+// One pass for M = 1 (K <= 64 * 8 * U): wave w owns rows w, w + W, ... (W waves in the grid).
+// Lane l holds 16-byte chunks l, l + 64, ... of its row of Wg and Wu and of hidden.  Per row:
+// G and U (fp32 fma per lane, wave butterfly), dg and du (act_grad, all lanes; lane 0 stores them
+// at the workspace head), the row of dWg and dWu (dg * h and du * h, one rounding each), and dh's
+// two contributions accumulated per lane.  The workgroup's waves then add their dh sums in LDS in
+// order 0, 1, ..., and the sum becomes the workgroup's partial: partial[b][2][K].
+template <int U, int WAVES>
+__global__ void __launch_bounds__(WAVES * kWave)
+fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+              const uint16_t* __restrict__ up_w, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dgu,
+              uint16_t* __restrict__ dwg, uint16_t* __restrict__ dwu, float* __restrict__ partial, int N, int K)
+{
+    extern __shared__ float red1[];  // [2][K]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + wave);
+    const int nwaves = gridDim.x * WAVES;
+    const int nchunks = K >> 3;
+
+    u32x4_b hw[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = lane + kWave * u;
+        ok[u] = c < nchunks;
+        hw[u] = ok[u] ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)c * 8) : u32x4_b{0u, 0u, 0u, 0u};
+    }
+    float ag[U][8], au[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ag[u][e] = 0.0f;
+            au[u][e] = 0.0f;
+        }
+    }
+
+    // a row's loads: its chunks of Wg and Wu and its upstream gradient (issued together, so waiting
+    // for one row never waits for the next row's prefetch)
+    auto load_row = [&](int j, u32x4_b (&wg)[U], u32x4_b (&wu)[U], uint16_t& go) __attribute__((always_inline)) {
+        go = dout[j];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = min(lane + kWave * u, nchunks - 1);  // past K: re-read a valid chunk, zeroed below
+            wg[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(gate_w + (int64_t)j * K + c * 8));
+            wu[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(up_w + (int64_t)j * K + c * 8));
+        }
+    };
+    auto process = [&](int j, u32x4_b (&wg)[U], u32x4_b (&wu)[U], uint16_t go) __attribute__((always_inline)) {
+        float pg = 0.0f, pu = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4_b z = {0u, 0u, 0u, 0u};
+            const u32x4_b g4 = ok[u] ? wg[u] : z;
+            const u32x4_b u4 = ok[u] ? wu[u] : z;
+            wg[u] = g4;
+            wu[u] = u4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                pg = __builtin_fmaf(bf16lo(hw[u][q]), bf16lo(g4[q]), pg);
+                pg = __builtin_fmaf(bf16hi(hw[u][q]), bf16hi(g4[q]), pg);
+                pu = __builtin_fmaf(bf16lo(hw[u][q]), bf16lo(u4[q]), pu);
+                pu = __builtin_fmaf(bf16hi(hw[u][q]), bf16hi(u4[q]), pu);
+            }
+        }
+        const float G = wave_sum(pg);
+        const float Uv = wave_sum(pu);
+        uint16_t dgb, dub;
+        act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)), bf16_to_f32(go), &dgb, &dub);
+        if (lane == 0) {
+            dgu[j] = dgb;
+            dgu[N + j] = dub;
+        }
+        const float dg = bf16_to_f32(dgb);
+        const float du = bf16_to_f32(dub);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4_b og, ou;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float h0 = bf16lo(hw[u][q]), h1 = bf16hi(hw[u][q]);
+                og[q] = (uint32_t)f32_to_bf16_rne(dg * h0) | ((uint32_t)f32_to_bf16_rne(dg * h1) << 16);
+                ou[q] = (uint32_t)f32_to_bf16_rne(du * h0) | ((uint32_t)f32_to_bf16_rne(du * h1) << 16);
+                ag[u][2 * q] = __builtin_fmaf(dg, bf16lo(wg[u][q]), ag[u][2 * q]);
+                ag[u][2 * q + 1] = __builtin_fmaf(dg, bf16hi(wg[u][q]), ag[u][2 * q + 1]);
+                au[u][2 * q] = __builtin_fmaf(du, bf16lo(wu[u][q]), au[u][2 * q]);
+                au[u][2 * q + 1] = __builtin_fmaf(du, bf16hi(wu[u][q]), au[u][2 * q + 1]);
+            }
+            if (ok[u]) {
+                const int c = lane + kWave * u;
+                __builtin_nontemporal_store(og, reinterpret_cast<u32x4_b*>(dwg + (int64_t)j * K + c * 8));
+                __builtin_nontemporal_store(ou, reinterpret_cast<u32x4_b*>(dwu + (int64_t)j * K + c * 8));
+            }
+        }
+    };
+
+    // the next row's loads are issued before this row is processed (two register sets alternate);
+    // past the wave's last row the prefetch re-reads the current row, so no load sits behind a branch
+    // (a second row in flight measured slower: 50.5 against 48.0 us at K=2560 N=9216)
+    u32x4_b ga[U], ua[U], gb[U], ub[U];
+    uint16_t oa = 0, ob = 0;
+    int j = gw;
+    if (j < N) load_row(j, ga, ua, oa);
+    while (j < N) {
+        const int j1 = j + nwaves;
+        load_row(j1 < N ? j1 : j, gb, ub, ob);
+        process(j, ga, ua, oa);
+        if (j1 >= N) break;
+        const int j2 = j1 + nwaves;
+        load_row(j2 < N ? j2 : j1, ga, ua, oa);
+        process(j1, gb, ub, ob);
+        j = j2;
+    }
+
+    // the waves' dh sums in order 0, 1, ..., WAVES - 1
+    for (int w = 0; w < WAVES; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                const int c = (lane + kWave * u) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float vg = w == 0 ? ag[u][e] : red1[c + e] + ag[u][e];
+                    const float vu = w == 0 ? au[u][e] : red1[K + c + e] + au[u][e];
+                    if (w + 1 < WAVES) {
+                        red1[c + e] = vg;
+                        red1[K + c + e] = vu;
+                    } else {
+                        partial[((int64_t)blockIdx.x * 2 + 0) * K + c + e] = vg;
+                        partial[((int64_t)blockIdx.x * 2 + 1) * K + c + e] = vu;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // dh[m][c] = bf16(fp32(bf16(sum Pg) + bf16(sum Pu))) over the row ranges' partials.  A lane
 // owns 4 consecutive elements (16-byte loads); lane group p sums ranges p, p + 16, p + 32, ... in
 // order, then group 0 adds the 16 group sums in order 0..15.  M * K % 4 == 0 (K % 8 == 0).
@@ -290,12 +432,26 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     if (p.rows_per_range < 1) p.rows_per_range = 1;
     p.nranges = (int)((N + p.rows_per_range - 1) / p.rows_per_range);
     if (p.nranges < 1) p.nranges = 1;
+    // one pass for M = 1 and K <= 64 * 8 * kFusedMaxU: workgroups of kFusedWaves waves, about
+    // fused_waves_per_cu waves per CU, each wave the same number of rows to within one
+    p.fused = M == 1 && K >= 8 && (K / 8 + kWave - 1) / kWave <= kFusedMaxU;
+    int64_t rows_per_wave = 0;
+    if (p.fused) {
+        const int64_t target = (int64_t)kCUsForPlan * fused_waves_per_cu((int)((K / 8 + kWave - 1) / kWave));
+        rows_per_wave = (N + target - 1) / target;
+        const int64_t waves = (N + rows_per_wave - 1) / rows_per_wave;
+        p.fused_grid = (int)((waves + kFusedWaves - 1) / kFusedWaves);
+        p.nranges = p.fused_grid;  // the reduction sums one partial per workgroup
+    }
     p.gu_bytes = ((int64_t)2 * M * N * 2 + 255) / 256 * 256;
     p.partial_bytes = (int64_t)p.nranges * 2 * M * K * 4;
     p.workspace_bytes = p.gu_bytes + p.partial_bytes;
-    // dh: within a wave its rows in order, then 4 waves, then every 16th range, then the 16 group sums
-    p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves +
-                    (p.nranges + kReduceParts - 1) / kReduceParts + kReduceParts;
+    // dh: within a wave its rows in order, then the waves of a workgroup, then every 16th partial,
+    // then the 16 group sums
+    p.accum_depth = p.fused ? (int)(rows_per_wave + kFusedWaves + (p.nranges + kReduceParts - 1) / kReduceParts +
+                                    kReduceParts)
+                            : (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves +
+                                  (p.nranges + kReduceParts - 1) / kReduceParts + kReduceParts;
     return p;
 }
 
@@ -318,6 +474,24 @@ hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, cons
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kBwdThreads), 0, stream, hidden, gate_w, up_w, dgu, dwg, dwu,
                        partial, N, K, p.nslabs, p.rows_per_range);
+    return hipGetLastError();
+}
+
+hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                        const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial, int N, int K,
+                        hipStream_t stream)
+{
+    using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, uint16_t*,
+                        uint16_t*, float*, int, int);
+    static const Fn table[kFusedMaxU] = {
+        fused1_kernel<1, kFusedWaves>, fused1_kernel<2, kFusedWaves>, fused1_kernel<3, kFusedWaves>,
+        fused1_kernel<4, kFusedWaves>, fused1_kernel<5, kFusedWaves>,
+    };
+    const int U = (K / 8 + kWave - 1) / kWave;
+    if (!p.fused || U < 1 || U > kFusedMaxU || (K & 7) != 0 || N < 1 || p.fused_grid < 1) return hipErrorInvalidValue;
+    const size_t lds = (size_t)2 * K * sizeof(float);
+    hipLaunchKernelGGL(table[U - 1], dim3(p.fused_grid), dim3(kFusedWaves * kWave), lds, stream, hidden, gate_w,
+                       up_w, dout, dgu, dwg, dwu, partial, N, K);
     return hipGetLastError();
 }
 

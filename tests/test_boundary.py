@@ -345,8 +345,11 @@ def test_gemm_plans_and_overrides(lib):
 # ---- backward -----------------------------------------------------------------
 
 def test_backward_plan_and_workspace(lib):
-    p = api.backward_plan(1, 9216, 2560)
+    p = api.backward_plan(1, 9216, 2560)   # M = 1, K <= 2560: one pass, then the reduction
+    assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 2
+    p = api.backward_plan(2, 9216, 2560)   # the grouped GEMV, gradients, contraction, reduction
     assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 4 and p["grid"] % 5 == 0
+    assert api.backward_plan(1, 9216, 2568)["launches"] == 4
     assert api.backward_workspace_bytes(1, 9216, 2560) > 2 * 9216 * 2
     assert api.backward_workspace_bytes(0, 9216, 2560) == 0
     assert api.backward_plan(0, 5, 8)["kernel"] == api.KERNEL_ZERO   # weight gradients of an empty batch
