@@ -16,7 +16,7 @@ Prints ONE JSON line.  Other modes:
                        rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE scaling)
   --summarize KIND DIR turn rocprofv3 output in DIR into the text summaries
                        kept under profiles/ (KIND: trace | trace-grid |
-                       counters); host only, no GPU
+                       counters | counter-table); host only, no GPU
 """
 from __future__ import annotations
 
@@ -416,6 +416,29 @@ def summarize_trace_grid(d: str):
     return "\n".join(lines)
 
 
+def summarize_counter_table(d: str):
+    """Mean of each collected counter per (kernel, grid) from rocprofv3 --pmc csv output."""
+    rows = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        if not name.startswith(("glu::", "void glu::")):
+            continue
+        key = (name.split("(")[0].replace("void ", ""), int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0),
+               r["Counter_Name"])
+        # a dispatch may report several rows of one counter (per dimension): sum them per dispatch
+        disp = (r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        acc.setdefault(key, {}).setdefault(disp, 0.0)
+        acc[key][disp] += float(r["Counter_Value"])
+    lines = ["| kernel | grid (threads) | counter | dispatches | mean per dispatch |", "|---|---|---|---|---|"]
+    for (name, grid, cname), per in sorted(acc.items()):
+        vals = list(per.values())
+        lines.append(f"| `{name}` | {grid} | {cname} | {len(vals)} | {sum(vals) / len(vals):.2f} |")
+    return "\n".join(lines)
+
+
 def summarize_counters(d: str, command: str):
     """FETCH_SIZE / WRITE_SIZE per dispatch, scaled by the calibration copy of known size.
 
@@ -473,6 +496,8 @@ def main():
             print(summarize_trace(d))
         elif kind == "trace-grid":
             print(summarize_trace_grid(d))
+        elif kind == "counter-table":
+            print(summarize_counter_table(d))
         else:
             print(json.dumps(summarize_counters(d, args.command), indent=1))
         return
