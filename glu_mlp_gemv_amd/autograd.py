@@ -4,7 +4,7 @@ Mirrors the segKI "Plan B" design (DeepSpeed PR #9057 discussion, "Plan B
 Design"): the Function keeps hidden, gate_w and up_w, reads the weight
 Parameters in place in both directions, and returns gradients for all three,
 so training and generation share one forward and one set of weights.
-Forward: glu_dual_gemv; backward: glu_dual_gemv_backward (M <= 8 rows of
+Forward: glu_dual_gemv; backward: glu_dual_gemv_backward (M <= 64 rows of
 hidden).  Only argument marshalling happens here.
 """
 import torch

@@ -624,10 +624,25 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     st = run_grouped(hidden, K, proj, 2, M, K, stream, nullptr);
     if (st != GLU_OK) return st;
     e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
-    if (e == hipSuccess) {
-        e = glu::contract_launch(bp, (int)M, hidden, gate_w, up_w, gu, dwg, dwu, partial, (int)N, (int)K, s);
+    const uint16_t* dg_all = gu;
+    const uint16_t* du_all = gu + mn;
+    if (M <= glu::kBwdChunkM) {
+        if (e == hipSuccess) {
+            e = glu::contract_launch(bp, (int)M, true, hidden, gate_w, up_w, dg_all, du_all, dwg, dwu, partial, (int)N,
+                                     (int)K, s);
+        }
+        if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
+        return e == hipSuccess ? GLU_OK : fail_launch(e);
     }
-    if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
+    // more rows: dh in chunks of rows of hidden (each chunk streams the weights), then the weight
+    // gradients over all rows in one launch
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += glu::kBwdChunkM) {
+        const int mc = (int)(M - m0 < glu::kBwdChunkM ? M - m0 : glu::kBwdChunkM);
+        e = glu::contract_launch(bp, mc, false, hidden, gate_w, up_w, dg_all + m0 * N, du_all + m0 * N, dwg, dwu,
+                                 partial, (int)N, (int)K, s);
+        if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh + m0 * K, K, mc, (int)K, s);
+    }
+    if (e == hipSuccess) e = glu::dw_launch(bp, (int)M, hidden, dg_all, du_all, dwg, dwu, (int)N, (int)K, s);
     return e == hipSuccess ? GLU_OK : fail_launch(e);
 }
 
@@ -812,7 +827,7 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     const bool run_all = M > 0 && N > 0 && K > 0;
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
-    plan->launches = run_all ? (bp.fused ? 2 : 4) : 0;
+    plan->launches = run_all ? (bp.fused ? 2 : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8)))) : 0;
     plan->grid = run_all ? (bp.fused ? bp.fused_grid : bp.nranges * bp.nslabs) : 0;
     plan->block = 256;
     plan->accum_depth = bp.accum_depth;

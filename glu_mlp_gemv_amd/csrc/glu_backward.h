@@ -5,7 +5,8 @@
 
 namespace glu {
 
-constexpr int kBwdMaxM = 8;
+constexpr int kBwdMaxM = 64;    // rows of hidden per call
+constexpr int kBwdChunkM = 8;   // rows of hidden per contraction launch (dh); dw_kernel takes all
 constexpr int kBwdTargetBlocks = 512;  // contraction workgroups aimed for (2 per CU)
 
 constexpr int kFusedMaxU = 5;        // one-pass kernel: up to 5 16-byte chunks per lane (K <= 2560)
@@ -28,10 +29,14 @@ struct BwdPlan {
 
 BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K);
 hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int M, int N, hipStream_t stream);
-// K % 8 == 0, hidden / gate_w / up_w / dwg / dwu 16-byte aligned, packed rows
-hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
-                           const uint16_t* up_w, const uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial,
-                           int N, int K, hipStream_t stream);
+// K % 8 == 0, hidden / gate_w / up_w / dwg / dwu 16-byte aligned, packed rows.  M <= 8; dw: also
+// the weight gradients (then these M rows are all rows of hidden).  dgm, dum: [M][N].
+hipError_t contract_launch(const BwdPlan& p, int M, bool dw, const uint16_t* hidden, const uint16_t* gate_w,
+                           const uint16_t* up_w, const uint16_t* dgm, const uint16_t* dum, uint16_t* dwg,
+                           uint16_t* dwu, float* partial, int N, int K, hipStream_t stream);
+// weight gradients over all M <= kBwdMaxM rows of hidden
+hipError_t dw_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* dgm, const uint16_t* dum,
+                     uint16_t* dwg, uint16_t* dwu, int N, int K, hipStream_t stream);
 hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                         const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial, int N, int K,
                         hipStream_t stream);

@@ -211,8 +211,9 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * workspace: device memory of at least glu_dual_gemv_backward_workspace()
  * bytes, 256-byte aligned, not overlapping any argument.  On return it
  * begins with dg and du, the bf16 gradients of the gate and up
- * pre-activations ([2][M][N], dense); the rest is scratch.  Limits: M <= 8 (else GLU_ERR_UNSUPPORTED); hidden, gate_w, up_w,
- * dgate_w, dup_w 16-byte aligned and K % 8 == 0 (else GLU_ERR_UNSUPPORTED).
+ * pre-activations ([2][M][N], dense); the rest is scratch.  Limits:
+ * M <= 64 (else GLU_ERR_UNSUPPORTED); hidden, gate_w, up_w, dgate_w, dup_w
+ * 16-byte aligned and K % 8 == 0 (else GLU_ERR_UNSUPPORTED).
  * Empty sums give +0: N == 0 zero-fills dhidden, M == 0 zero-fills both
  * weight gradients; K == 0 has nothing to write.  Validation (NULL arrays,
  * shapes, 2-byte alignment, overlap of an output or the workspace with an
@@ -227,7 +228,7 @@ glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w
 
 /* Workspace bytes glu_dual_gemv_backward needs for (M, N, K), into *bytes
  * (0 when an extent is zero).  Host only.  GLU_ERR_BAD_SHAPE or
- * GLU_ERR_UNSUPPORTED (M > 8) as the call would return. */
+ * GLU_ERR_UNSUPPORTED (M > 64) as the call would return. */
 glu_status glu_dual_gemv_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 
 /* The backward's launch for (M, N, K), host only: kernel GLU_KERNEL_BACKWARD,

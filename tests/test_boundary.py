@@ -356,7 +356,7 @@ def test_backward_plan_and_workspace(lib):
     assert api.backward_plan(3, 0, 8)["kernel"] == api.KERNEL_ZERO   # hidden's gradient of no outputs
     assert api.backward_plan(3, 5, 0)["kernel"] == api.KERNEL_NONE
     with pytest.raises(api.GluError):
-        api.backward_plan(9, 10, 64)          # M > 8
+        api.backward_plan(65, 10, 64)         # M > 64
     with pytest.raises(api.GluError):
         api.backward_workspace_bytes(-1, 10, 64)
     b = ctypes.c_int64(0)
@@ -407,7 +407,7 @@ def test_backward_validation_before_any_hip_call(lib, change, status):
 
 def test_backward_shape_limits(lib):
     p, ws = _bwd_ptrs(2, 64, 128)
-    assert api.dual_gemv_backward_raw(*p[:7], 9, 64, 128, p[7], ws) == UNSUP      # M > 8
+    assert api.dual_gemv_backward_raw(*p[:7], 65, 64, 128, p[7], ws) == UNSUP     # M > 64
     assert api.dual_gemv_backward_raw(*p[:7], 2, 64, 100, p[7], ws) == UNSUP      # K % 8 != 0
     assert api.dual_gemv_backward_raw(*p[:7], -1, 64, 128, p[7], ws) == SHAPE
     assert api.dual_gemv_backward_raw(*p[:7], 2, 1 << 40, 1 << 40, p[7], ws) == SHAPE

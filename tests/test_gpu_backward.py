@@ -82,7 +82,9 @@ def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
 
 
 CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2048), (5, 1, 520),
-         (8, 513, 4096), (8, 12288, 4096), (6, 3000, 1024), (7, 64, 40000)]
+         (8, 513, 4096), (8, 12288, 4096), (6, 3000, 1024), (7, 64, 40000),
+         # more than 8 rows of hidden: dh in chunks of 8, the weight gradients over all rows at once
+         (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8)]
 
 
 @pytest.mark.parametrize("M,N,K", CASES)
