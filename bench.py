@@ -203,7 +203,7 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         del pool
         torch.cuda.empty_cache()
     # backward: gradients of hidden and both weights (reads Wg, Wu once more, writes dWg, dWu)
-    for (K, N), Ms in ((((2560, 9216), (1, 4)), ((4096, 12288), (1, 8))) if want("backward") else ()):
+    for (K, N), Ms in ((((2560, 9216), (1, 4, 16, 64)), ((4096, 12288), (1, 8))) if want("backward") else ()):
         per = 4 * N * K * 2  # weights and their gradients per set
         sets = max(4, -(-1_400_000_000 // per))
         pool = [(*inputs.weights(N, K, 600 + i, device=dev),
