@@ -614,8 +614,11 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < bp.workspace_bytes) return GLU_ERR_WORKSPACE;
     uint16_t* gu = static_cast<uint16_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + bp.gu_bytes);
-    if (bp.fused) {
-        e = glu::fused1_launch(bp, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K, s);
+    if (bp.path == glu::kPathFused1 || bp.path == glu::kPathSplitK) {
+        e = bp.path == glu::kPathFused1
+                ? glu::fused1_launch(bp, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K, s)
+                : glu::splitk_launch(bp, (int)M, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K,
+                                     s);
         if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
         return e == hipSuccess ? GLU_OK : fail_launch(e);
     }
@@ -827,9 +830,14 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     const bool run_all = M > 0 && N > 0 && K > 0;
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
-    plan->launches = run_all ? (bp.fused ? 2 : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8)))) : 0;
-    plan->grid = run_all ? (bp.fused ? bp.fused_grid : bp.nranges * bp.nslabs) : 0;
-    plan->block = 256;
+    plan->launches = run_all ? (bp.path != glu::kPathChunks ? 2
+                                                            : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8))))
+                             : 0;
+    plan->grid = run_all ? (bp.path == glu::kPathFused1   ? bp.fused_grid
+                            : bp.path == glu::kPathSplitK ? bp.split_grid
+                                                          : bp.nranges * bp.nslabs)
+                         : 0;
+    plan->block = bp.path == glu::kPathSplitK ? bp.split_waves * glu::kWave : 256;
     plan->accum_depth = bp.accum_depth;
     return GLU_OK;
 }

@@ -15,9 +15,30 @@ constexpr int kFusedWaves = 4;       // waves per workgroup of the one-pass kern
 constexpr int fused_waves_per_cu(int U) { return U >= 5 ? 4 : 8; }
 constexpr int kCUsForPlan = 256;     // MI355X compute units
 
+constexpr int kSplitMaxWaves = 8;     // K-split kernel: waves per workgroup at most (256 VGPRs a lane)
+constexpr int kSplitMaxM = 4;         // rows of hidden at most (beyond, the dot products' butterflies
+                                      // and the dh accumulators make the four-launch path faster)
+constexpr int kSplitMaxM2 = 3;        // rows of hidden at most with two chunks per lane
+constexpr int kSplitMinK = 2568;      // at K <= 2560 a workgroup of at most 5 waves per CU hides too
+                                      // little latency: M = 1 takes fused1_kernel, M >= 2 the four launches
+constexpr int kSplitMaxThreads = kSplitMaxWaves * 64;
+// weight rows per batch of the K-split kernel (their loads are issued one batch ahead): as many as
+// the registers beside M rows of dh accumulators allow
+constexpr int split_rows(int M, int U) { return U == 1 ? (M <= 2 ? 4 : 2) : (M <= 2 ? 2 : 1); }
+
+// which kernels a backward call runs
+constexpr int kPathChunks = 0;   // grouped GEMV, gradient step, contraction (in chunks of 8 rows), reduction
+constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
+constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
+
 struct BwdPlan {
+    int path;                // kPathChunks, kPathFused1 or kPathSplitK
     bool fused;              // M == 1, K <= 2560: the one-pass kernel
     int fused_grid;          // its workgroups (each leaves one partial of dh)
+    int split_u;             // K-split kernel: chunks per lane (1 or 2)
+    int split_waves;         // waves per workgroup
+    int split_rpb;           // weight rows per workgroup
+    int split_grid;          // workgroups (each leaves one partial of dh)
     int nslabs;              // 512-column slabs of K
     int nranges;             // row ranges of N (the one-pass kernel: its workgroups)
     int rows_per_range;
@@ -40,6 +61,9 @@ hipError_t dw_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint
 hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                         const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial, int N, int K,
                         hipStream_t stream);
+hipError_t splitk_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                         const uint16_t* up_w, const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu,
+                         float* partial, int N, int K, hipStream_t stream);
 hipError_t dh_reduce_launch(const BwdPlan& p, const float* partial, uint16_t* dh, int64_t ldh_out, int M, int K,
                             hipStream_t stream);
 

@@ -11,6 +11,9 @@
 // M = 1 with K <= 2560: one pass (fused1_kernel, below) reads each row of Wg
 // and Wu once, forms G and U, dg and du, writes the row of dWg and dWu and
 // accumulates dh, then dh_reduce_kernel adds the workgroups' partials.
+// M <= 4 with 2560 < K <= 4096 (K <= 8192 for M <= 3): also one pass
+// (splitk_kernel), K split over the lanes of a workgroup so that each lane
+// keeps its columns of dh for all M rows in registers, then dh_reduce_kernel.
 // Otherwise four launches (after the grouped GEMV has written
 // g = bf16(h Wg^T) and u = bf16(h Wu^T) into the workspace):
 //  * act_grad_kernel: dg and du from g, u and dout, elementwise, in place;
@@ -24,8 +27,11 @@
 //    groups over interleaved ranges, then the groups in order), rounds each
 //    contribution and their fp32 sum to bf16.
 // No atomics: results are bitwise reproducible.
+#include <algorithm>
+
 #include "glu_backward.h"
 #include "glu_device.h"
+#include "glu_launch.h"
 
 namespace glu {
 
@@ -272,6 +278,226 @@ dw_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ dgm,
     }
 }
 
+// One pass for M <= 4 with K split over the lanes of a workgroup: W waves (W = blockDim / 64),
+// lane t owns 16-byte chunks t + 64 W u (u < U) of every row.  Workgroup b owns the rows
+// [b * rpb, min(N, (b + 1) * rpb)), taken kSplitRows at a time with the next rows' loads issued
+// first.  Per batch: each wave's partial dot products (wave butterfly) go to LDS; lanes
+// t < rows * M add the W wave sums in order, form (dg, du) for one (row, m) each and share them
+// through LDS (and the workspace head); then every lane writes its columns of the rows of dWg and
+// dWu and accumulates its columns of dh, which it writes as the workgroup's partial at the end.
+template <int M, int U, bool HLDS>
+__global__ void __launch_bounds__(kSplitMaxThreads)
+splitk_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+              const uint16_t* __restrict__ up_w, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dgu,
+              uint16_t* __restrict__ dwg, uint16_t* __restrict__ dwu, float* __restrict__ partial, int N, int K,
+              int rpb)
+{
+    constexpr int R = split_rows(M, U);
+    __shared__ float wsum[kSplitMaxWaves][R][M][2];
+    __shared__ float gsh[R][M][2];
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int W = blockDim.x / kWave;
+    const int nchunks = K >> 3;
+    const int j_begin = blockIdx.x * rpb;
+    const int j_end = min(j_begin + rpb, N);
+    const int64_t MN = (int64_t)M * N;
+
+    // hidden: this lane's chunks in registers, or (HLDS) in LDS at [m][chunk], where only the lane
+    // that owns a chunk writes it
+    extern __shared__ u32x4_b hsh[];
+    int cidx[U];
+    bool ok[U];
+    u32x4_b hw[HLDS ? 1 : M][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = t + kWave * W * u;
+        ok[u] = c < nchunks;
+        cidx[u] = ok[u] ? c : nchunks - 1;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const u32x4_b v = ok[u] ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + (int64_t)c * 8)
+                                    : u32x4_b{0u, 0u, 0u, 0u};
+            if constexpr (HLDS) {
+                if (ok[u]) hsh[m * nchunks + c] = v;
+            } else {
+                hw[m][u] = v;
+            }
+        }
+    }
+    if constexpr (HLDS) __syncthreads();  // lanes past K read the last chunk, written by another wave
+    auto H = [&](int m, int u) __attribute__((always_inline)) -> u32x4_b {
+        if constexpr (HLDS) {
+            return hsh[m * nchunks + cidx[u]];
+        } else {
+            return hw[m][u];
+        }
+    };
+    float ag[M][U][8], au[M][U][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ag[m][u][e] = 0.0f;
+                au[m][u][e] = 0.0f;
+            }
+        }
+    }
+
+    // a batch's loads (rows past the range re-read the range's last row; they are never used)
+    auto load = [&](int j0, u32x4_b (&wg)[R][U], u32x4_b (&wu)[R][U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t j = min(j0 + r, j_end - 1);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                wg[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(gate_w + j * K + cidx[u] * 8));
+                wu[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(up_w + j * K + cidx[u] * 8));
+            }
+        }
+    };
+    auto batch = [&](int j0, u32x4_b (&wg)[R][U], u32x4_b (&wu)[R][U]) __attribute__((always_inline)) {
+        // partial dots of this lane's chunks, summed over the wave
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) {
+                    wg[r][u] = u32x4_b{0u, 0u, 0u, 0u};
+                    wu[r][u] = u32x4_b{0u, 0u, 0u, 0u};
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float pg = 0.0f, pu = 0.0f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const u32x4_b hv = H(m, u);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        pg = __builtin_fmaf(bf16lo(hv[q]), bf16lo(wg[r][u][q]), pg);
+                        pg = __builtin_fmaf(bf16hi(hv[q]), bf16hi(wg[r][u][q]), pg);
+                        pu = __builtin_fmaf(bf16lo(hv[q]), bf16lo(wu[r][u][q]), pu);
+                        pu = __builtin_fmaf(bf16hi(hv[q]), bf16hi(wu[r][u][q]), pu);
+                    }
+                }
+                pg = wave_sum(pg);
+                pu = wave_sum(pu);
+                if (lane == 0) {
+                    wsum[wave][r][m][0] = pg;
+                    wsum[wave][r][m][1] = pu;
+                }
+            }
+        }
+        __syncthreads();
+        // (row, m) pairs: the wave sums in order, then the gradient step
+        if (t < R * M) {
+            const int r = t / M, m = t - (t / M) * M;
+            const int j = j0 + r;
+            float G = 0.0f, Uv = 0.0f;
+            for (int w = 0; w < W; ++w) {
+                G += wsum[w][r][m][0];
+                Uv += wsum[w][r][m][1];
+            }
+            uint16_t dgb = 0, dub = 0;
+            if (j < j_end) {
+                act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)),
+                         bf16_to_f32(dout[(int64_t)m * N + j]), &dgb, &dub);
+                dgu[(int64_t)m * N + j] = dgb;
+                dgu[MN + (int64_t)m * N + j] = dub;
+            }
+            gsh[r][m][0] = bf16_to_f32(dgb);
+            gsh[r][m][1] = bf16_to_f32(dub);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int j = j0 + r;
+            if (j >= j_end) break;  // uniform over the workgroup
+            // (dg, du) are the same in every lane: scalar registers
+            float dg[M], du[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                dg[m] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gsh[r][m][0])));
+                du[m] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gsh[r][m][1])));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float wgf[8], wuf[8];
+                float sg[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};  // +0: sums of zeros are +0
+                float su[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    wgf[2 * q] = bf16lo(wg[r][u][q]);
+                    wgf[2 * q + 1] = bf16hi(wg[r][u][q]);
+                    wuf[2 * q] = bf16lo(wu[r][u][q]);
+                    wuf[2 * q + 1] = bf16hi(wu[r][u][q]);
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const u32x4_b hv = H(m, u);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float h0 = bf16lo(hv[q]), h1 = bf16hi(hv[q]);
+                        // the weights' gradients add the M rows in order
+                        sg[2 * q] = __builtin_fmaf(dg[m], h0, sg[2 * q]);
+                        sg[2 * q + 1] = __builtin_fmaf(dg[m], h1, sg[2 * q + 1]);
+                        su[2 * q] = __builtin_fmaf(du[m], h0, su[2 * q]);
+                        su[2 * q + 1] = __builtin_fmaf(du[m], h1, su[2 * q + 1]);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ag[m][u][e] = __builtin_fmaf(dg[m], wgf[e], ag[m][u][e]);
+                        au[m][u][e] = __builtin_fmaf(du[m], wuf[e], au[m][u][e]);
+                    }
+                }
+                u32x4_b og, ou;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    og[q] = (uint32_t)f32_to_bf16_rne(sg[2 * q]) | ((uint32_t)f32_to_bf16_rne(sg[2 * q + 1]) << 16);
+                    ou[q] = (uint32_t)f32_to_bf16_rne(su[2 * q]) | ((uint32_t)f32_to_bf16_rne(su[2 * q + 1]) << 16);
+                }
+                if (ok[u]) {
+                    __builtin_nontemporal_store(og, reinterpret_cast<u32x4_b*>(dwg + (int64_t)j * K + cidx[u] * 8));
+                    __builtin_nontemporal_store(ou, reinterpret_cast<u32x4_b*>(dwu + (int64_t)j * K + cidx[u] * 8));
+                }
+            }
+        }
+    };
+
+    u32x4_b ga[R][U], ua[R][U], gb[R][U], ub[R][U];
+    int j0 = j_begin;
+    if (j0 < j_end) load(j0, ga, ua);
+    while (j0 < j_end) {
+        const int j1 = j0 + R;
+        load(j1 < j_end ? j1 : j0, gb, ub);
+        batch(j0, ga, ua);
+        if (j1 >= j_end) break;
+        const int j2 = j1 + R;
+        load(j2 < j_end ? j2 : j1, ga, ua);
+        batch(j1, gb, ub);
+        j0 = j2;
+    }
+    // this lane's columns of the workgroup's dh partial
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float* pg = partial + (((int64_t)blockIdx.x * 2 + 0) * M + m) * K + (int64_t)cidx[u] * 8;
+            float* pu = partial + (((int64_t)blockIdx.x * 2 + 1) * M + m) * K + (int64_t)cidx[u] * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pg[e] = ag[m][u][e];
+                pu[e] = au[m][u][e];
+            }
+        }
+    }
+}
+
 // One pass for M = 1 (K <= 64 * 8 * U): wave w owns rows w, w + W, ... (W waves in the grid).
 // Lane l holds 16-byte chunks l, l + 64, ... of its row of Wg and Wu and of hidden.  Per row:
 // G and U (fp32 fma per lane, wave butterfly), dg and du (act_grad, all lanes; lane 0 stores them
@@ -496,10 +722,22 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     // one pass for M = 1 and K <= 64 * 8 * kFusedMaxU: workgroups of kFusedWaves waves, about
     // fused_waves_per_cu waves per CU, each wave the same number of rows to within one
     p.fused = M == 1 && K >= 8 && (K / 8 + kWave - 1) / kWave <= kFusedMaxU;
+    p.path = p.fused ? kPathFused1 : kPathChunks;
     int64_t rows_per_wave = 0;
+    // split over K: K / 8 chunks over at most 8 waves of 1 or 2 chunks per lane
+    const int64_t nch = K / 8;
+    const int64_t split_cap = (int64_t)kSplitMaxWaves * kWave * (M <= kSplitMaxM2 ? 2 : 1);
+    if (!p.fused && M >= 1 && M <= kSplitMaxM && K >= kSplitMinK && nch <= split_cap) {
+        p.path = kPathSplitK;
+        p.split_u = nch <= (int64_t)kSplitMaxWaves * kWave ? 1 : 2;
+        p.split_waves = (int)((nch + (int64_t)kWave * p.split_u - 1) / ((int64_t)kWave * p.split_u));
+        p.split_rpb = N > 0 ? (int)((N + kCUsForPlan - 1) / kCUsForPlan) : 1;  // about one workgroup per CU
+        p.split_grid = (int)((N + p.split_rpb - 1) / p.split_rpb);
+        p.nranges = p.split_grid;  // one partial of dh per workgroup
+    }
     if (p.fused) {
         const int64_t target = (int64_t)kCUsForPlan * fused_waves_per_cu((int)((K / 8 + kWave - 1) / kWave));
-        rows_per_wave = (N + target - 1) / target;
+        rows_per_wave = N > 0 ? (N + target - 1) / target : 1;
         const int64_t waves = (N + rows_per_wave - 1) / rows_per_wave;
         p.fused_grid = (int)((waves + kFusedWaves - 1) / kFusedWaves);
         p.nranges = p.fused_grid;  // the reduction sums one partial per workgroup
@@ -509,10 +747,17 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     p.workspace_bytes = p.gu_bytes + p.partial_bytes;
     // dh: within a wave its rows in order, then the waves of a workgroup, then every 16th partial,
     // then the 16 group sums
-    p.accum_depth = p.fused ? (int)(rows_per_wave + kFusedWaves + (p.nranges + kReduceParts - 1) / kReduceParts +
-                                    kReduceParts)
-                            : (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves +
-                                  (p.nranges + kReduceParts - 1) / kReduceParts + kReduceParts;
+    const int reduce_depth = (p.nranges + kReduceParts - 1) / kReduceParts + kReduceParts;
+    // the one-pass kernels also form G and U: a lane's 8 U products in order, the wave's
+    // butterfly, then (K split) the waves of the workgroup in order
+    if (p.path == kPathFused1) {
+        const int u = (int)((K / 8 + kWave - 1) / kWave);
+        p.accum_depth = std::max((int)(rows_per_wave + kFusedWaves) + reduce_depth, 8 * u + 6);
+    } else if (p.path == kPathSplitK) {
+        p.accum_depth = std::max(p.split_rpb + reduce_depth, 8 * p.split_u + 6 + p.split_waves);
+    } else {
+        p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves + reduce_depth;
+    }
     return p;
 }
 
@@ -565,6 +810,38 @@ hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_
     const size_t lds = (size_t)2 * K * sizeof(float);
     hipLaunchKernelGGL(table[U - 1], dim3(p.fused_grid), dim3(kFusedWaves * kWave), lds, stream, hidden, gate_w,
                        up_w, dout, dgu, dwg, dwu, partial, N, K);
+    return hipGetLastError();
+}
+
+hipError_t splitk_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                         const uint16_t* up_w, const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu,
+                         float* partial, int N, int K, hipStream_t stream)
+{
+    using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, uint16_t*,
+                        uint16_t*, float*, int, int, int);
+    // hidden in LDS where M U chunks would not fit beside the accumulators
+    static const Fn table[2][kSplitMaxM] = {
+        {splitk_kernel<1, 1, false>, splitk_kernel<2, 1, false>, splitk_kernel<3, 1, false>,
+         splitk_kernel<4, 1, false>},
+        {splitk_kernel<1, 2, false>, splitk_kernel<2, 2, true>, splitk_kernel<3, 2, true>, nullptr},
+    };
+    if (p.path != kPathSplitK || M < 1 || M > kSplitMaxM || p.split_u < 1 || p.split_u > 2 ||
+        (p.split_u == 2 && M > kSplitMaxM2) || p.split_waves < 1 ||
+        p.split_waves > kSplitMaxWaves || (int64_t)p.split_waves * kWave * p.split_u * 8 < K || (K & 7) != 0 ||
+        p.split_grid < 1 || p.split_rpb < 1) {
+        return hipErrorInvalidValue;
+    }
+    const Fn fn = table[p.split_u - 1][M - 1];
+    const bool hlds = p.split_u == 2 && M >= 2;
+    const size_t lds = hlds ? (size_t)M * K * 2 : 0;
+    if (lds > (size_t)kLdsMax - 4096) return hipErrorInvalidValue;
+    if (lds > 48 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(p.split_grid), dim3(p.split_waves * kWave), lds, stream, hidden, gate_w, up_w, dout,
+                       dgu, dwg, dwu, partial, N, K, p.split_rpb);
     return hipGetLastError();
 }
 

@@ -217,9 +217,12 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * Empty sums give +0: N == 0 zero-fills dhidden, M == 0 zero-fills both
  * weight gradients; K == 0 has nothing to write.  Validation (NULL arrays,
  * shapes, 2-byte alignment, overlap of an output or the workspace with an
- * input or another output, workspace) happens before any HIP call.  Four
- * launches on stream (the grouped GEMV for g and u, then the gradient
- * kernels), asynchronous, deterministic, allocating nothing.
+ * input or another output, workspace) happens before any HIP call.  On
+ * stream, asynchronous, deterministic, allocating nothing: for M = 1 with
+ * K <= 8192, and for M <= 4 with 2560 < K <= 4096 (K <= 8192 when M <= 3),
+ * two launches, a pass that reads each
+ * weight row once and the reduction of dhidden's partial sums; otherwise
+ * the grouped GEMV for g and u, then the gradient kernels.
  */
 glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                                   const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
@@ -231,9 +234,11 @@ glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w
  * GLU_ERR_UNSUPPORTED (M > 64) as the call would return. */
 glu_status glu_dual_gemv_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 
-/* The backward's launch for (M, N, K), host only: kernel GLU_KERNEL_BACKWARD,
- * grid of the contraction kernel, accum_depth = longest fp32 addition chain
- * behind one of dhidden's two contributions. */
+/* The backward's launches for (M, N, K), host only: kernel
+ * GLU_KERNEL_BACKWARD, launches per call, grid and block of the kernel that
+ * reads the weights for the gradients, accum_depth = longest fp32 addition
+ * chain behind one of dhidden's two contributions or, where that kernel
+ * also forms them, behind the gate and up pre-activations. */
 glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan* plan);
 
 #ifdef __cplusplus

@@ -347,9 +347,18 @@ def test_gemm_plans_and_overrides(lib):
 def test_backward_plan_and_workspace(lib):
     p = api.backward_plan(1, 9216, 2560)   # M = 1, K <= 2560: one pass, then the reduction
     assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 2
+    p = api.backward_plan(2, 12288, 4096)  # M <= 4: one pass with K split over 8 waves, the reduction
+    assert p["launches"] == 2 and p["block"] == 512 and p["grid"] == 256
+    p = api.backward_plan(1, 9216, 2568)
+    assert p["launches"] == 2 and p["block"] == 384
+    p = api.backward_plan(3, 100, 8192)    # two chunks per lane up to M = 3
+    assert p["launches"] == 2 and p["block"] == 512 and p["grid"] == 100
     p = api.backward_plan(2, 9216, 2560)   # the grouped GEMV, gradients, contraction, reduction
     assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 4 and p["grid"] % 5 == 0
-    assert api.backward_plan(1, 9216, 2568)["launches"] == 4
+    assert api.backward_plan(5, 9216, 4096)["launches"] == 4
+    assert api.backward_plan(4, 9216, 4104)["launches"] == 4
+    assert api.backward_plan(9, 9216, 2560)["launches"] == 3 + 2 * 2
+    assert api.backward_plan(1, 0, 8)["kernel"] == api.KERNEL_ZERO
     assert api.backward_workspace_bytes(1, 9216, 2560) > 2 * 9216 * 2
     assert api.backward_workspace_bytes(0, 9216, 2560) == 0
     assert api.backward_plan(0, 5, 8)["kernel"] == api.KERNEL_ZERO   # weight gradients of an empty batch

@@ -54,7 +54,9 @@ def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
     diff = np.argwhere((dg_gpu != ref.dg) | (du_gpu != ref.du))
     if diff.size:
         fwd = oracle.dual_gemv(hb, gb, ub, with_pre=True)
-        depth = api.grouped_plan(M, K, 2 * N, True, None, N % 4 == 0)["accum_depth"]
+        # G and U come from the grouped GEMV or from the backward's one-pass kernel
+        depth = max(api.grouped_plan(M, K, 2 * N, True, None, N % 4 == 0)["accum_depth"],
+                    api.backward_plan(M, N, K)["accum_depth"])
         for m, j in diff:
             g_set = check.admissible_bf16_set(fwd.gate_pre[m, j], fwd.gate_abs[m, j], depth, K)
             u_set = check.admissible_bf16_set(fwd.up_pre[m, j], fwd.up_abs[m, j], depth, K)
@@ -83,6 +85,9 @@ def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
 
 CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2048), (5, 1, 520),
          (8, 513, 4096), (8, 12288, 4096), (6, 3000, 1024), (7, 64, 40000),
+         # one pass with K split over a workgroup: ragged last wave, two chunks a lane, hidden in LDS
+         (4, 9216, 3072), (1, 12288, 4096), (2, 700, 2568), (3, 300, 8192), (2, 99, 6152), (3, 255, 4096),
+         (2, 257, 2600), (1, 3, 4104), (4, 1, 2576), (4, 4104, 4096), (1, 513, 8192),
          # more than 8 rows of hidden: dh in chunks of 8, the weight gradients over all rows at once
          (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8)]
 
