@@ -133,10 +133,11 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
         c.hidden = glu::kHiddenL2;
     }
     // 8 weight rows per wave halve the MFMAs, operand reads and hidden-slice
-    // traffic per weight byte, which pays once the slices carry more than 8
-    // rows of hidden; below that 4 rows stream the weights faster
+    // traffic per weight byte, which pays once the slices carry more than 16
+    // rows of hidden; up to 16 rows 4 rows per wave stream the weights faster
+    // (K=5120 N=17408: 62.7 against 64.9 us at M = 16, 71.8 against 81.6 at 32)
     const bool seg8 = seg_req == 0 || seg_req == 4 || seg_req == 8;  // stage sizes built for 8 rows
-    const int rows_dflt = (c.hidden == glu::kHiddenSlices && m_pl > 8 && seg8) ? 8 : 4;
+    const int rows_dflt = (c.hidden == glu::kHiddenSlices && m_pl > 16 && seg8) ? 8 : 4;
     c.rows = (t && t->rows_per_wave) ? t->rows_per_wave : rows_dflt;
     if (c.rows != 4 && !(c.rows == 8 && c.hidden == glu::kHiddenSlices)) return GLU_ERR_UNSUPPORTED;
     // segments of 128 K-elements at 4 rows per wave, of 64 at 8
