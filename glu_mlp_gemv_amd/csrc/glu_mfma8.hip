@@ -1,5 +1,6 @@
-// MFMA kernel for the dual-weight GLU projection at 8 < M <= 32 when hidden
-// does not fit in LDS: groups of 8 weight rows per wave.
+// MFMA kernel for the dual-weight GLU projection when hidden does not fit in
+// LDS: groups of 8 weight rows per wave (the planner's default at 16 < M <= 32;
+// any M <= 32 on request).
 //
 // Same block-diagonal use of v_mfma_f32_16x16x32_bf16 as the 4-row kernel,
 // with 8 rows x 2 blocks instead of 4 rows x 4 blocks:
