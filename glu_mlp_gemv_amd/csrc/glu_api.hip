@@ -614,7 +614,7 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     if (!fast) return GLU_ERR_UNSUPPORTED;
     if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < bp.workspace_bytes) return GLU_ERR_WORKSPACE;
     uint16_t* gu = static_cast<uint16_t*>(ws);
-    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + bp.gu_bytes);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + bp.off_partial);
     if (bp.path == glu::kPathFused1 || bp.path == glu::kPathSplitK) {
         e = bp.path == glu::kPathFused1
                 ? glu::fused1_launch(bp, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K, s)
@@ -630,6 +630,26 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
     const uint16_t* dg_all = gu;
     const uint16_t* du_all = gu + mn;
+    if (bp.path == glu::kPathMfma) {
+        // zero-padded operand copies, then dh's partial sums over ranges of weight rows, their
+        // reduction, and both weight gradients
+        char* w = static_cast<char*>(ws);
+        uint16_t* g2 = reinterpret_cast<uint16_t*>(w + bp.off_g2);
+        uint16_t* u2 = g2 + (int64_t)bp.mp16 * bp.np32;
+        uint16_t* gT = reinterpret_cast<uint16_t*>(w + bp.off_gT);
+        uint16_t* uT = gT + N * bp.mp32;
+        uint16_t* hT = reinterpret_cast<uint16_t*>(w + bp.off_hT);
+        const int m = (int)M, n = (int)N, k = (int)K;
+        if (e == hipSuccess) e = glu::repack_launch(dg_all, N, g2, m, n, bp.mp16, bp.np32, false, s);
+        if (e == hipSuccess) e = glu::repack_launch(du_all, N, u2, m, n, bp.mp16, bp.np32, false, s);
+        if (e == hipSuccess) e = glu::repack_launch(dg_all, N, gT, m, n, bp.mp32, 0, true, s);
+        if (e == hipSuccess) e = glu::repack_launch(du_all, N, uT, m, n, bp.mp32, 0, true, s);
+        if (e == hipSuccess) e = glu::repack_launch(hidden, K, hT, m, k, bp.mp32, 0, true, s);
+        if (e == hipSuccess) e = glu::dh_mfma_launch(bp, m, gate_w, up_w, g2, u2, partial, n, k, s);
+        if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, m, k, s);
+        if (e == hipSuccess) e = glu::dw_mfma_launch(bp, hT, gT, uT, dwg, dwu, n, k, s);
+        return e == hipSuccess ? GLU_OK : fail_launch(e);
+    }
     if (M <= glu::kBwdChunkM) {
         if (e == hipSuccess) {
             e = glu::contract_launch(bp, (int)M, true, hidden, gate_w, up_w, dg_all, du_all, dwg, dwu, partial, (int)N,
@@ -831,11 +851,14 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     const bool run_all = M > 0 && N > 0 && K > 0;
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
-    plan->launches = run_all ? (bp.path != glu::kPathChunks ? 2
-                                                            : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8))))
+    // the grouped GEMV counts as one launch
+    plan->launches = run_all ? (bp.path == glu::kPathMfma     ? 10
+                                : bp.path != glu::kPathChunks ? 2
+                                                              : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8))))
                              : 0;
     plan->grid = run_all ? (bp.path == glu::kPathFused1   ? bp.fused_grid
                             : bp.path == glu::kPathSplitK ? bp.split_grid
+                            : bp.path == glu::kPathMfma   ? (int)((K + 63) / 64) * bp.dh_splits
                                                           : bp.nranges * bp.nslabs)
                          : 0;
     plan->block = bp.path == glu::kPathSplitK ? bp.split_waves * glu::kWave : 256;

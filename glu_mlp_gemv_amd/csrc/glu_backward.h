@@ -30,6 +30,9 @@ constexpr int split_rows(int M, int U) { return U == 1 ? (M <= 2 ? 4 : 2) : (M <
 constexpr int kPathChunks = 0;   // grouped GEMV, gradient step, contraction (in chunks of 8 rows), reduction
 constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
 constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
+constexpr int kPathMfma = 3;     // 8 < M <= 64: grouped GEMV, gradient step, repacking, dh_mfma_kernel,
+                                 // reduction, dw_mfma_kernel
+constexpr int kBwdMfmaMinM = 9;  // rows of hidden from which the contractions run on MFMA
 
 struct BwdPlan {
     int path;                // kPathChunks, kPathFused1 or kPathSplitK
@@ -39,6 +42,11 @@ struct BwdPlan {
     int split_waves;         // waves per workgroup
     int split_rpb;           // weight rows per workgroup
     int split_grid;          // workgroups (each leaves one partial of dh)
+    int mp16, mp32;          // MFMA path: M rounded up to 16 (dh's B operand) and to 32 (dW's contraction)
+    int np32;                // N rounded up to 32 (the columns of dg2, du2)
+    int dh_splits, dh_jr;    // ranges of weight rows (jr rows each, a multiple of 32) = dh's partials
+    int dh_steps;            // 32-row steps of the longest range
+    int64_t off_g2, off_gT, off_hT, off_partial;  // workspace offsets of dg2/du2, dgT/duT, hT, the partials
     int nslabs;              // 512-column slabs of K
     int nranges;             // row ranges of N (the one-pass kernel: its workgroups)
     int rows_per_range;
@@ -64,6 +72,12 @@ hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_
 hipError_t splitk_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
                          const uint16_t* up_w, const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu,
                          float* partial, int N, int K, hipStream_t stream);
+hipError_t repack_launch(const uint16_t* src, int64_t ld, uint16_t* dst, int R, int C, int Rp, int Cp, bool transpose,
+                         hipStream_t stream);
+hipError_t dw_mfma_launch(const BwdPlan& p, const uint16_t* hT, const uint16_t* dgT, const uint16_t* duT,
+                          uint16_t* dwg, uint16_t* dwu, int N, int K, hipStream_t stream);
+hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* g2,
+                          const uint16_t* u2, float* partial, int N, int K, hipStream_t stream);
 hipError_t dh_reduce_launch(const BwdPlan& p, const float* partial, uint16_t* dh, int64_t ldh_out, int M, int K,
                             hipStream_t stream);
 

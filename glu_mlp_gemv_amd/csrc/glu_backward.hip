@@ -742,9 +742,34 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.fused_grid = (int)((waves + kFusedWaves - 1) / kFusedWaves);
         p.nranges = p.fused_grid;  // the reduction sums one partial per workgroup
     }
-    p.gu_bytes = ((int64_t)2 * M * N * 2 + 255) / 256 * 256;
-    p.partial_bytes = (int64_t)p.nranges * 2 * (M < kBwdChunkM ? M : kBwdChunkM) * K * 4;  // one chunk of rows
-    p.workspace_bytes = p.gu_bytes + p.partial_bytes;
+    auto pad256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    p.gu_bytes = pad256((int64_t)2 * M * N * 2);
+    int64_t mfma_bytes = 0;  // the MFMA path's operand copies
+    if (M >= kBwdMfmaMinM && M <= kBwdMaxM && N > 0 && K >= 8) {
+        p.path = kPathMfma;
+        p.mp16 = (int)((M + 15) / 16 * 16);
+        p.mp32 = (int)((M + 31) / 32 * 32);
+        p.np32 = (int)((N + 31) / 32 * 32);
+        // about 512 workgroups of 64 columns x one range of rows, ranges a multiple of 32 rows
+        const int64_t ktiles = (K + 63) / 64;
+        const int64_t steps_all = p.np32 / 32;
+        int64_t splits = (kBwdTargetBlocks + ktiles - 1) / ktiles;
+        splits = splits < 1 ? 1 : (splits > steps_all ? steps_all : splits);
+        const int64_t steps = (steps_all + splits - 1) / splits;
+        p.dh_jr = (int)(steps * 32);
+        p.dh_splits = (int)((N + p.dh_jr - 1) / p.dh_jr);
+        p.dh_steps = (int)steps;
+        p.nranges = p.dh_splits;
+        p.off_g2 = p.gu_bytes;
+        p.off_gT = p.off_g2 + pad256((int64_t)2 * p.mp16 * p.np32 * 2);
+        p.off_hT = p.off_gT + pad256((int64_t)2 * N * p.mp32 * 2);
+        p.off_partial = p.off_hT + pad256((int64_t)K * p.mp32 * 2);
+        mfma_bytes = p.off_partial - p.gu_bytes;
+    } else {
+        p.off_partial = p.gu_bytes;
+    }
+    p.partial_bytes = (int64_t)p.nranges * 2 * (p.path == kPathMfma ? M : (M < kBwdChunkM ? M : kBwdChunkM)) * K * 4;
+    p.workspace_bytes = p.gu_bytes + mfma_bytes + p.partial_bytes;
     // dh: within a wave its rows in order, then the waves of a workgroup, then every 16th partial,
     // then the 16 group sums
     const int reduce_depth = (p.nranges + kReduceParts - 1) / kReduceParts + kReduceParts;
@@ -755,6 +780,11 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.accum_depth = std::max((int)(rows_per_wave + kFusedWaves) + reduce_depth, 8 * u + 6);
     } else if (p.path == kPathSplitK) {
         p.accum_depth = std::max(p.split_rpb + reduce_depth, 8 * p.split_u + 6 + p.split_waves);
+    } else if (p.path == kPathMfma) {
+        // each MFMA adds a 32-product block (a tree of depth 5) to its accumulator, counted at twice
+        // the fp32 unit roundoff as the forward's MFMA kernels are: dh over a range's steps, then
+        // the reduction; dW over one or two blocks of the M rows
+        p.accum_depth = std::max(2 * (p.dh_steps + 5) + reduce_depth, 2 * (p.mp32 / 32 + 5));
     } else {
         p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves + reduce_depth;
     }

@@ -1,0 +1,295 @@
+// Backward of the dual-weight GLU projection for 8 < M <= 64 rows of hidden:
+// the three contractions as v_mfma_f32_16x16x32_bf16 products.
+//
+// After the grouped GEMV and the elementwise step have left dg and du
+// ([2][M][N] bf16) at the workspace head, repack_kernel writes zero-padded
+// operand copies:
+//  * dg2, du2 [Mp16][Np]: dg and du with rows padded to a multiple of 16 and
+//    columns to a multiple of 32 (the B operand of dh, contraction over j);
+//  * dgT, duT [N][Mp32] and hT [K][Mp32]: dg, du and hidden transposed, the
+//    contraction index m padded to a multiple of 32 (both operands of dW).
+// Padding is +0, so it adds exact zeros to every sum.
+//
+// dw_mfma_kernel: dWg^T = hT . dgT^T as a [K][N] product, and dWu likewise.
+// The contraction over the M rows takes one or two MFMAs per 16 x 16 tile.
+// A wave owns 64 x 64 of (k, j). Lane l holds k = 4(l/16)+e, j = l%16 of a
+// tile, so four consecutive k of one row of dW go out as one 8-byte store.
+//
+// dh_mfma_kernel: partial[split][mat][m][k] = sum over the split's rows j of
+// dG[m][j] W[j][k], as D[k][m] with the contraction over j, 32 rows per MFMA.
+// A workgroup of 4 waves owns 64 columns k (16 per wave) and one range of
+// rows j. Per 32-row step:
+//  1. every thread loads one 16-byte chunk of Wg and of Wu (8 columns of one
+//     row), issued D steps ahead;
+//  2. writes it transposed into LDS, with rows past the range as zeros;
+//  3. after one barrier each wave reads its A operand (16 k x 32 j) from
+//     there and its B operands (dg2, du2: 16 rows m x 32 j) from the
+//     workspace.
+// The weights are read once. dh_reduce_kernel then adds the splits' partials
+// in a fixed order and applies dh's roundings.
+// No atomics anywhere: the results are bitwise reproducible.
+#include "glu_backward.h"
+#include "glu_device.h"
+#include "glu_mfma_common.h"
+
+namespace glu {
+
+namespace {
+
+constexpr int kRepackThreads = 256;
+constexpr int kMfmaBwdThreads = 256;  // 4 waves
+constexpr int kDwTile = 64;           // k and j extent of a wave's dW tile
+constexpr int kDhK = 64;              // columns k per dh workgroup (16 per wave)
+constexpr int kDhStep = 32;           // weight rows per dh step (one MFMA contraction)
+constexpr int kDhTS = 40;             // elements per LDS row of the transposed tile (32 rows j + 8 of padding,
+                                      // 80 bytes: 16-byte aligned A reads, spread over the banks)
+constexpr int kDhDepth = 4;           // steps whose loads are in flight
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+}
+
+}  // namespace
+
+// transpose == 0: dst[r][c] = src[r][c] (dst rows of Cp elements, Rp rows);
+// transpose != 0: dst[c][r] = src[r][c] (dst rows of Rp elements, C rows).
+// Entries with r >= R or c >= C are +0.  src rows are ld elements apart.
+__global__ void __launch_bounds__(kRepackThreads)
+repack_kernel(const uint16_t* __restrict__ src, int64_t ld, uint16_t* __restrict__ dst, int R, int C, int Rp, int Cp,
+              int transpose)
+{
+    const int64_t i = (int64_t)blockIdx.x * kRepackThreads + threadIdx.x;
+    int64_t r, c;
+    if (transpose) {
+        if (i >= (int64_t)C * Rp) return;
+        c = i / Rp;
+        r = i - c * Rp;
+    } else {
+        if (i >= (int64_t)Rp * Cp) return;
+        r = i / Cp;
+        c = i - r * Cp;
+    }
+    dst[i] = (r < R && c < C) ? src[r * ld + c] : (uint16_t)0;
+}
+
+// KS = Mp32 / 32 (1 or 2).  ktiles = ceil(K / 64); wave tiles ntiles = ktiles * ceil(N / 64).
+template <int KS>
+__global__ void __launch_bounds__(kMfmaBwdThreads)
+dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT, const uint16_t* __restrict__ duT,
+               uint16_t* __restrict__ dwg, uint16_t* __restrict__ dwu, int N, int K, int ktiles, int64_t ntiles)
+{
+    constexpr int MP = 32 * KS;
+    constexpr int T = kDwTile / 16;  // 16 x 16 tiles per side
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t tile = (int64_t)blockIdx.x * (kMfmaBwdThreads / kWave) + (threadIdx.x / kWave);
+    if (tile >= ntiles) return;  // whole wave; no barriers below
+    const int k0 = (int)(tile % ktiles) * kDwTile;
+    const int64_t j0 = (tile / ktiles) * kDwTile;
+    const int i16 = lane & 15, q = lane >> 4;
+
+    u32x4_t a[KS][T], bg[KS][T], bu[KS][T];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            // rows past K or N re-read the last row: their results are never stored
+            const int64_t k = min(k0 + 16 * t + i16, K - 1);
+            const int64_t j = min(j0 + 16 * t + i16, (int64_t)N - 1);
+            a[ks][t] = *reinterpret_cast<const u32x4_t*>(hT + k * MP + 32 * ks + 8 * q);
+            bg[ks][t] = *reinterpret_cast<const u32x4_t*>(dgT + j * MP + 32 * ks + 8 * q);
+            bu[ks][t] = *reinterpret_cast<const u32x4_t*>(duT + j * MP + 32 * ks + 8 * q);
+        }
+    }
+#pragma unroll
+    for (int tj = 0; tj < T; ++tj) {
+        f32x4_t cg[T], cu[T];
+#pragma unroll
+        for (int tk = 0; tk < T; ++tk) {
+            cg[tk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            cu[tk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                cg[tk] = mfma16(a[ks][tk], bg[ks][tj], cg[tk]);
+                cu[tk] = mfma16(a[ks][tk], bu[ks][tj], cu[tk]);
+            }
+        }
+        const int64_t j = j0 + 16 * tj + i16;
+#pragma unroll
+        for (int tk = 0; tk < T; ++tk) {
+            const int k = k0 + 16 * tk + 4 * q;  // k % 4 == 0 and K % 8 == 0: k < K covers k + 3
+            if (j < N && k < K) {
+                uint2 vg, vu;
+                vg.x = pack_bf16x2(cg[tk][0], cg[tk][1]);
+                vg.y = pack_bf16x2(cg[tk][2], cg[tk][3]);
+                vu.x = pack_bf16x2(cu[tk][0], cu[tk][1]);
+                vu.y = pack_bf16x2(cu[tk][2], cu[tk][3]);
+                *reinterpret_cast<uint2*>(dwg + j * K + k) = vg;
+                *reinterpret_cast<uint2*>(dwu + j * K + k) = vu;
+            }
+        }
+    }
+}
+
+// MT = Mp16 / 16 (1..4).  Workgroup b: columns [64 (b % ktiles), +64), rows j of split
+// b / ktiles: [split * jr, min(N, (split + 1) * jr)), jr a multiple of 32.  g2, u2: dg2, du2
+// ([Mp16][np] with np a multiple of 32).  partial: [splits][2][M][K] fp32.
+template <int MT>
+__global__ void __launch_bounds__(kMfmaBwdThreads)
+dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__ up_w,
+               const uint16_t* __restrict__ g2, const uint16_t* __restrict__ u2, float* __restrict__ partial, int M,
+               int N, int K, int np, int ktiles, int jr)
+{
+    constexpr int D = kDhDepth;
+    __shared__ __align__(16) uint16_t tw[2][2][kDhK * kDhTS];  // [buffer][matrix][k][j]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int k0 = (int)(blockIdx.x % ktiles) * kDhK;
+    const int split = (int)(blockIdx.x / ktiles);
+    const int jb = split * jr;
+    const int je = min(jb + jr, N);
+    const int nsteps = (je - jb + kDhStep - 1) / kDhStep;  // >= 1: the plan leaves no split empty
+    const int i16 = lane & 15, q = lane >> 4;
+
+    // this thread's weight chunk: row r_ld of the step, columns k0 + 8 c_ld .. + 7
+    const int r_ld = tid >> 3, c_ld = tid & 7;
+    const bool col_ok = k0 + 8 * c_ld < K;
+    const int kc = col_ok ? k0 + 8 * c_ld : K - 8;  // in bounds; such columns are stored as zeros
+
+    auto load = [&](int s, u32x4_t (&w)[2], u32x4_t (&b)[2][MT]) __attribute__((always_inline)) {
+        const int64_t j = min(jb + kDhStep * s + r_ld, N - 1);  // rows past the range: stored as zeros
+        w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gate_w + j * K + kc));
+        w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up_w + j * K + kc));
+        // B: rows m = 16 mt + l%16 of dg2 and du2, columns jb + 32 s + 8 (l/16) .. + 7 (zero past N)
+        const int64_t jj = jb + kDhStep * s + 8 * q;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int64_t off = (int64_t)(16 * mt + i16) * np + jj;
+            b[0][mt] = *reinterpret_cast<const u32x4_t*>(g2 + off);
+            b[1][mt] = *reinterpret_cast<const u32x4_t*>(u2 + off);
+        }
+    };
+    auto publish = [&](int buf, int s, const u32x4_t (&w)[2]) __attribute__((always_inline)) {
+        const bool row_ok = jb + kDhStep * s + r_ld < je;
+#pragma unroll
+        for (int mat = 0; mat < 2; ++mat) {
+            uint16_t* t = &tw[buf][mat][0];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t v = w[mat][e >> 1];
+                const uint16_t x = (uint16_t)((e & 1) ? (v >> 16) : (v & 0xFFFFu));
+                t[(8 * c_ld + e) * kDhTS + r_ld] = (row_ok && col_ok) ? x : (uint16_t)0;
+            }
+        }
+    };
+
+    f32x4_t acc[2][MT];
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mat][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    auto compute = [&](int buf, const u32x4_t (&b)[2][MT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mat = 0; mat < 2; ++mat) {
+            const u32x4_t a =
+                *reinterpret_cast<const u32x4_t*>(&tw[buf][mat][(16 * wave + i16) * kDhTS + 8 * q]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mat][mt] = mfma16(a, b[mat][mt], acc[mat][mt]);
+        }
+    };
+
+    u32x4_t W[D][2];
+    u32x4_t B[D][2][MT];
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        if (s < nsteps) load(s, W[s], B[s]);
+    }
+    // step s (s % D == Q): publish its weights, one barrier, its MFMAs, then refill its registers
+    // with step s + D.  D is even, so the LDS buffer s & 1 is Q & 1.  In the steady state every
+    // refill is live and nothing branches around a load, so the waits leave D - 1 steps in flight.
+    auto stage = [&](auto Qc, auto tailc, int s) __attribute__((always_inline)) {
+        constexpr int Q = decltype(Qc)::value;
+        constexpr bool TAIL = decltype(tailc)::value;
+        publish(Q & 1, s, W[Q]);
+        __syncthreads();
+        compute(Q & 1, B[Q]);
+        if (!TAIL || s + D < nsteps) load(s + D, W[Q], B[Q]);
+    };
+    auto steady = [&](auto Qc, int s) __attribute__((always_inline)) { stage(Qc, std::false_type{}, s); };
+    auto tail = [&](auto Qc, int s) __attribute__((always_inline)) { stage(Qc, std::true_type{}, s); };
+    int s0 = 0;
+    for (; s0 + 2 * D <= nsteps; s0 += D) run_stages<0, D>(steady, s0, nsteps);
+    for (; s0 < nsteps; s0 += D) run_stages<0, D>(tail, s0, nsteps);
+
+    // lane l holds D[4(l/16) + e][l%16]: columns k = k0 + 16 wave + 4(l/16) + e of row m = 16 mt + l%16
+    const int k = k0 + 16 * wave + 4 * q;
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + i16;
+            if (m < M && k < K) {
+                *reinterpret_cast<f32x4_t*>(partial + (((int64_t)split * 2 + mat) * M + m) * K + k) = acc[mat][mt];
+            }
+        }
+    }
+}
+
+hipError_t repack_launch(const uint16_t* src, int64_t ld, uint16_t* dst, int R, int C, int Rp, int Cp, bool transpose,
+                         hipStream_t stream)
+{
+    const int64_t n = transpose ? (int64_t)C * Rp : (int64_t)Rp * Cp;
+    if (n <= 0) return hipSuccess;
+    if (R > Rp || (!transpose && C > Cp)) return hipErrorInvalidValue;
+    const int64_t grid = (n + kRepackThreads - 1) / kRepackThreads;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(kRepackThreads), 0, stream, src, ld, dst, R, C, Rp,
+                       Cp, transpose ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t dw_mfma_launch(const BwdPlan& p, const uint16_t* hT, const uint16_t* dgT, const uint16_t* duT,
+                          uint16_t* dwg, uint16_t* dwu, int N, int K, hipStream_t stream)
+{
+    const int ktiles = (K + kDwTile - 1) / kDwTile;
+    const int64_t ntiles = (int64_t)ktiles * ((N + kDwTile - 1) / kDwTile);
+    const int64_t grid = (ntiles + 3) / 4;
+    if (p.path != kPathMfma || N < 1 || K < 8 || (K & 7) != 0 || grid < 1 || grid > 0x7fffffff) {
+        return hipErrorInvalidValue;
+    }
+    if (p.mp32 == 32) {
+        hipLaunchKernelGGL(dw_mfma_kernel<1>, dim3((unsigned)grid), dim3(kMfmaBwdThreads), 0, stream, hT, dgT, duT,
+                           dwg, dwu, N, K, ktiles, ntiles);
+    } else if (p.mp32 == 64) {
+        hipLaunchKernelGGL(dw_mfma_kernel<2>, dim3((unsigned)grid), dim3(kMfmaBwdThreads), 0, stream, hT, dgT, duT,
+                           dwg, dwu, N, K, ktiles, ntiles);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* g2,
+                          const uint16_t* u2, float* partial, int N, int K, hipStream_t stream)
+{
+    using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, float*, int, int, int,
+                        int, int, int);
+    static const Fn table[4] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, dh_mfma_kernel<3>, dh_mfma_kernel<4>};
+    const int mt = p.mp16 / 16;
+    const int ktiles = (K + kDhK - 1) / kDhK;
+    if (p.path != kPathMfma || mt < 1 || mt > 4 || M < 1 || M > p.mp16 || N < 1 || K < 8 || (K & 7) != 0 ||
+        p.dh_jr < kDhStep || p.dh_jr % kDhStep != 0 || p.np32 < N || p.np32 % kDhStep != 0 || p.dh_splits < 1 ||
+        (int64_t)(p.dh_splits - 1) * p.dh_jr >= N || (int64_t)p.dh_splits * p.dh_jr < N ||
+        p.dh_splits != p.nranges) {
+        return hipErrorInvalidValue;
+    }
+    const int64_t grid = (int64_t)ktiles * p.dh_splits;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(table[mt - 1], dim3((unsigned)grid), dim3(kMfmaBwdThreads), 0, stream, gate_w, up_w, g2, u2,
+                       partial, M, N, K, p.np32, ktiles, p.dh_jr);
+    return hipGetLastError();
+}
+
+}  // namespace glu

@@ -70,9 +70,12 @@ def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
     c = contract(hb, gb, ub, dg_gpu, du_gpu)
     dh, dwg, dwu = (bits(t) for t in got)
     plan = api.backward_plan(M, N, K)
+    # the weight gradients add the M rows in order (depth M), or on the matrix cores above 8 rows,
+    # whose depth the plan's accum_depth covers
+    dw_depth = max(M, plan["accum_depth"]) if M > 8 else M
     reps = {
-        "dwg": check.compare_linear(dwg, LinearResult(c.dwg, c.dwg_pre, c.dwg_abs), depth=M, k_len=M),
-        "dwu": check.compare_linear(dwu, LinearResult(c.dwu, c.dwu_pre, c.dwu_abs), depth=M, k_len=M),
+        "dwg": check.compare_linear(dwg, LinearResult(c.dwg, c.dwg_pre, c.dwg_abs), depth=dw_depth, k_len=M),
+        "dwu": check.compare_linear(dwu, LinearResult(c.dwu, c.dwu_pre, c.dwu_abs), depth=dw_depth, k_len=M),
         "dh": check.compare_grad_sum(dh, c.dh, c.dhg_pre, c.dhg_abs, c.dhu_pre, c.dhu_abs,
                                      depth=plan["accum_depth"], k_len=N),
     }
@@ -88,8 +91,10 @@ CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2
          # one pass with K split over a workgroup: ragged last wave, two chunks a lane, hidden in LDS
          (4, 9216, 3072), (1, 12288, 4096), (2, 700, 2568), (3, 300, 8192), (2, 99, 6152), (3, 255, 4096),
          (2, 257, 2600), (1, 3, 4104), (4, 1, 2576), (4, 4104, 4096), (1, 513, 8192),
-         # more than 8 rows of hidden: dh in chunks of 8, the weight gradients over all rows at once
-         (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8)]
+         # more than 8 rows of hidden: the contractions on the matrix cores (zero-padded operands,
+         # ragged row ranges and column tiles, partial 16-row tiles of hidden)
+         (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8), (17, 1000, 2568),
+         (40, 333, 520), (48, 4097, 72), (12, 31, 4096), (64, 9216, 2560)]
 
 
 @pytest.mark.parametrize("M,N,K", CASES)

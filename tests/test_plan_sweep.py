@@ -82,10 +82,22 @@ def test_backward_plans_cover_rows_and_partials(M):
                     assert p["block"] % 64 == 0 and p["block"] <= 512
                     assert p["block"] * 8 * 2 >= K and (p["block"] * 8 >= K or M <= 3)
                     assert p["block"] - 64 < math.ceil(K / 8 / (1 if p["block"] * 8 >= K else 2))
+            elif M > 8:
+                # MFMA contractions: ranges of 32-row steps of the weights x 64-column tiles, one
+                # fp32 partial of dh per range; zero-padded operand copies before the partials
+                ktiles = math.ceil(K / 64)
+                assert p["launches"] == 10 and p["grid"] % ktiles == 0
+                splits = p["grid"] // ktiles
+                jr = math.ceil(N / splits / 32) * 32 if splits > 1 else math.ceil(N / 32) * 32
+                assert (splits - 1) * jr < N <= splits * jr or splits == 1
+                mp16, mp32, np32 = math.ceil(M / 16) * 16, math.ceil(M / 32) * 32, math.ceil(N / 32) * 32
+                pad = lambda b: -(-b // 256) * 256
+                copies = pad(2 * mp16 * np32 * 2) + pad(2 * N * mp32 * 2) + pad(K * mp32 * 2)
+                assert ws == gu + copies + splits * 2 * M * K * 4, (M, N, K)
             else:
                 nslabs = math.ceil(K / 512)
                 assert p["grid"] % nslabs == 0
                 nranges = p["grid"] // nslabs
                 assert nranges <= N
                 assert ws == gu + nranges * 2 * min(M, 8) * K * 4, (M, N, K)
-                assert p["launches"] == (4 if M <= 8 else 3 + 2 * math.ceil(M / 8))
+                assert p["launches"] == 4
