@@ -640,11 +640,14 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
         uint16_t* uT = gT + N * bp.mp32;
         uint16_t* hT = reinterpret_cast<uint16_t*>(w + bp.off_hT);
         const int m = (int)M, n = (int)N, k = (int)K;
-        if (e == hipSuccess) e = glu::repack_launch(dg_all, N, g2, m, n, bp.mp16, bp.np32, false, s);
-        if (e == hipSuccess) e = glu::repack_launch(du_all, N, u2, m, n, bp.mp16, bp.np32, false, s);
-        if (e == hipSuccess) e = glu::repack_launch(dg_all, N, gT, m, n, bp.mp32, 0, true, s);
-        if (e == hipSuccess) e = glu::repack_launch(du_all, N, uT, m, n, bp.mp32, 0, true, s);
-        if (e == hipSuccess) e = glu::repack_launch(hidden, K, hT, m, k, bp.mp32, 0, true, s);
+        glu::RepackJobs jobs{};
+        jobs.job[0] = {dg_all, N, g2, m, n, bp.mp16, bp.np32, 0, 0, 0};
+        jobs.job[1] = {du_all, N, u2, m, n, bp.mp16, bp.np32, 0, 0, 0};
+        jobs.job[2] = {dg_all, N, gT, m, n, bp.mp32, 0, 1, 0, 0};
+        jobs.job[3] = {du_all, N, uT, m, n, bp.mp32, 0, 1, 0, 0};
+        jobs.job[4] = {hidden, K, hT, m, k, bp.mp32, 0, 1, 0, 0};
+        jobs.n = 5;
+        if (e == hipSuccess) e = glu::repack_launch(jobs, s);
         if (e == hipSuccess) e = glu::dh_mfma_launch(bp, m, gate_w, up_w, g2, u2, partial, n, k, s);
         if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, m, k, s);
         if (e == hipSuccess) e = glu::dw_mfma_launch(bp, hT, gT, uT, dwg, dwu, n, k, s);
@@ -852,7 +855,7 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
     // the grouped GEMV counts as one launch
-    plan->launches = run_all ? (bp.path == glu::kPathMfma     ? 10
+    plan->launches = run_all ? (bp.path == glu::kPathMfma     ? 6
                                 : bp.path != glu::kPathChunks ? 2
                                                               : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8))))
                              : 0;

@@ -42,7 +42,7 @@ struct BwdPlan {
     int split_waves;         // waves per workgroup
     int split_rpb;           // weight rows per workgroup
     int split_grid;          // workgroups (each leaves one partial of dh)
-    int mp16, mp32;          // MFMA path: M rounded up to 16 (dh's B operand) and to 32 (dW's contraction)
+    int mp16, mp32;          // MFMA path: M rounded up to 16, 32 or 64 (dh's B operand) and to 32 (dW's)
     int np32;                // N rounded up to 32 (the columns of dg2, du2)
     int dh_splits, dh_jr;    // ranges of weight rows (jr rows each, a multiple of 32) = dh's partials
     int dh_steps;            // 32-row steps of the longest range
@@ -72,8 +72,21 @@ hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_
 hipError_t splitk_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
                          const uint16_t* up_w, const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu,
                          float* partial, int N, int K, hipStream_t stream);
-hipError_t repack_launch(const uint16_t* src, int64_t ld, uint16_t* dst, int R, int C, int Rp, int Cp, bool transpose,
-                         hipStream_t stream);
+// zero-padded copies of R x C bf16 matrices (rows ld elements apart) for the MFMA backward
+struct RepackJob {
+    const uint16_t* src;
+    int64_t ld;
+    uint16_t* dst;
+    int R, C, Rp, Cp;   // Rp >= R rows (transposed: the row length), Cp >= C columns (not transposed)
+    int transpose;
+    int64_t first, count;  // set by repack_launch
+};
+constexpr int kMaxRepackJobs = 5;
+struct RepackJobs {
+    RepackJob job[kMaxRepackJobs];
+    int n;
+};
+hipError_t repack_launch(RepackJobs jobs, hipStream_t stream);
 hipError_t dw_mfma_launch(const BwdPlan& p, const uint16_t* hT, const uint16_t* dgT, const uint16_t* duT,
                           uint16_t* dwg, uint16_t* dwu, int N, int K, hipStream_t stream);
 hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* g2,

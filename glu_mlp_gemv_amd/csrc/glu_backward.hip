@@ -747,7 +747,7 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     int64_t mfma_bytes = 0;  // the MFMA path's operand copies
     if (M >= kBwdMfmaMinM && M <= kBwdMaxM && N > 0 && K >= 8) {
         p.path = kPathMfma;
-        p.mp16 = (int)((M + 15) / 16 * 16);
+        p.mp16 = M <= 16 ? 16 : (M <= 32 ? 32 : 64);  // 1, 2 or 4 tiles of 16 rows: 4 waves split evenly
         p.mp32 = (int)((M + 31) / 32 * 32);
         p.np32 = (int)((N + 31) / 32 * 32);
         // about 512 workgroups of 64 columns x one range of rows, ranges a multiple of 32 rows

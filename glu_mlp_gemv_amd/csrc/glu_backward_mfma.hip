@@ -4,7 +4,7 @@
 // After the grouped GEMV and the elementwise step have left dg and du
 // ([2][M][N] bf16) at the workspace head, repack_kernel writes zero-padded
 // operand copies:
-//  * dg2, du2 [Mp16][Np]: dg and du with rows padded to a multiple of 16 and
+//  * dg2, du2 [Mp16][Np]: dg and du with rows padded to 16, 32 or 64 and
 //    columns to a multiple of 32 (the B operand of dh, contraction over j);
 //  * dgT, duT [N][Mp32] and hT [K][Mp32]: dg, du and hidden transposed, the
 //    contraction index m padded to a multiple of 32 (both operands of dW).
@@ -21,10 +21,12 @@
 // rows j. Per 32-row step:
 //  1. every thread loads one 16-byte chunk of Wg and of Wu (8 columns of one
 //     row), issued D steps ahead;
-//  2. writes it transposed into LDS, with rows past the range as zeros;
-//  3. after one barrier each wave reads its A operand (16 k x 32 j) from
-//     there and its B operands (dg2, du2: 16 rows m x 32 j) from the
-//     workspace.
+//  2. writes it transposed into LDS (rows past the range as zeros), pairing
+//     two rows per 32-bit write through a DPP exchange;
+//  3. after one barrier each wave reads its A operands (16 k x 32 j each)
+//     from there and its B operands (dg2, du2: 16 rows m x 32 j) from the
+//     workspace. A wave owns one 16-row tile of hidden and 4 / (tiles)
+//     column subtiles, so no two waves load the same B operand.
 // The weights are read once. dh_reduce_kernel then adds the splits' partials
 // in a fixed order and applies dh's roundings.
 // No atomics anywhere: the results are bitwise reproducible.
@@ -45,6 +47,8 @@ constexpr int kDhTS = 40;             // elements per LDS row of the transposed 
                                       // 80 bytes: 16-byte aligned A reads, spread over the banks)
 constexpr int kDhDepth = 4;           // steps whose loads are in flight
 
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
     return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
@@ -52,25 +56,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 
 }  // namespace
 
-// transpose == 0: dst[r][c] = src[r][c] (dst rows of Cp elements, Rp rows);
-// transpose != 0: dst[c][r] = src[r][c] (dst rows of Rp elements, C rows).
-// Entries with r >= R or c >= C are +0.  src rows are ld elements apart.
+// One launch for all the copies: thread i serves the copy whose range [first, first + count)
+// holds i.  transpose == 0: dst[r][c] = src[r][c] (Rp rows of Cp elements); transpose != 0:
+// dst[c][r] = src[r][c] (C rows of Rp elements).  Entries with r >= R or c >= C are +0.
 __global__ void __launch_bounds__(kRepackThreads)
-repack_kernel(const uint16_t* __restrict__ src, int64_t ld, uint16_t* __restrict__ dst, int R, int C, int Rp, int Cp,
-              int transpose)
+repack_kernel(RepackJobs jobs)
 {
     const int64_t i = (int64_t)blockIdx.x * kRepackThreads + threadIdx.x;
+    int q = 0;
+    while (q + 1 < jobs.n && i >= jobs.job[q + 1].first) ++q;
+    const RepackJob& jb = jobs.job[q];
+    const int64_t x = i - jb.first;
+    if (x < 0 || x >= jb.count) return;
     int64_t r, c;
-    if (transpose) {
-        if (i >= (int64_t)C * Rp) return;
-        c = i / Rp;
-        r = i - c * Rp;
+    if (jb.transpose) {
+        c = x / jb.Rp;
+        r = x - c * jb.Rp;
     } else {
-        if (i >= (int64_t)Rp * Cp) return;
-        r = i / Cp;
-        c = i - r * Cp;
+        r = x / jb.Cp;
+        c = x - r * jb.Cp;
     }
-    dst[i] = (r < R && c < C) ? src[r * ld + c] : (uint16_t)0;
+    jb.dst[x] = (r < jb.R && c < jb.C) ? jb.src[r * jb.ld + c] : (uint16_t)0;
 }
 
 // KS = Mp32 / 32 (1 or 2).  ktiles = ceil(K / 64); wave tiles ntiles = ktiles * ceil(N / 64).
@@ -119,19 +125,18 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
         for (int tk = 0; tk < T; ++tk) {
             const int k = k0 + 16 * tk + 4 * q;  // k % 4 == 0 and K % 8 == 0: k < K covers k + 3
             if (j < N && k < K) {
-                uint2 vg, vu;
-                vg.x = pack_bf16x2(cg[tk][0], cg[tk][1]);
-                vg.y = pack_bf16x2(cg[tk][2], cg[tk][3]);
-                vu.x = pack_bf16x2(cu[tk][0], cu[tk][1]);
-                vu.y = pack_bf16x2(cu[tk][2], cu[tk][3]);
-                *reinterpret_cast<uint2*>(dwg + j * K + k) = vg;
-                *reinterpret_cast<uint2*>(dwu + j * K + k) = vu;
+                const u32x2_t vg = {pack_bf16x2(cg[tk][0], cg[tk][1]), pack_bf16x2(cg[tk][2], cg[tk][3])};
+                const u32x2_t vu = {pack_bf16x2(cu[tk][0], cu[tk][1]), pack_bf16x2(cu[tk][2], cu[tk][3])};
+                // plain stores: the L2 merges a wave's four 32-byte pieces of a row into whole lines
+                // (nontemporal ones measured 1.3-1.7x slower for the whole backward)
+                *reinterpret_cast<u32x2_t*>(dwg + j * K + k) = vg;
+                *reinterpret_cast<u32x2_t*>(dwu + j * K + k) = vu;
             }
         }
     }
 }
 
-// MT = Mp16 / 16 (1..4).  Workgroup b: columns [64 (b % ktiles), +64), rows j of split
+// MT = Mp16 / 16 (1, 2 or 4).  Workgroup b: columns [64 (b % ktiles), +64), rows j of split
 // b / ktiles: [split * jr, min(N, (split + 1) * jr)), jr a multiple of 32.  g2, u2: dg2, du2
 // ([Mp16][np] with np a multiple of 32).  partial: [splits][2][M][K] fp32.
 template <int MT>
@@ -151,35 +156,53 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     const int je = min(jb + jr, N);
     const int nsteps = (je - jb + kDhStep - 1) / kDhStep;  // >= 1: the plan leaves no split empty
     const int i16 = lane & 15, q = lane >> 4;
+    // the 4 x MT (column subtile, row tile) pairs: wave w takes row tile w % MT of hidden and the
+    // MT column subtiles from (w / MT) MT on, so that no two waves load the same B operand
+    const int mt = wave % MT;
+    const int ks0 = (wave / MT) * MT;
 
     // this thread's weight chunk: row r_ld of the step, columns k0 + 8 c_ld .. + 7
     const int r_ld = tid >> 3, c_ld = tid & 7;
     const bool col_ok = k0 + 8 * c_ld < K;
     const int kc = col_ok ? k0 + 8 * c_ld : K - 8;  // in bounds; such columns are stored as zeros
 
-    auto load = [&](int s, u32x4_t (&w)[2], u32x4_t (&b)[2][MT]) __attribute__((always_inline)) {
+    auto load = [&](int s, u32x4_t (&w)[2], u32x4_t (&b)[2]) __attribute__((always_inline)) {
         const int64_t j = min(jb + kDhStep * s + r_ld, N - 1);  // rows past the range: stored as zeros
         w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gate_w + j * K + kc));
         w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up_w + j * K + kc));
         // B: rows m = 16 mt + l%16 of dg2 and du2, columns jb + 32 s + 8 (l/16) .. + 7 (zero past N)
-        const int64_t jj = jb + kDhStep * s + 8 * q;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int64_t off = (int64_t)(16 * mt + i16) * np + jj;
-            b[0][mt] = *reinterpret_cast<const u32x4_t*>(g2 + off);
-            b[1][mt] = *reinterpret_cast<const u32x4_t*>(u2 + off);
-        }
+        const int64_t off = (int64_t)(16 * mt + i16) * np + jb + kDhStep * s + 8 * q;
+        b[0] = *reinterpret_cast<const u32x4_t*>(g2 + off);
+        b[1] = *reinterpret_cast<const u32x4_t*>(u2 + off);
     };
+    // Transposed publication.  Rows r and r ^ 1 of a chunk column sit in lanes l and l ^ 8, which
+    // trade half their chunk through one DPP row rotation by 8: the even row's thread then holds
+    // columns 8c .. 8c+3 and the odd row's 8c+4 .. 8c+7 of both rows, and writes them as four
+    // 32-bit (row, row + 1) pairs.  Element (k, j) sits at T[k][8 ((j >> 3) ^ (k >> 4)) + (j & 7)]:
+    // the 64 lanes of one write then hit 64 different banks, and a wave's A read (k >> 4 == wave)
+    // still takes 16 contiguous bytes per lane.
+    const bool odd = (r_ld & 1) != 0;
     auto publish = [&](int buf, int s, const u32x4_t (&w)[2]) __attribute__((always_inline)) {
-        const bool row_ok = jb + kDhStep * s + r_ld < je;
+        const bool ok = col_ok && jb + kDhStep * s + r_ld < je;
+        const int kb = 8 * c_ld + (odd ? 4 : 0);
+        const int jo = r_ld & 6;  // the pair's first row within its block of 8
 #pragma unroll
         for (int mat = 0; mat < 2; ++mat) {
-            uint16_t* t = &tw[buf][mat][0];
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            const u32x4_t v = ok ? w[mat] : z;
+            const uint32_t s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0x128, 0xF, 0xF, false);
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0x128, 0xF, 0xF, false);
+            // lo: four columns of the even row, hi: the same columns of the odd row
+            const uint32_t lo0 = odd ? r0 : v[0], lo1 = odd ? r1 : v[1];
+            const uint32_t hi0 = odd ? v[2] : r0, hi1 = odd ? v[3] : r1;
+            const uint32_t pr[4] = {(lo0 & 0xFFFFu) | (hi0 << 16), (lo0 >> 16) | (hi0 & 0xFFFF0000u),
+                                    (lo1 & 0xFFFFu) | (hi1 << 16), (lo1 >> 16) | (hi1 & 0xFFFF0000u)};
+            uint32_t* t = reinterpret_cast<uint32_t*>(&tw[buf][mat][0]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t v = w[mat][e >> 1];
-                const uint16_t x = (uint16_t)((e & 1) ? (v >> 16) : (v & 0xFFFFu));
-                t[(8 * c_ld + e) * kDhTS + r_ld] = (row_ok && col_ok) ? x : (uint16_t)0;
+            for (int e = 0; e < 4; ++e) {
+                const int k = kb + e;
+                t[(k * kDhTS + 8 * (wave ^ (k >> 4)) + jo) >> 1] = pr[e];
             }
         }
     };
@@ -190,18 +213,21 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mat][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    auto compute = [&](int buf, const u32x4_t (&b)[2][MT]) __attribute__((always_inline)) {
+    auto compute = [&](int buf, const u32x4_t (&b)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mat = 0; mat < 2; ++mat) {
-            const u32x4_t a =
-                *reinterpret_cast<const u32x4_t*>(&tw[buf][mat][(16 * wave + i16) * kDhTS + 8 * q]);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mat][mt] = mfma16(a, b[mat][mt], acc[mat][mt]);
+            for (int t = 0; t < MT; ++t) {
+                const int ks = ks0 + t;  // column subtile: k >> 4 == ks, the read's swizzle
+                const u32x4_t a =
+                    *reinterpret_cast<const u32x4_t*>(&tw[buf][mat][(16 * ks + i16) * kDhTS + 8 * (q ^ ks)]);
+                acc[mat][t] = mfma16(a, b[mat], acc[mat][t]);
+            }
         }
     };
 
     u32x4_t W[D][2];
-    u32x4_t B[D][2][MT];
+    u32x4_t B[D][2];
 #pragma unroll
     for (int s = 0; s < D; ++s) {
         if (s < nsteps) load(s, W[s], B[s]);
@@ -223,30 +249,35 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     for (; s0 + 2 * D <= nsteps; s0 += D) run_stages<0, D>(steady, s0, nsteps);
     for (; s0 < nsteps; s0 += D) run_stages<0, D>(tail, s0, nsteps);
 
-    // lane l holds D[4(l/16) + e][l%16]: columns k = k0 + 16 wave + 4(l/16) + e of row m = 16 mt + l%16
-    const int k = k0 + 16 * wave + 4 * q;
+    // lane l holds D[4(l/16) + e][l%16]: columns k = k0 + 16 ks + 4(l/16) + e of row m = 16 mt + l%16
+    const int m = 16 * mt + i16;
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + i16;
+        for (int t = 0; t < MT; ++t) {
+            const int k = k0 + 16 * (ks0 + t) + 4 * q;
             if (m < M && k < K) {
-                *reinterpret_cast<f32x4_t*>(partial + (((int64_t)split * 2 + mat) * M + m) * K + k) = acc[mat][mt];
+                *reinterpret_cast<f32x4_t*>(partial + (((int64_t)split * 2 + mat) * M + m) * K + k) = acc[mat][t];
             }
         }
     }
 }
 
-hipError_t repack_launch(const uint16_t* src, int64_t ld, uint16_t* dst, int R, int C, int Rp, int Cp, bool transpose,
-                         hipStream_t stream)
+hipError_t repack_launch(RepackJobs jobs, hipStream_t stream)
 {
-    const int64_t n = transpose ? (int64_t)C * Rp : (int64_t)Rp * Cp;
-    if (n <= 0) return hipSuccess;
-    if (R > Rp || (!transpose && C > Cp)) return hipErrorInvalidValue;
-    const int64_t grid = (n + kRepackThreads - 1) / kRepackThreads;
+    if (jobs.n < 1 || jobs.n > kMaxRepackJobs) return hipErrorInvalidValue;
+    int64_t total = 0;
+    for (int q = 0; q < jobs.n; ++q) {
+        RepackJob& j = jobs.job[q];
+        if (j.R > j.Rp || (!j.transpose && j.C > j.Cp) || j.R < 0 || j.C < 0) return hipErrorInvalidValue;
+        j.count = j.transpose ? (int64_t)j.C * j.Rp : (int64_t)j.Rp * j.Cp;
+        j.first = total;
+        total += j.count;
+    }
+    if (total <= 0) return hipSuccess;
+    const int64_t grid = (total + kRepackThreads - 1) / kRepackThreads;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(kRepackThreads), 0, stream, src, ld, dst, R, C, Rp,
-                       Cp, transpose ? 1 : 0);
+    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(kRepackThreads), 0, stream, jobs);
     return hipGetLastError();
 }
 
@@ -276,10 +307,10 @@ hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const
 {
     using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, float*, int, int, int,
                         int, int, int);
-    static const Fn table[4] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, dh_mfma_kernel<3>, dh_mfma_kernel<4>};
+    static const Fn table[4] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>};
     const int mt = p.mp16 / 16;
     const int ktiles = (K + kDhK - 1) / kDhK;
-    if (p.path != kPathMfma || mt < 1 || mt > 4 || M < 1 || M > p.mp16 || N < 1 || K < 8 || (K & 7) != 0 ||
+    if (p.path != kPathMfma || mt < 1 || mt > 4 || !table[mt - 1] || M < 1 || M > p.mp16 || N < 1 || K < 8 || (K & 7) != 0 ||
         p.dh_jr < kDhStep || p.dh_jr % kDhStep != 0 || p.np32 < N || p.np32 % kDhStep != 0 || p.dh_splits < 1 ||
         (int64_t)(p.dh_splits - 1) * p.dh_jr >= N || (int64_t)p.dh_splits * p.dh_jr < N ||
         p.dh_splits != p.nranges) {
