@@ -623,10 +623,17 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
         if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
         return e == hipSuccess ? GLU_OK : fail_launch(e);
     }
-    // g = bf16(h Wg^T), u = bf16(h Wu^T): the grouped GEMV into the workspace
-    glu_projection proj[2] = {{gate_w, gu, N, K, N}, {up_w, gu + mn, N, K, N}};
-    st = run_grouped(hidden, K, proj, 2, M, K, stream, nullptr);
-    if (st != GLU_OK) return st;
+    // g = bf16(h Wg^T), u = bf16(h Wu^T) into the workspace: the grouped GEMV, or above 32 rows of
+    // hidden the tiled GEMM (which reads the weights once where the GEMV's 32-row slices would
+    // read them once per slice)
+    if (bp.gu_gemm) {
+        e = glu::gemm_linear_launch((int)M, hidden, gate_w, up_w, gu, (int)N, (int)K, s);
+        if (e != hipSuccess) return fail_launch(e);
+    } else {
+        glu_projection proj[2] = {{gate_w, gu, N, K, N}, {up_w, gu + mn, N, K, N}};
+        st = run_grouped(hidden, K, proj, 2, M, K, stream, nullptr);
+        if (st != GLU_OK) return st;
+    }
     e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
     const uint16_t* dg_all = gu;
     const uint16_t* du_all = gu + mn;

@@ -46,6 +46,7 @@ struct BwdPlan {
     int np32;                // N rounded up to 32 (the columns of dg2, du2)
     int dh_splits, dh_jr;    // ranges of weight rows (jr rows each, a multiple of 32) = dh's partials
     int dh_steps;            // 32-row steps of the longest range
+    bool gu_gemm;            // g and u from the tiled GEMM (M > 32, N % 4 == 0) instead of the grouped GEMV
     int64_t off_g2, off_gT, off_hT, off_partial;  // workspace offsets of dg2/du2, dgT/duT, hT, the partials
     int nslabs;              // 512-column slabs of K
     int nranges;             // row ranges of N (the one-pass kernel: its workgroups)

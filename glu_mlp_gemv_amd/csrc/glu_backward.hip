@@ -759,6 +759,7 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.dh_jr = (int)(steps * 32);
         p.dh_splits = (int)((N + p.dh_jr - 1) / p.dh_jr);
         p.dh_steps = (int)steps;
+        p.gu_gemm = M > 32 && N % 4 == 0;
         p.nranges = p.dh_splits;
         p.off_g2 = p.gu_bytes;
         p.off_gT = p.off_g2 + pad256((int64_t)2 * p.mp16 * p.np32 * 2);
@@ -785,6 +786,8 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         // the fp32 unit roundoff as the forward's MFMA kernels are: dh over a range's steps, then
         // the reduction; dW over one or two blocks of the M rows
         p.accum_depth = std::max(2 * (p.dh_steps + 5) + reduce_depth, 2 * (p.mp32 / 32 + 5));
+        // g and u from the GEMM: one MFMA per 32-element block of K, plus the tile's fixed steps
+        if (p.gu_gemm) p.accum_depth = std::max(p.accum_depth, (int)(2 * ((K + 31) / 32 + 6)));
     } else {
         p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves + reduce_depth;
     }

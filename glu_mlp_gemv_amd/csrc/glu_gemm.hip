@@ -39,7 +39,9 @@ __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 // with 2, two register sets alternate and a stage's data has two stages of
 // compute to arrive).
 // nbm: M tiles; the grid holds ceil(N / BN) * nbm workgroups.
-template <int BN, int BM, bool KTAIL, int PF>
+// LIN: write bf16(G) and bf16(U) instead of the GLU product: G to out, U to out + M ldo (the
+// backward's [2][M][N] workspace head).
+template <int BN, int BM, bool KTAIL, int PF, bool LIN = false>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __restrict__ gate, int64_t ldg,
             const uint16_t* __restrict__ up, int64_t ldu, uint16_t* __restrict__ out, int64_t ldo, int M, int N,
@@ -184,6 +186,18 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
             const int m = m0 + wm * WM + 16 * j + i16;
+            if constexpr (LIN) {
+                if (m < M && n + 3 < N) {  // N % 4 == 0 for this form (checked by the launcher)
+                    uint2 wg, wu;
+                    wg.x = (uint32_t)f32_to_bf16_rne(ag[i][j][0]) | ((uint32_t)f32_to_bf16_rne(ag[i][j][1]) << 16);
+                    wg.y = (uint32_t)f32_to_bf16_rne(ag[i][j][2]) | ((uint32_t)f32_to_bf16_rne(ag[i][j][3]) << 16);
+                    wu.x = (uint32_t)f32_to_bf16_rne(au[i][j][0]) | ((uint32_t)f32_to_bf16_rne(au[i][j][1]) << 16);
+                    wu.y = (uint32_t)f32_to_bf16_rne(au[i][j][2]) | ((uint32_t)f32_to_bf16_rne(au[i][j][3]) << 16);
+                    *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + n) = wg;
+                    *reinterpret_cast<uint2*>(out + ((int64_t)M + m) * ldo + n) = wu;
+                }
+                continue;
+            }
             uint16_t v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = glu_epilogue(ag[i][j][e], au[i][j][e]);
@@ -264,6 +278,22 @@ hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const
     const int vec_out = (((uintptr_t)out & 7u) == 0 && (ld.o & 3) == 0) ? 1 : 0;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), lds, stream, hidden, ld.h, gate_w, ld.g, up_w,
                        ld.u, out, ld.o, M, N, K, nbm, vec_out);
+    return hipGetLastError();
+}
+
+hipError_t gemm_linear_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                              uint16_t* gu, int N, int K, hipStream_t stream)
+{
+    // 64 x 64 tiles, two stages of loads in flight; N % 4 == 0 so that each lane's 4 outputs of a
+    // row are whole 8-byte stores inside the row
+    if (M < 1 || N < 4 || (N & 3) != 0 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
+    const bool ktail = (K % kStageK) != 0;
+    GemmFn fn = ktail ? gemm_kernel<64, 64, true, 2, true> : gemm_kernel<64, 64, false, 2, true>;
+    const int64_t nbm = (M + 63) / 64;
+    const int64_t grid = ((N + 63) / 64) * nbm;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), gemm_lds_bytes(64, 64), stream, hidden, (int64_t)K,
+                       gate_w, (int64_t)K, up_w, (int64_t)K, gu, (int64_t)N, M, N, K, (int)nbm, 1);
     return hipGetLastError();
 }
 

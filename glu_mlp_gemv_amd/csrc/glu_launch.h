@@ -105,5 +105,9 @@ int64_t gemm_grid(const GemmConfig& c, int64_t M, int64_t N);
 // K % 8 == 0, 16-byte aligned rows (fast layout); out rows may have any stride
 hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int N, int K, const RowStrides& ld, hipStream_t stream);
+// g = bf16(h Wg^T) into gu [M][N] and u = bf16(h Wu^T) into gu + M N: the same tiles (64 x 64) without
+// the GLU epilogue, for the backward at M > 32.  Dense operands; N % 4 == 0, K % 8 == 0.
+hipError_t gemm_linear_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                              uint16_t* gu, int N, int K, hipStream_t stream);
 
 }  // namespace glu
