@@ -13,7 +13,8 @@
 // dw_mfma_kernel: dWg^T = hT . dgT^T as a [K][N] product, and dWu likewise.
 // The contraction over the M rows takes one or two MFMAs per 16 x 16 tile.
 // A wave owns 64 x 64 of (k, j). Lane l holds k = 4(l/16)+e, j = l%16 of a
-// tile, so four consecutive k of one row of dW go out as one 8-byte store.
+// tile; lanes l and l ^ 16 trade a tile of each pair so that every lane
+// stores 8 consecutive k of one row of dW as one 16-byte store.
 //
 // dh_mfma_kernel: partial[split][mat][m][k] = sum over the split's rows j of
 // dG[m][j] W[j][k], as D[k][m] with the contraction over j, 32 rows per MFMA.
@@ -46,8 +47,6 @@ constexpr int kDhStep = 32;           // weight rows per dh step (one MFMA contr
 constexpr int kDhTS = 40;             // elements per LDS row of the transposed tile (32 rows j + 8 of padding,
                                       // 80 bytes: 16-byte aligned A reads, spread over the banks)
 constexpr int kDhDepth = 4;           // steps whose loads are in flight
-
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
@@ -120,17 +119,27 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
                 cu[tk] = mfma16(a[ks][tk], bu[ks][tj], cu[tk]);
             }
         }
+        // Lane (l%16, q = l/16) holds columns 16 tk + 4q .. +3 of row j for each tile tk.  Lanes q and
+        // q ^ 1 (l ^ 16) trade one tile of a pair (tk, tk + 1): the even q then holds 8 consecutive
+        // columns of tile tk, the odd q 8 of tile tk + 1, so each lane stores 16 bytes and four lanes
+        // write 64 contiguous bytes of the row.  Plain stores: nontemporal ones measured 1.3-1.7x
+        // slower for the whole backward.
         const int64_t j = j0 + 16 * tj + i16;
+        const bool oddq = (q & 1) != 0;
 #pragma unroll
-        for (int tk = 0; tk < T; ++tk) {
-            const int k = k0 + 16 * tk + 4 * q;  // k % 4 == 0 and K % 8 == 0: k < K covers k + 3
-            if (j < N && k < K) {
-                const u32x2_t vg = {pack_bf16x2(cg[tk][0], cg[tk][1]), pack_bf16x2(cg[tk][2], cg[tk][3])};
-                const u32x2_t vu = {pack_bf16x2(cu[tk][0], cu[tk][1]), pack_bf16x2(cu[tk][2], cu[tk][3])};
-                // plain stores: the L2 merges a wave's four 32-byte pieces of a row into whole lines
-                // (nontemporal ones measured 1.3-1.7x slower for the whole backward)
-                *reinterpret_cast<u32x2_t*>(dwg + j * K + k) = vg;
-                *reinterpret_cast<u32x2_t*>(dwu + j * K + k) = vu;
+        for (int tk = 0; tk < T; tk += 2) {
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                const f32x4_t& c0 = mat == 0 ? cg[tk] : cu[tk];
+                const f32x4_t& c1 = mat == 0 ? cg[tk + 1] : cu[tk + 1];
+                const uint32_t a0 = pack_bf16x2(c0[0], c0[1]), a1 = pack_bf16x2(c0[2], c0[3]);
+                const uint32_t b0 = pack_bf16x2(c1[0], c1[1]), b1 = pack_bf16x2(c1[2], c1[3]);
+                const uint32_t s0 = oddq ? a0 : b0, s1 = oddq ? a1 : b1;
+                const uint32_t r0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)s0, 0x401F);  // lane ^ 16
+                const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)s1, 0x401F);
+                const u32x4_t v = oddq ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+                const int k = k0 + 16 * (tk + (oddq ? 1 : 0)) + 4 * (q & 2);  // a multiple of 8: k < K covers k + 7
+                if (j < N && k < K) *reinterpret_cast<u32x4_t*>((mat == 0 ? dwg : dwu) + j * K + k) = v;
             }
         }
     }
