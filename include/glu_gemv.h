@@ -222,7 +222,8 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * K <= 8192, and for M <= 4 with 2560 < K <= 4096 (K <= 8192 when M <= 3),
  * two launches, a pass that reads each
  * weight row once and the reduction of dhidden's partial sums; otherwise
- * the grouped GEMV for g and u, then the gradient kernels.
+ * the grouped GEMV for g and u (above M = 32 with N % 4 == 0 a tiled GEMM),
+ * then the gradient kernels (above M = 8 on the matrix cores).
  */
 glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                                   const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
