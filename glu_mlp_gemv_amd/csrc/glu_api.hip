@@ -660,23 +660,12 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
         if (e == hipSuccess) e = glu::dw_mfma_launch(bp, hT, gT, uT, dwg, dwu, n, k, s);
         return e == hipSuccess ? GLU_OK : fail_launch(e);
     }
-    if (M <= glu::kBwdChunkM) {
-        if (e == hipSuccess) {
-            e = glu::contract_launch(bp, (int)M, true, hidden, gate_w, up_w, dg_all, du_all, dwg, dwu, partial, (int)N,
-                                     (int)K, s);
-        }
-        if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
-        return e == hipSuccess ? GLU_OK : fail_launch(e);
+    // 2 <= M <= 8: the contraction (weight gradients and dh's partial sums), then the reduction
+    if (e == hipSuccess) {
+        e = glu::contract_launch(bp, (int)M, hidden, gate_w, up_w, dg_all, du_all, dwg, dwu, partial, (int)N, (int)K,
+                                 s);
     }
-    // more rows: dh in chunks of rows of hidden (each chunk streams the weights), then the weight
-    // gradients over all rows in one launch
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += glu::kBwdChunkM) {
-        const int mc = (int)(M - m0 < glu::kBwdChunkM ? M - m0 : glu::kBwdChunkM);
-        e = glu::contract_launch(bp, mc, false, hidden, gate_w, up_w, dg_all + m0 * N, du_all + m0 * N, dwg, dwu,
-                                 partial, (int)N, (int)K, s);
-        if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh + m0 * K, K, mc, (int)K, s);
-    }
-    if (e == hipSuccess) e = glu::dw_launch(bp, (int)M, hidden, dg_all, du_all, dwg, dwu, (int)N, (int)K, s);
+    if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);
     return e == hipSuccess ? GLU_OK : fail_launch(e);
 }
 
@@ -864,7 +853,7 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     // the grouped GEMV counts as one launch
     plan->launches = run_all ? (bp.path == glu::kPathMfma     ? 6
                                 : bp.path != glu::kPathChunks ? 2
-                                                              : (M <= glu::kBwdChunkM ? 4 : (int)(3 + 2 * ((M + 7) / 8))))
+                                                              : 4)
                              : 0;
     plan->grid = run_all ? (bp.path == glu::kPathFused1   ? bp.fused_grid
                             : bp.path == glu::kPathSplitK ? bp.split_grid

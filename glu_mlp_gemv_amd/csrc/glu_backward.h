@@ -6,7 +6,7 @@
 namespace glu {
 
 constexpr int kBwdMaxM = 64;    // rows of hidden per call
-constexpr int kBwdChunkM = 8;   // rows of hidden per contraction launch (dh); dw_kernel takes all
+constexpr int kBwdChunkM = 8;   // rows of hidden of the VALU contraction kernel at most
 constexpr int kBwdTargetBlocks = 512;  // contraction workgroups aimed for (2 per CU)
 
 constexpr int kFusedMaxU = 5;        // one-pass kernel: up to 5 16-byte chunks per lane (K <= 2560)
@@ -27,7 +27,7 @@ constexpr int kSplitMaxThreads = kSplitMaxWaves * 64;
 constexpr int split_rows(int M, int U) { return U == 1 ? (M <= 2 ? 4 : 2) : (M <= 2 ? 2 : 1); }
 
 // which kernels a backward call runs
-constexpr int kPathChunks = 0;   // grouped GEMV, gradient step, contraction (in chunks of 8 rows), reduction
+constexpr int kPathChunks = 0;   // 2 <= M <= 8: grouped GEMV, gradient step, contraction, reduction
 constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
 constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
 constexpr int kPathMfma = 3;     // 8 < M <= 64: grouped GEMV, gradient step, repacking, dh_mfma_kernel,
@@ -35,7 +35,7 @@ constexpr int kPathMfma = 3;     // 8 < M <= 64: grouped GEMV, gradient step, re
 constexpr int kBwdMfmaMinM = 9;  // rows of hidden from which the contractions run on MFMA
 
 struct BwdPlan {
-    int path;                // kPathChunks, kPathFused1 or kPathSplitK
+    int path;                // kPathChunks, kPathFused1, kPathSplitK or kPathMfma
     bool fused;              // M == 1, K <= 2560: the one-pass kernel
     int fused_grid;          // its workgroups (each leaves one partial of dh)
     int split_u;             // K-split kernel: chunks per lane (1 or 2)
@@ -61,12 +61,10 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K);
 hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int M, int N, hipStream_t stream);
 // K % 8 == 0, hidden / gate_w / up_w / dwg / dwu 16-byte aligned, packed rows.  M <= 8; dw: also
 // the weight gradients (then these M rows are all rows of hidden).  dgm, dum: [M][N].
-hipError_t contract_launch(const BwdPlan& p, int M, bool dw, const uint16_t* hidden, const uint16_t* gate_w,
+hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
                            const uint16_t* up_w, const uint16_t* dgm, const uint16_t* dum, uint16_t* dwg,
                            uint16_t* dwu, float* partial, int N, int K, hipStream_t stream);
 // weight gradients over all M <= kBwdMaxM rows of hidden
-hipError_t dw_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* dgm, const uint16_t* dum,
-                     uint16_t* dwg, uint16_t* dwu, int N, int K, hipStream_t stream);
 hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                         const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial, int N, int K,
                         hipStream_t stream);

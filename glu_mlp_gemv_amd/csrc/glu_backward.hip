@@ -14,7 +14,8 @@
 // M <= 4 with 2560 < K <= 4096 (K <= 8192 for M <= 3): also one pass
 // (splitk_kernel), K split over the lanes of a workgroup so that each lane
 // keeps its columns of dh for all M rows in registers, then dh_reduce_kernel.
-// Otherwise four launches (after the grouped GEMV has written
+// Above M = 8 the contractions run on the matrix cores (glu_backward_mfma.hip).
+// Otherwise, 2 <= M <= 8, four launches (after the grouped GEMV has written
 // g = bf16(h Wg^T) and u = bf16(h Wu^T) into the workspace):
 //  * act_grad_kernel: dg and du from g, u and dout, elementwise, in place;
 //  * contract_kernel: workgroups own (row range, 512-column slab) tiles.  Each
@@ -87,10 +88,9 @@ act_grad_kernel(uint16_t* __restrict__ gu, const uint16_t* __restrict__ dout, in
 
 // M: rows of hidden (1..8).  Workgroup b: slab b % nslabs, rows
 // [r * rows_per_range, min(N, (r + 1) * rows_per_range)) with r = b / nslabs.
-// dgm, dum: dg and du of these M rows ([M][N]).  partial: [nranges][2][M][K] fp32.
-// DW: also the weight gradients (all rows of hidden are these M); without it only dh's partials
-// (for M > 8 the rows are taken in chunks and dw_kernel forms the weight gradients).
-template <int M, bool DW>
+// dgm, dum: dg and du of these M rows ([M][N]).  partial: [nranges][2][M][K] fp32.  Also the
+// weight gradients: the same rows' slab of dWg and dWu.
+template <int M>
 __global__ void __launch_bounds__(kBwdThreads)
 contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
                 const uint16_t* __restrict__ up_w, const uint16_t* __restrict__ dgm, const uint16_t* __restrict__ dum,
@@ -108,9 +108,9 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
     const int j_end = min(j_begin + rows_per_range, N);
 
     // this lane's 8 columns of every row of hidden, as packed bf16 pairs (widened where used)
-    u32x4_b hw[DW ? M : 1];
+    u32x4_b hw[M];
 #pragma unroll
-    for (int m = 0; m < (DW ? M : 0); ++m) {
+    for (int m = 0; m < M; ++m) {
         hw[m] = u32x4_b{0u, 0u, 0u, 0u};
         if (col_ok) hw[m] = *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + c0);
     }
@@ -167,7 +167,7 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
                     au[m][e] = __builtin_fmaf(du[i][m], wuf[e], au[m][e]);
                 }
             }
-            if (!DW || !col_ok) continue;
+            if (!col_ok) continue;
             // this row's slab of dWg and dWu: sums over the rows of hidden in order
             u32x4_b pg, pu;
 #pragma unroll
@@ -177,7 +177,7 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
                 for (int h2 = 0; h2 < 2; ++h2) {
                     float sg = 0.0f, su = 0.0f;
 #pragma unroll
-                    for (int m = 0; m < (DW ? M : 0); ++m) {
+                    for (int m = 0; m < M; ++m) {
                         const float hme = h2 ? bf16hi(hw[m][q]) : bf16lo(hw[m][q]);
                         sg = __builtin_fmaf(dg[i][m], hme, sg);
                         su = __builtin_fmaf(du[i][m], hme, su);
@@ -218,63 +218,6 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
             }
         }
         __syncthreads();
-    }
-}
-
-// Weight gradients for M rows of hidden (M <= kBwdMaxM): dWg[j][c] = bf16(sum_m dg[m][j] h[m][c])
-// and likewise dWu, the M terms added in order.  Workgroups own (row range, 512-column slab) tiles
-// as contract_kernel does; the slab of hidden for all M rows sits in LDS; per weight row, lane m
-// loads dg[m][j] and du[m][j] and readlane hands them to the whole wave.
-__global__ void __launch_bounds__(kBwdThreads)
-dw_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ dgm, const uint16_t* __restrict__ dum,
-          uint16_t* __restrict__ dwg, uint16_t* __restrict__ dwu, int M, int N, int K, int nslabs,
-          int rows_per_range)
-{
-    extern __shared__ u32x4_b hs[];  // [M][kSlab / 8] chunks of 8 bf16
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int slab = blockIdx.x % nslabs;
-    const int range = blockIdx.x / nslabs;
-    const int c0 = slab * kSlab + lane * 8;
-    const bool col_ok = c0 < K;
-    const int j_begin = range * rows_per_range;
-    const int j_end = min(j_begin + rows_per_range, N);
-    for (int i = threadIdx.x; i < M * kWave; i += kBwdThreads) {
-        const int m = i / kWave;
-        const int cc = slab * kSlab + (i - m * kWave) * 8;
-        hs[i] = cc < K ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + cc) : u32x4_b{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-    for (int j = j_begin + wave; j < j_end; j += kBwdWaves) {
-        const float dg_l = lane < M ? bf16_to_f32(dgm[(int64_t)lane * N + j]) : 0.0f;
-        const float du_l = lane < M ? bf16_to_f32(dum[(int64_t)lane * N + j]) : 0.0f;
-        float sg[8], su[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sg[e] = 0.0f;
-            su[e] = 0.0f;
-        }
-        for (int m = 0; m < M; ++m) {
-            const float dg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dg_l), m));
-            const float du = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, du_l), m));
-            const u32x4_b h4 = hs[m * kWave + lane];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sg[2 * q] = __builtin_fmaf(dg, bf16lo(h4[q]), sg[2 * q]);
-                sg[2 * q + 1] = __builtin_fmaf(dg, bf16hi(h4[q]), sg[2 * q + 1]);
-                su[2 * q] = __builtin_fmaf(du, bf16lo(h4[q]), su[2 * q]);
-                su[2 * q + 1] = __builtin_fmaf(du, bf16hi(h4[q]), su[2 * q + 1]);
-            }
-        }
-        if (!col_ok) continue;
-        u32x4_b pg, pu;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            pg[q] = (uint32_t)f32_to_bf16_rne(sg[2 * q]) | ((uint32_t)f32_to_bf16_rne(sg[2 * q + 1]) << 16);
-            pu[q] = (uint32_t)f32_to_bf16_rne(su[2 * q]) | ((uint32_t)f32_to_bf16_rne(su[2 * q + 1]) << 16);
-        }
-        __builtin_nontemporal_store(pg, reinterpret_cast<u32x4_b*>(dwg + (int64_t)j * K + c0));
-        __builtin_nontemporal_store(pu, reinterpret_cast<u32x4_b*>(dwu + (int64_t)j * K + c0));
     }
 }
 
@@ -687,23 +630,22 @@ namespace {
 using ContractFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                             uint16_t*, uint16_t*, float*, int, int, int, int);
 
-template <bool DW>
-ContractFn pick_contract_dw(int M)
+ContractFn pick_contract(int M)
 {
     switch (M) {
-    case 1: return contract_kernel<1, DW>;
-    case 2: return contract_kernel<2, DW>;
-    case 3: return contract_kernel<3, DW>;
-    case 4: return contract_kernel<4, DW>;
-    case 5: return contract_kernel<5, DW>;
-    case 6: return contract_kernel<6, DW>;
-    case 7: return contract_kernel<7, DW>;
-    case 8: return contract_kernel<8, DW>;
+    case 1: return contract_kernel<1>;
+    case 2: return contract_kernel<2>;
+    case 3: return contract_kernel<3>;
+    case 4: return contract_kernel<4>;
+    case 5: return contract_kernel<5>;
+    case 6: return contract_kernel<6>;
+    case 7: return contract_kernel<7>;
+    case 8: return contract_kernel<8>;
     default: return nullptr;
     }
 }
 
-ContractFn pick_contract(int M, bool dw) { return dw ? pick_contract_dw<true>(M) : pick_contract_dw<false>(M); }
+
 
 }  // namespace
 
@@ -769,7 +711,7 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     } else {
         p.off_partial = p.gu_bytes;
     }
-    p.partial_bytes = (int64_t)p.nranges * 2 * (p.path == kPathMfma ? M : (M < kBwdChunkM ? M : kBwdChunkM)) * K * 4;
+    p.partial_bytes = (int64_t)p.nranges * 2 * M * K * 4;  // every path keeps dh partials for all M rows
     p.workspace_bytes = p.gu_bytes + mfma_bytes + p.partial_bytes;
     // dh: within a wave its rows in order, then the waves of a workgroup, then every 16th partial,
     // then the 16 group sums
@@ -803,28 +745,16 @@ hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int 
     return hipGetLastError();
 }
 
-hipError_t contract_launch(const BwdPlan& p, int M, bool dw, const uint16_t* hidden, const uint16_t* gate_w,
+hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
                            const uint16_t* up_w, const uint16_t* dgm, const uint16_t* dum, uint16_t* dwg,
                            uint16_t* dwu, float* partial, int N, int K, hipStream_t stream)
 {
-    ContractFn fn = pick_contract(M, dw);
+    ContractFn fn = pick_contract(M);
     if (!fn || N < 1 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.nranges * p.nslabs;
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kBwdThreads), 0, stream, hidden, gate_w, up_w, dgm, dum, dwg,
                        dwu, partial, N, K, p.nslabs, p.rows_per_range);
-    return hipGetLastError();
-}
-
-hipError_t dw_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* dgm, const uint16_t* dum,
-                     uint16_t* dwg, uint16_t* dwu, int N, int K, hipStream_t stream)
-{
-    if (M < 1 || M > kBwdMaxM || N < 1 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
-    const int64_t grid = (int64_t)p.nranges * p.nslabs;
-    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidValue;
-    const size_t lds = (size_t)M * kSlab * sizeof(uint16_t);
-    hipLaunchKernelGGL(dw_kernel, dim3((unsigned)grid), dim3(kBwdThreads), lds, stream, hidden, dgm, dum, dwg, dwu, M,
-                       N, K, p.nslabs, p.rows_per_range);
     return hipGetLastError();
 }
 
