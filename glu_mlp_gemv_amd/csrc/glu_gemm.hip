@@ -35,8 +35,8 @@ __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 
 // BN: weight rows per tile (64 or 128); BM: hidden rows per tile (64 or 128).
 // KTAIL: K is not a multiple of 64 (chunks past K are read as zeros).
-// PF: stages whose global loads are in flight while a stage computes (1 or 2;
-// with 2, two register sets alternate and a stage's data has two stages of
+// PF: stages whose global loads are in flight while a stage computes (1 to 4;
+// from 2 on, PF register sets rotate and a stage's data has PF stages of
 // compute to arrive).
 // nbm: M tiles; the grid holds ceil(N / BN) * nbm workgroups.
 // LIN: write bf16(G) and bf16(U) instead of the GLU product: G to out, U to out + M ldo (the
@@ -91,8 +91,8 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
     }
 
     // a stage's loads land in a register set; ok: the chunk lies inside K (else it is stored as zeros)
-    u32x4_t pa[LPT], pb[LPT];
-    bool oka = true, okb = true;
+    u32x4_t P[PF][LPT];
+    bool okp[PF];
     auto gload = [&](int s, u32x4_t (&pf)[LPT], bool& ok) __attribute__((always_inline)) {
         const int kc = s * kStageChunks + c_ld;
         const int kcc = KTAIL ? min(kc, nchunks - 1) : kc;
@@ -148,35 +148,39 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
     };
 
     if constexpr (PF == 1) {
-        gload(0, pa, oka);
-        lstore(0, pa, oka);
+        gload(0, P[0], okp[0]);
+        lstore(0, P[0], okp[0]);
         __syncthreads();
         for (int s = 0; s < nstages; ++s) {
-            if (s + 1 < nstages) gload(s + 1, pa, oka);
+            if (s + 1 < nstages) gload(s + 1, P[0], okp[0]);
             compute(s & 1);
-            if (s + 1 < nstages) lstore((s + 1) & 1, pa, oka);
+            if (s + 1 < nstages) lstore((s + 1) & 1, P[0], okp[0]);
             __syncthreads();
         }
     } else {
-        // stage s's data sits in set s % 2: stage s + 2 is loaded into the set stage s just left
-        // (stored to LDS at the end of stage s - 1), stage s + 1's set is stored after stage s
-        auto step = [&](int s, u32x4_t (&cur)[LPT], bool& cur_ok, u32x4_t (&nxt)[LPT], bool nxt_ok)
-            __attribute__((always_inline)) {
-            if (s + 2 < nstages) gload(s + 2, cur, cur_ok);
+        // A ring of PF register sets: stage s's loads sit in set s % PF.  Stage s refills its own set
+        // (stored to LDS at the end of stage s - 1) with stage s + PF, computes, then stores stage
+        // s + 1's set into the other LDS buffer.  In the steady state every refill is live and
+        // nothing branches around a load, so the waits leave PF - 1 stages of loads in flight.
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            if (s < nstages) gload(s, P[s], okp[s]);
+        }
+        lstore(0, P[0], okp[0]);
+        __syncthreads();
+        auto stage = [&](auto Qc, auto tailc, int s) __attribute__((always_inline)) {
+            constexpr int Q = decltype(Qc)::value;
+            constexpr bool TAIL = decltype(tailc)::value;
+            if (!TAIL || s + PF < nstages) gload(s + PF, P[Q], okp[Q]);
             compute(s & 1);
-            if (s + 1 < nstages) lstore((s + 1) & 1, nxt, nxt_ok);
+            if (!TAIL || s + 1 < nstages) lstore((s + 1) & 1, P[(Q + 1) % PF], okp[(Q + 1) % PF]);
             __syncthreads();
         };
-        gload(0, pa, oka);
-        if (nstages > 1) gload(1, pb, okb);
-        lstore(0, pa, oka);
-        __syncthreads();
-        int s = 0;
-        for (; s + 1 < nstages; s += 2) {
-            step(s, pa, oka, pb, okb);
-            step(s + 1, pb, okb, pa, oka);
-        }
-        if (s < nstages) step(s, pa, oka, pb, okb);
+        auto steady = [&](auto Qc, int s) __attribute__((always_inline)) { stage(Qc, std::false_type{}, s); };
+        auto tail = [&](auto Qc, int s) __attribute__((always_inline)) { stage(Qc, std::true_type{}, s); };
+        int s0 = 0;
+        for (; s0 + 2 * PF <= nstages; s0 += PF) run_stages<0, PF>(steady, s0, nstages);
+        for (; s0 < nstages; s0 += PF) run_stages<0, PF>(tail, s0, nstages);
     }
 
     // lane l holds G and U of weight rows 4(l/16) + e, hidden row l % 16, of each 16 x 16 tile
@@ -229,6 +233,8 @@ GemmFn pick_tail(bool ktail, int pf)
 {
     if (pf == 1) return ktail ? gemm_kernel<BN, BM, true, 1> : gemm_kernel<BN, BM, false, 1>;
     if (pf == 2) return ktail ? gemm_kernel<BN, BM, true, 2> : gemm_kernel<BN, BM, false, 2>;
+    if (pf == 3) return ktail ? gemm_kernel<BN, BM, true, 3> : gemm_kernel<BN, BM, false, 3>;
+    if (pf == 4) return ktail ? gemm_kernel<BN, BM, true, 4> : gemm_kernel<BN, BM, false, 4>;
     return nullptr;
 }
 

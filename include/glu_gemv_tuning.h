@@ -34,7 +34,7 @@ typedef struct glu_tuning {
     int mfma_depth;       /* MFMA with mfma_hidden = 3: pipeline stages of weights kept
                              in flight (4 rows: 4 at 2 segments, 2 at 4; 8 rows: 2 or 4
                              at 4 segments, 1 or 2 at 8).  GEMM: stages of loads in
-                             flight while a stage computes (1 or 2) */
+                             flight while a stage computes (1 to 4) */
     int gemm_tile_n;      /* GEMM: weight rows per output tile (64 or 128) */
     int gemm_tile_m;      /* GEMM: hidden rows per output tile (64 or 128) */
 } glu_tuning;

@@ -27,4 +27,5 @@ GEMM_SHAPES = [(33, 200, 520), (64, 1000, 1024), (70, 333, 2560), (128, 300, 103
 GEMM_TILES = [dict(), dict(gemm_tile_n=64, gemm_tile_m=64), dict(gemm_tile_n=64, gemm_tile_m=128),
               dict(gemm_tile_n=128, gemm_tile_m=64), dict(gemm_tile_n=128, gemm_tile_m=128),
               dict(mfma_depth=1), dict(gemm_tile_n=64, gemm_tile_m=128, mfma_depth=1),
-              dict(gemm_tile_n=128, gemm_tile_m=128, mfma_depth=1)]
+              dict(gemm_tile_n=128, gemm_tile_m=128, mfma_depth=1), dict(mfma_depth=3), dict(mfma_depth=4),
+              dict(gemm_tile_n=64, gemm_tile_m=128, mfma_depth=3), dict(gemm_tile_n=64, gemm_tile_m=128, mfma_depth=4)]

@@ -326,8 +326,10 @@ def test_gemm_plans_and_overrides(lib):
     p = api.Plan()
     assert api.plan(64, 1000, 1024, True, api.make_tuning(kernel=api.KERNEL_GEMM, mfma_depth=1))["kernel_symbol"] \
         == "glu::gemm_kernel<64, 64, false, 1>"
+    assert api.plan(64, 1000, 1024, True, api.make_tuning(kernel=api.KERNEL_GEMM, mfma_depth=4))["kernel_symbol"] \
+        == "glu::gemm_kernel<64, 64, false, 4>"
     for bad in (dict(kernel=api.KERNEL_MFMA, gemm_tile_n=64), dict(kernel=api.KERNEL_GEMM, gemm_tile_n=96),
-                dict(kernel=api.KERNEL_GEMM, mfma_depth=3),
+                dict(kernel=api.KERNEL_GEMM, mfma_depth=5),
                 dict(kernel=api.KERNEL_GEMM, gemm_tile_m=32), dict(kernel=api.KERNEL_GEMM, mfma_segments=4),
                 dict(kernel=api.KERNEL_GEMM, grid=10), dict(kernel=api.KERNEL_GEMM, waves_per_block=2)):
         t = api.make_tuning(**bad)
