@@ -359,12 +359,13 @@ def dual_gemv_strided_raw(hidden_ptr: int, ldh: int, gate_ptr: int, ldg: int, up
 
 
 def grouped_plan(M: int, K: int, rows: int, fast: bool = True, tuning: Optional[Tuning] = None,
-                 mult4: bool = True) -> dict:
+                 mult4: bool = True, mult8: bool = False) -> dict:
     """The launch glu_grouped_gemv would make (host only): rows = sum of N over the projections,
-    ``fast`` whether the layout is a fast one, ``mult4`` whether every N is a multiple of 4."""
+    ``fast`` whether the layout is a fast one, ``mult4`` / ``mult8`` whether every N is a multiple
+    of 4 / of 8."""
     p = Plan()
     lib = library()
-    flags = int(fast) | (2 if mult4 else 0)
+    flags = int(fast) | (2 if mult4 else 0) | (4 if mult8 and mult4 else 0)
     if tuning is None:
         st = lib.glu_grouped_gemv_plan(M, K, rows, flags, ctypes.byref(p))
     else:

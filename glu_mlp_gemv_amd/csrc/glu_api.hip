@@ -29,6 +29,7 @@ constexpr int kValuDefaultWaves = 4;       // waves per workgroup
 constexpr int kValuWavesPerCU = 3;         // persistent waves per CU the grid aims for
 constexpr int kMfmaDefaultWaves = 4;
 constexpr int kMfmaWavesPerCU = 4;
+constexpr int kGrouped8MinM = 8;  // grouped MFMA: 8-row groups by default above this many rows of hidden
 constexpr int64_t kGemmSlice = 65536;        // rows of hidden per GEMM launch
 constexpr int64_t kGemmMaxN = 1 << 30;       // GEMM tile row indices stay in 32 bits
 constexpr int kMfmaSlice = 32;
@@ -349,11 +350,13 @@ glu_status run(const uint16_t* hidden, int64_t ldh, const uint16_t* gate_w, int6
 // ---- grouped GEMV ------------------------------------------------------------
 
 // Grouped GEMV launch.  `fast`: the layout meets the fast kernels' conditions;
-// `mult4`: every projection's row count is a multiple of 4.  M >= 2 (or a
-// forced MFMA) with both takes the block-diagonal MFMA kernel, M <= 32 per
-// launch; else the VALU kernel (at most 16 chunks per lane per row, K <= 8192,
-// M <= 8 per launch); else the generic kernel.
-glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult4, const glu_tuning* t, Launch* L)
+// `mult4` / `mult8`: every projection's row count is a multiple of 4 / 8.  M >= 2
+// (or a forced MFMA) with fast and mult4 takes the block-diagonal MFMA kernel,
+// M <= 32 per launch, in groups of 8 weight rows above 8 rows of hidden when
+// mult8 holds and hidden fits in LDS; else the VALU kernel (at most 16 chunks
+// per lane per row, K <= 8192, M <= 8 per launch); else the generic kernel.
+glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult4, bool mult8, const glu_tuning* t,
+                        Launch* L)
 {
     if (M < 0 || K < 0 || rows < 0 || M > kMaxDim || K > kMaxDim || rows > kMaxDim) return GLU_ERR_BAD_SHAPE;
     const int64_t lim = INT64_MAX / 2;
@@ -375,7 +378,9 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
     if (forced == GLU_KERNEL_MFMA && !mfma) return GLU_ERR_UNSUPPORTED;
     if (mfma_fields && !mfma) return GLU_ERR_UNSUPPORTED;
     if (mfma) {
-        if (t && (t->mfma_depth || t->rows_per_wave)) return GLU_ERR_UNSUPPORTED;
+        if (t && (t->mfma_depth || (t->rows_per_wave && t->rows_per_wave != 4 && t->rows_per_wave != 8))) {
+            return GLU_ERR_UNSUPPORTED;
+        }
         if (rows % 4 != 0) return GLU_ERR_UNSUPPORTED;  // whole 4-row groups only
         glu::MfmaConfig c{};
         const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
@@ -383,6 +388,38 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
         c.MT4 = (int)((m_pl + 3) / 4);
         const int64_t nchunks = K / 8;
         const int64_t nsegs = ceil_div(nchunks, 16);
+        // 8 weight rows per group (the 8-row layout) above 8 rows of hidden held in LDS: half the
+        // MFMAs and LDS operand reads per weight byte (K=2560, a 63 MB quad: 18.3 -> 16.8 us at
+        // M = 16, 31.1 -> 21.6 at M = 32)
+        const bool can8 = mult8 && m_pl > 8 && nchunks % 16 == 0 && (!t || !t->mfma_hidden || t->mfma_hidden == 1) &&
+                          glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsMax;
+        const int rows_req = t ? t->rows_per_wave : 0;
+        if (rows_req == 8 && !can8) return GLU_ERR_UNSUPPORTED;
+        if (can8 && (rows_req == 8 || (rows_req == 0 && m_pl > kGrouped8MinM))) {
+            const int64_t nsegs8 = nchunks / 8;
+            c.rows = 8;
+            c.MT4 = (int)((m_pl + 7) / 8);
+            c.hidden = glu::kHiddenLds;
+            c.U = (t && t->mfma_segments) ? t->mfma_segments : (nsegs8 % 8 == 0 || nsegs8 % 5 != 0 ? 8 : 5);
+            if (c.U < 1) return GLU_ERR_UNSUPPORTED;
+            c.nsg = (int)ceil_div(nsegs8, c.U);
+            c.ragged = (int64_t)c.nsg * c.U * 8 != nchunks;
+            const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
+            if (waves < 1 || waves * glu::kWave > glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
+            c.block = waves * glu::kWave;
+            const bool two_fit = 2 * glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsMax;
+            const int64_t per_cu = two_fit ? 2 * kMfmaWavesPerCU : kMfmaWavesPerCU;
+            const int64_t grid = (t && t->grid > 0) ? t->grid
+                                                    : ceil_div(balanced_waves(rows / 8, (int64_t)kCUs * per_cu), waves);
+            c.grid = (int)(grid < 1 ? 1 : grid);
+            if (!glu::grouped_mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
+            L->kernel = GLU_KERNEL_MFMA;
+            L->mfma = c;
+            L->m_per_launch = (int)m_pl;
+            L->launches = (int)ceil_div(M, m_pl);
+            L->accum_depth = (int)(2 * (nsegs8 + 5 + 2));
+            return GLU_OK;
+        }
         if (t && t->mfma_hidden) {
             c.hidden = t->mfma_hidden - 1;
         } else {
@@ -473,7 +510,7 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         rows += proj[i].N;
     }
     Launch L;
-    glu_status st = plan_grouped(M, K, rows, false, false, nullptr, &L);  // shape errors first
+    glu_status st = plan_grouped(M, K, rows, false, false, false, nullptr, &L);  // shape errors first
     if (st != GLU_OK) return st;
     if (M == 0 || rows == 0) return GLU_OK;
     // strides and extents
@@ -511,13 +548,14 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         }
     }
     bool fast = (a16 & 15u) == 0 && K % 8 == 0 && (ldh & 7) == 0 && ldh <= kMaxFastK;
-    bool mult4 = true;
+    bool mult4 = true, mult8 = true;
     glu::GroupDesc d{};
     for (int i = 0; i < n; ++i) {
         const glu_projection& p = proj[i];
         if (p.N == 0) continue;
         fast = fast && (p.ldw & 7) == 0 && p.ldw <= kMaxFastK;
         mult4 = mult4 && p.N % 4 == 0;
+        mult8 = mult8 && p.N % 8 == 0;
         d.w[d.n] = p.weight;
         d.out[d.n] = p.out;
         d.ldw[d.n] = p.ldw;
@@ -527,7 +565,7 @@ glu_status run_grouped(const uint16_t* hidden, int64_t ldh, const glu_projection
         ++d.n;
     }
     d.row0[d.n] = d.rows;
-    st = plan_grouped(M, K, rows, fast, mult4, t, &L);
+    st = plan_grouped(M, K, rows, fast, mult4, mult8, t, &L);
     if (st != GLU_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
@@ -738,7 +776,7 @@ glu_status glu_grouped_gemv_plan_tuned(int64_t M, int64_t K, int64_t rows, int f
 {
     if (!plan) return GLU_ERR_NULL_POINTER;
     Launch L;
-    const glu_status st = plan_grouped(M, K, rows, (fast & 1) != 0, (fast & 2) != 0, tuning, &L);
+    const glu_status st = plan_grouped(M, K, rows, (fast & 1) != 0, (fast & 2) != 0, (fast & 4) != 0, tuning, &L);
     if (st != GLU_OK) return st;
     fill_plan(L, plan);
     if (L.kernel == GLU_KERNEL_GENERIC) plan->block = glu::kGroupedGenericWaves * glu::kWave;
@@ -776,7 +814,9 @@ void describe_launch(const Launch& L, bool grouped, char* buf, int len)
     }
     case GLU_KERNEL_MFMA: {
         const glu::MfmaConfig& c = L.mfma;
-        if (grouped) {
+        if (grouped && c.rows == 8) {
+            snprintf(buf, (size_t)len, "glu::grouped_mfma_kernel<%d, %d, true, %s, 8>", c.MT4, c.U, tf[c.ragged]);
+        } else if (grouped) {
             snprintf(buf, (size_t)len, "glu::grouped_mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,
                      tf[c.hidden == glu::kHiddenLds], tf[c.ragged]);
         } else if (c.hidden == glu::kHiddenSlices && c.rows == 8) {
@@ -824,7 +864,7 @@ glu_status glu_grouped_gemv_describe(int64_t M, int64_t K, int64_t rows, int fas
     if (!buf || len < 1) return GLU_ERR_NULL_POINTER;
     buf[0] = '\0';
     Launch L;
-    const glu_status st = plan_grouped(M, K, rows, (fast & 1) != 0, (fast & 2) != 0, tuning, &L);
+    const glu_status st = plan_grouped(M, K, rows, (fast & 1) != 0, (fast & 2) != 0, (fast & 4) != 0, tuning, &L);
     if (st != GLU_OK) return st;
     describe_launch(L, true, buf, len);
     return GLU_OK;

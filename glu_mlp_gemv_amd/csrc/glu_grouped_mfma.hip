@@ -1,5 +1,6 @@
-// Grouped GEMV at batch M >= 2: the block-diagonal MFMA layout of the dual
-// kernel (glu_mfma.hip) with one weight stream.
+// Grouped GEMV at batch M >= 2: the block-diagonal MFMA layouts of the dual
+// kernels (glu_mfma.hip: 4 rows x 4 blocks; glu_mfma8.hip: 8 rows x 2 blocks,
+// here for 8 < M <= 32 with hidden in LDS) with one weight stream.
 //
 // The virtual row space of the n projections (glu_grouped.hip) is cut into
 // groups of 4 rows; every projection's row count is a multiple of 4, so a
@@ -44,14 +45,19 @@ __device__ __forceinline__ GroupRef group_ref(const GroupDesc& d, int row)
 
 }  // namespace
 
-// MT4: hidden-row tiles of 4 (M <= 4*MT4); U: 128-element segments per stage;
-// nsg: stages per group (nsg*U*16 >= K/8, equality unless RAGGED); d.rows % 4 == 0.
+// ROWS = 4: MT4 hidden-row tiles of 4 (M <= 4*MT4), U segments of 128 elements per stage, 4 weight
+// rows x 4 K-blocks per MFMA.  ROWS = 8 (hidden in LDS, K/8 a multiple of 16): MT4 tiles of 8
+// hidden rows (M <= 8*MT4), U segments of 64 elements, 8 weight rows x 2 K-blocks per MFMA as in
+// the dual kernel's 8-row layout (half of D useful: per weight byte half the MFMAs and LDS reads).
+// nsg: stages per group (nsg*U*segment >= K/8, equality unless RAGGED); d.rows % ROWS == 0.
 // Dynamic LDS when HLDS: M * K * 2 bytes, or M * (K/8 + 1) * 16 when K/8 is not a multiple of 4
 // (up to the 160 KiB of one workgroup: M = 32 at K = 2560).
-template <int MT4, int U, bool HLDS, bool RAGGED>
+template <int MT4, int U, bool HLDS, bool RAGGED, int ROWS = 4>
 __global__ void __launch_bounds__(kMfmaMaxThreads)
 grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int K, GroupDesc d, int nsg)
 {
+    static_assert(ROWS == 4 || (ROWS == 8 && HLDS), "8 rows per group with hidden in LDS only");
+    constexpr int SEGC = ROWS == 4 ? 16 : 8;  // 16-byte chunks of a row per segment
     extern __shared__ u32x4_t h_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
@@ -60,8 +66,11 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
     const int nchunks = K >> 3;
     const uint32_t ldh8 = (uint32_t)(ldh >> 3);
     const int i16 = lane & 15;
-    const int rho_a = i16 >> 2;                     // weight row of this lane's A data
-    const int cseg = (i16 & 3) * 4 + (lane >> 4);   // 16-byte chunk within a 256-byte segment
+    // weight row of this lane's A data (also its hidden row within a tile) and its 16-byte chunk of
+    // a segment: 4 rows x 4 blocks of 32, or 8 rows x 2 blocks
+    const int rho_a = ROWS == 4 ? i16 >> 2 : i16 >> 1;
+    const int cseg = ROWS == 4 ? (i16 & 3) * 4 + (lane >> 4) : (i16 & 1) * 4 + (lane >> 4);
+    auto swz = [](int r) __attribute__((always_inline)) { return ROWS == 4 ? lds_swz4(r) : lds_swz8(r); };
     const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
 
     const bool hswz = (nchunks & 3) == 0;
@@ -84,21 +93,21 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
                 if (i < total) {
                     const int m = i / nchunks;
                     const int c = i - m * nchunks;
-                    h_lds[m * hpitch + (hswz ? c ^ lds_swz4(m) : c)] = v[q];
+                    h_lds[m * hpitch + (hswz ? c ^ swz(m) : c)] = v[q];
                 }
             }
         }
         __syncthreads();
     }
 
-    const int ngroups = d.rows / 4;
+    const int ngroups = d.rows / ROWS;
     if (wave_id >= ngroups) return;  // no barrier follows
     const int my_groups = (ngroups - 1 - wave_id) / nwaves + 1;
     const int nstages = my_groups * nsg;
 
     int hrow[MT4];  // hidden rows of this lane's B data (rows past M repeat row M-1, never stored)
 #pragma unroll
-    for (int t = 0; t < MT4; ++t) hrow[t] = min(4 * t + rho_a, M - 1);
+    for (int t = 0; t < MT4; ++t) hrow[t] = min(ROWS * t + rho_a, M - 1);
 
     constexpr int BT = HLDS ? 1 : MT4;
     constexpr int BU = HLDS ? 1 : U;
@@ -106,14 +115,14 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
     auto load = [&](int s, u32x4_t (&A)[U], u32x4_t (&Bq)[BT][BU]) {
         const int gi = s / nsg;
         const int sb = s - gi * nsg;
-        const GroupRef ref = group_ref(d, 4 * (wave_id + gi * nwaves));
+        const GroupRef ref = group_ref(d, ROWS * (wave_id + gi * nwaves));
         const char* wp = reinterpret_cast<const char*>(ref.w);
         const uint32_t ldw8 = (uint32_t)(ref.ldw >> 3);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int c = (sb * U + u) * 16 + cseg;
+            int c = (sb * U + u) * SEGC + cseg;
             if (RAGGED) c = min(c, nchunks - 1);
-            const uint32_t off = ((uint32_t)rho_a * ldw8 + (uint32_t)c) * 16u;  // bytes, below 4 rows at the stride
+            const uint32_t off = ((uint32_t)rho_a * ldw8 + (uint32_t)c) * 16u;  // bytes, below ROWS rows at the stride
             A[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + off));
         }
         if constexpr (!HLDS) {
@@ -121,7 +130,7 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
             for (int t = 0; t < MT4; ++t) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    int c = (sb * U + u) * 16 + cseg;
+                    int c = (sb * U + u) * SEGC + cseg;
                     if (RAGGED) c = min(c, nchunks - 1);
                     const uint32_t off = ((uint32_t)hrow[t] * ldh8 + (uint32_t)c) * 16u;
                     Bq[t][u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(hidden) + off);
@@ -133,6 +142,23 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
     f32x4_t acc[MT4];
 
     auto finish_group = [&](int g) {
+        if constexpr (ROWS == 8) {
+            // lanes l and l^1 hold the two blocks of the same (weight row, hidden row) pairs:
+            // entries l%2 (weight row 2(l/16)) and 2 + l%2 (row 2(l/16) + 1); one DPP step adds them
+            const bool odd = (lane & 1) != 0;
+            const int row = 8 * g + 2 * (lane >> 4) + (lane & 1);
+#pragma unroll
+            for (int t = 0; t < MT4; ++t) {
+                const f32x4_t dd = acc[t];
+                float v0 = odd ? dd[1] : dd[0];
+                float v1 = odd ? dd[3] : dd[2];
+                v0 = dpp_add<0xB1>(v0);  // lane ^ 1
+                v1 = dpp_add<0xB1>(v1);
+                const int m = 8 * t + (i16 >> 1);
+                if (m < M) group_store(d, m, row, f32_to_bf16_rne(odd ? v1 : v0));
+            }
+            return;
+        }
         // useful entry e = lane % 4, then the quad sum over the four blocks
         const int e = lane & 3;
         float res[(MT4 + 3) / 4];
@@ -164,7 +190,7 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
         const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = (sb * U + u) * 16 + cseg;
+            const int c = (sb * U + u) * SEGC + cseg;
             const bool ok = !RAGGED || c < nchunks;
             const int cc = RAGGED ? min(c, nchunks - 1) : c;
             const u32x4_t a = RAGGED ? (ok ? A[u] : z) : A[u];
@@ -172,7 +198,7 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
             for (int t = 0; t < MT4; ++t) {
                 u32x4_t b;
                 if constexpr (HLDS) {
-                    b = h_lds[hrow[t] * hpitch + (hswz ? cc ^ lds_swz4(hrow[t]) : cc)];
+                    b = h_lds[hrow[t] * hpitch + (hswz ? cc ^ swz(hrow[t]) : cc)];
                 } else {
                     b = Bq[t][u];
                 }
@@ -221,6 +247,27 @@ GroupedMfmaFn pick_u(int U)
     }
 }
 
+// 8 rows per group: tiles of 8 hidden rows (MT8 = 2 to 4: 8 < M <= 32), hidden in LDS
+template <int MT8, bool RG>
+GroupedMfmaFn pick8_u(int U)
+{
+    switch (U) {
+    case 5: return grouped_mfma_kernel<MT8, 5, true, RG, 8>;
+    case 8: return grouped_mfma_kernel<MT8, 8, true, RG, 8>;
+    default: return nullptr;
+    }
+}
+
+GroupedMfmaFn pick8(int mt8, int U, bool ragged)
+{
+    switch (mt8) {
+    case 2: return ragged ? pick8_u<2, true>(U) : pick8_u<2, false>(U);
+    case 3: return ragged ? pick8_u<3, true>(U) : pick8_u<3, false>(U);
+    case 4: return ragged ? pick8_u<4, true>(U) : pick8_u<4, false>(U);
+    default: return nullptr;
+    }
+}
+
 template <int MT4>
 GroupedMfmaFn pick_flags(int U, bool hlds, bool ragged)
 {
@@ -247,17 +294,25 @@ GroupedMfmaFn pick(int mt4, int U, bool hlds, bool ragged)
 
 bool grouped_mfma_supported(const MfmaConfig& c)
 {
-    if (c.rows != 4 || (c.hidden != kHiddenLds && c.hidden != kHiddenL2)) return false;
     if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
+    if (c.rows == 8) return c.hidden == kHiddenLds && pick8(c.MT4, c.U, c.ragged) != nullptr;
+    if (c.rows != 4 || (c.hidden != kHiddenLds && c.hidden != kHiddenL2)) return false;
     return pick(c.MT4, c.U, c.hidden == kHiddenLds, c.ragged) != nullptr;
 }
 
 hipError_t grouped_mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, int64_t ldh, int64_t K,
                                const GroupDesc& d, hipStream_t stream)
 {
-    const int mt4 = (M + 3) / 4;
     const bool hlds = c.hidden == kHiddenLds;
-    GroupedMfmaFn fn = pick(mt4, c.U, hlds, c.ragged);
+    GroupedMfmaFn fn;
+    if (c.rows == 8) {
+        // the 8-row layout's XOR swizzle permutes 16-chunk blocks of a row of hidden in LDS
+        if (!hlds || (K / 8) % 16 != 0 || d.rows % 8 != 0) return hipErrorInvalidValue;
+        // a last slice of 8 rows or fewer runs on 2 tiles: padded rows repeat row M - 1, never stored
+        fn = pick8(M <= 8 ? 2 : (M + 7) / 8, c.U, c.ragged);
+    } else {
+        fn = pick((M + 3) / 4, c.U, hlds, c.ragged);
+    }
     if (!fn || M < 1 || d.rows % 4 != 0) return hipErrorInvalidValue;
     const size_t lds = hlds ? mfma_hidden_lds_bytes(M, K) : 0;
     if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;

@@ -184,7 +184,8 @@ glu_status glu_grouped_gemv(const uint16_t* hidden, int64_t ldh, const glu_proje
  * The launch glu_grouped_gemv would make for M rows of hidden, K, and `rows`
  * = sum of N over the projections (host only, no HIP call).  `fast` is a
  * bit set: 1 = the layout is a fast layout (above), 2 = every N is a
- * multiple of 4.
+ * multiple of 4, 4 = every N is a multiple of 8 (above 8 rows of hidden
+ * held in LDS the MFMA kernel then takes groups of 8 weight rows).
  */
 glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, glu_plan* plan);
 

@@ -291,6 +291,20 @@ def test_grouped_plans():
     # hidden in LDS up to one workgroup's 160 KiB (32 rows at K = 2560), else read through L2
     assert api.grouped_plan(16, 2560, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<4, 5, true, false>"
     assert api.grouped_plan(32, 2560, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 5, true, false>"
+    # every N a multiple of 8, above 8 rows of hidden in LDS: groups of 8 weight rows
+    assert api.grouped_plan(32, 2560, 104, mult8=True)["kernel_symbol"] == \
+        "glu::grouped_mfma_kernel<4, 8, true, false, 8>"
+    assert api.grouped_plan(17, 2176, 104, mult8=True)["kernel_symbol"] == \
+        "glu::grouped_mfma_kernel<3, 8, true, true, 8>"
+    assert api.grouped_plan(16, 2560, 104, mult8=True)["kernel_symbol"] == \
+        "glu::grouped_mfma_kernel<2, 8, true, false, 8>"
+    assert api.grouped_plan(8, 2560, 104, mult8=True)["kernel_symbol"] == "glu::grouped_mfma_kernel<2, 5, true, false>"
+    assert api.grouped_plan(32, 2568, 104, mult8=True)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 2, false, true>"
+    t8 = api.make_tuning(rows_per_wave=4)
+    assert api.grouped_plan(32, 2560, 104, tuning=t8, mult8=True)["kernel_symbol"] == \
+        "glu::grouped_mfma_kernel<8, 5, true, false>"
+    with pytest.raises(api.GluError):
+        api.grouped_plan(32, 2560, 104, tuning=api.make_tuning(rows_per_wave=8))  # not every N a multiple of 8
     assert api.grouped_plan(32, 2568, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 2, false, true>"
     # otherwise the VALU kernel in slices of 8
     p = api.grouped_plan(9, 2560, 100, mult4=False)
@@ -309,6 +323,7 @@ def test_grouped_plans():
         with pytest.raises(api.GluError):
             api.grouped_plan(4, 64, 100, tuning=api.make_tuning(kernel=api.KERNEL_MFMA), **bad)
     for bad in (dict(mfma_depth=2), dict(mfma_segments=3), dict(mfma_hidden=3), dict(rows_per_wave=8),
+                dict(rows_per_wave=2),
                 dict(kernel=api.KERNEL_MFMA, mfma_segments=4, mfma_hidden=2)):
         with pytest.raises(api.GluError):
             api.grouped_plan(4, 2560, 100, tuning=api.make_tuning(**bad))

@@ -55,7 +55,7 @@ def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
     if diff.size:
         fwd = oracle.dual_gemv(hb, gb, ub, with_pre=True)
         # G and U come from the grouped GEMV or from the backward's one-pass kernel
-        depth = max(api.grouped_plan(M, K, 2 * N, True, None, N % 4 == 0)["accum_depth"],
+        depth = max(api.grouped_plan(M, K, 2 * N, True, None, N % 4 == 0, N % 8 == 0)["accum_depth"],
                     api.backward_plan(M, N, K)["accum_depth"])
         for m, j in diff:
             g_set = check.admissible_bf16_set(fwd.gate_pre[m, j], fwd.gate_abs[m, j], depth, K)

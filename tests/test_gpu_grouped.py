@@ -40,7 +40,8 @@ def check_all(h, ws, outs, tuning=None, fast=True, label=""):
     M, K = h.shape
     rows = sum(w.shape[0] for w in ws)
     mult4 = all(w.shape[0] % 4 == 0 for w in ws)
-    plan = api.grouped_plan(M, K, rows, fast, tuning, mult4)
+    mult8 = all(w.shape[0] % 8 == 0 for w in ws)
+    plan = api.grouped_plan(M, K, rows, fast, tuning, mult4, mult8)
     print(f"[grouped] {label} M={M} K={K} Ns={[w.shape[0] for w in ws]} plan={plan}", flush=True)
     reps = []
     for i, (w, o) in enumerate(zip(ws, outs)):
@@ -86,6 +87,17 @@ CASES = [
     ((1, 1), 520, 2, {}),                     # fewer rows than one 4-row group, M >= 2
     ((2,), 520, 5, {}),
     ((3,), 64, 33, {}),
+    # groups of 8 weight rows above 8 rows of hidden held in LDS (every N a multiple of 8)
+    ((2048, 1024, 32, 32), 2560, 9, {}),      # two 8-row tiles, the second mostly padding
+    ((1024, 256), 1024, 33 + 8, {}),          # slices of 32 and 9 rows, both in 8-row groups
+    ((8192, 4096, 32, 32), 2560, 32, {}),     # GDN-input-like quad
+    ((4096, 1024, 1024), 2560, 17, {}),       # three 8-row tiles, the third mostly padding
+    ((2048, 1024, 32, 32), 1024, 24, {}),
+    ((1024, 512, 8), 2176, 32, {}),           # ragged stages (34 segments of 64 in stages of 8)
+    ((1024, 512, 8), 2176, 20, dict(mfma_segments=5)),
+    ((4096, 1024, 1024), 2560, 32, dict(rows_per_wave=4)),  # the 4-row layout on request
+    ((1024, 1032), 2560, 32, {}),             # 1032 = 8 x 129 rows
+    ((1024, 256), 1024, 40, {}),              # slices of 32 (8-row groups) and of 8 rows
 ]
 
 
