@@ -125,7 +125,8 @@ def test_grouped_generic_layouts():
         check_all(h, ws, [o.cpu() for o in outs], fast=False, label=f"generic K={K} pad={pad}")
 
 
-STRIDED = [((700, 130, 64), 4), ((700, 132, 64), 4), ((700, 132, 64), 16)]
+STRIDED = [((700, 130, 64), 4), ((700, 132, 64), 4), ((700, 132, 64), 16),
+           ((704, 136, 64), 16), ((704, 136, 64), 32)]  # every N a multiple of 8: the 8-row groups
 
 
 @pytest.mark.parametrize("Ns,M", STRIDED)
