@@ -655,7 +655,7 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + bp.off_partial);
     if (bp.path == glu::kPathFused1 || bp.path == glu::kPathSplitK) {
         e = bp.path == glu::kPathFused1
-                ? glu::fused1_launch(bp, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K, s)
+                ? glu::fused1_launch(bp, (int)M, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K, s)
                 : glu::splitk_launch(bp, (int)M, hidden, gate_w, up_w, dout, gu, dwg, dwu, partial, (int)N, (int)K,
                                      s);
         if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, (int)M, (int)K, s);

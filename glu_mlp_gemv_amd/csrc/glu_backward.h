@@ -12,7 +12,10 @@ constexpr int kBwdTargetBlocks = 512;  // contraction workgroups aimed for (2 pe
 constexpr int kFusedMaxU = 5;        // one-pass kernel: up to 5 16-byte chunks per lane (K <= 2560)
 constexpr int kFusedWaves = 4;       // waves per workgroup of the one-pass kernel
 // persistent waves per CU it aims for: 8, or 4 at 5 chunks per lane (over 256 registers a wave)
-constexpr int fused_waves_per_cu(int U) { return U >= 5 ? 4 : 8; }
+constexpr int kFusedMaxM = 2;        // one-pass kernel: up to 2 rows of hidden (with 3 the four-launch
+                                      // path measured faster: 57.7 against 68.0 us at K=2048 N=8192)
+constexpr int fused_max_u(int M) { return M <= 2 ? kFusedMaxU : 0; }
+constexpr int fused_waves_per_cu(int M, int U) { return M == 1 && U < 5 ? 8 : 4; }
 constexpr int kCUsForPlan = 256;     // MI355X compute units
 
 constexpr int kSplitMaxWaves = 8;     // K-split kernel: waves per workgroup at most (256 VGPRs a lane)
@@ -65,7 +68,7 @@ hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, cons
                            const uint16_t* up_w, const uint16_t* dgm, const uint16_t* dum, uint16_t* dwg,
                            uint16_t* dwu, float* partial, int N, int K, hipStream_t stream);
 // weight gradients over all M <= kBwdMaxM rows of hidden
-hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+hipError_t fused1_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                         const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial, int N, int K,
                         hipStream_t stream);
 hipError_t splitk_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,

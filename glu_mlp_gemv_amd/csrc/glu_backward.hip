@@ -8,7 +8,7 @@
 //   ds = bf16(dout u), du = bf16(dout s), dg = bf16(silu'(g) ds) in fp32,
 //   dh = bf16(fp32(bf16(dg Wg) + bf16(du Wu))), dWg = bf16(dg^T h), dWu = bf16(du^T h).
 //
-// M = 1 with K <= 2560: one pass (fused1_kernel, below) reads each row of Wg
+// M <= 2 with K <= 2560: one pass (fused1_kernel, below) reads each row of Wg
 // and Wu once, forms G and U, dg and du, writes the row of dWg and dWu and
 // accumulates dh, then dh_reduce_kernel adds the workgroups' partials.
 // M <= 4 with 2560 < K <= 4096 (K <= 8192 for M <= 3): also one pass
@@ -441,47 +441,58 @@ splitk_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
     }
 }
 
-// One pass for M = 1 (K <= 64 * 8 * U): wave w owns rows w, w + W, ... (W waves in the grid).
-// Lane l holds 16-byte chunks l, l + 64, ... of its row of Wg and Wu and of hidden.  Per row:
-// G and U (fp32 fma per lane, wave butterfly), dg and du (act_grad, all lanes; lane 0 stores them
-// at the workspace head), the row of dWg and dWu (dg * h and du * h, one rounding each), and dh's
-// two contributions accumulated per lane.  The workgroup's waves then add their dh sums in LDS in
-// order 0, 1, ..., and the sum becomes the workgroup's partial: partial[b][2][K].
-template <int U, int WAVES>
+// One pass for M <= 2 rows of hidden (K <= 64 * 8 * U): wave w owns weight rows w, w + W, ... (W
+// waves in the grid).  Lane l holds 16-byte chunks l, l + 64, ... of its row of Wg and Wu and of every
+// row of hidden.  Per weight row j: G and U for each hidden row m (fp32 fma per lane, wave
+// butterfly); dg and du (act_grad; above M = 1 lane m forms row m's pair and readlane hands it to
+// the wave, lanes 0 .. M-1 store them at the workspace head); the row of dWg and dWu (the M products
+// dg[m] h[m] added in order, one rounding); and dh's two contributions accumulated per lane.  The
+// workgroup's waves then add their dh sums in LDS in order 0, 1, ..., and the sum becomes the
+// workgroup's partial: partial[b][2][M][K].
+template <int M, int U, int WAVES>
 __global__ void __launch_bounds__(WAVES * kWave)
 fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
               const uint16_t* __restrict__ up_w, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dgu,
               uint16_t* __restrict__ dwg, uint16_t* __restrict__ dwu, float* __restrict__ partial, int N, int K)
 {
-    extern __shared__ float red1[];  // [2][K]
+    extern __shared__ float red1[];  // [2][M][K]
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + wave);
     const int nwaves = gridDim.x * WAVES;
     const int nchunks = K >> 3;
+    const int64_t MN = (int64_t)M * N, MK = (int64_t)M * K;
 
-    u32x4_b hw[U];
+    u32x4_b hw[M][U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = lane + kWave * u;
         ok[u] = c < nchunks;
-        hw[u] = ok[u] ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)c * 8) : u32x4_b{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            hw[m][u] = ok[u] ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + (int64_t)c * 8)
+                             : u32x4_b{0u, 0u, 0u, 0u};
+        }
     }
-    float ag[U][8], au[U][8];
+    float ag[M][U][8], au[M][U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int m = 0; m < M; ++m) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            ag[u][e] = 0.0f;
-            au[u][e] = 0.0f;
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ag[m][u][e] = 0.0f;
+                au[m][u][e] = 0.0f;
+            }
         }
     }
 
-    // a row's loads: its chunks of Wg and Wu and its upstream gradient (issued together, so waiting
+    // a row's loads: its chunks of Wg and Wu and its upstream gradients (issued together, so waiting
     // for one row never waits for the next row's prefetch)
-    auto load_row = [&](int j, u32x4_b (&wg)[U], u32x4_b (&wu)[U], uint16_t& go) __attribute__((always_inline)) {
-        go = dout[j];
+    auto load_row = [&](int j, u32x4_b (&wg)[U], u32x4_b (&wu)[U], uint16_t (&go)[M]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) go[m] = dout[(int64_t)m * N + j];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = min(lane + kWave * u, nchunks - 1);  // past K: re-read a valid chunk, zeroed below
@@ -489,8 +500,13 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             wu[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_b*>(up_w + (int64_t)j * K + c * 8));
         }
     };
-    auto process = [&](int j, u32x4_b (&wg)[U], u32x4_b (&wu)[U], uint16_t go) __attribute__((always_inline)) {
-        float pg = 0.0f, pu = 0.0f;
+    auto process = [&](int j, u32x4_b (&wg)[U], u32x4_b (&wu)[U], const uint16_t (&go)[M]) __attribute__((always_inline)) {
+        float pg[M], pu[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            pg[m] = 0.0f;
+            pu[m] = 0.0f;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const u32x4_b z = {0u, 0u, 0u, 0u};
@@ -499,35 +515,76 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             wg[u] = g4;
             wu[u] = u4;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                pg = __builtin_fmaf(bf16lo(hw[u][q]), bf16lo(g4[q]), pg);
-                pg = __builtin_fmaf(bf16hi(hw[u][q]), bf16hi(g4[q]), pg);
-                pu = __builtin_fmaf(bf16lo(hw[u][q]), bf16lo(u4[q]), pu);
-                pu = __builtin_fmaf(bf16hi(hw[u][q]), bf16hi(u4[q]), pu);
+            for (int m = 0; m < M; ++m) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pg[m] = __builtin_fmaf(bf16lo(hw[m][u][q]), bf16lo(g4[q]), pg[m]);
+                    pg[m] = __builtin_fmaf(bf16hi(hw[m][u][q]), bf16hi(g4[q]), pg[m]);
+                    pu[m] = __builtin_fmaf(bf16lo(hw[m][u][q]), bf16lo(u4[q]), pu[m]);
+                    pu[m] = __builtin_fmaf(bf16hi(hw[m][u][q]), bf16hi(u4[q]), pu[m]);
+                }
             }
         }
-        const float G = wave_sum(pg);
-        const float Uv = wave_sum(pu);
-        uint16_t dgb, dub;
-        act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)), bf16_to_f32(go), &dgb, &dub);
-        if (lane == 0) {
-            dgu[j] = dgb;
-            dgu[N + j] = dub;
+        float dg[M], du[M];
+        if constexpr (M == 1) {
+            const float G = wave_sum(pg[0]);
+            const float Uv = wave_sum(pu[0]);
+            uint16_t dgb, dub;
+            act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)), bf16_to_f32(go[0]), &dgb,
+                     &dub);
+            if (lane == 0) {
+                dgu[j] = dgb;
+                dgu[N + j] = dub;
+            }
+            dg[0] = bf16_to_f32(dgb);
+            du[0] = bf16_to_f32(dub);
+        } else {
+            // lane m takes hidden row m's sums and upstream gradient, forms its (dg, du) and stores it;
+            // readlane then hands every row's pair to the whole wave
+            float Gm = 0.0f, Um = 0.0f;
+            uint16_t gom = 0;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float G = wave_sum(pg[m]);
+                const float Uv = wave_sum(pu[m]);
+                Gm = lane == m ? G : Gm;
+                Um = lane == m ? Uv : Um;
+                gom = lane == m ? go[m] : gom;
+            }
+            uint16_t dgb = 0, dub = 0;
+            if (lane < M) {
+                act_grad(bf16_to_f32(f32_to_bf16_rne(Gm)), bf16_to_f32(f32_to_bf16_rne(Um)), bf16_to_f32(gom), &dgb,
+                         &dub);
+                dgu[(int64_t)lane * N + j] = dgb;
+                dgu[MN + (int64_t)lane * N + j] = dub;
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                dg[m] = bf16_to_f32((uint16_t)__builtin_amdgcn_readlane((int)dgb, m));
+                du[m] = bf16_to_f32((uint16_t)__builtin_amdgcn_readlane((int)dub, m));
+            }
         }
-        const float dg = bf16_to_f32(dgb);
-        const float du = bf16_to_f32(dub);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             u32x4_b og, ou;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float h0 = bf16lo(hw[u][q]), h1 = bf16hi(hw[u][q]);
-                og[q] = (uint32_t)f32_to_bf16_rne(dg * h0) | ((uint32_t)f32_to_bf16_rne(dg * h1) << 16);
-                ou[q] = (uint32_t)f32_to_bf16_rne(du * h0) | ((uint32_t)f32_to_bf16_rne(du * h1) << 16);
-                ag[u][2 * q] = __builtin_fmaf(dg, bf16lo(wg[u][q]), ag[u][2 * q]);
-                ag[u][2 * q + 1] = __builtin_fmaf(dg, bf16hi(wg[u][q]), ag[u][2 * q + 1]);
-                au[u][2 * q] = __builtin_fmaf(du, bf16lo(wu[u][q]), au[u][2 * q]);
-                au[u][2 * q + 1] = __builtin_fmaf(du, bf16hi(wu[u][q]), au[u][2 * q + 1]);
+                // the weights' gradients add the M products in order from +0
+                float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const float h0 = bf16lo(hw[m][u][q]), h1 = bf16hi(hw[m][u][q]);
+                    g0 = __builtin_fmaf(dg[m], h0, g0);
+                    g1 = __builtin_fmaf(dg[m], h1, g1);
+                    u0 = __builtin_fmaf(du[m], h0, u0);
+                    u1 = __builtin_fmaf(du[m], h1, u1);
+                    ag[m][u][2 * q] = __builtin_fmaf(dg[m], bf16lo(wg[u][q]), ag[m][u][2 * q]);
+                    ag[m][u][2 * q + 1] = __builtin_fmaf(dg[m], bf16hi(wg[u][q]), ag[m][u][2 * q + 1]);
+                    au[m][u][2 * q] = __builtin_fmaf(du[m], bf16lo(wu[u][q]), au[m][u][2 * q]);
+                    au[m][u][2 * q + 1] = __builtin_fmaf(du[m], bf16hi(wu[u][q]), au[m][u][2 * q + 1]);
+                }
+                og[q] = (uint32_t)f32_to_bf16_rne(g0) | ((uint32_t)f32_to_bf16_rne(g1) << 16);
+                ou[q] = (uint32_t)f32_to_bf16_rne(u0) | ((uint32_t)f32_to_bf16_rne(u1) << 16);
             }
             if (ok[u]) {
                 const int c = lane + kWave * u;
@@ -539,9 +596,14 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
 
     // the next row's loads are issued before this row is processed (two register sets alternate);
     // past the wave's last row the prefetch re-reads the current row, so no load sits behind a branch
-    // (a second row in flight measured slower: 50.5 against 48.0 us at K=2560 N=9216)
+    // (a second row in flight measured slower at M = 1: 50.5 against 48.0 us at K=2560 N=9216)
     u32x4_b ga[U], ua[U], gb[U], ub[U];
-    uint16_t oa = 0, ob = 0;
+    uint16_t oa[M], ob[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        oa[m] = 0;
+        ob[m] = 0;
+    }
     int j = gw;
     if (j < N) load_row(j, ga, ua, oa);
     while (j < N) {
@@ -559,19 +621,22 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
     for (int w = 0; w < WAVES; ++w) {
         if (wave == w) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!ok[u]) continue;
-                const int c = (lane + kWave * u) * 8;
+            for (int m = 0; m < M; ++m) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float vg = w == 0 ? ag[u][e] : red1[c + e] + ag[u][e];
-                    const float vu = w == 0 ? au[u][e] : red1[K + c + e] + au[u][e];
-                    if (w + 1 < WAVES) {
-                        red1[c + e] = vg;
-                        red1[K + c + e] = vu;
-                    } else {
-                        partial[((int64_t)blockIdx.x * 2 + 0) * K + c + e] = vg;
-                        partial[((int64_t)blockIdx.x * 2 + 1) * K + c + e] = vu;
+                for (int u = 0; u < U; ++u) {
+                    if (!ok[u]) continue;
+                    const int64_t c = (int64_t)m * K + (lane + kWave * u) * 8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float vg = w == 0 ? ag[m][u][e] : red1[c + e] + ag[m][u][e];
+                        const float vu = w == 0 ? au[m][u][e] : red1[MK + c + e] + au[m][u][e];
+                        if (w + 1 < WAVES) {
+                            red1[c + e] = vg;
+                            red1[MK + c + e] = vu;
+                        } else {
+                            partial[((int64_t)blockIdx.x * 2 + 0) * MK + c + e] = vg;
+                            partial[((int64_t)blockIdx.x * 2 + 1) * MK + c + e] = vu;
+                        }
                     }
                 }
             }
@@ -661,9 +726,9 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     if (p.rows_per_range < 1) p.rows_per_range = 1;
     p.nranges = (int)((N + p.rows_per_range - 1) / p.rows_per_range);
     if (p.nranges < 1) p.nranges = 1;
-    // one pass for M = 1 and K <= 64 * 8 * kFusedMaxU: workgroups of kFusedWaves waves, about
+    // one pass for M <= 2 and K <= 64 * 8 * kFusedMaxU: workgroups of kFusedWaves waves, about
     // fused_waves_per_cu waves per CU, each wave the same number of rows to within one
-    p.fused = M == 1 && K >= 8 && (K / 8 + kWave - 1) / kWave <= kFusedMaxU;
+    p.fused = M >= 1 && M <= kFusedMaxM && K >= 8 && (K / 8 + kWave - 1) / kWave <= fused_max_u((int)M);
     p.path = p.fused ? kPathFused1 : kPathChunks;
     int64_t rows_per_wave = 0;
     // split over K: K / 8 chunks over at most 8 waves of 1 or 2 chunks per lane
@@ -678,7 +743,7 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.nranges = p.split_grid;  // one partial of dh per workgroup
     }
     if (p.fused) {
-        const int64_t target = (int64_t)kCUsForPlan * fused_waves_per_cu((int)((K / 8 + kWave - 1) / kWave));
+        const int64_t target = (int64_t)kCUsForPlan * fused_waves_per_cu((int)M, (int)((K / 8 + kWave - 1) / kWave));
         rows_per_wave = N > 0 ? (N + target - 1) / target : 1;
         const int64_t waves = (N + rows_per_wave - 1) / rows_per_wave;
         p.fused_grid = (int)((waves + kFusedWaves - 1) / kFusedWaves);
@@ -758,21 +823,27 @@ hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, cons
     return hipGetLastError();
 }
 
-hipError_t fused1_launch(const BwdPlan& p, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+hipError_t fused1_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                         const uint16_t* dout, uint16_t* dgu, uint16_t* dwg, uint16_t* dwu, float* partial, int N, int K,
                         hipStream_t stream)
 {
     using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, uint16_t*,
                         uint16_t*, float*, int, int);
-    static const Fn table[kFusedMaxU] = {
-        fused1_kernel<1, kFusedWaves>, fused1_kernel<2, kFusedWaves>, fused1_kernel<3, kFusedWaves>,
-        fused1_kernel<4, kFusedWaves>, fused1_kernel<5, kFusedWaves>,
+    static const Fn table[kFusedMaxM][kFusedMaxU] = {
+        {fused1_kernel<1, 1, kFusedWaves>, fused1_kernel<1, 2, kFusedWaves>, fused1_kernel<1, 3, kFusedWaves>,
+         fused1_kernel<1, 4, kFusedWaves>, fused1_kernel<1, 5, kFusedWaves>},
+        {fused1_kernel<2, 1, kFusedWaves>, fused1_kernel<2, 2, kFusedWaves>, fused1_kernel<2, 3, kFusedWaves>,
+         fused1_kernel<2, 4, kFusedWaves>, fused1_kernel<2, 5, kFusedWaves>},
     };
     const int U = (K / 8 + kWave - 1) / kWave;
-    if (!p.fused || U < 1 || U > kFusedMaxU || (K & 7) != 0 || N < 1 || p.fused_grid < 1) return hipErrorInvalidValue;
-    const size_t lds = (size_t)2 * K * sizeof(float);
-    hipLaunchKernelGGL(table[U - 1], dim3(p.fused_grid), dim3(kFusedWaves * kWave), lds, stream, hidden, gate_w,
-                       up_w, dout, dgu, dwg, dwu, partial, N, K);
+    if (!p.fused || M < 1 || M > kFusedMaxM || U < 1 || U > fused_max_u(M) || (K & 7) != 0 || N < 1 ||
+        p.fused_grid < 1) {
+        return hipErrorInvalidValue;
+    }
+    const size_t lds = (size_t)2 * M * K * sizeof(float);
+    if (lds > (size_t)kLdsBudget) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(table[M - 1][U - 1], dim3(p.fused_grid), dim3(kFusedWaves * kWave), lds, stream, hidden,
+                       gate_w, up_w, dout, dgu, dwg, dwu, partial, N, K);
     return hipGetLastError();
 }
 

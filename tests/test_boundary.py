@@ -370,7 +370,10 @@ def test_backward_plan_and_workspace(lib):
     assert p["launches"] == 2 and p["block"] == 384
     p = api.backward_plan(3, 100, 8192)    # two chunks per lane up to M = 3
     assert p["launches"] == 2 and p["block"] == 512 and p["grid"] == 100
-    p = api.backward_plan(2, 9216, 2560)   # the grouped GEMV, gradients, contraction, reduction
+    p = api.backward_plan(2, 9216, 2560)   # M <= 2, K <= 2560: one pass (a wave per weight row)
+    assert p["launches"] == 2 and p["block"] == 256
+    assert api.backward_plan(3, 9216, 2048)["launches"] == 4   # three rows: the four launches
+    p = api.backward_plan(4, 9216, 2560)   # the grouped GEMV, gradients, contraction, reduction
     assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 4 and p["grid"] % 5 == 0
     assert api.backward_plan(5, 9216, 4096)["launches"] == 4
     assert api.backward_plan(4, 9216, 4104)["launches"] == 4

@@ -91,6 +91,8 @@ CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2
          # one pass with K split over a workgroup: ragged last wave, two chunks a lane, hidden in LDS
          (4, 9216, 3072), (1, 12288, 4096), (2, 700, 2568), (3, 300, 8192), (2, 99, 6152), (3, 255, 4096),
          (2, 257, 2600), (1, 3, 4104), (4, 1, 2576), (4, 4104, 4096), (1, 513, 8192),
+         # one pass with a wave per weight row for two rows of hidden (three: the four launches)
+         (2, 9216, 2560), (3, 3000, 2048), (2, 1, 520), (3, 65, 1032), (2, 300, 2552),
          # more than 8 rows of hidden: the contractions on the matrix cores (zero-padded operands,
          # ragged row ranges and column tiles, partial 16-row tiles of hidden)
          (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8), (17, 1000, 2568),
