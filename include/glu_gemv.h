@@ -219,9 +219,9 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * weight gradients; K == 0 has nothing to write.  Validation (NULL arrays,
  * shapes, 2-byte alignment, overlap of an output or the workspace with an
  * input or another output, workspace) happens before any HIP call.  On
- * stream, asynchronous, deterministic, allocating nothing: for M = 1 with
- * K <= 8192, and for M <= 4 with 2560 < K <= 4096 (K <= 8192 when M <= 3),
- * two launches, a pass that reads each
+ * stream, asynchronous, deterministic, allocating nothing: for M <= 2 with
+ * K <= 2560, for M = 1 with K <= 8192, and for M <= 4 with 2560 < K <= 4096
+ * (K <= 8192 when M <= 3), two launches, a pass that reads each
  * weight row once and the reduction of dhidden's partial sums; otherwise
  * the grouped GEMV for g and u (above M = 32 with N % 4 == 0 a tiled GEMM),
  * then the gradient kernels (above M = 8 on the matrix cores).
