@@ -81,7 +81,7 @@ struct RepackJob {
     uint16_t* dst;
     int R, C, Rp, Cp;   // Rp >= R rows (transposed: the row length), Cp >= C columns (not transposed)
     int transpose;
-    int64_t first, count;  // set by repack_launch
+    int64_t first_block, nblocks;  // set by repack_launch: the job's workgroups of the launch
 };
 constexpr int kMaxRepackJobs = 5;
 struct RepackJobs {

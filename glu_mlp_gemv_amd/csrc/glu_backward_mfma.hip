@@ -40,6 +40,7 @@ namespace glu {
 namespace {
 
 constexpr int kRepackThreads = 256;
+constexpr int kRepackTile = 64;       // columns per transposing workgroup, and rows of dst at most
 constexpr int kMfmaBwdThreads = 256;  // 4 waves
 constexpr int kDwTile = 64;           // k and j extent of a wave's dW tile
 constexpr int kDhK = 64;              // columns k per dh workgroup (16 per wave)
@@ -55,27 +56,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 
 }  // namespace
 
-// One launch for all the copies: thread i serves the copy whose range [first, first + count)
-// holds i.  transpose == 0: dst[r][c] = src[r][c] (Rp rows of Cp elements); transpose != 0:
-// dst[c][r] = src[r][c] (C rows of Rp elements).  Entries with r >= R or c >= C are +0.
+// One launch for all the copies; workgroup b serves the job whose range of workgroups holds b.
+// transpose == 0: dst[r][c] = src[r][c] (Rp rows of Cp elements), one element per thread.
+// transpose != 0: dst[c][r] = src[r][c] (C rows of Rp <= 64 elements): a workgroup moves a tile of
+// 64 columns through LDS, reading rows of src and writing rows of dst, both contiguous.
+// Entries with r >= R or c >= C are +0.
 __global__ void __launch_bounds__(kRepackThreads)
 repack_kernel(RepackJobs jobs)
 {
-    const int64_t i = (int64_t)blockIdx.x * kRepackThreads + threadIdx.x;
+    __shared__ uint16_t tile[kRepackTile][kRepackTile + 2];  // [r][c]; odd word stride spreads the banks
+    const int64_t b = blockIdx.x;
     int q = 0;
-    while (q + 1 < jobs.n && i >= jobs.job[q + 1].first) ++q;
+    while (q + 1 < jobs.n && b >= jobs.job[q + 1].first_block) ++q;  // uniform over the workgroup
     const RepackJob& jb = jobs.job[q];
-    const int64_t x = i - jb.first;
-    if (x < 0 || x >= jb.count) return;
-    int64_t r, c;
-    if (jb.transpose) {
-        c = x / jb.Rp;
-        r = x - c * jb.Rp;
-    } else {
-        r = x / jb.Cp;
-        c = x - r * jb.Cp;
+    const int64_t bl = b - jb.first_block;
+    if (bl < 0 || bl >= jb.nblocks) return;  // whole workgroup
+    if (!jb.transpose) {
+        const int64_t x = bl * kRepackThreads + threadIdx.x;
+        if (x >= (int64_t)jb.Rp * jb.Cp) return;  // no barrier in this branch
+        const int64_t r = x / jb.Cp, c = x - (x / jb.Cp) * jb.Cp;
+        jb.dst[x] = (r < jb.R && c < jb.C) ? jb.src[r * jb.ld + c] : (uint16_t)0;
+        return;
     }
-    jb.dst[x] = (r < jb.R && c < jb.C) ? jb.src[r * jb.ld + c] : (uint16_t)0;
+    const int64_t c0 = bl * kRepackTile;
+    for (int i = threadIdx.x; i < kRepackTile * kRepackTile; i += kRepackThreads) {
+        const int r = i / kRepackTile, cc = i % kRepackTile;
+        const int64_t c = c0 + cc;
+        tile[r][cc] = (r < jb.R && c < jb.C) ? jb.src[(int64_t)r * jb.ld + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kRepackTile * jb.Rp; i += kRepackThreads) {
+        const int cc = i / jb.Rp, r = i % jb.Rp;
+        const int64_t c = c0 + cc;
+        if (c < jb.C) jb.dst[c * jb.Rp + r] = tile[r][cc];
+    }
 }
 
 // KS = Mp32 / 32 (1 or 2).  ktiles = ceil(K / 64); wave tiles ntiles = ktiles * ceil(N / 64).
@@ -275,16 +289,17 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
 hipError_t repack_launch(RepackJobs jobs, hipStream_t stream)
 {
     if (jobs.n < 1 || jobs.n > kMaxRepackJobs) return hipErrorInvalidValue;
-    int64_t total = 0;
+    int64_t grid = 0;
     for (int q = 0; q < jobs.n; ++q) {
         RepackJob& j = jobs.job[q];
-        if (j.R > j.Rp || (!j.transpose && j.C > j.Cp) || j.R < 0 || j.C < 0) return hipErrorInvalidValue;
-        j.count = j.transpose ? (int64_t)j.C * j.Rp : (int64_t)j.Rp * j.Cp;
-        j.first = total;
-        total += j.count;
+        if (j.R > j.Rp || j.R < 0 || j.C < 0) return hipErrorInvalidValue;
+        if (j.transpose ? j.Rp > kRepackTile : j.C > j.Cp) return hipErrorInvalidValue;
+        j.nblocks = j.transpose ? ((int64_t)j.C + kRepackTile - 1) / kRepackTile
+                                : ((int64_t)j.Rp * j.Cp + kRepackThreads - 1) / kRepackThreads;
+        j.first_block = grid;
+        grid += j.nblocks;
     }
-    if (total <= 0) return hipSuccess;
-    const int64_t grid = (total + kRepackThreads - 1) / kRepackThreads;
+    if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(kRepackThreads), 0, stream, jobs);
     return hipGetLastError();
