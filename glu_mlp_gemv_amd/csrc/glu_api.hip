@@ -62,6 +62,29 @@ int64_t balanced_waves(int64_t units, int64_t target)
     return ceil_div(units, per);
 }
 
+// Workgroups for the grouped 8-row layout: `groups` groups of 8 weight rows, at most `slots` waves
+// resident, `waves` per workgroup.  One CU's share of the bandwidth saturates near
+// kMfmaWavesPerCU waves of this kernel, so a CU takes about max(its groups / kMfmaWavesPerCU, the
+// groups of its busiest wave) group-times.  For p = 1..4 more than the fewest groups per wave that
+// fit the slots, spread evenly, the plan takes the p with the fewest such steps (ties: more waves).
+// Measured at K = 2560 with 12 and 16 rows of hidden: two 9216-row projections run in 19.7 and
+// 20.6 us on 192 workgroups against 25.0 and 26.3 on the 288 of an even spread over all 2048 slots.
+int64_t grouped8_grid(int64_t groups, int64_t slots, int64_t waves)
+{
+    const int64_t p0 = ceil_div(groups, slots < 1 ? 1 : slots);
+    int64_t best = 1, best_steps = INT64_MAX;
+    for (int64_t p = p0; p < p0 + 4; ++p) {
+        const int64_t blocks = ceil_div(ceil_div(groups, p), waves);
+        const int64_t waves_per_cu = ceil_div(blocks * waves, kCUs);
+        const int64_t steps = p * ceil_div(waves_per_cu, kMfmaWavesPerCU);
+        if (steps < best_steps) {
+            best_steps = steps;
+            best = blocks;
+        }
+    }
+    return best;
+}
+
 glu_status plan_valu(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
 {
     if (M > glu::kValuMaxM || K > kMaxValuK) return GLU_ERR_UNSUPPORTED;
@@ -409,8 +432,7 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
             c.block = waves * glu::kWave;
             const bool two_fit = 2 * glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsMax;
             const int64_t per_cu = two_fit ? 2 * kMfmaWavesPerCU : kMfmaWavesPerCU;
-            const int64_t grid = (t && t->grid > 0) ? t->grid
-                                                    : ceil_div(balanced_waves(rows / 8, (int64_t)kCUs * per_cu), waves);
+            const int64_t grid = (t && t->grid > 0) ? t->grid : grouped8_grid(rows / 8, (int64_t)kCUs * per_cu, waves);
             c.grid = (int)(grid < 1 ? 1 : grid);
             if (!glu::grouped_mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
             L->kernel = GLU_KERNEL_MFMA;
