@@ -98,6 +98,10 @@ CASES = [
     ((4096, 1024, 1024), 2560, 32, dict(rows_per_wave=4)),  # the 4-row layout on request
     ((1024, 1032), 2560, 32, {}),             # 1032 = 8 x 129 rows
     ((1024, 256), 1024, 40, {}),              # slices of 32 (8-row groups) and of 8 rows
+    ((1024, 512), 2560, 12, dict(rows_per_wave=4)),  # 4-row layout, three tiles, 5 segments per stage
+    ((2048, 1024, 32, 32), 2560, 12, dict(mfma_segments=5)),  # 8-row layout, 5 segments per stage
+    ((9216, 9216), 2560, 12, {}),             # 2304 groups of 8 rows: three per wave on 192 workgroups
+    ((9216, 9216), 2560, 16, dict(grid=384)),  # uneven: half the waves take two groups, half one
 ]
 
 
