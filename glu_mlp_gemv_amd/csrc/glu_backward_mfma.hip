@@ -12,7 +12,7 @@
 //
 // dw_mfma_kernel: dWg^T = hT . dgT^T as a [K][N] product, and dWu likewise.
 // The contraction over the M rows takes one or two MFMAs per 16 x 16 tile.
-// A wave owns 64 x 64 of (k, j). Lane l holds k = 4(l/16)+e, j = l%16 of a
+// A wave owns 64 x 64 tiles of (k, j), one after another. Lane l holds k = 4(l/16)+e, j = l%16 of a
 // tile; lanes l and l ^ 16 trade a tile of each pair so that every lane
 // stores 8 consecutive k of one row of dW as one 16-byte store.
 //
@@ -43,6 +43,11 @@ constexpr int kRepackThreads = 256;
 constexpr int kRepackTile = 64;       // columns per transposing workgroup, and rows of dst at most
 constexpr int kMfmaBwdThreads = 256;  // 4 waves
 constexpr int kDwTile = 64;           // k and j extent of a wave's dW tile
+// dW tiles per wave at KS = 1 (the grid's waves stride over the tiles; at KS = 2 one per wave):
+// K=2560 N=9216, whole backward: M = 16 94.4 -> 91.7 us, M = 32 111.9 -> 110.1 (5760 tiles against
+// 4096 resident waves at one tile per wave); at M = 64 (KS = 2) three per wave took 133.9 against
+// 131.6
+constexpr int kDwTilesPerWave = 3;
 constexpr int kDhK = 64;              // columns k per dh workgroup (16 per wave)
 constexpr int kDhStep = 32;           // weight rows per dh step (one MFMA contraction)
 constexpr int kDhTS = 40;             // elements per LDS row of the transposed tile (32 rows j + 8 of padding,
@@ -93,6 +98,9 @@ repack_kernel(RepackJobs jobs)
 }
 
 // KS = Mp32 / 32 (1 or 2).  ktiles = ceil(K / 64); wave tiles ntiles = ktiles * ceil(N / 64).
+// Persistent: wave w takes tiles w, w + W, w + 2W, ... (W waves in the grid), one after another.
+// (Loading the next tile's operands during the current tile's stores takes a second register set:
+// 2 waves per SIMD instead of 4 at KS = 1, and the whole backward measured slower at M = 64.)
 template <int KS>
 __global__ void __launch_bounds__(kMfmaBwdThreads)
 dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT, const uint16_t* __restrict__ duT,
@@ -101,61 +109,75 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
     constexpr int MP = 32 * KS;
     constexpr int T = kDwTile / 16;  // 16 x 16 tiles per side
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t tile = (int64_t)blockIdx.x * (kMfmaBwdThreads / kWave) + (threadIdx.x / kWave);
+    const int64_t nwaves = (int64_t)gridDim.x * (kMfmaBwdThreads / kWave);
+    int64_t tile = (int64_t)blockIdx.x * (kMfmaBwdThreads / kWave) + (threadIdx.x / kWave);
     if (tile >= ntiles) return;  // whole wave; no barriers below
-    const int k0 = (int)(tile % ktiles) * kDwTile;
-    const int64_t j0 = (tile / ktiles) * kDwTile;
     const int i16 = lane & 15, q = lane >> 4;
 
+    auto load = [&](int64_t tl, u32x4_t (&a)[KS][T], u32x4_t (&bg)[KS][T], u32x4_t (&bu)[KS][T]) {
+        const int k0 = (int)(tl % ktiles) * kDwTile;
+        const int64_t j0 = (tl / ktiles) * kDwTile;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                // rows past K or N re-read the last row: their results are never stored
+                const int64_t k = min(k0 + 16 * t + i16, K - 1);
+                const int64_t j = min(j0 + 16 * t + i16, (int64_t)N - 1);
+                a[ks][t] = *reinterpret_cast<const u32x4_t*>(hT + k * MP + 32 * ks + 8 * q);
+                bg[ks][t] = *reinterpret_cast<const u32x4_t*>(dgT + j * MP + 32 * ks + 8 * q);
+                bu[ks][t] = *reinterpret_cast<const u32x4_t*>(duT + j * MP + 32 * ks + 8 * q);
+            }
+        }
+    };
+
+    auto emit = [&](int64_t tl, const u32x4_t (&a)[KS][T], const u32x4_t (&bg)[KS][T],
+                    const u32x4_t (&bu)[KS][T]) {
+        const int k0 = (int)(tl % ktiles) * kDwTile;
+        const int64_t j0 = (tl / ktiles) * kDwTile;
+#pragma unroll
+        for (int tj = 0; tj < T; ++tj) {
+            f32x4_t cg[T], cu[T];
+#pragma unroll
+            for (int tk = 0; tk < T; ++tk) {
+                cg[tk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                cu[tk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    cg[tk] = mfma16(a[ks][tk], bg[ks][tj], cg[tk]);
+                    cu[tk] = mfma16(a[ks][tk], bu[ks][tj], cu[tk]);
+                }
+            }
+            // Lane (l%16, q = l/16) holds columns 16 tk + 4q .. +3 of row j for each tile tk.  Lanes q
+            // and q ^ 1 (l ^ 16) trade one tile of a pair (tk, tk + 1): the even q then holds 8
+            // consecutive columns of tile tk, the odd q 8 of tile tk + 1, so each lane stores 16 bytes
+            // and four lanes write 64 contiguous bytes of the row.  Plain stores: nontemporal ones
+            // measured 1.3-1.7x slower for the whole backward.
+            const int64_t j = j0 + 16 * tj + i16;
+            const bool oddq = (q & 1) != 0;
+#pragma unroll
+            for (int tk = 0; tk < T; tk += 2) {
+#pragma unroll
+                for (int mat = 0; mat < 2; ++mat) {
+                    const f32x4_t& c0 = mat == 0 ? cg[tk] : cu[tk];
+                    const f32x4_t& c1 = mat == 0 ? cg[tk + 1] : cu[tk + 1];
+                    const uint32_t a0 = pack_bf16x2(c0[0], c0[1]), a1 = pack_bf16x2(c0[2], c0[3]);
+                    const uint32_t b0 = pack_bf16x2(c1[0], c1[1]), b1 = pack_bf16x2(c1[2], c1[3]);
+                    const uint32_t s0 = oddq ? a0 : b0, s1 = oddq ? a1 : b1;
+                    const uint32_t r0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)s0, 0x401F);  // lane ^ 16
+                    const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)s1, 0x401F);
+                    const u32x4_t v = oddq ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+                    const int k = k0 + 16 * (tk + (oddq ? 1 : 0)) + 4 * (q & 2);  // a multiple of 8: k < K covers k + 7
+                    if (j < N && k < K) *reinterpret_cast<u32x4_t*>((mat == 0 ? dwg : dwu) + j * K + k) = v;
+                }
+            }
+        }
+    };
+
     u32x4_t a[KS][T], bg[KS][T], bu[KS][T];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            // rows past K or N re-read the last row: their results are never stored
-            const int64_t k = min(k0 + 16 * t + i16, K - 1);
-            const int64_t j = min(j0 + 16 * t + i16, (int64_t)N - 1);
-            a[ks][t] = *reinterpret_cast<const u32x4_t*>(hT + k * MP + 32 * ks + 8 * q);
-            bg[ks][t] = *reinterpret_cast<const u32x4_t*>(dgT + j * MP + 32 * ks + 8 * q);
-            bu[ks][t] = *reinterpret_cast<const u32x4_t*>(duT + j * MP + 32 * ks + 8 * q);
-        }
-    }
-#pragma unroll
-    for (int tj = 0; tj < T; ++tj) {
-        f32x4_t cg[T], cu[T];
-#pragma unroll
-        for (int tk = 0; tk < T; ++tk) {
-            cg[tk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            cu[tk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                cg[tk] = mfma16(a[ks][tk], bg[ks][tj], cg[tk]);
-                cu[tk] = mfma16(a[ks][tk], bu[ks][tj], cu[tk]);
-            }
-        }
-        // Lane (l%16, q = l/16) holds columns 16 tk + 4q .. +3 of row j for each tile tk.  Lanes q and
-        // q ^ 1 (l ^ 16) trade one tile of a pair (tk, tk + 1): the even q then holds 8 consecutive
-        // columns of tile tk, the odd q 8 of tile tk + 1, so each lane stores 16 bytes and four lanes
-        // write 64 contiguous bytes of the row.  Plain stores: nontemporal ones measured 1.3-1.7x
-        // slower for the whole backward.
-        const int64_t j = j0 + 16 * tj + i16;
-        const bool oddq = (q & 1) != 0;
-#pragma unroll
-        for (int tk = 0; tk < T; tk += 2) {
-#pragma unroll
-            for (int mat = 0; mat < 2; ++mat) {
-                const f32x4_t& c0 = mat == 0 ? cg[tk] : cu[tk];
-                const f32x4_t& c1 = mat == 0 ? cg[tk + 1] : cu[tk + 1];
-                const uint32_t a0 = pack_bf16x2(c0[0], c0[1]), a1 = pack_bf16x2(c0[2], c0[3]);
-                const uint32_t b0 = pack_bf16x2(c1[0], c1[1]), b1 = pack_bf16x2(c1[2], c1[3]);
-                const uint32_t s0 = oddq ? a0 : b0, s1 = oddq ? a1 : b1;
-                const uint32_t r0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)s0, 0x401F);  // lane ^ 16
-                const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)s1, 0x401F);
-                const u32x4_t v = oddq ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
-                const int k = k0 + 16 * (tk + (oddq ? 1 : 0)) + 4 * (q & 2);  // a multiple of 8: k < K covers k + 7
-                if (j < N && k < K) *reinterpret_cast<u32x4_t*>((mat == 0 ? dwg : dwu) + j * K + k) = v;
-            }
-        }
+    for (; tile < ntiles; tile += nwaves) {
+        load(tile, a, bg, bu);
+        emit(tile, a, bg, bu);
     }
 }
 
@@ -310,7 +332,8 @@ hipError_t dw_mfma_launch(const BwdPlan& p, const uint16_t* hT, const uint16_t* 
 {
     const int ktiles = (K + kDwTile - 1) / kDwTile;
     const int64_t ntiles = (int64_t)ktiles * ((N + kDwTile - 1) / kDwTile);
-    const int64_t grid = (ntiles + 3) / 4;
+    const int64_t per_wave = p.mp32 == 32 ? kDwTilesPerWave : 1;
+    const int64_t grid = (ntiles + 4 * per_wave - 1) / (4 * per_wave);
     if (p.path != kPathMfma || N < 1 || K < 8 || (K & 7) != 0 || grid < 1 || grid > 0x7fffffff) {
         return hipErrorInvalidValue;
     }
