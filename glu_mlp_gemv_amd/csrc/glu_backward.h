@@ -82,6 +82,7 @@ struct RepackJob {
     int R, C, Rp, Cp;   // Rp >= R rows (transposed: the row length), Cp >= C columns (not transposed)
     int transpose;
     int64_t first_block, nblocks;  // set by repack_launch: the job's workgroups of the launch
+    int vec;                       // set by repack_launch: 16-byte accesses (see repack_kernel)
 };
 constexpr int kMaxRepackJobs = 5;
 struct RepackJobs {

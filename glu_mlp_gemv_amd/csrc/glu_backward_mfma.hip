@@ -62,10 +62,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 }  // namespace
 
 // One launch for all the copies; workgroup b serves the job whose range of workgroups holds b.
-// transpose == 0: dst[r][c] = src[r][c] (Rp rows of Cp elements), one element per thread.
+// transpose == 0: dst[r][c] = src[r][c] (Rp rows of Cp elements), one element per thread, or with
+// vec 8 (one 16-byte load and store).
 // transpose != 0: dst[c][r] = src[r][c] (C rows of Rp <= 64 elements): a workgroup moves a tile of
-// 64 columns through LDS, reading rows of src and writing rows of dst, both contiguous.
-// Entries with r >= R or c >= C are +0.
+// 64 columns through LDS, reading rows of src and writing rows of dst, both contiguous (with vec in
+// 16-byte pieces on both sides).
+// Entries with r >= R or c >= C are +0.  vec requires 16-byte aligned src and dst, ld, C and the
+// padded row length (Cp, or Rp when transposing) multiples of 8: a piece of 8 is then wholly inside
+// or wholly outside the source.
 __global__ void __launch_bounds__(kRepackThreads)
 repack_kernel(RepackJobs jobs)
 {
@@ -76,7 +80,18 @@ repack_kernel(RepackJobs jobs)
     const RepackJob& jb = jobs.job[q];
     const int64_t bl = b - jb.first_block;
     if (bl < 0 || bl >= jb.nblocks) return;  // whole workgroup
+    const u32x4_t z = {0u, 0u, 0u, 0u};
     if (!jb.transpose) {
+        if (jb.vec) {
+            const int64_t cp8 = jb.Cp / 8;
+            const int64_t x = bl * kRepackThreads + threadIdx.x;  // piece of 8
+            if (x >= (int64_t)jb.Rp * cp8) return;  // no barrier in this branch
+            const int64_t r = x / cp8, c = (x - r * cp8) * 8;
+            const u32x4_t v =
+                (r < jb.R && c < jb.C) ? *reinterpret_cast<const u32x4_t*>(jb.src + r * jb.ld + c) : z;
+            *reinterpret_cast<u32x4_t*>(jb.dst + 8 * x) = v;
+            return;
+        }
         const int64_t x = bl * kRepackThreads + threadIdx.x;
         if (x >= (int64_t)jb.Rp * jb.Cp) return;  // no barrier in this branch
         const int64_t r = x / jb.Cp, c = x - (x / jb.Cp) * jb.Cp;
@@ -84,16 +99,44 @@ repack_kernel(RepackJobs jobs)
         return;
     }
     const int64_t c0 = bl * kRepackTile;
-    for (int i = threadIdx.x; i < kRepackTile * kRepackTile; i += kRepackThreads) {
-        const int r = i / kRepackTile, cc = i % kRepackTile;
-        const int64_t c = c0 + cc;
-        tile[r][cc] = (r < jb.R && c < jb.C) ? jb.src[(int64_t)r * jb.ld + c] : (uint16_t)0;
+    if (jb.vec) {
+        // 64 rows x 8 pieces of 8 columns
+        for (int i = threadIdx.x; i < kRepackTile * (kRepackTile / 8); i += kRepackThreads) {
+            const int r = i / (kRepackTile / 8), cc = 8 * (i % (kRepackTile / 8));
+            const int64_t c = c0 + cc;
+            const u32x4_t v =
+                (r < jb.R && c < jb.C) ? *reinterpret_cast<const u32x4_t*>(jb.src + (int64_t)r * jb.ld + c) : z;
+            __builtin_memcpy(&tile[r][cc], &v, sizeof(v));  // columns cc .. cc + 7 of tile row r
+        }
+    } else {
+        for (int i = threadIdx.x; i < kRepackTile * kRepackTile; i += kRepackThreads) {
+            const int r = i / kRepackTile, cc = i % kRepackTile;
+            const int64_t c = c0 + cc;
+            tile[r][cc] = (r < jb.R && c < jb.C) ? jb.src[(int64_t)r * jb.ld + c] : (uint16_t)0;
+        }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kRepackTile * jb.Rp; i += kRepackThreads) {
-        const int cc = i / jb.Rp, r = i % jb.Rp;
-        const int64_t c = c0 + cc;
-        if (c < jb.C) jb.dst[c * jb.Rp + r] = tile[r][cc];
+    if (jb.vec) {
+        // dst row c: Rp / 8 pieces of 8 consecutive r
+        const int rp8 = jb.Rp / 8;
+        for (int i = threadIdx.x; i < kRepackTile * rp8; i += kRepackThreads) {
+            const int cc = i / rp8, r = 8 * (i % rp8);
+            const int64_t c = c0 + cc;
+            if (c < jb.C) {
+                u32x4_t v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = (uint32_t)tile[r + 2 * e][cc] | ((uint32_t)tile[r + 2 * e + 1][cc] << 16);
+                }
+                *reinterpret_cast<u32x4_t*>(jb.dst + c * jb.Rp + r) = v;
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < kRepackTile * jb.Rp; i += kRepackThreads) {
+            const int cc = i / jb.Rp, r = i % jb.Rp;
+            const int64_t c = c0 + cc;
+            if (c < jb.C) jb.dst[c * jb.Rp + r] = tile[r][cc];
+        }
     }
 }
 
@@ -316,8 +359,11 @@ hipError_t repack_launch(RepackJobs jobs, hipStream_t stream)
         RepackJob& j = jobs.job[q];
         if (j.R > j.Rp || j.R < 0 || j.C < 0) return hipErrorInvalidValue;
         if (j.transpose ? j.Rp > kRepackTile : j.C > j.Cp) return hipErrorInvalidValue;
+        const bool al = (((uintptr_t)j.src | (uintptr_t)j.dst) & 15u) == 0 && j.ld % 8 == 0 && j.C % 8 == 0;
+        j.vec = al && (j.transpose ? j.Rp % 8 == 0 : j.Cp % 8 == 0) ? 1 : 0;
+        const int64_t per_thread = j.vec ? 8 : 1;
         j.nblocks = j.transpose ? ((int64_t)j.C + kRepackTile - 1) / kRepackTile
-                                : ((int64_t)j.Rp * j.Cp + kRepackThreads - 1) / kRepackThreads;
+                                : ((int64_t)j.Rp * j.Cp / per_thread + kRepackThreads - 1) / kRepackThreads;
         j.first_block = grid;
         grid += j.nblocks;
     }
