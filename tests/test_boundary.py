@@ -279,6 +279,38 @@ def test_grouped_plan_tiny_row_counts(M, rows):
             assert p["kernel"] in (api.KERNEL_NONE, api.KERNEL_VALU, api.KERNEL_GENERIC, api.KERNEL_MFMA)
 
 
+def test_grouped_8row_grid():
+    """Workgroups of the 8-row layout: per CU, the larger of its groups / 4 waves and its busiest
+    wave's groups decides the time, so the planner takes the groups per wave with the fewest such
+    steps (ties: more waves); a grid override is taken as given."""
+    def grid(Ns, M, **kw):
+        t = api.make_tuning(**kw) if kw else None
+        return api.grouped_plan(M, 2560, sum(Ns), tuning=t, mult8=True)["grid"]
+    # two workgroups per CU fit (M <= 16 at K = 2560): 2048 wave slots
+    assert grid((9216, 9216), 12) == 192      # 2304 groups: 3 per wave (288 would put 2 workgroups on 32 CUs)
+    assert grid((9216, 9216), 16) == 192
+    assert grid((12288, 12288), 16) == 256    # 3072 groups: 3 per wave on every CU
+    assert grid((8192, 4096, 32, 32), 12) == 386  # 1544 groups: 1 per wave (tie with 2 per wave on 193)
+    assert grid((4096, 1024, 1024), 16) == 192  # 768 groups: 1 per wave
+    # one workgroup per CU (M = 32): 1024 slots
+    assert grid((9216, 9216), 32) == 192
+    assert grid((8192, 4096, 32, 32), 32) == 193
+    assert grid((12288, 12288), 32) == 256
+    assert grid((9216, 9216), 16, grid=384) == 384
+    # the model itself: every choice within 4 groups per wave of the fewest the slots allow
+    for rows in range(8, 80000, 8 * 97):
+        for M in (12, 32):
+            g = api.grouped_plan(M, 2560, rows, mult8=True)
+            if not g["kernel_symbol"].endswith(", 8>"):
+                continue
+            groups = rows // 8
+            waves = g["grid"] * g["block"] // 64
+            assert 1 <= g["grid"] and waves >= 1
+            per_wave = -(-groups // waves)
+            slots = 256 * (8 if M <= 16 else 4)
+            assert -(-groups // slots) <= per_wave <= -(-groups // slots) + 3
+
+
 def test_grouped_plans():
     p = api.grouped_plan(1, 2560, 4096 + 1024 + 1024)
     assert p["kernel"] == api.KERNEL_VALU and p["launches"] == 1
