@@ -124,9 +124,10 @@ contract_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict_
         }
     }
 
-    // rows j0 + 4i (i < RPI) per iteration: their loads are issued together (fewer rows above
-    // M = 4, where the dh accumulators take most of the registers)
-    constexpr int RPI = M <= 4 ? kRowsPerIter : (M <= 6 ? kRowsPerIter / 2 : 1);
+    // rows j0 + 4i (i < RPI) per iteration: their loads are issued together (fewer rows from
+    // M = 4, where the dh accumulators take most of the registers; K=2560 N=9216, whole backward:
+    // M = 4 75.9 -> 73.7 us with 2 rows instead of 4, M = 3 72.4 against 73.2 with 4)
+    constexpr int RPI = M <= 3 ? kRowsPerIter : (M <= 6 ? kRowsPerIter / 2 : 1);
     for (int j0 = j_begin + wave; j0 < j_end; j0 += kBwdWaves * RPI) {
         u32x4_b wgv[RPI], wuv[RPI];
         float dg[RPI][M], du[RPI][M];
