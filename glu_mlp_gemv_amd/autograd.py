@@ -1,7 +1,7 @@
 """The dual-weight GLU as an autograd Function over the library's two entry points.
 
-Mirrors the segKI "Plan B" design (DeepSpeed PR #9057 discussion, "Plan B
-Design"): the Function keeps hidden, gate_w and up_w, reads the weight
+Mirrors the segKI "Plan B" design (DeepSpeed PR #8602, comment "Plan B:
+Dual-Weight GEMV", section "Plan B Design"): the Function keeps hidden, gate_w and up_w, reads the weight
 Parameters in place in both directions, and returns gradients for all three,
 so training and generation share one forward and one set of weights.
 Forward: glu_dual_gemv; backward: glu_dual_gemv_backward (M <= 64 rows of

@@ -2,8 +2,8 @@
 //
 // The segKI "Plan B" autograd Function keeps hidden, gate_w and up_w and
 // returns gradients for all three, equal to those of the composite
-// silu(h Wg^T) * (h Wu^T) (DeepSpeed PR #9057 discussion, "Plan B Design" and
-// "Verification Results").  Over bf16 tensors every gradient tensor is
+// silu(h Wg^T) * (h Wu^T) (DeepSpeed PR #8602, comment "Plan B: Dual-Weight
+// GEMV", sections "Plan B Design" and "Verification Results").  Over bf16 tensors every gradient tensor is
 // rounded once to bf16, as autograd of the bf16 composite does:
 //   ds = bf16(dout u), du = bf16(dout s), dg = bf16(silu'(g) ds) in fp32,
 //   dh = bf16(fp32(bf16(dg Wg) + bf16(du Wu))), dWg = bf16(dg^T h), dWu = bf16(du^T h).

@@ -4,7 +4,7 @@
 // The pages route the QKV and GatedDeltaNet input projections (three or four
 // weight matrices applied to the same hidden) through single/triple/quad
 // GEMV kernels, later unified behind one grouped_linear(x, weights,
-// glu_epilogue) dispatcher (DeepSpeed PR #8602, commit notes); their segment
+// glu_epilogue) dispatcher (DeepSpeed PR #9057, commit notes); their segment
 // fusion concatenates the four GDN weights into one [qkv|z|b|a] block to get
 // one GEMM.  Here the n weights stay separate: the kernel streams them as one
 // virtual row space of sum N_i rows, and resolves each row to its projection

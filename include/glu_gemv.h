@@ -68,9 +68,10 @@ typedef enum glu_status {
  * unchecked.  K == 0: every output is +0 (the empty sums give silu(0) * 0).
  * Fast path: hidden, gate_w and up_w 16-byte aligned, K a multiple of 8 and
  * K <= 2^25; any other 2-byte-aligned input takes a slower path with the same
- * result contract.  M == 1 with K <= 4096 runs a VALU GEMV; other shapes run a
- * block-diagonal MFMA kernel; M > 32 is processed in slices of 32 rows of
- * hidden (one launch per slice, each streaming the weights again).
+ * result contract.  M == 1 with K <= 4096 runs a VALU GEMV; other shapes up
+ * to M = 32 run a block-diagonal MFMA kernel; M > 32 runs a tiled MFMA GEMM
+ * (GLU_KERNEL_GEMM), one launch per 65536 rows of hidden, each reading the
+ * weights once.
  */
 glu_status glu_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream);
@@ -142,8 +143,9 @@ glu_status glu_dual_gemv_plan(int64_t M, int64_t N, int64_t K, int aligned16, gl
 /*
  * Grouped GEMV: n projections of one hidden, out_i = bf16(hidden @ W_i^T)
  * for i < n, each W_i read in place.  This is the pages' single/triple/quad
- * GEMV (the QKV and GatedDeltaNet input projections) behind the
- * grouped_linear dispatcher of DeepSpeed PR #8602 (commit notes), without
+ * GEMV (the QKV and GatedDeltaNet input projections), which DeepSpeed PR
+ * #9057 "fix(module-inject): preserve HF precision boundaries in segKI
+ * kernels" (commit notes) folds into one grouped_linear dispatcher, without
  * the GLU epilogue: every output is the fp32 dot product rounded once to
  * bf16 (round to nearest, ties to even), as a bf16 nn.Linear output.
  */
@@ -193,8 +195,9 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * Backward of glu_dual_gemv: the gradients of hidden, gate_w and up_w for an
  * upstream gradient dout of out.  The segKI "Plan B" autograd Function keeps
  * hidden, gate_w and up_w and returns gradients equal to those of the
- * composite silu(h Wg^T) * (h Wu^T) (DeepSpeed PR #9057 discussion, sections
- * "Plan B Design" and "Verification Results"); over bf16 tensors each
+ * composite silu(h Wg^T) * (h Wu^T) (DeepSpeed PR #8602, comment "Plan B:
+ * Dual-Weight GEMV", sections "Plan B Design" and "Verification Results");
+ * over bf16 tensors each
  * gradient tensor is rounded once to bf16, round to nearest even, as
  * autograd of the bf16 composite rounds it.  With g, u, s the forward's bf16
  * gate, up and silu(g) (glu_dual_gemv):

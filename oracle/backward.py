@@ -3,11 +3,11 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 leg may import this module; it shares no code with the HIP library.
 
-What it computes.  The dual-weight GLU (DeepSpeed PR #9057 / segKI "Plan B
-Design") is an autograd Function that keeps hidden, gate_w and up_w for the
-backward, and the pages check that its gradients for all three equal those of
-the composite silu(h @ Wg^T) * (h @ Wu^T) (section "Verification Results",
-"Gradient exactness").  Read together with the forward's bf16 tensor
+What it computes.  The dual-weight GLU (DeepSpeed PR #8602, comment "Plan B:
+Dual-Weight GEMV", section "Plan B Design") is an autograd Function that keeps
+hidden, gate_w and up_w for the backward, and the same comment checks that its
+gradients for all three equal those of the composite silu(h @ Wg^T) *
+(h @ Wu^T) (section "Verification Results", "Gradient exactness").  Read together with the forward's bf16 tensor
 boundaries (PR #9057, "Changes"), the backward is autograd of that composite
 over bf16 tensors: each gradient tensor is computed in fp32 (or exactly) and
 rounded once to bf16, round to nearest even.  For every m < M, j < N, k < K,

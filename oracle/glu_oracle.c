@@ -31,8 +31,8 @@
  *      round once to bf16.  s*u is exact in fp32 unless it underflows.
  *
  * A second function, glu_oracle_linear, evaluates one projection of a
- * grouped GEMV: the pages' single/triple/quad GEMV kernels behind PR #8602's
- * grouped_linear(x, weights, glu_epilogue) dispatcher (commit notes), taken
+ * grouped GEMV: the pages' single/triple/quad GEMV kernels, which PR #9057
+ * (commit notes) folds into one grouped_linear(x, weights, glu_epilogue), taken
  * without the GLU epilogue, i.e. n nn.Linear projections of one hidden.  A
  * bf16 nn.Linear output is one bf16 tensor, so
  *   out[m,j] = RNE_bf16( sum_k h[m,k]*W[j,k] ),  the sum in fp64 as in 1.
