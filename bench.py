@@ -12,6 +12,11 @@ over time.
 Prints ONE JSON line.  Other modes:
   --workloads FILE     also time the batched workloads (JSON written to FILE);
                        --filter S keeps the sections whose name contains S
+  --ceiling FILE       also time the streaming-read yardstick (glu_read_ceiling:
+                       the GEMV's loads without its arithmetic) against the
+                       GEMV: on the 32-layer stack at several launch shapes,
+                       and at 12-357 MB per launch with a fit t = a + bytes/BW
+                       (JSON written to FILE)
   --calibrate-copy     run a 256 MiB device copy first (reference kernel for
                        rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE scaling)
   --summarize KIND DIR turn rocprofv3 output in DIR into the text summaries
@@ -119,8 +124,20 @@ def time_region(torch, fn, steps, warmup, stream):
     return start.elapsed_time(end)
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(torch, ws, hs, layers_sample: int, min_seconds: float):
-    """The oracle as it stands, on the host, over the first layers of the same stack."""
+    """The oracle as it stands, on the host, over the first layers of the same stack: once with all
+    the OpenMP threads it takes by default (the reported value) and once on one thread."""
     import numpy as np
     import oracle
 
@@ -128,21 +145,31 @@ def cpu_baseline(torch, ws, hs, layers_sample: int, min_seconds: float):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
     host = [(bits(ws[l][0]), bits(ws[l][1]), bits(hs[l:l + 1])) for l in range(layers_sample)]
-    threads = oracle.max_threads()
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        for wg, wu, h in host:
-            oracle.dual_gemv(h, wg, wu, threads=threads)
-            calls += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
     N, K = host[0][0].shape
-    gbs = calls * algorithmic_bytes(1, N, K) / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} oracle calls over layers 0-{layers_sample - 1} of the 32-layer "
-                      f"M=1 K={K} N={N} stack, {el:.1f} s wall, {threads} OpenMP threads"}
+
+    def timed(threads):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            for wg, wu, h in host:
+                oracle.dual_gemv(h, wg, wu, threads=threads)
+                calls += 1
+                if time.perf_counter() - t0 >= min_seconds:
+                    break
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                return calls, el
+
+    threads = oracle.max_threads()
+    calls, el = timed(threads)
+    calls1, el1 = timed(1)
+    per = algorithmic_bytes(1, N, K)
+    return {"value": round(calls * per / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(calls1 * per / el1 / 1e9, 3),
+            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{calls} oracle calls ({threads} OpenMP threads, {el:.1f} s wall) and {calls1} calls "
+                      f"(1 thread, {el1:.1f} s) over layers 0-{layers_sample - 1} of the 32-layer "
+                      f"M=1 K={K} N={N} stack; seconds per call {el / calls:.4f} and {el1 / calls1:.4f}"}
 
 
 BATCHED_ROUNDS = 6  # interleaved timing rounds of the batched workloads
@@ -323,6 +350,131 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
     return res
 
 
+PREWARM_SECONDS = 0.5     # untimed replays of the headline graph before its timed trials
+TRIALS = 5                # timed trials of the headline (Olympic average reported)
+
+
+def olympic(xs):
+    """Mean without the smallest and the largest value (of 3 or more)."""
+    s = sorted(xs)
+    return sum(s[1:-1]) / (len(s) - 2) if len(s) >= 3 else sum(s) / len(s)
+
+
+CEILING_ROUNDS = 5        # interleaved timing rounds of the yardstick comparisons (median reported)
+CEILING_ROWS = (1200, 2400, 4608, 9216, 18432, 34880)  # rows of K = 2560: 12-357 MB per launch
+CEILING_SHAPES = (        # (kernel, label, tuning fields) timed on the 32-layer stack
+    ("gemv", "default", {}),
+    ("ceiling", "default", {}),
+    ("ceiling", "xcd_bands", {"xcd_bands": 1}),
+    ("ceiling", "rows2", {"rows_per_wave": 2}),
+    ("ceiling", "grid256x4", {"grid": 256, "waves_per_block": 4}),
+    ("ceiling", "grid512x2", {"grid": 512, "waves_per_block": 2}),
+    ("ceiling", "rows2_grid256x4", {"rows_per_wave": 2, "grid": 256, "waves_per_block": 4}),
+    ("ceiling", "rows2_grid128x4", {"rows_per_wave": 2, "grid": 128, "waves_per_block": 4}),
+    ("gemv", "rows2", {"rows_per_wave": 2}),
+    ("gemv", "rows2_grid256x4", {"rows_per_wave": 2, "grid": 256, "waves_per_block": 4}),
+    ("gemv", "rows2_grid128x4", {"rows_per_wave": 2, "grid": 128, "waves_per_block": 4}),
+    ("gemv", "rows2_grid512x2", {"rows_per_wave": 2, "grid": 512, "waves_per_block": 2}),
+    ("gemv", "grid256x4", {"grid": 256, "waves_per_block": 4}),
+)
+
+
+def interleaved(torch, graphs, reps, stream, rounds=CEILING_ROUNDS):
+    """Median microseconds per replay of each graph, timed in interleaved rounds after 0.3 s of
+    untimed interleaved replays."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+    times = [[] for _ in graphs]
+    for _ in range(rounds):
+        for i, g in enumerate(graphs):
+            times[i].append(time_region(torch, g.replay, reps, 1, stream) * 1e3 / reps)
+    return [statistics.median(t) for t in times], times
+
+
+def fit_latency_bandwidth(points):
+    """Least-squares t = a + bytes / BW over (bytes, us) points: (a in us, BW in GB/s)."""
+    n = len(points)
+    xs = [b / 1e6 for b, _ in points]  # MB
+    ys = [t for _, t in points]
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx  # us per MB
+    a = my - slope * mx
+    return a, 1e3 / slope
+
+
+def bench_ceiling(torch, api, inputs, dev, ws, hs, reps=20, shapes=CEILING_SHAPES, sizes=True):
+    """The streaming-read yardstick against the GEMV: (1) the 32-layer stack at several launch shapes
+    of the yardstick, (2) both kernels at 12-357 MB per launch, fitted to t = a + bytes/BW."""
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    L = len(ws)
+    N, K = ws[0][0].shape
+    out = {"stack": [], "sizes": []}
+    outs = torch.empty(L, N, dtype=torch.bfloat16, device=dev)
+    graphs, labels = [], []
+    for kind, label, fields in shapes:
+        t = api.make_tuning(**fields) if fields else None
+        if kind == "gemv":
+            def stack(t=t):
+                for l in range(L):
+                    api.dual_gemv(hs[l], ws[l][0], ws[l][1], out=outs[l], tuning=t)
+            plan = api.plan(1, N, K, True, t)
+        else:
+            def stack(t=t):
+                for l in range(L):
+                    api.read_ceiling(ws[l][0], ws[l][1], sink, tuning=t)
+            plan = api.read_ceiling_plan(N, 2 * K, t)
+        graphs.append(capture(torch, stack))
+        labels.append((kind, label, fields, plan))
+    med, rounds = interleaved(torch, graphs, reps, stream)
+    b = algorithmic_bytes(1, N, K)
+    for (kind, label, fields, plan), us, ts in zip(labels, med, rounds):
+        per = us / L
+        out["stack"].append({"kernel": kind, "shape": label, "tuning": fields,
+                             "grid": plan["grid"], "block": plan["block"], "us_per_launch": round(per, 3),
+                             "GBs": round(b / per / 1e3, 1), "hbm_frac": round(b / per / 1e3 / HBM_PEAK_GBS, 4),
+                             "rounds_us_per_launch": [round(x / L, 3) for x in ts]})
+        print(f"[ceiling] {out['stack'][-1]}", file=sys.stderr, flush=True)
+    del graphs
+    torch.cuda.synchronize()
+    for rows in (CEILING_ROWS if sizes else ()):
+        per_set = 2 * rows * K * 2
+        sets = max(4, -(-1_400_000_000 // per_set))
+        pool = [inputs.weights(rows, K, 700 + i, device=dev) for i in range(sets)]
+        h = inputs.hidden(1, K, 0).to(dev)
+        o = torch.empty(1, rows, dtype=torch.bfloat16, device=dev)
+
+        def gemv_pool():
+            for wg, wu in pool:
+                api.dual_gemv(h, wg, wu, out=o)
+
+        def ceil_pool():
+            for wg, wu in pool:
+                api.read_ceiling(wg, wu, sink)
+        gs = [capture(torch, gemv_pool), capture(torch, ceil_pool)]
+        med, _ = interleaved(torch, gs, max(2, reps // 4), stream)
+        b = algorithmic_bytes(1, rows, K)
+        ent = {"rows": rows, "K": K, "bytes_per_launch": b, "pool_sets": sets,
+               "gemv_us": round(med[0] / sets, 3), "ceiling_us": round(med[1] / sets, 3),
+               "gemv_grid": api.plan(1, rows, K)["grid"], "ceiling_grid": api.read_ceiling_plan(rows, 2 * K)["grid"]}
+        ent["gemv_GBs"] = round(b / ent["gemv_us"] / 1e3, 1)
+        ent["ceiling_GBs"] = round(b / ent["ceiling_us"] / 1e3, 1)
+        out["sizes"].append(ent)
+        print(f"[ceiling] {ent}", file=sys.stderr, flush=True)
+        del gs, pool
+        torch.cuda.empty_cache()
+    for kind in (("gemv", "ceiling") if sizes else ()):
+        a, bw = fit_latency_bandwidth([(e["bytes_per_launch"], e[kind + "_us"]) for e in out["sizes"]])
+        out[kind + "_fit"] = {"a_us": round(a, 3), "BW_GBs": round(bw, 1),
+                              "at_94MB_frac": round(b94 / (a + b94 / bw / 1e3) / 1e3 / HBM_PEAK_GBS, 4)
+                              if (b94 := algorithmic_bytes(1, N, K)) else None}
+    return out
+
+
 def run(args):
     import torch
     from glu_mlp_gemv_amd import api, inputs
@@ -350,7 +502,12 @@ def run(args):
             api.dual_gemv(hs[l], ws[l][0], ws[l][1], out=outs[l], tuning=tuning)
 
     graph = capture(torch, step)
-    ms = time_region(torch, graph.replay, args.steps, args.warmup, stream)
+    # the first ~10 ms of replays of a fresh graph run slower: replay it untimed for PREWARM_SECONDS
+    # first (reported), then time TRIALS regions of exactly `steps` replays, each after `warmup`
+    # untimed ones, and take the Olympic average (drop the fastest and the slowest, mean of the rest)
+    warm(torch, graph.replay, PREWARM_SECONDS)
+    trials = [time_region(torch, graph.replay, args.steps, args.warmup, stream) for _ in range(TRIALS)]
+    ms = olympic(trials)
     ms_per_step = ms / args.steps
     bytes_call = algorithmic_bytes(M, N, K)
     gbs = bytes_call * L / (ms_per_step * 1e-3) / 1e9
@@ -390,6 +547,10 @@ def run(args):
                    "M": M, "K": K, "N": N, "layers": L, "bytes_per_call": bytes_call,
                    "us_per_call": round(launch_us * plan["launches"], 3),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "timing": {"prewarm_s": PREWARM_SECONDS, "trials": TRIALS, "average": "olympic",
+                              "trial_ms_per_step": [round(t / args.steps, 5) for t in trials],
+                              "median_ms_per_step": round(statistics.median(trials) / args.steps, 5),
+                              "min_ms_per_step": round(min(trials) / args.steps, 5)},
                    "eager_ms_per_step": None if ms_eager is None else round(ms_eager / args.steps, 5),
                    "kernel": kernel, "plan": plan, "accumulate": "fp32",
                    "tuning": json.loads(args.tuning) if args.tuning else None},
@@ -398,6 +559,12 @@ def run(args):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, ws, hs, layers_sample=4, min_seconds=args.cpu_seconds)
+    if args.ceiling:
+        shapes = [tuple(s) for s in json.loads(args.shapes)] if args.shapes else CEILING_SHAPES
+        res = bench_ceiling(torch, api, inputs, dev, ws, hs, shapes=shapes, sizes=not args.no_sizes)
+        os.makedirs(os.path.dirname(os.path.abspath(args.ceiling)), exist_ok=True)
+        with open(args.ceiling, "w") as f:
+            json.dump(res, f, indent=1)
     if args.workloads:
         extra = {"workloads": bench_workloads(torch, api, inputs, dev, only=args.filter), "stack": line}
         os.makedirs(os.path.dirname(os.path.abspath(args.workloads)), exist_ok=True)
@@ -520,6 +687,11 @@ def main():
     ap.add_argument("--filter", default=None, help="with --workloads: only the sections whose name contains this "
                                                    "(batched, prefill, backward, rows, grouped)")
     ap.add_argument("--tuning", default=None, help="JSON dict of glu_tuning fields")
+    ap.add_argument("--ceiling", default=None, metavar="FILE",
+                    help="also time the streaming-read yardstick against the GEMV")
+    ap.add_argument("--shapes", default=None, help="with --ceiling: JSON list of [kernel ('gemv' or 'ceiling'), "
+                                                   "label, tuning fields] timed on the stack")
+    ap.add_argument("--no-sizes", action="store_true", help="with --ceiling: skip the 12-357 MB size sweep")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"))
     ap.add_argument("--command", default="", help="the profiled command, recorded in counter summaries")

@@ -22,9 +22,11 @@ GLU_OK = 0
 GLU_ERR_UNSUPPORTED = 6
 GLU_ERR_BAD_STRIDE = 7
 GLU_ERR_WORKSPACE = 8
-KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC, KERNEL_GEMM, KERNEL_BACKWARD = range(7)
+(KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC, KERNEL_GEMM, KERNEL_BACKWARD,
+ KERNEL_CEILING) = range(8)
 KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
-                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic", KERNEL_GEMM: "gemm", KERNEL_BACKWARD: "backward"}
+                KERNEL_MFMA: "mfma", KERNEL_GENERIC: "generic", KERNEL_GEMM: "gemm", KERNEL_BACKWARD: "backward",
+                KERNEL_CEILING: "ceiling"}
 
 EXPORTED_SYMBOLS = (
     "glu_dual_gemv",
@@ -45,6 +47,8 @@ EXPORTED_SYMBOLS = (
     "glu_dual_gemv_backward",
     "glu_dual_gemv_backward_workspace",
     "glu_dual_gemv_backward_plan",
+    "glu_read_ceiling",
+    "glu_read_ceiling_plan",
 )
 
 
@@ -69,7 +73,8 @@ class Plan(ctypes.Structure):
 class Tuning(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("rows_per_wave", ctypes.c_int), ("waves_per_block", ctypes.c_int),
                 ("grid", ctypes.c_int), ("mfma_segments", ctypes.c_int), ("mfma_hidden", ctypes.c_int),
-                ("mfma_depth", ctypes.c_int), ("gemm_tile_n", ctypes.c_int), ("gemm_tile_m", ctypes.c_int)]
+                ("mfma_depth", ctypes.c_int), ("gemm_tile_n", ctypes.c_int), ("gemm_tile_m", ctypes.c_int),
+                ("xcd_bands", ctypes.c_int), ("mfma_order", ctypes.c_int)]
 
 
 class Projection(ctypes.Structure):
@@ -134,6 +139,10 @@ def library() -> ctypes.CDLL:
     lib.glu_dual_gemv_backward_workspace.restype = ctypes.c_int
     lib.glu_dual_gemv_backward_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     lib.glu_dual_gemv_backward_plan.restype = ctypes.c_int
+    lib.glu_read_ceiling.argtypes = [vp, vp, i64, i64, vp, ctypes.POINTER(Tuning), vp]
+    lib.glu_read_ceiling.restype = ctypes.c_int
+    lib.glu_read_ceiling_plan.argtypes = [i64, i64, ctypes.POINTER(Tuning), ctypes.POINTER(Plan)]
+    lib.glu_read_ceiling_plan.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -441,3 +450,29 @@ def grouped_gemv_raw(hidden_ptr: int, ldh: int, projections, M: int, K: int, str
     for i, p in enumerate(projections):
         arr[i] = Projection(*p)
     return lib.glu_grouped_gemv(hidden_ptr, ldh, arr, len(projections) if n is None else n, M, K, stream_handle)
+
+
+def read_ceiling_plan(rows: int, row_bytes: int, tuning: Optional[Tuning] = None) -> dict:
+    """Launch shape of the streaming-read yardstick (host only)."""
+    p = Plan()
+    st = library().glu_read_ceiling_plan(rows, row_bytes, ctypes.byref(tuning) if tuning is not None else None,
+                                         ctypes.byref(p))
+    _raise_for(st)
+    d = p.as_dict()
+    d["kernel_symbol"] = "glu::(anonymous namespace)::read_ceiling_kernel"
+    return d
+
+
+def read_ceiling(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor, tuning: Optional[Tuning] = None) -> None:
+    """Streaming-read yardstick over two equal 2-D device tensors (rows of a multiple of 1 KiB): reads them
+    as the M = 1 GEMV reads its weights.  sink: >= 64 int32 on the same device."""
+    if a.dim() != 2 or a.shape != b.shape or a.dtype != b.dtype:
+        raise ValueError("a and b must be 2-D tensors of one shape and dtype")
+    if not (a.is_contiguous() and b.is_contiguous() and sink.is_contiguous()):
+        raise ValueError("a, b and sink must be contiguous")
+    if sink.numel() * sink.element_size() < 256 or not (a.device == b.device == sink.device) or a.device.type != "cuda":
+        raise ValueError("sink must hold 64 32-bit words on the device of a and b")
+    st = library().glu_read_ceiling(a.data_ptr(), b.data_ptr(), a.shape[0], a.shape[1] * a.element_size(),
+                                    sink.data_ptr(), ctypes.byref(tuning) if tuning is not None else None,
+                                    torch.cuda.current_stream(a.device).cuda_stream)
+    _raise_for(st)

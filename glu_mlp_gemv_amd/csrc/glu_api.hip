@@ -195,6 +195,17 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
         grid = ceil_div(balanced_waves(groups, (int64_t)kCUs * kMfmaWavesPerCU), waves);
     }
     c.grid = (int)(grid < 1 ? 1 : grid);
+    // 8 rows per wave: the order of the K walk (block by block, or K once for up to
+    // kPassBlocks blocks of a workgroup, each hidden slice loaded once for all of them)
+    const int order_req = t ? t->mfma_order : 0;
+    if (order_req < 0 || order_req > 2 || (order_req && c.rows != 8)) return GLU_ERR_UNSUPPORTED;
+    c.order = glu::kOrderBlocks;
+    if (c.rows == 8) {
+        const bool pass_fits = c.U == 8 && c.depth == 1 && m_pl > 8 &&
+                               (int64_t)c.grid * glu::kPassBlocks >= glu::mfma8_blocks(N);
+        if (order_req == 2 && !pass_fits) return GLU_ERR_UNSUPPORTED;
+        c.order = order_req == 2 ? glu::kOrderSlices : glu::kOrderBlocks;
+    }
     if (c.hidden == glu::kHiddenSlices && c.block != glu::kMfmaMaxThreads) return GLU_ERR_UNSUPPORTED;
     if (!glu::mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
     L->kernel = GLU_KERNEL_MFMA;
@@ -240,7 +251,7 @@ glu_status plan_gemm(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     return GLU_OK;
 }
 
-glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const glu_tuning* t, Launch* L)
+glu_status plan_launch_any(int64_t M, int64_t N, int64_t K, bool aligned16, const glu_tuning* t, Launch* L)
 {
     if (M < 0 || N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return GLU_ERR_BAD_SHAPE;
     const int64_t lim = INT64_MAX / 2;  // element counts must also fit as byte counts
@@ -256,6 +267,7 @@ glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const gl
         return GLU_OK;
     }
     const int forced = t ? t->kernel : 0;
+    if (t && t->xcd_bands) return GLU_ERR_UNSUPPORTED;  // only the streaming-read yardstick takes it
     const bool fast = aligned16 && (K % 8 == 0) && K <= kMaxFastK;
     if (forced != 0 && forced != GLU_KERNEL_GENERIC && !fast) return GLU_ERR_UNSUPPORTED;
     const bool gemm_fields = t && (t->gemm_tile_n || t->gemm_tile_m);
@@ -276,6 +288,50 @@ glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const gl
     L->generic_grid = (int)ceil_div(N, 4);
     L->accum_depth = (int)ceil_div(K, glu::kWave) + glu::kWaveSumDepth;
     return GLU_OK;
+}
+
+// Streaming-read ceiling: the VALU GEMV's launch shape for two matrices of `rows`
+// rows of row_bytes bytes (a row of K bf16 weights is 2K bytes).
+struct CeilingLaunch {
+    int U = 0, R = 0, grid = 0, block = 0;
+    bool xcd_bands = false;
+};
+
+glu_status plan_ceiling(int64_t rows, int64_t row_bytes, const glu_tuning* t, CeilingLaunch* c)
+{
+    if (rows < 0 || row_bytes < 0 || rows > kMaxDim) return GLU_ERR_BAD_SHAPE;
+    if (mul_overflows(rows, row_bytes, INT64_MAX / 2)) return GLU_ERR_BAD_SHAPE;
+    if (t && (t->kernel || t->mfma_segments || t->mfma_hidden || t->mfma_depth || t->gemm_tile_n ||
+              t->gemm_tile_m)) {
+        return GLU_ERR_UNSUPPORTED;
+    }
+    *c = CeilingLaunch{};
+    if (rows == 0) return GLU_OK;
+    if (row_bytes == 0 || row_bytes % 1024 != 0) return GLU_ERR_UNSUPPORTED;
+    c->U = (int)(row_bytes / 1024 < 9 ? row_bytes / 1024 : 0);
+    c->R = (t && t->rows_per_wave) ? t->rows_per_wave : 1;
+    if (!glu::read_ceiling_supported(c->U, c->R)) return GLU_ERR_UNSUPPORTED;
+    const int waves = (t && t->waves_per_block) ? t->waves_per_block : kValuDefaultWaves;
+    if (waves < 1 || waves * glu::kWave > glu::kValuMaxThreads) return GLU_ERR_UNSUPPORTED;
+    c->block = waves * glu::kWave;
+    const int64_t groups = ceil_div(rows, c->R);
+    const int64_t grid = (t && t->grid > 0) ? t->grid
+                                            : ceil_div(balanced_waves(groups, (int64_t)kCUs * kValuWavesPerCU), waves);
+    c->grid = (int)(grid < 1 ? 1 : grid);
+    c->xcd_bands = t && t->xcd_bands;
+    if (c->xcd_bands && c->grid % glu::kXcds != 0) return GLU_ERR_UNSUPPORTED;
+    return GLU_OK;
+}
+
+glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const glu_tuning* t, Launch* L)
+{
+    const glu_status st = plan_launch_any(M, N, K, aligned16, t, L);
+    // the K-walk order is a field of the 8-row MFMA kernel only
+    if (st == GLU_OK && t && t->mfma_order && L->kernel != GLU_KERNEL_NONE &&
+        !(L->kernel == GLU_KERNEL_MFMA && L->mfma.rows == 8)) {
+        return GLU_ERR_UNSUPPORTED;
+    }
+    return st;
 }
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes)
@@ -395,7 +451,7 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
         return GLU_OK;
     }
     const int forced = t ? t->kernel : 0;
-    if (t && (t->gemm_tile_n || t->gemm_tile_m)) return GLU_ERR_UNSUPPORTED;
+    if (t && (t->gemm_tile_n || t->gemm_tile_m || t->xcd_bands || t->mfma_order)) return GLU_ERR_UNSUPPORTED;
     const bool mfma_fields = t && (t->mfma_segments || t->mfma_hidden || t->mfma_depth);
     const bool mfma = fast && mult4 && (forced == GLU_KERNEL_MFMA || (forced == 0 && (M >= 2 || mfma_fields)));
     if (forced == GLU_KERNEL_MFMA && !mfma) return GLU_ERR_UNSUPPORTED;
@@ -841,6 +897,9 @@ void describe_launch(const Launch& L, bool grouped, char* buf, int len)
         } else if (grouped) {
             snprintf(buf, (size_t)len, "glu::grouped_mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,
                      tf[c.hidden == glu::kHiddenLds], tf[c.ragged]);
+        } else if (c.hidden == glu::kHiddenSlices && c.rows == 8 && c.order == glu::kOrderSlices) {
+            snprintf(buf, (size_t)len, "glu::mfma8_pass_kernel<%d, %d, %d, %s>", (4 * c.MT4 + 7) / 8, c.U,
+                     glu::kPassBlocks, tf[c.ragged]);
         } else if (c.hidden == glu::kHiddenSlices && c.rows == 8) {
             snprintf(buf, (size_t)len, "glu::mfma8_slice_kernel<%d, %d, %d, %s>", (4 * c.MT4 + 7) / 8, c.U,
                      c.depth, tf[c.ragged]);
@@ -934,6 +993,38 @@ glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w
 {
     return run_backward(hidden, gate_w, up_w, dout, dhidden, dgate_w, dup_w, M, N, K, workspace, workspace_bytes,
                         stream);
+}
+
+glu_status glu_read_ceiling_plan(int64_t rows, int64_t row_bytes, const glu_tuning* tuning, glu_plan* plan)
+{
+    if (!plan) return GLU_ERR_NULL_POINTER;
+    CeilingLaunch c;
+    const glu_status st = plan_ceiling(rows, row_bytes, tuning, &c);
+    if (st != GLU_OK) return st;
+    *plan = glu_plan{};
+    plan->kernel = rows > 0 ? GLU_KERNEL_CEILING : GLU_KERNEL_NONE;
+    plan->m_per_launch = 0;
+    plan->launches = rows > 0 ? 1 : 0;
+    plan->grid = c.grid;
+    plan->block = c.block;
+    plan->accum_depth = 0;
+    return GLU_OK;
+}
+
+glu_status glu_read_ceiling(const void* a, const void* b, int64_t rows, int64_t row_bytes, uint32_t* sink,
+                            const glu_tuning* tuning, void* stream)
+{
+    CeilingLaunch c;
+    glu_status st = plan_ceiling(rows, row_bytes, tuning, &c);
+    if (st != GLU_OK) return st;
+    if (rows == 0) return GLU_OK;
+    if (!a || !b || !sink) return GLU_ERR_NULL_POINTER;
+    if ((((uintptr_t)a | (uintptr_t)b) & 15u) != 0 || ((uintptr_t)sink & 3u) != 0) return GLU_ERR_MISALIGNED;
+    const int64_t bytes = rows * row_bytes;
+    if (overlaps(sink, 64 * 4, a, bytes) || overlaps(sink, 64 * 4, b, bytes)) return GLU_ERR_ALIASING;
+    const hipError_t e = glu::read_ceiling_launch(a, b, (int)rows, c.U, c.R, c.grid, c.block, c.xcd_bands, sink,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? GLU_OK : fail_launch(e);
 }
 
 const char* glu_status_string(int status)

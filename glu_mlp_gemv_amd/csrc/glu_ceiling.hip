@@ -1,0 +1,144 @@
+// Streaming-read ceiling: the HBM access of the M = 1 VALU GEMV with its
+// arithmetic taken out, as a yardstick for what that kernel can reach.
+//
+// The decode projection is bound by reading both weight matrices once (DeepSpeed
+// PR #8602, comment "Plan B: Dual-Weight GEMV", section on why library-level
+// bandwidth is reachable at batch 1, which puts the remaining gap down to launch
+// overhead and the access pattern).  This kernel reads two [rows, row_bytes]
+// matrices exactly as valu_kernel reads gate_w and up_w: persistent waves own the
+// row groups w, w+W, ... of R rows, lane l loads the 16-byte chunks l, l+64, ...
+// of every row with nontemporal global_load_dwordx4, and two register buffers
+// keep the next group's loads in flight while the current group is consumed.
+// Consuming a group is an XOR of its words into one register; a store that
+// depends on that register (taken only for one 32-bit value) keeps the loads
+// alive.  Whatever time separates the GEMV from this kernel at the same launch
+// shape is arithmetic, reduction and epilogue; whatever separates this kernel
+// from the bytes at peak bandwidth is the memory system and the launch.
+#include "glu_launch.h"
+
+namespace glu {
+
+namespace {
+
+typedef unsigned u32x4c __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kSinkMagic = 0x7f3a5c91u;  // the store happens only if the XOR equals this
+
+// Workgroup order.  The dispatcher deals consecutive workgroups to the 8 XCDs in
+// turn, so by default the workgroups one XCD runs are spread over the whole row
+// space.  With xcd_bands, workgroup b takes the logical index (b % 8) * (G / 8) +
+// b / 8 (G a multiple of 8): each XCD streams one contiguous band of rows.
+__device__ __forceinline__ int logical_block(bool xcd_bands)
+{
+    const int b = blockIdx.x, G = gridDim.x;
+    return xcd_bands ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+}
+
+// rows of both matrices [rows, U * 1024 bytes], 16-byte aligned; sink: 64 words
+template <int U, int R>
+__global__ void __launch_bounds__(kValuMaxThreads)
+read_ceiling_kernel(const u32x4c* __restrict__ a, const u32x4c* __restrict__ b, int rows, uint32_t* sink,
+                    bool xcd_bands)
+{
+    constexpr int CPR = U * kWave;  // 16-byte chunks per row
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int wave_id = __builtin_amdgcn_readfirstlane(logical_block(xcd_bands) * wpb + threadIdx.x / kWave);
+    const int nwaves = gridDim.x * wpb;
+    const int ngroups = (rows + R - 1) / R;
+    if (wave_id >= ngroups) return;
+    const int nsteps = (ngroups - 1 - wave_id) / nwaves + 1;
+
+    auto load = [&](int s, u32x4c (&x)[R][U], u32x4c (&y)[R][U]) {
+        const int g = wave_id + s * nwaves;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(g * R + r, rows - 1);
+            const u32x4c* pa = a + (int64_t)row * CPR + lane;
+            const u32x4c* pb = b + (int64_t)row * CPR + lane;
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                x[r][i] = __builtin_nontemporal_load(pa + i * kWave);
+                y[r][i] = __builtin_nontemporal_load(pb + i * kWave);
+            }
+        }
+    };
+    uint32_t acc = 0;
+    auto consume = [&](const u32x4c (&x)[R][U], const u32x4c (&y)[R][U]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const u32x4c v = x[r][i] ^ y[r][i];
+                acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+            }
+        }
+    };
+
+    u32x4c xa[R][U], ya[R][U], xb[R][U], yb[R][U];
+    load(0, xa, ya);
+    int s = 0;
+    while (true) {
+        if (s + 1 >= nsteps) {
+            consume(xa, ya);
+            break;
+        }
+        load(s + 1, xb, yb);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(xa, ya);
+        ++s;
+        if (s + 1 >= nsteps) {
+            consume(xb, yb);
+            break;
+        }
+        load(s + 1, xa, ya);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(xb, yb);
+        ++s;
+    }
+    if (acc == kSinkMagic) sink[lane] = acc;
+}
+
+using CeilingFn = void (*)(const u32x4c*, const u32x4c*, int, uint32_t*, bool);
+
+template <int R>
+CeilingFn pick_u(int U)
+{
+    switch (U) {
+    case 1: return read_ceiling_kernel<1, R>;
+    case 2: return read_ceiling_kernel<2, R>;
+    case 3: return read_ceiling_kernel<3, R>;
+    case 4: return read_ceiling_kernel<4, R>;
+    case 5: return read_ceiling_kernel<5, R>;
+    case 6: return read_ceiling_kernel<6, R>;
+    case 7: return read_ceiling_kernel<7, R>;
+    case 8: return read_ceiling_kernel<8, R>;
+    default: return nullptr;
+    }
+}
+
+CeilingFn pick(int U, int R)
+{
+    switch (R) {
+    case 1: return pick_u<1>(U);
+    case 2: return pick_u<2>(U);
+    case 4: return pick_u<4>(U);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+bool read_ceiling_supported(int U, int R) { return pick(U, R) != nullptr; }
+
+hipError_t read_ceiling_launch(const void* a, const void* b, int rows, int U, int R, int grid, int block,
+                               bool xcd_bands, uint32_t* sink, hipStream_t stream)
+{
+    CeilingFn fn = pick(U, R);
+    if (!fn || (xcd_bands && grid % kXcds != 0)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(block), 0, stream, static_cast<const u32x4c*>(a),
+                       static_cast<const u32x4c*>(b), rows, sink, xcd_bands);
+    return hipGetLastError();
+}
+
+}  // namespace glu

@@ -13,6 +13,7 @@ constexpr int kValuMaxThreads = 512;
 constexpr int kLdsBudget = 64 * 1024;  // dynamic LDS per workgroup, bytes
 constexpr int kLdsMax = 160 * 1024;    // LDS of one workgroup on gfx950, bytes
 constexpr int kMfmaMaxThreads = 256;  // 4 waves: the compiler may use AGPRs for the accumulators
+constexpr int kXcds = 8;               // accelerator complex dies of an MI355X; workgroups are dealt to them in turn
 
 struct ValuConfig {
     int M;        // rows of hidden in this launch (1..8)
@@ -29,6 +30,11 @@ constexpr int kHiddenLds = 0;     // all of it in LDS (mfma_hidden_lds_bytes <= 
 constexpr int kHiddenL2 = 1;      // read from L2 with each stage's weights
 constexpr int kHiddenSlices = 2;  // per-stage K-slices in an LDS ring, waves in lockstep
 
+// Order of the 8-row K-slice kernel's work (MfmaConfig::order)
+constexpr int kOrderBlocks = 0;  // each block of 4 groups walks K in turn
+constexpr int kOrderSlices = 1;  // K walked once for all of a workgroup's blocks (at most kPassBlocks)
+constexpr int kPassBlocks = 3;
+
 struct MfmaConfig {
     int rows;         // weight rows per wave: 4, or 8 (kHiddenSlices only)
     int MT4;          // hidden-row tiles of 4 (M <= 4 * MT4 <= 32)
@@ -37,6 +43,7 @@ struct MfmaConfig {
     bool ragged;      // the stages run past K: clamp and zero the excess chunks
     int hidden;       // kHiddenLds, kHiddenL2 or kHiddenSlices
     int depth;        // kHiddenSlices: pipeline stages of weights in flight
+    int order;        // 8 rows per wave: kOrderBlocks or kOrderSlices
     int grid;         // workgroups (persistent)
     int block;        // threads per workgroup (multiple of 64)
 };
@@ -76,13 +83,22 @@ size_t mfma_hidden_lds_bytes(int m, int64_t k);
 // the 8-row lockstep kernel (glu_mfma8.hip): mt8 hidden tiles of 8 rows
 size_t mfma8_slice_lds_bytes(int mt8, int u);
 int mfma8_slice_depth(int u);
-bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block);
-hipError_t mfma8_launch(int M, int U, int depth, int nsg, bool ragged, int grid, const uint16_t* hidden,
+// order: kOrderBlocks walks K per block of 4 groups in turn (mfma8_slice_kernel); kOrderSlices walks K
+// once for all of a workgroup's blocks (mfma8_pass_kernel: U == 8, depth 1, grid * kPassBlocks >= blocks)
+bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block, int order);
+int64_t mfma8_blocks(int64_t N);  // blocks of 4 groups of 8 weight rows
+hipError_t mfma8_launch(int M, int U, int depth, int order, int nsg, bool ragged, int grid, const uint16_t* hidden,
                         const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K,
                         RowStrides ld, hipStream_t stream);
 hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K, RowStrides ld,
                        hipStream_t stream);
+
+// Streaming-read ceiling (glu_ceiling.hip): two [rows, U * 1024 bytes] matrices read
+// as the VALU GEMV reads gate_w and up_w, R rows per group, U in 1..8, R in {1, 2, 4}.
+bool read_ceiling_supported(int U, int R);
+hipError_t read_ceiling_launch(const void* a, const void* b, int rows, int U, int R, int grid, int block,
+                               bool xcd_bands, uint32_t* sink, hipStream_t stream);
 
 // Any alignment (2-byte), any K >= 1, any strides; M <= 8 per launch.
 hipError_t generic_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,

@@ -450,7 +450,8 @@ size_t mfma_hidden_lds_bytes(int m, int64_t k)
 bool mfma_supported(const MfmaConfig& c)
 {
     if (c.rows == 8) {
-        return c.hidden == kHiddenSlices && mfma8_supported((4 * c.MT4 + 7) / 8, c.U, c.depth, c.ragged, c.block);
+        return c.hidden == kHiddenSlices &&
+               mfma8_supported((4 * c.MT4 + 7) / 8, c.U, c.depth, c.ragged, c.block, c.order);
     }
     if (c.rows != 4) return false;
     if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
@@ -464,7 +465,8 @@ hipError_t mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const
 {
     if (c.rows == 8) {
         if (c.hidden != kHiddenSlices) return hipErrorInvalidValue;
-        return mfma8_launch(M, c.U, c.depth, c.nsg, c.ragged, c.grid, hidden, gate_w, up_w, out, N, K, ld, stream);
+        return mfma8_launch(M, c.U, c.depth, c.order, c.nsg, c.ragged, c.grid, hidden, gate_w, up_w, out, N, K, ld,
+                            stream);
     }
     MfmaConfig cm = c;
     cm.MT4 = (M + 3) / 4;

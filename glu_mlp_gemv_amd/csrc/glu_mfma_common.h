@@ -44,4 +44,14 @@ __device__ __forceinline__ void run_stages(F& f, int s0, int n)
     }
 }
 
+// calls f(integral_constant<Q>) for Q = Q0 .. L-1
+template <int Q, int L, class F>
+__device__ __forceinline__ void for_positions(F& f)
+{
+    if constexpr (Q < L) {
+        f(std::integral_constant<int, Q>{});
+        for_positions<Q + 1, L>(f);
+    }
+}
+
 }  // namespace glu

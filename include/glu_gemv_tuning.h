@@ -37,6 +37,12 @@ typedef struct glu_tuning {
                              flight while a stage computes (1 to 4) */
     int gemm_tile_n;      /* GEMM: weight rows per output tile (64 or 128) */
     int gemm_tile_m;      /* GEMM: hidden rows per output tile (64 or 128) */
+    int xcd_bands;        /* glu_read_ceiling: 1 = the workgroups one XCD runs take one
+                             contiguous band of rows (grid a multiple of 8) */
+    int mfma_order;       /* MFMA, 8 rows per wave: 1 = each block of 32 weight rows walks K
+                             in turn; 2 = a workgroup walks K once for all its blocks (at
+                             most 3), loading each K-slice of hidden once (8 segments,
+                             depth 1, more than 8 rows of hidden) */
 } glu_tuning;
 
 glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
@@ -77,6 +83,35 @@ glu_status glu_dual_gemv_describe(int64_t M, int64_t N, int64_t K, int aligned16
  * (glu_gemv.h), e.g. "glu::grouped_mfma_kernel<1, 5, true, false>". */
 glu_status glu_grouped_gemv_describe(int64_t M, int64_t K, int64_t rows, int fast, const glu_tuning* tuning,
                                      char* buf, int len);
+
+/*
+ * Streaming-read ceiling, a measuring stick for the M = 1 GEMV rather than a
+ * part of the projection.  The pages put the GEMV's distance from peak
+ * bandwidth down to launch overhead and the memory access pattern (DeepSpeed
+ * PR #8602, comment "Plan B: Dual-Weight GEMV", section on why library-level
+ * performance is reachable at batch 1); this call isolates those two.  It
+ * reads two matrices a and b of `rows` rows of row_bytes bytes each (dense,
+ * device memory, 16-byte aligned) with the GEMV's own access pattern and
+ * launch shape (glu_dual_gemv_plan at M = 1 and K = row_bytes / 2: the same
+ * grid, waves and rows per wave; `tuning` may override rows_per_wave (1, 2 or
+ * 4), waves_per_block, grid and xcd_bands, nothing else) and does no arithmetic beyond
+ * an XOR of the words read.  sink: 64 uint32 of device memory, written only if
+ * that XOR equals one fixed 32-bit value (it exists so that the loads cannot
+ * be removed); it may not overlap a or b.
+ *
+ * row_bytes must be a multiple of 1024 up to 8192 (K = 512 ... 4096 bf16),
+ * else GLU_ERR_UNSUPPORTED.  rows == 0: GLU_OK, nothing launched.  Errors as
+ * glu_dual_gemv (NULL -> GLU_ERR_NULL_POINTER, alignment ->
+ * GLU_ERR_MISALIGNED, sink overlapping -> GLU_ERR_ALIASING, shape ->
+ * GLU_ERR_BAD_SHAPE), decided before any HIP call.  Asynchronous on stream,
+ * graph-capturable, allocates nothing.
+ */
+glu_status glu_read_ceiling(const void* a, const void* b, int64_t rows, int64_t row_bytes, uint32_t* sink,
+                            const glu_tuning* tuning, void* stream);
+
+/* The launch glu_read_ceiling would make (host only, no HIP call):
+ * kernel GLU_KERNEL_CEILING, grid and block. */
+glu_status glu_read_ceiling_plan(int64_t rows, int64_t row_bytes, const glu_tuning* tuning, glu_plan* plan);
 
 #ifdef __cplusplus
 }

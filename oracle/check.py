@@ -45,6 +45,24 @@ from . import DualGemvResult, LinearResult, round_bf16, silu_bf16
 U32 = 2.0 ** -24  # unit roundoff of fp32
 SMALL_SAMPLE_SLACK = 3  # non-bit-exact outputs always allowed (each still within the ULP bar)
 
+# Every report made in this process, so that a test session can state how much of the bar's
+# slack was used: outputs admitted by the interval, of those the ones inside only its +-2 ULP
+# widening, reports that met the bit-exact bar only through SMALL_SAMPLE_SLACK, and grouped
+# calls that met it only as a pooled rate.
+LEDGER: list = []
+POOLED_ONLY: list = []
+
+
+def slack_summary() -> dict:
+    reps = [r for r in LEDGER]
+    return {"reports": len(reps), "outputs": sum(r.n for r in reps),
+            "over_2ulp": sum(r.over_2ulp for r in reps),
+            "interval_pass": sum(r.interval_pass for r in reps),
+            "widened_pass": sum(r.widened_pass for r in reps),
+            "small_sample_slack_reports": sum(1 for r in reps if r.slack_used),
+            "pooled_only_calls": len(POOLED_ONLY),
+            "failures": sum(r.failures for r in reps)}
+
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
@@ -119,6 +137,7 @@ class Report:
     interval_pass: int = 0
     interval_max_kappa: float = 0.0
     interval_min_kappa: float = float("inf")
+    widened_pass: int = 0  # interval passes inside the +-2 ULP widening only (compare)
     failures: int = 0
     bit_exact_frac: float = 1.0
     mean_rel: float = 0.0
@@ -131,6 +150,11 @@ class Report:
         return self.bit_exact_frac >= 0.999 or inexact <= SMALL_SAMPLE_SLACK
 
     @property
+    def slack_used(self) -> bool:
+        """The bit-exact bar was met only through SMALL_SAMPLE_SLACK."""
+        return self.bit_exact_frac < 0.999 and self.bit_exact_ok
+
+    @property
     def ok(self) -> bool:
         return self.failures == 0 and self.bit_exact_ok and self.mean_rel <= 3e-3
 
@@ -140,8 +164,9 @@ class Report:
 
     def summary(self) -> str:
         s = (f"n={self.n} max_ulp={self.max_ulp} over2={self.over_2ulp} "
-             f"interval_pass={self.interval_pass} (kappa {self.interval_min_kappa:.3g}..{self.interval_max_kappa:.3g}) "
-             f"failures={self.failures} bit_exact={self.bit_exact_frac:.6f} "
+             f"interval_pass={self.interval_pass} (kappa {self.interval_min_kappa:.3g}..{self.interval_max_kappa:.3g}; "
+             f"{self.widened_pass} only in the widening) "
+             f"failures={self.failures} bit_exact={self.bit_exact_frac:.6f}{' (slack)' if self.slack_used else ''} "
              f"mean_rel={self.mean_rel:.3e}")
         if self.failure_info:
             s += f" first failures: {self.failure_info[:3]}"
@@ -185,6 +210,7 @@ def compare(got: np.ndarray, ref: DualGemvResult, depth: int, k_len: int,
             ok = lo - 2 <= o <= hi + 2
         if ok:
             rep.interval_pass += 1
+            rep.widened_pass += int(not (lo <= o <= hi))
             rep.interval_max_kappa = max(rep.interval_max_kappa, float(kappa))
             rep.interval_min_kappa = min(rep.interval_min_kappa, float(kappa))
         else:
@@ -197,6 +223,7 @@ def compare(got: np.ndarray, ref: DualGemvResult, depth: int, k_len: int,
                 if lo is not None:
                     info["interval"] = [lo, hi, o]
                 rep.failure_info.append(info)
+    LEDGER.append(rep)
     return rep
 
 
@@ -240,6 +267,7 @@ def compare_linear(got: np.ndarray, ref: LinearResult, depth: int, k_len: int, m
                 if lo is not None:
                     info["interval"] = [lo, hi, o]
                 rep.failure_info.append(info)
+    LEDGER.append(rep)
     return rep
 
 
@@ -284,6 +312,7 @@ def compare_grad_sum(got: np.ndarray, want: np.ndarray, A: np.ndarray, Aabs: np.
                 rep.failure_idx.append(int(i))
                 rep.failure_info.append({"index": int(i), "got": f"{int(got[i]):#06x}",
                                          "want": f"{int(want[i]):#06x}", "ulp": int(d[i])})
+    LEDGER.append(rep)
     return rep
 
 
@@ -300,4 +329,7 @@ def pooled_bit_exact_ok(reports: List[Report]) -> bool:
     """The bit-exact bar over every output of one call that writes several projections."""
     n = sum(r.n for r in reports)
     inexact = sum(r.inexact for r in reports)
-    return n == 0 or inexact <= 1e-3 * n or inexact <= SMALL_SAMPLE_SLACK
+    ok = n == 0 or inexact <= 1e-3 * n or inexact <= SMALL_SAMPLE_SLACK
+    if ok and not all(r.bit_exact_ok for r in reports):
+        POOLED_ONLY.append((n, inexact))
+    return ok

@@ -472,3 +472,97 @@ def test_backward_shape_limits(lib):
     assert api.dual_gemv_backward_raw(*p[:7], 2, 64, 100, p[7], ws) == UNSUP      # K % 8 != 0
     assert api.dual_gemv_backward_raw(*p[:7], -1, 64, 128, p[7], ws) == SHAPE
     assert api.dual_gemv_backward_raw(*p[:7], 2, 1 << 40, 1 << 40, p[7], ws) == SHAPE
+
+
+def test_read_ceiling_plan_matches_the_gemv_launch(lib):
+    # the yardstick runs the M = 1 GEMV's launch shape on the GEMV's bytes
+    for N, K in ((9216, 2560), (3000, 1024), (12288, 4096), (34880, 2560)):
+        g = api.plan(1, N, K)
+        c = api.read_ceiling_plan(N, 2 * K)
+        assert c["kernel"] == api.KERNEL_CEILING
+        assert (c["grid"], c["block"]) == (g["grid"], g["block"])
+    t = api.make_tuning(rows_per_wave=2, waves_per_block=8, grid=128, xcd_bands=1)
+    c = api.read_ceiling_plan(9216, 5120, t)
+    assert (c["grid"], c["block"]) == (128, 512)
+    assert api.read_ceiling_plan(0, 5120)["kernel"] == api.KERNEL_NONE
+
+
+@pytest.mark.parametrize("rows,row_bytes,tuning,status", [
+    (9216, 5000, None, UNSUP),             # not a multiple of 1 KiB
+    (9216, 9216, None, UNSUP),             # more than 8 KiB per row
+    (-1, 5120, None, SHAPE),
+    (1 << 40, 5120, None, SHAPE),
+    (9216, 5120, dict(rows_per_wave=3), UNSUP),
+    (9216, 5120, dict(kernel=2), UNSUP),
+    (9216, 5120, dict(grid=100, xcd_bands=1), UNSUP),   # bands need a grid that is a multiple of 8
+    (9216, 5120, dict(waves_per_block=9), UNSUP),
+])
+def test_read_ceiling_plan_rejects(lib, rows, row_bytes, tuning, status):
+    p = api.Plan()
+    t = api.make_tuning(**tuning) if tuning else None
+    assert lib.glu_read_ceiling_plan(rows, row_bytes, ctypes.byref(t) if t else None, ctypes.byref(p)) == status
+
+
+A16 = 1 << 32            # a: 16 rows of 5120 bytes
+B16 = A16 + (1 << 20)    # b
+S16 = A16 + (1 << 21)    # sink
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, B16, 16, 5120, S16), NULLP),
+    ((A16, 0, 16, 5120, S16), NULLP),
+    ((A16, B16, 16, 5120, 0), NULLP),
+    ((A16 + 8, B16, 16, 5120, S16), ALIGN),
+    ((A16, B16 + 4, 16, 5120, S16), ALIGN),
+    ((A16, B16, 16, 5120, S16 + 2), ALIGN),
+    ((A16, B16, 16, 5120, A16 + 5120 * 16 - 4), ALIAS),   # sink over a's last word
+    ((A16, B16, 16, 5120, B16 - 252), ALIAS),             # ... and b's first
+    ((A16, B16, 0, 5120, 0), OK),                         # nothing to read: nothing checked or launched
+    ((A16, B16, 16, 5000, S16), UNSUP),
+])
+def test_read_ceiling_validation_before_any_hip_call(lib, args, status):
+    a, b, rows, row_bytes, sink = args
+    assert lib.glu_read_ceiling(a, b, rows, row_bytes, sink, None, None) == status
+    assert lib.glu_last_hip_error() == 0
+
+
+def test_tuning_xcd_bands_only_for_the_yardstick(lib):
+    p = api.Plan()
+    t = api.make_tuning(xcd_bands=1)
+    assert lib.glu_dual_gemv_plan_tuned(1, 9216, 2560, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP
+    assert lib.glu_grouped_gemv_plan_tuned(1, 2560, 9216, 7, ctypes.byref(t), ctypes.byref(p)) == UNSUP
+
+
+def test_mfma8_order_plans(lib):
+    """The 8-row kernel's K-walk order: slice-major only where its kernel is built (8 segments per
+    stage, one stage of weights in flight, more than 8 rows of hidden, at most 3 blocks per workgroup)."""
+    def plan_st(M, N, K, **kw):
+        p = api.Plan()
+        t = api.make_tuning(**kw)
+        return lib.glu_dual_gemv_plan_tuned(M, N, K, 1, ctypes.byref(t), ctypes.byref(p)), p
+    st, p = plan_st(32, 17408, 5120, kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2)
+    assert st == OK
+    assert api.plan(32, 17408, 5120, True, api.make_tuning(rows_per_wave=8, mfma_order=2))["kernel_symbol"] == \
+        "glu::mfma8_pass_kernel<4, 8, 3, false>"
+    assert plan_st(32, 17408, 5120, kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=1)[0] == OK
+    # at most 3 blocks per workgroup: 544 blocks need 182 workgroups
+    assert plan_st(32, 17408, 5120, rows_per_wave=8, mfma_order=2, grid=181)[0] == UNSUP
+    assert plan_st(32, 17408, 5120, rows_per_wave=8, mfma_order=2, grid=182)[0] == OK
+    for kw in (dict(mfma_segments=4), dict(mfma_depth=2)):
+        assert plan_st(32, 17408, 5120, rows_per_wave=8, mfma_order=2, **kw)[0] == UNSUP
+    assert plan_st(8, 17408, 5120, rows_per_wave=8, mfma_order=2)[0] == UNSUP   # 8 rows of hidden or fewer
+    assert plan_st(32, 17408, 5120, mfma_order=3)[0] == UNSUP
+    assert plan_st(16, 17408, 5120, rows_per_wave=4, mfma_order=2)[0] == UNSUP  # 4-row kernel
+    assert plan_st(1, 9216, 2560, mfma_order=1)[0] == UNSUP                    # VALU
+    assert plan_st(64, 9216, 2560, mfma_order=1)[0] == UNSUP                   # GEMM
+    assert plan_st(0, 9216, 2560, mfma_order=1)[0] == OK                       # nothing to launch
+
+
+@pytest.mark.parametrize("segments", [10, 12, 16])
+def test_mfma8_rings_above_64k_refused(lib, segments):
+    """Stages of more than 512 elements at 32 rows of hidden need a slice ring above 64 KiB
+    (2 x 32 rows x segments x 128 bytes); the 8-row kernel is not built for them."""
+    p = api.Plan()
+    t = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_segments=segments)
+    assert lib.glu_dual_gemv_plan_tuned(32, 17408, 5120, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP
+    assert 2 * 32 * segments * 128 > 64 * 1024

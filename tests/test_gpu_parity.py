@@ -302,3 +302,61 @@ def test_graph_capture_replays():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), eager), f"replay {i}"
+
+
+# ---- the 8-row kernel's two K-walk orders -------------------------------------
+
+PASS_SHAPES = [(9, 100, 512), (16, 1000, 1032), (17, 333, 2560), (32, 3000, 1024), (31, 64, 5120),
+               (24, 2052, 5120), (32, 9, 64), (20, 7, 520)]
+
+
+def mfma8_blocks(N):
+    return -(-(-(-N // 8)) // 4)
+
+
+@pytest.mark.parametrize("jb", [1, 2, 3])
+@pytest.mark.parametrize("M,N,K", PASS_SHAPES)
+def test_mfma8_slice_major_order(M, N, K, jb):
+    """K walked once for up to three blocks of a workgroup: within the bar against the oracle,
+    and bitwise equal to the block-by-block order (the per-lane summation order is the same)."""
+    grid = -(-mfma8_blocks(N) // jb)
+    h, wg, wu = inputs.hidden(M, K, 6), *inputs.weights(N, K, 6)
+    t_pass = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2, grid=grid)
+    t_blk = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=1, mfma_segments=8,
+                            mfma_depth=1, grid=grid)
+    assert api.plan(M, N, K, True, t_pass)["kernel_symbol"].startswith("glu::mfma8_pass_kernel")
+    rep, got, _ = parity(h, wg, wu, tuning=t_pass, label=f"mfma8 slice-major grid {grid}")
+    assert rep.ok, rep.summary()
+    ref = bits(gpu_run(h.to(DEV), wg.to(DEV), wu.to(DEV), t_blk))
+    assert check.compare_strict_bits(got, ref) is None
+
+
+def test_mfma8_slice_major_graph_replays():
+    """The slice-major kernel at the M=32 K=5120 N=17408 workload, captured in a graph and replayed
+    back to back with its inputs changing in place between replays: every replay matches the eager
+    call on the same inputs bitwise."""
+    M, N, K = 32, 17408, 5120
+    t = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2)
+    say(f"[graph] {api.plan(M, N, K, True, t)}")
+    h0, wg, wu = inputs.case("mfma_k5120_n17408", M=M, seed=0)
+    h, wg, wu = h0.to(DEV), wg.to(DEV), wu.to(DEV)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.dual_gemv(h, wg, wu, out=out, tuning=t)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            api.dual_gemv(h, wg, wu, out=out, tuning=t)
+    torch.cuda.synchronize()
+    for r in range(6):
+        h.copy_((h0.float() * (1.0 + r / 8.0)).to(torch.bfloat16).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = api.dual_gemv(h, wg, wu, tuning=t)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {r}"
