@@ -286,7 +286,7 @@ def dual_gemv_backward(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.T
     """Gradients (dhidden, dgate_w, dup_w) of dual_gemv for the upstream gradient ``dout``.
 
     hidden [M, K] (or [K], then dout is [N] and dhidden [K]), gate_w and up_w
-    [N, K], dout [M, N]; all bf16, contiguous, on one GPU; M <= 64.  Outputs are
+    [N, K], dout [M, N]; all bf16, contiguous, on one GPU; M <= 65536.  Outputs are
     allocated unless given (contiguous, overwritten).  ``workspace``: a uint8
     device tensor of at least backward_workspace_bytes(M, N, K) bytes, else one
     is allocated; on return it begins with dg and du, the bf16 gradients of the

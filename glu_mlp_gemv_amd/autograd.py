@@ -4,8 +4,8 @@ Mirrors the segKI "Plan B" design (DeepSpeed PR #8602, comment "Plan B:
 Dual-Weight GEMV", section "Plan B Design"): the Function keeps hidden, gate_w and up_w, reads the weight
 Parameters in place in both directions, and returns gradients for all three,
 so training and generation share one forward and one set of weights.
-Forward: glu_dual_gemv; backward: glu_dual_gemv_backward (M <= 64 rows of
-hidden).  Only argument marshalling happens here.
+Forward: glu_dual_gemv; backward: glu_dual_gemv_backward (up to 65536 rows
+of hidden per call).  Only argument marshalling happens here.
 """
 import torch
 

@@ -136,7 +136,7 @@ int default_segments(int64_t nsegs, int mt4, int hidden)
     return cap < 4 ? cap : 4;
 }
 
-glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
+glu_status plan_mfma_shape(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
 {
     glu::MfmaConfig c{};
     const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
@@ -176,6 +176,7 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     if (c.hidden == glu::kHiddenSlices) {
         int dflt = c.rows == 8 ? glu::mfma8_slice_depth(c.U) : glu::mfma_slice_depth(c.U);
         if (c.rows == 8 && c.U == 8 && m_pl <= 16) dflt = 2;  // fewer MFMAs per stage: room for a deeper pipeline
+        if (c.rows == 8 && t && t->mfma_order == 2) dflt = 1;  // the slice-major kernel keeps one stage in flight
         c.depth = (t && t->mfma_depth) ? t->mfma_depth : dflt;
     } else if (t && t->mfma_depth) {
         return GLU_ERR_UNSUPPORTED;  // only the lockstep kernels take a depth
@@ -219,6 +220,28 @@ glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     // twice the fp32 unit roundoff (a truncating adder)
     L->accum_depth = (int)(2 * (nseg + 5 + 2));
     return GLU_OK;
+}
+
+// Above 8 rows of hidden, when hidden does not fit in LDS, the default is 8 weight rows per wave
+// with the K walk done once for up to 3 blocks of a workgroup (each K-slice of hidden loaded and
+// published once for all of them).  K=5120 N=17408, interleaved warm graphs: M = 16 60.5 us
+// against 62.3 for 4 rows per wave; M = 24 62.7 against 68.7 and M = 32 64.9 against 71.7 for the
+// block-by-block walk (M = 1 at that shape: 53.3).  Overrides of the rows, the order, the stage
+// size, the depth or where hidden lives plan exactly what they ask for.
+glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
+{
+    const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
+    const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
+    const bool free_shape = !t || (!t->rows_per_wave && !t->mfma_order && !t->mfma_segments && !t->mfma_depth &&
+                                   !t->mfma_hidden);
+    if (free_shape && m_pl > 8 && waves * glu::kWave == glu::kMfmaMaxThreads &&
+        glu::mfma_hidden_lds_bytes((int)m_pl, K) > (size_t)glu::kLdsBudget) {
+        glu_tuning t8 = t ? *t : glu_tuning{};
+        t8.rows_per_wave = 8;
+        t8.mfma_order = 2;
+        if (plan_mfma_shape(M, N, K, &t8, L) == GLU_OK) return GLU_OK;
+    }
+    return plan_mfma_shape(M, N, K, t, L);
 }
 
 // Tiled GEMM: 64 weight rows per tile; 64 hidden rows up to M = 256, else 128.
@@ -753,19 +776,20 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
     const uint16_t* dg_all = gu;
     const uint16_t* du_all = gu + mn;
-    if (bp.path == glu::kPathMfma) {
+    if (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm) {
         // zero-padded operand copies, then dh's partial sums over ranges of weight rows, their
         // reduction, and both weight gradients
         char* w = static_cast<char*>(ws);
+        const int rows2 = bp.mp16 * bp.dh_mslices;  // dg2, du2 rows: hidden padded to whole tiles
         uint16_t* g2 = reinterpret_cast<uint16_t*>(w + bp.off_g2);
-        uint16_t* u2 = g2 + (int64_t)bp.mp16 * bp.np32;
+        uint16_t* u2 = g2 + (int64_t)rows2 * bp.np32;
         uint16_t* gT = reinterpret_cast<uint16_t*>(w + bp.off_gT);
         uint16_t* uT = gT + N * bp.mp32;
         uint16_t* hT = reinterpret_cast<uint16_t*>(w + bp.off_hT);
         const int m = (int)M, n = (int)N, k = (int)K;
         glu::RepackJobs jobs{};
-        jobs.job[0] = {dg_all, N, g2, m, n, bp.mp16, bp.np32, 0, 0, 0};
-        jobs.job[1] = {du_all, N, u2, m, n, bp.mp16, bp.np32, 0, 0, 0};
+        jobs.job[0] = {dg_all, N, g2, m, n, rows2, bp.np32, 0, 0, 0};
+        jobs.job[1] = {du_all, N, u2, m, n, rows2, bp.np32, 0, 0, 0};
         jobs.job[2] = {dg_all, N, gT, m, n, bp.mp32, 0, 1, 0, 0};
         jobs.job[3] = {du_all, N, uT, m, n, bp.mp32, 0, 1, 0, 0};
         jobs.job[4] = {hidden, K, hT, m, k, bp.mp32, 0, 1, 0, 0};
@@ -773,7 +797,10 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
         if (e == hipSuccess) e = glu::repack_launch(jobs, s);
         if (e == hipSuccess) e = glu::dh_mfma_launch(bp, m, gate_w, up_w, g2, u2, partial, n, k, s);
         if (e == hipSuccess) e = glu::dh_reduce_launch(bp, partial, dh, K, m, k, s);
-        if (e == hipSuccess) e = glu::dw_mfma_launch(bp, hT, gT, uT, dwg, dwu, n, k, s);
+        if (e == hipSuccess) {
+            e = bp.path == glu::kPathGemm ? glu::gemm_dw_launch(bp.mp32, hT, gT, uT, dwg, dwu, n, k, s)
+                                          : glu::dw_mfma_launch(bp, hT, gT, uT, dwg, dwu, n, k, s);
+        }
         return e == hipSuccess ? GLU_OK : fail_launch(e);
     }
     // 2 <= M <= 8: the contraction (weight gradients and dh's partial sums), then the reduction
@@ -972,13 +999,14 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
     // the grouped GEMV counts as one launch
-    plan->launches = run_all ? (bp.path == glu::kPathMfma     ? 6
+    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm ? 6
                                 : bp.path != glu::kPathChunks ? 2
                                                               : 4)
                              : 0;
     plan->grid = run_all ? (bp.path == glu::kPathFused1   ? bp.fused_grid
                             : bp.path == glu::kPathSplitK ? bp.split_grid
-                            : bp.path == glu::kPathMfma   ? (int)((K + 63) / 64) * bp.dh_splits
+                            : bp.path == glu::kPathMfma || bp.path == glu::kPathGemm
+                                ? (int)((K + 63) / 64) * bp.dh_splits * bp.dh_mslices
                                                           : bp.nranges * bp.nslabs)
                          : 0;
     plan->block = bp.path == glu::kPathSplitK ? bp.split_waves * glu::kWave : 256;

@@ -5,7 +5,8 @@
 
 namespace glu {
 
-constexpr int kBwdMaxM = 64;    // rows of hidden per call
+constexpr int kBwdMaxM = 1 << 16;  // rows of hidden per call
+constexpr int kBwdMfmaMaxM = 64;   // the matrix-core contractions of kPathMfma serve up to here
 constexpr int kBwdChunkM = 8;   // rows of hidden of the VALU contraction kernel at most
 constexpr int kBwdTargetBlocks = 512;  // contraction workgroups aimed for (2 per CU)
 
@@ -35,10 +36,13 @@ constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
 constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
 constexpr int kPathMfma = 3;     // 8 < M <= 64: grouped GEMV, gradient step, repacking, dh_mfma_kernel,
                                  // reduction, dw_mfma_kernel
+constexpr int kPathGemm = 4;     // M > 64: tiled GEMM for g and u, gradient step, repacking,
+                                 // dh_mfma_kernel over slices of 64 rows of hidden, reduction, and the
+                                 // weight gradients as one transposed tiled GEMM (gemm_dw_launch)
 constexpr int kBwdMfmaMinM = 9;  // rows of hidden from which the contractions run on MFMA
 
 struct BwdPlan {
-    int path;                // kPathChunks, kPathFused1, kPathSplitK or kPathMfma
+    int path;                // kPathChunks, kPathFused1, kPathSplitK, kPathMfma or kPathGemm
     bool fused;              // M == 1, K <= 2560: the one-pass kernel
     int fused_grid;          // its workgroups (each leaves one partial of dh)
     int split_u;             // K-split kernel: chunks per lane (1 or 2)
@@ -48,6 +52,7 @@ struct BwdPlan {
     int mp16, mp32;          // MFMA path: M rounded up to 16, 32 or 64 (dh's B operand) and to 32 (dW's)
     int np32;                // N rounded up to 32 (the columns of dg2, du2)
     int dh_splits, dh_jr;    // ranges of weight rows (jr rows each, a multiple of 32) = dh's partials
+    int dh_mslices;          // slices of mp16 rows of hidden dh's grid covers (1 up to 64 rows)
     int dh_steps;            // 32-row steps of the longest range
     bool gu_gemm;            // g and u from the tiled GEMM (M > 32, N % 4 == 0) instead of the grouped GEMV
     int64_t off_g2, off_gT, off_hT, off_partial;  // workspace offsets of dg2/du2, dgT/duT, hT, the partials

@@ -1,4 +1,4 @@
-// Backward of the dual-weight GLU projection for M <= 64 rows of hidden.
+// Backward of the dual-weight GLU projection (up to 65536 rows of hidden per call).
 //
 // The segKI "Plan B" autograd Function keeps hidden, gate_w and up_w and
 // returns gradients for all three, equal to those of the composite
@@ -754,14 +754,18 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     p.gu_bytes = pad256((int64_t)2 * M * N * 2);
     int64_t mfma_bytes = 0;  // the MFMA path's operand copies
     if (M >= kBwdMfmaMinM && M <= kBwdMaxM && N > 0 && K >= 8) {
-        p.path = kPathMfma;
+        const bool big = M > kBwdMfmaMaxM;
+        p.path = big ? kPathGemm : kPathMfma;
         p.mp16 = M <= 16 ? 16 : (M <= 32 ? 32 : 64);  // 1, 2 or 4 tiles of 16 rows: 4 waves split evenly
+        p.dh_mslices = big ? (int)((M + 63) / 64) : 1;  // above 64 rows: slices of 64
         p.mp32 = (int)((M + 31) / 32 * 32);
         p.np32 = (int)((N + 31) / 32 * 32);
-        // about 512 workgroups of 64 columns x one range of rows, ranges a multiple of 32 rows
+        // about 512 workgroups of 64 columns x one range of rows (x one slice of hidden), ranges a
+        // multiple of 32 rows
         const int64_t ktiles = (K + 63) / 64;
         const int64_t steps_all = p.np32 / 32;
-        int64_t splits = (kBwdTargetBlocks + ktiles - 1) / ktiles;
+        const int64_t per_split = ktiles * p.dh_mslices;
+        int64_t splits = (kBwdTargetBlocks + per_split - 1) / per_split;
         splits = splits < 1 ? 1 : (splits > steps_all ? steps_all : splits);
         const int64_t steps = (steps_all + splits - 1) / splits;
         p.dh_jr = (int)(steps * 32);
@@ -770,7 +774,7 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.gu_gemm = M > 32 && N % 4 == 0;
         p.nranges = p.dh_splits;
         p.off_g2 = p.gu_bytes;
-        p.off_gT = p.off_g2 + pad256((int64_t)2 * p.mp16 * p.np32 * 2);
+        p.off_gT = p.off_g2 + pad256((int64_t)2 * p.mp16 * p.dh_mslices * p.np32 * 2);
         p.off_hT = p.off_gT + pad256((int64_t)2 * N * p.mp32 * 2);
         p.off_partial = p.off_hT + pad256((int64_t)K * p.mp32 * 2);
         mfma_bytes = p.off_partial - p.gu_bytes;
@@ -795,6 +799,10 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         // the reduction; dW over one or two blocks of the M rows
         p.accum_depth = std::max(2 * (p.dh_steps + 5) + reduce_depth, 2 * (p.mp32 / 32 + 5));
         // g and u from the GEMM: one MFMA per 32-element block of K, plus the tile's fixed steps
+        if (p.gu_gemm) p.accum_depth = std::max(p.accum_depth, (int)(2 * ((K + 31) / 32 + 6)));
+    } else if (p.path == kPathGemm) {
+        // dh as above; the weight gradients from the GEMM over the mp32 padded rows of hidden
+        p.accum_depth = std::max(2 * (p.dh_steps + 5) + reduce_depth, 2 * (p.mp32 / 32 + 6));
         if (p.gu_gemm) p.accum_depth = std::max(p.accum_depth, (int)(2 * ((K + 31) / 32 + 6)));
     } else {
         p.accum_depth = (p.rows_per_range + kBwdWaves - 1) / kBwdWaves + kBwdWaves + reduce_depth;

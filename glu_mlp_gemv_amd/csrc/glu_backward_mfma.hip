@@ -1,5 +1,8 @@
-// Backward of the dual-weight GLU projection for 8 < M <= 64 rows of hidden:
-// the three contractions as v_mfma_f32_16x16x32_bf16 products.
+// Backward of the dual-weight GLU projection above 8 rows of hidden: the three
+// contractions as v_mfma_f32_16x16x32_bf16 products.  Up to 64 rows as below;
+// above, dh_mfma_kernel runs over slices of 64 rows of hidden and the weight
+// gradients are one tiled GEMM (gemm_dw_launch, glu_gemm.hip) on the same
+// transposed copies.
 //
 // After the grouped GEMV and the elementwise step have left dg and du
 // ([2][M][N] bf16) at the workspace head, repack_kernel writes zero-padded
@@ -64,9 +67,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 // One launch for all the copies; workgroup b serves the job whose range of workgroups holds b.
 // transpose == 0: dst[r][c] = src[r][c] (Rp rows of Cp elements), one element per thread, or with
 // vec 8 (one 16-byte load and store).
-// transpose != 0: dst[c][r] = src[r][c] (C rows of Rp <= 64 elements): a workgroup moves a tile of
-// 64 columns through LDS, reading rows of src and writing rows of dst, both contiguous (with vec in
-// 16-byte pieces on both sides).
+// transpose != 0: dst[c][r] = src[r][c] (C rows of Rp elements): a workgroup moves a tile of 64
+// columns x 64 rows (rows 64 rt .. of src, rt = the workgroup's row tile) through LDS, reading rows
+// of src and writing rows of dst, both contiguous (with vec in 16-byte pieces on both sides).
 // Entries with r >= R or c >= C are +0.  vec requires 16-byte aligned src and dst, ld, C and the
 // padded row length (Cp, or Rp when transposing) multiples of 8: a piece of 8 is then wholly inside
 // or wholly outside the source.
@@ -98,27 +101,31 @@ repack_kernel(RepackJobs jobs)
         jb.dst[x] = (r < jb.R && c < jb.C) ? jb.src[r * jb.ld + c] : (uint16_t)0;
         return;
     }
-    const int64_t c0 = bl * kRepackTile;
+    const int rtiles = (jb.Rp + kRepackTile - 1) / kRepackTile;
+    const int64_t c0 = (bl / rtiles) * kRepackTile;
+    const int r0 = (int)(bl % rtiles) * kRepackTile;
+    const int rn = min(kRepackTile, jb.Rp - r0);  // rows of dst's row segment this tile writes
     if (jb.vec) {
         // 64 rows x 8 pieces of 8 columns
         for (int i = threadIdx.x; i < kRepackTile * (kRepackTile / 8); i += kRepackThreads) {
             const int r = i / (kRepackTile / 8), cc = 8 * (i % (kRepackTile / 8));
             const int64_t c = c0 + cc;
-            const u32x4_t v =
-                (r < jb.R && c < jb.C) ? *reinterpret_cast<const u32x4_t*>(jb.src + (int64_t)r * jb.ld + c) : z;
+            const u32x4_t v = (r0 + r < jb.R && c < jb.C)
+                                  ? *reinterpret_cast<const u32x4_t*>(jb.src + (int64_t)(r0 + r) * jb.ld + c)
+                                  : z;
             __builtin_memcpy(&tile[r][cc], &v, sizeof(v));  // columns cc .. cc + 7 of tile row r
         }
     } else {
         for (int i = threadIdx.x; i < kRepackTile * kRepackTile; i += kRepackThreads) {
             const int r = i / kRepackTile, cc = i % kRepackTile;
             const int64_t c = c0 + cc;
-            tile[r][cc] = (r < jb.R && c < jb.C) ? jb.src[(int64_t)r * jb.ld + c] : (uint16_t)0;
+            tile[r][cc] = (r0 + r < jb.R && c < jb.C) ? jb.src[(int64_t)(r0 + r) * jb.ld + c] : (uint16_t)0;
         }
     }
     __syncthreads();
     if (jb.vec) {
-        // dst row c: Rp / 8 pieces of 8 consecutive r
-        const int rp8 = jb.Rp / 8;
+        // dst row c: rn / 8 pieces of 8 consecutive r
+        const int rp8 = rn / 8;
         for (int i = threadIdx.x; i < kRepackTile * rp8; i += kRepackThreads) {
             const int cc = i / rp8, r = 8 * (i % rp8);
             const int64_t c = c0 + cc;
@@ -128,14 +135,14 @@ repack_kernel(RepackJobs jobs)
                 for (int e = 0; e < 4; ++e) {
                     v[e] = (uint32_t)tile[r + 2 * e][cc] | ((uint32_t)tile[r + 2 * e + 1][cc] << 16);
                 }
-                *reinterpret_cast<u32x4_t*>(jb.dst + c * jb.Rp + r) = v;
+                *reinterpret_cast<u32x4_t*>(jb.dst + c * jb.Rp + r0 + r) = v;
             }
         }
     } else {
-        for (int i = threadIdx.x; i < kRepackTile * jb.Rp; i += kRepackThreads) {
-            const int cc = i / jb.Rp, r = i % jb.Rp;
+        for (int i = threadIdx.x; i < kRepackTile * rn; i += kRepackThreads) {
+            const int cc = i / rn, r = i % rn;
             const int64_t c = c0 + cc;
-            if (c < jb.C) jb.dst[c * jb.Rp + r] = tile[r][cc];
+            if (c < jb.C) jb.dst[c * jb.Rp + r0 + r] = tile[r][cc];
         }
     }
 }
@@ -224,22 +231,34 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
     }
 }
 
-// MT = Mp16 / 16 (1, 2 or 4).  Workgroup b: columns [64 (b % ktiles), +64), rows j of split
-// b / ktiles: [split * jr, min(N, (split + 1) * jr)), jr a multiple of 32.  g2, u2: dg2, du2
-// ([Mp16][np] with np a multiple of 32).  partial: [splits][2][M][K] fp32.
+// MT = Mp16 / 16 (1, 2 or 4).  Workgroup b: columns [64 (t % ktiles), +64), rows j of split
+// t / ktiles: [split * jr, min(N, (split + 1) * jr)), jr a multiple of 32, where t = b with one
+// slice of rows of hidden.  Above 64 rows (mslices > 1, MT = 4) t = b' / mslices and the workgroup
+// takes rows 64 (b' % mslices) .. + 63 of hidden, b' being b renumbered so that the workgroups one
+// XCD receives (the hardware deals them to the 8 XCDs in turn) are consecutive: the slices of one
+// (column tile, split) then run on one XCD and read its weight tile from that XCD's L2 after the
+// first.  g2, u2: dg2, du2 ([mslices * Mp16][np] with np a multiple of 32).  partial:
+// [splits][2][M][K] fp32.
 template <int MT>
 __global__ void __launch_bounds__(kMfmaBwdThreads)
 dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__ up_w,
                const uint16_t* __restrict__ g2, const uint16_t* __restrict__ u2, float* __restrict__ partial, int M,
-               int N, int K, int np, int ktiles, int jr)
+               int N, int K, int np, int ktiles, int jr, int mslices)
 {
     constexpr int D = kDhDepth;
     __shared__ __align__(16) uint16_t tw[2][2][kDhK * kDhTS];  // [buffer][matrix][k][j]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int k0 = (int)(blockIdx.x % ktiles) * kDhK;
-    const int split = (int)(blockIdx.x / ktiles);
+    int bt = (int)blockIdx.x;
+    if (mslices > 1) {
+        const int G = (int)gridDim.x, per = G >> 3, rem = G & 7, xcd = bt & 7, slot = bt >> 3;
+        bt = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+    }
+    const int mbase = 16 * MT * (bt % mslices);
+    bt /= mslices;
+    const int k0 = (bt % ktiles) * kDhK;
+    const int split = bt / ktiles;
     const int jb = split * jr;
     const int je = min(jb + jr, N);
     const int nsteps = (je - jb + kDhStep - 1) / kDhStep;  // >= 1: the plan leaves no split empty
@@ -259,7 +278,7 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
         w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gate_w + j * K + kc));
         w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up_w + j * K + kc));
         // B: rows m = 16 mt + l%16 of dg2 and du2, columns jb + 32 s + 8 (l/16) .. + 7 (zero past N)
-        const int64_t off = (int64_t)(16 * mt + i16) * np + jb + kDhStep * s + 8 * q;
+        const int64_t off = (int64_t)(mbase + 16 * mt + i16) * np + jb + kDhStep * s + 8 * q;
         b[0] = *reinterpret_cast<const u32x4_t*>(g2 + off);
         b[1] = *reinterpret_cast<const u32x4_t*>(u2 + off);
     };
@@ -338,7 +357,7 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     for (; s0 < nsteps; s0 += D) run_stages<0, D>(tail, s0, nsteps);
 
     // lane l holds D[4(l/16) + e][l%16]: columns k = k0 + 16 ks + 4(l/16) + e of row m = 16 mt + l%16
-    const int m = 16 * mt + i16;
+    const int m = mbase + 16 * mt + i16;
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
@@ -358,11 +377,12 @@ hipError_t repack_launch(RepackJobs jobs, hipStream_t stream)
     for (int q = 0; q < jobs.n; ++q) {
         RepackJob& j = jobs.job[q];
         if (j.R > j.Rp || j.R < 0 || j.C < 0) return hipErrorInvalidValue;
-        if (j.transpose ? j.Rp > kRepackTile : j.C > j.Cp) return hipErrorInvalidValue;
+        if (!j.transpose && j.C > j.Cp) return hipErrorInvalidValue;
         const bool al = (((uintptr_t)j.src | (uintptr_t)j.dst) & 15u) == 0 && j.ld % 8 == 0 && j.C % 8 == 0;
         j.vec = al && (j.transpose ? j.Rp % 8 == 0 : j.Cp % 8 == 0) ? 1 : 0;
         const int64_t per_thread = j.vec ? 8 : 1;
-        j.nblocks = j.transpose ? ((int64_t)j.C + kRepackTile - 1) / kRepackTile
+        j.nblocks = j.transpose ? ((int64_t)j.C + kRepackTile - 1) / kRepackTile *
+                                      (((int64_t)j.Rp + kRepackTile - 1) / kRepackTile)
                                 : ((int64_t)j.Rp * j.Cp / per_thread + kRepackThreads - 1) / kRepackThreads;
         j.first_block = grid;
         grid += j.nblocks;
@@ -380,7 +400,7 @@ hipError_t dw_mfma_launch(const BwdPlan& p, const uint16_t* hT, const uint16_t* 
     const int64_t ntiles = (int64_t)ktiles * ((N + kDwTile - 1) / kDwTile);
     const int64_t per_wave = p.mp32 == 32 ? kDwTilesPerWave : 1;
     const int64_t grid = (ntiles + 4 * per_wave - 1) / (4 * per_wave);
-    if (p.path != kPathMfma || N < 1 || K < 8 || (K & 7) != 0 || grid < 1 || grid > 0x7fffffff) {
+    if (p.path != kPathMfma || N < 1 || K < 8 || (K & 7) != 0 || grid < 1 || grid > 0x7fffffff) {  // M <= 64
         return hipErrorInvalidValue;
     }
     if (p.mp32 == 32) {
@@ -399,20 +419,22 @@ hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const
                           const uint16_t* u2, float* partial, int N, int K, hipStream_t stream)
 {
     using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, float*, int, int, int,
-                        int, int, int);
+                        int, int, int, int);
     static const Fn table[4] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>};
     const int mt = p.mp16 / 16;
     const int ktiles = (K + kDhK - 1) / kDhK;
-    if (p.path != kPathMfma || mt < 1 || mt > 4 || !table[mt - 1] || M < 1 || M > p.mp16 || N < 1 || K < 8 || (K & 7) != 0 ||
+    const int ms = p.dh_mslices;
+    if ((p.path != kPathMfma && p.path != kPathGemm) || mt < 1 || mt > 4 || !table[mt - 1] || ms < 1 ||
+        (ms > 1 && mt != 4) || M < 1 || M > (int64_t)ms * p.mp16 || N < 1 || K < 8 || (K & 7) != 0 ||
         p.dh_jr < kDhStep || p.dh_jr % kDhStep != 0 || p.np32 < N || p.np32 % kDhStep != 0 || p.dh_splits < 1 ||
         (int64_t)(p.dh_splits - 1) * p.dh_jr >= N || (int64_t)p.dh_splits * p.dh_jr < N ||
         p.dh_splits != p.nranges) {
         return hipErrorInvalidValue;
     }
-    const int64_t grid = (int64_t)ktiles * p.dh_splits;
+    const int64_t grid = (int64_t)ktiles * p.dh_splits * ms;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(table[mt - 1], dim3((unsigned)grid), dim3(kMfmaBwdThreads), 0, stream, gate_w, up_w, g2, u2,
-                       partial, M, N, K, p.np32, ktiles, p.dh_jr);
+                       partial, M, N, K, p.np32, ktiles, p.dh_jr, ms);
     return hipGetLastError();
 }
 

@@ -39,14 +39,19 @@ __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 // from 2 on, PF register sets rotate and a stage's data has PF stages of
 // compute to arrive).
 // nbm: M tiles; the grid holds ceil(N / BN) * nbm workgroups.
-// LIN: write bf16(G) and bf16(U) instead of the GLU product: G to out, U to out + M ldo (the
+// LIN: write bf16(G) and bf16(U) instead of the GLU product: G to out, U to out2 (the
 // backward's [2][M][N] workspace head).
-template <int BN, int BM, bool KTAIL, int PF, bool LIN = false>
+// TRANS (with LIN): the MFMA operands swap places, so each lane holds 4 consecutive hidden rows
+// of one weight row, and G, U are stored transposed, out[n][m] and out2[n][m] (rows ldo apart;
+// M a multiple of 4).  The backward's weight gradients are this product with dg^T, du^T as the
+// two weights and hidden^T as the hidden (contraction over the rows of hidden).
+template <int BN, int BM, bool KTAIL, int PF, bool LIN = false, bool TRANS = false>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __restrict__ gate, int64_t ldg,
-            const uint16_t* __restrict__ up, int64_t ldu, uint16_t* __restrict__ out, int64_t ldo, int M, int N,
-            int K, int nbm, int vec_out)
+            const uint16_t* __restrict__ up, int64_t ldu, uint16_t* __restrict__ out, uint16_t* __restrict__ out2,
+            int64_t ldo, int M, int N, int K, int nbm, int vec_out)
 {
+    static_assert(LIN || !TRANS, "the transposed store is a form of the linear epilogue");
     constexpr int ROWS = 2 * BN + BM;                           // LDS rows per stage
     constexpr int LPT = ROWS * kStageChunks / kGemmThreads;     // 16-byte loads per thread per stage
     constexpr int WN = BN / 2, WM = BM / 2;
@@ -140,8 +145,13 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
                 const u32x4_t a_u = L[ru * kStageChunks + (c ^ gemm_swz(ru))];
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
-                    ag[i][j] = mfma16(a_g, b[j], ag[i][j]);
-                    au[i][j] = mfma16(a_u, b[j], au[i][j]);
+                    if constexpr (TRANS) {
+                        ag[i][j] = mfma16(b[j], a_g, ag[i][j]);
+                        au[i][j] = mfma16(b[j], a_u, au[i][j]);
+                    } else {
+                        ag[i][j] = mfma16(a_g, b[j], ag[i][j]);
+                        au[i][j] = mfma16(a_u, b[j], au[i][j]);
+                    }
                 }
             }
         }
@@ -183,6 +193,27 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
         for (; s0 < nstages; s0 += PF) run_stages<0, PF>(tail, s0, nstages);
     }
 
+    if constexpr (TRANS) {
+        // lane l holds G and U of weight row l % 16, hidden rows 4(l/16) + e, of each 16 x 16 tile
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            const int n = n0 + wn * WN + 16 * i + i16;
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                const int m = m0 + wm * WM + 16 * j + 4 * q16;
+                if (n < N && m < M) {  // M % 4 == 0 for this form (checked by the launcher)
+                    uint2 wg, wu;
+                    wg.x = (uint32_t)f32_to_bf16_rne(ag[i][j][0]) | ((uint32_t)f32_to_bf16_rne(ag[i][j][1]) << 16);
+                    wg.y = (uint32_t)f32_to_bf16_rne(ag[i][j][2]) | ((uint32_t)f32_to_bf16_rne(ag[i][j][3]) << 16);
+                    wu.x = (uint32_t)f32_to_bf16_rne(au[i][j][0]) | ((uint32_t)f32_to_bf16_rne(au[i][j][1]) << 16);
+                    wu.y = (uint32_t)f32_to_bf16_rne(au[i][j][2]) | ((uint32_t)f32_to_bf16_rne(au[i][j][3]) << 16);
+                    *reinterpret_cast<uint2*>(out + (int64_t)n * ldo + m) = wg;
+                    *reinterpret_cast<uint2*>(out2 + (int64_t)n * ldo + m) = wu;
+                }
+            }
+        }
+        return;
+    }
     // lane l holds G and U of weight rows 4(l/16) + e, hidden row l % 16, of each 16 x 16 tile
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
@@ -198,7 +229,7 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
                     wu.x = (uint32_t)f32_to_bf16_rne(au[i][j][0]) | ((uint32_t)f32_to_bf16_rne(au[i][j][1]) << 16);
                     wu.y = (uint32_t)f32_to_bf16_rne(au[i][j][2]) | ((uint32_t)f32_to_bf16_rne(au[i][j][3]) << 16);
                     *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + n) = wg;
-                    *reinterpret_cast<uint2*>(out + ((int64_t)M + m) * ldo + n) = wu;
+                    *reinterpret_cast<uint2*>(out2 + (int64_t)m * ldo + n) = wu;
                 }
                 continue;
             }
@@ -226,7 +257,7 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
 namespace {
 
 using GemmFn = void (*)(const uint16_t*, int64_t, const uint16_t*, int64_t, const uint16_t*, int64_t, uint16_t*,
-                        int64_t, int, int, int, int, int);
+                        uint16_t*, int64_t, int, int, int, int, int);
 
 template <int BN, int BM>
 GemmFn pick_tail(bool ktail, int pf)
@@ -283,7 +314,7 @@ hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const
     // 8-byte output stores need 8-byte aligned rows
     const int vec_out = (((uintptr_t)out & 7u) == 0 && (ld.o & 3) == 0) ? 1 : 0;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), lds, stream, hidden, ld.h, gate_w, ld.g, up_w,
-                       ld.u, out, ld.o, M, N, K, nbm, vec_out);
+                       ld.u, out, out, ld.o, M, N, K, nbm, vec_out);
     return hipGetLastError();
 }
 
@@ -299,7 +330,24 @@ hipError_t gemm_linear_launch(int M, const uint16_t* hidden, const uint16_t* gat
     const int64_t grid = ((N + 63) / 64) * nbm;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), gemm_lds_bytes(64, 64), stream, hidden, (int64_t)K,
-                       gate_w, (int64_t)K, up_w, (int64_t)K, gu, (int64_t)N, M, N, K, (int)nbm, 1);
+                       gate_w, (int64_t)K, up_w, (int64_t)K, gu, gu + (int64_t)M * N, (int64_t)N, M, N, K, (int)nbm, 1);
+    return hipGetLastError();
+}
+
+hipError_t gemm_dw_launch(int mp, const uint16_t* hT, const uint16_t* dgT, const uint16_t* duT, uint16_t* dwg,
+                          uint16_t* dwu, int N, int K, hipStream_t stream)
+{
+    // dWg[j][k] = bf16(sum_m dgT[j][m] hT[k][m]), dWu likewise: the linear GEMM with dgT, duT as the
+    // weights (N rows), hT as the hidden (K rows), a contraction of mp (padded rows of hidden, zeros
+    // past M), stored transposed.  64 x 64 tiles, two stages of loads in flight.
+    if (mp < 32 || (mp & 31) != 0 || N < 1 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
+    const bool ktail = (mp % kStageK) != 0;
+    GemmFn fn = ktail ? gemm_kernel<64, 64, true, 2, true, true> : gemm_kernel<64, 64, false, 2, true, true>;
+    const int64_t nbm = (K + 63) / 64;
+    const int64_t grid = ((N + 63) / 64) * nbm;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), gemm_lds_bytes(64, 64), stream, hT, (int64_t)mp,
+                       dgT, (int64_t)mp, duT, (int64_t)mp, dwg, dwu, (int64_t)K, K, N, mp, (int)nbm, 1);
     return hipGetLastError();
 }
 

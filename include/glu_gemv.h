@@ -217,7 +217,7 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * bytes, 256-byte aligned, not overlapping any argument.  On return it
  * begins with dg and du, the bf16 gradients of the gate and up
  * pre-activations ([2][M][N], dense); the rest is scratch.  Limits:
- * M <= 64 (else GLU_ERR_UNSUPPORTED); hidden, gate_w, up_w, dgate_w, dup_w
+ * M <= 65536 (else GLU_ERR_UNSUPPORTED); hidden, gate_w, up_w, dgate_w, dup_w
  * 16-byte aligned and K % 8 == 0 (else GLU_ERR_UNSUPPORTED).
  * Empty sums give +0: N == 0 zero-fills dhidden, M == 0 zero-fills both
  * weight gradients; K == 0 has nothing to write.  Validation (NULL arrays,
@@ -228,7 +228,9 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * (K <= 8192 when M <= 3), two launches, a pass that reads each
  * weight row once and the reduction of dhidden's partial sums; otherwise
  * the grouped GEMV for g and u (above M = 32 with N % 4 == 0 a tiled GEMM),
- * then the gradient kernels (above M = 8 on the matrix cores).
+ * then the gradient kernels (above M = 8 on the matrix cores; above M = 64
+ * dhidden over slices of 64 rows of hidden and the weight gradients as one
+ * tiled GEMM contracting over the rows of hidden).
  */
 glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                                   const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
@@ -237,7 +239,7 @@ glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w
 
 /* Workspace bytes glu_dual_gemv_backward needs for (M, N, K), into *bytes
  * (0 when an extent is zero).  Host only.  GLU_ERR_BAD_SHAPE or
- * GLU_ERR_UNSUPPORTED (M > 64) as the call would return. */
+ * GLU_ERR_UNSUPPORTED (M > 65536) as the call would return. */
 glu_status glu_dual_gemv_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 
 /* The backward's launches for (M, N, K), host only: kernel

@@ -81,7 +81,14 @@ def test_plan(lib, M, N, K, aligned, kernel, launches):
 def test_describe_names_the_instantiated_kernel(lib):
     assert api.plan(1, 9216, 2560)["kernel_symbol"] == "glu::valu_kernel<1, 1, 5, 1, false, false>"
     assert api.plan(8, 12288, 4096)["kernel_symbol"] == "glu::mfma_kernel<2, 4, true, false>"
-    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma8_slice_kernel<4, 8, 1, false>"
+    assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<4, 8, 3, false>"
+    assert api.plan(16, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<2, 8, 3, false>"
+    assert api.plan(24, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<3, 8, 3, false>"
+    # an override of the rows per wave or the order plans what it asks for
+    assert api.plan(32, 17408, 5120, True, api.make_tuning(mfma_order=1, rows_per_wave=8))["kernel_symbol"] == \
+        "glu::mfma8_slice_kernel<4, 8, 1, false>"
+    assert api.plan(16, 17408, 5120, True, api.make_tuning(rows_per_wave=4))["kernel_symbol"] == \
+        "glu::mfma_slice_kernel<4, 4, 2, false>"
     assert api.plan(8, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<2, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
     assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false, 2>"
@@ -417,7 +424,9 @@ def test_backward_plan_and_workspace(lib):
     assert api.backward_plan(3, 0, 8)["kernel"] == api.KERNEL_ZERO   # hidden's gradient of no outputs
     assert api.backward_plan(3, 5, 0)["kernel"] == api.KERNEL_NONE
     with pytest.raises(api.GluError):
-        api.backward_plan(65, 10, 64)         # M > 64
+        api.backward_plan(65537, 10, 64)      # M > 65536
+    assert api.backward_plan(65, 10, 64)["launches"] == 6       # above 64 rows: the GEMM regime
+    assert api.backward_plan(512, 9216, 2560)["grid"] == 40 * 2 * 8   # dh: column tiles x splits x slices
     with pytest.raises(api.GluError):
         api.backward_workspace_bytes(-1, 10, 64)
     b = ctypes.c_int64(0)
@@ -468,7 +477,7 @@ def test_backward_validation_before_any_hip_call(lib, change, status):
 
 def test_backward_shape_limits(lib):
     p, ws = _bwd_ptrs(2, 64, 128)
-    assert api.dual_gemv_backward_raw(*p[:7], 65, 64, 128, p[7], ws) == UNSUP     # M > 64
+    assert api.dual_gemv_backward_raw(*p[:7], 65537, 64, 128, p[7], ws) == UNSUP  # M > 65536
     assert api.dual_gemv_backward_raw(*p[:7], 2, 64, 100, p[7], ws) == UNSUP      # K % 8 != 0
     assert api.dual_gemv_backward_raw(*p[:7], -1, 64, 128, p[7], ws) == SHAPE
     assert api.dual_gemv_backward_raw(*p[:7], 2, 1 << 40, 1 << 40, p[7], ws) == SHAPE
@@ -551,6 +560,13 @@ def test_mfma8_order_plans(lib):
     for kw in (dict(mfma_segments=4), dict(mfma_depth=2)):
         assert plan_st(32, 17408, 5120, rows_per_wave=8, mfma_order=2, **kw)[0] == UNSUP
     assert plan_st(8, 17408, 5120, rows_per_wave=8, mfma_order=2)[0] == UNSUP   # 8 rows of hidden or fewer
+    for M, N, K in ((9, 100, 512), (16, 1000, 1032), (17, 333, 2560), (24, 2052, 5120), (32, 9, 64)):
+        blocks = -(-(-(-N // 8)) // 4)
+        for jb in (1, 2, 3):
+            g = api.plan(M, N, K, True, api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2,
+                                                       grid=-(-blocks // jb)))
+            assert g["kernel_symbol"].startswith("glu::mfma8_pass_kernel<")
+        assert plan_st(M, N, K, rows_per_wave=8, mfma_order=2, mfma_depth=2)[0] == UNSUP
     assert plan_st(32, 17408, 5120, mfma_order=3)[0] == UNSUP
     assert plan_st(16, 17408, 5120, rows_per_wave=4, mfma_order=2)[0] == UNSUP  # 4-row kernel
     assert plan_st(1, 9216, 2560, mfma_order=1)[0] == UNSUP                    # VALU

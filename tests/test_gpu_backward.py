@@ -96,7 +96,12 @@ CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2
          # more than 8 rows of hidden: the contractions on the matrix cores (zero-padded operands,
          # ragged row ranges and column tiles, partial 16-row tiles of hidden)
          (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8), (17, 1000, 2568),
-         (40, 333, 520), (48, 4097, 72), (12, 31, 4096), (64, 9216, 2560)]
+         (40, 333, 520), (48, 4097, 72), (12, 31, 4096), (64, 9216, 2560),
+         # more than 64 rows: g and u from the tiled GEMM (N % 4 == 0; else the grouped GEMV in slices),
+         # dh over slices of 64 rows of hidden, the weight gradients as one transposed GEMM (a ragged
+         # last 32-row block of the contraction, transposes over several 64-row tiles)
+         (65, 700, 1032), (100, 333, 520), (128, 1000, 1024), (96, 4097, 72), (200, 64, 2048),
+         (130, 12, 8), (512, 9216, 2560)]
 
 
 @pytest.mark.parametrize("M,N,K", CASES)
@@ -179,9 +184,11 @@ def test_backward_gate_zero_closed_form():
     check_backward(h, wg, wu, go, (dh, dwg, dwu), dg, du, label="gate zero")
 
 
-def test_autograd_function_matches_both_entry_points():
-    """The autograd Function's forward is glu_dual_gemv and its gradients glu_dual_gemv_backward."""
-    M, N, K = 2, 700, 1024
+@pytest.mark.parametrize("M", [2, 160])
+def test_autograd_function_matches_both_entry_points(M):
+    """The autograd Function's forward is glu_dual_gemv and its gradients glu_dual_gemv_backward,
+    at a decode batch and at a training micro-batch of more than 64 rows."""
+    N, K = 700, 1024
     h, (wg, wu), go = inputs.hidden(M, K, 76), inputs.weights(N, K, 76), inputs.grad_out(M, N, 76)
     hd, gd, ud = (t.to(DEV).requires_grad_() for t in (h, wg, wu))
     out = autograd.dual_weight_glu(hd, gd, ud)
