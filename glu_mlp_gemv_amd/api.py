@@ -22,6 +22,8 @@ GLU_OK = 0
 GLU_ERR_UNSUPPORTED = 6
 GLU_ERR_BAD_STRIDE = 7
 GLU_ERR_WORKSPACE = 8
+GLU_ERR_SCRATCH_LIMIT = 9
+NOALLOC_SCRATCH_BYTES = 48 << 20  # the device array glu_dual_gemv_backward_noalloc works in
 (KERNEL_NONE, KERNEL_ZERO, KERNEL_VALU, KERNEL_MFMA, KERNEL_GENERIC, KERNEL_GEMM, KERNEL_BACKWARD,
  KERNEL_CEILING) = range(8)
 KERNEL_NAMES = {KERNEL_NONE: "none", KERNEL_ZERO: "zero", KERNEL_VALU: "valu",
@@ -49,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "glu_dual_gemv_backward_plan",
     "glu_read_ceiling",
     "glu_read_ceiling_plan",
+    "glu_dual_gemv_backward_noalloc",
 )
 
 
@@ -139,6 +142,8 @@ def library() -> ctypes.CDLL:
     lib.glu_dual_gemv_backward_workspace.restype = ctypes.c_int
     lib.glu_dual_gemv_backward_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     lib.glu_dual_gemv_backward_plan.restype = ctypes.c_int
+    lib.glu_dual_gemv_backward_noalloc.argtypes = [u16p, u16p, u16p, u16p, u16p, u16p, u16p, i64, i64, i64, vp]
+    lib.glu_dual_gemv_backward_noalloc.restype = ctypes.c_int
     lib.glu_read_ceiling.argtypes = [vp, vp, i64, i64, vp, ctypes.POINTER(Tuning), vp]
     lib.glu_read_ceiling.restype = ctypes.c_int
     lib.glu_read_ceiling_plan.argtypes = [i64, i64, ctypes.POINTER(Tuning), ctypes.POINTER(Plan)]
@@ -279,19 +284,8 @@ def backward_plan(M: int, N: int, K: int) -> dict:
     return p.as_dict()
 
 
-def dual_gemv_backward(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor, dout: torch.Tensor,
-                       dhidden: Optional[torch.Tensor] = None, dgate_w: Optional[torch.Tensor] = None,
-                       dup_w: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       stream: Optional[torch.cuda.Stream] = None):
-    """Gradients (dhidden, dgate_w, dup_w) of dual_gemv for the upstream gradient ``dout``.
-
-    hidden [M, K] (or [K], then dout is [N] and dhidden [K]), gate_w and up_w
-    [N, K], dout [M, N]; all bf16, contiguous, on one GPU; M <= 65536.  Outputs are
-    allocated unless given (contiguous, overwritten).  ``workspace``: a uint8
-    device tensor of at least backward_workspace_bytes(M, N, K) bytes, else one
-    is allocated; on return it begins with dg and du, the bf16 gradients of the
-    gate and up pre-activations ([2, M, N]).
-    """
+def _backward_args(hidden, gate_w, up_w, dout, dhidden, dgate_w, dup_w):
+    """Checked shapes of a backward call and its output tensors (allocated unless given)."""
     _check("hidden", hidden, (1, 2))
     _check("gate_w", gate_w, (2,))
     _check("up_w", up_w, (2,))
@@ -322,6 +316,23 @@ def dual_gemv_backward(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.T
     dhidden = out_tensor("dhidden", dhidden, tuple(hidden.shape))
     dgate_w = out_tensor("dgate_w", dgate_w, (N, K))
     dup_w = out_tensor("dup_w", dup_w, (N, K))
+    return M, N, K, dev, dhidden, dgate_w, dup_w
+
+
+def dual_gemv_backward(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor, dout: torch.Tensor,
+                       dhidden: Optional[torch.Tensor] = None, dgate_w: Optional[torch.Tensor] = None,
+                       dup_w: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None):
+    """Gradients (dhidden, dgate_w, dup_w) of dual_gemv for the upstream gradient ``dout``.
+
+    hidden [M, K] (or [K], then dout is [N] and dhidden [K]), gate_w and up_w
+    [N, K], dout [M, N]; all bf16, contiguous, on one GPU; M <= 65536.  Outputs are
+    allocated unless given (contiguous, overwritten).  ``workspace``: a uint8
+    device tensor of at least backward_workspace_bytes(M, N, K) bytes, else one
+    is allocated; on return it begins with dg and du, the bf16 gradients of the
+    gate and up pre-activations ([2, M, N]).
+    """
+    M, N, K, dev, dhidden, dgate_w, dup_w = _backward_args(hidden, gate_w, up_w, dout, dhidden, dgate_w, dup_w)
     need = backward_workspace_bytes(M, N, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -333,6 +344,23 @@ def dual_gemv_backward(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.T
         st = lib.glu_dual_gemv_backward(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(), dout.data_ptr(),
                                         dhidden.data_ptr(), dgate_w.data_ptr(), dup_w.data_ptr(), M, N, K,
                                         workspace.data_ptr(), workspace.numel(), s.cuda_stream)
+    _raise_for(st)
+    return dhidden, dgate_w, dup_w
+
+
+def dual_gemv_backward_noalloc(hidden: torch.Tensor, gate_w: torch.Tensor, up_w: torch.Tensor,
+                               dout: torch.Tensor, dhidden: Optional[torch.Tensor] = None,
+                               dgate_w: Optional[torch.Tensor] = None, dup_w: Optional[torch.Tensor] = None,
+                               stream: Optional[torch.cuda.Stream] = None):
+    """dual_gemv_backward through glu_dual_gemv_backward_noalloc: the library works in its own fixed
+    device array (NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace, so with all three outputs
+    given nothing is allocated at all.  Calls that overlap on one GPU race on that array."""
+    M, N, K, dev, dhidden, dgate_w, dup_w = _backward_args(hidden, gate_w, up_w, dout, dhidden, dgate_w, dup_w)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = library().glu_dual_gemv_backward_noalloc(hidden.data_ptr(), gate_w.data_ptr(), up_w.data_ptr(),
+                                                      dout.data_ptr(), dhidden.data_ptr(), dgate_w.data_ptr(),
+                                                      dup_w.data_ptr(), M, N, K, s.cuda_stream)
     _raise_for(st)
     return dhidden, dgate_w, dup_w
 

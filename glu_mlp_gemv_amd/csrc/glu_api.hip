@@ -715,7 +715,7 @@ glu_status plan_backward(int64_t M, int64_t N, int64_t K, glu::BwdPlan* bp)
 
 glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* dout,
                         uint16_t* dh, uint16_t* dwg, uint16_t* dwu, int64_t M, int64_t N, int64_t K, void* ws,
-                        int64_t ws_bytes, void* stream)
+                        int64_t ws_bytes, void* stream, bool validate_only = false)
 {
     glu::BwdPlan bp;
     glu_status st = plan_backward(M, N, K, &bp);
@@ -739,6 +739,9 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
             if (b > a && overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return GLU_ERR_ALIASING;
         }
     }
+    const bool fast = ((((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w | (uintptr_t)dwg | (uintptr_t)dwu) &
+                        15u) == 0) && K % 8 == 0 && K <= kMaxFastK;
+    if (validate_only) return (run_all && !fast) ? GLU_ERR_UNSUPPORTED : GLU_OK;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (!run_all) {
@@ -748,8 +751,6 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
         if (M == 0 && nk > 0 && e == hipSuccess) e = glu::zero_launch(dwu, N, K, K, s);
         return e == hipSuccess ? GLU_OK : fail_launch(e);
     }
-    const bool fast = ((((uintptr_t)hidden | (uintptr_t)gate_w | (uintptr_t)up_w | (uintptr_t)dwg | (uintptr_t)dwu) &
-                        15u) == 0) && K % 8 == 0 && K <= kMaxFastK;
     if (!fast) return GLU_ERR_UNSUPPORTED;
     if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < bp.workspace_bytes) return GLU_ERR_WORKSPACE;
     uint16_t* gu = static_cast<uint16_t*>(ws);
@@ -829,6 +830,27 @@ void fill_plan(const Launch& L, glu_plan* p)
 }
 
 }  // namespace
+
+namespace glu {
+
+glu_status backward_entry(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* dout,
+                          uint16_t* dh, uint16_t* dwg, uint16_t* dwu, int64_t M, int64_t N, int64_t K, void* ws,
+                          int64_t ws_bytes, void* stream, bool validate_only)
+{
+    return run_backward(hidden, gate_w, up_w, dout, dh, dwg, dwu, M, N, K, ws, ws_bytes, stream, validate_only);
+}
+
+glu_status launch_failed(hipError_t e) { return fail_launch(e); }
+
+glu_status backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes)
+{
+    BwdPlan bp;
+    const glu_status st = plan_backward(M, N, K, &bp);
+    *bytes = (st == GLU_OK && M > 0 && N > 0 && K > 0) ? bp.workspace_bytes : 0;
+    return st;
+}
+
+}  // namespace glu
 
 extern "C" {
 
@@ -1067,6 +1089,8 @@ const char* glu_status_string(int status)
     case GLU_ERR_UNSUPPORTED: return "GLU_ERR_UNSUPPORTED: the requested launch shape is not available";
     case GLU_ERR_BAD_STRIDE: return "GLU_ERR_BAD_STRIDE: a row stride is shorter than its row, or the rows overflow";
     case GLU_ERR_WORKSPACE: return "GLU_ERR_WORKSPACE: the workspace is NULL, misaligned or too small";
+    case GLU_ERR_SCRATCH_LIMIT:
+        return "GLU_ERR_SCRATCH_LIMIT: the call needs more scratch than the library's fixed device array holds";
     default: return "unknown glu_status";
     }
 }

@@ -1,6 +1,7 @@
 // Internal interface of the backward kernels (glu_backward.hip).
 #pragma once
 
+#include "../../include/glu_gemv.h"
 #include "glu_launch.h"
 
 namespace glu {
@@ -66,6 +67,15 @@ struct BwdPlan {
 };
 
 BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K);
+// glu_dual_gemv_backward's validation and launches (glu_api.hip); validate_only: return after the
+// checks that need no workspace, before any HIP call
+glu_status backward_entry(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* dout,
+                          uint16_t* dh, uint16_t* dwg, uint16_t* dwu, int64_t M, int64_t N, int64_t K, void* ws,
+                          int64_t ws_bytes, void* stream, bool validate_only);
+// GLU_ERR_LAUNCH, recording e as the calling thread's last HIP error
+glu_status launch_failed(hipError_t e);
+// workspace bytes of a backward call (0 when an extent is zero), with plan_backward's status
+glu_status backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int M, int N, hipStream_t stream);
 // K % 8 == 0, hidden / gate_w / up_w / dwg / dwu 16-byte aligned, packed rows.  M <= 8; dw: also
 // the weight gradients (then these M rows are all rows of hidden).  dgm, dum: [M][N].

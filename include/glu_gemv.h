@@ -57,8 +57,10 @@ typedef enum glu_status {
     GLU_ERR_UNSUPPORTED = 6,  /* a tuning override the library cannot serve (glu_gemv_tuning.h) */
     GLU_ERR_BAD_STRIDE = 7,   /* glu_dual_gemv_strided: a row stride below its row length, or
                                  rows whose extent overflows int64 */
-    GLU_ERR_WORKSPACE = 8     /* glu_dual_gemv_backward: workspace NULL, not 256-byte aligned
+    GLU_ERR_WORKSPACE = 8,    /* glu_dual_gemv_backward: workspace NULL, not 256-byte aligned
                                  or smaller than glu_dual_gemv_backward_workspace asks */
+    GLU_ERR_SCRATCH_LIMIT = 9 /* glu_dual_gemv_backward_noalloc: the call needs more scratch than
+                                 the library's fixed device array holds */
 } glu_status;
 
 /*
@@ -236,6 +238,26 @@ glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w
                                   const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
                                   int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                                   void* stream);
+
+/*
+ * glu_dual_gemv_backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument, no allocation.  The scratch the backward
+ * needs lives in one 48 MiB device array of the library (50,331,648 bytes;
+ * each GPU the library runs on holds its own copy until the process ends).
+ * Same arguments, results and validation as glu_dual_gemv_backward without the
+ * workspace; a shape whose glu_dual_gemv_backward_workspace exceeds 48 MiB
+ * returns GLU_ERR_SCRATCH_LIMIT before any HIP call (e.g. K=2560 N=9216 is
+ * served up to M = 253, K=4096 N=12288 up to M = 217).  The first
+ * call on a device looks the array up (hipGetSymbolAddress).  All calls on one
+ * GPU share its array and leave the last call's contents there (on return it
+ * begins with dg and du, as the workspace does): calls that overlap on one GPU
+ * (two streams, or a graph replay and another call in flight) race and must
+ * be ordered by the caller.
+ */
+glu_status glu_dual_gemv_backward_noalloc(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
+                                          const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w,
+                                          uint16_t* dup_w, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Workspace bytes glu_dual_gemv_backward needs for (M, N, K), into *bytes
  * (0 when an extent is zero).  Host only.  GLU_ERR_BAD_SHAPE or

@@ -582,3 +582,24 @@ def test_mfma8_rings_above_64k_refused(lib, segments):
     t = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_segments=segments)
     assert lib.glu_dual_gemv_plan_tuned(32, 17408, 5120, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP
     assert 2 * 32 * segments * 128 > 64 * 1024
+
+
+def test_backward_noalloc_validation_before_any_hip_call(lib):
+    """The no-allocation backward checks its arguments as the workspace entry point does, and refuses
+    a shape whose scratch exceeds its fixed array, all before any HIP call."""
+    M, N, K = 2, 64, 128
+    p, _ = _bwd_ptrs(M, N, K)
+    call = lib.glu_dual_gemv_backward_noalloc
+    assert call(0, *p[1:7], M, N, K, None) == NULLP
+    assert call(p[0] + 1, *p[1:7], M, N, K, None) == ALIGN
+    assert call(p[0], p[1], p[2], p[3], p[0] + 2, p[5], p[6], M, N, K, None) == ALIAS
+    assert call(*p[:7], M, N, 100, None) == UNSUP          # K % 8 != 0
+    assert call(*p[:7], -1, N, K, None) == SHAPE
+    assert call(*p[:7], 65537, N, K, None) == UNSUP
+    # K=2560 N=9216 M=512 needs more than the 48 MiB array: refused whatever the pointers
+    assert api.backward_workspace_bytes(512, 9216, 2560) > api.NOALLOC_SCRATCH_BYTES
+    big = [1 << 40, (1 << 40) + (1 << 32), (1 << 40) + (2 << 32), (1 << 40) + (3 << 32),
+           (1 << 40) + (4 << 32), (1 << 40) + (5 << 32), (1 << 40) + (6 << 32)]
+    assert call(*big, 512, 9216, 2560, None) == api.GLU_ERR_SCRATCH_LIMIT
+    assert lib.glu_last_hip_error() == 0
+    assert api.status_string(api.GLU_ERR_SCRATCH_LIMIT).startswith("GLU_ERR_SCRATCH_LIMIT")
