@@ -15,7 +15,9 @@ import torch  # loads torch's HIP runtime first, so the library binds to the sam
 
 from . import build as _build
 
-LIBRARY_PATH = _build.LIBRARY
+# another build of the same sources (the host-sanitized one of glu_mlp_gemv_amd/sanitize.py) may be
+# named in GLU_GEMV_LIBRARY
+LIBRARY_PATH = os.environ.get("GLU_GEMV_LIBRARY") or _build.LIBRARY
 
 # enum values of include/glu_gemv.h
 GLU_OK = 0
@@ -77,7 +79,7 @@ class Tuning(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("rows_per_wave", ctypes.c_int), ("waves_per_block", ctypes.c_int),
                 ("grid", ctypes.c_int), ("mfma_segments", ctypes.c_int), ("mfma_hidden", ctypes.c_int),
                 ("mfma_depth", ctypes.c_int), ("gemm_tile_n", ctypes.c_int), ("gemm_tile_m", ctypes.c_int),
-                ("xcd_bands", ctypes.c_int), ("mfma_order", ctypes.c_int)]
+                ("xcd_bands", ctypes.c_int), ("gemv_dot", ctypes.c_int), ("mfma_order", ctypes.c_int)]
 
 
 class Projection(ctypes.Structure):

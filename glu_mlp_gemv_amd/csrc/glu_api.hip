@@ -113,6 +113,9 @@ glu_status plan_valu(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     }
     c.grid = (int)(grid < 1 ? 1 : grid);
     c.M = (int)m_pl;
+    const int dot = t ? t->gemv_dot : 0;
+    if (dot < 0 || dot > 2 || (dot == 2 && M != 1)) return GLU_ERR_UNSUPPORTED;
+    c.diag = dot == 2;
     if (!glu::valu_supported(c)) return GLU_ERR_UNSUPPORTED;
     glu::ValuConfig last = c;  // the last slice may be narrower: it must be instantiated too
     last.M = (int)(M - (ceil_div(M, m_pl) - 1) * m_pl);
@@ -121,7 +124,11 @@ glu_status plan_valu(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launc
     L->valu = c;
     L->m_per_launch = (int)m_pl;
     L->launches = (int)ceil_div(M, m_pl);
-    L->accum_depth = 8 * c.U * c.NB + glu::kWaveSumDepth;
+    // FMA: a lane's 8 products per chunk in order, then the butterfly.  Matrix cores: per row one
+    // MFMA per 512-element piece, each adding a 32-product block (a tree of depth 5) to the
+    // accumulator, counted at twice the fp32 unit roundoff (the core's internal rounding is not
+    // specified), then the butterfly over the 16 diagonal entries
+    L->accum_depth = c.diag ? 2 * (c.U * c.NB + 5) + glu::kWaveSumDepth : 8 * c.U * c.NB + glu::kWaveSumDepth;
     return GLU_OK;
 }
 
@@ -325,7 +332,7 @@ glu_status plan_ceiling(int64_t rows, int64_t row_bytes, const glu_tuning* t, Ce
     if (rows < 0 || row_bytes < 0 || rows > kMaxDim) return GLU_ERR_BAD_SHAPE;
     if (mul_overflows(rows, row_bytes, INT64_MAX / 2)) return GLU_ERR_BAD_SHAPE;
     if (t && (t->kernel || t->mfma_segments || t->mfma_hidden || t->mfma_depth || t->gemm_tile_n ||
-              t->gemm_tile_m)) {
+              t->gemm_tile_m || t->mfma_order || t->gemv_dot)) {
         return GLU_ERR_UNSUPPORTED;
     }
     *c = CeilingLaunch{};
@@ -349,9 +356,12 @@ glu_status plan_ceiling(int64_t rows, int64_t row_bytes, const glu_tuning* t, Ce
 glu_status plan_launch(int64_t M, int64_t N, int64_t K, bool aligned16, const glu_tuning* t, Launch* L)
 {
     const glu_status st = plan_launch_any(M, N, K, aligned16, t, L);
-    // the K-walk order is a field of the 8-row MFMA kernel only
+    // the K-walk order is a field of the 8-row MFMA kernel only, the dot products' unit of the VALU GEMV
     if (st == GLU_OK && t && t->mfma_order && L->kernel != GLU_KERNEL_NONE &&
         !(L->kernel == GLU_KERNEL_MFMA && L->mfma.rows == 8)) {
+        return GLU_ERR_UNSUPPORTED;
+    }
+    if (st == GLU_OK && t && t->gemv_dot && L->kernel != GLU_KERNEL_NONE && L->kernel != GLU_KERNEL_VALU) {
         return GLU_ERR_UNSUPPORTED;
     }
     return st;
@@ -474,7 +484,9 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
         return GLU_OK;
     }
     const int forced = t ? t->kernel : 0;
-    if (t && (t->gemm_tile_n || t->gemm_tile_m || t->xcd_bands || t->mfma_order)) return GLU_ERR_UNSUPPORTED;
+    if (t && (t->gemm_tile_n || t->gemm_tile_m || t->xcd_bands || t->mfma_order || t->gemv_dot)) {
+        return GLU_ERR_UNSUPPORTED;
+    }
     const bool mfma_fields = t && (t->mfma_segments || t->mfma_hidden || t->mfma_depth);
     const bool mfma = fast && mult4 && (forced == GLU_KERNEL_MFMA || (forced == 0 && (M >= 2 || mfma_fields)));
     if (forced == GLU_KERNEL_MFMA && !mfma) return GLU_ERR_UNSUPPORTED;
@@ -935,8 +947,13 @@ void describe_launch(const Launch& L, bool grouped, char* buf, int len)
     switch (L.kernel) {
     case GLU_KERNEL_VALU: {
         const glu::ValuConfig& c = L.valu;
-        snprintf(buf, (size_t)len, "glu::%s<%d, %d, %d, %d, %s, %s>", grouped ? "grouped_kernel" : "valu_kernel",
-                 c.M, c.R, c.U, c.NB, tf[glu::valu_hidden_in_lds(c.M, c.U, c.NB)], tf[c.ragged]);
+        if (c.diag) {
+            snprintf(buf, (size_t)len, "glu::valu_kernel<%d, %d, %d, %d, %s, %s, true>", c.M, c.R, c.U, c.NB,
+                     tf[glu::valu_hidden_in_lds(c.M, c.U, c.NB)], tf[c.ragged]);
+        } else {
+            snprintf(buf, (size_t)len, "glu::%s<%d, %d, %d, %d, %s, %s>", grouped ? "grouped_kernel" : "valu_kernel",
+                     c.M, c.R, c.U, c.NB, tf[glu::valu_hidden_in_lds(c.M, c.U, c.NB)], tf[c.ragged]);
+        }
         break;
     }
     case GLU_KERNEL_MFMA: {

@@ -23,6 +23,7 @@ struct ValuConfig {
     bool ragged;  // NB * U * 64 > K / 8: clamp and zero the excess chunks
     int grid;     // workgroups (persistent)
     int block;    // threads per workgroup (multiple of 64)
+    bool diag;    // M == 1: dot products on the matrix cores (the diagonal of one MFMA per chunk-set)
 };
 
 // Where the MFMA kernel keeps hidden [M,K]:
@@ -58,7 +59,7 @@ struct RowStrides {
 
 // per-M instantiation tables (glu_valu_m<M>.hip)
 using ValuFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, RowStrides);
-ValuFn valu_pick_1(int R, int U, int NB, bool ragged);
+ValuFn valu_pick_1(int R, int U, int NB, bool ragged, bool diag);
 ValuFn valu_pick_2(int R, int U, int NB, bool ragged);
 ValuFn valu_pick_3(int R, int U, int NB, bool ragged);
 ValuFn valu_pick_4(int R, int U, int NB, bool ragged);

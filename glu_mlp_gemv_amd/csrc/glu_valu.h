@@ -28,12 +28,26 @@
 // in fp32, so each step rounds once).  The per-lane order does not depend on
 // M or R, so every row of a batched call is bitwise equal to the M=1 call on
 // that row.
+//
+// DIAG (M = 1): the same loads, with the dot products on the matrix cores.  A
+// wave's chunk-set of a row (lane l: chunk l of the set) is fed to
+// v_mfma_f32_16x16x32_bf16 as A = the weight chunks and B = the hidden chunks
+// exactly as loaded: lane l supplies A row l%16 and B column l%16 at K-block
+// l/16, so D[i][i] = sum over q < 4 of (weight chunk i+16q) . (hidden chunk
+// i+16q), while the off-diagonal entries pair unrelated chunks and are never
+// read.  The U chunk-sets of a row accumulate into one D; lane l holds
+// D[4(l/16)+e][l%16], so the 16 diagonal entries sit in lanes 0-3, 20-23,
+// 40-43 and 60-63 (e = l%4), and the wave butterfly over those values (zeros
+// elsewhere, which add exactly) gives the row's dot product.  This removes
+// the widening and the FMAs from the vector ALU (about 200 instructions per
+// row and wave) while keeping the streaming pattern of whole 1 KiB row pieces.
 #pragma once
 
 #include <type_traits>
 
 #include "glu_device.h"
 #include "glu_launch.h"
+#include "glu_mfma_common.h"
 
 namespace glu {
 
@@ -54,13 +68,16 @@ __device__ __forceinline__ float dot_chunk(const u32x4& h, const u32x4& w, float
 
 // hidden [M,K], gate_w/up_w [N,K] (16-byte aligned, K % 8 == 0), out [M,N], rows at the strides of ld.
 // NB <= 2; NB * U * 64 >= K/8, with equality unless RAGGED.  Dynamic LDS: M * K * 2 bytes when HLDS, else none.
-template <int M, int R, int U, int NB, bool HLDS, bool RAGGED>
-__global__ void __launch_bounds__(kValuMaxThreads)
+// DIAG launches at most 4 waves per workgroup (one per SIMD at the default 4): a wave may then
+// hold its MFMA operands, accumulators and two stages of loads in up to 512 registers.
+template <int M, int R, int U, int NB, bool HLDS, bool RAGGED, bool DIAG = false>
+__global__ void __launch_bounds__(DIAG ? kMfmaMaxThreads : kValuMaxThreads)
 valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
             const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
             int N, int K, RowStrides ld)
 {
     static_assert(NB == 1 || NB == 2, "a row group streams in one or two batches");
+    static_assert(!DIAG || (M == 1 && !HLDS), "the matrix-core dot products serve one row of hidden in registers");
     const int64_t ldo = ld.o;
     const int ldh8 = (int)(ld.h >> 3);  // hidden row stride in 16-byte chunks
     constexpr int MR = M * R;
@@ -121,6 +138,7 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     };
 
     float ag[M][R], au[M][R];
+    f32x4_t dg[R], du[R];  // DIAG: the row's D of gate and up
     float resG = 0.0f, resU = 0.0f;
 
     // Results of group gi sit in lanes (gi % SLOTS)*MR + m*R + r; the epilogue
@@ -144,6 +162,22 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     auto accumulate = [&](auto Bc, const u32x4 (&wg)[R][U], const u32x4 (&wu)[R][U]) {
         constexpr int B = decltype(Bc)::value;
         const u32x4 z = {0u, 0u, 0u, 0u};
+        if constexpr (DIAG) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int c = (B * U + i) * kWave + lane;
+                const bool ok = !RAGGED || c < nchunks;
+                const u32x4 h = RAGGED ? (ok ? hreg[0][B][i] : z) : hreg[0][B][i];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const u32x4 xg = RAGGED ? (ok ? wg[r][i] : z) : wg[r][i];
+                    const u32x4 xu = RAGGED ? (ok ? wu[r][i] : z) : wu[r][i];
+                    dg[r] = mfma16(xg, h, dg[r]);
+                    du[r] = mfma16(xu, h, du[r]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int c = (B * U + i) * kWave + lane;
@@ -180,6 +214,13 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
                     au[m][r] = 0.0f;
                 }
             }
+            if constexpr (DIAG) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    dg[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    du[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+            }
         }
         if constexpr (NB == 1) {
             accumulate(std::integral_constant<int, 0>{}, wg, wu);
@@ -192,6 +233,20 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
         }
         if (b == NB - 1) {
             const int slot = gi % SLOTS;
+            if constexpr (DIAG) {
+                // lane l holds D[4(l/16) + e][l%16]: the diagonal entry e = l%4 in lanes with l%16 / 4 == l/16
+                const int e = lane & 3;
+                const bool diag = ((lane & 15) >> 2) == (lane >> 4);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    auto pick = [&](const f32x4_t& d) {
+                        const float v = e == 0 ? d[0] : (e == 1 ? d[1] : (e == 2 ? d[2] : d[3]));
+                        return diag ? v : 0.0f;
+                    };
+                    ag[0][r] = pick(dg[r]);
+                    au[0][r] = pick(du[r]);
+                }
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
 #pragma unroll
@@ -231,34 +286,34 @@ valu_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ ga
     }
 }
 
-template <int M, int R, int U, int NB, bool RAGGED>
+template <int M, int R, int U, int NB, bool RAGGED, bool DIAG = false>
 constexpr ValuFn valu_fn()
 {
-    return valu_kernel<M, R, U, NB, valu_hidden_in_lds(M, U, NB), RAGGED>;
+    return valu_kernel<M, R, U, NB, valu_hidden_in_lds(M, U, NB), RAGGED, DIAG>;
 }
 
 // U in 1..8 for NB == 1, 5..8 for NB == 2 (NB == 2 arises only when K/8 > 512).
-template <int M, int R, int NB, bool RAGGED>
+template <int M, int R, int NB, bool RAGGED, bool DIAG = false>
 ValuFn valu_pick_u(int U)
 {
     switch (U) {
-    case 1: if constexpr (NB == 1) return valu_fn<M, R, 1, NB, RAGGED>(); else return nullptr;
-    case 2: if constexpr (NB == 1) return valu_fn<M, R, 2, NB, RAGGED>(); else return nullptr;
-    case 3: if constexpr (NB == 1) return valu_fn<M, R, 3, NB, RAGGED>(); else return nullptr;
-    case 4: if constexpr (NB == 1) return valu_fn<M, R, 4, NB, RAGGED>(); else return nullptr;
-    case 5: return valu_fn<M, R, 5, NB, RAGGED>();
-    case 6: return valu_fn<M, R, 6, NB, RAGGED>();
-    case 7: return valu_fn<M, R, 7, NB, RAGGED>();
-    case 8: return valu_fn<M, R, 8, NB, RAGGED>();
+    case 1: if constexpr (NB == 1) return valu_fn<M, R, 1, NB, RAGGED, DIAG>(); else return nullptr;
+    case 2: if constexpr (NB == 1) return valu_fn<M, R, 2, NB, RAGGED, DIAG>(); else return nullptr;
+    case 3: if constexpr (NB == 1) return valu_fn<M, R, 3, NB, RAGGED, DIAG>(); else return nullptr;
+    case 4: if constexpr (NB == 1) return valu_fn<M, R, 4, NB, RAGGED, DIAG>(); else return nullptr;
+    case 5: return valu_fn<M, R, 5, NB, RAGGED, DIAG>();
+    case 6: return valu_fn<M, R, 6, NB, RAGGED, DIAG>();
+    case 7: return valu_fn<M, R, 7, NB, RAGGED, DIAG>();
+    case 8: return valu_fn<M, R, 8, NB, RAGGED, DIAG>();
     default: return nullptr;
     }
 }
 
-template <int M, int R>
+template <int M, int R, bool DIAG = false>
 ValuFn valu_pick_m(int U, int NB, bool ragged)
 {
-    if (NB == 1) return ragged ? valu_pick_u<M, R, 1, true>(U) : valu_pick_u<M, R, 1, false>(U);
-    if (NB == 2) return ragged ? valu_pick_u<M, R, 2, true>(U) : valu_pick_u<M, R, 2, false>(U);
+    if (NB == 1) return ragged ? valu_pick_u<M, R, 1, true, DIAG>(U) : valu_pick_u<M, R, 1, false, DIAG>(U);
+    if (NB == 2) return ragged ? valu_pick_u<M, R, 2, true, DIAG>(U) : valu_pick_u<M, R, 2, false, DIAG>(U);
     return nullptr;
 }
 

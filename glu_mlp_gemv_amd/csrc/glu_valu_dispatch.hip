@@ -7,8 +7,9 @@ namespace {
 
 ValuFn pick(const ValuConfig& c)
 {
+    if (c.diag && c.M != 1) return nullptr;
     switch (c.M) {
-    case 1: return valu_pick_1(c.R, c.U, c.NB, c.ragged);
+    case 1: return valu_pick_1(c.R, c.U, c.NB, c.ragged, c.diag);
     case 2: return valu_pick_2(c.R, c.U, c.NB, c.ragged);
     case 3: return valu_pick_3(c.R, c.U, c.NB, c.ragged);
     case 4: return valu_pick_4(c.R, c.U, c.NB, c.ragged);
@@ -24,7 +25,7 @@ ValuFn pick(const ValuConfig& c)
 
 bool valu_supported(const ValuConfig& c)
 {
-    if (c.block < kWave || c.block > kValuMaxThreads || c.block % kWave != 0) return false;
+    if (c.block < kWave || c.block > (c.diag ? kMfmaMaxThreads : kValuMaxThreads) || c.block % kWave != 0) return false;
     return pick(c) != nullptr;
 }
 

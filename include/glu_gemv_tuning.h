@@ -39,6 +39,9 @@ typedef struct glu_tuning {
     int gemm_tile_m;      /* GEMM: hidden rows per output tile (64 or 128) */
     int xcd_bands;        /* glu_read_ceiling: 1 = the workgroups one XCD runs take one
                              contiguous band of rows (grid a multiple of 8) */
+    int gemv_dot;         /* VALU at M = 1: 1 = dot products as fp32 FMAs on the vector ALU,
+                             2 = on the matrix cores (the diagonal of one MFMA per 512-element
+                             piece of a row; at most 4 waves per workgroup) */
     int mfma_order;       /* MFMA, 8 rows per wave: 1 = each block of 32 weight rows walks K
                              in turn; 2 = a workgroup walks K once for all its blocks (at
                              most 3), loading each K-slice of hidden once (8 segments,

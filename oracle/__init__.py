@@ -61,6 +61,11 @@ def _load() -> ctypes.CDLL:
     if _ACTIVE is not None:
         return _ACTIVE
     if _DEFAULT is None:
+        # a sanitized build of the same source (glu_mlp_gemv_amd/sanitize.py) may be named here
+        alt = os.environ.get("GLU_ORACLE_LIBRARY")
+        if alt:
+            _DEFAULT = _bind(alt)
+            return _DEFAULT
         if not os.path.exists(_build.LIBRARY):
             _build.build()
         _DEFAULT = _bind(_build.LIBRARY)

@@ -60,8 +60,11 @@ def test_fp32_kernels_pass_and_planted_errors_fail():
     assert rep.failures == 1 and not rep.ok
     # a systematic 1-ULP bias on every output fails the bit-exact bar
     biased = check.from_ordered(check.ordered(got.ravel()) + 1)
-    rep = check.compare(biased, ref, depth=depth, k_len=1024)
-    assert not rep.ok
+    rep2 = check.compare(biased, ref, depth=depth, k_len=1024)
+    assert not rep2.ok
+    # the planted errors are not results of the device path: keep them out of the session's slack report
+    check.LEDGER.remove(rep)
+    check.LEDGER.remove(rep2)
 
 
 def test_gate_on_a_rounding_boundary_admits_both_neighbours():

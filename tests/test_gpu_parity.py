@@ -360,3 +360,19 @@ def test_mfma8_slice_major_graph_replays():
         want = api.dual_gemv(h, wg, wu, tuning=t)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {r}"
+
+
+# ---- M = 1 with the dot products on the matrix cores ----------------------------
+
+DOT_SHAPES = [s for s in SMALL if s[0] == 1] + [(1, 9216, 2560), (1, 12288, 4096), (1, 4000, 8192), (1, 70, 64)]
+
+
+@pytest.mark.parametrize("rows", [1, 2])
+@pytest.mark.parametrize("M,N,K", DOT_SHAPES)
+def test_valu_matrix_core_dot(M, N, K, rows):
+    """The M = 1 GEMV with each 512-element piece of a row dotted by one MFMA (the diagonal of D):
+    within the bar against the oracle, ragged K and N tails included."""
+    h, wg, wu = inputs.hidden(M, K, 9), *inputs.weights(N, K, 9)
+    t = api.make_tuning(kernel=api.KERNEL_VALU, gemv_dot=2, rows_per_wave=rows)
+    rep, _, _ = parity(h, wg, wu, tuning=t, label=f"valu matrix-core dot, {rows} rows per wave")
+    assert rep.ok, rep.summary()
