@@ -505,7 +505,7 @@ def run(args):
     # the first ~10 ms of replays of a fresh graph run slower: replay it untimed for PREWARM_SECONDS
     # first (reported), then time TRIALS regions of exactly `steps` replays, each after `warmup`
     # untimed ones, and take the Olympic average (drop the fastest and the slowest, mean of the rest)
-    warm(torch, graph.replay, PREWARM_SECONDS)
+    warm(torch, graph.replay, args.prewarm)
     trials = [time_region(torch, graph.replay, args.steps, args.warmup, stream) for _ in range(TRIALS)]
     ms = olympic(trials)
     ms_per_step = ms / args.steps
@@ -547,7 +547,7 @@ def run(args):
                    "M": M, "K": K, "N": N, "layers": L, "bytes_per_call": bytes_call,
                    "us_per_call": round(launch_us * plan["launches"], 3),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "timing": {"prewarm_s": PREWARM_SECONDS, "trials": TRIALS, "average": "olympic",
+                   "timing": {"prewarm_s": args.prewarm, "trials": TRIALS, "average": "olympic",
                               "trial_ms_per_step": [round(t / args.steps, 5) for t in trials],
                               "median_ms_per_step": round(statistics.median(trials) / args.steps, 5),
                               "min_ms_per_step": round(min(trials) / args.steps, 5)},
@@ -683,6 +683,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--prewarm", type=float, default=PREWARM_SECONDS,
+                    help="seconds of untimed replays of the headline graph before its timed trials")
     ap.add_argument("--workloads", default=None, metavar="FILE", help="also time the batched workloads")
     ap.add_argument("--filter", default=None, help="with --workloads: only the sections whose name contains this "
                                                    "(batched, prefill, backward, rows, grouped)")

@@ -16,7 +16,7 @@ MFMA_TUNINGS = [dict(), dict(mfma_segments=2), dict(mfma_segments=8, waves_per_b
                 dict(rows_per_wave=8, mfma_segments=4, grid=3)]
 
 # kernels driven through the exhaustive epilogue test
-EPILOGUE_PATHS = {"valu": dict(kernel=api.KERNEL_VALU), "generic": dict(kernel=api.KERNEL_GENERIC),
+EPILOGUE_PATHS = {"valu": dict(kernel=api.KERNEL_VALU, gemv_dot=1), "generic": dict(kernel=api.KERNEL_GENERIC),
                   "valu_mfma_dot": dict(kernel=api.KERNEL_VALU, gemv_dot=2),
                   "mfma": dict(kernel=api.KERNEL_MFMA),
                   "mfma8": dict(kernel=api.KERNEL_MFMA, rows_per_wave=8),

@@ -79,7 +79,9 @@ def test_plan(lib, M, N, K, aligned, kernel, launches):
 
 
 def test_describe_names_the_instantiated_kernel(lib):
-    assert api.plan(1, 9216, 2560)["kernel_symbol"] == "glu::valu_kernel<1, 1, 5, 1, false, false>"
+    assert api.plan(1, 9216, 2560)["kernel_symbol"] == "glu::valu_kernel<1, 1, 5, 1, false, false, true>"
+    assert api.plan(1, 9216, 2560, True, api.make_tuning(gemv_dot=1))["kernel_symbol"] == \
+        "glu::valu_kernel<1, 1, 5, 1, false, false>"
     assert api.plan(8, 12288, 4096)["kernel_symbol"] == "glu::mfma_kernel<2, 4, true, false>"
     assert api.plan(32, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<4, 8, 3, false>"
     assert api.plan(16, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<2, 8, 3, false>"
@@ -98,9 +100,15 @@ def test_describe_names_the_instantiated_kernel(lib):
 
 
 def test_plan_accum_depth_valu(lib):
-    p = api.plan(1, 9216, 2560, True)
+    p = api.plan(1, 9216, 2560, True, api.make_tuning(gemv_dot=1))
     # 2560 / 8 = 320 chunks over 64 lanes = 5 chunks of 8 terms, plus 6 butterfly levels
     assert p["accum_depth"] == 5 * 8 + 6
+    # on the matrix cores: 5 MFMAs of 32-product blocks (tree depth 5), at twice the unit roundoff,
+    # plus the butterfly over the diagonal
+    assert api.plan(1, 9216, 2560, True)["accum_depth"] == 2 * (5 + 5) + 6
+    p = api.Plan()
+    t = api.make_tuning(gemv_dot=2, waves_per_block=8)
+    assert lib.glu_dual_gemv_plan_tuned(1, 9216, 2560, 1, ctypes.byref(t), ctypes.byref(p)) == UNSUP
 
 
 @pytest.mark.parametrize("M,N,K", [(-1, 1, 1), (1, -1, 1), (1, 1, -1), (1, 1 << 31, 8), (1, 8, 1 << 31),

@@ -95,11 +95,13 @@ def test_decode_stack_parity():
 
 
 
+@pytest.mark.parametrize("dot", [0, 1])
 @pytest.mark.parametrize("M,N,K", SMALL)
-def test_small_valu(M, N, K):
+def test_small_valu(M, N, K, dot):
+    """dot 0: the default (at M = 1 the matrix-core dot products), 1: fp32 FMAs at every M."""
     h, wg, wu = inputs.hidden(M, K, 3), *inputs.weights(N, K, 3)
-    t = api.make_tuning(kernel=api.KERNEL_VALU)
-    rep, _, _ = parity(h, wg, wu, tuning=t, label="valu")
+    t = api.make_tuning(kernel=api.KERNEL_VALU, gemv_dot=dot)
+    rep, _, _ = parity(h, wg, wu, tuning=t, label=f"valu dot {dot}")
     assert rep.ok, rep.summary()
 
 
@@ -210,11 +212,11 @@ def test_determinism_and_freshness():
 
 @pytest.mark.parametrize("M", [2, 3, 4, 8])
 def test_batched_rows_equal_single_row_valu(M):
-    """VALU path: row m of a batched call is bitwise the M=1 call on hidden row m."""
+    """VALU path with fp32 FMAs: row m of a batched call is bitwise the M=1 call on hidden row m."""
     h, wg, wu = inputs.case("batch_k4096_n12288", M=8, seed=1)
     h = h[:M].contiguous()
     hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
-    t = api.make_tuning(kernel=api.KERNEL_VALU)
+    t = api.make_tuning(kernel=api.KERNEL_VALU, gemv_dot=1)
     batched = bits(gpu_run(hd, gd, ud, t))
     for m in range(M):
         single = bits(gpu_run(hd[m:m + 1].contiguous(), gd, ud, t))
