@@ -6,6 +6,19 @@
 
 namespace glu {
 
+// Two fp32 values to a packed pair of bf16 (lo in bits 0-15), round to nearest with ties to even:
+// gfx950's v_cvt_pk_bf16_f32, one instruction for the pair (f32_to_bf16_rne takes about five per
+// value).  Used where a result is written once and never fed to further arithmetic (a NaN comes
+// out as some quiet NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+
 constexpr int kBwdMaxM = 1 << 16;  // rows of hidden per call
 constexpr int kBwdMfmaMaxM = 64;   // the matrix-core contractions of kPathMfma serve up to here
 constexpr int kBwdChunkM = 8;   // rows of hidden of the VALU contraction kernel at most

@@ -33,6 +33,7 @@
 #include "glu_backward.h"
 #include "glu_device.h"
 #include "glu_launch.h"
+#include "glu_mfma_common.h"
 
 namespace glu {
 
@@ -508,6 +509,11 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             pg[m] = 0.0f;
             pu[m] = 0.0f;
         }
+        // one row of hidden: the dot products on the matrix cores, as the forward's M = 1 GEMV
+        // takes them (each 512-element piece of the row dotted by the diagonal of one
+        // v_mfma_f32_16x16x32_bf16; lane l holds D[4(l/16) + e][l%16], the diagonal entry in lanes
+        // with l%16 / 4 == l/16 at e = l%4, zeros elsewhere for the butterfly)
+        f32x4_t dgm = {0.0f, 0.0f, 0.0f, 0.0f}, dum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const u32x4_b z = {0u, 0u, 0u, 0u};
@@ -515,16 +521,29 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             const u32x4_b u4 = ok[u] ? wu[u] : z;
             wg[u] = g4;
             wu[u] = u4;
+            if constexpr (M == 1) {
+                dgm = mfma16(g4, hw[0][u], dgm);
+                dum = mfma16(u4, hw[0][u], dum);
+            } else {
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
+                for (int m = 0; m < M; ++m) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    pg[m] = __builtin_fmaf(bf16lo(hw[m][u][q]), bf16lo(g4[q]), pg[m]);
-                    pg[m] = __builtin_fmaf(bf16hi(hw[m][u][q]), bf16hi(g4[q]), pg[m]);
-                    pu[m] = __builtin_fmaf(bf16lo(hw[m][u][q]), bf16lo(u4[q]), pu[m]);
-                    pu[m] = __builtin_fmaf(bf16hi(hw[m][u][q]), bf16hi(u4[q]), pu[m]);
+                    for (int q = 0; q < 4; ++q) {
+                        pg[m] = __builtin_fmaf(bf16lo(hw[m][u][q]), bf16lo(g4[q]), pg[m]);
+                        pg[m] = __builtin_fmaf(bf16hi(hw[m][u][q]), bf16hi(g4[q]), pg[m]);
+                        pu[m] = __builtin_fmaf(bf16lo(hw[m][u][q]), bf16lo(u4[q]), pu[m]);
+                        pu[m] = __builtin_fmaf(bf16hi(hw[m][u][q]), bf16hi(u4[q]), pu[m]);
+                    }
                 }
             }
+        }
+        if constexpr (M == 1) {
+            const int e = lane & 3;
+            const bool on = ((lane & 15) >> 2) == (lane >> 4);
+            const float vg = e == 0 ? dgm[0] : (e == 1 ? dgm[1] : (e == 2 ? dgm[2] : dgm[3]));
+            const float vu = e == 0 ? dum[0] : (e == 1 ? dum[1] : (e == 2 ? dum[2] : dum[3]));
+            pg[0] = on ? vg : 0.0f;
+            pu[0] = on ? vu : 0.0f;
         }
         float dg[M], du[M];
         if constexpr (M == 1) {
@@ -584,8 +603,8 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
                     au[m][u][2 * q] = __builtin_fmaf(du[m], bf16lo(wu[u][q]), au[m][u][2 * q]);
                     au[m][u][2 * q + 1] = __builtin_fmaf(du[m], bf16hi(wu[u][q]), au[m][u][2 * q + 1]);
                 }
-                og[q] = (uint32_t)f32_to_bf16_rne(g0) | ((uint32_t)f32_to_bf16_rne(g1) << 16);
-                ou[q] = (uint32_t)f32_to_bf16_rne(u0) | ((uint32_t)f32_to_bf16_rne(u1) << 16);
+                og[q] = pack_bf16x2_rne(g0, g1);
+                ou[q] = pack_bf16x2_rne(u0, u1);
             }
             if (ok[u]) {
                 const int c = lane + kWave * u;
@@ -789,8 +808,11 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     // the one-pass kernels also form G and U: a lane's 8 U products in order, the wave's
     // butterfly, then (K split) the waves of the workgroup in order
     if (p.path == kPathFused1) {
+        // G and U: at M = 2 a lane's 8 products per chunk then the butterfly; at M = 1 one MFMA per
+        // chunk-set (a 32-product tree, counted at twice the unit roundoff) then the butterfly
         const int u = (int)((K / 8 + kWave - 1) / kWave);
-        p.accum_depth = std::max((int)(rows_per_wave + kFusedWaves) + reduce_depth, 8 * u + 6);
+        const int gu_depth = M == 1 ? 2 * (u + 5) + 6 : 8 * u + 6;
+        p.accum_depth = std::max((int)(rows_per_wave + kFusedWaves) + reduce_depth, gu_depth);
     } else if (p.path == kPathSplitK) {
         p.accum_depth = std::max(p.split_rpb + reduce_depth, 8 * p.split_u + 6 + p.split_waves);
     } else if (p.path == kPathMfma) {
