@@ -267,6 +267,23 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         pool = [(*inputs.weights(N, K, 600 + i, device=dev),
                  torch.empty(N, K, dtype=torch.bfloat16, device=dev),
                  torch.empty(N, K, dtype=torch.bfloat16, device=dev)) for i in range(sets)]
+        # yardstick for this read/write mix: device copies of both weights into the gradient buffers
+        # (every byte the backward must move at M = 1, read once and written once)
+
+        def copy_pass():
+            for wg, wu, dwg, dwu in pool:
+                dwg.copy_(wg)
+                dwu.copy_(wu)
+        g = capture(torch, copy_pass)
+        warm(torch, g.replay, WORKLOAD_WARM_SECONDS)
+        ms = time_region(torch, g.replay, reps, 2, stream)
+        us = ms * 1e3 / (reps * sets)
+        b = 8 * N * K
+        res.append({"workload": f"backward_k{K}_n{N}", "M": 0, "K": K, "N": N, "us_per_call": round(us, 3),
+                    "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                    "kernel": "device copy of Wg and Wu (the read/write yardstick)", "pool_sets": sets})
+        print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+        del g
         for M in Ms:
             h = inputs.hidden(M, K, 0).to(dev)
             go = inputs.grad_out(M, N, 0).to(dev)
