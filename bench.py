@@ -193,18 +193,22 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         pool = [inputs.weights(w.N, w.K, 100 + i, device=dev, outlier_frac=w.outlier_frac) for i in range(sets)]
         # every M's graph is built first, then timed in interleaved rounds (median per M), so that
         # the ratios to M = 1 do not depend on the order or on the clock drifting during the run
-        Ms = (1,) + w.Ms
+        # (M, tuning, label): the planner's default for every M, and where hidden is staged in K-slices
+        # above 8 rows also the 8-row kernel's block-by-block K walk, for comparison
+        cases = [(M, None, "default") for M in (1,) + w.Ms]
+        cases += [(M, api.make_tuning(rows_per_wave=8, mfma_order=1), "block_by_block") for M in w.Ms
+                  if M > 8 and M * w.K * 2 > 65536]
         graphs = []
-        for M in Ms:
+        for M, t, _ in cases:
             h = inputs.hidden(M, w.K, 0, row0_scale=w.row0_scale).to(dev)
             out = torch.empty(M, w.N, dtype=torch.bfloat16, device=dev)
 
-            def one_pass(h=h, out=out):
+            def one_pass(h=h, out=out, t=t):
                 for wg, wu in pool:
-                    api.dual_gemv(h, wg, wu, out=out)
+                    api.dual_gemv(h, wg, wu, out=out, tuning=t)
             graphs.append((capture(torch, one_pass), h, out))
         per_round = max(1, reps // BATCHED_ROUNDS)
-        times = [[] for _ in Ms]
+        times = [[] for _ in cases]
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < BATCHED_WARM_SECONDS:  # untimed, interleaved as below
             for g, _, _ in graphs:
@@ -213,7 +217,7 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         for _ in range(BATCHED_ROUNDS):
             for i, (g, _, _) in enumerate(graphs):
                 times[i].append(time_region(torch, g.replay, per_round, 1, stream) * 1e3 / (per_round * sets))
-        for M, ts in zip(Ms, times):
+        for (M, t, label), ts in zip(cases, times):
             us = statistics.median(ts)
             b = algorithmic_bytes(M, w.N, w.K)
             flops = 4 * M * w.N * w.K
@@ -222,7 +226,8 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
                         "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
                         "TFLOPs": round(flops / us / 1e6, 2),
                         "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5),
-                        "kernel": api.plan(M, w.N, w.K)["kernel_symbol"], "pool_sets": sets})
+                        "kernel": api.plan(M, w.N, w.K, True, t)["kernel_symbol"], "variant": label,
+                        "pool_sets": sets})
             print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
         del graphs
         del pool
@@ -261,7 +266,7 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         del pool
         torch.cuda.empty_cache()
     # backward: gradients of hidden and both weights (reads Wg, Wu once more, writes dWg, dWu)
-    for (K, N), Ms in ((((2560, 9216), (1, 4, 16, 64)), ((4096, 12288), (1, 2, 8))) if want("backward") else ()):
+    for (K, N), Ms in ((((2560, 9216), (1, 4, 16, 64, 512)), ((4096, 12288), (1, 2, 8))) if want("backward") else ()):
         per = 4 * N * K * 2  # weights and their gradients per set
         sets = max(4, -(-1_400_000_000 // per))
         pool = [(*inputs.weights(N, K, 600 + i, device=dev),
@@ -298,8 +303,11 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
             ms = time_region(torch, g.replay, reps, 2, stream)
             us = ms * 1e3 / (reps * sets)
             b = 8 * N * K + 4 * M * K + 2 * M * N
+            flops = 12 * M * N * K  # G and U again, dh, and both weight gradients
             res.append({"workload": f"backward_k{K}_n{N}", "M": M, "K": K, "N": N, "us_per_call": round(us, 3),
                         "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "TFLOPs": round(flops / us / 1e6, 2),
+                        "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5),
                         "kernel": "backward", "pool_sets": sets})
             print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
             del g

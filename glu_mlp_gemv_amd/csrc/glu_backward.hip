@@ -445,8 +445,8 @@ splitk_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
 
 // One pass for M <= 2 rows of hidden (K <= 64 * 8 * U): wave w owns weight rows w, w + W, ... (W
 // waves in the grid).  Lane l holds 16-byte chunks l, l + 64, ... of its row of Wg and Wu and of every
-// row of hidden.  Per weight row j: G and U for each hidden row m (fp32 fma per lane, wave
-// butterfly); dg and du (act_grad; above M = 1 lane m forms row m's pair and readlane hands it to
+// row of hidden.  Per weight row j: G and U for each hidden row m (at M = 1 the diagonal of one
+// MFMA per 512-element piece of the row, at M = 2 fp32 fma per lane; then the wave butterfly); dg and du (act_grad; above M = 1 lane m forms row m's pair and readlane hands it to
 // the wave, lanes 0 .. M-1 store them at the workspace head); the row of dWg and dWu (the M products
 // dg[m] h[m] added in order, one rounding); and dh's two contributions accumulated per lane.  The
 // workgroup's waves then add their dh sums in LDS in order 0, 1, ..., and the sum becomes the
