@@ -17,6 +17,9 @@ Prints ONE JSON line.  Other modes:
                        GEMV: on the 32-layer stack at several launch shapes,
                        and at 12-357 MB per launch with a fit t = a + bytes/BW
                        (JSON written to FILE)
+  --units FILE         also time the unit ceilings (glu_unit_ceiling): matrix-core
+                       issue rate of the 16x16x32 and 32x32x16 bf16 MFMA shapes
+                       and the LDS read rate, at 4, 8 and 16 waves per CU
   --calibrate-copy     run a 256 MiB device copy first (reference kernel for
                        rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE scaling)
   --summarize KIND DIR turn rocprofv3 output in DIR into the text summaries
@@ -500,6 +503,38 @@ def bench_ceiling(torch, api, inputs, dev, ws, hs, reps=20, shapes=CEILING_SHAPE
     return out
 
 
+UNIT_NAMES = {1: "mfma_16x16x32_bf16", 2: "mfma_32x32x16_bf16", 3: "lds_read_b128"}
+UNIT_WAVES = (4, 8, 16)  # waves per compute unit: 1, 2 and 4 per SIMD
+CLOCK_GHZ = 2.4          # MI355X peak engine clock, published
+
+
+def bench_units(torch, api, dev, reps=3):
+    """The unit ceilings: matrix-core issue rate of the two bf16 MFMA shapes and LDS read rate, one
+    workgroup per compute unit, a launch of ~0.2-1 s of work per point, median of `reps` launches."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = []
+    for unit in (1, 2, 3):
+        for waves in UNIT_WAVES:
+            iters = 20000 if unit != 3 else 4000
+            api.unit_ceiling(unit, waves, cus, 100, sink)  # warm
+            ts = sorted(time_region(torch, lambda: api.unit_ceiling(unit, waves, cus, iters, sink), 1, 0, stream)
+                        for _ in range(reps))
+            ms = ts[len(ts) // 2]
+            work = api.unit_ceiling_work(unit, waves, cus, iters)
+            ent = {"unit": UNIT_NAMES[unit], "waves_per_cu": waves, "cus": cus, "iterations": iters,
+                   "ms": round(ms, 4)}
+            if unit == 3:
+                ent["bytes_per_clk_per_cu"] = round(work / (ms * 1e-3) / (CLOCK_GHZ * 1e9) / cus, 1)
+            else:
+                ent["tflops"] = round(work / (ms * 1e-3) / 1e12, 1)
+                ent["frac_of_bf16_peak"] = round(ent["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+            out.append(ent)
+            print(f"[units] {ent}", file=sys.stderr, flush=True)
+    return out
+
+
 def run(args):
     import torch
     from glu_mlp_gemv_amd import api, inputs
@@ -589,6 +624,11 @@ def run(args):
         res = bench_ceiling(torch, api, inputs, dev, ws, hs, shapes=shapes, sizes=not args.no_sizes)
         os.makedirs(os.path.dirname(os.path.abspath(args.ceiling)), exist_ok=True)
         with open(args.ceiling, "w") as f:
+            json.dump(res, f, indent=1)
+    if args.units:
+        res = bench_units(torch, api, dev)
+        os.makedirs(os.path.dirname(os.path.abspath(args.units)), exist_ok=True)
+        with open(args.units, "w") as f:
             json.dump(res, f, indent=1)
     if args.workloads:
         extra = {"workloads": bench_workloads(torch, api, inputs, dev, only=args.filter), "stack": line}
@@ -719,6 +759,8 @@ def main():
     ap.add_argument("--shapes", default=None, help="with --ceiling: JSON list of [kernel ('gemv' or 'ceiling'), "
                                                    "label, tuning fields] timed on the stack")
     ap.add_argument("--no-sizes", action="store_true", help="with --ceiling: skip the 12-357 MB size sweep")
+    ap.add_argument("--units", default=None, metavar="FILE",
+                    help="also time the unit ceilings (MFMA shapes, LDS reads) into FILE")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"))
     ap.add_argument("--command", default="", help="the profiled command, recorded in counter summaries")

@@ -54,6 +54,8 @@ EXPORTED_SYMBOLS = (
     "glu_read_ceiling",
     "glu_read_ceiling_plan",
     "glu_dual_gemv_backward_noalloc",
+    "glu_unit_ceiling",
+    "glu_unit_ceiling_work",
 )
 
 
@@ -150,6 +152,10 @@ def library() -> ctypes.CDLL:
     lib.glu_read_ceiling.restype = ctypes.c_int
     lib.glu_read_ceiling_plan.argtypes = [i64, i64, ctypes.POINTER(Tuning), ctypes.POINTER(Plan)]
     lib.glu_read_ceiling_plan.restype = ctypes.c_int
+    lib.glu_unit_ceiling.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, vp, vp]
+    lib.glu_unit_ceiling.restype = ctypes.c_int
+    lib.glu_unit_ceiling_work.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, ctypes.POINTER(ctypes.c_double)]
+    lib.glu_unit_ceiling_work.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -480,6 +486,28 @@ def grouped_gemv_raw(hidden_ptr: int, ldh: int, projections, M: int, K: int, str
     for i, p in enumerate(projections):
         arr[i] = Projection(*p)
     return lib.glu_grouped_gemv(hidden_ptr, ldh, arr, len(projections) if n is None else n, M, K, stream_handle)
+
+
+UNIT_MFMA_16X16X32_BF16 = 1
+UNIT_MFMA_32X32X16_BF16 = 2
+UNIT_LDS_READ_B128 = 3
+
+
+def unit_ceiling_work(unit: int, waves_per_cu: int, workgroups: int, iterations: int) -> float:
+    """Flops (MFMA units) or LDS bytes (LDS unit) of one glu_unit_ceiling launch (host only)."""
+    w = ctypes.c_double()
+    _raise_for(library().glu_unit_ceiling_work(unit, waves_per_cu, workgroups, iterations, ctypes.byref(w)))
+    return w.value
+
+
+def unit_ceiling(unit: int, waves_per_cu: int, workgroups: int, iterations: int, sink: torch.Tensor) -> None:
+    """One launch of a unit-throughput yardstick (MFMA shape or LDS reads) on the current stream of sink's
+    device.  sink: >= 64 int32 of device memory."""
+    if not sink.is_contiguous() or sink.numel() * sink.element_size() < 256 or sink.device.type != "cuda":
+        raise ValueError("sink must hold 64 contiguous 32-bit words of device memory")
+    st = library().glu_unit_ceiling(unit, waves_per_cu, workgroups, iterations, sink.data_ptr(),
+                                    torch.cuda.current_stream(sink.device).cuda_stream)
+    _raise_for(st)
 
 
 def read_ceiling_plan(rows: int, row_bytes: int, tuning: Optional[Tuning] = None) -> dict:

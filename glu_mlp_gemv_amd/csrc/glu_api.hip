@@ -11,6 +11,7 @@
 #include "../../include/glu_gemv.h"
 #include "../../include/glu_gemv_tuning.h"
 #include "glu_backward.h"
+#include "glu_ceiling.h"
 #include "glu_grouped.h"
 #include "glu_launch.h"
 
@@ -1093,6 +1094,41 @@ glu_status glu_read_ceiling(const void* a, const void* b, int64_t rows, int64_t 
     const int64_t bytes = rows * row_bytes;
     if (overlaps(sink, 64 * 4, a, bytes) || overlaps(sink, 64 * 4, b, bytes)) return GLU_ERR_ALIASING;
     const hipError_t e = glu::read_ceiling_launch(a, b, (int)rows, c.U, c.R, c.grid, c.block, c.xcd_bands, sink,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? GLU_OK : fail_launch(e);
+}
+
+namespace {
+
+glu_status check_unit_ceiling(int unit, int waves, int64_t workgroups, int64_t iterations)
+{
+    if (unit < GLU_UNIT_MFMA_16X16X32_BF16 || unit > GLU_UNIT_LDS_READ_B128) return GLU_ERR_UNSUPPORTED;
+    if (waves < 1 || waves > 16 || workgroups < 1 || workgroups > 65536) return GLU_ERR_UNSUPPORTED;
+    if (iterations < 1 || iterations > ((int64_t)1 << 20)) return GLU_ERR_UNSUPPORTED;
+    return GLU_OK;
+}
+
+}  // namespace
+
+glu_status glu_unit_ceiling_work(int unit, int waves_per_cu, int64_t workgroups, int64_t iterations, double* work)
+{
+    const glu_status st = check_unit_ceiling(unit, waves_per_cu, workgroups, iterations);
+    if (st != GLU_OK) return st;
+    if (!work) return GLU_ERR_NULL_POINTER;
+    const double bodies = (double)workgroups * waves_per_cu * (double)iterations;
+    *work = bodies * (unit == GLU_UNIT_MFMA_16X16X32_BF16 ? 8.0 * 16384.0
+                      : unit == GLU_UNIT_MFMA_32X32X16_BF16 ? 4.0 * 32768.0 : 16.0 * 1024.0);
+    return GLU_OK;
+}
+
+glu_status glu_unit_ceiling(int unit, int waves_per_cu, int64_t workgroups, int64_t iterations, uint32_t* sink,
+                            void* stream)
+{
+    const glu_status st = check_unit_ceiling(unit, waves_per_cu, workgroups, iterations);
+    if (st != GLU_OK) return st;
+    if (!sink) return GLU_ERR_NULL_POINTER;
+    if (((uintptr_t)sink & 3u) != 0) return GLU_ERR_MISALIGNED;
+    const hipError_t e = glu::unit_ceiling_launch(unit, (int)workgroups, waves_per_cu, iterations, sink,
                                                   (hipStream_t)stream);
     return e == hipSuccess ? GLU_OK : fail_launch(e);
 }

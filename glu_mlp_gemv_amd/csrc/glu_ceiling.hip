@@ -14,7 +14,9 @@
 // alive.  Whatever time separates the GEMV from this kernel at the same launch
 // shape is arithmetic, reduction and epilogue; whatever separates this kernel
 // from the bytes at peak bandwidth is the memory system and the launch.
+#include "glu_ceiling.h"
 #include "glu_launch.h"
+#include "glu_mfma_common.h"
 
 namespace glu {
 
@@ -99,6 +101,62 @@ read_ceiling_kernel(const u32x4c* __restrict__ a, const u32x4c* __restrict__ b, 
     if (acc == kSinkMagic) sink[lane] = acc;
 }
 
+// Unit ceilings: one workgroup of `waves` waves per compute unit repeats a body that
+// exercises a single unit of the CU and nothing else, so that time per body is that
+// unit's issue rate.  MFMA bodies keep 8 (16x16x32) or 4 (32x32x16) accumulators
+// that no other instruction touches; operands are fixed registers holding finite
+// bf16 values.  The LDS body reads 16 KiB per wave (16 ds_read_b128 of 1 KiB,
+// lane l at byte 16 l of a 1 KiB row chosen from the iteration, conflict-free)
+// from a 64 KiB array and folds the words by XOR.  Like the read ceiling, the
+// single store happens only if the folded value equals kSinkMagic.
+typedef float f32x16c __attribute__((ext_vector_type(16)));
+
+template <int UNIT>
+__global__ void __launch_bounds__(1024)
+unit_ceiling_kernel(int64_t iters, uint32_t* sink)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    uint32_t acc = 0;
+    if constexpr (UNIT == 1 || UNIT == 2) {
+        const u32x4c a = u32x4c{0x3f803f80u ^ (uint32_t)lane, 0x3e003e00u, 0x3d803d80u, 0x3c003c00u + (uint32_t)wave};
+        const u32x4c b = u32x4c{0x3c003c00u, 0x3f003f00u ^ (uint32_t)lane, 0x3e803e80u, 0x3b803b80u};
+        const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, a), bb = __builtin_bit_cast(bf16x8_t, b);
+        if constexpr (UNIT == 1) {
+            f32x4_t d[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bb, d[i], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc ^= __builtin_bit_cast(uint32_t, d[i][0] + d[i][3]);
+        } else {
+            f32x16c d[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = f32x16c{};
+            for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb, d[i], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc ^= __builtin_bit_cast(uint32_t, d[i][0] + d[i][15]);
+        }
+    } else {
+        __shared__ u32x4c L[4096];  // 64 KiB
+        for (int i = threadIdx.x; i < 4096; i += blockDim.x) L[i] = u32x4c{(uint32_t)i, 1u, 2u, 3u};
+        __syncthreads();
+        u32x4c x = {0u, 0u, 0u, 0u};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x ^= L[lane + kWave * (((int)it + 5 * r + 3 * wave) & 63)];
+        }
+        acc = x[0] ^ x[1] ^ x[2] ^ x[3];
+    }
+    if (acc == kSinkMagic) sink[lane] = acc;
+}
+
 using CeilingFn = void (*)(const u32x4c*, const u32x4c*, int, uint32_t*, bool);
 
 template <int R>
@@ -138,6 +196,15 @@ hipError_t read_ceiling_launch(const void* a, const void* b, int rows, int U, in
     if (!fn || (xcd_bands && grid % kXcds != 0)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(block), 0, stream, static_cast<const u32x4c*>(a),
                        static_cast<const u32x4c*>(b), rows, sink, xcd_bands);
+    return hipGetLastError();
+}
+
+hipError_t unit_ceiling_launch(int unit, int cus, int waves, int64_t iters, uint32_t* sink, hipStream_t stream)
+{
+    void (*fn)(int64_t, uint32_t*) = unit == 1 ? unit_ceiling_kernel<1> : unit == 2 ? unit_ceiling_kernel<2>
+                                   : unit == 3 ? unit_ceiling_kernel<3> : nullptr;
+    if (!fn || cus < 1 || waves < 1 || waves * kWave > 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(cus), dim3(waves * kWave), 0, stream, iters, sink);
     return hipGetLastError();
 }
 

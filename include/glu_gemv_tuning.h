@@ -116,6 +116,38 @@ glu_status glu_read_ceiling(const void* a, const void* b, int64_t rows, int64_t 
  * kernel GLU_KERNEL_CEILING, grid and block. */
 glu_status glu_read_ceiling_plan(int64_t rows, int64_t row_bytes, const glu_tuning* tuning, glu_plan* plan);
 
+/*
+ * Unit ceilings: the issue rate of one unit of a compute unit, a measuring stick
+ * for the matrix-core kernels (the tiled GEMM, the backward's contractions)
+ * rather than a part of the projection.  `workgroups` workgroups of
+ * waves_per_cu waves run (pass the device's compute-unit count for one
+ * workgroup per CU); every wave repeats one body `iterations` times:
+ *   GLU_UNIT_MFMA_16X16X32_BF16: 8 independent v_mfma_f32_16x16x32_bf16 on
+ *     register operands, 8 * 16384 flops;
+ *   GLU_UNIT_MFMA_32X32X16_BF16: 4 independent v_mfma_f32_32x32x16_bf16,
+ *     4 * 32768 flops;
+ *   GLU_UNIT_LDS_READ_B128: 16 conflict-free ds_read_b128 of a 64 KiB LDS
+ *     array folded by XOR, 16 KiB read.
+ * glu_unit_ceiling_work gives the flops (MFMA) or LDS bytes (LDS) of one
+ * launch.  sink: 64 uint32 of device memory, written only if a folded result
+ * equals one fixed 32-bit value (it keeps the work from being removed).
+ * unit outside the three, waves_per_cu outside 1..16, workgroups outside
+ * 1..65536 or iterations outside 1..2^20 -> GLU_ERR_UNSUPPORTED; sink NULL ->
+ * GLU_ERR_NULL_POINTER, not 4-byte aligned -> GLU_ERR_MISALIGNED; all decided
+ * before any HIP call.  Asynchronous on stream, graph-capturable, allocates
+ * nothing.
+ */
+#define GLU_UNIT_MFMA_16X16X32_BF16 1
+#define GLU_UNIT_MFMA_32X32X16_BF16 2
+#define GLU_UNIT_LDS_READ_B128 3
+
+glu_status glu_unit_ceiling(int unit, int waves_per_cu, int64_t workgroups, int64_t iterations, uint32_t* sink,
+                            void* stream);
+
+/* The work of that launch (host only): flops for the MFMA units, bytes read for
+ * the LDS unit, in *work; same argument checks. */
+glu_status glu_unit_ceiling_work(int unit, int waves_per_cu, int64_t workgroups, int64_t iterations, double* work);
+
 #ifdef __cplusplus
 }
 #endif

@@ -611,3 +611,34 @@ def test_backward_noalloc_validation_before_any_hip_call(lib):
     assert call(*big, 512, 9216, 2560, None) == api.GLU_ERR_SCRATCH_LIMIT
     assert lib.glu_last_hip_error() == 0
     assert api.status_string(api.GLU_ERR_SCRATCH_LIMIT).startswith("GLU_ERR_SCRATCH_LIMIT")
+
+
+@pytest.mark.parametrize("unit,waves,groups,iters,status", [
+    (0, 4, 256, 10, api.GLU_ERR_UNSUPPORTED),
+    (4, 4, 256, 10, api.GLU_ERR_UNSUPPORTED),
+    (1, 0, 256, 10, api.GLU_ERR_UNSUPPORTED),
+    (1, 17, 256, 10, api.GLU_ERR_UNSUPPORTED),
+    (2, 4, 0, 10, api.GLU_ERR_UNSUPPORTED),
+    (2, 4, 65537, 10, api.GLU_ERR_UNSUPPORTED),
+    (3, 4, 256, 0, api.GLU_ERR_UNSUPPORTED),
+    (3, 4, 256, (1 << 20) + 1, api.GLU_ERR_UNSUPPORTED),
+])
+def test_unit_ceiling_validation_before_any_hip_call(lib, unit, waves, groups, iters, status):
+    w = ctypes.c_double()
+    assert lib.glu_unit_ceiling_work(unit, waves, groups, iters, ctypes.byref(w)) == status
+    assert lib.glu_unit_ceiling(unit, waves, groups, iters, ctypes.c_void_p(1 << 20), None) == status
+    assert lib.glu_last_hip_error() == 0
+
+
+def test_unit_ceiling_pointer_checks(lib):
+    assert lib.glu_unit_ceiling(1, 4, 256, 10, None, None) == NULLP
+    assert lib.glu_unit_ceiling(1, 4, 256, 10, ctypes.c_void_p((1 << 20) + 2), None) == ALIGN
+    assert lib.glu_unit_ceiling_work(1, 4, 256, 10, None) == NULLP
+
+
+def test_unit_ceiling_work():
+    # bodies = workgroups * waves * iterations; 8 MFMAs of 16x16x32 (16384 flops), 4 of 32x32x16
+    # (32768 flops), 16 KiB of LDS reads
+    assert api.unit_ceiling_work(api.UNIT_MFMA_16X16X32_BF16, 4, 256, 1000) == 256 * 4 * 1000 * 8 * 16384
+    assert api.unit_ceiling_work(api.UNIT_MFMA_32X32X16_BF16, 8, 256, 1000) == 256 * 8 * 1000 * 4 * 32768
+    assert api.unit_ceiling_work(api.UNIT_LDS_READ_B128, 16, 3, 7) == 3 * 16 * 7 * 16 * 1024

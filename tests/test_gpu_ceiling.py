@@ -50,3 +50,14 @@ def test_yardstick_leaves_the_sink_alone_on_plain_data():
     api.read_ceiling(a, b, sink)
     torch.cuda.synchronize()
     assert (sink.cpu() == 7).all()
+
+
+@pytest.mark.parametrize("unit", [api.UNIT_MFMA_16X16X32_BF16, api.UNIT_MFMA_32X32X16_BF16, api.UNIT_LDS_READ_B128])
+@pytest.mark.parametrize("waves", [1, 4, 16])
+def test_unit_ceiling_runs_and_leaves_the_sink_alone(unit, waves):
+    # the folded results never equal the fixed value for these operands, so the sink stays as it was
+    print(f"unit ceiling unit={unit} waves={waves}", flush=True)
+    sink = torch.full((64,), 7, dtype=torch.int32, device=DEV)
+    api.unit_ceiling(unit, waves, 256, 50, sink)
+    torch.cuda.synchronize()
+    assert (sink.cpu() == 7).all()
