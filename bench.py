@@ -356,13 +356,22 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         sets = max(4, -(-1_400_000_000 // per))
         pool = [[inputs.weights(n_i, K, 400 + 10 * i + t, device=dev)[0] for t, n_i in enumerate(Ns)]
                 for i in range(sets)]
-        for M in (1, 4, 16, 32):
+        # (M, tuning, label): the planner's default, and above 8 rows the same call with hidden read
+        # from L2 per stage instead of staged whole into every workgroup's LDS first
+        cases = [(M, None, "default") for M in (1, 4, 16, 32)]
+        cases += [(M, api.make_tuning(mfma_hidden=2), "hidden_from_l2") for M in (16, 32)]
+        # and with K-slices of hidden streamed under the weights, one, two or three blocks of 4 groups
+        # of 8 rows per workgroup
+        blocks = -(-rows // 32)
+        cases += [(M, api.make_tuning(mfma_hidden=3, grid=-(-blocks // jb)), f"k_slices_{jb}")
+                  for M in (16, 32) for jb in (1, 2, 3)]
+        for M, t, label in cases:
             h = inputs.hidden(M, K, 0).to(dev)
             outs = [torch.empty(M, n_i, dtype=torch.bfloat16, device=dev) for n_i in Ns]
 
             def one_pass():
                 for ws in pool:
-                    api.grouped_gemv(h, ws, outs=outs)
+                    api.grouped_gemv(h, ws, outs=outs, tuning=t)
             g = capture(torch, one_pass)
             warm(torch, g.replay, WORKLOAD_WARM_SECONDS)
             ms = time_region(torch, g.replay, reps, 2, stream)
@@ -370,7 +379,9 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
             b = per + M * K * 2 + M * rows * 2
             res.append({"workload": name, "M": M, "K": K, "N": list(Ns), "us_per_call": round(us, 3),
                         "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                        "kernel": api.grouped_plan(M, K, rows)["kernel_name"], "pool_sets": sets})
+                        "kernel": api.grouped_plan(M, K, rows, tuning=t, mult8=all(n_i % 8 == 0 for n_i in Ns))["kernel_symbol"],
+                        "variant": label,
+                        "pool_sets": sets})
             print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
             del g
         del pool

@@ -512,6 +512,42 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
         const bool can8 = mult8 && m_pl > 8 && nchunks % 16 == 0 && (!t || !t->mfma_hidden || t->mfma_hidden == 1) &&
                           glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsMax;
         const int rows_req = t ? t->rows_per_wave : 0;
+        // 8-row layout with K-slices of hidden streamed under the weights (mfma_hidden = 3, and the
+        // default above 8 rows of hidden when every projection's N is a multiple of 8): a workgroup of
+        // 4 waves walks K once for up to 3 blocks of 4 groups.  Against hidden staged whole into LDS
+        // first (K=2560): a QKV-like triple (31.5 MB) at M = 16 / 32 9.7 / 10.7 us against 11.0 / 15.0,
+        // a GDN-input-like quad (63.2 MB) 14.5 / 16.4 against 17.0 / 21.6
+        const bool slices_default = mult8 && m_pl > kGrouped8MinM &&
+                                    (!t || (!t->mfma_hidden && !t->mfma_segments && !t->rows_per_wave &&
+                                            !t->waves_per_block && !t->grid));
+        if (slices_default || (t && t->mfma_hidden == 3)) {
+            if (!mult8 || (t && ((rows_req && rows_req != 8) || (t->mfma_segments && t->mfma_segments != 8) ||
+                                 (t->waves_per_block && t->waves_per_block != 4)))) {
+                return GLU_ERR_UNSUPPORTED;
+            }
+            const int64_t nsegs8 = ceil_div(nchunks, 8);
+            c.rows = 8;
+            c.MT4 = (int)(m_pl <= 8 ? 2 : (m_pl + 7) / 8);
+            c.hidden = glu::kHiddenSlices;
+            c.U = 8;
+            c.nsg = (int)ceil_div(nsegs8, c.U);
+            c.ragged = (int64_t)c.nsg * c.U * 8 != nchunks;
+            c.block = glu::kMfmaMaxThreads;
+            const int64_t blocks = ceil_div(rows / 8, 4);
+            // about one workgroup per CU: the fewest blocks per workgroup that keep the grid within the
+            // CUs (QKV-like 192 blocks: one each; GDN-like 386: two each, measured best of 1, 2, 3)
+            const int64_t jb = std::min<int64_t>(ceil_div(blocks, kCUs), glu::kPassBlocks);
+            const int64_t grid = (t && t->grid > 0) ? t->grid : ceil_div(blocks, jb);
+            if (grid < ceil_div(blocks, glu::kPassBlocks) || grid > blocks) return GLU_ERR_UNSUPPORTED;
+            c.grid = (int)grid;
+            if (!glu::grouped_mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
+            L->kernel = GLU_KERNEL_MFMA;
+            L->mfma = c;
+            L->m_per_launch = (int)m_pl;
+            L->launches = (int)ceil_div(M, m_pl);
+            L->accum_depth = (int)(2 * (nsegs8 + 5 + 2));
+            return GLU_OK;
+        }
         if (rows_req == 8 && !can8) return GLU_ERR_UNSUPPORTED;
         if (can8 && (rows_req == 8 || (rows_req == 0 && m_pl > kGrouped8MinM))) {
             const int64_t nsegs8 = nchunks / 8;
@@ -962,7 +998,10 @@ void describe_launch(const Launch& L, bool grouped, char* buf, int len)
     }
     case GLU_KERNEL_MFMA: {
         const glu::MfmaConfig& c = L.mfma;
-        if (grouped && c.rows == 8) {
+        if (grouped && c.rows == 8 && c.hidden == glu::kHiddenSlices) {
+            snprintf(buf, (size_t)len, "glu::grouped_slice_kernel<%d, %d, %d, %s>", c.MT4, c.U, glu::kPassBlocks,
+                     tf[c.ragged]);
+        } else if (grouped && c.rows == 8) {
             snprintf(buf, (size_t)len, "glu::grouped_mfma_kernel<%d, %d, true, %s, 8>", c.MT4, c.U, tf[c.ragged]);
         } else if (grouped) {
             snprintf(buf, (size_t)len, "glu::grouped_mfma_kernel<%d, %d, %s, %s>", c.MT4, c.U,

@@ -232,6 +232,183 @@ grouped_mfma_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int
     }
 }
 
+// 8-row layout with hidden staged in K-slices (above 8 rows of hidden): the slice-major walk of the
+// dual kernel's mfma8_pass_kernel with one weight stream.  The W = 4 waves of a workgroup own
+// blocks of 4 consecutive 8-row groups (blocks blockIdx.x + j * gridDim.x, j < jb <= JBMAX) and walk
+// K once for all of them: stage t is (slice t / jb, block t % jb).  Each K-slice of all M hidden rows
+// (U * 64 elements) is loaded once per workgroup into registers one slice ahead, published to the
+// other half of a two-slice LDS ring after the slice's last stage, and read by every block's stage;
+// one barrier per slice.  Instead of staging all of hidden into every workgroup's LDS before its
+// first weight load (M * K * 2 bytes: 160 KiB at M = 32, K = 2560, as much traffic as a 31 MB
+// projection set's weights over the chip), the slices stream under the weights.  The per-output
+// summation order is that of the 8-row grouped kernel with hidden whole in LDS: bitwise equal.
+// Dynamic LDS: 2 * 8 * MT8 * U * 8 * 16 bytes.  blockDim.x == 256.
+template <int MT8, int U, int JBMAX, bool RAGGED>
+__global__ void __launch_bounds__(kMfmaMaxThreads)
+grouped_slice_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, int M, int K, GroupDesc d, int nsg)
+{
+    constexpr int W = kMfmaMaxThreads / kWave;
+    constexpr int MP = 8 * MT8;
+    constexpr int SC = U * 8;  // 16-byte chunks of a row in one slice
+    static_assert(SC % 16 == 0, "the LDS swizzle permutes 16-chunk blocks of a row");
+    constexpr int HPT = (MP * SC + kMfmaMaxThreads - 1) / kMfmaMaxThreads;
+    extern __shared__ u32x4_t hs[];  // [2][MP][SC], chunk c of row r at c ^ lds_swz8(r)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nchunks = K >> 3;
+    const uint32_t ldh8 = (uint32_t)(ldh >> 3);
+    const int i16 = lane & 15;
+    const int rho = i16 >> 1;                     // weight row (A) and hidden row (B) in its group / tile
+    const int cw = (i16 & 1) * 4 + (lane >> 4);  // 16-byte chunk within a 64-element segment
+    const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hidden);
+
+    const int ngroups = d.rows / 8;
+    const int nblocks = (ngroups + W - 1) / W;
+    if ((int)blockIdx.x >= nblocks) return;  // whole workgroup
+    // blocks of this workgroup; the host launches at least ceil(nblocks / JBMAX) workgroups
+    const int jb = (nblocks - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+
+    auto group_of = [&](int j) __attribute__((always_inline)) {
+        return ((int)blockIdx.x + j * (int)gridDim.x) * W + wave;
+    };
+    auto load_h = [&](int sb, u32x4_t (&hr)[HPT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < HPT; ++i) {
+            const int e = min(i * kMfmaMaxThreads + (int)threadIdx.x, MP * SC - 1);
+            const int m = min(e / SC, M - 1);  // padded rows repeat row M-1, never stored
+            int c = sb * SC + (e % SC);
+            if (RAGGED) c = min(c, nchunks - 1);
+            hr[i] = h4[(uint32_t)m * ldh8 + (uint32_t)c];
+        }
+    };
+    auto store_h = [&](int sb, const u32x4_t (&hr)[HPT]) __attribute__((always_inline)) {
+        u32x4_t* dst = hs + (sb & 1) * MP * SC;
+#pragma unroll
+        for (int i = 0; i < HPT; ++i) {
+            const int e = i * kMfmaMaxThreads + (int)threadIdx.x;
+            if ((MP * SC) % kMfmaMaxThreads == 0 || e < MP * SC) dst[e ^ lds_swz8(e / SC)] = hr[i];
+        }
+    };
+    auto load_w = [&](int sb, int j, u32x4_t (&A)[U]) __attribute__((always_inline)) {
+        const int g = min(group_of(j), ngroups - 1);  // past the last group: re-read it, never stored
+        const GroupRef ref = group_ref(d, 8 * g);     // wave-uniform base, 32-bit lane offsets
+        const char* wp = reinterpret_cast<const char*>(ref.w);
+        const uint32_t ldw8 = (uint32_t)(ref.ldw >> 3);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int c = (sb * U + u) * 8 + cw;
+            if (RAGGED) c = min(c, nchunks - 1);
+            A[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + ((uint32_t)rho * ldw8 + (uint32_t)c) * 16u));
+        }
+    };
+
+    auto finish_group = [&](int g, const f32x4_t (&acc)[MT8]) __attribute__((always_inline)) {
+        if (g >= ngroups) return;
+        // lanes l and l^1 hold the two blocks of the same (weight row, hidden row) pairs:
+        // entries l%2 (weight row 2(l/16)) and 2 + l%2 (row 2(l/16) + 1); one DPP step adds them
+        const bool odd = (lane & 1) != 0;
+        const int row = 8 * g + 2 * (lane >> 4) + (lane & 1);
+#pragma unroll
+        for (int t = 0; t < MT8; ++t) {
+            const f32x4_t dd = acc[t];
+            float v0 = odd ? dd[1] : dd[0];
+            float v1 = odd ? dd[3] : dd[2];
+            v0 = dpp_add<0xB1>(v0);  // lane ^ 1
+            v1 = dpp_add<0xB1>(v1);
+            const int m = 8 * t + (i16 >> 1);
+            if (m < M) group_store(d, m, row, f32_to_bf16_rne(odd ? v1 : v0));
+        }
+    };
+
+    auto compute = [&](int sb, const u32x4_t (&A)[U], f32x4_t (&acc)[MT8]) __attribute__((always_inline)) {
+        if (sb == 0) {
+#pragma unroll
+            for (int t = 0; t < MT8; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        const u32x4_t* src = hs + (sb & 1) * MP * SC;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        u32x4_t b[2][MT8];
+        auto read_b = [&](int u, u32x4_t (&bt)[MT8]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < MT8; ++t) bt[t] = src[(8 * t + rho) * SC + ((u * 8 + cw) ^ lds_swz8(rho))];
+        };
+        read_b(0, b[0]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u + 1 < U) read_b(u + 1, b[(u + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool ok = !RAGGED || (sb * U + u) * 8 + cw < nchunks;
+            const u32x4_t a = RAGGED ? (ok ? A[u] : z) : A[u];
+#pragma unroll
+            for (int t = 0; t < MT8; ++t) {
+                u32x4_t bt = b[u & 1][t];
+                if constexpr (RAGGED) bt = ok ? bt : z;
+                acc[t] = mfma16(a, bt, acc[t]);
+            }
+        }
+    };
+
+    auto body = [&](auto JBc) __attribute__((always_inline)) {
+        constexpr int JB = decltype(JBc)::value;
+        constexpr int L = 2 * JB;  // stages per unrolled step: weight slot t % 2 and block t % JB are static
+        u32x4_t A[2][U];           // weights of stage t in A[t % 2]
+        u32x4_t hr[HPT];           // the next K-slice of hidden, between its load and its publication
+        f32x4_t acc[JB][MT8];
+
+        auto stage = [&](auto Qc, auto tailc, int sb) __attribute__((always_inline)) {
+            constexpr int Q = decltype(Qc)::value;
+            constexpr bool TAIL = decltype(tailc)::value;
+            constexpr int j = Q % JB;
+            constexpr int slot = Q % 2;
+            const bool more = !TAIL || sb + 1 < nsg;
+            if constexpr (j == 0) {
+                if (more) load_h(sb + 1, hr);
+            }
+            if constexpr (j + 1 < JB) {
+                load_w(sb, j + 1, A[1 - slot]);
+            } else {
+                if (more) load_w(sb + 1, 0, A[1 - slot]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // the prefetches are issued before any of this stage's math
+            compute(sb, A[slot], acc[j]);
+            if constexpr (j == JB - 1) {
+                if (more) store_h(sb + 1, hr);
+                __syncthreads();
+            }
+            if (TAIL && sb == nsg - 1) finish_group(group_of(j), acc[j]);
+        };
+        auto steps = [&](auto tailc, int sp) __attribute__((always_inline)) {
+            auto one = [&](auto Qc) __attribute__((always_inline)) {
+                constexpr int Q = decltype(Qc)::value;
+                if (!decltype(tailc)::value || sp + Q / JB < nsg) stage(Qc, tailc, sp + Q / JB);
+            };
+            for_positions<0, L>(one);
+        };
+
+        load_h(0, hr);
+        load_w(0, 0, A[0]);
+        store_h(0, hr);
+        __syncthreads();
+        int sp = 0;
+        for (; sp + 2 < nsg; sp += 2) steps(std::false_type{}, sp);  // every slice here has a next one
+        steps(std::true_type{}, sp);                                   // the last one or two slices
+    };
+
+    if constexpr (JBMAX >= 3) {
+        if (jb >= 3) {
+            body(std::integral_constant<int, 3>{});
+            return;
+        }
+    }
+    if constexpr (JBMAX >= 2) {
+        if (jb == 2) {
+            body(std::integral_constant<int, 2>{});
+            return;
+        }
+    }
+    body(std::integral_constant<int, 1>{});
+}
+
 namespace {
 
 using GroupedMfmaFn = void (*)(const uint16_t*, int64_t, int, int, GroupDesc, int);
@@ -254,6 +431,16 @@ GroupedMfmaFn pick8_u(int U)
     switch (U) {
     case 5: return grouped_mfma_kernel<MT8, 5, true, RG, 8>;
     case 8: return grouped_mfma_kernel<MT8, 8, true, RG, 8>;
+    default: return nullptr;
+    }
+}
+
+GroupedMfmaFn pick_slices(int mt8, bool ragged)
+{
+    switch (mt8) {
+    case 2: return ragged ? grouped_slice_kernel<2, 8, kPassBlocks, true> : grouped_slice_kernel<2, 8, kPassBlocks, false>;
+    case 3: return ragged ? grouped_slice_kernel<3, 8, kPassBlocks, true> : grouped_slice_kernel<3, 8, kPassBlocks, false>;
+    case 4: return ragged ? grouped_slice_kernel<4, 8, kPassBlocks, true> : grouped_slice_kernel<4, 8, kPassBlocks, false>;
     default: return nullptr;
     }
 }
@@ -295,6 +482,7 @@ GroupedMfmaFn pick(int mt4, int U, bool hlds, bool ragged)
 bool grouped_mfma_supported(const MfmaConfig& c)
 {
     if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
+    if (c.rows == 8 && c.hidden == kHiddenSlices) return c.block == kMfmaMaxThreads && c.U == 8 && pick_slices(c.MT4, c.ragged);
     if (c.rows == 8) return c.hidden == kHiddenLds && pick8(c.MT4, c.U, c.ragged) != nullptr;
     if (c.rows != 4 || (c.hidden != kHiddenLds && c.hidden != kHiddenL2)) return false;
     return pick(c.MT4, c.U, c.hidden == kHiddenLds, c.ragged) != nullptr;
@@ -305,6 +493,17 @@ hipError_t grouped_mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidde
 {
     const bool hlds = c.hidden == kHiddenLds;
     GroupedMfmaFn fn;
+    if (c.rows == 8 && c.hidden == kHiddenSlices) {
+        // 4 waves in lockstep; every workgroup owns at most kPassBlocks blocks of 4 groups
+        const int mt8 = M <= 8 ? 2 : (M + 7) / 8;
+        fn = c.block == kMfmaMaxThreads && c.U == 8 ? pick_slices(mt8, c.ragged) : nullptr;
+        const int64_t blocks = (d.rows / 8 + 3) / 4;
+        if (!fn || M < 1 || d.rows % 8 != 0 || (int64_t)c.grid * kPassBlocks < blocks) return hipErrorInvalidValue;
+        const size_t lds = (size_t)2 * 8 * mt8 * c.U * 8 * 16;
+        if (lds > (size_t)kLdsBudget) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.block), lds, stream, hidden, ldh, M, (int)K, d, c.nsg);
+        return hipGetLastError();
+    }
     if (c.rows == 8) {
         // the 8-row layout's XOR swizzle permutes 16-chunk blocks of a row of hidden in LDS
         if (!hlds || (K / 8) % 16 != 0 || d.rows % 8 != 0) return hipErrorInvalidValue;

@@ -295,11 +295,11 @@ def test_grouped_plan_tiny_row_counts(M, rows):
 
 
 def test_grouped_8row_grid():
-    """Workgroups of the 8-row layout: per CU, the larger of its groups / 4 waves and its busiest
-    wave's groups decides the time, so the planner takes the groups per wave with the fewest such
-    steps (ties: more waves); a grid override is taken as given."""
+    """Workgroups of the 8-row layout with hidden whole in LDS (on request): per CU, the larger of
+    its groups / 4 waves and its busiest wave's groups decides the time, so the planner takes the
+    groups per wave with the fewest such steps (ties: more waves); a grid override is taken as given."""
     def grid(Ns, M, **kw):
-        t = api.make_tuning(**kw) if kw else None
+        t = api.make_tuning(rows_per_wave=8, **kw)
         return api.grouped_plan(M, 2560, sum(Ns), tuning=t, mult8=True)["grid"]
     # two workgroups per CU fit (M <= 16 at K = 2560): 2048 wave slots
     assert grid((9216, 9216), 12) == 192      # 2304 groups: 3 per wave (288 would put 2 workgroups on 32 CUs)
@@ -315,7 +315,7 @@ def test_grouped_8row_grid():
     # the model itself: every choice within 4 groups per wave of the fewest the slots allow
     for rows in range(8, 80000, 8 * 97):
         for M in (12, 32):
-            g = api.grouped_plan(M, 2560, rows, mult8=True)
+            g = api.grouped_plan(M, 2560, rows, tuning=api.make_tuning(rows_per_wave=8), mult8=True)
             if not g["kernel_symbol"].endswith(", 8>"):
                 continue
             groups = rows // 8
@@ -338,15 +338,25 @@ def test_grouped_plans():
     # hidden in LDS up to one workgroup's 160 KiB (32 rows at K = 2560), else read through L2
     assert api.grouped_plan(16, 2560, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<4, 5, true, false>"
     assert api.grouped_plan(32, 2560, 100)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 5, true, false>"
-    # every N a multiple of 8, above 8 rows of hidden in LDS: groups of 8 weight rows
+    # every N a multiple of 8, above 8 rows of hidden: groups of 8 weight rows with K-slices of hidden
+    # streamed under the weights, the fewest blocks per workgroup that fit the grid in 256 CUs
     assert api.grouped_plan(32, 2560, 104, mult8=True)["kernel_symbol"] == \
-        "glu::grouped_mfma_kernel<4, 8, true, false, 8>"
+        "glu::grouped_slice_kernel<4, 8, 3, false>"
     assert api.grouped_plan(17, 2176, 104, mult8=True)["kernel_symbol"] == \
+        "glu::grouped_slice_kernel<3, 8, 3, true>"
+    for rows, grid in ((6144, 192), (12352, 193), (18432, 192), (8 * 4 * 256, 256), (8 * 4 * 257, 129),
+                       (8 * 4 * 1000, 334)):
+        p = api.grouped_plan(32, 2560, rows, mult8=True)
+        assert p["grid"] == grid and p["block"] == 256
+    # hidden whole in LDS first, on request
+    assert api.grouped_plan(32, 2560, 104, tuning=api.make_tuning(rows_per_wave=8), mult8=True)["kernel_symbol"] == \
+        "glu::grouped_mfma_kernel<4, 8, true, false, 8>"
+    assert api.grouped_plan(17, 2176, 104, tuning=api.make_tuning(mfma_hidden=1), mult8=True)["kernel_symbol"] == \
         "glu::grouped_mfma_kernel<3, 8, true, true, 8>"
-    assert api.grouped_plan(16, 2560, 104, mult8=True)["kernel_symbol"] == \
-        "glu::grouped_mfma_kernel<2, 8, true, false, 8>"
+    assert api.grouped_plan(16, 2560, 104, mult8=True)["kernel_symbol"] == "glu::grouped_slice_kernel<2, 8, 3, false>"
     assert api.grouped_plan(8, 2560, 104, mult8=True)["kernel_symbol"] == "glu::grouped_mfma_kernel<2, 5, true, false>"
-    assert api.grouped_plan(32, 2568, 104, mult8=True)["kernel_symbol"] == "glu::grouped_mfma_kernel<8, 2, false, true>"
+    # K/8 = 321 chunks: stages of 512 elements run past K (the slices take hidden that LDS could not hold whole)
+    assert api.grouped_plan(32, 2568, 104, mult8=True)["kernel_symbol"] == "glu::grouped_slice_kernel<4, 8, 3, true>"
     t8 = api.make_tuning(rows_per_wave=4)
     assert api.grouped_plan(32, 2560, 104, tuning=t8, mult8=True)["kernel_symbol"] == \
         "glu::grouped_mfma_kernel<8, 5, true, false>"
@@ -642,3 +652,18 @@ def test_unit_ceiling_work():
     assert api.unit_ceiling_work(api.UNIT_MFMA_16X16X32_BF16, 4, 256, 1000) == 256 * 4 * 1000 * 8 * 16384
     assert api.unit_ceiling_work(api.UNIT_MFMA_32X32X16_BF16, 8, 256, 1000) == 256 * 8 * 1000 * 4 * 32768
     assert api.unit_ceiling_work(api.UNIT_LDS_READ_B128, 16, 3, 7) == 3 * 16 * 7 * 16 * 1024
+
+
+def test_grouped_slice_plans():
+    t = api.make_tuning(mfma_hidden=3)
+    p = api.grouped_plan(32, 2560, 6144, tuning=t, mult8=True)
+    assert p["kernel_symbol"] == "glu::grouped_slice_kernel<4, 8, 3, false>" and p["grid"] == 192
+    assert p["block"] == 256
+    # three blocks per workgroup at most: 192 blocks need at least 64 workgroups
+    assert api.grouped_plan(32, 2560, 6144, tuning=api.make_tuning(mfma_hidden=3, grid=64), mult8=True)["grid"] == 64
+    for bad in (dict(mfma_hidden=3, grid=63), dict(mfma_hidden=3, grid=193), dict(mfma_hidden=3, waves_per_block=2),
+                dict(mfma_hidden=3, mfma_segments=5), dict(mfma_hidden=3, rows_per_wave=4)):
+        with pytest.raises(api.GluError):
+            api.grouped_plan(32, 2560, 6144, tuning=api.make_tuning(**bad), mult8=True)
+    with pytest.raises(api.GluError):  # not every projection a multiple of 8 rows
+        api.grouped_plan(32, 2560, 6144, tuning=t, mult8=False)

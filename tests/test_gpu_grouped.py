@@ -102,6 +102,17 @@ CASES = [
     ((2048, 1024, 32, 32), 2560, 12, dict(mfma_segments=5)),  # 8-row layout, 5 segments per stage
     ((9216, 9216), 2560, 12, {}),             # 2304 groups of 8 rows: three per wave on 192 workgroups
     ((9216, 9216), 2560, 16, dict(grid=384)),  # uneven: half the waves take two groups, half one
+    # 8-row layout with K-slices of hidden streamed under the weights, one to three blocks per workgroup
+    ((4096, 1024, 1024), 2560, 32, dict(mfma_hidden=3)),            # 192 blocks, one each
+    ((4096, 1024, 1024), 2560, 32, dict(mfma_hidden=3, grid=64)),   # three blocks per workgroup
+    ((8192, 4096, 32, 32), 2560, 32, dict(mfma_hidden=3, grid=193)),  # 386 blocks, two each
+    ((8192, 4096, 32, 32), 2560, 24, dict(mfma_hidden=3, grid=129)),  # 3 tiles; three, three, ..., two
+    ((2048, 1024, 32, 32), 2560, 9, dict(mfma_hidden=3)),           # two tiles, the second mostly padding
+    ((1024, 512, 8), 2176, 32, dict(mfma_hidden=3)),                # ragged: 34 segments, stages of 8
+    ((1024, 512, 8), 2176, 17, dict(mfma_hidden=3, grid=22)),       # 193 groups: a block of one group
+    ((1024, 256), 1024, 40, dict(mfma_hidden=3)),                   # slices of 32 and 8 rows of hidden
+    ((64, 8), 1024, 2, dict(mfma_hidden=3)),                        # nine groups: 3 blocks, 3 waves idle
+    ((4096, 1024), 8192, 16, dict(mfma_hidden=3, grid=60)),         # 16 slices, blocks of three and two
 ]
 
 
@@ -200,3 +211,18 @@ def test_grouped_k_zero_and_determinism():
     b = api.grouped_gemv(hh, ww)
     torch.cuda.synchronize()
     assert all(np.array_equal(bits(x), bits(y)) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("Ns,K,M,grid", [((4096, 1024, 1024), 2560, 32, 0), ((8192, 4096, 32, 32), 2560, 24, 129),
+                                         ((1024, 512, 8), 2176, 17, 22), ((2048, 1024, 32, 32), 1024, 9, 0)])
+def test_grouped_slices_bitwise_equal_to_hidden_in_lds(Ns, K, M, grid):
+    """The K-slice walk adds every output's products in the order of the 8-row kernel with hidden
+    whole in LDS: the two agree bit for bit."""
+    print(f"grouped slices Ns={Ns} K={K} M={M} grid={grid}", flush=True)
+    h = inputs.hidden(M, K, 33).to(DEV)
+    ws = [w.to(DEV) for w in weight_set(Ns, K, 33)]
+    a = api.grouped_gemv(h, ws, tuning=api.make_tuning(mfma_hidden=3, grid=grid))
+    b = api.grouped_gemv(h, ws, tuning=api.make_tuning(rows_per_wave=8, mfma_hidden=1))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
