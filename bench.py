@@ -289,7 +289,22 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         b = 8 * N * K
         res.append({"workload": f"backward_k{K}_n{N}", "M": 0, "K": K, "N": N, "us_per_call": round(us, 3),
                     "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                    "kernel": "device copy of Wg and Wu (the read/write yardstick)", "pool_sets": sets})
+                    "kernel": "device copy of Wg and Wu (torch copy_)", "pool_sets": sets})
+        print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+        del g
+        # the same copy streamed like the GEMV reads, with nontemporal stores (glu_copy_ceiling)
+
+        def stream_pass():
+            for wg, wu, dwg, dwu in pool:
+                api.copy_ceiling(wg, wu, dwg, dwu)
+        g = capture(torch, stream_pass)
+        warm(torch, g.replay, WORKLOAD_WARM_SECONDS)
+        ms = time_region(torch, g.replay, reps, 2, stream)
+        us = ms * 1e3 / (reps * sets)
+        res.append({"workload": f"backward_k{K}_n{N}", "M": 0, "K": K, "N": N, "us_per_call": round(us, 3),
+                    "GBs": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                    "kernel": "streaming copy of Wg and Wu (glu_copy_ceiling: the read/write yardstick)",
+                    "pool_sets": sets})
         print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
         del g
         for M in Ms:

@@ -56,6 +56,7 @@ EXPORTED_SYMBOLS = (
     "glu_dual_gemv_backward_noalloc",
     "glu_unit_ceiling",
     "glu_unit_ceiling_work",
+    "glu_copy_ceiling",
 )
 
 
@@ -156,6 +157,8 @@ def library() -> ctypes.CDLL:
     lib.glu_unit_ceiling.restype = ctypes.c_int
     lib.glu_unit_ceiling_work.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, ctypes.POINTER(ctypes.c_double)]
     lib.glu_unit_ceiling_work.restype = ctypes.c_int
+    lib.glu_copy_ceiling.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.POINTER(Tuning), vp]
+    lib.glu_copy_ceiling.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -507,6 +510,21 @@ def unit_ceiling(unit: int, waves_per_cu: int, workgroups: int, iterations: int,
         raise ValueError("sink must hold 64 contiguous 32-bit words of device memory")
     st = library().glu_unit_ceiling(unit, waves_per_cu, workgroups, iterations, sink.data_ptr(),
                                     torch.cuda.current_stream(sink.device).cuda_stream)
+    _raise_for(st)
+
+
+def copy_ceiling(a: torch.Tensor, b: torch.Tensor, ca: torch.Tensor, cb: torch.Tensor,
+                 tuning: Optional[Tuning] = None) -> None:
+    """Read/write yardstick: ca[:] = a, cb[:] = b with the M = 1 GEMV's streaming pattern and nontemporal
+    stores (four equal 2-D contiguous device tensors, rows of a multiple of 1 KiB)."""
+    ts = (a, b, ca, cb)
+    if a.dim() != 2 or any(t.shape != a.shape or t.dtype != a.dtype for t in ts):
+        raise ValueError("a, b, ca and cb must be 2-D tensors of one shape and dtype")
+    if not all(t.is_contiguous() and t.device == a.device for t in ts) or a.device.type != "cuda":
+        raise ValueError("a, b, ca and cb must be contiguous and on one GPU")
+    st = library().glu_copy_ceiling(a.data_ptr(), b.data_ptr(), ca.data_ptr(), cb.data_ptr(), a.shape[0],
+                                    a.shape[1] * a.element_size(), ctypes.byref(tuning) if tuning is not None else None,
+                                    torch.cuda.current_stream(a.device).cuda_stream)
     _raise_for(st)
 
 

@@ -1137,6 +1137,27 @@ glu_status glu_read_ceiling(const void* a, const void* b, int64_t rows, int64_t 
     return e == hipSuccess ? GLU_OK : fail_launch(e);
 }
 
+glu_status glu_copy_ceiling(const void* a, const void* b, void* ca, void* cb, int64_t rows, int64_t row_bytes,
+                            const glu_tuning* tuning, void* stream)
+{
+    if (tuning && (tuning->xcd_bands || tuning->rows_per_wave > 2)) return GLU_ERR_UNSUPPORTED;
+    CeilingLaunch c;
+    glu_status st = plan_ceiling(rows, row_bytes, tuning, &c);
+    if (st != GLU_OK) return st;
+    if (rows == 0) return GLU_OK;
+    if (!glu::copy_ceiling_supported(c.U, c.R)) return GLU_ERR_UNSUPPORTED;
+    if (!a || !b || !ca || !cb) return GLU_ERR_NULL_POINTER;
+    if ((((uintptr_t)a | (uintptr_t)b | (uintptr_t)ca | (uintptr_t)cb) & 15u) != 0) return GLU_ERR_MISALIGNED;
+    const int64_t bytes = rows * row_bytes;
+    if (overlaps(ca, bytes, a, bytes) || overlaps(ca, bytes, b, bytes) || overlaps(cb, bytes, a, bytes) ||
+        overlaps(cb, bytes, b, bytes) || overlaps(ca, bytes, cb, bytes)) {
+        return GLU_ERR_ALIASING;
+    }
+    const hipError_t e = glu::copy_ceiling_launch(a, b, ca, cb, (int)rows, c.U, c.R, c.grid, c.block,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? GLU_OK : fail_launch(e);
+}
+
 namespace {
 
 glu_status check_unit_ceiling(int unit, int waves, int64_t workgroups, int64_t iterations)

@@ -157,6 +157,74 @@ unit_ceiling_kernel(int64_t iters, uint32_t* sink)
     if (acc == kSinkMagic) sink[lane] = acc;
 }
 
+// Copy ceiling: the same streaming pattern reading a and b and writing them to ca and cb with
+// nontemporal 16-byte stores, the read/write yardstick for the backward's one-pass kernels (which
+// read both weight matrices once and write both weight gradients once).  Rows of groups the wave
+// does not own are never touched; the padded rows of a last group re-read row rows-1 and skip
+// their stores.
+template <int U, int R>
+__global__ void __launch_bounds__(kValuMaxThreads)
+copy_ceiling_kernel(const u32x4c* __restrict__ a, const u32x4c* __restrict__ b, u32x4c* __restrict__ ca,
+                    u32x4c* __restrict__ cb, int rows)
+{
+    constexpr int CPR = U * kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + threadIdx.x / kWave);
+    const int nwaves = gridDim.x * wpb;
+    const int ngroups = (rows + R - 1) / R;
+    for (int g = wave_id; g < ngroups; g += nwaves) {
+        u32x4c x[R][U], y[R][U];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(g * R + r, rows - 1);
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                x[r][i] = __builtin_nontemporal_load(a + (int64_t)row * CPR + lane + i * kWave);
+                y[r][i] = __builtin_nontemporal_load(b + (int64_t)row * CPR + lane + i * kWave);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = g * R + r;
+            if (row < rows) {
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    __builtin_nontemporal_store(x[r][i], ca + (int64_t)row * CPR + lane + i * kWave);
+                    __builtin_nontemporal_store(y[r][i], cb + (int64_t)row * CPR + lane + i * kWave);
+                }
+            }
+        }
+    }
+}
+
+using CopyFn = void (*)(const u32x4c*, const u32x4c*, u32x4c*, u32x4c*, int);
+
+template <int R>
+CopyFn pick_copy_u(int U)
+{
+    switch (U) {
+    case 1: return copy_ceiling_kernel<1, R>;
+    case 2: return copy_ceiling_kernel<2, R>;
+    case 3: return copy_ceiling_kernel<3, R>;
+    case 4: return copy_ceiling_kernel<4, R>;
+    case 5: return copy_ceiling_kernel<5, R>;
+    case 6: return copy_ceiling_kernel<6, R>;
+    case 7: return copy_ceiling_kernel<7, R>;
+    case 8: return copy_ceiling_kernel<8, R>;
+    default: return nullptr;
+    }
+}
+
+CopyFn pick_copy(int U, int R)
+{
+    switch (R) {
+    case 1: return pick_copy_u<1>(U);
+    case 2: return pick_copy_u<2>(U);
+    default: return nullptr;
+    }
+}
+
 using CeilingFn = void (*)(const u32x4c*, const u32x4c*, int, uint32_t*, bool);
 
 template <int R>
@@ -196,6 +264,18 @@ hipError_t read_ceiling_launch(const void* a, const void* b, int rows, int U, in
     if (!fn || (xcd_bands && grid % kXcds != 0)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(block), 0, stream, static_cast<const u32x4c*>(a),
                        static_cast<const u32x4c*>(b), rows, sink, xcd_bands);
+    return hipGetLastError();
+}
+
+bool copy_ceiling_supported(int U, int R) { return pick_copy(U, R) != nullptr; }
+
+hipError_t copy_ceiling_launch(const void* a, const void* b, void* ca, void* cb, int rows, int U, int R, int grid,
+                               int block, hipStream_t stream)
+{
+    CopyFn fn = pick_copy(U, R);
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(block), 0, stream, static_cast<const u32x4c*>(a),
+                       static_cast<const u32x4c*>(b), static_cast<u32x4c*>(ca), static_cast<u32x4c*>(cb), rows);
     return hipGetLastError();
 }
 

@@ -117,6 +117,21 @@ glu_status glu_read_ceiling(const void* a, const void* b, int64_t rows, int64_t 
 glu_status glu_read_ceiling_plan(int64_t rows, int64_t row_bytes, const glu_tuning* tuning, glu_plan* plan);
 
 /*
+ * Read/write ceiling: copies a to ca and b to cb (each `rows` rows of
+ * row_bytes bytes, dense device memory, 16-byte aligned) in the launch shape
+ * of glu_read_ceiling, with nontemporal 16-byte loads and stores.  It is the
+ * measuring stick for the backward's one-pass kernels, which read both weight
+ * matrices once and write both weight gradients once (the same bytes each
+ * way at M = 1).  tuning: as glu_read_ceiling, with rows_per_wave 1 or 2 and
+ * no xcd_bands.  The four arrays may not overlap (GLU_ERR_ALIASING); other
+ * errors as glu_read_ceiling, all decided before any HIP call.  rows == 0:
+ * GLU_OK, nothing launched.  Asynchronous on stream, graph-capturable,
+ * allocates nothing.
+ */
+glu_status glu_copy_ceiling(const void* a, const void* b, void* ca, void* cb, int64_t rows, int64_t row_bytes,
+                            const glu_tuning* tuning, void* stream);
+
+/*
  * Unit ceilings: the issue rate of one unit of a compute unit, a measuring stick
  * for the matrix-core kernels (the tiled GEMM, the backward's contractions)
  * rather than a part of the projection.  `workgroups` workgroups of

@@ -667,3 +667,22 @@ def test_grouped_slice_plans():
             api.grouped_plan(32, 2560, 6144, tuning=api.make_tuning(**bad), mult8=True)
     with pytest.raises(api.GluError):  # not every projection a multiple of 8 rows
         api.grouped_plan(32, 2560, 6144, tuning=t, mult8=False)
+
+
+@pytest.mark.parametrize("args,tuning,status", [
+    ((0, 1 << 24, 2 << 24, 3 << 24, 16, 5120), None, NULLP),
+    ((1 << 20, 1 << 24, 2 << 24, 0, 16, 5120), None, NULLP),
+    ((1 << 20, 1 << 24, (2 << 24) + 8, 3 << 24, 16, 5120), None, ALIGN),
+    ((1 << 20, 1 << 24, 1 << 20, 3 << 24, 16, 5120), None, ALIAS),                  # ca on a
+    ((1 << 20, 1 << 24, 2 << 24, (1 << 24) + 5120 * 15, 16, 5120), None, ALIAS),    # cb over b's last row
+    ((1 << 20, 1 << 24, 2 << 24, (2 << 24) + 5120 * 8, 16, 5120), None, ALIAS),     # cb over ca
+    ((1 << 20, 1 << 24, 2 << 24, 3 << 24, 16, 5000), None, UNSUP),
+    ((1 << 20, 1 << 24, 2 << 24, 3 << 24, 16, 5120), dict(rows_per_wave=4), UNSUP),
+    ((1 << 20, 1 << 24, 2 << 24, 3 << 24, 16, 5120), dict(xcd_bands=1), UNSUP),
+    ((1 << 20, 1 << 24, 2 << 24, 3 << 24, 0, 5120), None, OK),
+])
+def test_copy_ceiling_validation_before_any_hip_call(lib, args, tuning, status):
+    t = api.make_tuning(**tuning) if tuning else None
+    a, b, ca, cb, rows, row_bytes = args
+    assert lib.glu_copy_ceiling(a, b, ca, cb, rows, row_bytes, ctypes.byref(t) if t else None, None) == status
+    assert lib.glu_last_hip_error() == 0

@@ -61,3 +61,19 @@ def test_unit_ceiling_runs_and_leaves_the_sink_alone(unit, waves):
     api.unit_ceiling(unit, waves, 256, 50, sink)
     torch.cuda.synchronize()
     assert (sink.cpu() == 7).all()
+
+
+@pytest.mark.parametrize("rows,K,fields", [(9216, 2560, {}), (3001, 1024, {"rows_per_wave": 2}), (77, 4096, {}),
+                                           (12288, 4096, {"grid": 256, "waves_per_block": 4})])
+def test_copy_ceiling_copies_every_row_and_nothing_else(rows, K, fields):
+    print(f"copy ceiling rows={rows} K={K} {fields}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(rows + K)
+    a = torch.randn(rows, K, generator=g).to(torch.bfloat16).to(DEV)
+    b = torch.randn(rows, K, generator=g).to(torch.bfloat16).to(DEV)
+    ca = torch.full((rows + 1, K), 7.0, dtype=torch.bfloat16, device=DEV)  # one canary row after the copy
+    cb = torch.full((rows + 1, K), 7.0, dtype=torch.bfloat16, device=DEV)
+    api.copy_ceiling(a, b, ca[:rows], cb[:rows], tuning=api.make_tuning(**fields) if fields else None)
+    torch.cuda.synchronize()
+    assert torch.equal(ca[:rows].view(torch.int16), a.view(torch.int16))
+    assert torch.equal(cb[:rows].view(torch.int16), b.view(torch.int16))
+    assert (ca[rows] == 7.0).all() and (cb[rows] == 7.0).all()
