@@ -30,6 +30,8 @@ constexpr int kFusedWaves = 4;       // waves per workgroup of the one-pass kern
 constexpr int kFusedMaxM = 2;        // one-pass kernel: up to 2 rows of hidden (with 3 the four-launch
                                       // path measured faster: 57.7 against 68.0 us at K=2048 N=8192)
 constexpr int fused_max_u(int M) { return M <= 2 ? kFusedMaxU : 0; }
+// M = 1 at U = 5 (K = 2560) keeps hidden in LDS, within 256 registers
+constexpr bool fused1_hidden_in_lds(int M, int U) { return M == 1 && U == 5; }
 constexpr int fused_waves_per_cu(int M, int U) { return M == 1 && U < 5 ? 8 : 4; }
 constexpr int kCUsForPlan = 256;     // MI355X compute units
 

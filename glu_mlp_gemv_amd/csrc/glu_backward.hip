@@ -452,12 +452,16 @@ splitk_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
 // workgroup's waves then add their dh sums in LDS in order 0, 1, ..., and the sum becomes the
 // workgroup's partial: partial[b][2][M][K].
 template <int M, int U, int WAVES>
-__global__ void __launch_bounds__(WAVES * kWave)
+__global__ void __launch_bounds__(WAVES * kWave, fused1_hidden_in_lds(M, U) ? 2 : 1)
 fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
               const uint16_t* __restrict__ up_w, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dgu,
               uint16_t* __restrict__ dwg, uint16_t* __restrict__ dwu, float* __restrict__ partial, int N, int K)
 {
-    extern __shared__ float red1[];  // [2][M][K]
+    // HLDS: the row of hidden sits in LDS after red1 and each use reads the lane's chunk there: 20
+    // registers fewer (256 at K = 2560; K=2560 N=9216, whole backward 49.4 -> 48.6 us at one wave
+    // per SIMD; two waves per SIMD, which these registers would allow, measured 53.9 us)
+    constexpr bool HLDS = fused1_hidden_in_lds(M, U);
+    extern __shared__ float red1[];  // [2][M][K], then (HLDS) hidden's K / 8 chunks
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + wave);
@@ -465,18 +469,36 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
     const int nchunks = K >> 3;
     const int64_t MN = (int64_t)M * N, MK = (int64_t)M * K;
 
-    u32x4_b hw[M][U];
+    constexpr int HR = HLDS ? 1 : M, HU = HLDS ? 1 : U;
+    u32x4_b hw[HR][HU];
+    u32x4_b* const hl = reinterpret_cast<u32x4_b*>(red1 + 2 * MK);
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = lane + kWave * u;
         ok[u] = c < nchunks;
+        if constexpr (!HLDS) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            hw[m][u] = ok[u] ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + (int64_t)c * 8)
-                             : u32x4_b{0u, 0u, 0u, 0u};
+            for (int m = 0; m < M; ++m) {
+                hw[m][u] = ok[u] ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)m * K + (int64_t)c * 8)
+                                 : u32x4_b{0u, 0u, 0u, 0u};
+            }
         }
     }
+    if constexpr (HLDS) {
+        for (int c = (int)threadIdx.x; c < kWave * U; c += WAVES * kWave) {
+            hl[c] = c < nchunks ? *reinterpret_cast<const u32x4_b*>(hidden + (int64_t)c * 8) : u32x4_b{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+    }
+    // chunk u of hidden row m for this lane
+    auto hid = [&](int m, int u) __attribute__((always_inline)) -> u32x4_b {
+        if constexpr (HLDS) {
+            return hl[lane + kWave * u];
+        } else {
+            return hw[m][u];
+        }
+    };
     float ag[M][U][8], au[M][U][8];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -522,8 +544,9 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             wg[u] = g4;
             wu[u] = u4;
             if constexpr (M == 1) {
-                dgm = mfma16(g4, hw[0][u], dgm);
-                dum = mfma16(u4, hw[0][u], dum);
+                const u32x4_b h = hid(0, u);
+                dgm = mfma16(g4, h, dgm);
+                dum = mfma16(u4, h, dum);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
@@ -587,13 +610,16 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             u32x4_b og, ou;
+            u32x4_b hu[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) hu[m] = hid(m, u);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 // the weights' gradients add the M products in order from +0
                 float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    const float h0 = bf16lo(hw[m][u][q]), h1 = bf16hi(hw[m][u][q]);
+                    const float h0 = bf16lo(hu[m][q]), h1 = bf16hi(hu[m][q]);
                     g0 = __builtin_fmaf(dg[m], h0, g0);
                     g1 = __builtin_fmaf(dg[m], h1, g1);
                     u0 = __builtin_fmaf(du[m], h0, u0);
@@ -871,7 +897,7 @@ hipError_t fused1_launch(const BwdPlan& p, int M, const uint16_t* hidden, const 
         p.fused_grid < 1) {
         return hipErrorInvalidValue;
     }
-    const size_t lds = (size_t)2 * M * K * sizeof(float);
+    const size_t lds = (size_t)2 * M * K * sizeof(float) + (fused1_hidden_in_lds(M, U) ? (size_t)kWave * U * 16 : 0);
     if (lds > (size_t)kLdsBudget) return hipErrorInvalidValue;
     hipLaunchKernelGGL(table[M - 1][U - 1], dim3(p.fused_grid), dim3(kFusedWaves * kWave), lds, stream, hidden,
                        gate_w, up_w, dout, dgu, dwg, dwu, partial, N, K);
