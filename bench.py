@@ -235,8 +235,9 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         del graphs
         del pool
         torch.cuda.empty_cache()
-    # large batches (prefill-like): the tiled GEMM, and the 32-row chunked MFMA path it replaces
-    for (K, N), Ms in ((((5120, 17408), (64, 128, 256, 512, 1024)), ((2560, 9216), (64, 256, 1024)))
+    # large batches (prefill-like): the default plan (the slice-major 8-row MFMA kernel in launches of
+    # 64 rows up to M = 64, the tiled GEMM above) and the alternatives beside it
+    for (K, N), Ms in ((((5120, 17408), (48, 64, 128, 256, 512, 1024)), ((2560, 9216), (48, 64, 256, 1024)))
                        if want("prefill") else ()):
         per = 2 * N * K * 2
         sets = max(4, -(-1_400_000_000 // per))
@@ -244,9 +245,13 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
         for M in Ms:
             h = inputs.hidden(M, K, 0).to(dev)
             out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            variants = [("gemm", None)]
-            if M in (64, 256):
-                variants.append(("mfma_chunks", api.make_tuning(kernel=api.KERNEL_MFMA)))
+            variants = [("default", None)]
+            if M <= 64:
+                variants.append(("gemm", api.make_tuning(kernel=api.KERNEL_GEMM)))
+                variants.append(("mfma_32_row_launches", api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8,
+                                                                         mfma_order=2)))
+            elif M <= 256:
+                variants.append(("mfma_64_row_launches", api.make_tuning(kernel=api.KERNEL_MFMA)))
             for kname, t in variants:
                 def one_pass():
                     for wg, wu in pool:

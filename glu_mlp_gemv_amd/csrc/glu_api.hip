@@ -150,15 +150,21 @@ int default_segments(int64_t nsegs, int mt4, int hidden)
 glu_status plan_mfma_shape(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
 {
     glu::MfmaConfig c{};
-    const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
+    // the slice-major 8-row kernel with stages of 4 segments takes up to 64 rows of hidden per launch
+    const bool pass64 = t && t->rows_per_wave == 8 && t->mfma_order == 2 && t->mfma_segments == 4;
+    const int64_t m_cap = pass64 ? 2 * kMfmaSlice : kMfmaSlice;
+    const int64_t m_pl = M < m_cap ? M : m_cap;
+    if (pass64 && m_pl <= kMfmaSlice) return GLU_ERR_UNSUPPORTED;  // 4-segment stages serve 33..64 rows
     c.MT4 = (int)((m_pl + 3) / 4);
     const int64_t nchunks = K / 8;
     const int64_t nsegs = ceil_div(nchunks, 16);
     const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
     const int seg_req = t ? t->mfma_segments : 0;
+    const int rows_req = t ? t->rows_per_wave : 0;
+    const int order_req = t ? t->mfma_order : 0;
     if (t && t->mfma_hidden) {
         c.hidden = t->mfma_hidden - 1;
-    } else if (t && t->rows_per_wave == 8) {
+    } else if (rows_req == 8) {
         c.hidden = glu::kHiddenSlices;  // the only place 8 rows per wave are built for
     } else if (glu::mfma_hidden_lds_bytes((int)m_pl, K) <= (size_t)glu::kLdsBudget) {
         c.hidden = glu::kHiddenLds;
@@ -173,21 +179,21 @@ glu_status plan_mfma_shape(int64_t M, int64_t N, int64_t K, const glu_tuning* t,
     // (K=5120 N=17408: 62.7 against 64.9 us at M = 16, 71.8 against 81.6 at 32)
     const bool seg8 = seg_req == 0 || seg_req == 4 || seg_req == 8;  // stage sizes built for 8 rows
     const int rows_dflt = (c.hidden == glu::kHiddenSlices && m_pl > 16 && seg8) ? 8 : 4;
-    c.rows = (t && t->rows_per_wave) ? t->rows_per_wave : rows_dflt;
+    c.rows = rows_req ? rows_req : rows_dflt;
     if (c.rows != 4 && !(c.rows == 8 && c.hidden == glu::kHiddenSlices)) return GLU_ERR_UNSUPPORTED;
     // segments of 128 K-elements at 4 rows per wave, of 64 at 8
     const int64_t seg_chunks = c.rows == 8 ? 8 : 16;
     const int64_t nseg = ceil_div(nchunks, seg_chunks);
     if (c.rows == 8) {
-        c.U = (t && t->mfma_segments) ? t->mfma_segments : 8;
+        c.U = seg_req ? seg_req : 8;
     } else {
-        c.U = (t && t->mfma_segments) ? t->mfma_segments : default_segments(nsegs, c.MT4, c.hidden);
+        c.U = seg_req ? seg_req : default_segments(nsegs, c.MT4, c.hidden);
     }
     if (c.U < 1) return GLU_ERR_UNSUPPORTED;
     if (c.hidden == glu::kHiddenSlices) {
         int dflt = c.rows == 8 ? glu::mfma8_slice_depth(c.U) : glu::mfma_slice_depth(c.U);
         if (c.rows == 8 && c.U == 8 && m_pl <= 16) dflt = 2;  // fewer MFMAs per stage: room for a deeper pipeline
-        if (c.rows == 8 && t && t->mfma_order == 2) dflt = 1;  // the slice-major kernel keeps one stage in flight
+        if (c.rows == 8 && order_req == 2) dflt = 1;  // the slice-major kernel keeps one stage in flight
         c.depth = (t && t->mfma_depth) ? t->mfma_depth : dflt;
     } else if (t && t->mfma_depth) {
         return GLU_ERR_UNSUPPORTED;  // only the lockstep kernels take a depth
@@ -209,12 +215,11 @@ glu_status plan_mfma_shape(int64_t M, int64_t N, int64_t K, const glu_tuning* t,
     c.grid = (int)(grid < 1 ? 1 : grid);
     // 8 rows per wave: the order of the K walk (block by block, or K once for up to
     // kPassBlocks blocks of a workgroup, each hidden slice loaded once for all of them)
-    const int order_req = t ? t->mfma_order : 0;
     if (order_req < 0 || order_req > 2 || (order_req && c.rows != 8)) return GLU_ERR_UNSUPPORTED;
     c.order = glu::kOrderBlocks;
     if (c.rows == 8) {
-        const bool pass_fits = c.U == 8 && c.depth == 1 && m_pl > 8 &&
-                               (int64_t)c.grid * glu::kPassBlocks >= glu::mfma8_blocks(N);
+        const bool pass_fits = ((c.U == 8 && m_pl > 8 && m_pl <= kMfmaSlice) || (c.U == 4 && m_pl > kMfmaSlice)) &&
+                               c.depth == 1 && (int64_t)c.grid * glu::kPassBlocks >= glu::mfma8_blocks(N);
         if (order_req == 2 && !pass_fits) return GLU_ERR_UNSUPPORTED;
         c.order = order_req == 2 ? glu::kOrderSlices : glu::kOrderBlocks;
     }
@@ -237,19 +242,22 @@ glu_status plan_mfma_shape(int64_t M, int64_t N, int64_t K, const glu_tuning* t,
 // with the K walk done once for up to 3 blocks of a workgroup (each K-slice of hidden loaded and
 // published once for all of them).  K=5120 N=17408, interleaved warm graphs: M = 16 60.5 us
 // against 62.3 for 4 rows per wave; M = 24 62.7 against 68.7 and M = 32 64.9 against 71.7 for the
-// block-by-block walk (M = 1 at that shape: 53.3).  Overrides of the rows, the order, the stage
-// size, the depth or where hidden lives plan exactly what they ask for.
+// block-by-block walk (M = 1 at that shape: 53.3).  Above 32 rows the same kernel takes launches of
+// 64 rows with stages of 4 segments: M = 64 74.4 us against 128.6 for two launches of 32 rows and
+// 111.2 for the tiled GEMM, which the default path takes above 64 rows.  Overrides of the rows, the
+// order, the stage size, the depth or where hidden lives plan exactly what they ask for.
 glu_status plan_mfma(int64_t M, int64_t N, int64_t K, const glu_tuning* t, Launch* L)
 {
     const int64_t m_pl = M < kMfmaSlice ? M : kMfmaSlice;
     const int waves = (t && t->waves_per_block) ? t->waves_per_block : kMfmaDefaultWaves;
     const bool free_shape = !t || (!t->rows_per_wave && !t->mfma_order && !t->mfma_segments && !t->mfma_depth &&
                                    !t->mfma_hidden);
-    if (free_shape && m_pl > 8 && waves * glu::kWave == glu::kMfmaMaxThreads &&
-        glu::mfma_hidden_lds_bytes((int)m_pl, K) > (size_t)glu::kLdsBudget) {
+    if (free_shape && waves * glu::kWave == glu::kMfmaMaxThreads &&
+        (M > kMfmaSlice || (m_pl > 8 && glu::mfma_hidden_lds_bytes((int)m_pl, K) > (size_t)glu::kLdsBudget))) {
         glu_tuning t8 = t ? *t : glu_tuning{};
         t8.rows_per_wave = 8;
         t8.mfma_order = 2;
+        if (M > kMfmaSlice) t8.mfma_segments = 4;  // launches of 64 rows
         if (plan_mfma_shape(M, N, K, &t8, L) == GLU_OK) return GLU_OK;
     }
     return plan_mfma_shape(M, N, K, t, L);
@@ -310,7 +318,7 @@ glu_status plan_launch_any(int64_t M, int64_t N, int64_t K, bool aligned16, cons
     if (forced == GLU_KERNEL_MFMA) return plan_mfma(M, N, K, t, L);
     if (forced == GLU_KERNEL_GEMM) return plan_gemm(M, N, K, t, L);
     if (forced == 0 && fast) {
-        if (gemm_fields || (M > kMfmaSlice && N <= kGemmMaxN)) return plan_gemm(M, N, K, t, L);
+        if (gemm_fields || (M > 2 * kMfmaSlice && N <= kGemmMaxN)) return plan_gemm(M, N, K, t, L);
         if (M == 1 && K <= kValuMaxDefaultK) return plan_valu(M, N, K, t, L);
         return plan_mfma(M, N, K, t, L);
     }

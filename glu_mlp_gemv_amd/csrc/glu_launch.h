@@ -38,7 +38,7 @@ constexpr int kPassBlocks = 3;
 
 struct MfmaConfig {
     int rows;         // weight rows per wave: 4, or 8 (kHiddenSlices only)
-    int MT4;          // hidden-row tiles of 4 (M <= 4 * MT4 <= 32)
+    int MT4;          // hidden-row tiles of 4 (M <= 4 * MT4 <= 32; 64 for the slice-major 8-row kernel)
     int U;            // K segments per pipeline stage: 128 elements at 4 rows, 64 at 8
     int nsg;          // stages per row group: nsg * U * seg >= K, seg = 128 or 64
     bool ragged;      // the stages run past K: clamp and zero the excess chunks
@@ -52,7 +52,8 @@ struct MfmaConfig {
 // Row strides in elements: row m of hidden at hidden + m*h, row j of gate_w
 // at gate_w + j*g, of up_w at up_w + j*u, row m of out at out + m*o.  The
 // fast kernels take h, g and u as multiples of 8 no larger than 2^25 (their
-// lane offsets are 32-bit byte counts over up to 32 rows).
+// lane offsets are 32-bit: byte counts over up to 32 rows, or counts of
+// 16-byte chunks over the 64 rows of the slice-major 8-row kernel).
 struct RowStrides {
     int64_t h, g, u, o;
 };
@@ -85,7 +86,8 @@ size_t mfma_hidden_lds_bytes(int m, int64_t k);
 size_t mfma8_slice_lds_bytes(int mt8, int u);
 int mfma8_slice_depth(int u);
 // order: kOrderBlocks walks K per block of 4 groups in turn (mfma8_slice_kernel); kOrderSlices walks K
-// once for all of a workgroup's blocks (mfma8_pass_kernel: U == 8, depth 1, grid * kPassBlocks >= blocks)
+// once for all of a workgroup's blocks (mfma8_pass_kernel: depth 1, grid * kPassBlocks >= blocks; U == 8
+// for mt8 2..4, U == 4 for mt8 5..8)
 bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block, int order);
 int64_t mfma8_blocks(int64_t N);  // blocks of 4 groups of 8 weight rows
 hipError_t mfma8_launch(int M, int U, int depth, int order, int nsg, bool ragged, int grid, const uint16_t* hidden,

@@ -403,14 +403,28 @@ namespace {
 
 using Mfma8Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, RowStrides, int);
 
-Mfma8Fn pick_pass(int mt8, bool ragged)
+// 8 < M <= 32: stages of 8 segments (512 elements); 32 < M <= 64: stages of 4 (256 elements), which
+// keep the accumulators of 3 blocks and 8 tiles of hidden rows within the registers
+Mfma8Fn pick_pass(int mt8, int U, bool ragged)
 {
-    switch (mt8) {
-    case 2: return ragged ? mfma8_pass_kernel<2, 8, kPassBlocks, true> : mfma8_pass_kernel<2, 8, kPassBlocks, false>;
-    case 3: return ragged ? mfma8_pass_kernel<3, 8, kPassBlocks, true> : mfma8_pass_kernel<3, 8, kPassBlocks, false>;
-    case 4: return ragged ? mfma8_pass_kernel<4, 8, kPassBlocks, true> : mfma8_pass_kernel<4, 8, kPassBlocks, false>;
-    default: return nullptr;
+    if (U == 8) {
+        switch (mt8) {
+        case 2: return ragged ? mfma8_pass_kernel<2, 8, kPassBlocks, true> : mfma8_pass_kernel<2, 8, kPassBlocks, false>;
+        case 3: return ragged ? mfma8_pass_kernel<3, 8, kPassBlocks, true> : mfma8_pass_kernel<3, 8, kPassBlocks, false>;
+        case 4: return ragged ? mfma8_pass_kernel<4, 8, kPassBlocks, true> : mfma8_pass_kernel<4, 8, kPassBlocks, false>;
+        default: return nullptr;
+        }
     }
+    if (U == 4) {
+        switch (mt8) {
+        case 5: return ragged ? mfma8_pass_kernel<5, 4, kPassBlocks, true> : mfma8_pass_kernel<5, 4, kPassBlocks, false>;
+        case 6: return ragged ? mfma8_pass_kernel<6, 4, kPassBlocks, true> : mfma8_pass_kernel<6, 4, kPassBlocks, false>;
+        case 7: return ragged ? mfma8_pass_kernel<7, 4, kPassBlocks, true> : mfma8_pass_kernel<7, 4, kPassBlocks, false>;
+        case 8: return ragged ? mfma8_pass_kernel<8, 4, kPassBlocks, true> : mfma8_pass_kernel<8, 4, kPassBlocks, false>;
+        default: return nullptr;
+        }
+    }
+    return nullptr;
 }
 
 template <int MT8, bool RG>
@@ -445,7 +459,7 @@ bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block, int orde
 {
     if (block != kMfmaMaxThreads) return false;
     if (mfma8_slice_lds_bytes(mt8, U) > (size_t)kLdsBudget) return false;
-    if (order == kOrderSlices) return U == 8 && depth == 1 && pick_pass(mt8, ragged) != nullptr;
+    if (order == kOrderSlices) return depth == 1 && pick_pass(mt8, U, ragged) != nullptr;
     return order == kOrderBlocks && pick8(mt8, U, depth, ragged) != nullptr;
 }
 
@@ -455,11 +469,14 @@ hipError_t mfma8_launch(int M, int U, int depth, int order, int nsg, bool ragged
                         const uint16_t* gate_w, const uint16_t* up_w, uint16_t* out, int64_t N, int64_t K,
                         RowStrides ld, hipStream_t stream)
 {
-    const int mt8 = (M + 7) / 8;
+    int mt8 = (M + 7) / 8;
+    // a last slice with fewer rows than the slice-major kernels are built for runs on their smallest
+    // tile count (padded rows repeat row M - 1 and are never stored)
+    if (order == kOrderSlices) mt8 = U == 4 ? (mt8 < 5 ? 5 : mt8) : (mt8 < 2 ? 2 : mt8);
     Mfma8Fn fn = nullptr;
     if (order == kOrderSlices) {
         // the slice-major kernel serves at most kPassBlocks blocks per workgroup
-        if (U == 8 && depth == 1 && (int64_t)grid * kPassBlocks >= mfma8_blocks(N)) fn = pick_pass(mt8, ragged);
+        if (depth == 1 && (int64_t)grid * kPassBlocks >= mfma8_blocks(N)) fn = pick_pass(mt8, U, ragged);
     } else if (order == kOrderBlocks) {
         fn = pick8(mt8, U, depth, ragged);
     }

@@ -71,9 +71,9 @@ typedef enum glu_status {
  * Fast path: hidden, gate_w and up_w 16-byte aligned, K a multiple of 8 and
  * K <= 2^25; any other 2-byte-aligned input takes a slower path with the same
  * result contract.  M == 1 with K <= 4096 runs a VALU GEMV; other shapes up
- * to M = 32 run a block-diagonal MFMA kernel; M > 32 runs a tiled MFMA GEMM
- * (GLU_KERNEL_GEMM), one launch per 65536 rows of hidden, each reading the
- * weights once.
+ * to M = 64 run a block-diagonal MFMA kernel (one launch, reading the
+ * weights once); M > 64 runs a tiled MFMA GEMM (GLU_KERNEL_GEMM), one launch
+ * per 65536 rows of hidden, each reading the weights once.
  */
 glu_status glu_dual_gemv(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, void* stream);
@@ -134,9 +134,9 @@ enum {
     GLU_KERNEL_NONE = 0,    /* M == 0 or N == 0 */
     GLU_KERNEL_ZERO = 1,    /* K == 0: fill out with +0 */
     GLU_KERNEL_VALU = 2,    /* M == 1, K <= 4096, fast path (any M <= 8 on request) */
-    GLU_KERNEL_MFMA = 3,    /* other fast-path shapes up to M = 32 */
+    GLU_KERNEL_MFMA = 3,    /* other fast-path shapes up to M = 64 */
     GLU_KERNEL_GENERIC = 4, /* unaligned, K % 8 != 0 or K > 2^25 */
-    GLU_KERNEL_GEMM = 5,    /* M > 32, fast path: tiled MFMA GEMM, slices of 65536 rows of hidden */
+    GLU_KERNEL_GEMM = 5,    /* M > 64, fast path: tiled MFMA GEMM, slices of 65536 rows of hidden */
     GLU_KERNEL_BACKWARD = 6, /* glu_dual_gemv_backward_plan: the four backward launches */
     GLU_KERNEL_CEILING = 7   /* glu_read_ceiling_plan (glu_gemv_tuning.h): the streaming-read yardstick */
 };

@@ -22,7 +22,7 @@ EPILOGUE_PATHS = {"valu": dict(kernel=api.KERNEL_VALU, gemv_dot=1), "generic": d
                   "mfma8": dict(kernel=api.KERNEL_MFMA, rows_per_wave=8),
                   "gemm": dict(kernel=api.KERNEL_GEMM)}
 
-# tiled GEMM (M > 32 by default): shapes x tile overrides, ragged M, N and K tails
+# tiled GEMM (M > 64 by default): shapes x tile overrides, ragged M, N and K tails
 GEMM_SHAPES = [(33, 200, 520), (64, 1000, 1024), (70, 333, 2560), (128, 300, 1032), (200, 129, 2048),
                (256, 1000, 1024), (1, 5, 8), (17, 64, 64), (300, 77, 136)]
 GEMM_TILES = [dict(), dict(gemm_tile_n=64, gemm_tile_m=64), dict(gemm_tile_n=64, gemm_tile_m=128),

@@ -59,8 +59,10 @@ def test_version_and_strings(lib):
     (1, 12288, 8200, True, api.KERNEL_MFMA, 1),      # past the VALU path's 16 chunks per lane
     (9, 100, 512, True, api.KERNEL_MFMA, 1),
     (32, 17408, 5120, True, api.KERNEL_MFMA, 1),
-    (70, 17408, 5120, True, api.KERNEL_GEMM, 1),     # tiled GEMM above 32 rows
-    (33, 100, 512, True, api.KERNEL_GEMM, 1),
+    (64, 17408, 5120, True, api.KERNEL_MFMA, 1),     # 64 rows in one launch of the 8-row kernel
+    (33, 100, 512, True, api.KERNEL_MFMA, 1),
+    (65, 17408, 5120, True, api.KERNEL_GEMM, 1),     # tiled GEMM above 64 rows
+    (70, 100, 512, True, api.KERNEL_GEMM, 1),
     (100000, 300, 64, True, api.KERNEL_GEMM, 2),     # slices of 65536 rows
     (1, 100, 2560, False, api.KERNEL_GENERIC, 1),    # unaligned
     (1, 100, 1003, True, api.KERNEL_GENERIC, 1),     # K % 8 != 0
@@ -68,6 +70,7 @@ def test_version_and_strings(lib):
     (1, 100, 65536, True, api.KERNEL_MFMA, 1),       # K past the VALU path's 16 chunks per lane
     (4, 100, 9000, True, api.KERNEL_MFMA, 1),
     (32, 4, 1 << 25, True, api.KERNEL_MFMA, 1),       # 32-bit byte offsets cover 32 rows of K
+    (64, 4, 1 << 25, True, api.KERNEL_MFMA, 1),       # 32-bit 16-byte-chunk offsets cover 64
     (32, 4, (1 << 25) + 8, True, api.KERNEL_GENERIC, 4),
 ])
 def test_plan(lib, M, N, K, aligned, kernel, launches):
@@ -93,7 +96,9 @@ def test_describe_names_the_instantiated_kernel(lib):
         "glu::mfma_slice_kernel<4, 4, 2, false>"
     assert api.plan(8, 17408, 5120)["kernel_symbol"] == "glu::mfma_slice_kernel<2, 4, 2, false>"
     assert api.plan(1, 100, 1003)["kernel_symbol"] == "glu::generic_kernel<1>"
-    assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false, 2>"
+    assert api.plan(64, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<8, 4, 3, false>"
+    assert api.plan(40, 17408, 5120)["kernel_symbol"] == "glu::mfma8_pass_kernel<5, 4, 3, false>"
+    assert api.plan(65, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 64, false, 2>"
     assert api.plan(1024, 17408, 5120)["kernel_symbol"] == "glu::gemm_kernel<64, 128, false, 2>"
     assert api.plan(200, 129, 1032)["kernel_symbol"] == "glu::gemm_kernel<64, 64, true, 2>"
     assert lib.glu_dual_gemv_describe(1, 1, 8, 1, None, None, 0) == NULLP
@@ -561,8 +566,9 @@ def test_tuning_xcd_bands_only_for_the_yardstick(lib):
 
 
 def test_mfma8_order_plans(lib):
-    """The 8-row kernel's K-walk order: slice-major only where its kernel is built (8 segments per
-    stage, one stage of weights in flight, more than 8 rows of hidden, at most 3 blocks per workgroup)."""
+    """The 8-row kernel's K-walk order: slice-major only where its kernel is built (one stage of
+    weights in flight, more than 8 rows of hidden, at most 3 blocks per workgroup; stages of 8
+    segments up to 32 rows per launch, of 4 segments for 33 to 64)."""
     def plan_st(M, N, K, **kw):
         p = api.Plan()
         t = api.make_tuning(**kw)
@@ -585,10 +591,25 @@ def test_mfma8_order_plans(lib):
                                                        grid=-(-blocks // jb)))
             assert g["kernel_symbol"].startswith("glu::mfma8_pass_kernel<")
         assert plan_st(M, N, K, rows_per_wave=8, mfma_order=2, mfma_depth=2)[0] == UNSUP
+    # 64 rows per launch with stages of 4 segments; 32 rows or fewer keep stages of 8
+    for M, N, K, sym, launches in ((64, 17408, 5120, "glu::mfma8_pass_kernel<8, 4, 3, false>", 1),
+                                   (33, 100, 512, "glu::mfma8_pass_kernel<5, 4, 3, false>", 1),
+                                   (57, 7, 520, "glu::mfma8_pass_kernel<8, 4, 3, true>", 1),
+                                   (100, 9216, 2560, "glu::mfma8_pass_kernel<8, 4, 3, false>", 2),
+                                   (128, 17408, 5120, "glu::mfma8_pass_kernel<8, 4, 3, false>", 2)):
+        g = api.plan(M, N, K, True, api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2,
+                                                   mfma_segments=4))
+        assert (g["kernel_symbol"], g["launches"], g["m_per_launch"]) == (sym, launches, min(M, 64)), g
+    assert plan_st(32, 17408, 5120, kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2,
+                   mfma_segments=4)[0] == UNSUP
+    assert plan_st(64, 17408, 5120, kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2, mfma_segments=4,
+                   grid=181)[0] == UNSUP
+    assert plan_st(64, 17408, 5120, kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2, mfma_segments=4,
+                   mfma_depth=2)[0] == UNSUP
     assert plan_st(32, 17408, 5120, mfma_order=3)[0] == UNSUP
     assert plan_st(16, 17408, 5120, rows_per_wave=4, mfma_order=2)[0] == UNSUP  # 4-row kernel
     assert plan_st(1, 9216, 2560, mfma_order=1)[0] == UNSUP                    # VALU
-    assert plan_st(64, 9216, 2560, mfma_order=1)[0] == UNSUP                   # GEMM
+    assert plan_st(65, 9216, 2560, mfma_order=1)[0] == UNSUP                   # GEMM
     assert plan_st(0, 9216, 2560, mfma_order=1)[0] == OK                       # nothing to launch
 
 

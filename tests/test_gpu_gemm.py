@@ -1,4 +1,4 @@
-"""GPU parity of the tiled dual GEMM (M > 32) against the oracle, through the C ABI
+"""GPU parity of the tiled dual GEMM (M > 64) against the oracle, through the C ABI
 (needs an MI355X).
 
 The bar is the one of oracle/check.py.  Shapes cover ragged M, N and K tails
@@ -46,8 +46,9 @@ def test_gemm_parity(M, N, K, tile):
 
 
 def test_gemm_default_for_large_m():
-    assert api.plan(33, 1000, 1024)["kernel"] == api.KERNEL_GEMM
-    assert api.plan(32, 1000, 1024)["kernel"] == api.KERNEL_MFMA
+    assert api.plan(65, 1000, 1024)["kernel"] == api.KERNEL_GEMM
+    assert api.plan(64, 1000, 1024)["kernel"] == api.KERNEL_MFMA
+    assert api.plan(33, 1000, 1024)["kernel"] == api.KERNEL_MFMA
 
 
 @pytest.mark.parametrize("M,seed", [(256, 0), (96, 1)])

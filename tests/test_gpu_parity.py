@@ -333,6 +333,46 @@ def test_mfma8_slice_major_order(M, N, K, jb):
     assert check.compare_strict_bits(got, ref) is None
 
 
+PASS64_SHAPES = [(33, 100, 512), (40, 9, 64), (48, 1000, 1032), (57, 7, 520), (64, 3000, 1024),
+                 (64, 2052, 5120), (65, 333, 2560), (100, 9216, 2560)]
+
+
+@pytest.mark.parametrize("M,N,K", PASS64_SHAPES)
+def test_mfma8_slice_major_64_rows(M, N, K):
+    """Up to 64 rows of hidden per launch in the slice-major kernel (stages of 4 segments): within
+    the bar against the oracle, and bitwise equal to the block-by-block order over launches of
+    32 rows (each output's summation order does not depend on the hidden rows beside it)."""
+    h, wg, wu = inputs.hidden(M, K, 7), *inputs.weights(N, K, 7)
+    t_pass = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=2, mfma_segments=4)
+    t_blk = api.make_tuning(kernel=api.KERNEL_MFMA, rows_per_wave=8, mfma_order=1, mfma_segments=4)
+    p = api.plan(M, N, K, True, t_pass)
+    assert p["kernel_symbol"].startswith("glu::mfma8_pass_kernel") and p["m_per_launch"] == min(M, 64), p
+    rep, got, _ = parity(h, wg, wu, tuning=t_pass, label="mfma8 slice-major 64 rows")
+    assert rep.ok, rep.summary()
+    ref = bits(gpu_run(h.to(DEV), wg.to(DEV), wu.to(DEV), t_blk))
+    assert check.compare_strict_bits(got, ref) is None
+
+
+@pytest.mark.parametrize("M,seed", [(64, 0), (48, 1)])
+def test_mfma8_slice_major_64_rows_full_size_sampled(M, seed):
+    """K=5120 N=17408 (1 % outlier weights) at the default plan for 33..64 rows of hidden: the
+    whole output from the GPU, the oracle on a sample of rows (first, last and random)."""
+    h, wg, wu = inputs.case("mfma_k5120_n17408", M=32, seed=seed)
+    K = h.shape[1]
+    hh = inputs.hidden(M, K, 60 + seed)
+    hh[:32] = h
+    plan = api.plan(M, wg.shape[0], K)
+    assert plan["kernel_symbol"].startswith("glu::mfma8_pass_kernel<") and plan["launches"] == 1, plan
+    say(f"[mfma8 64] full size M={M} plan={plan}")
+    got = bits(api.dual_gemv(hh.to(DEV), wg.to(DEV), wu.to(DEV)))
+    torch.cuda.synchronize()
+    rows = sorted({0, 31, 32, M - 1, *np.random.default_rng(seed).integers(0, M, 3).tolist()})
+    ref = oracle.dual_gemv(bits(hh[rows]), bits(wg), bits(wu), with_pre=True)
+    rep = check.compare(got[rows], ref, depth=plan["accum_depth"], k_len=K)
+    say(f"[mfma8 64] rows {rows}: {rep.summary()}")
+    assert rep.ok, rep.summary()
+
+
 def test_mfma8_slice_major_graph_replays():
     """The slice-major kernel at the M=32 K=5120 N=17408 workload, captured in a graph and replayed
     back to back with its inputs changing in place between replays: every replay matches the eager
