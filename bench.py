@@ -271,6 +271,26 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
                             "pool_sets": sets})
                 print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
                 del g
+            # yardstick, not this library's path: the two products alone on the platform's GEMM
+            # library (torch.mm, G and U written in bf16, no epilogue), eager on the same pools
+            gy = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            uy = torch.empty_like(gy)
+
+            def lib_pass():
+                for wg, wu in pool:
+                    torch.mm(h, wg.t(), out=gy)
+                    torch.mm(h, wu.t(), out=uy)
+            r = max(3, reps // max(1, M // 64))
+            warm(torch, lib_pass, WORKLOAD_WARM_SECONDS)
+            us = time_region(torch, lib_pass, r, 1, stream) * 1e3 / (r * sets)
+            flops = 4 * M * N * K
+            res.append({"workload": f"prefill_k{K}_n{N}", "M": M, "K": K, "N": N, "us_per_call": round(us, 3),
+                        "TFLOPs": round(flops / us / 1e6, 2),
+                        "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "kernel": "torch.mm x2 (library GEMM, no epilogue)", "variant": "library_gemm_yardstick",
+                        "pool_sets": sets})
+            print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
+            del gy, uy
         del pool
         torch.cuda.empty_cache()
     # backward: gradients of hidden and both weights (reads Wg, Wu once more, writes dWg, dWu)
@@ -378,7 +398,9 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
                 for i in range(sets)]
         # (M, tuning, label): the planner's default, and above 8 rows the same call with hidden read
         # from L2 per stage instead of staged whole into every workgroup's LDS first
-        cases = [(M, None, "default") for M in (1, 4, 16, 32)]
+        cases = [(M, None, "default") for M in (1, 4, 16, 32, 48, 64)]
+        # 33..64 rows in one launch: stages of 4 segments (64 KiB ring) against the default 8 (128 KiB)
+        cases += [(M, api.make_tuning(mfma_hidden=3, mfma_segments=4), "k_slices_stages_of_4") for M in (48, 64)]
         cases += [(M, api.make_tuning(mfma_hidden=2), "hidden_from_l2") for M in (16, 32)]
         # and with K-slices of hidden streamed under the weights, one, two or three blocks of 4 groups
         # of 8 rows per workgroup

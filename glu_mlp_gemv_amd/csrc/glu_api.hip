@@ -34,6 +34,7 @@ constexpr int kGrouped8MinM = 8;  // grouped MFMA: 8-row groups by default above
 constexpr int64_t kGemmSlice = 65536;        // rows of hidden per GEMM launch
 constexpr int64_t kGemmMaxN = 1 << 30;       // GEMM tile row indices stay in 32 bits
 constexpr int kMfmaSlice = 32;
+constexpr int kGroupedSlices64U = 8;  // the grouped slice kernel's stage (64-element segments) at 33..64 rows
 
 bool mul_overflows(int64_t a, int64_t b, int64_t limit)
 {
@@ -526,18 +527,24 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
         // first (K=2560): a QKV-like triple (31.5 MB) at M = 16 / 32 9.7 / 10.7 us against 11.0 / 15.0,
         // a GDN-input-like quad (63.2 MB) 14.5 / 16.4 against 17.0 / 21.6
         const bool slices_default = mult8 && m_pl > kGrouped8MinM &&
-                                    (!t || (!t->mfma_hidden && !t->mfma_segments && !t->rows_per_wave &&
-                                            !t->waves_per_block && !t->grid));
+                                    (!t || (!t->mfma_hidden && (!t->mfma_segments || t->mfma_segments == 4) &&
+                                            !t->rows_per_wave && !t->waves_per_block && !t->grid));
         if (slices_default || (t && t->mfma_hidden == 3)) {
-            if (!mult8 || (t && ((rows_req && rows_req != 8) || (t->mfma_segments && t->mfma_segments != 8) ||
+            const int seg_req = t ? t->mfma_segments : 0;
+            if (!mult8 || (t && ((rows_req && rows_req != 8) || (seg_req && seg_req != 8 && seg_req != 4) ||
                                  (t->waves_per_block && t->waves_per_block != 4)))) {
                 return GLU_ERR_UNSUPPORTED;
             }
+            // up to 64 rows of hidden per launch (the weights read once where launches of 32 rows
+            // read them twice); stages of 4 segments only above 32 rows
+            const int64_t m_s = M < 2 * kMfmaSlice ? M : 2 * kMfmaSlice;
+            const int useg = seg_req ? seg_req : (m_s > kMfmaSlice ? kGroupedSlices64U : 8);
+            if (useg == 4 && m_s <= kMfmaSlice) return GLU_ERR_UNSUPPORTED;
             const int64_t nsegs8 = ceil_div(nchunks, 8);
             c.rows = 8;
-            c.MT4 = (int)(m_pl <= 8 ? 2 : (m_pl + 7) / 8);
+            c.MT4 = (int)(m_s <= 8 ? 2 : (m_s + 7) / 8);
             c.hidden = glu::kHiddenSlices;
-            c.U = 8;
+            c.U = useg;
             c.nsg = (int)ceil_div(nsegs8, c.U);
             c.ragged = (int64_t)c.nsg * c.U * 8 != nchunks;
             c.block = glu::kMfmaMaxThreads;
@@ -551,8 +558,8 @@ glu_status plan_grouped(int64_t M, int64_t K, int64_t rows, bool fast, bool mult
             if (!glu::grouped_mfma_supported(c)) return GLU_ERR_UNSUPPORTED;
             L->kernel = GLU_KERNEL_MFMA;
             L->mfma = c;
-            L->m_per_launch = (int)m_pl;
-            L->launches = (int)ceil_div(M, m_pl);
+            L->m_per_launch = (int)m_s;
+            L->launches = (int)ceil_div(M, m_s);
             L->accum_depth = (int)(2 * (nsegs8 + 5 + 2));
             return GLU_OK;
         }

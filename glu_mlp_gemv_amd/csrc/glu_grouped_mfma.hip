@@ -435,8 +435,24 @@ GroupedMfmaFn pick8_u(int U)
     }
 }
 
-GroupedMfmaFn pick_slices(int mt8, bool ragged)
+// 5 to 8 tiles of hidden rows (33..64 rows): stages of 4 or 8 segments (a 64 or 128 KiB ring)
+template <int U>
+GroupedMfmaFn pick_slices64(int mt8, bool ragged)
 {
+    switch (mt8) {
+    case 5: return ragged ? grouped_slice_kernel<5, U, kPassBlocks, true> : grouped_slice_kernel<5, U, kPassBlocks, false>;
+    case 6: return ragged ? grouped_slice_kernel<6, U, kPassBlocks, true> : grouped_slice_kernel<6, U, kPassBlocks, false>;
+    case 7: return ragged ? grouped_slice_kernel<7, U, kPassBlocks, true> : grouped_slice_kernel<7, U, kPassBlocks, false>;
+    case 8: return ragged ? grouped_slice_kernel<8, U, kPassBlocks, true> : grouped_slice_kernel<8, U, kPassBlocks, false>;
+    default: return nullptr;
+    }
+}
+
+// 2 to 4 tiles (9..32 rows; 8 or fewer run on 2): stages of 8 segments
+GroupedMfmaFn pick_slices(int mt8, int U, bool ragged)
+{
+    if (mt8 >= 5) return U == 8 ? pick_slices64<8>(mt8, ragged) : (U == 4 ? pick_slices64<4>(mt8, ragged) : nullptr);
+    if (U != 8) return nullptr;
     switch (mt8) {
     case 2: return ragged ? grouped_slice_kernel<2, 8, kPassBlocks, true> : grouped_slice_kernel<2, 8, kPassBlocks, false>;
     case 3: return ragged ? grouped_slice_kernel<3, 8, kPassBlocks, true> : grouped_slice_kernel<3, 8, kPassBlocks, false>;
@@ -444,6 +460,8 @@ GroupedMfmaFn pick_slices(int mt8, bool ragged)
     default: return nullptr;
     }
 }
+
+size_t slices_lds_bytes(int mt8, int U) { return (size_t)2 * 8 * mt8 * U * 8 * 16; }
 
 GroupedMfmaFn pick8(int mt8, int U, bool ragged)
 {
@@ -482,7 +500,10 @@ GroupedMfmaFn pick(int mt4, int U, bool hlds, bool ragged)
 bool grouped_mfma_supported(const MfmaConfig& c)
 {
     if (c.block < kWave || c.block > kMfmaMaxThreads || c.block % kWave != 0) return false;
-    if (c.rows == 8 && c.hidden == kHiddenSlices) return c.block == kMfmaMaxThreads && c.U == 8 && pick_slices(c.MT4, c.ragged);
+    if (c.rows == 8 && c.hidden == kHiddenSlices) {
+        return c.block == kMfmaMaxThreads && pick_slices(c.MT4, c.U, c.ragged) &&
+               slices_lds_bytes(c.MT4, c.U) <= (size_t)kLdsMax;
+    }
     if (c.rows == 8) return c.hidden == kHiddenLds && pick8(c.MT4, c.U, c.ragged) != nullptr;
     if (c.rows != 4 || (c.hidden != kHiddenLds && c.hidden != kHiddenL2)) return false;
     return pick(c.MT4, c.U, c.hidden == kHiddenLds, c.ragged) != nullptr;
@@ -494,13 +515,24 @@ hipError_t grouped_mfma_launch(const MfmaConfig& c, int M, const uint16_t* hidde
     const bool hlds = c.hidden == kHiddenLds;
     GroupedMfmaFn fn;
     if (c.rows == 8 && c.hidden == kHiddenSlices) {
-        // 4 waves in lockstep; every workgroup owns at most kPassBlocks blocks of 4 groups
-        const int mt8 = M <= 8 ? 2 : (M + 7) / 8;
-        fn = c.block == kMfmaMaxThreads && c.U == 8 ? pick_slices(mt8, c.ragged) : nullptr;
+        // 4 waves in lockstep; every workgroup owns at most kPassBlocks blocks of 4 groups.  A last
+        // slice with fewer rows than the kernels are built for runs on their smallest tile count
+        // (padded rows repeat row M - 1 and are never stored)
+        const int mt0 = (M + 7) / 8;
+        const int mt8 = c.U == 4 ? (mt0 < 5 ? 5 : mt0) : (mt0 < 2 ? 2 : mt0);
+        fn = c.block == kMfmaMaxThreads ? pick_slices(mt8, c.U, c.ragged) : nullptr;
         const int64_t blocks = (d.rows / 8 + 3) / 4;
-        if (!fn || M < 1 || d.rows % 8 != 0 || (int64_t)c.grid * kPassBlocks < blocks) return hipErrorInvalidValue;
-        const size_t lds = (size_t)2 * 8 * mt8 * c.U * 8 * 16;
-        if (lds > (size_t)kLdsBudget) return hipErrorInvalidValue;
+        if (!fn || M < 1 || M > 8 * mt8 || d.rows % 8 != 0 || (int64_t)c.grid * kPassBlocks < blocks) {
+            return hipErrorInvalidValue;
+        }
+        const size_t lds = slices_lds_bytes(mt8, c.U);
+        if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
+        if (lds > (size_t)kLdsBudget) {
+            // past 64 KiB of dynamic LDS the launch states its size to the runtime first
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.block), lds, stream, hidden, ldh, M, (int)K, d, c.nsg);
         return hipGetLastError();
     }

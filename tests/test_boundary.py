@@ -688,6 +688,20 @@ def test_grouped_slice_plans():
             api.grouped_plan(32, 2560, 6144, tuning=api.make_tuning(**bad), mult8=True)
     with pytest.raises(api.GluError):  # not every projection a multiple of 8 rows
         api.grouped_plan(32, 2560, 6144, tuning=t, mult8=False)
+    # up to 64 rows of hidden per launch: stages of 8 segments by default, of 4 on request above 32 rows
+    for M, kw, sym, launches in ((64, {}, "glu::grouped_slice_kernel<8, 8, 3, false>", 1),
+                                 (33, {}, "glu::grouped_slice_kernel<5, 8, 3, false>", 1),
+                                 (48, dict(mfma_segments=4), "glu::grouped_slice_kernel<6, 4, 3, false>", 1),
+                                 (100, {}, "glu::grouped_slice_kernel<8, 8, 3, false>", 2),
+                                 (64, dict(mfma_hidden=3), "glu::grouped_slice_kernel<8, 8, 3, false>", 1)):
+        p = api.grouped_plan(M, 2560, 6144, tuning=api.make_tuning(**kw) if kw else None, mult8=True)
+        assert (p["kernel_symbol"], p["launches"], p["m_per_launch"], p["grid"]) == (sym, launches, min(M, 64), 192)
+    assert api.grouped_plan(57, 2176, 1544, mult8=True)["kernel_symbol"] == "glu::grouped_slice_kernel<8, 8, 3, true>"
+    for bad in (dict(mfma_hidden=3, mfma_segments=4), dict(mfma_segments=4), dict(mfma_hidden=3, mfma_segments=2)):
+        with pytest.raises(api.GluError):  # stages of 4 segments only above 32 rows; 4 or 8 only
+            api.grouped_plan(32, 2560, 6144, tuning=api.make_tuning(**bad), mult8=True)
+    with pytest.raises(api.GluError):
+        api.grouped_plan(64, 2560, 6144, tuning=api.make_tuning(mfma_hidden=3, mfma_segments=2), mult8=True)
 
 
 @pytest.mark.parametrize("args,tuning,status", [

@@ -89,7 +89,7 @@ CASES = [
     ((3,), 64, 33, {}),
     # groups of 8 weight rows above 8 rows of hidden held in LDS (every N a multiple of 8)
     ((2048, 1024, 32, 32), 2560, 9, {}),      # two 8-row tiles, the second mostly padding
-    ((1024, 256), 1024, 33 + 8, {}),          # slices of 32 and 9 rows, both in 8-row groups
+    ((1024, 256), 1024, 33 + 8, {}),          # 41 rows in one launch of 6 tiles of 8 rows
     ((8192, 4096, 32, 32), 2560, 32, {}),     # GDN-input-like quad
     ((4096, 1024, 1024), 2560, 17, {}),       # three 8-row tiles, the third mostly padding
     ((2048, 1024, 32, 32), 1024, 24, {}),
@@ -97,7 +97,7 @@ CASES = [
     ((1024, 512, 8), 2176, 20, dict(mfma_segments=5)),
     ((4096, 1024, 1024), 2560, 32, dict(rows_per_wave=4)),  # the 4-row layout on request
     ((1024, 1032), 2560, 32, {}),             # 1032 = 8 x 129 rows
-    ((1024, 256), 1024, 40, {}),              # slices of 32 (8-row groups) and of 8 rows
+    ((1024, 256), 1024, 40, {}),              # 40 rows in one launch: 5 tiles of 8 rows
     ((1024, 512), 2560, 12, dict(rows_per_wave=4)),  # 4-row layout, three tiles, 5 segments per stage
     ((2048, 1024, 32, 32), 2560, 12, dict(mfma_segments=5)),  # 8-row layout, 5 segments per stage
     ((9216, 9216), 2560, 12, {}),             # 2304 groups of 8 rows: three per wave on 192 workgroups
@@ -110,9 +110,19 @@ CASES = [
     ((2048, 1024, 32, 32), 2560, 9, dict(mfma_hidden=3)),           # two tiles, the second mostly padding
     ((1024, 512, 8), 2176, 32, dict(mfma_hidden=3)),                # ragged: 34 segments, stages of 8
     ((1024, 512, 8), 2176, 17, dict(mfma_hidden=3, grid=22)),       # 193 groups: a block of one group
-    ((1024, 256), 1024, 40, dict(mfma_hidden=3)),                   # slices of 32 and 8 rows of hidden
+    ((1024, 256), 1024, 40, dict(mfma_hidden=3)),                   # 40 rows: 5 tiles, one launch
     ((64, 8), 1024, 2, dict(mfma_hidden=3)),                        # nine groups: 3 blocks, 3 waves idle
     ((4096, 1024), 8192, 16, dict(mfma_hidden=3, grid=60)),         # 16 slices, blocks of three and two
+    # up to 64 rows of hidden per launch: stages of 8 segments (a 128 KiB ring) or of 4 (64 KiB)
+    ((4096, 1024, 1024), 2560, 64, {}),                             # QKV-like, 8 tiles
+    ((4096, 1024, 1024), 2560, 64, dict(mfma_hidden=3, mfma_segments=4)),
+    ((8192, 4096, 32, 32), 2560, 48, dict(mfma_hidden=3, grid=193)),  # GDN-like, two blocks each
+    ((1024, 512, 8), 2176, 57, {}),                                 # ragged: 34 segments in stages of 8
+    ((1024, 512, 8), 2176, 33, dict(mfma_hidden=3, mfma_segments=4, grid=22)),  # ragged, stages of 4
+    ((1024, 256), 1024, 100, {}),                                   # launches of 64 and 36 rows
+    ((64, 8), 1024, 64, dict(mfma_hidden=3)),                       # nine groups: 3 blocks, 3 waves idle
+    ((4096, 1024), 8192, 64, dict(mfma_hidden=3, grid=60)),         # 32 slices, blocks of three and two
+    ((4096, 1024), 8192, 40, dict(mfma_segments=4)),
 ]
 
 
@@ -213,15 +223,18 @@ def test_grouped_k_zero_and_determinism():
     assert all(np.array_equal(bits(x), bits(y)) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("Ns,K,M,grid", [((4096, 1024, 1024), 2560, 32, 0), ((8192, 4096, 32, 32), 2560, 24, 129),
-                                         ((1024, 512, 8), 2176, 17, 22), ((2048, 1024, 32, 32), 1024, 9, 0)])
-def test_grouped_slices_bitwise_equal_to_hidden_in_lds(Ns, K, M, grid):
+@pytest.mark.parametrize("Ns,K,M,grid,seg", [((4096, 1024, 1024), 2560, 32, 0, 0), ((8192, 4096, 32, 32), 2560, 24, 129, 0),
+                                             ((1024, 512, 8), 2176, 17, 22, 0), ((2048, 1024, 32, 32), 1024, 9, 0, 0),
+                                             ((4096, 1024, 1024), 2560, 64, 0, 0), ((4096, 1024, 1024), 2560, 64, 0, 4),
+                                             ((1024, 512, 8), 2176, 57, 22, 0), ((1024, 512, 8), 2176, 41, 0, 4)])
+def test_grouped_slices_bitwise_equal_to_hidden_in_lds(Ns, K, M, grid, seg):
     """The K-slice walk adds every output's products in the order of the 8-row kernel with hidden
-    whole in LDS: the two agree bit for bit."""
-    print(f"grouped slices Ns={Ns} K={K} M={M} grid={grid}", flush=True)
+    whole in LDS (launches of at most 32 rows): the two agree bit for bit, also with 64 rows of
+    hidden per launch of the slice walk."""
+    print(f"grouped slices Ns={Ns} K={K} M={M} grid={grid} segments={seg}", flush=True)
     h = inputs.hidden(M, K, 33).to(DEV)
     ws = [w.to(DEV) for w in weight_set(Ns, K, 33)]
-    a = api.grouped_gemv(h, ws, tuning=api.make_tuning(mfma_hidden=3, grid=grid))
+    a = api.grouped_gemv(h, ws, tuning=api.make_tuning(mfma_hidden=3, grid=grid, mfma_segments=seg))
     b = api.grouped_gemv(h, ws, tuning=api.make_tuning(rows_per_wave=8, mfma_hidden=1))
     torch.cuda.synchronize()
     for x, y in zip(a, b):
