@@ -70,7 +70,8 @@ struct BwdPlan {
     int dh_splits, dh_jr;    // ranges of weight rows (jr rows each, a multiple of 32) = dh's partials
     int dh_mslices;          // slices of mp16 rows of hidden dh's grid covers (1 up to 64 rows)
     int dh_steps;            // 32-row steps of the longest range
-    bool gu_gemm;            // g and u from the tiled GEMM (M > 32, N % 4 == 0) instead of the grouped GEMV
+    bool gu_gemm;            // g and u from the tiled GEMM (N % 4 == 0 and M > 64, or M > 32 with N % 8 != 0)
+                             // instead of the grouped GEMV
     int64_t off_g2, off_gT, off_hT, off_partial;  // workspace offsets of dg2/du2, dgT/duT, hT, the partials
     int nslabs;              // 512-column slabs of K
     int nranges;             // row ranges of N (the one-pass kernel: its workgroups)

@@ -816,7 +816,9 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.dh_jr = (int)(steps * 32);
         p.dh_splits = (int)((N + p.dh_jr - 1) / p.dh_jr);
         p.dh_steps = (int)steps;
-        p.gu_gemm = M > 32 && N % 4 == 0;
+        // g and u: the grouped GEMV's K-slice kernel takes up to 64 rows of hidden in one launch when
+        // N % 8 == 0; the tiled GEMM above that (and above 32 rows when only N % 4 == 0)
+        p.gu_gemm = N % 4 == 0 && (M > 64 || (M > 32 && N % 8 != 0));
         p.nranges = p.dh_splits;
         p.off_g2 = p.gu_bytes;
         p.off_gT = p.off_g2 + pad256((int64_t)2 * p.mp16 * p.dh_mslices * p.np32 * 2);
@@ -846,8 +848,10 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         // the fp32 unit roundoff as the forward's MFMA kernels are: dh over a range's steps, then
         // the reduction; dW over one or two blocks of the M rows
         p.accum_depth = std::max(2 * (p.dh_steps + 5) + reduce_depth, 2 * (p.mp32 / 32 + 5));
-        // g and u from the GEMM: one MFMA per 32-element block of K, plus the tile's fixed steps
-        if (p.gu_gemm) p.accum_depth = std::max(p.accum_depth, (int)(2 * ((K + 31) / 32 + 6)));
+        // g and u from the GEMM: one MFMA per 32-element block of K, plus the tile's fixed steps; from
+        // the grouped GEMV: one MFMA per 64-element segment (at most), the pair sum and the tree
+        p.accum_depth = std::max(p.accum_depth, p.gu_gemm ? (int)(2 * ((K + 31) / 32 + 6))
+                                                          : (int)(2 * ((K + 63) / 64 + 7)));
     } else if (p.path == kPathGemm) {
         // dh as above; the weight gradients from the GEMM over the mp32 padded rows of hidden
         p.accum_depth = std::max(2 * (p.dh_steps + 5) + reduce_depth, 2 * (p.mp32 / 32 + 6));

@@ -97,6 +97,9 @@ CASES = [(1, 9216, 2560), (1, 300, 1032), (2, 1000, 512), (3, 257, 8), (4, 65, 2
          # ragged row ranges and column tiles, partial 16-row tiles of hidden)
          (9, 700, 1032), (16, 2048, 2560), (33, 300, 520), (64, 1000, 1024), (64, 5, 8), (17, 1000, 2568),
          (40, 333, 520), (48, 4097, 72), (12, 31, 4096), (64, 9216, 2560),
+         # 33..64 rows: g and u from one launch of the grouped GEMV's K-slice kernel (N % 8 == 0), ragged
+         # stages; with only N % 4 == 0 from the tiled GEMM
+         (56, 1024, 2176), (33, 2048, 2560), (36, 1004, 1032),
          # more than 64 rows: g and u from the tiled GEMM (N % 4 == 0; else the grouped GEMV in slices),
          # dh over slices of 64 rows of hidden, the weight gradients as one transposed GEMM (a ragged
          # last 32-row block of the contraction, transposes over several 64-row tiles)
