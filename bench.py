@@ -272,7 +272,8 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
                 print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
                 del g
             # yardstick, not this library's path: the two products alone on the platform's GEMM
-            # library (torch.mm, G and U written in bf16, no epilogue), eager on the same pools
+            # library (torch.mm, G and U written in bf16, no epilogue) on the same pools, replayed
+            # from a graph like the rows above (eager if the library refuses the capture)
             gy = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
             uy = torch.empty_like(gy)
 
@@ -280,17 +281,22 @@ def bench_workloads(torch, api, inputs, dev, reps=30, only=None):
                 for wg, wu in pool:
                     torch.mm(h, wg.t(), out=gy)
                     torch.mm(h, wu.t(), out=uy)
+            try:
+                lib_run, launch = capture(torch, lib_pass).replay, "graph"
+            except RuntimeError:
+                torch.cuda.synchronize()
+                lib_run, launch = lib_pass, "eager"
             r = max(3, reps // max(1, M // 64))
-            warm(torch, lib_pass, WORKLOAD_WARM_SECONDS)
-            us = time_region(torch, lib_pass, r, 1, stream) * 1e3 / (r * sets)
+            warm(torch, lib_run, WORKLOAD_WARM_SECONDS)
+            us = time_region(torch, lib_run, r, 1, stream) * 1e3 / (r * sets)
             flops = 4 * M * N * K
             res.append({"workload": f"prefill_k{K}_n{N}", "M": M, "K": K, "N": N, "us_per_call": round(us, 3),
                         "TFLOPs": round(flops / us / 1e6, 2),
                         "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                         "kernel": "torch.mm x2 (library GEMM, no epilogue)", "variant": "library_gemm_yardstick",
-                        "pool_sets": sets})
+                        "launch": launch, "pool_sets": sets})
             print(f"[workloads] {res[-1]}", file=sys.stderr, flush=True)
-            del gy, uy
+            del gy, uy, lib_run
         del pool
         torch.cuda.empty_cache()
     # backward: gradients of hidden and both weights (reads Wg, Wu once more, writes dWg, dWu)
