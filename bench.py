@@ -731,7 +731,8 @@ def summarize_trace_grid(d: str):
         name = r["Kernel_Name"]
         if not name.startswith(("glu::", "void glu::")):
             continue
-        key = (name.split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]), int(r["LDS_Block_Size"]))
+        key = (name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]),
+               int(r["LDS_Block_Size"]))
         groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines = ["| kernel | grid (threads) | LDS bytes | dispatches | average ns | median ns | min ns |",
              "|---|---|---|---|---|---|---|"]
