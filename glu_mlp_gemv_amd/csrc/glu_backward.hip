@@ -834,8 +834,11 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     if (M >= kBwdMfmaMinM && M <= kBwdMaxM && N > 0 && K >= 8) {
         const bool big = M > kBwdMfmaMaxM;
         p.path = big ? kPathGemm : kPathMfma;
-        p.mp16 = M <= 16 ? 16 : (M <= 32 ? 32 : 64);  // 1, 2 or 4 tiles of 16 rows: 4 waves split evenly
-        p.dh_mslices = big ? (int)((M + 63) / 64) : 1;  // above 64 rows: slices of 64
+        // dh's B operand: 1, 2 or 4 tiles of 16 rows (4 waves split evenly), above 64 rows slices of
+        // 8 tiles (two per wave: each weight tile read from beyond L2 half as often as with slices of
+        // 64)
+        p.mp16 = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
+        p.dh_mslices = big ? (int)((M + 127) / 128) : 1;
         p.mp32 = (int)((M + 31) / 32 * 32);
         p.np32 = (int)((N + 31) / 32 * 32);
         // about 512 workgroups of 64 columns x one range of rows (x one slice of hidden), ranges a
@@ -843,7 +846,9 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         const int64_t ktiles = (K + 63) / 64;
         const int64_t steps_all = p.np32 / 32;
         const int64_t per_split = ktiles * p.dh_mslices;
-        int64_t splits = (kBwdTargetBlocks + per_split - 1) / per_split;
+        // (above 64 rows at most that many: the 128-row kernel fits two workgroups per CU, and a second
+        // round for a few would cost a whole step loop)
+        int64_t splits = big ? kBwdTargetBlocks / per_split : (kBwdTargetBlocks + per_split - 1) / per_split;
         splits = splits < 1 ? 1 : (splits > steps_all ? steps_all : splits);
         const int64_t steps = (steps_all + splits - 1) / splits;
         p.dh_jr = (int)(steps * 32);

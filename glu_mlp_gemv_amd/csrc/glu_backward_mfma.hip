@@ -1,8 +1,8 @@
 // Backward of the dual-weight GLU projection above 8 rows of hidden: the three
 // contractions as v_mfma_f32_16x16x32_bf16 products.  Up to 64 rows as below;
-// above, dh_mfma_kernel runs over slices of 64 rows of hidden and the weight
-// gradients are one tiled GEMM (gemm_dw_launch, glu_gemm.hip) on the same
-// transposed copies.
+// above, dh_mfma_kernel runs over slices of 128 rows of hidden (two 16-row
+// tiles per wave) and the weight gradients are one tiled GEMM (gemm_dw_launch,
+// glu_gemm.hip) on the same transposed copies.
 //
 // After the grouped GEMV and the elementwise step have left dg and du
 // ([2][M][N] bf16) at the workspace head, repack_kernel writes zero-padded
@@ -30,7 +30,8 @@
 //  3. after one barrier each wave reads its A operands (16 k x 32 j each)
 //     from there and its B operands (dg2, du2: 16 rows m x 32 j) from the
 //     workspace. A wave owns one 16-row tile of hidden and 4 / (tiles)
-//     column subtiles, so no two waves load the same B operand.
+//     column subtiles (above 64 rows two tiles and all 4 subtiles), so no
+//     two waves load the same B operand.
 // The weights are read once. dh_reduce_kernel then adds the splits' partials
 // in a fixed order and applies dh's roundings.
 // No atomics anywhere: the results are bitwise reproducible.
@@ -231,10 +232,10 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
     }
 }
 
-// MT = Mp16 / 16 (1, 2 or 4).  Workgroup b: columns [64 (t % ktiles), +64), rows j of split
+// MT = Mp16 / 16 (1, 2, 4 or 8).  Workgroup b: columns [64 (t % ktiles), +64), rows j of split
 // t / ktiles: [split * jr, min(N, (split + 1) * jr)), jr a multiple of 32, where t = b with one
-// slice of rows of hidden.  Above 64 rows (mslices > 1, MT = 4) t = b' / mslices and the workgroup
-// takes rows 64 (b' % mslices) .. + 63 of hidden, b' being b renumbered so that the workgroups one
+// slice of rows of hidden.  Above 64 rows (mslices >= 1, MT = 8) t = b' / mslices and the workgroup
+// takes rows 128 (b' % mslices) .. + 127 of hidden, b' being b renumbered so that the workgroups one
 // XCD receives (the hardware deals them to the 8 XCDs in turn) are consecutive: the slices of one
 // (column tile, split) then run on one XCD and read its weight tile from that XCD's L2 after the
 // first.  g2, u2: dg2, du2 ([mslices * Mp16][np] with np a multiple of 32).  partial:
@@ -263,24 +264,31 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     const int je = min(jb + jr, N);
     const int nsteps = (je - jb + kDhStep - 1) / kDhStep;  // >= 1: the plan leaves no split empty
     const int i16 = lane & 15, q = lane >> 4;
-    // the 4 x MT (column subtile, row tile) pairs: wave w takes row tile w % MT of hidden and the
-    // MT column subtiles from (w / MT) MT on, so that no two waves load the same B operand
-    const int mt = wave % MT;
-    const int ks0 = (wave / MT) * MT;
+    // the 4 x MT (column subtile, row tile) pairs: up to MT = 4 wave w takes row tile w % MT of hidden
+    // and the MT column subtiles from (w / MT) MT on; at MT = 8 it takes row tiles w and w + 4 and all
+    // 4 column subtiles.  No two waves load the same B operand.
+    constexpr int RT = MT > 4 ? MT / 4 : 1;  // row tiles per wave
+    constexpr int KT = MT > 4 ? 4 : MT;      // column subtiles per wave
+    const int mt = MT > 4 ? wave : wave % MT;  // the wave's first row tile; the others 4 apart
+    const int ks0 = MT > 4 ? 0 : (wave / MT) * MT;
 
     // this thread's weight chunk: row r_ld of the step, columns k0 + 8 c_ld .. + 7
     const int r_ld = tid >> 3, c_ld = tid & 7;
     const bool col_ok = k0 + 8 * c_ld < K;
     const int kc = col_ok ? k0 + 8 * c_ld : K - 8;  // in bounds; such columns are stored as zeros
 
-    auto load = [&](int s, u32x4_t (&w)[2], u32x4_t (&b)[2]) __attribute__((always_inline)) {
+    auto load = [&](int s, u32x4_t (&w)[2], u32x4_t (&b)[RT][2]) __attribute__((always_inline)) {
         const int64_t j = min(jb + kDhStep * s + r_ld, N - 1);  // rows past the range: stored as zeros
         w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gate_w + j * K + kc));
         w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up_w + j * K + kc));
-        // B: rows m = 16 mt + l%16 of dg2 and du2, columns jb + 32 s + 8 (l/16) .. + 7 (zero past N)
-        const int64_t off = (int64_t)(mbase + 16 * mt + i16) * np + jb + kDhStep * s + 8 * q;
-        b[0] = *reinterpret_cast<const u32x4_t*>(g2 + off);
-        b[1] = *reinterpret_cast<const u32x4_t*>(u2 + off);
+        // B: rows m = 16 (mt + 4 r) + l%16 of dg2 and du2, columns jb + 32 s + 8 (l/16) .. + 7 (zero
+        // past N)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int64_t off = (int64_t)(mbase + 16 * (mt + 4 * r) + i16) * np + jb + kDhStep * s + 8 * q;
+            b[r][0] = *reinterpret_cast<const u32x4_t*>(g2 + off);
+            b[r][1] = *reinterpret_cast<const u32x4_t*>(u2 + off);
+        }
     };
     // Transposed publication.  Rows r and r ^ 1 of a chunk column sit in lanes l and l ^ 8, which
     // trade half their chunk through one DPP row rotation by 8: the even row's thread then holds
@@ -314,27 +322,31 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
         }
     };
 
-    f32x4_t acc[2][MT];
+    f32x4_t acc[2][RT][KT];
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mat][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int r = 0; r < RT; ++r) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t) acc[mat][r][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
     }
-    auto compute = [&](int buf, const u32x4_t (&b)[2]) __attribute__((always_inline)) {
+    auto compute = [&](int buf, const u32x4_t (&b)[RT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
+            for (int t = 0; t < KT; ++t) {
                 const int ks = ks0 + t;  // column subtile: k >> 4 == ks, the read's swizzle
                 const u32x4_t a =
                     *reinterpret_cast<const u32x4_t*>(&tw[buf][mat][(16 * ks + i16) * kDhTS + 8 * (q ^ ks)]);
-                acc[mat][t] = mfma16(a, b[mat], acc[mat][t]);
+#pragma unroll
+                for (int r = 0; r < RT; ++r) acc[mat][r][t] = mfma16(a, b[r][mat], acc[mat][r][t]);
             }
         }
     };
 
     u32x4_t W[D][2];
-    u32x4_t B[D][2];
+    u32x4_t B[D][RT][2];
 #pragma unroll
     for (int s = 0; s < D; ++s) {
         if (s < nsteps) load(s, W[s], B[s]);
@@ -356,15 +368,20 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     for (; s0 + 2 * D <= nsteps; s0 += D) run_stages<0, D>(steady, s0, nsteps);
     for (; s0 < nsteps; s0 += D) run_stages<0, D>(tail, s0, nsteps);
 
-    // lane l holds D[4(l/16) + e][l%16]: columns k = k0 + 16 ks + 4(l/16) + e of row m = 16 mt + l%16
-    const int m = mbase + 16 * mt + i16;
+    // lane l holds D[4(l/16) + e][l%16]: columns k = k0 + 16 ks + 4(l/16) + e of row
+    // m = 16 (mt + 4 r) + l%16
 #pragma unroll
-    for (int mat = 0; mat < 2; ++mat) {
+    for (int r = 0; r < RT; ++r) {
+        const int m = mbase + 16 * (mt + 4 * r) + i16;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int k = k0 + 16 * (ks0 + t) + 4 * q;
-            if (m < M && k < K) {
-                *reinterpret_cast<f32x4_t*>(partial + (((int64_t)split * 2 + mat) * M + m) * K + k) = acc[mat][t];
+        for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                const int k = k0 + 16 * (ks0 + t) + 4 * q;
+                if (m < M && k < K) {
+                    *reinterpret_cast<f32x4_t*>(partial + (((int64_t)split * 2 + mat) * M + m) * K + k) =
+                        acc[mat][r][t];
+                }
             }
         }
     }
@@ -420,12 +437,15 @@ hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const
 {
     using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, float*, int, int, int,
                         int, int, int, int);
-    static const Fn table[4] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>};
+    static const Fn table[8] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>,
+                                nullptr,           nullptr,           nullptr, dh_mfma_kernel<8>};
     const int mt = p.mp16 / 16;
     const int ktiles = (K + kDhK - 1) / kDhK;
     const int ms = p.dh_mslices;
-    if ((p.path != kPathMfma && p.path != kPathGemm) || mt < 1 || mt > 4 || !table[mt - 1] || ms < 1 ||
-        (ms > 1 && mt != 4) || M < 1 || M > (int64_t)ms * p.mp16 || N < 1 || K < 8 || (K & 7) != 0 ||
+    // slices of 128 rows (MT = 8) above 64 rows of hidden, one slice of up to 64 rows below
+    if ((p.path != kPathMfma && p.path != kPathGemm) || mt < 1 || mt > 8 || !table[mt - 1] || ms < 1 ||
+        (p.path == kPathGemm) != (mt == 8) || (ms > 1 && mt != 8) || M < 1 || M > (int64_t)ms * p.mp16 ||
+        N < 1 || K < 8 || (K & 7) != 0 ||
         p.dh_jr < kDhStep || p.dh_jr % kDhStep != 0 || p.np32 < N || p.np32 % kDhStep != 0 || p.dh_splits < 1 ||
         (int64_t)(p.dh_splits - 1) * p.dh_jr >= N || (int64_t)p.dh_splits * p.dh_jr < N ||
         p.dh_splits != p.nranges) {
