@@ -176,7 +176,9 @@ typedef struct glu_projection {
  * Kernels ("fast layout": hidden and every weight 16-byte aligned, K, ldh and
  * every ldw multiples of 8, strides at most 2^25): for M >= 2 with a fast
  * layout and every N a multiple of 4, a block-diagonal MFMA GEMV, M <= 32
- * rows of hidden per launch; else, with a fast layout and K <= 8192, a VALU
+ * rows of hidden per launch (M <= 64 above 8 rows when every N is a multiple
+ * of 8: K-slices of hidden streamed under the weights); else, with a fast
+ * layout and K <= 8192, a VALU
  * GEMV, M <= 8 rows per launch (both stream the n weights as one row space;
  * larger M runs in slices, each streaming the weights again); any other
  * layout takes a generic kernel with 2-byte loads and the same result
@@ -229,10 +231,11 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * K <= 2560, for M = 1 with K <= 8192, and for M <= 4 with 2560 < K <= 4096
  * (K <= 8192 when M <= 3), two launches, a pass that reads each
  * weight row once and the reduction of dhidden's partial sums; otherwise
- * the grouped GEMV for g and u (above M = 32 with N % 4 == 0 a tiled GEMM),
- * then the gradient kernels (above M = 8 on the matrix cores; above M = 64
- * dhidden over slices of 64 rows of hidden and the weight gradients as one
- * tiled GEMM contracting over the rows of hidden).
+ * the grouped GEMV for g and u (one launch up to M = 64 when N % 8 == 0;
+ * above M = 64, or above 32 when only N % 4 == 0, a tiled GEMM), then the
+ * gradient kernels (above M = 8 on the matrix cores; above M = 64 dhidden
+ * over slices of 128 rows of hidden and the weight gradients as one tiled
+ * GEMM contracting over the rows of hidden).
  */
 glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                                   const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
@@ -248,7 +251,7 @@ glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w
  * Same arguments, results and validation as glu_dual_gemv_backward without the
  * workspace; a shape whose glu_dual_gemv_backward_workspace exceeds 48 MiB
  * returns GLU_ERR_SCRATCH_LIMIT before any HIP call (e.g. K=2560 N=9216 is
- * served up to M = 253, K=4096 N=12288 up to M = 217).  The first
+ * served up to M = 197, K=4096 N=12288 up to M = 158).  The first
  * call on a device looks the array up (hipGetSymbolAddress).  All calls on one
  * GPU share its array and leave the last call's contents there (on return it
  * begins with dg and du, as the workspace does): calls that overlap on one GPU
