@@ -1103,7 +1103,8 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     plan->grid = run_all ? (bp.path == glu::kPathFused1   ? bp.fused_grid
                             : bp.path == glu::kPathSplitK ? bp.split_grid
                             : bp.path == glu::kPathMfma || bp.path == glu::kPathGemm
-                                ? (int)((K + 63) / 64) * bp.dh_splits * bp.dh_mslices
+                                ? (int)((K + glu::dh_cols(bp.mp16 / 16) - 1) / glu::dh_cols(bp.mp16 / 16)) *
+                                      bp.dh_splits * bp.dh_mslices
                                                           : bp.nranges * bp.nslabs)
                          : 0;
     plan->block = bp.path == glu::kPathSplitK ? bp.split_waves * glu::kWave : 256;

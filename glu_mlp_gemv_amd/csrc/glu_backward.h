@@ -56,6 +56,8 @@ constexpr int kPathGemm = 4;     // M > 64: tiled GEMM for g and u, gradient ste
                                  // dh_mfma_kernel over slices of 64 rows of hidden, reduction, and the
                                  // weight gradients as one transposed tiled GEMM (gemm_dw_launch)
 constexpr int kBwdMfmaMinM = 9;  // rows of hidden from which the contractions run on MFMA
+// columns of dh per dh_mfma_kernel workgroup for mt 16-row tiles of hidden per slice
+constexpr int dh_cols(int mt) { return mt <= 4 ? 128 : 64; }
 
 struct BwdPlan {
     int path;                // kPathChunks, kPathFused1, kPathSplitK, kPathMfma or kPathGemm

@@ -841,9 +841,9 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         p.dh_mslices = big ? (int)((M + 127) / 128) : 1;
         p.mp32 = (int)((M + 31) / 32 * 32);
         p.np32 = (int)((N + 31) / 32 * 32);
-        // about 512 workgroups of 64 columns x one range of rows (x one slice of hidden), ranges a
+        // about 512 workgroups of dh_cols columns x one range of rows (x one slice of hidden), ranges a
         // multiple of 32 rows
-        const int64_t ktiles = (K + 63) / 64;
+        const int64_t ktiles = (K + dh_cols(p.mp16 / 16) - 1) / dh_cols(p.mp16 / 16);
         const int64_t steps_all = p.np32 / 32;
         const int64_t per_split = ktiles * p.dh_mslices;
         // (above 64 rows at most that many: the 128-row kernel fits two workgroups per CU, and a second

@@ -21,15 +21,15 @@
 //
 // dh_mfma_kernel: partial[split][mat][m][k] = sum over the split's rows j of
 // dG[m][j] W[j][k], as D[k][m] with the contraction over j, 32 rows per MFMA.
-// A workgroup of 4 waves owns 64 columns k (16 per wave) and one range of
-// rows j. Per 32-row step:
-//  1. every thread loads one 16-byte chunk of Wg and of Wu (8 columns of one
-//     row), issued D steps ahead;
-//  2. writes it transposed into LDS (rows past the range as zeros), pairing
+// A workgroup of 4 waves owns 128 columns k (64 above 64 rows of hidden) and
+// one range of rows j. Per 32-row step:
+//  1. every thread loads two 16-byte chunks (one above 64 rows) of Wg and of
+//     Wu (8 columns of one row each, 64 columns apart), issued D steps ahead;
+//  2. writes them transposed into LDS (rows past the range as zeros), pairing
 //     two rows per 32-bit write through a DPP exchange;
 //  3. after one barrier each wave reads its A operands (16 k x 32 j each)
 //     from there and its B operands (dg2, du2: 16 rows m x 32 j) from the
-//     workspace. A wave owns one 16-row tile of hidden and 4 / (tiles)
+//     workspace. A wave owns one 16-row tile of hidden and 8 / (tiles)
 //     column subtiles (above 64 rows two tiles and all 4 subtiles), so no
 //     two waves load the same B operand.
 // The weights are read once. dh_reduce_kernel then adds the splits' partials
@@ -52,7 +52,6 @@ constexpr int kDwTile = 64;           // k and j extent of a wave's dW tile
 // 4096 resident waves at one tile per wave); at M = 64 (KS = 2) three per wave took 133.9 against
 // 131.6
 constexpr int kDwTilesPerWave = 3;
-constexpr int kDhK = 64;              // columns k per dh workgroup (16 per wave)
 constexpr int kDhStep = 32;           // weight rows per dh step (one MFMA contraction)
 constexpr int kDhTS = 40;             // elements per LDS row of the transposed tile (32 rows j + 8 of padding,
                                       // 80 bytes: 16-byte aligned A reads, spread over the banks)
@@ -240,6 +239,9 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
 // (column tile, split) then run on one XCD and read its weight tile from that XCD's L2 after the
 // first.  g2, u2: dg2, du2 ([mslices * Mp16][np] with np a multiple of 32).  partial:
 // [splits][2][M][K] fp32.
+// KK = dh_cols(MT) columns k per workgroup: 128 up to MT = 4 (8 column subtiles; each thread loads two
+// 16-byte chunks of its weight row per step, so a workgroup reads 256 contiguous bytes of each row),
+// 64 at MT = 8.
 template <int MT>
 __global__ void __launch_bounds__(kMfmaBwdThreads)
 dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__ up_w,
@@ -247,7 +249,10 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
                int N, int K, int np, int ktiles, int jr, int mslices)
 {
     constexpr int D = kDhDepth;
-    __shared__ __align__(16) uint16_t tw[2][2][kDhK * kDhTS];  // [buffer][matrix][k][j]
+    constexpr int KK = dh_cols(MT);
+    constexpr int NKS = KK / 16;  // column subtiles of 16
+    constexpr int HALVES = KK / 64;
+    __shared__ __align__(16) uint16_t tw[2][2][KK * kDhTS];  // [buffer][matrix][k][j]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -258,29 +263,37 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     }
     const int mbase = 16 * MT * (bt % mslices);
     bt /= mslices;
-    const int k0 = (bt % ktiles) * kDhK;
+    const int k0 = (bt % ktiles) * KK;
     const int split = bt / ktiles;
     const int jb = split * jr;
     const int je = min(jb + jr, N);
     const int nsteps = (je - jb + kDhStep - 1) / kDhStep;  // >= 1: the plan leaves no split empty
     const int i16 = lane & 15, q = lane >> 4;
-    // the 4 x MT (column subtile, row tile) pairs: up to MT = 4 wave w takes row tile w % MT of hidden
-    // and the MT column subtiles from (w / MT) MT on; at MT = 8 it takes row tiles w and w + 4 and all
-    // 4 column subtiles.  No two waves load the same B operand.
-    constexpr int RT = MT > 4 ? MT / 4 : 1;  // row tiles per wave
-    constexpr int KT = MT > 4 ? 4 : MT;      // column subtiles per wave
+    // the NKS x MT (column subtile, row tile) pairs: up to MT = 4 wave w takes row tile w % MT of hidden
+    // and the KT column subtiles from (w / MT) KT on; at MT = 8 it takes row tiles w and w + 4 and all
+    // column subtiles.  No two waves load the same B operand.
+    constexpr int RT = MT > 4 ? MT / 4 : 1;             // row tiles per wave
+    constexpr int KT = MT > 4 ? NKS : MT * NKS / 4;     // column subtiles per wave
     const int mt = MT > 4 ? wave : wave % MT;  // the wave's first row tile; the others 4 apart
-    const int ks0 = MT > 4 ? 0 : (wave / MT) * MT;
+    const int ks0 = MT > 4 ? 0 : (wave / MT) * KT;
 
-    // this thread's weight chunk: row r_ld of the step, columns k0 + 8 c_ld .. + 7
+    // this thread's weight chunks: row r_ld of the step, columns k0 + 64 h + 8 c_ld .. + 7 (h < HALVES)
     const int r_ld = tid >> 3, c_ld = tid & 7;
-    const bool col_ok = k0 + 8 * c_ld < K;
-    const int kc = col_ok ? k0 + 8 * c_ld : K - 8;  // in bounds; such columns are stored as zeros
+    bool col_ok[HALVES];
+    int kc[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+        col_ok[h] = k0 + 64 * h + 8 * c_ld < K;
+        kc[h] = col_ok[h] ? k0 + 64 * h + 8 * c_ld : K - 8;  // in bounds; such columns are stored as zeros
+    }
 
-    auto load = [&](int s, u32x4_t (&w)[2], u32x4_t (&b)[RT][2]) __attribute__((always_inline)) {
+    auto load = [&](int s, u32x4_t (&w)[HALVES][2], u32x4_t (&b)[RT][2]) __attribute__((always_inline)) {
         const int64_t j = min(jb + kDhStep * s + r_ld, N - 1);  // rows past the range: stored as zeros
-        w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gate_w + j * K + kc));
-        w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up_w + j * K + kc));
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+            w[h][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gate_w + j * K + kc[h]));
+            w[h][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up_w + j * K + kc[h]));
+        }
         // B: rows m = 16 (mt + 4 r) + l%16 of dg2 and du2, columns jb + 32 s + 8 (l/16) .. + 7 (zero
         // past N)
 #pragma unroll
@@ -293,18 +306,20 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     // Transposed publication.  Rows r and r ^ 1 of a chunk column sit in lanes l and l ^ 8, which
     // trade half their chunk through one DPP row rotation by 8: the even row's thread then holds
     // columns 8c .. 8c+3 and the odd row's 8c+4 .. 8c+7 of both rows, and writes them as four
-    // 32-bit (row, row + 1) pairs.  Element (k, j) sits at T[k][8 ((j >> 3) ^ (k >> 4)) + (j & 7)]:
-    // the 64 lanes of one write then hit 64 different banks, and a wave's A read (k >> 4 == wave)
-    // still takes 16 contiguous bytes per lane.
+    // 32-bit (row, row + 1) pairs.  Element (k, j) sits at T[k][8 ((j >> 3) ^ ((k >> 4) & 3)) + (j & 7)]:
+    // the 64 lanes of one write then hit 64 different banks (the second 64 columns repeat the first
+    // ones' pattern, KK * kDhTS / 2 words further on: a multiple of the 64 banks), and an A read of
+    // column subtile ks still takes 16 contiguous bytes per lane.
     const bool odd = (r_ld & 1) != 0;
-    auto publish = [&](int buf, int s, const u32x4_t (&w)[2]) __attribute__((always_inline)) {
-        const bool ok = col_ok && jb + kDhStep * s + r_ld < je;
-        const int kb = 8 * c_ld + (odd ? 4 : 0);
+    auto publish = [&](int buf, int s, const u32x4_t (&w)[HALVES][2]) __attribute__((always_inline)) {
+        const bool row_ok = jb + kDhStep * s + r_ld < je;
         const int jo = r_ld & 6;  // the pair's first row within its block of 8
 #pragma unroll
-        for (int mat = 0; mat < 2; ++mat) {
+        for (int hm = 0; hm < 2 * HALVES; ++hm) {
+            const int h = hm >> 1, mat = hm & 1;
+            const int kb = 64 * h + 8 * c_ld + (odd ? 4 : 0);
             const u32x4_t z = {0u, 0u, 0u, 0u};
-            const u32x4_t v = ok ? w[mat] : z;
+            const u32x4_t v = (row_ok && col_ok[h]) ? w[h][mat] : z;
             const uint32_t s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
             const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0x128, 0xF, 0xF, false);
             const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0x128, 0xF, 0xF, false);
@@ -317,7 +332,7 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int k = kb + e;
-                t[(k * kDhTS + 8 * (wave ^ (k >> 4)) + jo) >> 1] = pr[e];
+                t[(k * kDhTS + 8 * (wave ^ ((k >> 4) & 3)) + jo) >> 1] = pr[e];
             }
         }
     };
@@ -338,14 +353,14 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
             for (int t = 0; t < KT; ++t) {
                 const int ks = ks0 + t;  // column subtile: k >> 4 == ks, the read's swizzle
                 const u32x4_t a =
-                    *reinterpret_cast<const u32x4_t*>(&tw[buf][mat][(16 * ks + i16) * kDhTS + 8 * (q ^ ks)]);
+                    *reinterpret_cast<const u32x4_t*>(&tw[buf][mat][(16 * ks + i16) * kDhTS + 8 * (q ^ (ks & 3))]);
 #pragma unroll
                 for (int r = 0; r < RT; ++r) acc[mat][r][t] = mfma16(a, b[r][mat], acc[mat][r][t]);
             }
         }
     };
 
-    u32x4_t W[D][2];
+    u32x4_t W[D][HALVES][2];
     u32x4_t B[D][RT][2];
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -440,7 +455,7 @@ hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const
     static const Fn table[8] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>,
                                 nullptr,           nullptr,           nullptr, dh_mfma_kernel<8>};
     const int mt = p.mp16 / 16;
-    const int ktiles = (K + kDhK - 1) / kDhK;
+    const int ktiles = (K + dh_cols(mt) - 1) / dh_cols(mt);
     const int ms = p.dh_mslices;
     // slices of 128 rows (MT = 8) above 64 rows of hidden, one slice of up to 64 rows below
     if ((p.path != kPathMfma && p.path != kPathGemm) || mt < 1 || mt > 8 || !table[mt - 1] || ms < 1 ||

@@ -83,9 +83,10 @@ def test_backward_plans_cover_rows_and_partials(M):
                     assert p["block"] * 8 * 2 >= K and (p["block"] * 8 >= K or M <= 3)
                     assert p["block"] - 64 < math.ceil(K / 8 / (1 if p["block"] * 8 >= K else 2))
             elif M > 8:
-                # MFMA contractions: ranges of 32-row steps of the weights x 64-column tiles, one
-                # fp32 partial of dh per range; zero-padded operand copies before the partials
-                ktiles = math.ceil(K / 64)
+                # MFMA contractions: ranges of 32-row steps of the weights x 128-column tiles (up to
+                # 64 rows of hidden), one fp32 partial of dh per range; zero-padded operand copies
+                # before the partials
+                ktiles = math.ceil(K / 128)
                 assert p["launches"] == 6 and p["grid"] % ktiles == 0
                 splits = p["grid"] // ktiles
                 jr = math.ceil(N / splits / 32) * 32 if splits > 1 else math.ceil(N / 32) * 32
