@@ -151,7 +151,8 @@ def test_grouped_generic_layouts():
 
 
 STRIDED = [((700, 130, 64), 4), ((700, 132, 64), 4), ((700, 132, 64), 16),
-           ((704, 136, 64), 16), ((704, 136, 64), 32)]  # every N a multiple of 8: the 8-row groups
+           ((704, 136, 64), 16), ((704, 136, 64), 32),  # every N a multiple of 8: the 8-row groups
+           ((704, 136, 64), 48), ((704, 136, 64), 64)]  # 48 and 64 rows in one launch
 
 
 @pytest.mark.parametrize("Ns,M", STRIDED)

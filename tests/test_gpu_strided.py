@@ -45,7 +45,9 @@ CASES = [
     (8, 700, 5120, 8, 8, 8, 7, {}),                                      # 4-row K-slices
     (16, 700, 5120, 24, 8, 16, 0, {}),                                   # 8-row K-slices
     (32, 520, 5120, 8, 40, 8, 9, {}),                                    # 8-row K-slices, M = 32
-    (40, 333, 1024, 8, 8, 8, 4, {}),                                     # slices of 32 rows of hidden
+    (40, 333, 1024, 8, 8, 8, 4, {}),                                     # one launch of 40 rows (5 tiles)
+    (64, 700, 2560, 8, 16, 8, 3, {}),                                    # one launch of 64 rows (8 tiles)
+    (70, 520, 1024, 8, 8, 16, 2, {}),                                    # tiled GEMM above 64 rows
     (3, 257, 77, 3, 5, 0, 2, {}),                                        # generic: K % 8 != 0
     (2, 300, 1024, 3, 0, 0, 0, {}),                                      # generic: hidden stride not a multiple of 8
 ]
