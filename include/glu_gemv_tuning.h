@@ -44,8 +44,10 @@ typedef struct glu_tuning {
                              piece of a row; at most 4 waves per workgroup) */
     int mfma_order;       /* MFMA, 8 rows per wave: 1 = each block of 32 weight rows walks K
                              in turn; 2 = a workgroup walks K once for all its blocks (at
-                             most 3), loading each K-slice of hidden once (8 segments,
-                             depth 1, more than 8 rows of hidden) */
+                             most 3), loading each K-slice of hidden once (depth 1, more
+                             than 8 rows of hidden; 8 segments for launches of up to 32
+                             rows, 4 segments for launches of 64 rows: the default
+                             above 32 rows) */
 } glu_tuning;
 
 glu_status glu_dual_gemv_tuned(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
@@ -60,7 +62,11 @@ glu_status glu_dual_gemv_strided_tuned(const uint16_t* hidden, int64_t ldh, cons
 /* glu_grouped_gemv (glu_gemv.h) with overrides: kernel GLU_KERNEL_VALU,
  * GLU_KERNEL_MFMA or GLU_KERNEL_GENERIC; for VALU rows_per_wave 1 or 2 (2
  * only up to M = 4); for MFMA mfma_segments (2, 4, 5; 2 with hidden read
- * from L2) and mfma_hidden 1 or 2; waves_per_block and grid for both. */
+ * from L2) and mfma_hidden 1 or 2; waves_per_block and grid for both.
+ * With every N a multiple of 8, mfma_hidden 3 (the default above 8 rows of
+ * hidden) streams K-slices of hidden under the weights in 8-row groups,
+ * launches of up to 64 rows, stages of 8 segments (4 on request, above 32
+ * rows only). */
 glu_status glu_grouped_gemv_tuned(const uint16_t* hidden, int64_t ldh, const glu_projection* proj, int n,
                                   int64_t M, int64_t K, void* stream, const glu_tuning* tuning);
 
