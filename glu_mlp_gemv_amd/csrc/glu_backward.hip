@@ -837,8 +837,8 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         // dh's B operand: 1, 2 or 4 tiles of 16 rows (4 waves split evenly), above 64 rows slices of
         // 8 tiles (two per wave: each weight tile read from beyond L2 half as often as with slices of
         // 64)
-        p.mp16 = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
-        p.dh_mslices = big ? (int)((M + 127) / 128) : 1;
+        p.mp16 = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : (M <= 128 ? 128 : 256)));
+        p.dh_mslices = big ? (int)((M + p.mp16 - 1) / p.mp16) : 1;
         p.mp32 = (int)((M + 31) / 32 * 32);
         p.np32 = (int)((N + 31) / 32 * 32);
         // about 512 workgroups of dh_cols columns x one range of rows (x one slice of hidden), ranges a
@@ -848,7 +848,9 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
         const int64_t per_split = ktiles * p.dh_mslices;
         // (above 64 rows at most that many: the 128-row kernel fits two workgroups per CU, and a second
         // round for a few would cost a whole step loop)
-        int64_t splits = big ? kBwdTargetBlocks / per_split : (kBwdTargetBlocks + per_split - 1) / per_split;
+        // (slices of 256 rows hold one workgroup per CU: at most half as many)
+        const int64_t target = p.mp16 > 128 ? kBwdTargetBlocks / 2 : kBwdTargetBlocks;
+        int64_t splits = big ? target / per_split : (target + per_split - 1) / per_split;
         splits = splits < 1 ? 1 : (splits > steps_all ? steps_all : splits);
         const int64_t steps = (steps_all + splits - 1) / splits;
         p.dh_jr = (int)(steps * 32);

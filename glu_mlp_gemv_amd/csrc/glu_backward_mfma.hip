@@ -248,7 +248,7 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
                const uint16_t* __restrict__ g2, const uint16_t* __restrict__ u2, float* __restrict__ partial, int M,
                int N, int K, int np, int ktiles, int jr, int mslices)
 {
-    constexpr int D = kDhDepth;
+    constexpr int D = MT > 8 ? 2 : kDhDepth;  // 16 row tiles: four per wave, so two steps in flight
     constexpr int KK = dh_cols(MT);
     constexpr int NKS = KK / 16;  // column subtiles of 16
     constexpr int HALVES = KK / 64;
@@ -452,14 +452,16 @@ hipError_t dh_mfma_launch(const BwdPlan& p, int M, const uint16_t* gate_w, const
 {
     using Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, float*, int, int, int,
                         int, int, int, int);
-    static const Fn table[8] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>,
-                                nullptr,           nullptr,           nullptr, dh_mfma_kernel<8>};
+    static const Fn table[16] = {dh_mfma_kernel<1>, dh_mfma_kernel<2>, nullptr, dh_mfma_kernel<4>,
+                                 nullptr,           nullptr,           nullptr, dh_mfma_kernel<8>,
+                                 nullptr,           nullptr,           nullptr, nullptr,
+                                 nullptr,           nullptr,           nullptr, dh_mfma_kernel<16>};
     const int mt = p.mp16 / 16;
     const int ktiles = (K + dh_cols(mt) - 1) / dh_cols(mt);
     const int ms = p.dh_mslices;
     // slices of 128 rows (MT = 8) above 64 rows of hidden, one slice of up to 64 rows below
-    if ((p.path != kPathMfma && p.path != kPathGemm) || mt < 1 || mt > 8 || !table[mt - 1] || ms < 1 ||
-        (p.path == kPathGemm) != (mt == 8) || (ms > 1 && mt != 8) || M < 1 || M > (int64_t)ms * p.mp16 ||
+    if ((p.path != kPathMfma && p.path != kPathGemm) || mt < 1 || mt > 16 || !table[mt - 1] || ms < 1 ||
+        (p.path == kPathGemm) != (mt >= 8) || (ms > 1 && mt < 8) || M < 1 || M > (int64_t)ms * p.mp16 ||
         N < 1 || K < 8 || (K & 7) != 0 ||
         p.dh_jr < kDhStep || p.dh_jr % kDhStep != 0 || p.np32 < N || p.np32 % kDhStep != 0 || p.dh_splits < 1 ||
         (int64_t)(p.dh_splits - 1) * p.dh_jr >= N || (int64_t)p.dh_splits * p.dh_jr < N ||

@@ -449,7 +449,7 @@ def test_backward_plan_and_workspace(lib):
     with pytest.raises(api.GluError):
         api.backward_plan(65537, 10, 64)      # M > 65536
     assert api.backward_plan(65, 10, 64)["launches"] == 6       # above 64 rows: the GEMM regime
-    assert api.backward_plan(512, 9216, 2560)["grid"] == 40 * 3 * 4   # dh: column tiles x splits x 128-row slices
+    assert api.backward_plan(512, 9216, 2560)["grid"] == 40 * 3 * 2   # dh: column tiles x splits x 256-row slices
     with pytest.raises(api.GluError):
         api.backward_workspace_bytes(-1, 10, 64)
     b = ctypes.c_int64(0)
