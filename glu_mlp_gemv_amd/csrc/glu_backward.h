@@ -67,11 +67,11 @@ struct BwdPlan {
     int split_waves;         // waves per workgroup
     int split_rpb;           // weight rows per workgroup
     int split_grid;          // workgroups (each leaves one partial of dh)
-    int mp16, mp32;          // MFMA path: M rounded up to 16, 32 or 64, above 64 rows 128 per slice (dh's B
-                             // operand), and M rounded up to 32 (dW's)
+    int mp16, mp32;          // MFMA path: M rounded up to 16, 32 or 64, above 64 rows 128 and above 128 rows
+                             // 256 per slice (dh's B operand), and M rounded up to 32 (dW's)
     int np32;                // N rounded up to 32 (the columns of dg2, du2)
     int dh_splits, dh_jr;    // ranges of weight rows (jr rows each, a multiple of 32) = dh's partials
-    int dh_mslices;          // slices of mp16 rows of hidden dh's grid covers (1 up to 64 rows, then of 128)
+    int dh_mslices;          // slices of mp16 rows of hidden dh's grid covers (1 up to 128 rows)
     int dh_steps;            // 32-row steps of the longest range
     bool gu_gemm;            // g and u from the tiled GEMM (N % 4 == 0 and M > 64, or M > 32 with N % 8 != 0)
                              // instead of the grouped GEMV

@@ -1,8 +1,9 @@
 // Backward of the dual-weight GLU projection above 8 rows of hidden: the three
 // contractions as v_mfma_f32_16x16x32_bf16 products.  Up to 64 rows as below;
 // above, dh_mfma_kernel runs over slices of 128 rows of hidden (two 16-row
-// tiles per wave) and the weight gradients are one tiled GEMM (gemm_dw_launch,
-// glu_gemm.hip) on the same transposed copies.
+// tiles per wave; above 128 rows slices of 256, four tiles per wave) and the
+// weight gradients are one tiled GEMM (gemm_dw_launch, glu_gemm.hip) on the
+// same transposed copies.
 //
 // After the grouped GEMV and the elementwise step have left dg and du
 // ([2][M][N] bf16) at the workspace head, repack_kernel writes zero-padded
@@ -231,17 +232,17 @@ dw_mfma_kernel(const uint16_t* __restrict__ hT, const uint16_t* __restrict__ dgT
     }
 }
 
-// MT = Mp16 / 16 (1, 2, 4 or 8).  Workgroup b: columns [64 (t % ktiles), +64), rows j of split
+// MT = Mp16 / 16 (1, 2, 4, 8 or 16).  Workgroup b: columns [KK (t % ktiles), +KK), rows j of split
 // t / ktiles: [split * jr, min(N, (split + 1) * jr)), jr a multiple of 32, where t = b with one
-// slice of rows of hidden.  Above 64 rows (mslices >= 1, MT = 8) t = b' / mslices and the workgroup
-// takes rows 128 (b' % mslices) .. + 127 of hidden, b' being b renumbered so that the workgroups one
+// slice of rows of hidden.  Above 64 rows (mslices >= 1, MT = 8 or 16) t = b' / mslices and the
+// workgroup takes rows 16 MT (b' % mslices) .. + 16 MT - 1 of hidden, b' being b renumbered so that the workgroups one
 // XCD receives (the hardware deals them to the 8 XCDs in turn) are consecutive: the slices of one
 // (column tile, split) then run on one XCD and read its weight tile from that XCD's L2 after the
 // first.  g2, u2: dg2, du2 ([mslices * Mp16][np] with np a multiple of 32).  partial:
 // [splits][2][M][K] fp32.
 // KK = dh_cols(MT) columns k per workgroup: 128 up to MT = 4 (8 column subtiles; each thread loads two
 // 16-byte chunks of its weight row per step, so a workgroup reads 256 contiguous bytes of each row),
-// 64 at MT = 8.
+// 64 at MT = 8 and 16.
 template <int MT>
 __global__ void __launch_bounds__(kMfmaBwdThreads)
 dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__ up_w,
@@ -270,8 +271,8 @@ dh_mfma_kernel(const uint16_t* __restrict__ gate_w, const uint16_t* __restrict__
     const int nsteps = (je - jb + kDhStep - 1) / kDhStep;  // >= 1: the plan leaves no split empty
     const int i16 = lane & 15, q = lane >> 4;
     // the NKS x MT (column subtile, row tile) pairs: up to MT = 4 wave w takes row tile w % MT of hidden
-    // and the KT column subtiles from (w / MT) KT on; at MT = 8 it takes row tiles w and w + 4 and all
-    // column subtiles.  No two waves load the same B operand.
+    // and the KT column subtiles from (w / MT) KT on; at MT = 8 (16) it takes row tiles w, w + 4 (and
+    // w + 8, w + 12) and all column subtiles.  No two waves load the same B operand.
     constexpr int RT = MT > 4 ? MT / 4 : 1;             // row tiles per wave
     constexpr int KT = MT > 4 ? NKS : MT * NKS / 4;     // column subtiles per wave
     const int mt = MT > 4 ? wave : wave % MT;  // the wave's first row tile; the others 4 apart

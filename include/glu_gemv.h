@@ -234,8 +234,8 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * the grouped GEMV for g and u (one launch up to M = 64 when N % 8 == 0;
  * above M = 64, or above 32 when only N % 4 == 0, a tiled GEMM), then the
  * gradient kernels (above M = 8 on the matrix cores; above M = 64 dhidden
- * over slices of 128 rows of hidden and the weight gradients as one tiled
- * GEMM contracting over the rows of hidden).
+ * over slices of 128 rows of hidden, above M = 128 of 256, and the weight
+ * gradients as one tiled GEMM contracting over the rows of hidden).
  */
 glu_status glu_dual_gemv_backward(const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
                                   const uint16_t* dout, uint16_t* dhidden, uint16_t* dgate_w, uint16_t* dup_w,
