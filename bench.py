@@ -720,6 +720,12 @@ def summarize_trace(d: str):
     return "\n".join(lines)
 
 
+def short_kernel_name(name: str) -> str:
+    """A demangled kernel name without its argument list, return type or anonymous namespace (which
+    would otherwise cut the name at its first parenthesis)."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
+
+
 def summarize_trace_grid(d: str):
     """Per-dispatch kernel trace grouped by (kernel, grid size): a kernel run at several shapes gets
     one row per shape (the grid tells them apart), average and median duration."""
@@ -731,8 +737,7 @@ def summarize_trace_grid(d: str):
         name = r["Kernel_Name"]
         if not name.startswith(("glu::", "void glu::")):
             continue
-        key = (name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]),
-               int(r["LDS_Block_Size"]))
+        key = (short_kernel_name(name), int(r["Grid_Size_X"]), int(r["LDS_Block_Size"]))
         groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines = ["| kernel | grid (threads) | LDS bytes | dispatches | average ns | median ns | min ns |",
              "|---|---|---|---|---|---|---|"]
@@ -752,8 +757,7 @@ def summarize_counter_table(d: str):
         name = r.get("Kernel_Name", "")
         if not name.startswith(("glu::", "void glu::")):
             continue
-        key = (name.split("(")[0].replace("void ", ""), int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0),
-               r["Counter_Name"])
+        key = (short_kernel_name(name), int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0), r["Counter_Name"])
         # a dispatch may report several rows of one counter (per dimension): sum them per dispatch
         disp = (r.get("Dispatch_Id") or r.get("Correlation_Id"))
         acc.setdefault(key, {}).setdefault(disp, 0.0)
@@ -788,7 +792,7 @@ def summarize_counters(d: str, command: str):
     for (k, c), vs in per.items():
         if "glu::" not in k:
             continue
-        short = k.split("(")[0].replace("void ", "").strip()
+        short = short_kernel_name(k)
         ent = kernels.setdefault(short, {})
         ent[c + "_kib_per_dispatch"] = round(sum(vs) / len(vs), 2)
         ent["dispatches"] = len(vs)
