@@ -834,14 +834,15 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     // hidden the tiled GEMM (which reads the weights once where the GEMV's 32-row slices would
     // read them once per slice)
     if (bp.gu_gemm) {
-        e = glu::gemm_linear_launch((int)M, hidden, gate_w, up_w, gu, (int)N, (int)K, s);
+        // the elementwise step (dg, du) in the GEMM's epilogue
+        e = glu::gemm_linear_launch((int)M, hidden, gate_w, up_w, gu, (int)N, (int)K, dout, s);
         if (e != hipSuccess) return fail_launch(e);
     } else {
         glu_projection proj[2] = {{gate_w, gu, N, K, N}, {up_w, gu + mn, N, K, N}};
         st = run_grouped(hidden, K, proj, 2, M, K, stream, nullptr);
         if (st != GLU_OK) return st;
+        e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
     }
-    e = glu::act_grad_launch(gu, dout, N, (int)M, (int)N, s);
     const uint16_t* dg_all = gu;
     const uint16_t* du_all = gu + mn;
     if (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm) {
@@ -1095,8 +1096,8 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     const bool run_all = M > 0 && N > 0 && K > 0;
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
-    // the grouped GEMV counts as one launch
-    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm ? 6
+    // the grouped GEMV counts as one launch; the GEMM for g and u takes the elementwise step along
+    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm ? (bp.gu_gemm ? 5 : 6)
                                 : bp.path != glu::kPathChunks ? 2
                                                               : 4)
                              : 0;

@@ -2,9 +2,30 @@
 #pragma once
 
 #include "../../include/glu_gemv.h"
+#include "glu_device.h"
 #include "glu_launch.h"
 
 namespace glu {
+
+// The backward's elementwise step.  From g and u (the bf16 gate and up values of the forward) and go
+// (the bf16 upstream gradient of the output): du = bf16(go s) with s = bf16(silu(g)), and
+// dg = bf16(bf16(go u) sigma(g) (1 + g (1 - sigma(g)))), each fp32 step computed in fp64 and rounded
+// once to fp32 (for +, -, *, / of fp32 operands this equals the IEEE fp32 result: 53 >= 2 * 24 + 2
+// bits), exp as in the forward's epilogue.
+__device__ __forceinline__ void glu_act_grad(float g, float u, float go, uint16_t* dg_out, uint16_t* du_out)
+{
+    const float e = (float)exp(-(double)g);
+    const float d = (float)(1.0 + (double)e);
+    const float s = bf16_to_f32(f32_to_bf16_rne((float)((double)g / (double)d)));  // silu(g) as a bf16 tensor
+    const float ds = bf16_to_f32(f32_to_bf16_rne((float)((double)go * (double)u)));
+    *du_out = f32_to_bf16_rne((float)((double)go * (double)s));
+    const float sig = (float)(1.0 / (double)d);
+    const float t1 = (float)((double)ds * (double)sig);
+    const float t2 = (float)(1.0 - (double)sig);
+    const float t3 = (float)((double)g * (double)t2);
+    const float t4 = (float)(1.0 + (double)t3);
+    *dg_out = f32_to_bf16_rne((float)((double)t1 * (double)t4));
+}
 
 // Two fp32 values to a packed pair of bf16 (lo in bits 0-15), round to nearest with ties to even:
 // gfx950's v_cvt_pk_bf16_f32, one instruction for the pair (f32_to_bf16_rne takes about five per

@@ -51,24 +51,6 @@ constexpr int64_t kReduceFlatMinElems = 131072;  // M * K from which that reduct
 
 typedef unsigned u32x4_b __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float f32r(double x) { return (float)x; }
-
-// fp32 steps evaluated in fp64 and rounded once to fp32: for +, -, *, / of
-// fp32 operands this equals the IEEE fp32 result (53 >= 2 * 24 + 2 bits)
-__device__ __forceinline__ void act_grad(float g, float u, float go, uint16_t* dg_out, uint16_t* du_out)
-{
-    const float e = (float)exp(-(double)g);
-    const float d = f32r(1.0 + (double)e);
-    const float s = bf16_to_f32(f32_to_bf16_rne(f32r((double)g / (double)d)));  // silu(g) as a bf16 tensor
-    const float ds = bf16_to_f32(f32_to_bf16_rne(f32r((double)go * (double)u)));
-    *du_out = f32_to_bf16_rne(f32r((double)go * (double)s));
-    const float sig = f32r(1.0 / (double)d);
-    const float t1 = f32r((double)ds * (double)sig);
-    const float t2 = f32r(1.0 - (double)sig);
-    const float t3 = f32r((double)g * (double)t2);
-    const float t4 = f32r(1.0 + (double)t3);
-    *dg_out = f32_to_bf16_rne(f32r((double)t1 * (double)t4));
-}
 
 }  // namespace
 
@@ -85,7 +67,7 @@ act_grad_kernel(uint16_t* __restrict__ gu, const uint16_t* __restrict__ dout, in
     const float u = bf16_to_f32(gu[MN + i]);
     const float go = bf16_to_f32(dout[m * ldd + j]);
     uint16_t dg, du;
-    act_grad(g, u, go, &dg, &du);
+    glu_act_grad(g, u, go, &dg, &du);
     gu[i] = dg;
     gu[MN + i] = du;
 }
@@ -352,7 +334,7 @@ splitk_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             }
             uint16_t dgb = 0, dub = 0;
             if (j < j_end) {
-                act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)),
+                glu_act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)),
                          bf16_to_f32(dout[(int64_t)m * N + j]), &dgb, &dub);
                 dgu[(int64_t)m * N + j] = dgb;
                 dgu[MN + (int64_t)m * N + j] = dub;
@@ -576,7 +558,7 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             const float G = wave_sum(pg[0]);
             const float Uv = wave_sum(pu[0]);
             uint16_t dgb, dub;
-            act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)), bf16_to_f32(go[0]), &dgb,
+            glu_act_grad(bf16_to_f32(f32_to_bf16_rne(G)), bf16_to_f32(f32_to_bf16_rne(Uv)), bf16_to_f32(go[0]), &dgb,
                      &dub);
             if (lane == 0) {
                 dgu[j] = dgb;
@@ -599,7 +581,7 @@ fused1_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ 
             }
             uint16_t dgb = 0, dub = 0;
             if (lane < M) {
-                act_grad(bf16_to_f32(f32_to_bf16_rne(Gm)), bf16_to_f32(f32_to_bf16_rne(Um)), bf16_to_f32(gom), &dgb,
+                glu_act_grad(bf16_to_f32(f32_to_bf16_rne(Gm)), bf16_to_f32(f32_to_bf16_rne(Um)), bf16_to_f32(gom), &dgb,
                          &dub);
                 dgu[(int64_t)lane * N + j] = dgb;
                 dgu[MN + (int64_t)lane * N + j] = dub;

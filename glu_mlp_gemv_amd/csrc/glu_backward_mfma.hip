@@ -5,8 +5,9 @@
 // weight gradients are one tiled GEMM (gemm_dw_launch, glu_gemm.hip) on the
 // same transposed copies.
 //
-// After the grouped GEMV and the elementwise step have left dg and du
-// ([2][M][N] bf16) at the workspace head, repack_kernel writes zero-padded
+// After the grouped GEMV and the elementwise step (or the tiled GEMM with that
+// step in its epilogue) have left dg and du ([2][M][N] bf16) at the workspace
+// head, repack_kernel writes zero-padded
 // operand copies:
 //  * dg2, du2 [Mp16][Np]: dg and du with rows padded to 16, 32 or 64 and
 //    columns to a multiple of 32 (the B operand of dh, contraction over j);

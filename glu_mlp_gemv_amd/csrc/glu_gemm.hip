@@ -17,6 +17,7 @@
 // Tiles are ordered so that the consecutive workgroups an XCD receives (the
 // hardware deals workgroups to the 8 XCDs in turn) share weight tiles, which
 // then come from that XCD's L2 for every M tile after the first.
+#include "glu_backward.h"
 #include "glu_device.h"
 #include "glu_launch.h"
 #include "glu_mfma_common.h"
@@ -41,17 +42,20 @@ __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 // nbm: M tiles; the grid holds ceil(N / BN) * nbm workgroups.
 // LIN: write bf16(G) and bf16(U) instead of the GLU product: G to out, U to out2 (the
 // backward's [2][M][N] workspace head).
+// ACT (with LIN, not TRANS): the backward's elementwise step on the rounded G and U and the upstream
+// gradient dout ([M][N], row stride ldo): dG to out, dU to out2 instead of G and U.
 // TRANS (with LIN): the MFMA operands swap places, so each lane holds 4 consecutive hidden rows
 // of one weight row, and G, U are stored transposed, out[n][m] and out2[n][m] (rows ldo apart;
 // M a multiple of 4).  The backward's weight gradients are this product with dg^T, du^T as the
 // two weights and hidden^T as the hidden (contraction over the rows of hidden).
-template <int BN, int BM, bool KTAIL, int PF, bool LIN = false, bool TRANS = false>
+template <int BN, int BM, bool KTAIL, int PF, bool LIN = false, bool TRANS = false, bool ACT = false>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __restrict__ gate, int64_t ldg,
             const uint16_t* __restrict__ up, int64_t ldu, uint16_t* __restrict__ out, uint16_t* __restrict__ out2,
-            int64_t ldo, int M, int N, int K, int nbm, int vec_out)
+            int64_t ldo, int M, int N, int K, int nbm, int vec_out, const uint16_t* __restrict__ dout)
 {
     static_assert(LIN || !TRANS, "the transposed store is a form of the linear epilogue");
+    static_assert(!ACT || (LIN && !TRANS), "the elementwise step follows the row-major linear epilogue");
     constexpr int ROWS = 2 * BN + BM;                           // LDS rows per stage
     constexpr int LPT = ROWS * kStageChunks / kGemmThreads;     // 16-byte loads per thread per stage
     constexpr int WN = BN / 2, WM = BM / 2;
@@ -224,6 +228,22 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
             if constexpr (LIN) {
                 if (m < M && n + 3 < N) {  // N % 4 == 0 for this form (checked by the launcher)
                     uint2 wg, wu;
+                    if constexpr (ACT) {
+                        uint16_t dg[4], du[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            glu_act_grad(bf16_to_f32(f32_to_bf16_rne(ag[i][j][e])),
+                                         bf16_to_f32(f32_to_bf16_rne(au[i][j][e])),
+                                         bf16_to_f32(dout[(int64_t)m * ldo + n + e]), &dg[e], &du[e]);
+                        }
+                        wg.x = (uint32_t)dg[0] | ((uint32_t)dg[1] << 16);
+                        wg.y = (uint32_t)dg[2] | ((uint32_t)dg[3] << 16);
+                        wu.x = (uint32_t)du[0] | ((uint32_t)du[1] << 16);
+                        wu.y = (uint32_t)du[2] | ((uint32_t)du[3] << 16);
+                        *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + n) = wg;
+                        *reinterpret_cast<uint2*>(out2 + (int64_t)m * ldo + n) = wu;
+                        continue;
+                    }
                     wg.x = (uint32_t)f32_to_bf16_rne(ag[i][j][0]) | ((uint32_t)f32_to_bf16_rne(ag[i][j][1]) << 16);
                     wg.y = (uint32_t)f32_to_bf16_rne(ag[i][j][2]) | ((uint32_t)f32_to_bf16_rne(ag[i][j][3]) << 16);
                     wu.x = (uint32_t)f32_to_bf16_rne(au[i][j][0]) | ((uint32_t)f32_to_bf16_rne(au[i][j][1]) << 16);
@@ -257,7 +277,7 @@ gemm_kernel(const uint16_t* __restrict__ hidden, int64_t ldh, const uint16_t* __
 namespace {
 
 using GemmFn = void (*)(const uint16_t*, int64_t, const uint16_t*, int64_t, const uint16_t*, int64_t, uint16_t*,
-                        uint16_t*, int64_t, int, int, int, int, int);
+                        uint16_t*, int64_t, int, int, int, int, int, const uint16_t*);
 
 template <int BN, int BM>
 GemmFn pick_tail(bool ktail, int pf)
@@ -314,23 +334,26 @@ hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const
     // 8-byte output stores need 8-byte aligned rows
     const int vec_out = (((uintptr_t)out & 7u) == 0 && (ld.o & 3) == 0) ? 1 : 0;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), lds, stream, hidden, ld.h, gate_w, ld.g, up_w,
-                       ld.u, out, out, ld.o, M, N, K, nbm, vec_out);
+                       ld.u, out, out, ld.o, M, N, K, nbm, vec_out, nullptr);
     return hipGetLastError();
 }
 
 hipError_t gemm_linear_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
-                              uint16_t* gu, int N, int K, hipStream_t stream)
+                              uint16_t* gu, int N, int K, const uint16_t* dout, hipStream_t stream)
 {
     // 64 x 64 tiles, two stages of loads in flight; N % 4 == 0 so that each lane's 4 outputs of a
-    // row are whole 8-byte stores inside the row
+    // row are whole 8-byte stores inside the row.  With dout: the elementwise step in the epilogue
     if (M < 1 || N < 4 || (N & 3) != 0 || K < 8 || (K & 7) != 0) return hipErrorInvalidValue;
     const bool ktail = (K % kStageK) != 0;
-    GemmFn fn = ktail ? gemm_kernel<64, 64, true, 2, true> : gemm_kernel<64, 64, false, 2, true>;
+    GemmFn fn = dout ? (ktail ? gemm_kernel<64, 64, true, 2, true, false, true>
+                              : gemm_kernel<64, 64, false, 2, true, false, true>)
+                     : (ktail ? gemm_kernel<64, 64, true, 2, true> : gemm_kernel<64, 64, false, 2, true>);
     const int64_t nbm = (M + 63) / 64;
     const int64_t grid = ((N + 63) / 64) * nbm;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), gemm_lds_bytes(64, 64), stream, hidden, (int64_t)K,
-                       gate_w, (int64_t)K, up_w, (int64_t)K, gu, gu + (int64_t)M * N, (int64_t)N, M, N, K, (int)nbm, 1);
+                       gate_w, (int64_t)K, up_w, (int64_t)K, gu, gu + (int64_t)M * N, (int64_t)N, M, N, K, (int)nbm, 1,
+                       dout);
     return hipGetLastError();
 }
 
@@ -347,7 +370,7 @@ hipError_t gemm_dw_launch(int mp, const uint16_t* hT, const uint16_t* dgT, const
     const int64_t grid = ((N + 63) / 64) * nbm;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kGemmThreads), gemm_lds_bytes(64, 64), stream, hT, (int64_t)mp,
-                       dgT, (int64_t)mp, duT, (int64_t)mp, dwg, dwu, (int64_t)K, K, N, mp, (int)nbm, 1);
+                       dgT, (int64_t)mp, duT, (int64_t)mp, dwg, dwu, (int64_t)K, K, N, mp, (int)nbm, 1, nullptr);
     return hipGetLastError();
 }
 

@@ -125,9 +125,10 @@ int64_t gemm_grid(const GemmConfig& c, int64_t M, int64_t N);
 hipError_t gemm_launch(const GemmConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                        const uint16_t* up_w, uint16_t* out, int N, int K, const RowStrides& ld, hipStream_t stream);
 // g = bf16(h Wg^T) into gu [M][N] and u = bf16(h Wu^T) into gu + M N: the same tiles (64 x 64) without
-// the GLU epilogue, for the backward at M > 32.  Dense operands; N % 4 == 0, K % 8 == 0.
+// the GLU epilogue, for the backward at M > 32.  Dense operands; N % 4 == 0, K % 8 == 0.  With dout
+// ([M][N]) the backward's elementwise step runs in the epilogue: dg and du are stored instead.
 hipError_t gemm_linear_launch(int M, const uint16_t* hidden, const uint16_t* gate_w, const uint16_t* up_w,
-                              uint16_t* gu, int N, int K, hipStream_t stream);
+                              uint16_t* gu, int N, int K, const uint16_t* dout, hipStream_t stream);
 // dWg = bf16(dgT hT^T) [N][K] and dWu likewise, contraction over mp (a multiple of 32) padded rows of
 // hidden: hT [K][mp], dgT, duT [N][mp], all dense and 16-byte aligned, K % 8 == 0.
 hipError_t gemm_dw_launch(int mp, const uint16_t* hT, const uint16_t* dgT, const uint16_t* duT, uint16_t* dwg,

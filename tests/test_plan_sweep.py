@@ -87,7 +87,9 @@ def test_backward_plans_cover_rows_and_partials(M):
                 # 64 rows of hidden), one fp32 partial of dh per range; zero-padded operand copies
                 # before the partials
                 ktiles = math.ceil(K / 128)
-                assert p["launches"] == 6 and p["grid"] % ktiles == 0
+                # g and u from the tiled GEMM (elementwise step in its epilogue) or the grouped GEMV
+                gu_gemm = N % 4 == 0 and (M > 64 or (M > 32 and N % 8 != 0))
+                assert p["launches"] == (5 if gu_gemm else 6) and p["grid"] % ktiles == 0
                 splits = p["grid"] // ktiles
                 jr = math.ceil(N / splits / 32) * 32 if splits > 1 else math.ceil(N / 32) * 32
                 assert (splits - 1) * jr < N <= splits * jr or splits == 1
