@@ -777,6 +777,22 @@ glu_status plan_backward(int64_t M, int64_t N, int64_t K, glu::BwdPlan* bp)
     if (st != GLU_OK) return st;
     if (M > glu::kBwdMaxM) return GLU_ERR_UNSUPPORTED;
     *bp = glu::bwd_plan(M, N, K);
+    bp->gu_pass = false;
+    bp->gu_U = bp->gu_nsg = bp->gu_grid = 0;
+    bp->gu_ragged = false;
+    // 8 < M <= 64 with the grouped GEMV's shape: where the forward runs the slice-major 8-row kernel in
+    // one launch, that kernel forms dg and du in its epilogue (the same G and U; one launch fewer)
+    const glu::MfmaConfig& c = L.mfma;
+    if (bp->path == glu::kPathMfma && !bp->gu_gemm && L.kernel == GLU_KERNEL_MFMA && L.launches == 1 &&
+        c.rows == 8 && c.order == glu::kOrderSlices && c.hidden == glu::kHiddenSlices && c.depth == 1 &&
+        c.block == glu::kMfmaMaxThreads) {
+        bp->gu_pass = true;
+        bp->gu_U = c.U;
+        bp->gu_nsg = c.nsg;
+        bp->gu_grid = c.grid;
+        bp->gu_ragged = c.ragged;
+        bp->accum_depth = std::max(bp->accum_depth, L.accum_depth);
+    }
     return GLU_OK;
 }
 
@@ -836,6 +852,11 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
     if (bp.gu_gemm) {
         // the elementwise step (dg, du) in the GEMM's epilogue
         e = glu::gemm_linear_launch((int)M, hidden, gate_w, up_w, gu, (int)N, (int)K, dout, s);
+        if (e != hipSuccess) return fail_launch(e);
+    } else if (bp.gu_pass) {
+        // the same step in the epilogue of the forward's slice-major kernel
+        e = glu::mfma8_act_launch((int)M, bp.gu_U, bp.gu_nsg, bp.gu_ragged, bp.gu_grid, hidden, gate_w, up_w, dout, gu,
+                                  N, K, s);
         if (e != hipSuccess) return fail_launch(e);
     } else {
         glu_projection proj[2] = {{gate_w, gu, N, K, N}, {up_w, gu + mn, N, K, N}};
@@ -1096,8 +1117,10 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     const bool run_all = M > 0 && N > 0 && K > 0;
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
-    // the grouped GEMV counts as one launch; the GEMM for g and u takes the elementwise step along
-    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm ? (bp.gu_gemm ? 5 : 6)
+    // the grouped GEMV counts as one launch; the tiled GEMM for g and u, or the forward's slice-major
+    // kernel, takes the elementwise step along
+    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm
+                                    ? (bp.gu_gemm || bp.gu_pass ? 5 : 6)
                                 : bp.path != glu::kPathChunks ? 2
                                                               : 4)
                              : 0;

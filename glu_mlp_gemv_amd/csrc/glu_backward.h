@@ -71,11 +71,13 @@ constexpr int split_rows(int M, int U) { return U == 1 ? (M <= 2 ? 4 : 2) : (M <
 constexpr int kPathChunks = 0;   // 2 <= M <= 8: grouped GEMV, gradient step, contraction, reduction
 constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
 constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
-constexpr int kPathMfma = 3;     // 8 < M <= 64: grouped GEMV, gradient step, repacking, dh_mfma_kernel,
-                                 // reduction, dw_mfma_kernel
-constexpr int kPathGemm = 4;     // M > 64: tiled GEMM for g and u, gradient step, repacking,
-                                 // dh_mfma_kernel over slices of 64 rows of hidden, reduction, and the
-                                 // weight gradients as one transposed tiled GEMM (gemm_dw_launch)
+constexpr int kPathMfma = 3;     // 8 < M <= 64: dg and du (the forward's slice-major kernel with the
+                                 // gradient step as its epilogue, or the grouped GEMV and the gradient
+                                 // step), repacking, dh_mfma_kernel, reduction, dw_mfma_kernel
+constexpr int kPathGemm = 4;     // M > 64: tiled GEMM for g and u with the gradient step in its
+                                 // epilogue, repacking, dh_mfma_kernel over slices of 128 or 256 rows of
+                                 // hidden, reduction, and the weight gradients as one transposed tiled
+                                 // GEMM (gemm_dw_launch)
 constexpr int kBwdMfmaMinM = 9;  // rows of hidden from which the contractions run on MFMA
 // columns of dh per dh_mfma_kernel workgroup for mt 16-row tiles of hidden per slice
 constexpr int dh_cols(int mt) { return mt <= 4 ? 128 : 64; }
@@ -96,6 +98,11 @@ struct BwdPlan {
     int dh_steps;            // 32-row steps of the longest range
     bool gu_gemm;            // g and u from the tiled GEMM (N % 4 == 0 and M > 64, or M > 32 with N % 8 != 0)
                              // instead of the grouped GEMV
+    bool gu_pass;            // kPathMfma without gu_gemm: dg and du from the forward's slice-major kernel
+                             // (set by the API's planner where the forward's plan is that kernel in one
+                             // launch), else the grouped GEMV and act_grad_kernel
+    int gu_U, gu_nsg, gu_grid;  // that launch's stages, stages per row group and workgroups
+    bool gu_ragged;
     int64_t off_g2, off_gT, off_hT, off_partial;  // workspace offsets of dg2/du2, dgT/duT, hT, the partials
     int nslabs;              // 512-column slabs of K
     int nranges;             // row ranges of N (the one-pass kernel: its workgroups)
@@ -117,6 +124,12 @@ glu_status launch_failed(hipError_t e);
 // workspace bytes of a backward call (0 when an extent is zero), with plan_backward's status
 glu_status backward_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int M, int N, hipStream_t stream);
+// g and u with the elementwise step as the epilogue, on the forward's slice-major 8-row kernel
+// (glu_mfma8_act.hip): dg, du into gu ([2][M][N]).  U, nsg, ragged and grid as the forward's plan for
+// (M, N, K) has them (one launch, M <= 64); dense operands, K % 8 == 0.
+hipError_t mfma8_act_launch(int M, int U, int nsg, bool ragged, int grid, const uint16_t* hidden,
+                            const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* dout, uint16_t* gu,
+                            int64_t N, int64_t K, hipStream_t stream);
 // K % 8 == 0, hidden / gate_w / up_w / dwg / dwu 16-byte aligned, packed rows.  M <= 8; dw: also
 // the weight gradients (then these M rows are all rows of hidden).  dgm, dum: [M][N].
 hipError_t contract_launch(const BwdPlan& p, int M, const uint16_t* hidden, const uint16_t* gate_w,
