@@ -777,20 +777,22 @@ glu_status plan_backward(int64_t M, int64_t N, int64_t K, glu::BwdPlan* bp)
     if (st != GLU_OK) return st;
     if (M > glu::kBwdMaxM) return GLU_ERR_UNSUPPORTED;
     *bp = glu::bwd_plan(M, N, K);
-    bp->gu_pass = false;
-    bp->gu_U = bp->gu_nsg = bp->gu_grid = 0;
-    bp->gu_ragged = false;
-    // 8 < M <= 64 with the grouped GEMV's shape: where the forward runs the slice-major 8-row kernel in
-    // one launch, that kernel forms dg and du in its epilogue (the same G and U; one launch fewer)
+    bp->gu_fused = glu::kGuGrouped;
+    bp->gu_cfg = glu::MfmaConfig{};
+    // where the forward runs one MFMA launch for (M, N, K), that kernel forms dg and du in its epilogue
+    // (the same G and U; one launch fewer): the slice-major 8-row kernel for 8 < M <= 64, the 4-row
+    // kernel with hidden in LDS for the four-launch path
     const glu::MfmaConfig& c = L.mfma;
-    if (bp->path == glu::kPathMfma && !bp->gu_gemm && L.kernel == GLU_KERNEL_MFMA && L.launches == 1 &&
-        c.rows == 8 && c.order == glu::kOrderSlices && c.hidden == glu::kHiddenSlices && c.depth == 1 &&
-        c.block == glu::kMfmaMaxThreads) {
-        bp->gu_pass = true;
-        bp->gu_U = c.U;
-        bp->gu_nsg = c.nsg;
-        bp->gu_grid = c.grid;
-        bp->gu_ragged = c.ragged;
+    const bool one_mfma = L.kernel == GLU_KERNEL_MFMA && L.launches == 1 && c.block >= glu::kWave &&
+                          c.block <= glu::kMfmaMaxThreads;
+    if (one_mfma && bp->path == glu::kPathMfma && !bp->gu_gemm && c.rows == 8 && c.order == glu::kOrderSlices &&
+        c.hidden == glu::kHiddenSlices && c.depth == 1 && c.block == glu::kMfmaMaxThreads) {
+        bp->gu_fused = glu::kGuFusedPass;
+    } else if (one_mfma && bp->path == glu::kPathChunks && glu::mfma_act_supported(c, (int)M)) {
+        bp->gu_fused = glu::kGuFusedMfma4;
+    }
+    if (bp->gu_fused != glu::kGuGrouped) {
+        bp->gu_cfg = c;
         bp->accum_depth = std::max(bp->accum_depth, L.accum_depth);
     }
     return GLU_OK;
@@ -853,10 +855,14 @@ glu_status run_backward(const uint16_t* hidden, const uint16_t* gate_w, const ui
         // the elementwise step (dg, du) in the GEMM's epilogue
         e = glu::gemm_linear_launch((int)M, hidden, gate_w, up_w, gu, (int)N, (int)K, dout, s);
         if (e != hipSuccess) return fail_launch(e);
-    } else if (bp.gu_pass) {
+    } else if (bp.gu_fused == glu::kGuFusedPass) {
         // the same step in the epilogue of the forward's slice-major kernel
-        e = glu::mfma8_act_launch((int)M, bp.gu_U, bp.gu_nsg, bp.gu_ragged, bp.gu_grid, hidden, gate_w, up_w, dout, gu,
-                                  N, K, s);
+        const glu::MfmaConfig& c = bp.gu_cfg;
+        e = glu::mfma8_act_launch((int)M, c.U, c.nsg, c.ragged, c.grid, hidden, gate_w, up_w, dout, gu, N, K, s);
+        if (e != hipSuccess) return fail_launch(e);
+    } else if (bp.gu_fused == glu::kGuFusedMfma4) {
+        // and in the epilogue of the forward's 4-row kernel
+        e = glu::mfma_act_launch(bp.gu_cfg, (int)M, hidden, gate_w, up_w, dout, gu, N, K, s);
         if (e != hipSuccess) return fail_launch(e);
     } else {
         glu_projection proj[2] = {{gate_w, gu, N, K, N}, {up_w, gu + mn, N, K, N}};
@@ -1117,12 +1123,12 @@ glu_status glu_dual_gemv_backward_plan(int64_t M, int64_t N, int64_t K, glu_plan
     const bool run_all = M > 0 && N > 0 && K > 0;
     plan->kernel = run_all ? GLU_KERNEL_BACKWARD : ((M == 0) != (N == 0) && K > 0 ? GLU_KERNEL_ZERO : GLU_KERNEL_NONE);
     plan->m_per_launch = (int)M;
-    // the grouped GEMV counts as one launch; the tiled GEMM for g and u, or the forward's slice-major
-    // kernel, takes the elementwise step along
-    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm
-                                    ? (bp.gu_gemm || bp.gu_pass ? 5 : 6)
-                                : bp.path != glu::kPathChunks ? 2
-                                                              : 4)
+    // the grouped GEMV counts as one launch; the tiled GEMM for g and u, or the forward's MFMA kernel,
+    // takes the elementwise step along
+    const bool gu_one = bp.gu_gemm || bp.gu_fused != glu::kGuGrouped;  // dg and du in one launch
+    plan->launches = run_all ? (bp.path == glu::kPathMfma || bp.path == glu::kPathGemm ? (gu_one ? 5 : 6)
+                                : bp.path != glu::kPathChunks                         ? 2
+                                                                                      : (gu_one ? 3 : 4))
                              : 0;
     plan->grid = run_all ? (bp.path == glu::kPathFused1   ? bp.fused_grid
                             : bp.path == glu::kPathSplitK ? bp.split_grid

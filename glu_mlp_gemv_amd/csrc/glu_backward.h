@@ -68,7 +68,9 @@ constexpr int kSplitMaxThreads = kSplitMaxWaves * 64;
 constexpr int split_rows(int M, int U) { return U == 1 ? (M <= 2 ? 4 : 2) : (M <= 2 ? 2 : 1); }
 
 // which kernels a backward call runs
-constexpr int kPathChunks = 0;   // 2 <= M <= 8: grouped GEMV, gradient step, contraction, reduction
+constexpr int kPathChunks = 0;   // 2 <= M <= 8: dg and du (the forward's 4-row kernel with the gradient
+                                 // step as its epilogue, or the grouped GEMV and the gradient step),
+                                 // contraction, reduction
 constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
 constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
 constexpr int kPathMfma = 3;     // 8 < M <= 64: dg and du (the forward's slice-major kernel with the
@@ -79,6 +81,10 @@ constexpr int kPathGemm = 4;     // M > 64: tiled GEMM for g and u with the grad
                                  // hidden, reduction, and the weight gradients as one transposed tiled
                                  // GEMM (gemm_dw_launch)
 constexpr int kBwdMfmaMinM = 9;  // rows of hidden from which the contractions run on MFMA
+// where dg and du come from when the tiled GEMM does not form them (BwdPlan::gu_fused)
+constexpr int kGuGrouped = 0;
+constexpr int kGuFusedPass = 1;
+constexpr int kGuFusedMfma4 = 2;
 // columns of dh per dh_mfma_kernel workgroup for mt 16-row tiles of hidden per slice
 constexpr int dh_cols(int mt) { return mt <= 4 ? 128 : 64; }
 
@@ -98,11 +104,12 @@ struct BwdPlan {
     int dh_steps;            // 32-row steps of the longest range
     bool gu_gemm;            // g and u from the tiled GEMM (N % 4 == 0 and M > 64, or M > 32 with N % 8 != 0)
                              // instead of the grouped GEMV
-    bool gu_pass;            // kPathMfma without gu_gemm: dg and du from the forward's slice-major kernel
-                             // (set by the API's planner where the forward's plan is that kernel in one
-                             // launch), else the grouped GEMV and act_grad_kernel
-    int gu_U, gu_nsg, gu_grid;  // that launch's stages, stages per row group and workgroups
-    bool gu_ragged;
+    int gu_fused;            // without gu_gemm, set by the API's planner: kGuFusedPass (8 < M <= 64) or
+                             // kGuFusedMfma4 (2 <= M <= 8, four-launch path) where the forward's plan for
+                             // (M, N, K) is that kernel in one launch: dg and du from it, with the
+                             // elementwise step as its epilogue; else kGuGrouped (the grouped GEMV, then
+                             // act_grad_kernel)
+    MfmaConfig gu_cfg;       // the forward's launch it repeats
     int64_t off_g2, off_gT, off_hT, off_partial;  // workspace offsets of dg2/du2, dgT/duT, hT, the partials
     int nslabs;              // 512-column slabs of K
     int nranges;             // row ranges of N (the one-pass kernel: its workgroups)
@@ -127,6 +134,11 @@ hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int 
 // g and u with the elementwise step as the epilogue, on the forward's slice-major 8-row kernel
 // (glu_mfma8_act.hip): dg, du into gu ([2][M][N]).  U, nsg, ragged and grid as the forward's plan for
 // (M, N, K) has them (one launch, M <= 64); dense operands, K % 8 == 0.
+// the same for 2 <= M <= 8 on the forward's 4-row kernel with hidden in LDS (glu_mfma_act.hip)
+bool mfma_act_supported(const MfmaConfig& c, int M);
+hipError_t mfma_act_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
+                           const uint16_t* up_w, const uint16_t* dout, uint16_t* gu, int64_t N, int64_t K,
+                           hipStream_t stream);
 hipError_t mfma8_act_launch(int M, int U, int nsg, bool ragged, int grid, const uint16_t* hidden,
                             const uint16_t* gate_w, const uint16_t* up_w, const uint16_t* dout, uint16_t* gu,
                             int64_t N, int64_t K, hipStream_t stream);

@@ -211,6 +211,30 @@ namespace {
 
 using Mfma8Fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, RowStrides, int);
 
+// 8 < M <= 32: stages of 8 segments (512 elements); 32 < M <= 64: stages of 4 (256 elements), which
+// keep the accumulators of 3 blocks and 8 tiles of hidden rows within the registers
+Mfma8Fn pick_pass(int mt8, int U, bool ragged)
+{
+    if (U == 8) {
+        switch (mt8) {
+        case 2: return ragged ? mfma8_pass_kernel<2, 8, kPassBlocks, true> : mfma8_pass_kernel<2, 8, kPassBlocks, false>;
+        case 3: return ragged ? mfma8_pass_kernel<3, 8, kPassBlocks, true> : mfma8_pass_kernel<3, 8, kPassBlocks, false>;
+        case 4: return ragged ? mfma8_pass_kernel<4, 8, kPassBlocks, true> : mfma8_pass_kernel<4, 8, kPassBlocks, false>;
+        default: return nullptr;
+        }
+    }
+    if (U == 4) {
+        switch (mt8) {
+        case 5: return ragged ? mfma8_pass_kernel<5, 4, kPassBlocks, true> : mfma8_pass_kernel<5, 4, kPassBlocks, false>;
+        case 6: return ragged ? mfma8_pass_kernel<6, 4, kPassBlocks, true> : mfma8_pass_kernel<6, 4, kPassBlocks, false>;
+        case 7: return ragged ? mfma8_pass_kernel<7, 4, kPassBlocks, true> : mfma8_pass_kernel<7, 4, kPassBlocks, false>;
+        case 8: return ragged ? mfma8_pass_kernel<8, 4, kPassBlocks, true> : mfma8_pass_kernel<8, 4, kPassBlocks, false>;
+        default: return nullptr;
+        }
+    }
+    return nullptr;
+}
+
 template <int MT8, bool RG>
 Mfma8Fn pick8_u(int U, int depth)
 {
@@ -243,7 +267,7 @@ bool mfma8_supported(int mt8, int U, int depth, bool ragged, int block, int orde
 {
     if (block != kMfmaMaxThreads) return false;
     if (mfma8_slice_lds_bytes(mt8, U) > (size_t)kLdsBudget) return false;
-    if (order == kOrderSlices) return depth == 1 && pick_pass<false>(mt8, U, ragged) != nullptr;
+    if (order == kOrderSlices) return depth == 1 && pick_pass(mt8, U, ragged) != nullptr;
     return order == kOrderBlocks && pick8(mt8, U, depth, ragged) != nullptr;
 }
 
@@ -256,11 +280,11 @@ hipError_t mfma8_launch(int M, int U, int depth, int order, int nsg, bool ragged
     if (order == kOrderSlices) {
         const int mt8 = pass_tiles(M, U);
         // the slice-major kernel serves at most kPassBlocks blocks per workgroup
-        Mfma8PassFn fp = nullptr;
-        if (depth == 1 && (int64_t)grid * kPassBlocks >= mfma8_blocks(N)) fp = pick_pass<false>(mt8, U, ragged);
+        Mfma8Fn fp = nullptr;
+        if (depth == 1 && (int64_t)grid * kPassBlocks >= mfma8_blocks(N)) fp = pick_pass(mt8, U, ragged);
         if (!fp || M < 1 || M > 8 * mt8) return hipErrorInvalidValue;
         hipLaunchKernelGGL(fp, dim3(grid), dim3(kMfmaMaxThreads), mfma8_slice_lds_bytes(mt8, U), stream,
-                           hidden, gate_w, up_w, out, M, (int)N, (int)K, ld, nsg, nullptr);
+                           hidden, gate_w, up_w, out, M, (int)N, (int)K, ld, nsg);
         return hipGetLastError();
     }
     const int mt8 = (M + 7) / 8;

@@ -1,6 +1,6 @@
-// The slice-major 8-row MFMA kernel (mfma8_pass_kernel), shared by the forward's instantiations
-// (glu_mfma8.hip) and the backward's (glu_mfma8_act.hip: the same walk with the backward's
-// elementwise step as the epilogue).  The layout of the operands and of the accumulators is the
+// The slice-major 8-row MFMA walk (mfma8_pass_body), shared by the forward's kernel
+// (mfma8_pass_kernel, instantiated in glu_mfma8.hip) and the backward's (mfma8_pass_act_kernel in
+// glu_mfma8_act.hip: the same walk with the backward's elementwise step as the epilogue).  The layout of the operands and of the accumulators is the
 // 8-row block-diagonal one described at the top of glu_mfma8.hip.
 #pragma once
 
@@ -26,10 +26,10 @@ namespace glu {
 // upstream gradient dout ([M][N], rows ld.o apart) the lanes form dg and du (glu_act_grad) and store
 // them at out (dg, [M][N]) and out + M * ld.o (du); dout is unused otherwise.
 template <int MT8, int U, int JBMAX, bool RAGGED, bool ACT>
-__global__ void __launch_bounds__(kMfmaMaxThreads)
-mfma8_pass_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
-                  const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
-                  int M, int N, int K, RowStrides ld, int nsg, const uint16_t* __restrict__ dout)
+__device__ __forceinline__ void
+mfma8_pass_body(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+                const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
+                int M, int N, int K, RowStrides ld, int nsg, const uint16_t* __restrict__ dout)
 {
     const int64_t ldo = ld.o;
     const uint32_t ldh8 = (uint32_t)(ld.h >> 3), ldg8 = (uint32_t)(ld.g >> 3), ldu8 = (uint32_t)(ld.u >> 3);
@@ -234,32 +234,14 @@ mfma8_pass_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restric
     body(std::integral_constant<int, 1>{});
 }
 
-using Mfma8PassFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int, RowStrides, int,
-                             const uint16_t*);
-
-// 8 < M <= 32: stages of 8 segments (512 elements); 32 < M <= 64: stages of 4 (256 elements), which
-// keep the accumulators of 3 blocks and 8 tiles of hidden rows within the registers
-template <bool ACT>
-Mfma8PassFn pick_pass(int mt8, int U, bool ragged)
+// The forward's kernel: the walk above with the GLU epilogue.
+template <int MT8, int U, int JBMAX, bool RAGGED>
+__global__ void __launch_bounds__(kMfmaMaxThreads)
+mfma8_pass_kernel(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ gate_w,
+                  const uint16_t* __restrict__ up_w, uint16_t* __restrict__ out,
+                  int M, int N, int K, RowStrides ld, int nsg)
 {
-    if (U == 8) {
-        switch (mt8) {
-        case 2: return ragged ? mfma8_pass_kernel<2, 8, kPassBlocks, true, ACT> : mfma8_pass_kernel<2, 8, kPassBlocks, false, ACT>;
-        case 3: return ragged ? mfma8_pass_kernel<3, 8, kPassBlocks, true, ACT> : mfma8_pass_kernel<3, 8, kPassBlocks, false, ACT>;
-        case 4: return ragged ? mfma8_pass_kernel<4, 8, kPassBlocks, true, ACT> : mfma8_pass_kernel<4, 8, kPassBlocks, false, ACT>;
-        default: return nullptr;
-        }
-    }
-    if (U == 4) {
-        switch (mt8) {
-        case 5: return ragged ? mfma8_pass_kernel<5, 4, kPassBlocks, true, ACT> : mfma8_pass_kernel<5, 4, kPassBlocks, false, ACT>;
-        case 6: return ragged ? mfma8_pass_kernel<6, 4, kPassBlocks, true, ACT> : mfma8_pass_kernel<6, 4, kPassBlocks, false, ACT>;
-        case 7: return ragged ? mfma8_pass_kernel<7, 4, kPassBlocks, true, ACT> : mfma8_pass_kernel<7, 4, kPassBlocks, false, ACT>;
-        case 8: return ragged ? mfma8_pass_kernel<8, 4, kPassBlocks, true, ACT> : mfma8_pass_kernel<8, 4, kPassBlocks, false, ACT>;
-        default: return nullptr;
-        }
-    }
-    return nullptr;
+    mfma8_pass_body<MT8, U, JBMAX, RAGGED, false>(hidden, gate_w, up_w, out, M, N, K, ld, nsg, nullptr);
 }
 
 // Tiles of 8 hidden rows the pass kernel runs for M rows: a last slice with fewer rows than the

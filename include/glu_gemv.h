@@ -231,11 +231,13 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * K <= 2560, for M = 1 with K <= 8192, and for M <= 4 with 2560 < K <= 4096
  * (K <= 8192 when M <= 3), two launches, a pass that reads each
  * weight row once and the reduction of dhidden's partial sums; otherwise
- * dg and du from one launch of the forward's slice-major 8-row kernel with
- * the elementwise step as its epilogue (9 <= M <= 64 where the forward runs
- * that kernel in one launch), or above M = 64, or above 32 when only
- * N % 4 == 0, of a tiled GEMM with that step in its epilogue, else from the
- * grouped GEMV for g and u and the elementwise step; then the gradient kernels (above M = 8 on the matrix cores; above M = 64 dhidden
+ * dg and du from one launch of the forward's MFMA kernel for (M, N, K) with
+ * the elementwise step as its epilogue (the 4-row kernel with hidden in LDS
+ * for M <= 8, the slice-major 8-row kernel for 9 <= M <= 64, where the
+ * forward runs that kernel in one launch), or above M = 64, or above 32 when
+ * only N % 4 == 0, of a tiled GEMM with that step in its epilogue, else from
+ * the grouped GEMV for g and u and the elementwise step; then the gradient
+ * kernels (above M = 8 on the matrix cores; above M = 64 dhidden
  * over slices of 128 rows of hidden, above M = 128 of 256, and the weight
  * gradients as one tiled GEMM contracting over the rows of hidden).
  */

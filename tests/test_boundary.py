@@ -434,12 +434,21 @@ def test_backward_plan_and_workspace(lib):
     assert p["launches"] == 2 and p["block"] == 512 and p["grid"] == 100
     p = api.backward_plan(2, 9216, 2560)   # M <= 2, K <= 2560: one pass (a wave per weight row)
     assert p["launches"] == 2 and p["block"] == 256
-    assert api.backward_plan(3, 9216, 2048)["launches"] == 4   # three rows: the four launches
-    p = api.backward_plan(4, 9216, 2560)   # the grouped GEMV, gradients, contraction, reduction
-    assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 4 and p["grid"] % 5 == 0
-    assert api.backward_plan(5, 9216, 4096)["launches"] == 4
-    assert api.backward_plan(4, 9216, 4104)["launches"] == 4
-    assert api.backward_plan(9, 9216, 2560)["launches"] == 6   # M > 8: the contractions on MFMA
+    # three rows: dg and du from the forward's 4-row kernel with the elementwise step as its epilogue,
+    # the contraction, the reduction
+    assert api.backward_plan(3, 9216, 2048)["launches"] == 3
+    p = api.backward_plan(4, 9216, 2560)
+    assert p["kernel"] == api.KERNEL_BACKWARD and p["launches"] == 3 and p["grid"] % 5 == 0
+    assert api.backward_plan(5, 9216, 4096)["launches"] == 3
+    assert api.backward_plan(4, 9216, 4104)["launches"] == 3
+    # where the forward takes the 4-row kernel with hidden in L2 slices: the grouped GEMV, the
+    # elementwise kernel, the contraction, the reduction
+    assert api.plan(7, 64, 40000)["kernel_symbol"].startswith("glu::mfma_slice_kernel<")
+    assert api.backward_plan(7, 64, 40000)["launches"] == 4
+    # M > 8: the contractions on MFMA; at M = 9 the forward takes the 4-row kernel, so dg and du come
+    # from the grouped GEMV and the elementwise kernel; at M = 16 from the forward's slice-major kernel
+    assert api.backward_plan(9, 9216, 2560)["launches"] == 6
+    assert api.backward_plan(16, 9216, 2560)["launches"] == 5
     assert api.backward_plan(1, 0, 8)["kernel"] == api.KERNEL_ZERO
     assert api.backward_workspace_bytes(1, 9216, 2560) > 2 * 9216 * 2
     assert api.backward_workspace_bytes(0, 9216, 2560) == 0
