@@ -781,14 +781,15 @@ glu_status plan_backward(int64_t M, int64_t N, int64_t K, glu::BwdPlan* bp)
     bp->gu_cfg = glu::MfmaConfig{};
     // where the forward runs one MFMA launch for (M, N, K), that kernel forms dg and du in its epilogue
     // (the same G and U; one launch fewer): the slice-major 8-row kernel for 8 < M <= 64, the 4-row
-    // kernel with hidden in LDS for the four-launch path
+    // kernel with hidden in LDS up to 16 rows
     const glu::MfmaConfig& c = L.mfma;
     const bool one_mfma = L.kernel == GLU_KERNEL_MFMA && L.launches == 1 && c.block >= glu::kWave &&
                           c.block <= glu::kMfmaMaxThreads;
     if (one_mfma && bp->path == glu::kPathMfma && !bp->gu_gemm && c.rows == 8 && c.order == glu::kOrderSlices &&
         c.hidden == glu::kHiddenSlices && c.depth == 1 && c.block == glu::kMfmaMaxThreads) {
         bp->gu_fused = glu::kGuFusedPass;
-    } else if (one_mfma && bp->path == glu::kPathChunks && glu::mfma_act_supported(c, (int)M)) {
+    } else if (one_mfma && (bp->path == glu::kPathChunks || (bp->path == glu::kPathMfma && !bp->gu_gemm)) &&
+               glu::mfma_act_supported(c, (int)M)) {
         bp->gu_fused = glu::kGuFusedMfma4;
     }
     if (bp->gu_fused != glu::kGuGrouped) {

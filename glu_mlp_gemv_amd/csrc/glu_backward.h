@@ -73,9 +73,9 @@ constexpr int kPathChunks = 0;   // 2 <= M <= 8: dg and du (the forward's 4-row 
                                  // contraction, reduction
 constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
 constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
-constexpr int kPathMfma = 3;     // 8 < M <= 64: dg and du (the forward's slice-major kernel with the
-                                 // gradient step as its epilogue, or the grouped GEMV and the gradient
-                                 // step), repacking, dh_mfma_kernel, reduction, dw_mfma_kernel
+constexpr int kPathMfma = 3;     // 8 < M <= 64: dg and du (the forward's slice-major or 4-row kernel with
+                                 // the gradient step as its epilogue, or the grouped GEMV and the
+                                 // gradient step), repacking, dh_mfma_kernel, reduction, dw_mfma_kernel
 constexpr int kPathGemm = 4;     // M > 64: tiled GEMM for g and u with the gradient step in its
                                  // epilogue, repacking, dh_mfma_kernel over slices of 128 or 256 rows of
                                  // hidden, reduction, and the weight gradients as one transposed tiled
@@ -105,8 +105,8 @@ struct BwdPlan {
     bool gu_gemm;            // g and u from the tiled GEMM (N % 4 == 0 and M > 64, or M > 32 with N % 8 != 0)
                              // instead of the grouped GEMV
     int gu_fused;            // without gu_gemm, set by the API's planner: kGuFusedPass (8 < M <= 64) or
-                             // kGuFusedMfma4 (2 <= M <= 8, four-launch path) where the forward's plan for
-                             // (M, N, K) is that kernel in one launch: dg and du from it, with the
+                             // kGuFusedMfma4 (2 <= M <= 16) where the forward's plan for (M, N, K) is
+                             // that kernel in one launch: dg and du from it, with the
                              // elementwise step as its epilogue; else kGuGrouped (the grouped GEMV, then
                              // act_grad_kernel)
     MfmaConfig gu_cfg;       // the forward's launch it repeats
@@ -134,7 +134,8 @@ hipError_t act_grad_launch(uint16_t* gu, const uint16_t* dout, int64_t ldd, int 
 // g and u with the elementwise step as the epilogue, on the forward's slice-major 8-row kernel
 // (glu_mfma8_act.hip): dg, du into gu ([2][M][N]).  U, nsg, ragged and grid as the forward's plan for
 // (M, N, K) has them (one launch, M <= 64); dense operands, K % 8 == 0.
-// the same for 2 <= M <= 8 on the forward's 4-row kernel with hidden in LDS (glu_mfma_act.hip)
+// the same on the forward's 4-row kernel with hidden in LDS, up to kMfmaActMaxM rows (glu_mfma_act.hip)
+constexpr int kMfmaActMaxM = 16;
 bool mfma_act_supported(const MfmaConfig& c, int M);
 hipError_t mfma_act_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
                            const uint16_t* up_w, const uint16_t* dout, uint16_t* gu, int64_t N, int64_t K,

@@ -1,4 +1,4 @@
-// The backward's g and u step for 2 <= M <= 8 on the forward's 4-row MFMA kernel with hidden in LDS:
+// The backward's g and u step for 2 <= M <= 16 on the forward's 4-row MFMA kernel with hidden in LDS:
 // the same walk over the weights and the same per-lane sums as the forward's launch for (M, N, K)
 // (mfma_body), with the elementwise step (glu_act_grad) as the epilogue: one launch writes dg and
 // du at the workspace head.  Its own translation unit so that these instantiations compile beside
@@ -38,7 +38,8 @@ MfmaActFn pick_act_u(int U)
 
 bool mfma_act_supported(const MfmaConfig& c, int M)
 {
-    return c.rows == 4 && c.hidden == kHiddenLds && M >= 1 && M <= 8 && (c.U == 2 || c.U == 4 || c.U == 5 || c.U == 8);
+    return c.rows == 4 && c.hidden == kHiddenLds && M >= 1 && M <= kMfmaActMaxM &&
+           (c.U == 2 || c.U == 4 || c.U == 5 || c.U == 8);
 }
 
 hipError_t mfma_act_launch(const MfmaConfig& c, int M, const uint16_t* hidden, const uint16_t* gate_w,
@@ -49,9 +50,14 @@ hipError_t mfma_act_launch(const MfmaConfig& c, int M, const uint16_t* hidden, c
         c.block > kMfmaMaxThreads || c.block % kWave != 0) {
         return hipErrorInvalidValue;
     }
-    const int mt4 = (M + 3) / 4;
-    MfmaActFn fn = mt4 == 1 ? (c.ragged ? pick_act_u<1, true>(c.U) : pick_act_u<1, false>(c.U))
-                         : (c.ragged ? pick_act_u<2, true>(c.U) : pick_act_u<2, false>(c.U));
+    MfmaActFn fn = nullptr;
+    switch ((M + 3) / 4) {
+    case 1: fn = c.ragged ? pick_act_u<1, true>(c.U) : pick_act_u<1, false>(c.U); break;
+    case 2: fn = c.ragged ? pick_act_u<2, true>(c.U) : pick_act_u<2, false>(c.U); break;
+    case 3: fn = c.ragged ? pick_act_u<3, true>(c.U) : pick_act_u<3, false>(c.U); break;
+    case 4: fn = c.ragged ? pick_act_u<4, true>(c.U) : pick_act_u<4, false>(c.U); break;
+    default: break;
+    }
     if (!fn) return hipErrorInvalidValue;
     // dense operands: hidden [M][K], the weights [N][K], dout and both halves of gu [M][N]
     const RowStrides ld{K, K, K, N};

@@ -233,7 +233,7 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * weight row once and the reduction of dhidden's partial sums; otherwise
  * dg and du from one launch of the forward's MFMA kernel for (M, N, K) with
  * the elementwise step as its epilogue (the 4-row kernel with hidden in LDS
- * for M <= 8, the slice-major 8-row kernel for 9 <= M <= 64, where the
+ * up to M = 16, the slice-major 8-row kernel up to M = 64, where the
  * forward runs that kernel in one launch), or above M = 64, or above 32 when
  * only N % 4 == 0, of a tiled GEMM with that step in its epilogue, else from
  * the grouped GEMV for g and u and the elementwise step; then the gradient

@@ -445,10 +445,12 @@ def test_backward_plan_and_workspace(lib):
     # elementwise kernel, the contraction, the reduction
     assert api.plan(7, 64, 40000)["kernel_symbol"].startswith("glu::mfma_slice_kernel<")
     assert api.backward_plan(7, 64, 40000)["launches"] == 4
-    # M > 8: the contractions on MFMA; at M = 9 the forward takes the 4-row kernel, so dg and du come
-    # from the grouped GEMV and the elementwise kernel; at M = 16 from the forward's slice-major kernel
-    assert api.backward_plan(9, 9216, 2560)["launches"] == 6
+    # M > 8: the contractions on MFMA, dg and du from the forward's kernel (4-row at M = 9, slice-major
+    # at M = 16); at M = 24, K = 8 the forward's 4-row kernel has more tiles than the backward's
+    # instantiations: the grouped GEMV and the elementwise kernel
+    assert api.backward_plan(9, 9216, 2560)["launches"] == 5
     assert api.backward_plan(16, 9216, 2560)["launches"] == 5
+    assert api.backward_plan(24, 16384, 8)["launches"] == 6
     assert api.backward_plan(1, 0, 8)["kernel"] == api.KERNEL_ZERO
     assert api.backward_workspace_bytes(1, 9216, 2560) > 2 * 9216 * 2
     assert api.backward_workspace_bytes(0, 9216, 2560) == 0

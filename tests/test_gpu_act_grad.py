@@ -8,8 +8,8 @@ so only -0 becomes +0 (a sum that adds +0 to -0).  gate_w[:, 0] then runs over a
 patterns (NaN, infinities, subnormals included, spread over calls of 16384 rows), up_w[:, 0] and
 dout over seeded permutations of all patterns, and dg, du must equal the oracle's elementwise
 step bit for bit (a NaN only as a NaN).  The shapes pick the kernel that forms the step: the
-one-pass kernel (M = 1), the 4-row MFMA kernel's epilogue (M = 4 and 8 at K = 8), the separate
-elementwise kernel after the grouped GEMV (M = 8 at K = 4104, M = 16 at K = 8), the slice-major
+one-pass kernel (M = 1), the 4-row MFMA kernel's epilogue (M = 4, 8 and 16 at K = 8), the separate
+elementwise kernel after the grouped GEMV (M = 8 at K = 4104, M = 24 at K = 8), the slice-major
 8-row kernel's epilogue (M = 16, 40, 64 at K = 2560) and the tiled GEMM's epilogue (M = 100).
 """
 import numpy as np
@@ -39,8 +39,8 @@ def same_bits(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return np.where(nan_r, nan_g, (got == ref) & ~nan_g)
 
 
-@pytest.mark.parametrize("M,K", [(1, 8), (4, 8), (8, 8), (8, 4104), (16, 8), (16, 2560), (40, 2560), (64, 2560),
-                                 (100, 64)])
+@pytest.mark.parametrize("M,K", [(1, 8), (4, 8), (8, 8), (8, 4104), (16, 8), (24, 8), (16, 2560), (40, 2560),
+                                 (64, 2560), (100, 64)])
 @pytest.mark.parametrize("part", range(65536 // ROWS))
 def test_act_grad_every_gate_value(M, K, part):
     N = ROWS
@@ -53,9 +53,9 @@ def test_act_grad_every_gate_value(M, K, part):
     print(f"[act_grad] M={M} N={N} K={K} part={part} launches={p['launches']} forward={fwd}", flush=True)
     if (M, K) in ((16, 2560), (40, 2560), (64, 2560)):
         assert fwd.startswith("glu::mfma8_pass_kernel") and p["launches"] == 5  # the epilogue form
-    if (M, K) in ((4, 8), (8, 8)):
-        assert fwd.startswith("glu::mfma_kernel<") and p["launches"] == 3  # the 4-row kernel's epilogue
-    if (M, K) in ((8, 4104), (16, 8)):
+    if (M, K) in ((4, 8), (8, 8), (16, 8)):
+        assert fwd.startswith("glu::mfma_kernel<") and p["launches"] in (3, 5)  # the 4-row kernel's epilogue
+    if (M, K) in ((8, 4104), (24, 8)):
         assert p["launches"] in (4, 6)  # the separate elementwise kernel
     if M == 100:
         assert p["launches"] == 5
