@@ -54,7 +54,8 @@ def check_backward(h, wg, wu, go, got, dg_gpu, du_gpu, label=""):
     diff = np.argwhere((dg_gpu != ref.dg) | (du_gpu != ref.du))
     if diff.size:
         fwd = oracle.dual_gemv(hb, gb, ub, with_pre=True)
-        # G and U come from the grouped GEMV or from the backward's one-pass kernel
+        # G and U come from the grouped GEMV, from the forward's kernel for the shape (whose depth the
+        # backward's plan includes) or from the backward's one-pass kernel
         depth = max(api.grouped_plan(M, K, 2 * N, True, None, N % 4 == 0, N % 8 == 0)["accum_depth"],
                     api.backward_plan(M, N, K)["accum_depth"])
         for m, j in diff:
