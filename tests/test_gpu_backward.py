@@ -204,3 +204,46 @@ def test_autograd_function_matches_both_entry_points(M):
     assert np.array_equal(bits(out), bits(fwd))
     for a, b in zip((hd.grad, gd.grad, ud.grad), ref):
         assert np.array_equal(bits(a), bits(b))
+
+
+# one shape per way the backward runs: the one-pass kernel (M = 1), the K-split pass (M = 2,
+# K = 4096), the 4-row kernel's fused first step before the contraction (M = 4) and before the
+# matrix-core gradients (M = 12), the grouped GEMV with the separate elementwise kernel (M = 8 at
+# K = 4104), the slice-major kernel's fused first step (M = 16, 40) and the tiled GEMM's (M = 100)
+GRAPH_SHAPES = [(1, 1000, 1024, 2), (2, 500, 4096, 2), (4, 1000, 1024, 3), (8, 300, 4104, 4), (12, 1000, 1024, 5),
+                (16, 1000, 2560, 5), (40, 300, 520, 5), (100, 1000, 520, 5)]
+
+
+@pytest.mark.parametrize("M,N,K,launches", GRAPH_SHAPES)
+def test_backward_graph_replays(M, N, K, launches):
+    """A captured backward replays bitwise equal to an eager call, several times, with the outputs
+    and the workspace clobbered and unrelated eager work between the replays."""
+    assert api.backward_plan(M, N, K)["launches"] == launches
+    say(f"[graph] backward M={M} N={N} K={K} launches={launches}")
+    h, (wg, wu), go = inputs.hidden(M, K, 31), inputs.weights(N, K, 31), inputs.grad_out(M, N, 31)
+    hd, gd, ud, od = h.to(DEV), wg.to(DEV), wu.to(DEV), go.to(DEV)
+    ws = torch.empty(max(api.backward_workspace_bytes(M, N, K), 1), dtype=torch.uint8, device=DEV)
+    outs = [torch.empty(M, K, dtype=torch.bfloat16, device=DEV), torch.empty(N, K, dtype=torch.bfloat16, device=DEV),
+            torch.empty(N, K, dtype=torch.bfloat16, device=DEV)]
+    api.dual_gemv_backward(hd, gd, ud, od, *outs, workspace=ws)
+    torch.cuda.synchronize()
+    eager = [bits(t) for t in outs] + [bits(ws[:4 * M * N].view(torch.bfloat16))]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.dual_gemv_backward(hd, gd, ud, od, *outs, workspace=ws)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.dual_gemv_backward(hd, gd, ud, od, *outs, workspace=ws)
+    for i in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(0xA5)
+        _ = (hd.float() * 3).sum()  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        got = [bits(t) for t in outs] + [bits(ws[:4 * M * N].view(torch.bfloat16))]
+        for name, a, b in zip(("dhidden", "dgate_w", "dup_w", "dg|du"), got, eager):
+            assert np.array_equal(a, b), f"replay {i}: {name}"
