@@ -418,3 +418,66 @@ def test_valu_matrix_core_dot(M, N, K, rows):
     t = api.make_tuning(kernel=api.KERNEL_VALU, gemv_dot=2, rows_per_wave=rows)
     rep, _, _ = parity(h, wg, wu, tuning=t, label=f"valu matrix-core dot, {rows} rows per wave")
     assert rep.ok, rep.summary()
+
+
+# one shape per forward kernel family (the M = 1 GEMV has its own test above) and three grouped calls
+FWD_GRAPH_SHAPES = [(4, 1000, 1024, "glu::mfma_kernel<"), (7, 64, 40000, "glu::mfma_slice_kernel<"),
+                    (16, 1000, 2560, "glu::mfma8_pass_kernel<"), (48, 1000, 2560, "glu::mfma8_pass_kernel<"),
+                    (100, 1000, 520, "glu::gemm_kernel<")]
+
+
+@pytest.mark.parametrize("M,N,K,sym", FWD_GRAPH_SHAPES)
+def test_graph_replays_every_kernel(M, N, K, sym):
+    """Each forward kernel family, captured in a graph, replays bitwise equal to an eager call."""
+    assert api.plan(M, N, K)["kernel_symbol"].startswith(sym)
+    say(f"[graph] forward M={M} N={N} K={K} {api.plan(M, N, K)['kernel_symbol']}")
+    h, wg, wu = inputs.hidden(M, K, 41), *inputs.weights(N, K, 41)
+    hd, gd, ud = h.to(DEV), wg.to(DEV), wu.to(DEV)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    api.dual_gemv(hd, gd, ud, out=out)
+    torch.cuda.synchronize()
+    eager = bits(out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.dual_gemv(hd, gd, ud, out=out)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.dual_gemv(hd, gd, ud, out=out)
+    for i in range(3):
+        out.fill_(float("nan"))
+        _ = (hd.float() * 3).sum()  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), f"replay {i}"
+
+
+@pytest.mark.parametrize("M", [1, 16, 48])
+def test_grouped_graph_replays(M):
+    """A grouped call of three projections (QKV-like row counts), captured and replayed."""
+    K, Ns = 2560, (1024, 256, 256)
+    h = inputs.hidden(M, K, 42).to(DEV)
+    ws = [inputs.weights(n, K, 42 + i)[0].to(DEV) for i, n in enumerate(Ns)]
+    outs = [torch.empty(M, n, dtype=torch.bfloat16, device=DEV) for n in Ns]
+    api.grouped_gemv(h, ws, outs=outs)
+    torch.cuda.synchronize()
+    eager = [bits(o) for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.grouped_gemv(h, ws, outs=outs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.grouped_gemv(h, ws, outs=outs)
+    for i in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        _ = (h.float() * 3).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, o in enumerate(outs):
+            assert np.array_equal(bits(o), eager[j]), f"replay {i}, projection {j}"
