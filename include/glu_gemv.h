@@ -137,7 +137,7 @@ enum {
     GLU_KERNEL_MFMA = 3,    /* other fast-path shapes up to M = 64 */
     GLU_KERNEL_GENERIC = 4, /* unaligned, K % 8 != 0 or K > 2^25 */
     GLU_KERNEL_GEMM = 5,    /* M > 64, fast path: tiled MFMA GEMM, slices of 65536 rows of hidden */
-    GLU_KERNEL_BACKWARD = 6, /* glu_dual_gemv_backward_plan: the four backward launches */
+    GLU_KERNEL_BACKWARD = 6, /* glu_dual_gemv_backward_plan: the backward's launches (2 to 6) */
     GLU_KERNEL_CEILING = 7   /* glu_read_ceiling_plan (glu_gemv_tuning.h): the streaming-read yardstick */
 };
 
