@@ -72,7 +72,8 @@ constexpr int kPathChunks = 0;   // 2 <= M <= 8: dg and du (the forward's 4-row 
                                  // step as its epilogue, or the grouped GEMV and the gradient step),
                                  // contraction, reduction
 constexpr int kPathFused1 = 1;   // M == 1, K <= 2560: fused1_kernel, reduction
-constexpr int kPathSplitK = 2;   // M <= 4, 2560 < K <= 4096 (8192 for M <= 3): splitk_kernel, reduction
+constexpr int kPathSplitK = 2;   // M <= 2 with 2560 < K <= 8192, M = 3, 4 with 3584 < K <= 4096:
+                                 // splitk_kernel, reduction
 constexpr int kPathMfma = 3;     // 8 < M <= 64: dg and du (the forward's slice-major or 4-row kernel with
                                  // the gradient step as its epilogue, or the grouped GEMV and the
                                  // gradient step), repacking, dh_mfma_kernel, reduction, dw_mfma_kernel

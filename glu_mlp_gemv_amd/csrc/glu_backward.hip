@@ -11,7 +11,7 @@
 // M <= 2 with K <= 2560: one pass (fused1_kernel, below) reads each row of Wg
 // and Wu once, forms G and U, dg and du, writes the row of dWg and dWu and
 // accumulates dh, then dh_reduce_kernel adds the workgroups' partials.
-// M <= 4 with 2560 < K <= 4096 (K <= 8192 for M <= 3): also one pass
+// M <= 2 with 2560 < K <= 8192, and M = 3 or 4 with 3584 < K <= 4096: also one pass
 // (splitk_kernel), K split over the lanes of a workgroup so that each lane
 // keeps its columns of dh for all M rows in registers, then dh_reduce_kernel.
 // Above M = 8 the contractions run on the matrix cores (glu_backward_mfma.hip).
@@ -792,10 +792,15 @@ BwdPlan bwd_plan(int64_t M, int64_t N, int64_t K)
     p.fused = M >= 1 && M <= kFusedMaxM && K >= 8 && (K / 8 + kWave - 1) / kWave <= fused_max_u((int)M);
     p.path = p.fused ? kPathFused1 : kPathChunks;
     int64_t rows_per_wave = 0;
-    // split over K: K / 8 chunks over at most 8 waves of 1 or 2 chunks per lane
+    // split over K: K / 8 chunks over at most 8 waves of 1 or 2 chunks per lane.  Above 2 rows only
+    // at one chunk per lane on all 8 waves (3584 < K <= 4096): elsewhere the four-launch path, whose
+    // g and u step is the forward's 4-row kernel with the elementwise step as its epilogue, is faster
+    // (K=3072 N=9216 M = 3 / 4: 79.3 / 80.8 us against 94.3 / 93.7; K=8192 N=4096 M = 3: 87.2
+    // against 106.1), while at K = 4096 the split pass holds (N=12288 M = 4: 118.9 against 128.9)
     const int64_t nch = K / 8;
     const int64_t split_cap = (int64_t)kSplitMaxWaves * kWave * (M <= kSplitMaxM2 ? 2 : 1);
-    if (!p.fused && M >= 1 && M <= kSplitMaxM && K >= kSplitMinK && nch <= split_cap) {
+    const bool split_shape = M <= 2 || (nch > (int64_t)(kSplitMaxWaves - 1) * kWave && nch <= (int64_t)kSplitMaxWaves * kWave);
+    if (!p.fused && M >= 1 && M <= kSplitMaxM && K >= kSplitMinK && nch <= split_cap && split_shape) {
         p.path = kPathSplitK;
         p.split_u = nch <= (int64_t)kSplitMaxWaves * kWave ? 1 : 2;
         p.split_waves = (int)((nch + (int64_t)kWave * p.split_u - 1) / ((int64_t)kWave * p.split_u));

@@ -228,8 +228,8 @@ glu_status glu_grouped_gemv_plan(int64_t M, int64_t K, int64_t rows, int fast, g
  * shapes, 2-byte alignment, overlap of an output or the workspace with an
  * input or another output, workspace) happens before any HIP call.  On
  * stream, asynchronous, deterministic, allocating nothing: for M <= 2 with
- * K <= 2560, for M = 1 with K <= 8192, and for M <= 4 with 2560 < K <= 4096
- * (K <= 8192 when M <= 3), two launches, a pass that reads each
+ * K <= 2560, for M <= 2 with 2560 < K <= 8192, and for M = 3 or 4 with
+ * 3584 < K <= 4096, two launches, a pass that reads each
  * weight row once and the reduction of dhidden's partial sums; otherwise
  * dg and du from one launch of the forward's MFMA kernel for (M, N, K) with
  * the elementwise step as its epilogue (the 4-row kernel with hidden in LDS

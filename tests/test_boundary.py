@@ -430,8 +430,12 @@ def test_backward_plan_and_workspace(lib):
     assert p["launches"] == 2 and p["block"] == 512 and p["grid"] == 256
     p = api.backward_plan(1, 9216, 2568)
     assert p["launches"] == 2 and p["block"] == 384
-    p = api.backward_plan(3, 100, 8192)    # two chunks per lane up to M = 3
+    p = api.backward_plan(2, 100, 8192)    # two chunks per lane
     assert p["launches"] == 2 and p["block"] == 512 and p["grid"] == 100
+    # above 2 rows only at one chunk per lane on 8 waves (3584 < K <= 4096); else the four-launch path
+    assert api.backward_plan(3, 100, 8192)["launches"] == 3
+    assert api.backward_plan(4, 9216, 3072)["launches"] == 3
+    assert api.backward_plan(4, 12288, 4096)["launches"] == 2
     p = api.backward_plan(2, 9216, 2560)   # M <= 2, K <= 2560: one pass (a wave per weight row)
     assert p["launches"] == 2 and p["block"] == 256
     # three rows: dg and du from the forward's 4-row kernel with the elementwise step as its epilogue,
